@@ -1,0 +1,70 @@
+"""Seeded synthetic inputs shared by the GPU path's tests/bench and the oracle.
+
+This module draws random numbers and stores them in the input formats the
+library consumes (bf16, fp32, packed E4M3|bf16 rows via torch's own casts).
+It contains none of the attention method's arithmetic: no pooling, scoring,
+selection, normalisation or rotation.
+
+Every tensor is drawn from its own torch.Generator whose seed is derived from
+(workload seed, tensor name), so a tensor does not change when another one is
+added or resized.  The same seed gives the same values on the same device
+type; the oracle always reads the bytes the GPU reads (copied to host).
+"""
+
+import zlib
+
+import torch
+
+
+def _seed(seed, name):
+    return (int(seed) * 1_000_003 + zlib.crc32(name.encode())) % (2 ** 62)
+
+
+def _gen(seed, name, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(seed, name))
+    return g
+
+
+def normal(shape, seed, name, device="cpu", std=1.0, mean=0.0,
+           dtype=torch.float32):
+    """N(mean, std^2) values, drawn in float32 and cast (RNE) to dtype."""
+    g = _gen(seed, name, device)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    if mean != 0.0:
+        x.add_(mean)
+    return x.to(dtype)
+
+
+def integers(shape, lo, hi, seed, name, device="cpu", dtype=torch.float32):
+    """Uniform integers in [lo, hi], stored exactly in dtype."""
+    g = _gen(seed, name, device)
+    x = torch.randint(lo, hi + 1, shape, generator=g, device=device)
+    return x.to(dtype)
+
+
+def pack_values(vals, R):
+    """float32 [..., D] -> uint8 [..., D+R]: E4M3FN codes of dims [0, D-R)
+    followed by little-endian bf16 of dims [D-R, D) (torch casts)."""
+    D = vals.shape[-1]
+    lo = vals[..., : D - R].to(torch.float8_e4m3fn).view(torch.uint8)
+    hi = vals[..., D - R:].contiguous().to(torch.bfloat16).view(torch.uint8)
+    return torch.cat([lo, hi], dim=-1).contiguous()
+
+
+def packed_rows(shape, D, R, seed, name, device="cpu", chunk_rows=1 << 20):
+    """Packed rows whose D values are N(0,1): uint8 [*shape, D+R].
+
+    Drawn in row chunks so that very large caches need little scratch."""
+    rows = 1
+    for s in shape:
+        rows *= s
+    out = torch.empty((rows, D + R), dtype=torch.uint8, device=device)
+    g = _gen(seed, name, device)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        v = torch.randn((r1 - r0, D), generator=g, device=device)
+        out[r0:r1] = pack_values(v, R)
+    return out.view(*shape, D + R)

@@ -1,0 +1,221 @@
+"""Pins for the oracle's indexer, top-k and attention.
+
+Indexer: exact integer arithmetic against pure-Python loops.  Top-k: the
+rank definition checked pair by pair (brute force), ties to the lower index,
+"below the budget nothing is dropped".  Attention: torch's
+scaled_dot_product_attention in float64 with an explicit sink column (a
+library routine), sink sums, a closed form with identical rows, CSA with k
+covering every entry equals dense/HCA, relative-position (shift) invariance
+and permutation invariance."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attend as oa
+from oracle import compress as oc
+from oracle import indexer as oi
+
+from test_oracle_rope_compress import complex_rope
+
+
+# ---------------------------------------------------------------- indexer --
+
+def test_index_scores_integer_bruteforce():
+    g = np.random.default_rng(0)
+    HI, dI, N = 4, 32, 50
+    q = g.integers(-3, 4, (HI, dI))
+    w = g.integers(-3, 4, HI)
+    k = g.integers(-3, 4, (N, dI))
+    got = oi.index_scores(q, w, k, N)
+    for j in range(N):
+        total = 0
+        for h in range(HI):
+            dot = 0
+            for d in range(dI):
+                dot += int(q[h, d]) * int(k[j, d])
+            total += int(w[h]) * max(dot, 0)
+        assert got[j] == total
+    # only the first V entries are scored
+    assert oi.index_scores(q, w, k, 17).shape == (17,)
+
+
+def test_visible_entries():
+    assert oi.visible_entries(4095, 1024, 4) == 1024
+    assert oi.visible_entries(4094, 1024, 4) == 1023
+    assert oi.visible_entries(2, 1024, 4) == 0
+    assert oi.visible_entries((1 << 20) + 4095, 263168, 4) == 263168
+    assert oi.visible_entries((1 << 20) + 126, 8224, 128) == 8192
+
+
+def _topk_by_rank(scores, k):
+    """Brute force: j is kept iff fewer than k entries beat it, where i beats
+    j when s_i > s_j, or s_i == s_j and i < j."""
+    V = len(scores)
+    keep = []
+    for j in range(V):
+        beats = sum(1 for i in range(V)
+                    if scores[i] > scores[j] or (scores[i] == scores[j] and i < j))
+        if beats < k:
+            keep.append(j)
+    return keep
+
+
+@pytest.mark.parametrize("V,k,spread", [(300, 64, 3), (300, 64, 1000), (40, 64, 2),
+                                        (64, 64, 1), (1, 4, 0), (129, 128, 0)])
+def test_topk_matches_rank_definition(V, k, spread):
+    g = np.random.default_rng(V + k + spread)
+    s = g.integers(-spread, spread + 1, V).astype(np.float64)
+    got = oi.topk_select(s, k)
+    want = _topk_by_rank(list(s), k)
+    assert list(got[: len(want)]) == want
+    assert np.all(got[len(want):] == -1)
+    if V <= k:                         # below the budget nothing is dropped
+        assert list(got[:V]) == list(range(V))
+
+
+def test_topk_ties_go_to_lower_index():
+    s = np.zeros(10)
+    s[7] = 1.0
+    assert list(oi.topk_select(s, 3)) == [0, 1, 7]
+
+
+# --------------------------------------------------------------- attention --
+
+def _setup(H=4, D=128, R=64, n=20, seed=0):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((H, D)), 1 + 0.1 * g.standard_normal(D),
+            g.standard_normal((n, D)), g.standard_normal(H))
+
+
+def _sdpa_with_sink(qt, rows, sink, scale):
+    """torch SDPA (float64, CPU) over rows plus one zero key/value whose
+    additive mask is the sink logit."""
+    H, D = qt.shape
+    keys = np.concatenate([rows, np.zeros((1, D))])
+    mask = np.zeros((H, 1, keys.shape[0]))
+    mask[:, 0, -1] = sink
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qt)[:, None, :], torch.from_numpy(keys)[None].expand(H, -1, -1),
+        torch.from_numpy(keys)[None].expand(H, -1, -1), attn_mask=torch.from_numpy(mask),
+        scale=scale)
+    return out[:, 0, :].numpy()
+
+
+@pytest.mark.parametrize("t", [0, 5, 4095, (1 << 20) - 1])
+def test_attend_rows_matches_sdpa_with_sink(t):
+    q, gq, rows, sink = _setup(seed=t & 0xFF)
+    D = q.shape[1]
+    scale = D ** -0.5
+    out, p, lse = oa.attend_rows(q, gq, t, rows, sink, scale, 1e-6, 64, 1e4)
+    qn = torch.nn.functional.rms_norm(torch.from_numpy(q), (D,), torch.from_numpy(gq),
+                                      eps=1e-6).numpy()
+    qt = complex_rope(qn, t, 64, 1e4)
+    o = _sdpa_with_sink(qt, rows, sink, scale)
+    np.testing.assert_allclose(out, complex_rope(o, -t, 64, 1e4), rtol=1e-10, atol=1e-12)
+    # lse: log of the full denominator, sink included
+    logits = scale * qt @ rows.T
+    want = np.log(np.exp(sink) + np.exp(logits).sum(-1))
+    np.testing.assert_allclose(lse, want, rtol=1e-12)
+
+
+def test_sink_sums():
+    q, gq, rows, sink = _setup(seed=3)
+    _, p, lse = oa.attend_rows(q, gq, 9, rows, np.full(4, -np.inf), 0.1, 1e-6, 64, 1e4)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=1e-13)
+    _, p, lse = oa.attend_rows(q, gq, 9, rows, sink, 0.1, 1e-6, 64, 1e4)
+    assert np.all(p.sum(-1) < 1.0)
+    np.testing.assert_allclose(p.sum(-1), 1.0 - np.exp(sink - lse), rtol=1e-12)
+    # no rows at all: weight all on the sink, zero output
+    out, p, lse = oa.attend_rows(q, gq, 9, rows[:0], sink, 0.1, 1e-6, 64, 1e4)
+    assert np.all(out == 0) and np.allclose(lse, sink)
+
+
+def test_closed_form_identical_rows():
+    g = np.random.default_rng(5)
+    H, D, n = 3, 128, 37
+    u = g.standard_normal(D)
+    u[64:] = 0.0                        # zero rotary dims
+    rows = np.tile(u, (n, 1))
+    q = g.standard_normal((H, D))
+    sink = g.standard_normal(H)
+    scale = 0.3
+    out, _, _ = oa.attend_rows(q, np.ones(D), 123, rows, sink, scale, 1e-6, 64, 1e4)
+    qt = oc.rmsnorm(q, np.ones(D), 1e-6)    # RoPE leaves q . u unchanged here
+    a = scale * (qt @ u)
+    S = n * np.exp(a) / (n * np.exp(a) + np.exp(sink))
+    np.testing.assert_allclose(out, S[:, None] * u[None, :], rtol=1e-12, atol=1e-15)
+
+
+def _cache(T, m, D, R, seed):
+    """Float64 entries and window rows built by the oracle's compressor."""
+    g = np.random.default_rng(seed)
+    c = g.standard_normal((T, D))
+    s = g.standard_normal(T)
+    bias = 0.1 * g.standard_normal(2 * m)
+    gamma = np.ones(D)
+    _, ent = oc.compress_pool(c, s, 0, m, bias, gamma, 1e-6, R, 1e4)
+    return c, s, bias, gamma, ent
+
+
+def test_csa_with_full_k_equals_hca_and_dense():
+    T, m, D, R, H, W = 256, 4, 128, 64, 4, 16
+    c, s, bias, gamma, ent = _cache(T, m, D, R, 1)
+    g = np.random.default_rng(2)
+    q = g.standard_normal((1, H, D))
+    sink = g.standard_normal(H)
+    t = T - 1
+    N = ent.shape[0]
+    win = oc.compress_pack(c[t - W + 1:t + 1], t - W + 1, gamma, 1e-6, R, 1e4)
+    topk = np.arange(N, dtype=np.int32)[None]
+    a, la = oa.attend_csa(q, ent, topk, win, np.ones(D), sink, t, W, D ** -0.5, 1e-6, R, 1e4)
+    b, lb = oa.attend_hca(q, ent, N, m, win, np.ones(D), sink, t, W, D ** -0.5, 1e-6, R, 1e4)
+    np.testing.assert_allclose(a, b, rtol=1e-12)
+    np.testing.assert_allclose(la, lb, rtol=1e-12)
+    # a permuted top-k list (with -1 holes) gives the same output
+    perm = np.random.default_rng(3).permutation(N).astype(np.int32)
+    padded = np.concatenate([perm, np.full(7, -1, np.int32)])[None]
+    c2, _ = oa.attend_csa(q, ent, padded, win, np.ones(D), sink, t, W, D ** -0.5, 1e-6, R, 1e4)
+    np.testing.assert_allclose(c2, a, rtol=1e-12)
+    # W = 0 (no window): dense SDPA over every entry
+    d, _ = oa.attend_hca(q, ent, N, m, win[:0], np.ones(D), sink, t, 0, D ** -0.5, 1e-6, R, 1e4)
+    qt = complex_rope(oc.rmsnorm(q[0], np.ones(D), 1e-6), t, R, 1e4)
+    o = _sdpa_with_sink(qt, ent, sink, D ** -0.5)
+    np.testing.assert_allclose(d[0], complex_rope(o, -t, R, 1e4), rtol=1e-10, atol=1e-13)
+
+
+def test_relative_positions_shift_invariance():
+    """Shifting every position by a multiple of m leaves the output unchanged:
+    the output's inverse rotation removes the absolute position."""
+    T, m, D, R, H, W = 128, 4, 128, 64, 3, 8
+    g = np.random.default_rng(7)
+    c = g.standard_normal((T, D))
+    s = g.standard_normal(T)
+    bias = 0.1 * g.standard_normal(2 * m)
+    q = g.standard_normal((1, H, D))
+    sink = g.standard_normal(H)
+    outs = []
+    for shift in (0, 4 * 1000, 4 * 262144):
+        # the same T tokens at positions shift..shift+T-1; entries whose whole
+        # 2m window lies in the block (the first one would need older tokens)
+        js, ent = oc.compress_pool(c, s, shift, m, bias, np.ones(D), 1e-6, R, 1e4,
+                                   j0=shift // m + 1, n=T // m - 1)
+        assert js[0] == shift // m + 1
+        t = shift + T - 1
+        win = oc.compress_pack(c[T - W:], t - W + 1, np.ones(D), 1e-6, R, 1e4)
+        topk = np.arange(len(js), dtype=np.int32)[None]   # rows of `ent`
+        out, lse = oa.attend_csa(q, ent, topk, win, np.ones(D), sink, t, W, D ** -0.5,
+                                 1e-6, R, 1e4)
+        outs.append((out, lse))
+    for out, lse in outs[1:]:
+        np.testing.assert_allclose(out, outs[0][0], rtol=1e-8, atol=1e-9)
+        np.testing.assert_allclose(lse, outs[0][1], rtol=1e-12)
+
+
+def test_window_rows_at_sequence_start():
+    D, W = 8, 4
+    win = np.arange(2 + W - 1)[:, None] * np.ones(D)   # buffer rows for q_pos0=1, Tq=2
+    r0 = oa.window_rows(win, 1, 1, W)                   # t = 1 sees positions 0..1
+    assert r0.shape[0] == 2 and r0[0, 0] == 2 and r0[-1, 0] == 3
+    r1 = oa.window_rows(win, 2, 1, W)                   # t = 2 sees positions 0..2
+    assert r1.shape[0] == 3 and r1[-1, 0] == 4
