@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Decode throughput at a 1M-token context on one MI355X.
+
+One step is one decode token per sequence through
+  * a CSA layer (compression m = 4, top-k 1024, window 128), 8 sequences of
+    2^20 tokens: pack the new token's window row, pool the entry it completes,
+    indexer scores over all 262,144 entries, top-k, sparse attention;
+  * an HCA layer (compression m' = 128, window 128), 32 sequences of 2^20
+    tokens: pack, pool, dense attention over all 8,192 entries.
+All inputs are seeded synthetic N(0,1) data resident in HBM before timing.
+The HCA caches rotate over several copies so successive steps do not hit the
+256 MB Infinity Cache (each model layer has its own cache).
+
+Prints ONE JSON line: value = query-token-layers per second (8 CSA + 32 HCA
+query tokens per step / step time), per-layer rates, the per-kernel timing
+breakdown from HIP events, the roofline of the dominant kernel, and the
+float64 oracle timed on the host cores on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "decode query-tokens/s per layer at 1M ctx (CSA, HCA); % of HBM/MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_inputs(dev, rotate):
+    import torch
+    from long_context_sparse_csa_amd import synth
+    from long_context_sparse_csa_amd.configs import CSA_1M, HCA_1M
+
+    c, h = CSA_1M, HCA_1M
+    inp = {"csa": {}, "hca": {}}
+    # ---- CSA layer (cfg: 8 x 1M, m = 4)
+    d = inp["csa"]
+    N = c.T // c.m
+    d["N"] = N
+    d["t"] = c.T - 1
+    d["entries"] = synth.packed_rows((c.B, N), c.D, c.R, c.seed, "entries", dev,
+                                     chunk_rows=1 << 18)
+    d["k_idx"] = synth.normal((c.B, N, c.dI), c.seed, "kI", dev, dtype=torch.bfloat16)
+    d["q_idx"] = synth.normal((c.B, 1, c.HI, c.dI), c.seed, "qI", dev, dtype=torch.bfloat16)
+    d["w_idx"] = synth.normal((c.B, 1, c.HI), c.seed, "w", dev)
+    d["q"] = synth.normal((c.B, 1, c.H, c.D), c.seed, "q", dev, dtype=torch.bfloat16)
+    d["win"] = synth.packed_rows((c.B, c.W), c.D, c.R, c.seed, "win", dev)
+    d["raw"] = synth.normal((c.B, 2 * c.m, c.D), c.seed, "raw", dev, dtype=torch.bfloat16)
+    d["score"] = synth.normal((c.B, 2 * c.m), c.seed, "score", dev)
+    d["bias"] = synth.normal((2 * c.m,), c.seed, "bias", dev, std=0.1)
+    d["sink"] = synth.normal((c.H,), c.seed, "sink", dev)
+    d["gamma"] = torch.ones(c.D, device=dev)
+    # ---- HCA layer (cfg: 32 x 1M, m' = 128)
+    d = inp["hca"]
+    N = h.T // h.m
+    d["N"] = N
+    d["t"] = h.T - 1
+    d["entries"] = [synth.packed_rows((h.B, N), h.D, h.R, h.seed + 100 * i, "entries", dev)
+                    for i in range(rotate)]
+    d["q"] = synth.normal((h.B, 1, h.H, h.D), h.seed, "q", dev, dtype=torch.bfloat16)
+    d["win"] = synth.packed_rows((h.B, h.W), h.D, h.R, h.seed, "win", dev)
+    d["raw"] = synth.normal((h.B, 2 * h.m, h.D), h.seed, "raw", dev, dtype=torch.bfloat16)
+    d["score"] = synth.normal((h.B, 2 * h.m), h.seed, "score", dev)
+    d["bias"] = synth.normal((2 * h.m,), h.seed, "bias", dev, std=0.1)
+    d["sink"] = synth.normal((h.H,), h.seed, "sink", dev)
+    d["gamma"] = torch.ones(h.D, device=dev)
+    return inp
+
+
+def make_step(inp, dev):
+    """Returns (list of (name, fn) launches for one step, output buffers)."""
+    import torch
+    from long_context_sparse_csa_amd import ops
+    from long_context_sparse_csa_amd.configs import CSA_1M, HCA_1M
+
+    c, h = CSA_1M, HCA_1M
+    a, b = inp["csa"], inp["hca"]
+    Nc, Nh = a["N"], b["N"]
+    tc, th = a["t"], b["t"]
+    scores = torch.empty((c.B, ops.score_stride(1, Nc, tc, c.m)), dtype=torch.float32, device=dev)
+    topk = torch.empty((c.B, 1, c.k), dtype=torch.int32, device=dev)
+    tk_ws = torch.empty(max(ops.topk_select_workspace_bytes(c.B, 1, Nc, tc, c.m, c.k), 16),
+                        dtype=torch.uint8, device=dev)
+    out_c = torch.empty_like(a["q"])
+    out_h = torch.empty_like(b["q"])
+    csa_ws = torch.empty(max(ops.csa_attend_workspace_bytes(c.B, 1, c.H, c.D, c.k, c.W), 16),
+                         dtype=torch.uint8, device=dev)
+    hca_ws = torch.empty(max(ops.hca_attend_workspace_bytes(h.B, 1, h.H, h.D, Nh, h.m, th, h.W),
+                             16), dtype=torch.uint8, device=dev)
+    state = {"i": 0}
+
+    a["raw_last"] = a["raw"][:, -1:].contiguous()   # the new token's raw latent
+    b["raw_last"] = b["raw"][:, -1:].contiguous()
+
+    def csa_pack():
+        ops.compress_pack(a["raw_last"], a["gamma"], a["win"], raw_pos0=tc, out_row0=c.W - 1)
+
+    def csa_pool():
+        ops.compress_pool(a["raw"], a["score"], a["bias"], a["gamma"], a["entries"],
+                          raw_pos0=tc + 1 - 2 * c.m, m=c.m, entry0=Nc - 1, n_out=1,
+                          out_row0=Nc - 1)
+
+    def csa_score():
+        ops.index_score(a["q_idx"], a["w_idx"], a["k_idx"], n_entries=Nc, q_pos0=tc, m=c.m,
+                        scores=scores)
+
+    def csa_topk():
+        ops.topk_select(scores, B=c.B, Tq=1, n_entries=Nc, q_pos0=tc, m=c.m, k=c.k, topk=topk,
+                        workspace=tk_ws)
+
+    def csa_attend():
+        ops.csa_attend(a["q"], a["entries"], topk, a["win"], a["gamma"], a["sink"], q_pos0=tc,
+                       W=c.W, out=out_c, workspace=csa_ws)
+
+    def hca_ent():
+        return b["entries"][state["i"] % len(b["entries"])]
+
+    def hca_pack():
+        ops.compress_pack(b["raw_last"], b["gamma"], b["win"], raw_pos0=th, out_row0=h.W - 1)
+
+    def hca_pool():
+        ops.compress_pool(b["raw"], b["score"], b["bias"], b["gamma"], hca_ent(),
+                          raw_pos0=th + 1 - 2 * h.m, m=h.m, entry0=Nh - 1, n_out=1,
+                          out_row0=Nh - 1)
+
+    def hca_attend():
+        ops.hca_attend(b["q"], hca_ent(), b["win"], b["gamma"], b["sink"], n_entries=Nh, m=h.m,
+                       q_pos0=th, W=h.W, out=out_h, workspace=hca_ws)
+        state["i"] += 1
+
+    launches = [("csa_pack", csa_pack), ("csa_pool", csa_pool), ("index_score", csa_score),
+                ("topk_select", csa_topk), ("csa_attend", csa_attend), ("hca_pack", hca_pack),
+                ("hca_pool", hca_pool), ("hca_attend", hca_attend)]
+    return launches, {"topk": topk, "out_csa": out_c, "out_hca": out_h, "scores": scores}
+
+
+def algorithmic_bytes():
+    """Bytes each call must move by the method's definition (per step)."""
+    from long_context_sparse_csa_amd.configs import CSA_1M as c, HCA_1M as h
+    Nc, Nh = c.T // c.m, h.T // h.m
+    row = c.D + c.R
+    out = {
+        "index_score": c.B * (Nc * c.dI * 2 + c.HI * c.dI * 2 + c.HI * 4),
+        "csa_attend": c.B * ((c.k + c.W) * row + c.H * c.D * 2 * 2 + c.k * 4),
+        "hca_attend": h.B * ((Nh + h.W) * row + h.H * h.D * 2 * 2),
+        "csa_pool": c.B * (2 * c.m * (c.D * 2 + 4) + row),
+        "hca_pool": h.B * (2 * h.m * (h.D * 2 + 4) + row),
+        "csa_pack": c.B * (c.D * 2 + row),
+        "hca_pack": h.B * (h.D * 2 + row),
+    }
+    flops = {
+        "index_score": c.B * 2 * c.HI * c.dI * Nc,
+        "csa_attend": c.B * 4 * c.H * c.D * (c.k + c.W),
+        "hca_attend": h.B * 4 * h.H * h.D * (Nh + h.W),
+    }
+    return out, flops
+
+
+def run_timed(launches, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        for _, fn in launches:
+            fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        for _, fn in launches:
+            fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def run_breakdown(launches, steps):
+    """Per-call HIP-event durations on the launching (current) stream."""
+    import torch
+    names = [n for n, _ in launches]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        evs[s][0].record()
+        for i, (_, fn) in enumerate(launches):
+            fn()
+            evs[s][i + 1].record()
+    torch.cuda.synchronize()
+    tot = {n: 0.0 for n in names}
+    for s in range(steps):
+        for i, n in enumerate(names):
+            tot[n] += evs[s][i].elapsed_time(evs[s][i + 1])
+    return {n: tot[n] / steps * 1e3 for n in names}   # microseconds
+
+
+def cpu_baseline(inp, budget_s):
+    """The float64 oracle on a bounded sample of the same inputs: whole CSA
+    and HCA layers for single sequences, alternating, until the budget."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+    from long_context_sparse_csa_amd.configs import CSA_1M as c, HCA_1M as h
+    from oracle import attend as oa, codecs, compress as oc, indexer as oi
+
+    def f64(t):
+        return codecs.bf16_decode(t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+    a, b = inp["csa"], inp["hca"]
+    t_csa, t_hca, n_csa, n_hca = 0.0, 0.0, 0, 0
+    t0 = time.perf_counter()
+    s = 0
+    while time.perf_counter() - t0 < budget_s and s < 64:
+        bb = s % c.B
+        # host copies of the sequence's bytes (not timed: the oracle's input)
+        kI = a["k_idx"][bb].cpu()
+        ent = a["entries"][bb].cpu().numpy()
+        win = a["win"][bb].cpu().numpy()
+        raw = a["raw"][bb]
+        q, qI, w = a["q"][bb], a["q_idx"][bb], a["w_idx"][bb].cpu().double().numpy()
+        x0 = time.perf_counter()
+        e = oc.compress_pool(f64(raw), a["score"][bb].cpu().double().numpy(), c.T - 2 * c.m, c.m,
+                             a["bias"].cpu().double().numpy(), np.ones(c.D), c.eps, c.R,
+                             c.rope_base, j0=a["N"] - 1, n=1)[1]
+        ent[-1] = codecs.pack_rows(e, c.R)[0]
+        tk, _ = oi.index_topk(f64(qI), w, f64(kI), a["N"], [a["t"]], c.m, c.k)
+        rows = codecs.unpack_rows(ent[tk[0][tk[0] >= 0]], c.D, c.R)
+        rows = np.concatenate([rows, codecs.unpack_rows(win, c.D, c.R)])
+        oa.attend_rows(f64(q)[0], np.ones(c.D), a["t"], rows, a["sink"].cpu().double().numpy(),
+                       c.scale, c.eps, c.R, c.rope_base)
+        t_csa += time.perf_counter() - x0
+        n_csa += 1
+        # HCA sequence
+        hb = s % h.B
+        ent = inp["hca"]["entries"][0][hb].cpu().numpy()
+        win = b["win"][hb].cpu().numpy()
+        q = b["q"][hb]
+        x0 = time.perf_counter()
+        rows = np.concatenate([codecs.unpack_rows(ent, h.D, h.R), codecs.unpack_rows(win, h.D, h.R)])
+        oa.attend_rows(f64(q)[0], np.ones(h.D), b["t"], rows, b["sink"].cpu().double().numpy(),
+                       h.scale, h.eps, h.R, h.rope_base)
+        t_hca += time.perf_counter() - x0
+        n_hca += 1
+        s += 1
+    per_csa, per_hca = t_csa / n_csa, t_hca / n_hca
+    step = c.B * per_csa + h.B * per_hca
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": (c.B + h.B) / step,
+        "unit": "query-tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{n_csa} CSA-layer queries (compress of one entry, float64 indexer over "
+                   f"262,144 entries, top-1024, attention over 1152 rows) and {n_hca} HCA-layer "
+                   f"queries (attention over 8320 rows) at 1M context, extrapolated to the "
+                   f"8 + 32-query step"),
+        "csa_query_s": per_csa,
+        "hca_query_s": per_hca,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_sparse_csa_amd import ops
+    from long_context_sparse_csa_amd.configs import CSA_1M as c, HCA_1M as h
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    ops.lib()
+    log("generating inputs")
+    inp = build_inputs(dev, args.rotate)
+    launches, outs = make_step(inp, dev)
+    torch.cuda.synchronize()
+    log("timing")
+    ms, wall = run_timed(launches, args.steps, args.warmup)
+    log(f"step {ms * 1e3:.1f} us")
+    br = run_breakdown(launches, max(10, min(args.steps, 50)))
+    log("breakdown (us): " + ", ".join(f"{k} {v:.1f}" for k, v in br.items()))
+    abytes, aflops = algorithmic_bytes()
+
+    t_csa_us = sum(br[k] for k in ("csa_pack", "csa_pool", "index_score", "topk_select",
+                                   "csa_attend"))
+    t_hca_us = sum(br[k] for k in ("hca_pack", "hca_pool", "hca_attend"))
+    kernels = {}
+    for k, us in br.items():
+        ent = {"us": round(us, 2)}
+        if k in abytes:
+            ent["GBps"] = round(abytes[k] / (us * 1e-6) / 1e9, 1)
+            ent["hbm_frac"] = round(abytes[k] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        if k in aflops:
+            ent["TFLOPs"] = round(aflops[k] / (us * 1e-6) / 1e12, 2)
+        kernels[k] = ent
+    dom = "index_score"
+    ach = abytes[dom] / (br[dom] * 1e-6) / 1e9
+    roofline = {"kernel": "index_score_kernel<128,4>", "bound": "hbm",
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": abytes[dom]}
+
+    res = {
+        "metric": METRIC,
+        "value": round((c.B + h.B) / (ms * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_1m_csa_hca",
+            "csa": f"B={c.B} T=2^20 m={c.m} N={c.T // c.m} H={c.H} D={c.D} R={c.R} "
+                   f"HI={c.HI} dI={c.dI} k={c.k} W={c.W}",
+            "hca": f"B={h.B} T=2^20 m={h.m} N={h.T // h.m} H={h.H} D={h.D} R={h.R} W={h.W}",
+            "storage": "entries E4M3 (448 dims) + bf16 (64 rotary dims) = 576 B/row; "
+                       "indexer keys bf16",
+            "value_is": "query-token-layers/s: (8 CSA + 32 HCA query tokens) per step",
+            "hca_cache_copies": args.rotate,
+        },
+        "per_layer": {
+            "csa_query_tokens_per_s": round(c.B / (t_csa_us * 1e-6), 1),
+            "hca_query_tokens_per_s": round(h.B / (t_hca_us * 1e-6), 1),
+            "csa_layer_us": round(t_csa_us, 2),
+            "hca_layer_us": round(t_hca_us, 2),
+        },
+        "kernels": kernels,
+        "roofline": roofline,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (float64 oracle)")
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+/*
+ * v4attn.h -- C ABI of libv4attn.so: DeepSeek-V4 hybrid compressed attention
+ * (CSA + HCA) on AMD Instinct MI355X (gfx950).
+ *
+ * The method (from the pages "DeepSeek-V4: Making a Million Tokens
+ * Affordable", section "Two ways to shrink attention, interleaved", and
+ * "DeepSeek-V4 Explained: Compressed Sparse Attention and 1M Context at 10%
+ * KV", section "The attention stack, and why it is two mechanisms"):
+ *   - the KV stream of every m consecutive tokens is pooled into one entry
+ *     with learned per-token weights and positional biases over an
+ *     overlapping 2m-token window (CSA m = 4, HCA m' = 128);
+ *   - CSA scores each query against all entries with a lightning indexer,
+ *     keeps the top-k, and runs shared-KV multi-query attention over them
+ *     plus a 128-token uncompressed window;
+ *   - HCA attends densely to every entry plus the same window;
+ *   - queries and entries get RMSNorm, RoPE acts on the last 64 dims, the
+ *     output is rotated back by RoPE at -t, and a per-head sink logit lets
+ *     the attention weights sum to less than one;
+ *   - entries are stored with BF16 rotary dims and FP8 for the rest.
+ *
+ * Conventions shared by every call
+ *   - Tensors are caller-owned, contiguous DEVICE buffers (16-byte aligned),
+ *     row-major in the shapes given.  bf16 values are passed as uint16_t bit
+ *     patterns.  The library never allocates, frees or synchronises, and
+ *     keeps no state between calls; calls are thread-safe.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     and the call returns before the GPU finishes.  Device-side faults
+ *     surface at the caller's next synchronisation.
+ *   - Return value: V4ATTN_OK, or a negative status; on error nothing is
+ *     launched and v4attn_last_error() describes the problem.
+ *   - Positions are absolute token positions (int64).  A batch shares them:
+ *     every sequence of the batch has the same length.
+ *   - Packed row: (D - R) bytes of OCP FP8 E4M3FN (dims 0..D-R-1), then R
+ *     little-endian bf16 (dims D-R..D-1): D + R bytes (576 at D = 512).
+ *   - RoPE: adjacent pairs (D-R+2i, D-R+2i+1) rotate by p * base^(-2i/R).
+ *   - Supported sizes: D in {128, 256, 512}, R = 64, 1 <= H <= 64,
+ *     1 <= HI <= 64, dI in {32, 64, 128}, 1 <= m <= 256, 1 <= k <= 4096,
+ *     0 <= W <= 4096.  Others return V4ATTN_EUNSUPPORTED.
+ */
+#ifndef V4ATTN_H
+#define V4ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define V4ATTN_OK            0
+#define V4ATTN_EINVAL       (-1) /* bad pointer, shape or position          */
+#define V4ATTN_EUNSUPPORTED (-2) /* valid but not built (e.g. R != 64)      */
+#define V4ATTN_EWORKSPACE   (-3) /* workspace missing or too small          */
+#define V4ATTN_EHIP         (-4) /* HIP runtime error (no device, launch)   */
+
+/* v4attn_compress modes. */
+#define V4ATTN_POOL 0 /* pool 2m-token windows into compressed entries     */
+#define V4ATTN_PACK 1 /* one window row per raw token (no pooling)          */
+
+/* Library version, (major << 16) | minor. */
+int v4attn_version(void);
+
+/* Static description of a status code. */
+const char* v4attn_status_string(int status);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* v4attn_last_error(void);
+
+/*
+ * v4attn_compress -- sequence compression and window-row packing.
+ *
+ * Defines: per-token compression weights with positional biases over an
+ * overlapping 2m-token window, one entry per m tokens ("Two ways to shrink
+ * attention, interleaved"); the extra RMSNorm on entries and RoPE on their
+ * last R dims (same section); BF16-rotary / FP8-rest storage ("The attention
+ * stack, and why it is two mechanisms").
+ *
+ *   raw       bf16 [B, L, D]  raw latent c_t; row r is position raw_pos0 + r
+ *   tok_score f32  [B, L]     per-token score s_t          (POOL only)
+ *   pos_bias  f32  [2m]       positional bias b_0..b_2m-1  (POOL only)
+ *   gamma     f32  [D]        RMSNorm gain
+ *   mode      V4ATTN_POOL or V4ATTN_PACK
+ *   m         compression ratio (POOL only; ignored by PACK)
+ *   entry0, n_out
+ *             POOL: entries j = entry0 .. entry0+n_out-1 are written.  Entry
+ *             j pools positions [(j-1)m, (j+1)m) that exist (>= 0) with
+ *             weights softmax(s_t + b_{t-(j-1)m}); every such position must
+ *             lie in [raw_pos0, raw_pos0 + L), else V4ATTN_EINVAL.  Then
+ *             RMSNorm(gamma, eps), RoPE at position j*m, pack.
+ *             PACK: n_out rows are written, raw rows 0..n_out-1
+ *             (n_out <= L), each RMSNorm'd, rotated at its own position and
+ *             packed; entry0 is ignored.
+ *   out       u8 [B, out_rows, D+R]: output i of sequence b goes to row
+ *             b*out_rows + i (i = j - entry0 for POOL).  n_out <= out_rows.
+ * FP8 values are rounded to nearest-even after clamping to +-448.
+ */
+int v4attn_compress(const uint16_t* raw, const float* tok_score,
+                    const float* pos_bias, const float* gamma,
+                    int B, int L, int D, int R, int64_t raw_pos0,
+                    int mode, int m, int64_t entry0, int n_out,
+                    float eps, float rope_base,
+                    uint8_t* out, int64_t out_rows, void* stream);
+
+/*
+ * v4attn_index_topk -- lightning-indexer scores and top-k selection.
+ *
+ * Defines: a lightweight indexer scores each query against every compressed
+ * entry and a top-k selector keeps the best k (k = 1024 in V4-Pro) ("Two
+ * ways to shrink attention, interleaved"; "DeepSeek-V4, explained", steps 3
+ * and 4 of how one query's layer works).  The score form is the ReLU-weighted
+ * head sum score_{t,j} = sum_h w_{t,h} ReLU(q_{t,h} . k_j) with ONE indexer
+ * key per entry shared by all heads, accumulated in fp32 from bf16 inputs.
+ *
+ *   q_idx  bf16 [B, Tq, HI, dI]   indexer queries; query r is at q_pos0 + r
+ *   w_idx  f32  [B, Tq, HI]       per-query head weights
+ *   k_idx  bf16 [B, Ncap, dI]     indexer keys, entry j at row j
+ *   n_entries  entries that exist (<= Ncap)
+ *   m          compression ratio: query at t sees j < V_t =
+ *              min(n_entries, floor((t+1)/m))
+ *   topk   i32  [B, Tq, k] out    the min(k, V_t) best entries under
+ *              (score descending, index ascending) -- ties go to the lower
+ *              entry index -- written in ascending index order, then -1.
+ *   topk_score f32 [B, Tq, k] out, nullable: their scores (-inf for -1).
+ *   ws / ws_bytes  device workspace of at least
+ *              v4attn_index_topk_workspace(...) bytes; contents on entry
+ *              are ignored.
+ * NaN scores are never selected.
+ */
+size_t v4attn_index_topk_workspace(int B, int Tq, int64_t n_entries,
+                                   int64_t q_pos0, int m, int k);
+int v4attn_index_topk(const uint16_t* q_idx, const float* w_idx,
+                      const uint16_t* k_idx, int B, int Tq, int HI, int dI,
+                      int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m,
+                      int k, int32_t* topk, float* topk_score,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * v4attn_index_score / v4attn_topk_select -- the two halves of
+ * v4attn_index_topk, for callers that want the raw indexer scores (same
+ * definitions as above).
+ *
+ * v4attn_index_score writes scores f32 [B*Tq, score_stride]: row b*Tq + r
+ * holds score_{t,j} for j < V_t (t = q_pos0 + r); the rest of the row is not
+ * written.  score_stride >= min(n_entries, floor((q_pos0+Tq)/m)).
+ *
+ * v4attn_topk_select reads such a score buffer and writes topk (and
+ * topk_score, nullable) exactly as v4attn_index_topk does; its workspace is
+ * at least v4attn_topk_select_workspace(...) bytes (0 is possible: then ws
+ * may be NULL).
+ */
+int v4attn_index_score(const uint16_t* q_idx, const float* w_idx,
+                       const uint16_t* k_idx, int B, int Tq, int HI, int dI,
+                       int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m,
+                       float* scores, int64_t score_stride, void* stream);
+size_t v4attn_topk_select_workspace(int B, int Tq, int64_t n_entries,
+                                    int64_t q_pos0, int m, int k);
+int v4attn_topk_select(const float* scores, int64_t score_stride, int B,
+                       int Tq, int64_t n_entries, int64_t q_pos0, int m, int k,
+                       int32_t* topk, float* topk_score, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * v4attn_csa_attend -- CSA core attention: shared-KV multi-query attention
+ * over the selected entries plus the uncompressed window, with sink.
+ *
+ * Defines: attention runs over the selected positions only ("DeepSeek-V4,
+ * explained", step 5); a sliding-window branch of uncompressed recent tokens
+ * and a per-head attention sink ("The attention stack, and why it is two
+ * mechanisms"); RMSNorm on queries, RoPE on the last 64 dims, an entry is
+ * key and value, RoPE at -t on the output ("Two ways to shrink attention,
+ * interleaved").  Window and selected rows share ONE softmax with the sink:
+ *   q~  = RoPE_t(RMSNorm_gamma_q(q)),  l_x = scale * q~ . x,
+ *   p_x = exp(l_x) / (exp(sink_h) + sum_y exp(l_y)),
+ *   out = RoPE_{-t}(sum_x p_x x),      lse = log(exp(sink_h) + sum exp(l)).
+ *
+ *   q       bf16 [B, Tq, H, D]      query r at position t = q_pos0 + r
+ *   entries u8   [B, Ncap, D+R]     packed compressed entries
+ *   topk    i32  [B, Tq, k]         entry indices; values outside
+ *                                   [0, Ncap) (e.g. -1) are skipped
+ *   win     u8   [B, Tq+W-1, D+R]   packed window rows; row r is position
+ *                                   q_pos0-(W-1)+r.  The query at t uses
+ *                                   positions max(0, t-W+1)..t.
+ *   gamma_q f32 [D];  sink f32 [H]
+ *   out     bf16 [B, Tq, H, D] out;  lse f32 [B, Tq, H] out, nullable
+ *   ws / ws_bytes  >= v4attn_csa_attend_workspace(...) bytes
+ * Accumulation is fp32; q~ and the probabilities enter the matrix cores as
+ * bf16, FP8 rows are widened exactly to bf16.
+ */
+size_t v4attn_csa_attend_workspace(int B, int Tq, int H, int D, int k, int W);
+int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries,
+                      const int32_t* topk, const uint8_t* win,
+                      const float* gamma_q, const float* sink,
+                      int B, int Tq, int H, int D, int R, int64_t Ncap,
+                      int k, int W, int64_t q_pos0, float scale, float eps,
+                      float rope_base, uint16_t* out, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * v4attn_hca_attend -- HCA core attention: dense attention over every
+ * visible compressed entry plus the same window and sink.
+ *
+ * Defines: heavy compression (m' = 128) with fully dense attention over the
+ * result plus the same sliding-window branch ("Two ways to shrink
+ * attention, interleaved"; "DeepSeek-V4" visual-learn notes, "A coarse
+ * overview alongside local detail").  As v4attn_csa_attend, except that the
+ * query at t attends to every entry j < min(n_entries, floor((t+1)/m)).
+ *
+ *   entries u8 [B, Ncap, D+R]; n_entries <= Ncap
+ */
+size_t v4attn_hca_attend_workspace(int B, int Tq, int H, int D,
+                                   int64_t n_entries, int m, int64_t q_pos0,
+                                   int W);
+int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries,
+                      const uint8_t* win, const float* gamma_q,
+                      const float* sink, int B, int Tq, int H, int D, int R,
+                      int64_t Ncap, int64_t n_entries, int m, int W,
+                      int64_t q_pos0, float scale, float eps, float rope_base,
+                      uint16_t* out, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* V4ATTN_H */

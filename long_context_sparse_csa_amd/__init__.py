@@ -2,9 +2,9 @@
 
 The compute runs in hand-written HIP kernels for gfx950 inside the C-ABI
 library `libv4attn.so` (declared in include/v4attn.h).  `ops` is the thin
-Python binding over it (argument marshalling only; it raises if the library
-is missing).  `configs` names the workloads and `synth` draws their seeded
-inputs.
+Python binding over it (argument marshalling only; it loads the library on
+first use and raises if it is missing).  `configs` names the workloads and
+`synth` draws their seeded inputs.
 """
 
 import os
@@ -12,11 +12,3 @@ import os
 PACKAGE_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PACKAGE_DIR, "libv4attn.so")
 
-
-def __getattr__(name):
-    # The binding loads the shared library lazily so that the pure-Python
-    # parts (configs, synth) import on machines without a GPU.
-    if name == "ops":
-        from . import ops
-        return ops
-    raise AttributeError(name)

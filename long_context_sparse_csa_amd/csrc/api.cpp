@@ -1,0 +1,373 @@
+// C ABI of libv4attn.so (declared in include/v4attn.h): argument validation,
+// workspace layout and kernel launches.  Every check runs before any HIP call,
+// so invalid calls return an error without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/v4attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_err.clear();
+    return V4ATTN_OK;
+  }
+  return fail(V4ATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxK = 4096;
+constexpr int kMaxW = 4096;
+
+int check_dr(int D, int R) {
+  if (R != 64) return fail(V4ATTN_EUNSUPPORTED, "R = %d: only R = 64 rotary dims are built", R);
+  if (D != 128 && D != 256 && D != 512)
+    return fail(V4ATTN_EUNSUPPORTED, "D = %d: only D in {128, 256, 512} is built", D);
+  return V4ATTN_OK;
+}
+
+int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// Largest visible-entry count over queries q_pos0 .. q_pos0+Tq-1.
+int64_t vmax_of(int Tq, int64_t n_entries, int64_t q_pos0, int m) {
+  if (Tq <= 0) return 0;
+  return min64(n_entries, (q_pos0 + Tq) / m);
+}
+
+struct TopkWs {
+  size_t cand_bytes, total;
+  v4::TopkPlan plan;
+};
+
+TopkWs topk_ws(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m, int k) {
+  TopkWs w;
+  const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
+  w.plan = v4::topk_plan(vmax, k);
+  const int64_t rows = (int64_t)B * Tq;
+  w.cand_bytes = (size_t)(rows * w.plan.cand_elems) * sizeof(unsigned);
+  w.cand_bytes = (w.cand_bytes + 255) / 256 * 256;
+  w.total = 4 * w.cand_bytes;  // two (key, index) buffers
+  return w;
+}
+
+struct IndexWs {
+  int64_t score_stride;
+  size_t scores_bytes, total;
+  TopkWs tk;
+};
+
+IndexWs index_ws(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m, int k) {
+  IndexWs w;
+  const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
+  w.score_stride = (vmax + 63) / 64 * 64;
+  const int64_t rows = (int64_t)B * Tq;
+  w.scores_bytes = (size_t)(rows * w.score_stride) * sizeof(float);
+  w.scores_bytes = (w.scores_bytes + 255) / 256 * 256;
+  w.tk = topk_ws(B, Tq, n_entries, q_pos0, m, k);
+  w.total = w.scores_bytes + w.tk.total;
+  return w;
+}
+
+size_t attend_ws(int B, int Tq, int H, int D, int64_t rows_max, int* splits) {
+  const int s = v4::attend_splits(B, Tq, rows_max);
+  if (splits) *splits = s;
+  if (s <= 1) return 0;
+  const int64_t q = (int64_t)B * Tq;
+  size_t o = (size_t)(q * s * H * D) * sizeof(float);
+  o = (o + 255) / 256 * 256;
+  return o + (size_t)(q * s * H * 2) * sizeof(float);
+}
+
+int check_attend_common(const uint16_t* q, const uint8_t* entries, const uint8_t* win,
+                        const float* gamma_q, const float* sink, int B, int Tq, int H, int D,
+                        int R, int64_t Ncap, int W, int64_t q_pos0, float scale, float eps,
+                        float rope_base, const uint16_t* out) {
+  if (!q || !gamma_q || !sink || !out) return fail(V4ATTN_EINVAL, "null q, gamma_q, sink or out");
+  if (B < 0 || Tq < 0) return fail(V4ATTN_EINVAL, "negative B or Tq");
+  if (int st = check_dr(D, R)) return st;
+  if (H < 1 || H > 64) return fail(V4ATTN_EUNSUPPORTED, "H = %d: 1 <= H <= 64 is built", H);
+  if (Ncap < 0) return fail(V4ATTN_EINVAL, "negative Ncap");
+  if (W < 0 || W > kMaxW) return fail(V4ATTN_EUNSUPPORTED, "W = %d: 0 <= W <= %d", W, kMaxW);
+  if (q_pos0 < 0) return fail(V4ATTN_EINVAL, "negative q_pos0");
+  if (W > 0 && !win) return fail(V4ATTN_EINVAL, "null window buffer with W > 0");
+  if (Ncap > 0 && !entries) return fail(V4ATTN_EINVAL, "null entries with Ncap > 0");
+  if (!std::isfinite(scale) || !(eps >= 0.f) || !std::isfinite(eps) || !(rope_base > 0.f))
+    return fail(V4ATTN_EINVAL, "bad scale, eps or rope_base");
+  if (!aligned16(q) || !aligned16(entries) || !aligned16(win) || !aligned16(out))
+    return fail(V4ATTN_EINVAL, "q, entries, win and out must be 16-byte aligned");
+  return V4ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int v4attn_version(void) { return (0 << 16) | 1; }
+
+const char* v4attn_status_string(int status) {
+  switch (status) {
+    case V4ATTN_OK: return "ok";
+    case V4ATTN_EINVAL: return "invalid argument";
+    case V4ATTN_EUNSUPPORTED: return "unsupported size";
+    case V4ATTN_EWORKSPACE: return "workspace missing or too small";
+    case V4ATTN_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* v4attn_last_error(void) { return g_err.c_str(); }
+
+int v4attn_compress(const uint16_t* raw, const float* tok_score, const float* pos_bias,
+                    const float* gamma, int B, int L, int D, int R, int64_t raw_pos0, int mode,
+                    int m, int64_t entry0, int n_out, float eps, float rope_base, uint8_t* out,
+                    int64_t out_rows, void* stream) {
+  if (!raw || !gamma || !out) return fail(V4ATTN_EINVAL, "null raw, gamma or out");
+  if (B < 0 || L < 0 || n_out < 0 || out_rows < 0)
+    return fail(V4ATTN_EINVAL, "negative B, L, n_out or out_rows");
+  if (int st = check_dr(D, R)) return st;
+  if (mode != V4ATTN_POOL && mode != V4ATTN_PACK) return fail(V4ATTN_EINVAL, "bad mode %d", mode);
+  if (n_out > out_rows) return fail(V4ATTN_EINVAL, "n_out %d > out_rows %lld", n_out, (long long)out_rows);
+  if (!(eps >= 0.f) || !std::isfinite(eps) || !(rope_base > 0.f))
+    return fail(V4ATTN_EINVAL, "bad eps or rope_base");
+  if (!aligned16(raw) || !aligned16(out)) return fail(V4ATTN_EINVAL, "raw and out must be 16-byte aligned");
+  if (mode == V4ATTN_POOL) {
+    if (!tok_score || !pos_bias) return fail(V4ATTN_EINVAL, "POOL needs tok_score and pos_bias");
+    if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
+    if (entry0 < 0) return fail(V4ATTN_EINVAL, "negative entry0");
+    if (n_out > 0) {
+      const int64_t lo = (entry0 - 1) * (int64_t)m;
+      const int64_t first = lo > 0 ? lo : 0;
+      const int64_t last = (entry0 + n_out) * (int64_t)m;  // exclusive end of the last window
+      if (first < raw_pos0 || last > raw_pos0 + L)
+        return fail(V4ATTN_EINVAL,
+                    "entries %lld..%lld need positions [%lld, %lld) but rows hold [%lld, %lld)",
+                    (long long)entry0, (long long)(entry0 + n_out - 1), (long long)first,
+                    (long long)last, (long long)raw_pos0, (long long)(raw_pos0 + L));
+    }
+  } else {
+    if (n_out > L) return fail(V4ATTN_EINVAL, "PACK n_out %d > L %d", n_out, L);
+  }
+  v4::CompressArgs a{raw, tok_score, pos_bias, gamma, B, L, D, R, raw_pos0, mode, m, entry0,
+                     n_out, eps, rope_base, out, out_rows};
+  return hip_status(v4::launch_compress(a, (hipStream_t)stream), "compress launch");
+}
+
+size_t v4attn_index_topk_workspace(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m,
+                                   int k) {
+  if (B < 0 || Tq < 0 || n_entries < 0 || q_pos0 < 0 || m < 1 || k < 1) return 0;
+  return index_ws(B, Tq, n_entries, q_pos0, m, k).total;
+}
+
+size_t v4attn_topk_select_workspace(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m,
+                                    int k) {
+  if (B < 0 || Tq < 0 || n_entries < 0 || q_pos0 < 0 || m < 1 || k < 1) return 0;
+  return topk_ws(B, Tq, n_entries, q_pos0, m, k).total;
+}
+
+namespace {
+
+int check_index_common(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m) {
+  if (B < 0 || Tq < 0) return fail(V4ATTN_EINVAL, "negative B or Tq");
+  if (n_entries < 0) return fail(V4ATTN_EINVAL, "negative n_entries");
+  if (n_entries >= (int64_t)1 << 31) return fail(V4ATTN_EUNSUPPORTED, "n_entries >= 2^31");
+  if (q_pos0 < 0) return fail(V4ATTN_EINVAL, "negative q_pos0");
+  if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
+  return V4ATTN_OK;
+}
+
+int check_score_args(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx, int B,
+                     int Tq, int HI, int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0,
+                     int m) {
+  if (!q_idx || !w_idx) return fail(V4ATTN_EINVAL, "null q_idx or w_idx");
+  if (int st = check_index_common(B, Tq, n_entries, q_pos0, m)) return st;
+  if (HI < 1 || HI > 64) return fail(V4ATTN_EUNSUPPORTED, "HI = %d: 1 <= HI <= 64 is built", HI);
+  if (dI != 32 && dI != 64 && dI != 128)
+    return fail(V4ATTN_EUNSUPPORTED, "dI = %d: dI in {32, 64, 128} is built", dI);
+  if (Ncap < 0 || n_entries > Ncap) return fail(V4ATTN_EINVAL, "need 0 <= n_entries <= Ncap");
+  if (n_entries > 0 && !k_idx) return fail(V4ATTN_EINVAL, "null k_idx");
+  if (!aligned16(q_idx) || !aligned16(k_idx))
+    return fail(V4ATTN_EINVAL, "q_idx and k_idx must be 16-byte aligned");
+  return V4ATTN_OK;
+}
+
+hipError_t run_score(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx, int B,
+                     int Tq, int HI, int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0,
+                     int m, float* scores, int64_t stride, hipStream_t st) {
+  v4::IndexScoreArgs ia{q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m,
+                        vmax_of(Tq, n_entries, q_pos0, m), scores, stride};
+  return v4::launch_index_score(ia, st);
+}
+
+hipError_t run_topk(const float* scores, int64_t stride, int B, int Tq, int64_t n_entries,
+                    int64_t q_pos0, int m, int k, int32_t* topk, float* topk_score, void* ws,
+                    const TopkWs& w, hipStream_t st) {
+  uint8_t* cb = static_cast<uint8_t*>(ws);
+  v4::TopkArgs ta;
+  ta.scores = scores;
+  ta.score_stride = stride;
+  ta.B = B;
+  ta.Tq = Tq;
+  ta.n_entries = n_entries;
+  ta.q_pos0 = q_pos0;
+  ta.m = m;
+  ta.k = k;
+  ta.vmax = vmax_of(Tq, n_entries, q_pos0, m);
+  ta.cand_key[0] = reinterpret_cast<unsigned*>(cb);
+  ta.cand_idx[0] = reinterpret_cast<int*>(cb + w.cand_bytes);
+  ta.cand_key[1] = reinterpret_cast<unsigned*>(cb + 2 * w.cand_bytes);
+  ta.cand_idx[1] = reinterpret_cast<int*>(cb + 3 * w.cand_bytes);
+  ta.topk = topk;
+  ta.topk_score = topk_score;
+  return v4::launch_topk(ta, w.plan, st);
+}
+
+}  // namespace
+
+int v4attn_index_score(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx, int B,
+                       int Tq, int HI, int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0,
+                       int m, float* scores, int64_t score_stride, void* stream) {
+  if (int st = check_score_args(q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m))
+    return st;
+  const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
+  if (vmax > 0 && (!scores || score_stride < vmax))
+    return fail(V4ATTN_EINVAL, "scores missing or score_stride %lld < %lld",
+                (long long)score_stride, (long long)vmax);
+  return hip_status(run_score(q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m,
+                              scores, score_stride, (hipStream_t)stream),
+                    "index score launch");
+}
+
+int v4attn_topk_select(const float* scores, int64_t score_stride, int B, int Tq,
+                       int64_t n_entries, int64_t q_pos0, int m, int k, int32_t* topk,
+                       float* topk_score, void* ws, size_t ws_bytes, void* stream) {
+  if (!topk) return fail(V4ATTN_EINVAL, "null topk");
+  if (int st = check_index_common(B, Tq, n_entries, q_pos0, m)) return st;
+  if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
+  const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
+  if (vmax > 0 && (!scores || score_stride < vmax))
+    return fail(V4ATTN_EINVAL, "scores missing or score_stride %lld < %lld",
+                (long long)score_stride, (long long)vmax);
+  const TopkWs w = topk_ws(B, Tq, n_entries, q_pos0, m, k);
+  if (w.total > 0 && (!ws || ws_bytes < w.total))
+    return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
+  if ((int64_t)B * Tq == 0) return hip_status(hipSuccess, "");
+  return hip_status(run_topk(scores, score_stride, B, Tq, n_entries, q_pos0, m, k, topk,
+                             topk_score, ws, w, (hipStream_t)stream),
+                    "top-k launch");
+}
+
+int v4attn_index_topk(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx, int B,
+                      int Tq, int HI, int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0,
+                      int m, int k, int32_t* topk, float* topk_score, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (int st = check_score_args(q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m))
+    return st;
+  if (!topk) return fail(V4ATTN_EINVAL, "null topk");
+  if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
+  const IndexWs w = index_ws(B, Tq, n_entries, q_pos0, m, k);
+  if (w.total > 0 && (!ws || ws_bytes < w.total))
+    return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
+  if ((int64_t)B * Tq == 0) return hip_status(hipSuccess, "");
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* scores = reinterpret_cast<float*>(base);
+  hipError_t e = run_score(q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m,
+                           scores, w.score_stride, st);
+  if (e != hipSuccess) return hip_status(e, "index score launch");
+  return hip_status(run_topk(scores, w.score_stride, B, Tq, n_entries, q_pos0, m, k, topk,
+                             topk_score, base + w.scores_bytes, w.tk, st),
+                    "top-k launch");
+}
+
+size_t v4attn_csa_attend_workspace(int B, int Tq, int H, int D, int k, int W) {
+  if (B < 0 || Tq < 0 || H < 1 || D < 1 || k < 1 || W < 0) return 0;
+  return attend_ws(B, Tq, H, D, (int64_t)k + W, nullptr);
+}
+
+int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
+                      const uint8_t* win, const float* gamma_q, const float* sink, int B, int Tq,
+                      int H, int D, int R, int64_t Ncap, int k, int W, int64_t q_pos0,
+                      float scale, float eps, float rope_base, uint16_t* out, float* lse,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_attend_common(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, W,
+                                   q_pos0, scale, eps, rope_base, out))
+    return st;
+  if (!topk) return fail(V4ATTN_EINVAL, "null topk");
+  if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
+  int splits = 1;
+  const size_t need = attend_ws(B, Tq, H, D, (int64_t)k + W, &splits);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
+  v4::AttendArgs a{};
+  a.q = q; a.entries = entries; a.topk = topk; a.win = win; a.gamma_q = gamma_q; a.sink = sink;
+  a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R; a.Ncap = Ncap; a.k = k; a.n_entries = 0;
+  a.m = 1; a.W = W; a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps; a.rope_base = rope_base;
+  a.out = out; a.lse = lse; a.splits = splits;
+  a.part_o = static_cast<float*>(ws);
+  const int64_t q_rows = (int64_t)B * Tq;
+  size_t o_bytes = (size_t)(q_rows * splits * H * D) * sizeof(float);
+  o_bytes = (o_bytes + 255) / 256 * 256;
+  a.part_ml = splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + o_bytes) : nullptr;
+  a.rows_max = (int64_t)k + W;
+  return hip_status(v4::launch_attend(a, (hipStream_t)stream), "CSA attend launch");
+}
+
+size_t v4attn_hca_attend_workspace(int B, int Tq, int H, int D, int64_t n_entries, int m,
+                                   int64_t q_pos0, int W) {
+  if (B < 0 || Tq < 0 || H < 1 || D < 1 || n_entries < 0 || m < 1 || q_pos0 < 0 || W < 0) return 0;
+  return attend_ws(B, Tq, H, D, vmax_of(Tq, n_entries, q_pos0, m) + W, nullptr);
+}
+
+int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* win,
+                      const float* gamma_q, const float* sink, int B, int Tq, int H, int D, int R,
+                      int64_t Ncap, int64_t n_entries, int m, int W, int64_t q_pos0, float scale,
+                      float eps, float rope_base, uint16_t* out, float* lse, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (int st = check_attend_common(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, W,
+                                   q_pos0, scale, eps, rope_base, out))
+    return st;
+  if (n_entries < 0 || n_entries > Ncap) return fail(V4ATTN_EINVAL, "need 0 <= n_entries <= Ncap");
+  if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
+  const int64_t rows_max = vmax_of(Tq, n_entries, q_pos0, m) + W;
+  int splits = 1;
+  const size_t need = attend_ws(B, Tq, H, D, rows_max, &splits);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
+  v4::AttendArgs a{};
+  a.q = q; a.entries = entries; a.topk = nullptr; a.win = win; a.gamma_q = gamma_q; a.sink = sink;
+  a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R; a.Ncap = Ncap; a.k = 0; a.n_entries = n_entries;
+  a.m = m; a.W = W; a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps; a.rope_base = rope_base;
+  a.out = out; a.lse = lse; a.splits = splits;
+  a.part_o = static_cast<float*>(ws);
+  const int64_t q_rows = (int64_t)B * Tq;
+  size_t o_bytes = (size_t)(q_rows * splits * H * D) * sizeof(float);
+  o_bytes = (o_bytes + 255) / 256 * 256;
+  a.part_ml = splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + o_bytes) : nullptr;
+  a.rows_max = rows_max;
+  return hip_status(v4::launch_attend(a, (hipStream_t)stream), "HCA attend launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,221 @@
+// Sequence compression: overlapping 2m-window softmax pooling of raw latents
+// into compressed entries, and per-token packing of window rows.
+//
+// Pages: "DeepSeek-V4: Making a Million Tokens Affordable", section "Two ways
+// to shrink attention, interleaved" (per-token compression weights and
+// positional biases over 2m source tokens, one entry per m tokens; RMSNorm on
+// entries; RoPE on the last 64 dims), and "DeepSeek-V4 Explained: Compressed
+// Sparse Attention and 1M Context at 10% KV", section "The attention stack,
+// and why it is two mechanisms" (BF16 rotary dims, FP8 for the rest).
+//
+// Design: HBM-bound and tiny next to the attention reads (one entry per m
+// decoded tokens).  One 256-thread workgroup per entry: the 2m weights are
+// formed once per window in LDS, each of the 4 waves pools a quarter of the
+// window rows with every lane owning D/64 contiguous channels (coalesced
+// 16-byte loads at D = 512), the four partial sums meet in LDS and wave 0
+// normalises, rotates and packs the 576-byte row.  Each entry depends only on
+// its own window, so streaming (one entry per call) and batch calls produce
+// identical bytes.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace v4 {
+
+template <int VPL>
+__device__ __forceinline__ void load_bf16_row(const uint16_t* p, float (&x)[VPL]) {
+  if constexpr (VPL == 8) {
+    u32x4 w = *reinterpret_cast<const u32x4*>(p);
+    unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(ws[i] & 0xFFFFu);
+      x[2 * i + 1] = bf16_bits_to_f32(ws[i] >> 16);
+    }
+  } else if constexpr (VPL == 4) {
+    u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    x[0] = bf16_bits_to_f32(w.x & 0xFFFFu);
+    x[1] = bf16_bits_to_f32(w.x >> 16);
+    x[2] = bf16_bits_to_f32(w.y & 0xFFFFu);
+    x[3] = bf16_bits_to_f32(w.y >> 16);
+  } else {
+    unsigned w = *reinterpret_cast<const unsigned*>(p);
+    x[0] = bf16_bits_to_f32(w & 0xFFFFu);
+    x[1] = bf16_bits_to_f32(w >> 16);
+  }
+}
+
+// y holds this lane's VPL channels (lane*VPL ..) of an RMSNorm'd row.  Rotate
+// the channels that fall in the last R dims by position `pos` and store the
+// packed row: E4M3 for channels < D-R, bf16 for the rest.
+template <int VPL>
+__device__ __forceinline__ void rotate_and_pack(uint8_t* row, float (&y)[VPL], int lane, int R,
+                                                int64_t pos, float rope_base) {
+  constexpr int D = VPL * 64;
+  const int d0 = lane * VPL;
+  if (d0 >= D - R) {
+#pragma unroll
+    for (int v = 0; v < VPL; v += 2) {
+      float c, s;
+      rope_cos_sin(pos, (d0 + v - (D - R)) >> 1, R, rope_base, &c, &s);
+      float a = y[v], b = y[v + 1];
+      y[v] = a * c - b * s;
+      y[v + 1] = a * s + b * c;
+    }
+    uint8_t* dst = row + (D - R) + 2 * (d0 - (D - R));
+    if constexpr (VPL == 8) {
+      u32x4 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                 pack_bf16x2(y[6], y[7])};
+      *reinterpret_cast<u32x4*>(dst) = w;
+    } else if constexpr (VPL == 4) {
+      u32x2 w = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      *reinterpret_cast<u32x2*>(dst) = w;
+    } else {
+      *reinterpret_cast<unsigned*>(dst) = pack_bf16x2(y[0], y[1]);
+    }
+  } else {
+    uint8_t* dst = row + d0;
+    if constexpr (VPL == 8) {
+      u32x2 w = {pack_fp8x2(y[0], y[1]) | (pack_fp8x2(y[2], y[3]) << 16),
+                 pack_fp8x2(y[4], y[5]) | (pack_fp8x2(y[6], y[7]) << 16)};
+      *reinterpret_cast<u32x2*>(dst) = w;
+    } else if constexpr (VPL == 4) {
+      *reinterpret_cast<unsigned*>(dst) = pack_fp8x2(y[0], y[1]) | (pack_fp8x2(y[2], y[3]) << 16);
+    } else {
+      *reinterpret_cast<unsigned short*>(dst) = (unsigned short)pack_fp8x2(y[0], y[1]);
+    }
+  }
+}
+
+// RMSNorm of a row held as VPL channels per lane across one wave.
+template <int VPL>
+__device__ __forceinline__ void rmsnorm_wave(float (&y)[VPL], const float* __restrict__ gamma,
+                                             int lane, float eps) {
+  constexpr int D = VPL * 64;
+  float ss = 0.f;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) ss += y[v] * y[v];
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) y[v] = gamma[lane * VPL + v] * (y[v] * rs);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void compress_pool_kernel(
+    const uint16_t* __restrict__ raw, const float* __restrict__ score,
+    const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
+    int64_t raw_pos0, int m, int64_t entry0, float eps, float rope_base,
+    uint8_t* __restrict__ out, int64_t out_rows) {
+  constexpr int D = VPL * 64;
+  const int b = blockIdx.y;
+  const int64_t j = entry0 + blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float s_alpha[512];
+  __shared__ float s_part[4][D];
+  __shared__ float s_red[2][4];
+
+  const int64_t wlo = (j - 1) * (int64_t)m;  // window start; may be negative
+  const int64_t plo = wlo > 0 ? wlo : 0;       // first existing position
+  const int nw = (int)((j + 1) * (int64_t)m - plo);
+  const int64_t r0 = plo - raw_pos0;           // raw row of plo
+  const float* srow = score + (int64_t)b * L + r0;
+
+  // weights alpha_t = softmax over the window of (s_t + b_{t - wlo})
+  float mx = -INFINITY;
+  for (int t = tid; t < nw; t += 256) {
+    const float lg = srow[t] + bias[plo - wlo + t];
+    s_alpha[t] = lg;
+    mx = fmaxf(mx, lg);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) s_red[0][wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  float sum = 0.f;
+  for (int t = tid; t < nw; t += 256) {
+    const float e = expf(s_alpha[t] - mx);
+    s_alpha[t] = e;
+    sum += e;
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) s_red[1][wave] = sum;
+  __syncthreads();
+  const float inv = 1.0f / ((s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]));
+
+  // pooled = sum_t alpha_t c_t : wave w takes rows w, w+4, ...
+  float acc[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
+  const uint16_t* base = raw + ((int64_t)b * L + r0) * D + lane * VPL;
+  for (int t = wave; t < nw; t += 4) {
+    float x[VPL];
+    load_bf16_row<VPL>(base + (int64_t)t * D, x);
+    const float a = s_alpha[t];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, x[v], acc[v]);
+  }
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) s_part[wave][lane * VPL + v] = acc[v];
+  __syncthreads();
+  if (wave != 0) return;
+
+  float y[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int d = lane * VPL + v;
+    y[v] = ((s_part[0][d] + s_part[1][d]) + (s_part[2][d] + s_part[3][d])) * inv;
+  }
+  rmsnorm_wave<VPL>(y, gamma, lane, eps);
+  uint8_t* row = out + ((int64_t)b * out_rows + blockIdx.x) * (D + R);
+  rotate_and_pack<VPL>(row, y, lane, R, j * (int64_t)m, rope_base);
+}
+
+// One wave per raw row: RMSNorm, RoPE at the row's own position, pack.
+template <int VPL>
+__global__ __launch_bounds__(256) void compress_pack_kernel(
+    const uint16_t* __restrict__ raw, const float* __restrict__ gamma, int L, int R,
+    int64_t raw_pos0, int n_out, float eps, float rope_base, uint8_t* __restrict__ out,
+    int64_t out_rows) {
+  constexpr int D = VPL * 64;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n_out) return;
+  float y[VPL];
+  load_bf16_row<VPL>(raw + ((int64_t)b * L + r) * D + lane * VPL, y);
+  rmsnorm_wave<VPL>(y, gamma, lane, eps);
+  uint8_t* row = out + ((int64_t)b * out_rows + r) * (D + R);
+  rotate_and_pack<VPL>(row, y, lane, R, raw_pos0 + r, rope_base);
+}
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
+  if (a.n_out == 0 || a.B == 0) return hipSuccess;
+  if (a.mode == 0) {
+    dim3 grid(a.n_out, a.B);
+#define V4_POOL(VPL)                                                                       \
+  compress_pool_kernel<VPL><<<grid, 256, 0, st>>>(a.raw, a.tok_score, a.pos_bias, a.gamma,  \
+                                                  a.L, a.R, a.raw_pos0, a.m, a.entry0,     \
+                                                  a.eps, a.rope_base, a.out, a.out_rows)
+    switch (a.D) {
+      case 128: V4_POOL(2); break;
+      case 256: V4_POOL(4); break;
+      default: V4_POOL(8); break;
+    }
+#undef V4_POOL
+  } else {
+    dim3 grid((a.n_out + 3) / 4, a.B);
+#define V4_PACK(VPL)                                                                     \
+  compress_pack_kernel<VPL><<<grid, 256, 0, st>>>(a.raw, a.gamma, a.L, a.R, a.raw_pos0,   \
+                                                  a.n_out, a.eps, a.rope_base, a.out,     \
+                                                  a.out_rows)
+    switch (a.D) {
+      case 128: V4_PACK(2); break;
+      case 256: V4_PACK(4); break;
+      default: V4_PACK(8); break;
+    }
+#undef V4_PACK
+  }
+  return hipGetLastError();
+}
+
+}  // namespace v4

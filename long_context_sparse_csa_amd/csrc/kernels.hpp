@@ -1,0 +1,94 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the
+// kernels.  Arguments are validated by the caller before a launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace v4 {
+
+struct CompressArgs {
+  const uint16_t* raw;
+  const float* tok_score;
+  const float* pos_bias;
+  const float* gamma;
+  int B, L, D, R;
+  int64_t raw_pos0;
+  int mode, m;
+  int64_t entry0;
+  int n_out;
+  float eps, rope_base;
+  uint8_t* out;
+  int64_t out_rows;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
+
+// Lightning-indexer scoring into a dense fp32 score buffer.
+struct IndexScoreArgs {
+  const uint16_t* q_idx;  // [B, Tq, HI, dI]
+  const float* w_idx;     // [B, Tq, HI]
+  const uint16_t* k_idx;  // [B, Ncap, dI]
+  int B, Tq, HI, dI;
+  int64_t Ncap, n_entries, q_pos0;
+  int m;
+  int64_t vmax;           // max visible entries over the query block
+  float* scores;          // [B*Tq, score_stride]
+  int64_t score_stride;
+};
+hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t st);
+
+// Top-k selection: multi-stage reduction of per-part candidates.
+constexpr int kTopkPart = 16384;  // elements one workgroup selects from in LDS
+
+struct TopkPlan {
+  int stages;        // number of selection passes (>= 1)
+  int64_t parts0;    // parts of the first pass
+  int64_t cand_elems;  // elements of one candidate buffer (keys and indices)
+};
+TopkPlan topk_plan(int64_t vmax, int k);
+
+struct TopkArgs {
+  const float* scores;     // [B*Tq, score_stride]
+  int64_t score_stride;
+  int B, Tq;
+  int64_t n_entries, q_pos0;
+  int m, k;
+  int64_t vmax;
+  unsigned* cand_key[2];   // ping-pong candidate buffers
+  int* cand_idx[2];
+  int32_t* topk;           // [B*Tq, k]
+  float* topk_score;       // nullable
+};
+hipError_t launch_topk(const TopkArgs& a, const TopkPlan& plan, hipStream_t st);
+
+// Core attention (CSA when topk != nullptr, else HCA).
+struct AttendArgs {
+  const uint16_t* q;        // [B, Tq, H, D]
+  const uint8_t* entries;   // [B, Ncap, D+R]
+  const int32_t* topk;      // [B, Tq, k] or nullptr
+  const uint8_t* win;       // [B, Tq+W-1, D+R]
+  const float* gamma_q;
+  const float* sink;
+  int B, Tq, H, D, R;
+  int64_t Ncap;
+  int k;                    // CSA: top-k slots
+  int64_t n_entries;        // HCA: entries that exist
+  int m;                    // HCA: compression ratio
+  int W;
+  int64_t q_pos0;
+  float scale, eps, rope_base;
+  uint16_t* out;            // [B, Tq, H, D]
+  float* lse;               // [B, Tq, H] or nullptr
+  int splits;               // key-range splits per query (1 = no merge pass)
+  float* part_o;            // [B*Tq, splits, H, D]   (splits > 1)
+  float* part_ml;           // [B*Tq, splits, H, 2]  (max, sum)
+  int64_t rows_max;         // max rows (entries + window) over the block
+};
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+
+// Number of key-range splits the attention uses for a problem (shared by
+// the workspace query and the launch so both agree).
+int attend_splits(int B, int Tq, int64_t rows_max);
+
+}  // namespace v4

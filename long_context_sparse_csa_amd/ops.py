@@ -1,0 +1,312 @@
+"""Thin ctypes binding over libv4attn.so (include/v4attn.h).
+
+Argument marshalling only: shape/dtype checks, pointer and stream extraction,
+output and workspace allocation through torch.  Every step of the method runs
+in the library's HIP kernels; there is no fallback.  If the library is
+missing this module raises on first use.
+"""
+
+import ctypes
+import os
+import re
+
+import torch
+
+from . import LIB_PATH, PACKAGE_DIR
+
+V4ATTN_OK = 0
+V4ATTN_EINVAL = -1
+V4ATTN_EUNSUPPORTED = -2
+V4ATTN_EWORKSPACE = -3
+V4ATTN_EHIP = -4
+POOL = 0
+PACK = 1
+
+HEADER = os.path.join(os.path.dirname(PACKAGE_DIR), "include", "v4attn.h")
+
+_c = ctypes
+_P = _c.c_void_p
+_I = _c.c_int
+_L = _c.c_int64
+_F = _c.c_float
+_Z = _c.c_size_t
+
+_SIGS = {
+    "v4attn_version": (_I, []),
+    "v4attn_status_string": (_c.c_char_p, [_I]),
+    "v4attn_last_error": (_c.c_char_p, []),
+    "v4attn_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _I, _L, _I, _F, _F, _P, _L,
+                             _P]),
+    "v4attn_index_topk_workspace": (_Z, [_I, _I, _L, _L, _I, _I]),
+    "v4attn_index_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _I, _P, _P, _P, _Z,
+                               _P]),
+    "v4attn_index_score": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _P, _L, _P]),
+    "v4attn_topk_select_workspace": (_Z, [_I, _I, _L, _L, _I, _I]),
+    "v4attn_topk_select": (_I, [_P, _L, _I, _I, _L, _L, _I, _I, _P, _P, _P, _Z, _P]),
+    "v4attn_csa_attend_workspace": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "v4attn_csa_attend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _I, _I, _L, _F,
+                               _F, _F, _P, _P, _P, _Z, _P]),
+    "v4attn_hca_attend_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I]),
+    "v4attn_hca_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I, _L, _F,
+                               _F, _F, _P, _P, _P, _Z, _P]),
+}
+
+_lib = None
+
+
+class V4AttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"v4attn status {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m long_context_sparse_csa_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/v4attn.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(v4attn_\w+)\s*\(", text)))
+
+
+def check(status):
+    if status != V4ATTN_OK:
+        msg = lib().v4attn_last_error().decode()
+        raise V4AttnError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else _c.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return _c.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return ws
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws
+
+
+# ------------------------------------------------------------------ compress --
+
+def _row_ptr(out, row0, row_bytes):
+    if row0 < 0 or row0 > out.shape[1]:
+        raise ValueError("out_row0 out of range")
+    return _c.c_void_p(out.data_ptr() + row0 * row_bytes)
+
+
+def compress_pool(raw, tok_score, pos_bias, gamma, out, *, raw_pos0, m, entry0, n_out,
+                  out_row0=0, eps=1e-6, rope_base=10000.0, R=64):
+    """Pool 2m-token windows of raw bf16 latents [B, L, D] into packed entries
+    entry0..entry0+n_out-1, written to out[b, out_row0 + i] (uint8 [B, rows, D+R])."""
+    _need(raw, "raw", torch.bfloat16, 3)
+    _need(tok_score, "tok_score", torch.float32, 2)
+    _need(pos_bias, "pos_bias", torch.float32, 1)
+    _need(gamma, "gamma", torch.float32, 1)
+    _need(out, "out", torch.uint8, 3)
+    B, L, D = raw.shape
+    if tuple(tok_score.shape) != (B, L) or pos_bias.numel() != 2 * m or gamma.numel() != D \
+            or out.shape[0] != B or out.shape[2] != D + R or out_row0 + n_out > out.shape[1]:
+        raise ValueError("shape mismatch")
+    check(lib().v4attn_compress(_ptr(raw), _ptr(tok_score), _ptr(pos_bias), _ptr(gamma), B, L, D,
+                                R, int(raw_pos0), POOL, int(m), int(entry0), int(n_out),
+                                float(eps), float(rope_base), _row_ptr(out, out_row0, D + R),
+                                out.shape[1], _stream(raw)))
+    return out
+
+
+def compress_pack(raw, gamma, out, *, raw_pos0, n_out=None, out_row0=0, eps=1e-6,
+                  rope_base=10000.0, R=64):
+    """Pack raw rows 0..n_out-1 (positions raw_pos0..) as window rows, written
+    to out[b, out_row0 + i]."""
+    _need(raw, "raw", torch.bfloat16, 3)
+    _need(gamma, "gamma", torch.float32, 1)
+    _need(out, "out", torch.uint8, 3)
+    B, L, D = raw.shape
+    n_out = L if n_out is None else n_out
+    if gamma.numel() != D or out.shape[0] != B or out.shape[2] != D + R \
+            or out_row0 + n_out > out.shape[1]:
+        raise ValueError("shape mismatch")
+    check(lib().v4attn_compress(_ptr(raw), None, None, _ptr(gamma), B, L, D, R, int(raw_pos0),
+                                PACK, 1, 0, int(n_out), float(eps), float(rope_base),
+                                _row_ptr(out, out_row0, D + R), out.shape[1], _stream(raw)))
+    return out
+
+
+# ----------------------------------------------------------------- index/topk --
+
+def index_topk_workspace_bytes(B, Tq, n_entries, q_pos0, m, k):
+    return lib().v4attn_index_topk_workspace(B, Tq, n_entries, q_pos0, m, k)
+
+
+def index_topk(q_idx, w_idx, k_idx, *, n_entries, q_pos0, m, k, topk=None, topk_score=None,
+               want_scores=False, workspace=None):
+    """Top-k entry indices per query (int32 [B, Tq, k], ascending, -1 padded)."""
+    _need(q_idx, "q_idx", torch.bfloat16, 4)
+    _need(w_idx, "w_idx", torch.float32, 3)
+    _need(k_idx, "k_idx", torch.bfloat16, 3)
+    B, Tq, HI, dI = q_idx.shape
+    Ncap = k_idx.shape[1]
+    if tuple(w_idx.shape) != (B, Tq, HI) or k_idx.shape[0] != B or k_idx.shape[2] != dI:
+        raise ValueError("shape mismatch")
+    dev = q_idx.device
+    if topk is None:
+        topk = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
+    _need(topk, "topk", torch.int32, 3)
+    if want_scores and topk_score is None:
+        topk_score = torch.empty((B, Tq, k), dtype=torch.float32, device=dev)
+    nbytes = index_topk_workspace_bytes(B, Tq, n_entries, q_pos0, m, k)
+    workspace = _workspace(nbytes, dev, workspace)
+    check(lib().v4attn_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, Tq, HI, dI, Ncap,
+                                  int(n_entries), int(q_pos0), int(m), int(k), _ptr(topk),
+                                  _ptr(topk_score), _ptr(workspace), nbytes, _stream(q_idx)))
+    return topk, topk_score
+
+
+def score_stride(Tq, n_entries, q_pos0, m):
+    """Smallest score row length index_score accepts (rounded up to 64)."""
+    v = min(n_entries, (q_pos0 + Tq) // m) if Tq > 0 else 0
+    return (v + 63) // 64 * 64
+
+
+def index_score(q_idx, w_idx, k_idx, *, n_entries, q_pos0, m, scores=None):
+    """Indexer scores f32 [B*Tq, stride]; row b*Tq+r is valid for j < V_t."""
+    _need(q_idx, "q_idx", torch.bfloat16, 4)
+    _need(w_idx, "w_idx", torch.float32, 3)
+    _need(k_idx, "k_idx", torch.bfloat16, 3)
+    B, Tq, HI, dI = q_idx.shape
+    if tuple(w_idx.shape) != (B, Tq, HI) or k_idx.shape[0] != B or k_idx.shape[2] != dI:
+        raise ValueError("shape mismatch")
+    if scores is None:
+        scores = torch.empty((B * Tq, max(score_stride(Tq, n_entries, q_pos0, m), 1)),
+                             dtype=torch.float32, device=q_idx.device)
+    _need(scores, "scores", torch.float32, 2)
+    check(lib().v4attn_index_score(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, Tq, HI, dI,
+                                   k_idx.shape[1], int(n_entries), int(q_pos0), int(m),
+                                   _ptr(scores), scores.shape[1], _stream(q_idx)))
+    return scores
+
+
+def topk_select_workspace_bytes(B, Tq, n_entries, q_pos0, m, k):
+    return lib().v4attn_topk_select_workspace(B, Tq, n_entries, q_pos0, m, k)
+
+
+def topk_select(scores, *, B, Tq, n_entries, q_pos0, m, k, topk=None, topk_score=None,
+                want_scores=False, workspace=None):
+    """Top-k selection from an index_score buffer."""
+    _need(scores, "scores", torch.float32, 2)
+    dev = scores.device
+    if topk is None:
+        topk = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
+    _need(topk, "topk", torch.int32, 3)
+    if want_scores and topk_score is None:
+        topk_score = torch.empty((B, Tq, k), dtype=torch.float32, device=dev)
+    nbytes = topk_select_workspace_bytes(B, Tq, n_entries, q_pos0, m, k)
+    workspace = _workspace(nbytes, dev, workspace)
+    check(lib().v4attn_topk_select(_ptr(scores), scores.shape[1], B, Tq, int(n_entries),
+                                   int(q_pos0), int(m), int(k), _ptr(topk), _ptr(topk_score),
+                                   _ptr(workspace), nbytes, _stream(scores)))
+    return topk, topk_score
+
+
+# ------------------------------------------------------------------- attention --
+
+def _attend_io(q, out, lse, want_lse):
+    B, Tq, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 4)
+    if want_lse and lse is None:
+        lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def csa_attend_workspace_bytes(B, Tq, H, D, k, W):
+    return lib().v4attn_csa_attend_workspace(B, Tq, H, D, k, W)
+
+
+def hca_attend_workspace_bytes(B, Tq, H, D, n_entries, m, q_pos0, W):
+    return lib().v4attn_hca_attend_workspace(B, Tq, H, D, n_entries, m, q_pos0, W)
+
+
+def csa_attend(q, entries, topk, win, gamma_q, sink, *, q_pos0, W, scale=None, eps=1e-6,
+               rope_base=10000.0, R=64, out=None, lse=None, want_lse=False, workspace=None):
+    """Sparse shared-KV attention over the top-k entries plus the window."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(entries, "entries", torch.uint8, 3)
+    _need(topk, "topk", torch.int32, 3)
+    _need(win, "win", torch.uint8, 3)
+    _need(gamma_q, "gamma_q", torch.float32, 1)
+    _need(sink, "sink", torch.float32, 1)
+    B, Tq, H, D = q.shape
+    k = topk.shape[2]
+    if entries.shape[0] != B or entries.shape[2] != D + R or tuple(topk.shape[:2]) != (B, Tq) \
+            or tuple(win.shape) != (B, Tq + W - 1, D + R) or gamma_q.numel() != D \
+            or sink.numel() != H:
+        raise ValueError("shape mismatch")
+    scale = D ** -0.5 if scale is None else scale
+    out, lse = _attend_io(q, out, lse, want_lse)
+    nbytes = csa_attend_workspace_bytes(B, Tq, H, D, k, W)
+    workspace = _workspace(nbytes, q.device, workspace)
+    check(lib().v4attn_csa_attend(_ptr(q), _ptr(entries), _ptr(topk), _ptr(win), _ptr(gamma_q),
+                                  _ptr(sink), B, Tq, H, D, R, entries.shape[1], k, int(W),
+                                  int(q_pos0), float(scale), float(eps), float(rope_base),
+                                  _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(q)))
+    return out, lse
+
+
+def hca_attend(q, entries, win, gamma_q, sink, *, n_entries, m, q_pos0, W, scale=None,
+               eps=1e-6, rope_base=10000.0, R=64, out=None, lse=None, want_lse=False,
+               workspace=None):
+    """Dense shared-KV attention over every visible entry plus the window."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(entries, "entries", torch.uint8, 3)
+    _need(win, "win", torch.uint8, 3)
+    _need(gamma_q, "gamma_q", torch.float32, 1)
+    _need(sink, "sink", torch.float32, 1)
+    B, Tq, H, D = q.shape
+    if entries.shape[0] != B or entries.shape[2] != D + R \
+            or tuple(win.shape) != (B, Tq + W - 1, D + R) or gamma_q.numel() != D \
+            or sink.numel() != H:
+        raise ValueError("shape mismatch")
+    scale = D ** -0.5 if scale is None else scale
+    out, lse = _attend_io(q, out, lse, want_lse)
+    nbytes = hca_attend_workspace_bytes(B, Tq, H, D, n_entries, m, q_pos0, W)
+    workspace = _workspace(nbytes, q.device, workspace)
+    check(lib().v4attn_hca_attend(_ptr(q), _ptr(entries), _ptr(win), _ptr(gamma_q), _ptr(sink), B,
+                                  Tq, H, D, R, entries.shape[1], int(n_entries), int(m), int(W),
+                                  int(q_pos0), float(scale), float(eps), float(rope_base),
+                                  _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(q)))
+    return out, lse

@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and
+exports every function include/v4attn.h declares, workspace queries are pure
+host arithmetic, and invalid arguments return the documented status before
+any device call.  Every call below fails validation, so nothing is launched
+even on a machine with a GPU; the fake pointers are never dereferenced."""
+
+import ctypes
+
+import pytest
+
+from long_context_sparse_csa_amd import LIB_PATH
+import os
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH),
+                                reason="libv4attn.so not built (run __graft_entry__.build())")
+
+
+def L():
+    from long_context_sparse_csa_amd import ops
+    return ops.lib()
+
+
+def ops():
+    from long_context_sparse_csa_amd import ops as o
+    return o
+
+
+FAKE = ctypes.c_void_p(0x100000)     # aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+def test_exports_every_header_function():
+    names = ops().header_functions()
+    assert "v4attn_compress" in names and "v4attn_hca_attend" in names
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(L(), n), n
+    assert L().v4attn_version() == 1
+    assert L().v4attn_status_string(-3) == b"workspace missing or too small"
+
+
+def _compress(**kw):
+    a = dict(raw=FAKE, tok_score=FAKE, pos_bias=FAKE, gamma=FAKE, B=1, L=16, D=512, R=64,
+             raw_pos0=0, mode=0, m=4, entry0=0, n_out=4, eps=1e-6, base=1e4, out=FAKE,
+             out_rows=4, stream=None)
+    a.update(kw)
+    return L().v4attn_compress(a["raw"], a["tok_score"], a["pos_bias"], a["gamma"], a["B"],
+                               a["L"], a["D"], a["R"], a["raw_pos0"], a["mode"], a["m"],
+                               a["entry0"], a["n_out"], a["eps"], a["base"], a["out"],
+                               a["out_rows"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(raw=None), -1),
+    (dict(D=100), -2),
+    (dict(R=32), -2),
+    (dict(mode=7), -1),
+    (dict(m=0), -2),
+    (dict(m=300), -2),
+    (dict(n_out=5), -1),                  # n_out > out_rows
+    (dict(n_out=4, out_rows=4, L=15), -1),  # last window needs position 15
+    (dict(raw_pos0=1), -1),               # entry 0 needs position 0
+    (dict(entry0=-1), -1),
+    (dict(tok_score=None), -1),
+    (dict(raw=MISALIGNED), -1),
+    (dict(eps=-1.0), -1),
+    (dict(mode=1, n_out=17, out_rows=20), -1),   # PACK beyond L
+])
+def test_compress_rejects(kw, status):
+    assert _compress(**kw) == status
+    assert L().v4attn_last_error() != b""
+
+
+def _index(**kw):
+    a = dict(q=FAKE, w=FAKE, k=FAKE, B=2, Tq=1, HI=64, dI=128, Ncap=1000, n=1000, q_pos0=3999,
+             m=4, k_=64, topk=FAKE, ts=None, ws=FAKE, ws_bytes=0)
+    a.update(kw)
+    return L().v4attn_index_topk(a["q"], a["w"], a["k"], a["B"], a["Tq"], a["HI"], a["dI"],
+                                 a["Ncap"], a["n"], a["q_pos0"], a["m"], a["k_"], a["topk"],
+                                 a["ts"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1),
+    (dict(HI=65), -2),
+    (dict(dI=96), -2),
+    (dict(n=1001), -1),
+    (dict(k_=5000), -2),
+    (dict(m=0), -2),
+    (dict(q_pos0=-1), -1),
+    (dict(ws_bytes=10), -3),
+    (dict(ws=None, ws_bytes=1 << 40), -3),
+])
+def test_index_topk_rejects(kw, status):
+    assert _index(**kw) == status
+
+
+def test_workspace_sizes_are_host_arithmetic():
+    # 1M-token decode: 8 queries x 262144 fp32 scores plus two candidate buffers
+    n = L().v4attn_index_topk_workspace(8, 1, 262144, (1 << 20) - 1, 4, 1024)
+    assert n >= 8 * 262144 * 4
+    assert L().v4attn_index_topk_workspace(-1, 1, 10, 0, 4, 1) == 0
+    # tiny problems need no split partials
+    assert L().v4attn_csa_attend_workspace(4096, 1, 64, 512, 1024, 128) == 0
+    assert L().v4attn_hca_attend_workspace(32, 1, 64, 512, 8192, 128, (1 << 20) - 1, 128) > 0
+
+
+def _csa(**kw):
+    a = dict(q=FAKE, e=FAKE, t=FAKE, w=FAKE, g=FAKE, s=FAKE, B=1, Tq=1, H=64, D=512, R=64,
+             Ncap=100, k=64, W=128, q_pos0=500, scale=0.04, eps=1e-6, base=1e4, out=FAKE,
+             lse=None, ws=FAKE, ws_bytes=0)
+    a.update(kw)
+    return L().v4attn_csa_attend(a["q"], a["e"], a["t"], a["w"], a["g"], a["s"], a["B"], a["Tq"],
+                                 a["H"], a["D"], a["R"], a["Ncap"], a["k"], a["W"], a["q_pos0"],
+                                 a["scale"], a["eps"], a["base"], a["out"], a["lse"], a["ws"],
+                                 a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1),
+    (dict(t=None), -1),
+    (dict(H=0), -2),
+    (dict(H=65), -2),
+    (dict(D=384), -2),
+    (dict(k=0), -2),
+    (dict(W=5000), -2),
+    (dict(W=16, w=None), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(out=MISALIGNED), -1),
+    (dict(q_pos0=-5), -1),
+])
+def test_csa_attend_rejects(kw, status):
+    assert _csa(**kw) == status
+
+
+def test_hca_attend_rejects():
+    f = L().v4attn_hca_attend
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 512, 64, 10, 11, 128, 128, 5000, 0.04, 1e-6,
+            1e4, FAKE, None, FAKE, 0, None]
+    assert f(*args) == -1          # n_entries > Ncap
+    args[11] = 10
+    args[12] = 0
+    assert f(*args) == -2          # m = 0
+    args[12] = 128
+    args[21] = 0
+    # 32 sequences at 1M need split partials: workspace too small
+    args[5], args[10], args[11], args[14] = 32, 8192, 8192, (1 << 20) - 1
+    assert f(*args) == -3

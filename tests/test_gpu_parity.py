@@ -1,0 +1,374 @@
+"""GPU parity: every library call against the float64 oracle on the same
+seeded bytes, through the C ABI (ctypes binding).
+
+Bars: compressed rows within one ulp of the exact value (>= 99.9% of bytes
+identical to the oracle's rounding); top-k index sets bit-exact on
+integer-valued indexer inputs (ties to the lower index), near-tie tolerant
+on float inputs; attention outputs max-abs <= 2e-2 and rel-L2 <= 5e-3."""
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_csa_amd import synth
+from oracle import attend as oa
+from oracle import codecs
+from oracle import compress as oc
+from oracle import indexer as oi
+
+from helpers import (assert_attn_close, assert_rows_within_one_ulp, bf16_to_f64, err_stats,
+                     rows_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_sparse_csa_amd import ops
+    ops.lib()   # raises if the HIP library is missing
+    yield
+
+
+def ops():
+    from long_context_sparse_csa_amd import ops as o
+    return o
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ compress --
+
+def _compress_inputs(B, L, D, m, seed):
+    raw = synth.normal((B, L, D), seed, "raw", DEV, dtype=torch.bfloat16)
+    score = synth.normal((B, L), seed, "score", DEV)
+    bias = synth.normal((2 * m,), seed, "bias", DEV, std=0.1)
+    gamma = synth.normal((D,), seed, "gamma", DEV, mean=1.0, std=0.1)
+    return raw, score, bias, gamma
+
+
+@pytest.mark.parametrize("D,m,L", [(128, 4, 4096), (512, 4, 1024), (512, 128, 1024),
+                                   (256, 3, 301), (512, 1, 64)])
+def test_compress_pool_matches_oracle(D, m, L):
+    log(f"compress_pool D={D} m={m} L={L}")
+    B, R = 2, 64
+    raw, score, bias, gamma = _compress_inputs(B, L, D, m, 10 + D + m)
+    n = L // m
+    out = torch.zeros((B, n, D + R), dtype=torch.uint8, device=DEV)
+    ops().compress_pool(raw, score, bias, gamma, out, raw_pos0=0, m=m, entry0=0, n_out=n)
+    torch.cuda.synchronize()
+    c = bf16_to_f64(raw)
+    s, b, gm = score.cpu().double().numpy(), bias.cpu().double().numpy(), gamma.cpu().double().numpy()
+    for bb in range(B):
+        js, e = oc.compress_pool(c[bb], s[bb], 0, m, b, gm, 1e-6, R, 1e4)
+        assert list(js) == list(range(n))
+        assert_rows_within_one_ulp(out[bb].cpu().numpy(), e, D, R)
+
+
+def test_compress_pool_offset_positions_and_streaming():
+    """Entries of a block at positions P-m..P+L-1 (prefill-style), and one
+    entry per call (decode-style), give identical bytes."""
+    log("compress_pool streaming")
+    B, D, R, m = 2, 512, 64, 4
+    P = (1 << 20)
+    L = 4 * m + m
+    raw, score, bias, gamma = _compress_inputs(B, L, D, m, 77)
+    n = (L - m) // m                   # entries P/m .. P/m + n - 1
+    batch = torch.zeros((B, n, D + R), dtype=torch.uint8, device=DEV)
+    ops().compress_pool(raw, score, bias, gamma, batch, raw_pos0=P - m, m=m, entry0=P // m,
+                        n_out=n)
+    single = torch.zeros_like(batch)
+    for i in range(n):
+        j = P // m + i
+        r0 = (j - 1) * m - (P - m)
+        sub = raw[:, r0:r0 + 2 * m].contiguous()
+        tmp = torch.zeros((B, 1, D + R), dtype=torch.uint8, device=DEV)
+        ops().compress_pool(sub, score[:, r0:r0 + 2 * m].contiguous(), bias, gamma, tmp,
+                            raw_pos0=(j - 1) * m, m=m, entry0=j, n_out=1)
+        single[:, i] = tmp[:, 0]
+    torch.cuda.synchronize()
+    assert torch.equal(batch, single)
+    c = bf16_to_f64(raw)
+    for bb in range(B):
+        js, e = oc.compress_pool(c[bb], score[bb].cpu().double().numpy(), P - m, m,
+                                 bias.cpu().double().numpy(), gamma.cpu().double().numpy(), 1e-6,
+                                 R, 1e4, j0=P // m, n=n)
+        assert_rows_within_one_ulp(batch[bb].cpu().numpy(), e, D, R)
+
+
+@pytest.mark.parametrize("D", [128, 512])
+def test_compress_pack_matches_oracle(D):
+    log(f"compress_pack D={D}")
+    B, L, R = 3, 200, 64
+    raw, _, _, gamma = _compress_inputs(B, L, D, 4, 5 + D)
+    out = torch.zeros((B, L, D + R), dtype=torch.uint8, device=DEV)
+    pos0 = (1 << 20) - 150
+    ops().compress_pack(raw, gamma, out, raw_pos0=pos0)
+    torch.cuda.synchronize()
+    c = bf16_to_f64(raw)
+    for bb in range(B):
+        e = oc.compress_pack(c[bb], pos0, gamma.cpu().double().numpy(), 1e-6, R, 1e4)
+        assert_rows_within_one_ulp(out[bb].cpu().numpy(), e, D, R)
+
+
+def test_compress_rejects_missing_window_rows():
+    B, D, m = 1, 128, 4
+    raw, score, bias, gamma = _compress_inputs(B, 16, D, m, 3)
+    out = torch.zeros((B, 8, D + 64), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ops().V4AttnError) as ei:
+        # entry 4 needs positions 12..19 but the rows hold 0..15
+        ops().compress_pool(raw, score, bias, gamma, out, raw_pos0=0, m=m, entry0=0, n_out=5)
+    assert ei.value.status == ops().V4ATTN_EINVAL
+
+
+# ---------------------------------------------------------------- index/topk --
+
+def _indexer_inputs(B, Tq, HI, dI, Ncap, seed, integer):
+    if integer:
+        q = synth.integers((B, Tq, HI, dI), -3, 3, seed, "qI", DEV, torch.bfloat16)
+        w = synth.integers((B, Tq, HI), -3, 3, seed, "w", DEV, torch.float32)
+        k = synth.integers((B, Ncap, dI), -3, 3, seed, "kI", DEV, torch.bfloat16)
+    else:
+        q = synth.normal((B, Tq, HI, dI), seed, "qI", DEV, dtype=torch.bfloat16)
+        w = synth.normal((B, Tq, HI), seed, "w", DEV)
+        k = synth.normal((B, Ncap, dI), seed, "kI", DEV, dtype=torch.bfloat16)
+    return q, w, k
+
+
+INT_CASES = [
+    # B, Tq, HI, dI, Ncap, n_entries, q_pos0, m, k
+    (1, 1, 4, 32, 1024, 1024, 4095, 4, 64),        # tiny decode: 1024 entries, k=64
+    (2, 1, 64, 128, 40000, 40000, 159999, 4, 1024),  # three parts + a merge pass
+    (2, 1, 16, 64, 5000, 5000, 19999, 4, 1024),    # one part, V > k
+    (2, 1, 4, 32, 700, 700, 2799, 4, 1024),        # V < k: everything, then -1
+    (1, 37, 8, 32, 3000, 3000, 11800, 4, 256),     # causal block: V_t varies per query
+    (1, 3, 4, 32, 70000, 70000, 279999, 4, 16),    # five parts, tiny k, heavy ties
+    (1, 2, 4, 32, 100, 90, 4, 4, 8),               # V_t = 1 and 1: early positions
+]
+
+
+@pytest.mark.parametrize("case", INT_CASES)
+def test_index_topk_bit_exact_on_integer_inputs(case):
+    B, Tq, HI, dI, Ncap, n_ent, q_pos0, m, k = case
+    log(f"index_topk int {case}")
+    q, w, kk = _indexer_inputs(B, Tq, HI, dI, Ncap, sum(case) % 1000, True)
+    topk, ts = ops().index_topk(q, w, kk, n_entries=n_ent, q_pos0=q_pos0, m=m, k=k,
+                                want_scores=True)
+    torch.cuda.synchronize()
+    qn, wn, kn = bf16_to_f64(q), w.cpu().double().numpy(), bf16_to_f64(kk)
+    got, got_s = topk.cpu().numpy(), ts.cpu().numpy()
+    for b in range(B):
+        want, scores = oi.index_topk(qn[b], wn[b], kn[b], n_ent, q_pos0 + np.arange(Tq), m, k)
+        np.testing.assert_array_equal(got[b], want)
+        for r in range(Tq):
+            sel = want[r][want[r] >= 0]
+            np.testing.assert_array_equal(got_s[b, r, : len(sel)], scores[r][sel])
+            assert np.all(np.isneginf(got_s[b, r, len(sel):]))
+
+
+def test_index_topk_float_inputs_near_tie_tolerant():
+    B, Tq, HI, dI, N, k = 2, 2, 64, 128, 20000, 1024
+    log("index_topk float")
+    q, w, kk = _indexer_inputs(B, Tq, HI, dI, N, 42, False)
+    q_pos0 = 4 * N - 2
+    topk, ts = ops().index_topk(q, w, kk, n_entries=N, q_pos0=q_pos0, m=4, k=k, want_scores=True)
+    torch.cuda.synchronize()
+    qn, wn, kn = bf16_to_f64(q), w.cpu().double().numpy(), bf16_to_f64(kk)
+    got, got_s = topk.cpu().numpy(), ts.cpu().numpy()
+    for b in range(B):
+        for r in range(Tq):
+            V = oi.visible_entries(q_pos0 + r, N, 4)
+            sc = oi.index_scores(qn[b, r], wn[b, r], kn[b], V)
+            want = oi.topk_select(sc, k)
+            g = got[b, r]
+            assert np.all(np.diff(g[g >= 0]) > 0), "not ascending"
+            tau = np.sort(sc)[::-1][k - 1]
+            tol = 1e-4 * max(1.0, abs(tau)) + 1e-5 * np.abs(sc).max()
+            only_gpu = np.setdiff1d(g, want)
+            only_orc = np.setdiff1d(want, g)
+            assert np.all(sc[only_gpu] >= tau - tol)
+            assert np.all(sc[only_orc] <= tau + tol)
+            assert len(only_gpu) <= 0.01 * k
+            # scores of the selected entries: fp32 accumulation of bf16 products
+            np.testing.assert_allclose(got_s[b, r], sc[g], rtol=1e-5, atol=1e-5 * np.abs(sc).max())
+
+
+# ----------------------------------------------------------------- attention --
+
+def _attn_inputs(B, Tq, H, D, Ncap, W, seed, gamma_std=0.1):
+    R = 64
+    q = synth.normal((B, Tq, H, D), seed, "q", DEV, dtype=torch.bfloat16)
+    ent = synth.packed_rows((B, Ncap), D, R, seed, "entries", DEV)
+    win = synth.packed_rows((B, Tq + W - 1), D, R, seed, "win", DEV)
+    gq = synth.normal((D,), seed, "gamma_q", DEV, mean=1.0, std=gamma_std)
+    sink = synth.normal((H,), seed, "sink", DEV)
+    return q, ent, win, gq, sink
+
+
+def _random_topk(B, Tq, k, Ncap, seed, n_valid=None):
+    g = torch.Generator().manual_seed(seed)
+    t = torch.full((B, Tq, k), -1, dtype=torch.int32)
+    for b in range(B):
+        for r in range(Tq):
+            nv = k if n_valid is None else n_valid
+            sel = torch.randperm(Ncap, generator=g)[:nv].sort().values
+            t[b, r, :nv] = sel.to(torch.int32)
+    return t.to(DEV)
+
+
+def _oracle_csa(q, ent, topk, win, gq, sink, q_pos0, W, scale, D, R=64):
+    qn, en, wn = bf16_to_f64(q), rows_to_f64(ent, D, R), rows_to_f64(win, D, R)
+    tk = topk.cpu().numpy()
+    gqn, sk = gq.cpu().double().numpy(), sink.cpu().double().numpy()
+    outs, lses = [], []
+    for b in range(q.shape[0]):
+        o, l = oa.attend_csa(qn[b], en[b], tk[b], wn[b], gqn, sk, q_pos0, W, scale, 1e-6, R, 1e4)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+CSA_CASES = [
+    # B, Tq, H, D, Ncap, k, W, q_pos0, scale_mult, n_valid
+    (1, 1, 8, 128, 1024, 64, 128, 4095, 1.0, None),       # tiny decode shape
+    (2, 1, 64, 512, 4096, 1024, 128, (1 << 20) - 1, 1.0, None),
+    (2, 1, 64, 512, 4096, 1024, 128, (1 << 20) - 1, 4.0, 1000),  # peaked, -1 padding
+    (1, 9, 64, 512, 3000, 256, 128, 100, 1.0, None),      # block of queries, early window
+    (3, 1, 40, 256, 500, 100, 0, 5000, 2.0, 90),          # no window, H not a multiple of 16
+]
+
+
+@pytest.mark.parametrize("case", CSA_CASES)
+def test_csa_attend_matches_oracle(case):
+    B, Tq, H, D, Ncap, k, W, q_pos0, sm, nv = case
+    log(f"csa_attend {case}")
+    q, ent, win, gq, sink = _attn_inputs(B, Tq, H, D, Ncap, W, sum(case[:7]) % 997)
+    topk = _random_topk(B, Tq, k, Ncap, 3, nv)
+    scale = sm * D ** -0.5
+    out, lse = ops().csa_attend(q, ent, topk, win, gq, sink, q_pos0=q_pos0, W=W, scale=scale,
+                                want_lse=True)
+    torch.cuda.synchronize()
+    want, want_lse = _oracle_csa(q, ent, topk, win, gq, sink, q_pos0, W, scale, D)
+    ma, rl = assert_attn_close(bf16_to_f64(out), want, f"csa {case}", logit_mult=sm)
+    log(f"  max_abs {ma:.2e} rel_l2 {rl:.2e}")
+    np.testing.assert_allclose(lse.cpu().numpy(), want_lse, rtol=2e-3, atol=2e-3)
+
+
+HCA_CASES = [
+    # B, Tq, H, D, n_entries, m, W, q_pos0, scale_mult
+    (2, 1, 64, 512, 8192 // 8, 128, 128, (1 << 17) - 1, 1.0),
+    (1, 1, 8, 128, 300, 128, 128, 300 * 128 + 5, 4.0),
+    (1, 5, 64, 512, 40, 128, 128, 40 * 128 - 3, 1.0),     # causal: V_t changes in the block
+    (2, 1, 16, 512, 0, 128, 16, 100, 1.0),                # no entries yet: window only
+]
+
+
+@pytest.mark.parametrize("case", HCA_CASES)
+def test_hca_attend_matches_oracle(case):
+    B, Tq, H, D, n_ent, m, W, q_pos0, sm = case
+    log(f"hca_attend {case}")
+    Ncap = max(n_ent, 1)
+    q, ent, win, gq, sink = _attn_inputs(B, Tq, H, D, Ncap, W, sum(case[:7]) % 991)
+    scale = sm * D ** -0.5
+    out, lse = ops().hca_attend(q, ent, win, gq, sink, n_entries=n_ent, m=m, q_pos0=q_pos0, W=W,
+                                scale=scale, want_lse=True)
+    torch.cuda.synchronize()
+    qn, en, wn = bf16_to_f64(q), rows_to_f64(ent, D, 64), rows_to_f64(win, D, 64)
+    for b in range(B):
+        o, l = oa.attend_hca(qn[b], en[b], n_ent, m, wn[b], gq.cpu().double().numpy(),
+                             sink.cpu().double().numpy(), q_pos0, W, scale, 1e-6, 64, 1e4)
+        assert_attn_close(bf16_to_f64(out[b]), o, f"hca {case} b={b}", logit_mult=sm)
+        np.testing.assert_allclose(lse[b].cpu().numpy(), l, rtol=2e-3, atol=2e-3)
+
+
+def test_csa_with_every_entry_equals_hca_bitwise():
+    """CSA with the top-k list = every visible entry is the HCA computation."""
+    B, H, D, W, m = 2, 64, 512, 128, 128
+    n_ent = 700
+    q_pos0 = n_ent * m + 17
+    q, ent, win, gq, sink = _attn_inputs(B, 1, H, D, n_ent, W, 123)
+    topk = torch.arange(n_ent, dtype=torch.int32, device=DEV).expand(B, 1, n_ent).contiguous()
+    a, la = ops().csa_attend(q, ent, topk, win, gq, sink, q_pos0=q_pos0, W=W, want_lse=True)
+    h, lh = ops().hca_attend(q, ent, win, gq, sink, n_entries=n_ent, m=m, q_pos0=q_pos0, W=W,
+                             want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, h) and torch.equal(la, lh)
+
+
+def test_sink_closed_form_identical_rows():
+    """All rows equal u with zero rotary dims: out = S u with
+    S = n e^a / (n e^a + e^z) per head."""
+    B, H, D, R, W = 1, 64, 512, 64, 128
+    n_ent, k = 512, 256
+    u = synth.normal((D,), 9, "u", "cpu")
+    u[D - R:] = 0
+    row = synth.pack_values(u[None], R)[0]
+    ent = row.expand(B, n_ent, D + R).contiguous().to(DEV)
+    win = row.expand(B, W, D + R).contiguous().to(DEV)
+    q = synth.normal((B, 1, H, D), 9, "q", DEV, dtype=torch.bfloat16)
+    gq = torch.ones(D, device=DEV)
+    sink = synth.normal((H,), 9, "sink", DEV)
+    topk = _random_topk(B, 1, k, n_ent, 5)
+    out, _ = ops().csa_attend(q, ent, topk, win, gq, sink, q_pos0=10 ** 6, W=W)
+    torch.cuda.synchronize()
+    un = codecs.unpack_rows(row.numpy(), D, R)
+    qn = oc.rmsnorm(bf16_to_f64(q)[0, 0], np.ones(D), 1e-6)
+    a = (D ** -0.5) * (qn @ un)
+    n = k + W
+    z = sink.cpu().double().numpy()
+    S = n * np.exp(a) / (n * np.exp(a) + np.exp(z))
+    assert_attn_close(bf16_to_f64(out)[0, 0], S[:, None] * un[None, :], "closed form")
+
+
+def test_attend_deterministic():
+    B, H, D, Ncap, k, W = 2, 64, 512, 4096, 1024, 128
+    q, ent, win, gq, sink = _attn_inputs(B, 1, H, D, Ncap, W, 55)
+    topk = _random_topk(B, 1, k, Ncap, 8)
+    outs = [ops().csa_attend(q, ent, topk, win, gq, sink, q_pos0=1 << 20, W=W)[0]
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+# ---------------------------------------------------------- whole tiny pipeline --
+
+def test_tiny_csa_decode_pipeline_end_to_end():
+    """Tiny CSA decode: raw KV (T=4096, D=128) -> compress (m=4, 1024 entries)
+    and window rows -> integer indexer + top-64 -> attention; the oracle runs
+    the same pipeline from the same raw bytes."""
+    from long_context_sparse_csa_amd.configs import TINY_CSA as w
+    log("tiny pipeline")
+    B, T, D, R, m = w.B, w.T, w.D, w.R, w.m
+    raw, score, bias, _ = _compress_inputs(B, T, D, m, w.seed)
+    gamma = torch.ones(D, device=DEV)
+    N = T // m
+    ent = torch.zeros((B, N, D + R), dtype=torch.uint8, device=DEV)
+    ops().compress_pool(raw, score, bias, gamma, ent, raw_pos0=0, m=m, entry0=0, n_out=N)
+    t = T - 1
+    win = torch.zeros((B, w.W, D + R), dtype=torch.uint8, device=DEV)
+    ops().compress_pack(raw[:, T - w.W:].contiguous(), gamma, win, raw_pos0=T - w.W)
+    qI, wI, kI = _indexer_inputs(B, 1, w.HI, w.dI, N, w.seed, True)
+    topk, _ = ops().index_topk(qI, wI, kI, n_entries=N, q_pos0=t, m=m, k=w.k)
+    q = synth.normal((B, 1, w.H, D), w.seed, "q", DEV, dtype=torch.bfloat16)
+    sink = synth.normal((w.H,), w.seed, "sink", DEV)
+    out, _ = ops().csa_attend(q, ent, topk, win, gamma, sink, q_pos0=t, W=w.W)
+    torch.cuda.synchronize()
+    # oracle pipeline
+    c = bf16_to_f64(raw)[0]
+    js, e = oc.compress_pool(c, score[0].cpu().double().numpy(), 0, m,
+                             bias.cpu().double().numpy(), np.ones(D), 1e-6, R, 1e4)
+    ent_o = codecs.unpack_rows(codecs.pack_rows(e, R), D, R)
+    win_o = codecs.unpack_rows(codecs.pack_rows(
+        oc.compress_pack(c[T - w.W:], T - w.W, np.ones(D), 1e-6, R, 1e4), R), D, R)
+    tk, _ = oi.index_topk(bf16_to_f64(qI)[0], wI[0].cpu().double().numpy(), bf16_to_f64(kI)[0],
+                          N, [t], m, w.k)
+    np.testing.assert_array_equal(topk[0].cpu().numpy(), tk)
+    o, _ = oa.attend_csa(bf16_to_f64(q)[0], ent_o, tk, win_o, np.ones(D),
+                         sink.cpu().double().numpy(), t, w.W, w.scale, 1e-6, R, 1e4)
+    ma, rl = assert_attn_close(bf16_to_f64(out)[0], o, "tiny pipeline")
+    log(f"  max_abs {ma:.2e} rel_l2 {rl:.2e}")
