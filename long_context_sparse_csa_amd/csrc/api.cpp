@@ -106,6 +106,8 @@ int check_attend_common(const uint16_t* q, const uint8_t* entries, const uint8_t
   if (int st = check_dr(D, R)) return st;
   if (H < 1 || H > 64) return fail(V4ATTN_EUNSUPPORTED, "H = %d: 1 <= H <= 64 is built", H);
   if (Ncap < 0) return fail(V4ATTN_EINVAL, "negative Ncap");
+  if (Ncap * (int64_t)(D + R) >= ((int64_t)1 << 32))
+    return fail(V4ATTN_EUNSUPPORTED, "one sequence's entry cache must be below 4 GiB");
   if (W < 0 || W > kMaxW) return fail(V4ATTN_EUNSUPPORTED, "W = %d: 0 <= W <= %d", W, kMaxW);
   if (q_pos0 < 0) return fail(V4ATTN_EINVAL, "negative q_pos0");
   if (W > 0 && !win) return fail(V4ATTN_EINVAL, "null window buffer with W > 0");
@@ -212,8 +214,9 @@ int check_score_args(const uint16_t* q_idx, const float* w_idx, const uint16_t* 
 hipError_t run_score(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx, int B,
                      int Tq, int HI, int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0,
                      int m, float* scores, int64_t stride, hipStream_t st) {
+  const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
   v4::IndexScoreArgs ia{q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m,
-                        vmax_of(Tq, n_entries, q_pos0, m), scores, stride};
+                        vmax, scores, stride, v4::index_keys_per_wave(B, Tq, vmax)};
   return v4::launch_index_score(ia, st);
 }
 

@@ -146,13 +146,25 @@ __global__ __launch_bounds__(256) void compress_pool_kernel(
   float acc[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
+  // rows in batches of U per wave, all loads of a batch in flight together
+  constexpr int U = 64 / VPL;
   const uint16_t* base = raw + ((int64_t)b * L + r0) * D + lane * VPL;
-  for (int t = wave; t < nw; t += 4) {
-    float x[VPL];
-    load_bf16_row<VPL>(base + (int64_t)t * D, x);
-    const float a = s_alpha[t];
+  // (loads are unconditional -- rows past the window re-read the last row
+  // with weight 0 -- so the compiler keeps the whole batch in flight)
+  for (int t0 = wave; t0 < nw; t0 += 4 * U) {
+    float x[U][VPL];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, x[v], acc[v]);
+    for (int u = 0; u < U; ++u) {
+      const int t = min(t0 + 4 * u, nw - 1);
+      load_bf16_row<VPL>(base + (int64_t)t * D, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + 4 * u;
+      const float a = t < nw ? s_alpha[t] : 0.f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, x[u][v], acc[v]);
+    }
   }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) s_part[wave][lane * VPL + v] = acc[v];

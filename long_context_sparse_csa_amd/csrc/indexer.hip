@@ -8,8 +8,9 @@
 //
 // Design (decode): the dense contraction [HI heads x dI] x [dI x keys] runs on
 // the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with the query's heads as
-// the M dimension held in registers for the whole workgroup and the keys as
-// N.  Keys stream from HBM straight into MFMA operand registers: the MFMA
+// the M dimension, loaded once per wave and held in registers, and the keys as
+// N.  Each wave streams one contiguous range of keys in 64-key chunks, two
+// chunks deep, straight from HBM into MFMA operand registers: the MFMA
 // contracts over dI, so dI may be permuted freely as long as q and k agree;
 // each lane therefore owns one contiguous dI/4-element slice of a key row
 // (64 contiguous bytes at dI = 128) instead of four scattered 16-byte pieces.
@@ -32,8 +33,10 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
   const int64_t t = a.q_pos0 + r;
   int64_t V = (t + 1) / a.m;
   if (V > a.n_entries) V = a.n_entries;
-  const int64_t j0 = (int64_t)blockIdx.x * 256 + wave * 64;
-  if (j0 >= V) return;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;   // this wave's key range
+  const int64_t jbeg = gw * a.keys_per_wave;
+  if (jbeg >= V) return;
+  const int64_t jend = min(jbeg + a.keys_per_wave, V);
 
   const int64_t qrow = (int64_t)b * a.Tq + r;
   // A operand: head mb*16 + c, dims g*LPK + ks*8 .. +8 (the shared permutation)
@@ -41,11 +44,11 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
   const uint16_t* qp = a.q_idx + qrow * a.HI * DI;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int h = mb * 16 + c;
+    const int h = min(mb * 16 + c, a.HI - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (h < a.HI) v = *reinterpret_cast<const u32x4*>(qp + (int64_t)h * DI + g * LPK + ks * 8);
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + (int64_t)h * DI + g * LPK + ks * 8);
+      if (mb * 16 + c >= a.HI) v = u32x4{0u, 0u, 0u, 0u};
       qa[mb][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -57,52 +60,74 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = mb * 16 + g * 4 + i;
-      wv[mb][i] = h < a.HI ? wp[h] : 0.f;
+      const float x = wp[min(h, a.HI - 1)];
+      wv[mb][i] = h < a.HI ? x : 0.f;
     }
 
   const uint16_t* kp = a.k_idx + (int64_t)b * a.Ncap * DI + g * LPK;
   float* sp = a.scores + qrow * a.score_stride;
 
-  // all four 16-key blocks of this wave in flight at once
-  u32x4 kv[4][KS];
+  // 64-key chunks (four 16-key blocks), two chunks in registers: the next
+  // chunk's loads are in flight while the current one is contracted.  Keys
+  // past the range re-read the last visible key (its score is not stored).
+  auto load = [&](u32x4 (&kv)[4][KS], int64_t j0) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int64_t j = j0 + nb * 16 + c;
+    for (int nb = 0; nb < 4; ++nb) {
+      const int64_t j = min(j0 + nb * 16 + c, V - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j < V) v = *reinterpret_cast<const u32x4*>(kp + j * DI + ks * 8);
-      kv[nb][ks] = v;
+      for (int ks = 0; ks < KS; ++ks) kv[nb][ks] = *reinterpret_cast<const u32x4*>(kp + j * DI + ks * 8);
     }
-  }
+  };
+  auto score = [&](const u32x4 (&kv)[4][KS], int64_t j0) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    f32x4 acc[MB];
+    for (int nb = 0; nb < 4; ++nb) {
+      f32x4 acc[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kb = __builtin_bit_cast(bf16x8, kv[nb][ks]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, kv[nb][ks]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+      }
+      // lane holds key column c, heads mb*16 + g*4 + i
+      float s = 0.f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = fmaf(wv[mb][i], fmaxf(acc[mb][i], 0.f), s);
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      const int64_t j = j0 + nb * 16 + c;
+      if (g == 0 && j < jend) sp[j] = s;
     }
-    // lane holds key column c, heads mb*16 + g*4 + i
-    float s = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(wv[mb][i], fmaxf(acc[mb][i], 0.f), s);
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    const int64_t j = j0 + nb * 16 + c;
-    if (g == 0 && j < V) sp[j] = s;
+  };
+
+  u32x4 ka[4][KS], kb[4][KS];
+  load(ka, jbeg);
+  for (int64_t j0 = jbeg; j0 < jend; j0 += 128) {
+    load(kb, j0 + 64);
+    score(ka, j0);
+    if (j0 + 64 >= jend) break;
+    load(ka, j0 + 128);
+    score(kb, j0 + 64);
   }
+}
+
+int64_t index_keys_per_wave(int B, int Tq, int64_t vmax) {
+  const int64_t total = (int64_t)B * Tq * vmax;
+  const int64_t waves = 256 * 8;                 // 256 CUs x 8 waves
+  int64_t kpw = (total + waves - 1) / waves;
+  kpw = (kpw + 63) / 64 * 64;
+  if (kpw < 64) kpw = 64;
+  if (kpw > 8192) kpw = 8192;
+  return kpw;
 }
 
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t st) {
   if (a.vmax <= 0 || a.B == 0 || a.Tq == 0) return hipSuccess;
-  dim3 grid((unsigned)((a.vmax + 255) / 256), a.Tq, a.B);
+  dim3 grid((unsigned)((a.vmax + 4 * a.keys_per_wave - 1) / (4 * a.keys_per_wave)), a.Tq, a.B);
   const int mb = (a.HI + 15) / 16;
 #define V4_IDX(DI, MB) index_score_kernel<DI, MB><<<grid, 256, 0, st>>>(a)
 #define V4_IDX_MB(DI)          \

@@ -95,15 +95,55 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage_kernel(
   int len = 0;
   if (n_in > beg) len = (int)((n_in - beg) < kTopkPart ? (n_in - beg) : kTopkPart);
 
-  // load keys (and candidate indices) into LDS, count present keys
+  // load keys (and candidate indices) into LDS, count present keys.  All of
+  // a thread's 16-byte loads are issued before any is consumed, so the part
+  // arrives in about one memory latency instead of one per element.
   int nvalid = 0;
-  for (int i = tid; i < len; i += kTopkThreads) {
+  constexpr int U = kTopkPart / 4 / kTopkThreads;
+  const int64_t src0 = FIRST ? qr * score_stride + beg : qr * in_stride + beg;
+  const bool vec = FIRST ? (score_stride & 3) == 0 : (in_stride & 3) == 0;
+  const int len4 = vec ? (len >> 2) : 0;
+  if (len4 > 0) {
+    // unconditional loads (indices past the part re-read its last vector),
+    // so every load of the thread is in flight at once
+    u32x4 kv[U];
+    u32x4 iv[FIRST ? 1 : U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i4 = min(tid + u * kTopkThreads, len4 - 1);
+      if (FIRST) {
+        kv[u] = *reinterpret_cast<const u32x4*>(scores + src0 + 4 * i4);
+      } else {
+        kv[u] = *reinterpret_cast<const u32x4*>(in_key + src0 + 4 * i4);
+        iv[FIRST ? 0 : u] = *reinterpret_cast<const u32x4*>(in_idx + src0 + 4 * i4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i4 = tid + u * kTopkThreads;
+      if (i4 < len4) {
+        u32x4 k4 = kv[u];
+        if (FIRST) {
+          k4.x = score_key(__uint_as_float(k4.x));
+          k4.y = score_key(__uint_as_float(k4.y));
+          k4.z = score_key(__uint_as_float(k4.z));
+          k4.w = score_key(__uint_as_float(k4.w));
+        } else {
+          *reinterpret_cast<u32x4*>(&s_idx[4 * i4]) = iv[FIRST ? 0 : u];
+        }
+        *reinterpret_cast<u32x4*>(&s_key[4 * i4]) = k4;
+        nvalid += (k4.x != 0u) + (k4.y != 0u) + (k4.z != 0u) + (k4.w != 0u);
+      }
+    }
+  }
+#pragma unroll 8
+  for (int i = 4 * len4 + tid; i < len; i += kTopkThreads) {
     unsigned key;
     if (FIRST) {
-      key = score_key(scores[qr * score_stride + beg + i]);
+      key = score_key(scores[src0 + i]);
     } else {
-      key = in_key[qr * in_stride + beg + i];
-      s_idx[i] = in_idx[qr * in_stride + beg + i];
+      key = in_key[src0 + i];
+      s_idx[i] = in_idx[src0 + i];
     }
     s_key[i] = key;
     nvalid += key != 0u;
