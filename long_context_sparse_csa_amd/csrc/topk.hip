@@ -8,10 +8,12 @@
 //
 // Design: exact selection in LDS, no sorting.  Scores map to order-preserving
 // 32-bit keys.  A workgroup loads up to 16384 keys of one query into LDS and
-// runs an MSB-first radix select (11/11/10-bit digits, histograms with LDS
-// atomics, one block scan per pass) that fixes the exact k-th key tau and how
-// many of its ties are needed; it stops early once a digit bucket is needed
-// whole.  A stream compaction in position order then writes every key above
+// runs a bucket select: each pass bins the live key range [lo, hi] linearly
+// into at most 2048 LDS-atomic buckets (starting from the part's actual min
+// and max, so a clustered score distribution still spreads over the buckets
+// instead of piling onto a few exponent bins), keeps the bucket holding the
+// k-th key and stops when it is one key wide or needed whole -- at most three
+// passes for 32-bit keys.  A stream compaction in position order then writes every key above
 // tau and the lowest-positioned ties, so the output comes out in ascending
 // index order without a sort.  Longer rows are cut into parts: the union of
 // the parts' exact top-k always contains the row's top-k, so a second pass
@@ -22,9 +24,11 @@
 
 namespace v4 {
 
-constexpr int kTopkThreads = 512;
+constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kHistBins = 2048;
+constexpr int kTopkRounds = kTopkPart / kTopkThreads;
+static_assert(kTopkRounds * kTopkWaves <= kTopkThreads, "one scan entry per thread");
 
 TopkPlan topk_plan(int64_t vmax, int k) {
   TopkPlan p;
@@ -41,8 +45,8 @@ TopkPlan topk_plan(int64_t vmax, int k) {
   return p;
 }
 
-// Exclusive scan of one value per thread across the block (512 threads);
-// returns the prefix and writes the block total to *total.
+// Exclusive scan of one value per thread across the block; returns the
+// prefix and writes the block total to *total.
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -65,6 +69,17 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
   return before + x - v;
 }
 
+__device__ __forceinline__ unsigned wave_min_u(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ unsigned wave_max_u(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o));
+  return v;
+}
+
 template <bool FIRST>
 __global__ __launch_bounds__(kTopkThreads) void topk_stage_kernel(
     const float* __restrict__ scores, int64_t score_stride, const unsigned* __restrict__ in_key,
@@ -77,7 +92,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage_kernel(
   unsigned* s_hist = smem + kTopkPart;                      // [kHistBins]
   int* s_idx = reinterpret_cast<int*>(s_hist + kHistBins);  // [kTopkPart] (!FIRST)
   __shared__ int s_wave[kTopkWaves];
-  __shared__ int s_cnt[2][kTopkWaves][2];
+  __shared__ unsigned s_mm[2][kTopkWaves];
+  __shared__ int s_blk[2][kTopkRounds * kTopkWaves];  // per (round, wave) block
   __shared__ unsigned s_sel[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -95,17 +111,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage_kernel(
   int len = 0;
   if (n_in > beg) len = (int)((n_in - beg) < kTopkPart ? (n_in - beg) : kTopkPart);
 
-  // load keys (and candidate indices) into LDS, count present keys.  All of
-  // a thread's 16-byte loads are issued before any is consumed, so the part
-  // arrives in about one memory latency instead of one per element.
+  // load keys (and candidate indices) into LDS; count present keys and take
+  // their min and max.  All of a thread's 16-byte loads are issued before any
+  // is consumed (indices past the part re-read its last vector).
   int nvalid = 0;
+  unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
+  auto note = [&](unsigned key) {
+    nvalid += key != 0u;
+    if (key != 0u) {
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+    }
+  };
   constexpr int U = kTopkPart / 4 / kTopkThreads;
   const int64_t src0 = FIRST ? qr * score_stride + beg : qr * in_stride + beg;
   const bool vec = FIRST ? (score_stride & 3) == 0 : (in_stride & 3) == 0;
   const int len4 = vec ? (len >> 2) : 0;
   if (len4 > 0) {
-    // unconditional loads (indices past the part re-read its last vector),
-    // so every load of the thread is in flight at once
     u32x4 kv[U];
     u32x4 iv[FIRST ? 1 : U];
 #pragma unroll
@@ -132,7 +154,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage_kernel(
           *reinterpret_cast<u32x4*>(&s_idx[4 * i4]) = iv[FIRST ? 0 : u];
         }
         *reinterpret_cast<u32x4*>(&s_key[4 * i4]) = k4;
-        nvalid += (k4.x != 0u) + (k4.y != 0u) + (k4.z != 0u) + (k4.w != 0u);
+        note(k4.x);
+        note(k4.y);
+        note(k4.z);
+        note(k4.w);
       }
     }
   }
@@ -146,39 +171,58 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage_kernel(
       s_idx[i] = in_idx[src0 + i];
     }
     s_key[i] = key;
-    nvalid += key != 0u;
+    note(key);
+  }
+  kmin = wave_min_u(kmin);
+  kmax = wave_max_u(kmax);
+  if (lane == 0) {
+    s_mm[0][wave] = kmin;
+    s_mm[1][wave] = kmax;
   }
   int total_valid;
   (void)block_excl_scan(nvalid, s_wave, &total_valid);  // also syncs after the LDS writes
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    kmin = min(kmin, s_mm[0][w]);
+    kmax = max(kmax, s_mm[1][w]);
+  }
 
-  // radix select: find prefix (pbits bits) of the k-th key and the ties needed
+  // Bucket select: the kept keys form the contiguous key range [lo, hi]; each
+  // pass bins that range linearly into at most 2048 buckets (so the bins
+  // follow the data, not the exponent bits), keeps the bucket holding the
+  // k-th key and accounts for everything above it.  It ends when the bucket
+  // is one key wide (ties by position) or needed whole.
   const bool all = total_valid <= k;
-  unsigned prefix = 0;
-  int pbits = 0;
+  unsigned lo = kmin, hi = kmax;
   int need = all ? total_valid : k;
   if (!all) {
-    for (int pass = 0; pass < 3; ++pass) {
-      const int bits = pass < 2 ? 11 : 10;
-      const int nb = 1 << bits;
-      const int shift = 32 - pbits - bits;
+    while (true) {
+      const unsigned span = hi - lo;   // width - 1
+      int shift = 0;
+      while ((span >> shift) >= (unsigned)kHistBins) ++shift;
+      const int nb = (int)(span >> shift) + 1;   // <= kHistBins
       for (int i = tid; i < nb; i += kTopkThreads) s_hist[i] = 0u;
       __syncthreads();
+#pragma unroll 4
       for (int i = tid; i < len; i += kTopkThreads) {
         const unsigned key = s_key[i];
-        const bool in_group = key != 0u && (pbits == 0 || (key >> (32 - pbits)) == prefix);
-        if (in_group) atomicAdd(&s_hist[(key >> shift) & (unsigned)(nb - 1)], 1u);
+        if (key != 0u && key >= lo && key <= hi) atomicAdd(&s_hist[(key - lo) >> shift], 1u);
       }
       __syncthreads();
-      // thread t owns digits nb-1-per*t down to nb-per*(t+1) (high digits first)
-      const int per = nb / kTopkThreads;
+      // thread t owns buckets nb-1-2t and nb-2-2t (high buckets first)
       int loc = 0;
-      for (int u = 0; u < per; ++u) loc += (int)s_hist[nb - 1 - (per * tid + u)];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int d = nb - 1 - (2 * tid + u);
+        loc += d >= 0 ? (int)s_hist[d] : 0;
+      }
       int tot;
       int above = block_excl_scan(loc, s_wave, &tot);
-      for (int u = 0; u < per; ++u) {
-        const int d = nb - 1 - (per * tid + u);
-        const int cnt = (int)s_hist[d];
-        if (above < need && above + cnt >= need) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int d = nb - 1 - (2 * tid + u);
+        const int cnt = d >= 0 ? (int)s_hist[d] : 0;
+        if (d >= 0 && above < need && above + cnt >= need) {
           s_sel[0] = (unsigned)d;
           s_sel[1] = (unsigned)above;
           s_sel[2] = (unsigned)cnt;
@@ -190,54 +234,74 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage_kernel(
       const int cnt_gt = (int)s_sel[1], cnt_eq = (int)s_sel[2];
       __syncthreads();
       need -= cnt_gt;
-      prefix = (prefix << bits) | d;
-      pbits += bits;
-      if (cnt_eq == need) break;  // the whole bucket is selected
+      const unsigned nlo = lo + (d << shift);
+      const uint64_t nhi = (uint64_t)nlo + (1ull << shift) - 1u;
+      hi = nhi < (uint64_t)hi ? (unsigned)nhi : hi;
+      lo = nlo;
+      if (cnt_eq == need || lo == hi) break;
     }
   }
 
-  // stream compaction in position order
+  // Stream compaction in position order.  Round r covers positions
+  // [r*threads, (r+1)*threads); (round, wave) blocks are in position order.
+  // Pass A counts each block's keys above the bucket and in it with ballots,
+  // one scan over the (at most 256) blocks turns that into the first output
+  // slot and the first tie rank of every block, and pass B writes.
   const unsigned long long lt_mask = (1ull << lane) - 1ull;
-  int base_sel = 0, base_eq = 0;
   const int n_sel_total = all ? total_valid : k;
-  for (int r0 = 0, rnd = 0; r0 < len; r0 += kTopkThreads, ++rnd) {
-    const int i = r0 + tid;
-    const unsigned key = i < len ? s_key[i] : 0u;
-    bool gt, eq;
+  const int nrounds = (len + kTopkThreads - 1) / kTopkThreads;
+  auto classify = [&](int i, unsigned& key, bool& gt, bool& eq) {
+    key = i < len ? s_key[i] : 0u;
     if (all) {
       gt = key != 0u;
       eq = false;
     } else {
-      const unsigned top = key >> (32 - pbits);
-      gt = key != 0u && top > prefix;
-      eq = key != 0u && top == prefix;
+      gt = key != 0u && key > hi;
+      eq = key != 0u && key >= lo && key <= hi;
     }
+  };
+#pragma unroll 4
+  for (int rnd = 0; rnd < nrounds; ++rnd) {
+    unsigned key;
+    bool gt, eq;
+    classify(rnd * kTopkThreads + tid, key, gt, eq);
     const unsigned long long bg = __ballot(gt), be = __ballot(eq);
-    const int par = rnd & 1;
     if (lane == 0) {
-      s_cnt[par][wave][0] = __popcll(bg);
-      s_cnt[par][wave][1] = __popcll(be);
+      s_blk[0][rnd * kTopkWaves + wave] = __popcll(bg);
+      s_blk[1][rnd * kTopkWaves + wave] = __popcll(be);
     }
-    __syncthreads();
-    int sel_before = 0, eq_before = base_eq, rnd_sel = 0, rnd_eq = 0;
-    for (int w = 0; w < kTopkWaves; ++w) {
-      const int cg = s_cnt[par][w][0], ce = s_cnt[par][w][1];
-      int take = need - (base_eq + rnd_eq);
-      take = take < 0 ? 0 : (take > ce ? ce : take);
-      if (w < wave) {
-        sel_before += cg + take;
-        eq_before += ce;
-      }
-      rnd_sel += cg + take;
-      rnd_eq += ce;
+  }
+  __syncthreads();
+  {
+    const int e = tid;   // block (round e / waves, wave e % waves), position order
+    const bool own = e < nrounds * kTopkWaves;
+    const int cg = own ? s_blk[0][e] : 0, ce = own ? s_blk[1][e] : 0;
+    int tot;
+    const int eq_before = block_excl_scan(ce, s_wave, &tot);
+    int take = need - eq_before;
+    take = take < 0 ? 0 : (take > ce ? ce : take);
+    const int sel_before = block_excl_scan(cg + take, s_wave, &tot);
+    if (own) {
+      s_blk[0][e] = sel_before;
+      s_blk[1][e] = eq_before;
     }
-    const int my_eq_rank = eq_before + __popcll(be & lt_mask);
-    const bool sel = gt || (eq && my_eq_rank < need);
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int rnd = 0; rnd < nrounds; ++rnd) {
+    const int i = rnd * kTopkThreads + tid;
+    unsigned key;
+    bool gt, eq;
+    classify(i, key, gt, eq);
+    const unsigned long long bg = __ballot(gt), be = __ballot(eq);
+    const int e = rnd * kTopkWaves + wave;
+    const int sel_before = s_blk[0][e], eq_before = s_blk[1][e];
+    const int eq_lt = __popcll(be & lt_mask);
+    const bool sel = gt || (eq && eq_before + eq_lt < need);
     if (sel) {
       int take_lt = need - eq_before;
-      const int eq_lt = __popcll(be & lt_mask);
       take_lt = take_lt < 0 ? 0 : (take_lt > eq_lt ? eq_lt : take_lt);
-      const int pos = base_sel + sel_before + __popcll(bg & lt_mask) + take_lt;
+      const int pos = sel_before + __popcll(bg & lt_mask) + take_lt;
       const int idx = FIRST ? (int)(beg + i) : s_idx[i];
       if (last) {
         topk[qr * k + pos] = idx;
@@ -247,8 +311,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_stage_kernel(
         out_idx[qr * out_stride + (int64_t)part * k + pos] = idx;
       }
     }
-    base_sel += rnd_sel;
-    base_eq += rnd_eq;
   }
   // padding
   for (int p = n_sel_total + tid; p < k; p += kTopkThreads) {
