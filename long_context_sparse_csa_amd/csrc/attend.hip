@@ -14,25 +14,27 @@
 // Design.  One workgroup of eight waves owns one query token and one range of
 // its rows (entries, then window rows), so every packed row is fetched from
 // HBM once for all 64 heads.  Rows are gathered (CSA: through the top-k list)
-// 32 at a time with 16-byte coalesced loads, double-buffered through
-// registers, and widened once at staging (E4M3 -> bf16 is exact) into a bf16
-// LDS tile, so no wave converts anything in its inner loop.  Waves w
-// and w+4 share heads 16(w%4)..+15 and split the 512 dims in halves: each
-// contracts S over its half (holding only that half of q~), the pair adds the
-// two partial S through LDS, both run the same softmax, and each accumulates
-// the output for the same half of the dims.  Every wave therefore reads the
-// same 288 bytes of each row for both products, and the per-wave registers
-// (half of q~, half of the output) leave room for two workgroups per CU.
-//   S^T = K q~^T : K rows are the A operand (one 16-byte LDS read per lane),
-//                  q~ is the B operand held in registers for the whole kernel;
-//                  the result puts one head per lane column and keys down the
-//                  lane groups, so the softmax statistics need two cross-lane
-//                  steps;
-//   O^T += V^T P^T : V^T comes straight from the row-major tile with the
-//                  gfx950 transposing LDS read ds_read_b64_tr_b16; the
-//                  probabilities stay in the registers the S^T accumulators
-//                  left them in, because the MFMA's key order is permuted to
-//                  match (k slot j of lane group g = key 4g+j or 16+4g+j-4).
+// 64 at a time straight into LDS with global_load_lds (no staging registers,
+// no conversion on the way; four waves move 16 rows each) and kept in their
+// packed form: 576 bytes a row, E4M3 then bf16, 16-byte chunks XOR-swizzled
+// by row so that both LDS read patterns below are free of bank conflicts.
+// Two tile buffers alternate: the next tile lands while the current one is
+// used.
+//   Waves w and w+4 share heads 16(w%4)..+15 and split the dims in halves:
+// each contracts S over its half (holding only that half of q~), the pair
+// adds the two partial S through LDS, both run the same softmax, and each
+// accumulates the output for its half of the dims:
+//   S^T = K q~^T : K rows are the A operand, read 16 bytes a lane (two k-steps
+//                  of E4M3, widened exactly to bf16 in registers); q~ is the B
+//                  operand, held in registers with its dims permuted to match
+//                  the order in which the lanes read the row;
+//   O^T += V^T P^T : V^T comes from the packed rows with the gfx950
+//                  transposing LDS reads (ds_read_b64_tr_b8 for E4M3 dims,
+//                  ds_read_b64_tr_b16 for the bf16 ones), so nothing is stored
+//                  twice; the probabilities stay in the registers the S^T
+//                  accumulators left them in, because the key order of the
+//                  transposing reads is permuted to match (k slot j of lane
+//                  group g = key 4g+j or 16+4g+j-4 of each 32-key half).
 // O^T keeps one head per lane, so the online-softmax rescale needs no
 // shuffles, and the running maximum moves only when it grows by more than
 // 2^8 (probabilities stay below 256, exact enough in bf16 and fp32), which
@@ -43,26 +45,50 @@
 
 namespace v4 {
 
-constexpr int kAttTile = 32;      // rows per LDS tile
-constexpr int kAttThreads = 512;  // eight waves: four head groups x two halves
+constexpr int kAttTile = 64;      // rows per LDS tile
+constexpr int kAttThreads = 512;  // eight waves: four head groups x two dim halves
 constexpr int kMaxTopk = 4096;    // largest k the CSA kernel stages in LDS
 constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max moves
 constexpr float kNoMax = -1.0e30f; // running-max floor (no key seen yet)
 
+// Source of absent rows (masked out of the softmax; zeros keep 0 * V finite).
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row[1024];
+
 template <int D>
 struct AttGeom {
   static constexpr int R = 64;
-  static constexpr int ROW = D + R;            // packed bytes per row in HBM
-  static constexpr int BSTR = 2 * D + 32;      // bf16 LDS row stride (8-bank shift per row)
-  static constexpr int KSTEPS = D / 32;        // 32-dim k-steps of S^T
-  static constexpr int KSH = KSTEPS / 2;       // k-steps per half
-  static constexpr int DB = D / 16;            // 16-dim blocks of O^T
-  static constexpr int DBH = DB / 2;           // blocks per half
-  static constexpr int CPR = ROW / 16;         // 16-byte chunks per packed row
+  static constexpr int ROW = D + R;            // packed bytes per row (HBM and LDS)
+  static constexpr int CPR = ROW / 16;         // 16-byte chunks per row
   static constexpr int FP8_CPR = (D - R) / 16; // of which E4M3
-  static constexpr int CHUNKS = kAttTile * CPR;
-  static constexpr int CH = (CHUNKS + kAttThreads - 1) / kAttThreads;
+  static constexpr int KSTEPS = D / 32;        // 32-dim k-steps of S^T
+  static constexpr int KF = (D - R) / 32;      // of which over E4M3 dims
+  static constexpr int DB = D / 16;            // 16-dim blocks of O^T
+  static constexpr int FB = (D - R) / 16;      // of which over E4M3 dims
+  static constexpr int TILE_BYTES = kAttTile * ROW;
+  static constexpr int KSH = KSTEPS / 2;       // k-steps per dim half
+  static constexpr int DBH = DB / 2;           // output blocks per dim half
+  static constexpr int WPW = CPR / 4;          // 1 KiB copies per staging wave per tile (16 rows)
+  static constexpr int HALF = 32 * ROW;        // byte offset of the second 32-key half
+  static_assert(FP8_CPR % 4 == 0 && CPR % 4 == 0, "the chunk swizzle stays inside a region");
+  static_assert(KSH % 2 == 0, "k-step pairs do not straddle the dim halves");
+  static_assert(ROW <= 1024, "absent rows read the zero row");
 };
+
+// Physical chunk = logical chunk ^ swz(row): rows 4i..4i+3 rotate the four
+// chunks of every aligned group differently, which spreads 16 rows of one
+// logical chunk over all 16 chunk slots of a 256-byte bank line.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+// 64 lanes x 16 bytes from per-lane global addresses into 1 KiB of LDS at
+// `dst` (+16 bytes per lane).  Written as asm so that the compiler does not
+// track it (it would otherwise wait for the copy before every LDS read): the
+// tile loop waits for these copies itself (vmcnt) before the barrier that
+// publishes a tile.  The instruction has no register result; its address
+// registers are read at issue.
+__device__ __forceinline__ void copy_to_lds16(const void* src, V4_LDS void* dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
 
 struct RowSpace {
   int64_t n_ent;    // entry rows (CSA: k slots; HCA: visible entries)
@@ -85,6 +111,15 @@ __device__ __forceinline__ RowSpace row_space(const AttendArgs& a, bool csa, int
   return rs;
 }
 
+// q~ dims of k-step ks for lane group g, in the order the lanes read K rows:
+// E4M3 k-step pairs take 16 contiguous dims per lane group (one 16-byte chunk
+// read covers two k-steps), the bf16 k-steps 8 contiguous dims.
+template <int D>
+__device__ __forceinline__ int q_dim(int ks, int g) {
+  using G = AttGeom<D>;
+  return ks < G::KF ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : (D - G::R) + 32 * (ks - G::KF) + 8 * g;
+}
+
 template <int D, bool CSA>
 __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
   using G = AttGeom<D>;
@@ -99,11 +134,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
   const int head = hg * 16 + c;
   const bool active = hg * 16 < a.H;
 
-  // bf16 tiles: E4M3 dims are widened once here, at staging, not per wave
-  __shared__ __attribute__((aligned(16))) uint8_t s_tile[2][kAttTile * G::BSTR];
-  __shared__ __attribute__((aligned(16))) f32x4 s_x[8][64][2];  // partial S^T for the pair
-  __shared__ unsigned s_valid[2];
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[2][G::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) f32x4 s_x[8][4][64];  // partial S^T for the pair
+  __shared__ unsigned s_v[2][4];   // per buffer: row-present bits, 16 rows per staging wave
   __shared__ float s_cs[R / 2][2];
+  __shared__ __attribute__((aligned(16))) float s_gamma[D];
   __shared__ int s_sel[CSA ? kMaxTopk : 1];  // this split's slice of the top-k list
 
   const RowSpace rs = row_space(a, CSA, t);
@@ -113,14 +148,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
   int64_t row_end = row_beg + chunk;
   if (row_end > rs.n_rows) row_end = rs.n_rows;
   const int ntiles = row_end > row_beg ? (int)((row_end - row_beg + kAttTile - 1) / kAttTile) : 0;
-  // split-local row numbers fit in 32 bits; offsets within one sequence's
-  // cache fit in 32 bits (checked on the host)
+  // split-local row numbers fit in 32 bits
   const int nloc = (int)(row_end - row_beg);
   const int ent_loc = (int)max((int64_t)0, min(rs.n_ent, row_end) - row_beg);  // entry rows here
   const uint8_t* ent_b = a.entries + (int64_t)b * a.Ncap * G::ROW;
   const uint8_t* win_b = a.win + ((int64_t)b * (a.Tq + a.W - 1) +
                                   (rs.win_lo - (a.q_pos0 - (a.W - 1)))) * G::ROW;
-  const int64_t win_first = rs.n_ent - row_beg;   // split-local row of the first window row
+  const int win_first = (int)(rs.n_ent - row_beg);   // split-local row of the first window row
 
   if (tid < R / 2) {
     float cs, sn;
@@ -128,104 +162,61 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
     s_cs[tid][0] = cs;
     s_cs[tid][1] = sn;
   }
+  for (int d = 4 * tid; d < D; d += 4 * kAttThreads)
+    *reinterpret_cast<f32x4*>(&s_gamma[d]) = *reinterpret_cast<const f32x4*>(a.gamma_q + d);
   if constexpr (CSA) {
     const int32_t* sel = a.topk + (int64_t)qr * a.k + row_beg;
     for (int x = tid; x < ent_loc; x += kAttThreads) s_sel[x] = sel[x];
-    __syncthreads();
-  }
-
-  // local row x -> byte offset from its base (32-bit: one sequence's cache is
-  // below 4 GiB), or -1 if absent
-  const int row_beg32 = (int)row_beg;
-  const int win_first32 = (int)win_first;
-  auto row_src = [&](int x, const uint8_t*& base) -> int {
-    if (x >= nloc) return -1;
-    if (x < ent_loc) {
-      int j = x + row_beg32;
-      if constexpr (CSA) {
-        j = s_sel[x];
-        if (j < 0 || (int64_t)j >= a.Ncap) return -1;
-      }
-      base = ent_b;
-      return j * G::ROW;
-    }
-    base = win_b;
-    return (x - win_first32) * G::ROW;
-  };
-
-  // ---- staging: this thread's chunks u -> (row, 16-byte column), fixed per tile
-  int crow[G::CH], ccol[G::CH];
-#pragma unroll
-  for (int u = 0; u < G::CH; ++u) {
-    const int cidx = min(tid + u * kAttThreads, G::CHUNKS - 1);
-    crow[u] = cidx / G::CPR;
-    ccol[u] = cidx % G::CPR;
-  }
-  const uint8_t* dummy = a.Ncap > 0 ? a.entries : a.win;
-  u32x4 pref[G::CH];
-  bool pval[G::CH];
-  auto fetch_rows = [&](int tile) {
-#pragma unroll
-    for (int u = 0; u < G::CH; ++u) {
-      const uint8_t* base = ent_b;
-      const int off = row_src(tile * kAttTile + crow[u], base);
-      pval[u] = (u + 1) * kAttThreads <= G::CHUNKS || tid + u * kAttThreads < G::CHUNKS;
-      pval[u] = pval[u] && off >= 0;
-      // absent rows read a valid address and are zeroed at the store, so the
-      // loads are unconditional and all in flight together
-      const uint8_t* src = pval[u] ? base + (unsigned)off + ccol[u] * 16 : dummy;
-      pref[u] = *reinterpret_cast<const u32x4*>(src);
-    }
-  };
-  auto store_rows = [&](int tile, int buf) {
-    uint8_t* T = s_tile[buf];
-#pragma unroll
-    for (int u = 0; u < G::CH; ++u) {
-      if ((u + 1) * kAttThreads <= G::CHUNKS || tid + u * kAttThreads < G::CHUNKS) {
-        const int row = crow[u], col = ccol[u];
-        const u32x4 v = pval[u] ? pref[u] : u32x4{0u, 0u, 0u, 0u};
-        if (col < G::FP8_CPR) {   // 16 E4M3 values -> 16 bf16 (exact)
-          const u32x2 lo = fp8x4_to_bf16x4(v.x), hi = fp8x4_to_bf16x4(v.y);
-          const u32x2 lo2 = fp8x4_to_bf16x4(v.z), hi2 = fp8x4_to_bf16x4(v.w);
-          u32x4* dst = reinterpret_cast<u32x4*>(T + row * G::BSTR + col * 32);
-          dst[0] = u32x4{lo.x, lo.y, hi.x, hi.y};
-          dst[1] = u32x4{lo2.x, lo2.y, hi2.x, hi2.y};
-        } else {                  // 8 bf16 values
-          *reinterpret_cast<u32x4*>(T + row * G::BSTR + 2 * (D - R) + (col - G::FP8_CPR) * 16) = v;
-        }
-      }
-    }
-    if (tid < 64) {
-      const uint8_t* base = ent_b;
-      const bool ok = tid < kAttTile && row_src(tile * kAttTile + tid, base) >= 0;
-      const unsigned long long m = __ballot(ok);
-      if (tid == 0) s_valid[buf] = (unsigned)m;
-    }
-  };
-
-  if (ntiles > 0) {
-    fetch_rows(0);
-    store_rows(0, 0);
   }
   __syncthreads();
 
-  // ---- q~ = RoPE_t(RMSNorm(q)) as the B operand: head c, dims ks*32 + g*8 + e
+  // split-local row x -> its packed row in HBM, or nullptr if absent
+  auto row_ptr = [&](int x) -> const uint8_t* {
+    const bool ent = x < ent_loc;
+    int64_t j = (int64_t)x + row_beg;
+    bool ok = x < nloc;
+    if constexpr (CSA) {
+      j = s_sel[ent ? x : 0];
+      ok = ok && (!ent || (j >= 0 && j < a.Ncap));
+    }
+    const uint8_t* p = ent ? ent_b + j * G::ROW : win_b + (int64_t)(x - win_first) * G::ROW;
+    return ok ? p : nullptr;
+  };
+
+  // ---- staging (waves 0-3): wave w copies tile rows 16w..16w+15 as WPW
+  // windows of 64 16-byte slots; slot s holds physical chunk s % CPR of row
+  // s / CPR, loaded from logical chunk (s % CPR) ^ swz(row).  Lane l resolves
+  // row 16w + l%16.
+  const uint8_t* zero_row = g_zero_row;
+  auto issue_tile = [&](int tile, int buf) {
+    const uint8_t* rp = row_ptr(tile * kAttTile + 16 * wave + (lane & 15));
+    const bool ok = rp != nullptr;
+    const unsigned long long bal = __ballot(ok);
+    if (lane == 0) s_v[buf][wave] = (unsigned)(bal & 0xFFFFull);
+    const long long rpl = (long long)(uintptr_t)(ok ? rp : zero_row);
+    uint8_t* Tw = s_tile[buf] + 16 * wave * G::ROW;
+#pragma unroll
+    for (int i = 0; i < G::WPW; ++i) {
+      const int sl = 64 * i + lane;
+      const int rl = sl / G::CPR, pc = sl - rl * G::CPR;
+      const uint8_t* src = (const uint8_t*)(uintptr_t)__shfl(rpl, rl) + 16 * (pc ^ swz(rl));
+      copy_to_lds16(src, (V4_LDS void*)(Tw + 1024 * i));
+    }
+  };
+
+  if (ntiles > 0 && wave < 4) issue_tile(0, 0);
+
+  // ---- q~ = RoPE_t(RMSNorm(q)) as the B operand: head c, dims q_dim(ks, g) + e
   // for this wave's half of the k-steps (hf*KSH ..)
   constexpr int KSH = G::KSH;
   bf16x8 qb[KSH];
   {
     float ss = 0.f;
-    const uint16_t* qp = a.q + ((int64_t)qr * a.H + min(head, a.H - 1)) * D + g * 8;
+    const uint16_t* qp = a.q + ((int64_t)qr * a.H + min(head, a.H - 1)) * D;
     u32x4 qv[G::KSTEPS];
-    f32x4 gv[KSH][2];   // gamma_q for this wave's dims, loaded with q
 #pragma unroll
-    for (int ks = 0; ks < G::KSTEPS; ++ks) qv[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 32);
-#pragma unroll
-    for (int u = 0; u < KSH; ++u) {
-      const float* gp = a.gamma_q + (hf * KSH + u) * 32 + g * 8;
-      gv[u][0] = *reinterpret_cast<const f32x4*>(gp);
-      gv[u][1] = *reinterpret_cast<const f32x4*>(gp + 4);
-    }
+    for (int ks = 0; ks < G::KSTEPS; ++ks)
+      qv[ks] = *reinterpret_cast<const u32x4*>(qp + q_dim<D>(ks, g));
     if (head >= a.H) {
 #pragma unroll
       for (int ks = 0; ks < G::KSTEPS; ++ks) qv[ks] = u32x4{0u, 0u, 0u, 0u};
@@ -245,21 +236,19 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int u = 0; u < KSH; ++u) {
       const int ks = hf * KSH + u;
-      const int d0 = ks * 32 + g * 8;
+      const int d0 = q_dim<D>(ks, g);
       u32x4 q4 = qv[0];
 #pragma unroll
       for (int kk = 0; kk < G::KSTEPS; ++kk)
         if (kk == ks) q4 = qv[kk];
       const unsigned w[4] = {q4.x, q4.y, q4.z, q4.w};
-      const float gm[8] = {gv[u][0].x, gv[u][0].y, gv[u][0].z, gv[u][0].w,
-                           gv[u][1].x, gv[u][1].y, gv[u][1].z, gv[u][1].w};
       float qf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qf[2 * e] = gm[2 * e] * (bf16_bits_to_f32(w[e] & 0xFFFFu) * rsn);
-        qf[2 * e + 1] = gm[2 * e + 1] * (bf16_bits_to_f32(w[e] >> 16) * rsn);
+        qf[2 * e] = s_gamma[d0 + 2 * e] * (bf16_bits_to_f32(w[e] & 0xFFFFu) * rsn);
+        qf[2 * e + 1] = s_gamma[d0 + 2 * e + 1] * (bf16_bits_to_f32(w[e] >> 16) * rsn);
       }
-      if (d0 >= D - R) {
+      if (ks >= G::KF) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const int i = (d0 + e - (D - R)) >> 1;
@@ -283,57 +272,124 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
 #pragma unroll
   for (int db = 0; db < G::DBH; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // per-lane LDS offsets of the transposing V^T reads (k slot j of lane group
-  // g is key 4g+j for j < 4, key 16+4g+j-4 otherwise)
-  const int jv16 = (lane & 15) >> 2;
-  const int off16a = (4 * g + jv16) * G::BSTR + 8 * (lane & 3);
-  const int off16b = (16 + 4 * g + jv16) * G::BSTR + 8 * (lane & 3);
-  const int db0 = hf * G::DBH;       // this wave's first output dim block
+  // per-lane LDS offsets within a tile (second 32-key half: + HALF)
+  //  K rows (A of S^T): row kb*16 + c, chunk 4p + g -> + 64p
+  int koff[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = kb * 16 + c;
+    koff[kb] = row * G::ROW + 16 * (g ^ swz(row));
+  }
+  //  V^T via tr_b8: source lane (g, j = (lane&15)>>1, h = lane&1) addresses
+  //  key slot j of group g, dims 16db + 8h; chunk 4a + b -> + 64a
+  int v8off[4];
+  {
+    const int j = (lane & 15) >> 1, h = lane & 1;
+    const int row = j < 4 ? 4 * g + j : 16 + 4 * g + j - 4;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) v8off[bb] = row * G::ROW + 16 * (bb ^ swz(row)) + 8 * h;
+  }
+  //  V^T via tr_b16 (bf16 dims): source lane (g, j = (lane&15)>>2, q = lane&3)
+  //  addresses keys 4g+j (lo) and 16+4g+j (hi), dims (D-R) + 16e + 4q
+  int v16off[2][2];
+  {
+    const int j = (lane & 15) >> 2, q = lane & 3;
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) {
+      const int row = hl * 16 + 4 * g + j;
+#pragma unroll
+      for (int e1 = 0; e1 < 2; ++e1)
+        v16off[hl][e1] = row * G::ROW + 16 * (G::FP8_CPR + ((2 * e1 + (q >> 1)) ^ swz(row))) +
+                         8 * (q & 1);
+    }
+  }
 
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // Tile t lives in buffer t & 1.  A tile issues the copies of tile t+1 (into
+  // the buffer every wave finished reading before the last barrier), uses
+  // tile t, waits for its own copies and meets the other waves at the
+  // barrier, so tile t+1 is complete in LDS and every read of tile t is done.
   for (int tile = 0; tile < ntiles; ++tile) {
     const int cur = tile & 1;
-    const bool more = tile + 1 < ntiles;
-    if (more) fetch_rows(tile + 1);
+    if (tile + 1 < ntiles && wave < 4) issue_tile(tile + 1, cur ^ 1);
     const uint8_t* T = s_tile[cur];
-    // partial S^T over this wave's half of the dims, both 16-key blocks
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // partial S^T over this wave's half of the k-steps, 64 keys
+    f32x4 s[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[hh][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (active) {
 #pragma unroll
-      for (int u = 0; u < KSH; ++u) {
-        const int ks = hf * KSH + u;
+      for (int u2 = 0; u2 < KSH / 2; ++u2) {
+        const int p2 = hf * (KSH / 2) + u2;   // k-step pair
+        if (p2 < G::KF / 2) {                 // E4M3 dims 64p2 .. +63
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(T + (kb * 16 + c) * G::BSTR +
-                                                          2 * (ks * 32 + g * 8));
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), qb[u],
-                                                          s[kb], 0, 0, 0);
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              const u32x4 w =
+                  *reinterpret_cast<const u32x4*>(T + koff[kb] + hh * G::HALF + 64 * p2);
+              const u32x2 a0 = fp8x4_to_bf16x4(w.x), a1 = fp8x4_to_bf16x4(w.y);
+              const u32x2 a2 = fp8x4_to_bf16x4(w.z), a3 = fp8x4_to_bf16x4(w.w);
+              s[hh][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}), qb[2 * u2], s[hh][kb],
+                  0, 0, 0);
+              s[hh][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, u32x4{a2.x, a2.y, a3.x, a3.y}), qb[2 * u2 + 1],
+                  s[hh][kb], 0, 0, 0);
+            }
+        } else {                              // the bf16 dims
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(T + koff[kb] + hh * G::HALF +
+                                                                16 * G::FP8_CPR + 64 * rr);
+                s[hh][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, w), qb[2 * u2 + rr], s[hh][kb], 0, 0, 0);
+              }
         }
       }
     }
-    s_x[wave][lane][0] = s[0];
-    s_x[wave][lane][1] = s[1];
-    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s_x[wave][2 * hh + kb][lane] = s[hh][kb];
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (active) {
       // full S: own half + partner's half (a + b == b + a, so both waves agree)
-      f32x4 sk[2];
-      sk[0] = s[0] + s_x[wave ^ 4][lane][0];
-      sk[1] = s[1] + s_x[wave ^ 4][lane][1];
-      // online softmax for head c over this lane's 8 keys: kb*16 + 4g + i
-      const unsigned vmask = __builtin_amdgcn_readfirstlane(s_valid[cur]);
-      float x[2][4];
+      unsigned vmask[2];
+      vmask[0] = __builtin_amdgcn_readfirstlane(s_v[cur][0] | (s_v[cur][1] << 16));
+      vmask[1] = __builtin_amdgcn_readfirstlane(s_v[cur][2] | (s_v[cur][3] << 16));
+      float x[2][2][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[kb][i] = sk[kb][i] * sl2;
-      if (vmask != 0xFFFFFFFFu) {   // partial tile: mask the absent rows
+        for (int kb = 0; kb < 2; ++kb) {
+          const f32x4 sk = s[hh][kb] + s_x[wave ^ 4][2 * hh + kb][lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[hh][kb][i] = sk[i] * sl2;
+        }
+      // online softmax for head c over this lane's 16 keys: 32hh + 16kb + 4g + i
+      if ((vmask[0] & vmask[1]) != 0xFFFFFFFFu) {   // partial tile: mask the absent rows
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (!((vmask[hh] >> (kb * 16 + 4 * g + i)) & 1u)) x[hh][kb][i] = -INFINITY;
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!((vmask >> (kb * 16 + 4 * g + i)) & 1u)) x[kb][i] = -INFINITY;
-      }
-      float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+          mt = fmaxf(mt, fmaxf(fmaxf(x[hh][kb][0], x[hh][kb][1]), fmaxf(x[hh][kb][2], x[hh][kb][3])));
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       // move the running max only when it grows past the headroom
@@ -345,39 +401,60 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
         for (int db = 0; db < G::DBH; ++db) o[db] *= corr;
         m_run = m_new;
       }
-      float p[2][4];
+      bf16x8 pb[2];
       float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int hh = 0; hh < 2; ++hh) {
+        float p[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = __builtin_amdgcn_exp2f(x[kb][i] - m_run);
-          ls += p[kb][i];
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[kb][i] = __builtin_amdgcn_exp2f(x[hh][kb][i] - m_run);
+            ls += p[kb][i];
+          }
+        const u32x4 pk = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                          pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+        pb[hh] = __builtin_bit_cast(bf16x8, pk);
+      }
       l_run += ls;
-      const u32x4 pk = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                        pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
-      // O^T += V^T P^T for this wave's half of the dims
+      // O^T += V^T P^T for this wave's half of the dim blocks
 #pragma unroll
       for (int u = 0; u < G::DBH; ++u) {
-        const int dofs = 2 * (db0 + u) * 16;
-        const u32x2 lo = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((V4_LDS i16x4*)(T + off16a + dofs)));
-        const u32x2 hi = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((V4_LDS i16x4*)(T + off16b + dofs)));
-        o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), pb, o[u], 0, 0, 0);
+        const int db = hf * G::DBH + u;
+        if (db < G::FB) {   // E4M3 dims
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (V4_LDS i32x2*)(T + v8off[db & 3] + hh * G::HALF + 64 * (db >> 2)));
+            const u32x2 lo = fp8x4_to_bf16x4((unsigned)v.x), hi = fp8x4_to_bf16x4((unsigned)v.y);
+            o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), pb[hh], o[u], 0, 0, 0);
+          }
+        } else {            // bf16 dims
+          const int e = db - G::FB;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const u32x2 lo = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (V4_LDS i16x4*)(T + v16off[0][e & 1] + hh * G::HALF + 64 * (e >> 1))));
+            const u32x2 hi = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (V4_LDS i16x4*)(T + v16off[1][e & 1] + hh * G::HALF + 64 * (e >> 1))));
+            o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), pb[hh], o[u], 0, 0, 0);
+          }
+        }
       }
     }
-    if (more) store_rows(tile + 1, cur ^ 1);
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   if (!active || head >= a.H) return;
   // full denominator of this lane's head: sum the four lane groups
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  const int db0 = hf * G::DBH;       // this wave's first output dim block
   if (a.splits > 1) {
     // unnormalised partial (O, max, sum); the merge kernel adds the sink
     float* po = a.part_o + (((int64_t)qr * a.splits + split) * a.H + head) * D;
@@ -424,79 +501,83 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
 }
 
 // Combine split partials with the sink, rotate by -t, store bf16 and lse.
-// Grid: (ceil(H/8), B*Tq); 256 threads; each workgroup owns 8 heads.
+// Grid: (ceil(H / HPW), B*Tq) with HPW = 1024 / D heads per workgroup of 256
+// threads.  Wave w first turns the (max, sum) pairs of heads h0 + w, h0 + w + 4,
+// .. into one weight per split (splits <= 64: one lane each); then every thread merges
+// four dims of one head, all of its split loads in flight together.
 template <int D>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a) {
   constexpr int R = 64;
+  constexpr int QPH = D / 4;          // threads per head (four dims each)
+  constexpr int HPW = 256 / QPH;      // heads per workgroup
   const int qr = blockIdx.y;
-  const int h0 = blockIdx.x * 8;
+  const int h0 = blockIdx.x * HPW;
   const int64_t t = a.q_pos0 + (qr % a.Tq);
   const int S = a.splits;
-  __shared__ float s_w[8][64];   // per head, per split weight (splits <= 64)
+  __shared__ float s_w[HPW][64];
   __shared__ float s_cs[R / 2][2];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < R / 2) {
     float cs, sn;
     rope_cos_sin(t, tid, R, a.rope_base, &cs, &sn);
     s_cs[tid][0] = cs;
     s_cs[tid][1] = sn;
   }
-  if (tid < 8) {
-    const int h = h0 + tid;
-    if (h < a.H) {
-      const float* pm = a.part_ml + ((int64_t)qr * S * a.H + h) * 2;
-      const float z2 = a.sink[h] * kLog2e;
-      float M = z2;
-      for (int s = 0; s < S; ++s) M = fmaxf(M, pm[(int64_t)s * a.H * 2]);
-      float den = M == -INFINITY ? 0.f : exp2f(z2 - M);
-      for (int s = 0; s < S; ++s) {
-        const float ms = pm[(int64_t)s * a.H * 2], ls = pm[(int64_t)s * a.H * 2 + 1];
-        const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-        s_w[tid][s] = w;
-        den += ls * w;
-      }
-      const float inv = den > 0.f ? 1.0f / den : 0.f;
-      for (int s = 0; s < S; ++s) s_w[tid][s] *= inv;
-      if (a.lse) a.lse[(int64_t)qr * a.H + h] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f
-                                                           : -INFINITY;
-    }
+  for (int hw = wave; hw < HPW; hw += 4) {
+    const int h = h0 + hw;
+    if (h >= a.H) break;
+    const float* pm = a.part_ml + ((int64_t)qr * S * a.H + h) * 2;
+    const bool own = lane < S;
+    const f32x2 ml = own ? *reinterpret_cast<const f32x2*>(pm + (int64_t)lane * a.H * 2)
+                         : f32x2{-INFINITY, 0.f};
+    const float z2 = a.sink[h] * kLog2e;
+    const float M = fmaxf(wave_max(ml.x), z2);
+    const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+    float den = wave_sum(ml.y * w);
+    if (M != -INFINITY) den += exp2f(z2 - M);
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    s_w[hw][lane] = w * inv;
+    if (a.lse && lane == 0)
+      a.lse[(int64_t)qr * a.H + h] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
   }
   __syncthreads();
-  // each thread: a pair of dims of one head per step
-  for (int e = tid; e < 8 * (D / 2); e += 256) {
-    const int hh = e / (D / 2), d = 2 * (e % (D / 2));
-    const int h = h0 + hh;
-    if (h >= a.H) continue;
-    float x0 = 0.f, x1 = 0.f;
-    const float* po = a.part_o + ((int64_t)qr * S * a.H + h) * D + d;
-    for (int s0 = 0; s0 < S; s0 += 8) {   // eight split partials in flight
-      f32x2 v[8];
+  const int hh = tid / QPH, d = 4 * (tid % QPH);
+  const int h = h0 + hh;
+  if (hh >= HPW || h >= a.H) return;
+  const float* po = a.part_o + ((int64_t)qr * S * a.H + h) * D + d;
+  const int64_t sstride = (int64_t)a.H * D;
+  f32x4 x = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {   // eight split partials in flight
+    f32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = *reinterpret_cast<const f32x2*>(po + (int64_t)min(s0 + u, S - 1) * a.H * D);
+    for (int u = 0; u < 8; ++u)
+      v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)min(s0 + u, S - 1) * sstride);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = s0 + u < S ? s_w[hh][s0 + u] : 0.f;
-        x0 = fmaf(w, v[u].x, x0);
-        x1 = fmaf(w, v[u].y, x1);
-      }
+    for (int u = 0; u < 8; ++u) {
+      const float w = s0 + u < S ? s_w[hh][s0 + u] : 0.f;
+      x += w * v[u];
     }
-    if (d >= D - R) {
-      const int i = (d - (D - R)) >> 1;
-      const float cs = s_cs[i][0], sn = s_cs[i][1];
-      const float y0 = x0 * cs + x1 * sn, y1 = -x0 * sn + x1 * cs;
-      x0 = y0;
-      x1 = y1;
-    }
-    *reinterpret_cast<unsigned*>(a.out + ((int64_t)qr * a.H + h) * D + d) = pack_bf16x2(x0, x1);
   }
+  float y[4] = {x[0], x[1], x[2], x[3]};
+  if (d >= D - R) {
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const int i = (d + e - (D - R)) >> 1;
+      const float cs = s_cs[i][0], sn = s_cs[i][1];
+      const float x0 = y[e], x1 = y[e + 1];
+      y[e] = x0 * cs + x1 * sn;       // rotation by -t
+      y[e + 1] = -x0 * sn + x1 * cs;
+    }
+  }
+  const u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  *reinterpret_cast<u32x2*>(a.out + ((int64_t)qr * a.H + h) * D + d) = pk;
 }
 
 int attend_splits(int B, int Tq, int64_t rows_max) {
   const int64_t q = (int64_t)B * Tq;
   if (q <= 0 || rows_max <= 0) return 1;
-  int64_t s = (512 + q - 1) / q;                     // about two workgroups per CU
-  const int64_t by_rows = (rows_max + 127) / 128;    // at least 128 rows per split
+  int64_t s = (256 + q - 1) / q;                               // about one workgroup per CU
+  const int64_t by_rows = (rows_max + kAttTile - 1) / kAttTile;  // at least one tile per split
   if (s > by_rows) s = by_rows;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
@@ -513,7 +594,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
     if (csa) attend_kernel<D, true><<<grid, kAttThreads, 0, st>>>(a);         \
     else attend_kernel<D, false><<<grid, kAttThreads, 0, st>>>(a);            \
     if (a.splits > 1)                                                         \
-      attend_merge_kernel<D><<<dim3((a.H + 7) / 8, (unsigned)q), 256, 0, st>>>(a); \
+      attend_merge_kernel<D><<<dim3((a.H + 1024 / (D) - 1) / (1024 / (D)), (unsigned)q), 256, 0, st>>>(a); \
   } while (0)
   switch (a.D) {
     case 128: V4_ATT(128); break;

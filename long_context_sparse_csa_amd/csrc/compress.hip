@@ -9,13 +9,14 @@
 // and why it is two mechanisms" (BF16 rotary dims, FP8 for the rest).
 //
 // Design: HBM-bound and tiny next to the attention reads (one entry per m
-// decoded tokens).  One 256-thread workgroup per entry: the 2m weights are
-// formed once per window in LDS, each of the 4 waves pools a quarter of the
-// window rows with every lane owning D/64 contiguous channels (coalesced
-// 16-byte loads at D = 512), the four partial sums meet in LDS and wave 0
-// normalises, rotates and packs the 576-byte row.  Each entry depends only on
-// its own window, so streaming (one entry per call) and batch calls produce
-// identical bytes.
+// decoded tokens), so latency matters more than bandwidth.  One 1024-thread
+// workgroup per entry: the 2m weights are formed once per window in LDS, each
+// of the 16 waves pools every 16th window row with every lane owning D/64
+// contiguous channels (coalesced 16-byte loads at D = 512, eight rows in
+// flight per wave, so a 256-row window is two rounds of loads), the partial
+// sums meet in LDS and wave 0 normalises, rotates and packs the 576-byte row.
+// Each entry depends only on its own window, so streaming (one entry per
+// call) and batch calls produce identical bytes.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -100,8 +101,11 @@ __device__ __forceinline__ void rmsnorm_wave(float (&y)[VPL], const float* __res
   for (int v = 0; v < VPL; ++v) y[v] = gamma[lane * VPL + v] * (y[v] * rs);
 }
 
+constexpr int kPoolThreads = 1024;   // sixteen waves pool one entry's window
+constexpr int kPoolWaves = kPoolThreads / 64;
+
 template <int VPL>
-__global__ __launch_bounds__(256) void compress_pool_kernel(
+__global__ __launch_bounds__(kPoolThreads) void compress_pool_kernel(
     const uint16_t* __restrict__ raw, const float* __restrict__ score,
     const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
     int64_t raw_pos0, int m, int64_t entry0, float eps, float rope_base,
@@ -111,8 +115,8 @@ __global__ __launch_bounds__(256) void compress_pool_kernel(
   const int64_t j = entry0 + blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float s_alpha[512];
-  __shared__ float s_part[4][D];
-  __shared__ float s_red[2][4];
+  __shared__ float s_part[kPoolWaves][D];
+  __shared__ float s_red[2][kPoolWaves];
 
   const int64_t wlo = (j - 1) * (int64_t)m;  // window start; may be negative
   const int64_t plo = wlo > 0 ? wlo : 0;       // first existing position
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(256) void compress_pool_kernel(
 
   // weights alpha_t = softmax over the window of (s_t + b_{t - wlo})
   float mx = -INFINITY;
-  for (int t = tid; t < nw; t += 256) {
+  for (int t = tid; t < nw; t += kPoolThreads) {
     const float lg = srow[t] + bias[plo - wlo + t];
     s_alpha[t] = lg;
     mx = fmaxf(mx, lg);
@@ -130,9 +134,11 @@ __global__ __launch_bounds__(256) void compress_pool_kernel(
   mx = wave_max(mx);
   if (lane == 0) s_red[0][wave] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kPoolWaves; ++w) mx = fmaxf(mx, s_red[0][w]);
   float sum = 0.f;
-  for (int t = tid; t < nw; t += 256) {
+  for (int t = tid; t < nw; t += kPoolThreads) {
     const float e = expf(s_alpha[t] - mx);
     s_alpha[t] = e;
     sum += e;
@@ -140,9 +146,12 @@ __global__ __launch_bounds__(256) void compress_pool_kernel(
   sum = wave_sum(sum);
   if (lane == 0) s_red[1][wave] = sum;
   __syncthreads();
-  const float inv = 1.0f / ((s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]));
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kPoolWaves; ++w) tot += s_red[1][w];
+  const float inv = 1.0f / tot;
 
-  // pooled = sum_t alpha_t c_t : wave w takes rows w, w+4, ...
+  // pooled = sum_t alpha_t c_t : wave w takes rows w, w+16, ...
   float acc[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
@@ -151,16 +160,16 @@ __global__ __launch_bounds__(256) void compress_pool_kernel(
   const uint16_t* base = raw + ((int64_t)b * L + r0) * D + lane * VPL;
   // (loads are unconditional -- rows past the window re-read the last row
   // with weight 0 -- so the compiler keeps the whole batch in flight)
-  for (int t0 = wave; t0 < nw; t0 += 4 * U) {
+  for (int t0 = wave; t0 < nw; t0 += kPoolWaves * U) {
     float x[U][VPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = min(t0 + 4 * u, nw - 1);
+      const int t = min(t0 + kPoolWaves * u, nw - 1);
       load_bf16_row<VPL>(base + (int64_t)t * D, x[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = t0 + 4 * u;
+      const int t = t0 + kPoolWaves * u;
       const float a = t < nw ? s_alpha[t] : 0.f;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, x[u][v], acc[v]);
@@ -175,7 +184,10 @@ __global__ __launch_bounds__(256) void compress_pool_kernel(
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int d = lane * VPL + v;
-    y[v] = ((s_part[0][d] + s_part[1][d]) + (s_part[2][d] + s_part[3][d])) * inv;
+    float z = 0.f;
+#pragma unroll
+    for (int w = 0; w < kPoolWaves; ++w) z += s_part[w][d];
+    y[v] = z * inv;
   }
   rmsnorm_wave<VPL>(y, gamma, lane, eps);
   uint8_t* row = out + ((int64_t)b * out_rows + blockIdx.x) * (D + R);
@@ -205,7 +217,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   if (a.mode == 0) {
     dim3 grid(a.n_out, a.B);
 #define V4_POOL(VPL)                                                                       \
-  compress_pool_kernel<VPL><<<grid, 256, 0, st>>>(a.raw, a.tok_score, a.pos_bias, a.gamma,  \
+  compress_pool_kernel<VPL><<<grid, kPoolThreads, 0, st>>>(a.raw, a.tok_score, a.pos_bias, a.gamma,  \
                                                   a.L, a.R, a.raw_pos0, a.m, a.entry0,     \
                                                   a.eps, a.rope_base, a.out, a.out_rows)
     switch (a.D) {
