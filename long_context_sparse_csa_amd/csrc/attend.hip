@@ -40,6 +40,8 @@
 // 2^8 (probabilities stay below 256, exact enough in bf16 and fp32), which
 // skips almost every rescale.  Long rows are split over several workgroups
 // whose (O, max, sum) partials a merge kernel combines with the sink.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -61,16 +63,17 @@ struct AttGeom {
   static constexpr int CPR = ROW / 16;         // 16-byte chunks per row
   static constexpr int FP8_CPR = (D - R) / 16; // of which E4M3
   static constexpr int KSTEPS = D / 32;        // 32-dim k-steps of S^T
-  static constexpr int KF = (D - R) / 32;      // of which over E4M3 dims
+  static constexpr int NF8 = (D - 128) / 128;  // 128-dim E4M3 k-steps on the f8f6f4 MFMA
+  static constexpr int NF0 = (NF8 + 1) / 2;    // of which in dim half 0
+  static constexpr int TAIL = D - 128;         // first dim of the bf16-MFMA tail
+  static_assert(D % 128 == 0, "head dim is a multiple of 128");
   static constexpr int DB = D / 16;            // 16-dim blocks of O^T
   static constexpr int FB = (D - R) / 16;      // of which over E4M3 dims
   static constexpr int TILE_BYTES = kAttTile * ROW;
-  static constexpr int KSH = KSTEPS / 2;       // k-steps per dim half
   static constexpr int DBH = DB / 2;           // output blocks per dim half
   static constexpr int WPW = CPR / 4;          // 1 KiB copies per staging wave per tile (16 rows)
   static constexpr int HALF = 32 * ROW;        // byte offset of the second 32-key half
   static_assert(FP8_CPR % 4 == 0 && CPR % 4 == 0, "the chunk swizzle stays inside a region");
-  static_assert(KSH % 2 == 0, "k-step pairs do not straddle the dim halves");
   static_assert(ROW <= 1024, "absent rows read the zero row");
 };
 
@@ -109,15 +112,6 @@ __device__ __forceinline__ RowSpace row_space(const AttendArgs& a, bool csa, int
   const int64_t n_win = a.W > 0 ? (t - rs.win_lo + 1) : 0;
   rs.n_rows = rs.n_ent + n_win;
   return rs;
-}
-
-// q~ dims of k-step ks for lane group g, in the order the lanes read K rows:
-// E4M3 k-step pairs take 16 contiguous dims per lane group (one 16-byte chunk
-// read covers two k-steps), the bf16 k-steps 8 contiguous dims.
-template <int D>
-__device__ __forceinline__ int q_dim(int ks, int g) {
-  using G = AttGeom<D>;
-  return ks < G::KF ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : (D - G::R) + 32 * (ks - G::KF) + 8 * g;
 }
 
 template <int D, bool CSA>
@@ -206,24 +200,37 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
 
   if (ntiles > 0 && wave < 4) issue_tile(0, 0);
 
-  // ---- q~ = RoPE_t(RMSNorm(q)) as the B operand: head c, dims q_dim(ks, g) + e
-  // for this wave's half of the k-steps (hf*KSH ..)
-  constexpr int KSH = G::KSH;
-  bf16x8 qb[KSH];
+  // ---- q~ = RoPE_t(RMSNorm(q)) scaled by 2^qe (per head, exact), as the B
+  // operand of S^T.  The E4M3 dims run on the f8f6f4 MFMA with q~ split into
+  // two E4M3 terms (hi + lo: about 2^-8 relative, the scale keeps the lo term
+  // out of the subnormals); the last 64 E4M3 dims and the bf16 dims run on
+  // the bf16 MFMA.  Lane group g owns 8-dim slots: per f8 k-step s the dims
+  // 128s + 32g .. +31 (slots 4s .. 4s+3), then four tail slots t with dims
+  // TAIL + 32t + 8g .. +7 (E4M3 for t < 2, bf16 for t = 2, 3).  Dim half 0
+  // contracts f8 k-steps [0, NF0) and the bf16 tail, half 1 the f8 k-steps
+  // [NF0, NF8) and the E4M3 tail.
+  constexpr int NF8 = G::NF8, NF0 = G::NF0, TAIL = G::TAIL;
+  constexpr int NQ = NF0 > 0 ? NF0 : 1;
+  i32x8 qh[NQ], ql[NQ];
+  bf16x8 qt[2];
+  float qscale_inv;   // 2^-qe
   {
-    float ss = 0.f;
+    auto slot_dim = [&](int sl) {
+      return sl < 4 * NF8 ? 128 * (sl >> 2) + 32 * g + 8 * (sl & 3) : TAIL + 32 * (sl - 4 * NF8) + 8 * g;
+    };
     const uint16_t* qp = a.q + ((int64_t)qr * a.H + min(head, a.H - 1)) * D;
     u32x4 qv[G::KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < G::KSTEPS; ++ks)
-      qv[ks] = *reinterpret_cast<const u32x4*>(qp + q_dim<D>(ks, g));
+    for (int sl = 0; sl < G::KSTEPS; ++sl)
+      qv[sl] = *reinterpret_cast<const u32x4*>(qp + slot_dim(sl));
     if (head >= a.H) {
 #pragma unroll
-      for (int ks = 0; ks < G::KSTEPS; ++ks) qv[ks] = u32x4{0u, 0u, 0u, 0u};
+      for (int sl = 0; sl < G::KSTEPS; ++sl) qv[sl] = u32x4{0u, 0u, 0u, 0u};
     }
+    float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < G::KSTEPS; ++ks) {
-      const unsigned w[4] = {qv[ks].x, qv[ks].y, qv[ks].z, qv[ks].w};
+    for (int sl = 0; sl < G::KSTEPS; ++sl) {
+      const unsigned w[4] = {qv[sl].x, qv[sl].y, qv[sl].z, qv[sl].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = bf16_bits_to_f32(w[e] & 0xFFFFu), hi = bf16_bits_to_f32(w[e] >> 16);
@@ -233,22 +240,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
     const float rsn = 1.0f / sqrtf(ss / (float)D + a.eps);
-#pragma unroll
-    for (int u = 0; u < KSH; ++u) {
-      const int ks = hf * KSH + u;
-      const int d0 = q_dim<D>(ks, g);
-      u32x4 q4 = qv[0];
-#pragma unroll
-      for (int kk = 0; kk < G::KSTEPS; ++kk)
-        if (kk == ks) q4 = qv[kk];
-      const unsigned w[4] = {q4.x, q4.y, q4.z, q4.w};
-      float qf[8];
+    // q~ of one slot (8 dims), rotated where the dims are rotary
+    auto qtilde = [&](int sl, float (&qf)[8]) {
+      const int d0 = slot_dim(sl);
+      const unsigned w[4] = {qv[sl].x, qv[sl].y, qv[sl].z, qv[sl].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         qf[2 * e] = s_gamma[d0 + 2 * e] * (bf16_bits_to_f32(w[e] & 0xFFFFu) * rsn);
         qf[2 * e + 1] = s_gamma[d0 + 2 * e + 1] * (bf16_bits_to_f32(w[e] >> 16) * rsn);
       }
-      if (ks >= G::KF) {
+      if (d0 >= D - R) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const int i = (d0 + e - (D - R)) >> 1;
@@ -258,13 +259,67 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
           qf[e + 1] = x0 * sn + x1 * cs;
         }
       }
-      u32x4 pk = {pack_bf16x2(qf[0], qf[1]), pack_bf16x2(qf[2], qf[3]),
-                  pack_bf16x2(qf[4], qf[5]), pack_bf16x2(qf[6], qf[7])};
-      qb[u] = __builtin_bit_cast(bf16x8, pk);
+    };
+    // per-head scale: the largest |q~| lands in [128, 256)
+    float mx = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < G::KSTEPS; ++sl) {
+      float qf[8];
+      qtilde(sl, qf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qf[e]));
     }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const int qe = mx > 0.f ? 8 - __builtin_amdgcn_frexp_expf(mx) : 0;
+    qscale_inv = ldexpf(1.0f, -qe);
+    // The operands of this wave's half; the half is a compile-time constant
+    // inside so that every slot index is one (no run-time register indexing).
+    auto build = [&](auto half) {
+      constexpr int HF = decltype(half)::value;
+      // f8 k-steps: hi and lo E4M3 terms, 4 bytes per dword in dim order
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int s8 = HF == 0 ? u : NF0 + u;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float qf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if (s8 < NF8) qtilde(4 * s8 + v, qf);
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = ldexpf(qf[4 * h2 + e], qe);
+            int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+            hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
+            const float r[4] = {x[0] - __builtin_amdgcn_cvt_f32_fp8(hw, 0),
+                                x[1] - __builtin_amdgcn_cvt_f32_fp8(hw, 1),
+                                x[2] - __builtin_amdgcn_cvt_f32_fp8(hw, 2),
+                                x[3] - __builtin_amdgcn_cvt_f32_fp8(hw, 3)};
+            int lw = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+            lw = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], lw, true);
+            qh[u][2 * v + h2] = hw;
+            ql[u][2 * v + h2] = lw;
+          }
+        }
+      }
+      // tail k-steps: half 0 the bf16 dims (t = 2, 3), half 1 the E4M3 tail (t = 0, 1)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        float qf[8];
+        qtilde(4 * NF8 + (HF == 0 ? 2 : 0) + t2, qf);
+        u32x4 pk = {pack_bf16x2(ldexpf(qf[0], qe), ldexpf(qf[1], qe)),
+                    pack_bf16x2(ldexpf(qf[2], qe), ldexpf(qf[3], qe)),
+                    pack_bf16x2(ldexpf(qf[4], qe), ldexpf(qf[5], qe)),
+                    pack_bf16x2(ldexpf(qf[6], qe), ldexpf(qf[7], qe))};
+        qt[t2] = __builtin_bit_cast(bf16x8, pk);
+      }
+    };
+    if (hf == 0) build(std::integral_constant<int, 0>{});
+    else build(std::integral_constant<int, 1>{});
   }
 
-  const float sl2 = a.scale * kLog2e;
+  const float sl2 = a.scale * kLog2e * qscale_inv;   // undoes the q~ scale
   // running max starts at a finite floor, so masked keys (-inf) give p = 0
   // without special cases; an untouched max marks "no row seen"
   float m_run = kNoMax, l_run = 0.f;  // per head (lane column), log2 units
@@ -273,12 +328,25 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
   for (int db = 0; db < G::DBH; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // per-lane LDS offsets within a tile (second 32-key half: + HALF)
-  //  K rows (A of S^T): row kb*16 + c, chunk 4p + g -> + 64p
+  //  K rows of the bf16 tail (A of S^T): row kb*16 + c, chunk FP8_CPR + 4t + g
   int koff[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int row = kb * 16 + c;
     koff[kb] = row * G::ROW + 16 * (g ^ swz(row));
+  }
+  //  K rows for the f8f6f4 k-steps: chunks 8s + 2g + i (i = 0, 1) -> + 128s
+  int koff8[2][2];
+  //  K rows for the E4M3 tail: dims TAIL + 32t + 8g, 8 bytes
+  int ktoff[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = kb * 16 + c, sw = swz(row);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) koff8[kb][i] = row * G::ROW + 16 * ((2 * g + i) ^ sw);
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+      ktoff[kb][t2] = row * G::ROW + 16 * (TAIL / 16 + ((2 * t2 + (g >> 1)) ^ sw)) + 8 * (g & 1);
   }
   //  V^T via tr_b8: source lane (g, j = (lane&15)>>1, h = lane&1) addresses
   //  key slot j of group g, dims 16db + 8h; chunk 4a + b -> + 64a
@@ -321,38 +389,50 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[hh][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (active) {
+      // f8f6f4 k-steps of this half: K straight from the tile, q~ as hi + lo
 #pragma unroll
-      for (int u2 = 0; u2 < KSH / 2; ++u2) {
-        const int p2 = hf * (KSH / 2) + u2;   // k-step pair
-        if (p2 < G::KF / 2) {                 // E4M3 dims 64p2 .. +63
+      for (int u = 0; u < NQ; ++u) {
+        const int s8 = hf == 0 ? u : NF0 + u;
+        if (s8 < NF8 && (hf == 1 || u < NF0)) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-              const u32x4 w =
-                  *reinterpret_cast<const u32x4*>(T + koff[kb] + hh * G::HALF + 64 * p2);
-              const u32x2 a0 = fp8x4_to_bf16x4(w.x), a1 = fp8x4_to_bf16x4(w.y);
-              const u32x2 a2 = fp8x4_to_bf16x4(w.z), a3 = fp8x4_to_bf16x4(w.w);
-              s[hh][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}), qb[2 * u2], s[hh][kb],
-                  0, 0, 0);
-              s[hh][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, u32x4{a2.x, a2.y, a3.x, a3.y}), qb[2 * u2 + 1],
-                  s[hh][kb], 0, 0, 0);
+              const u32x4 w0 = *reinterpret_cast<const u32x4*>(T + koff8[kb][0] + hh * G::HALF + 128 * s8);
+              const u32x4 w1 = *reinterpret_cast<const u32x4*>(T + koff8[kb][1] + hh * G::HALF + 128 * s8);
+              const i32x8 ka = __builtin_bit_cast(
+                  i32x8, u32x8{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w});
+              s[hh][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qh[u], s[hh][kb], 0, 0, 0,
+                                                                           127, 0, 127);
+              s[hh][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, ql[u], s[hh][kb], 0, 0, 0,
+                                                                           127, 0, 127);
             }
-        } else {                              // the bf16 dims
-#pragma unroll
-          for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-              for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 w = *reinterpret_cast<const u32x4*>(T + koff[kb] + hh * G::HALF +
-                                                                16 * G::FP8_CPR + 64 * rr);
-                s[hh][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, w), qb[2 * u2 + rr], s[hh][kb], 0, 0, 0);
-              }
         }
+      }
+      if (hf == 0) {   // bf16 (rotary) dims
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              const u32x4 w = *reinterpret_cast<const u32x4*>(T + koff[kb] + hh * G::HALF +
+                                                              16 * G::FP8_CPR + 64 * t2);
+              s[hh][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), qt[t2],
+                                                                  s[hh][kb], 0, 0, 0);
+            }
+      } else {         // E4M3 tail, widened to bf16
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              const u32x2 w = *reinterpret_cast<const u32x2*>(T + ktoff[kb][t2] + hh * G::HALF);
+              const u32x2 lo = fp8x4_to_bf16x4(w.x), hi = fp8x4_to_bf16x4(w.y);
+              s[hh][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), qt[t2], s[hh][kb], 0, 0, 0);
+            }
       }
     }
 #pragma unroll

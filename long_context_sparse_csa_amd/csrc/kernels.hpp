@@ -35,9 +35,9 @@ struct IndexScoreArgs {
   int64_t vmax;           // max visible entries over the query block
   float* scores;          // [B*Tq, score_stride]
   int64_t score_stride;
-  int64_t keys_per_wave;  // contiguous keys one wave scores (multiple of 64)
+  int64_t keys_per_wave;  // contiguous keys one wave scores (multiple of 32)
 };
-// Keys per wave that spread a launch over about two waves per SIMD.
+// Keys per wave that spread a launch over three workgroups per CU.
 int64_t index_keys_per_wave(int B, int Tq, int64_t vmax);
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t st);
 
