@@ -54,18 +54,24 @@ int64_t vmax_of(int Tq, int64_t n_entries, int64_t q_pos0, int m) {
 }
 
 struct TopkWs {
-  size_t cand_bytes, total;
   v4::TopkPlan plan;
+  size_t part_bytes, cand_bytes, run_bytes, total;
 };
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 TopkWs topk_ws(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m, int k) {
   TopkWs w;
   const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
-  w.plan = v4::topk_plan(vmax, k);
+  w.plan = v4::topk_plan(vmax);
   const int64_t rows = (int64_t)B * Tq;
-  w.cand_bytes = (size_t)(rows * w.plan.cand_elems) * sizeof(unsigned);
-  w.cand_bytes = (w.cand_bytes + 255) / 256 * 256;
-  w.total = 4 * w.cand_bytes;  // two (key, index) buffers
+  const int64_t np = w.plan.nparts;
+  w.part_bytes = align256((size_t)(rows * np) * sizeof(int));
+  w.cand_bytes = align256((size_t)(rows * np * v4::kTopkPartCap) * sizeof(int));
+  w.run_bytes = align256((size_t)(rows * k) * sizeof(unsigned));
+  // part thresholds, counts and overflow maxima, leader keys and indices,
+  // partial-selection keys
+  w.total = w.plan.parts ? 3 * w.part_bytes + 2 * w.cand_bytes + w.run_bytes : 0;
   return w;
 }
 
@@ -187,6 +193,16 @@ size_t v4attn_topk_select_workspace(int B, int Tq, int64_t n_entries, int64_t q_
 
 namespace {
 
+// The selector keeps one offset per 1024-entry part of a row in LDS.
+int check_topk_len(int Tq, int64_t n_entries, int64_t q_pos0, int m) {
+  const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
+  const int64_t lim = (int64_t)v4::kTopkMaxParts * v4::kTopkPartLen;
+  if (vmax > lim)
+    return fail(V4ATTN_EUNSUPPORTED, "%lld visible entries: at most %lld per query are built",
+                (long long)vmax, (long long)lim);
+  return V4ATTN_OK;
+}
+
 int check_index_common(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m) {
   if (B < 0 || Tq < 0) return fail(V4ATTN_EINVAL, "negative B or Tq");
   if (n_entries < 0) return fail(V4ATTN_EINVAL, "negative n_entries");
@@ -233,11 +249,20 @@ hipError_t run_topk(const float* scores, int64_t stride, int B, int Tq, int64_t 
   ta.q_pos0 = q_pos0;
   ta.m = m;
   ta.k = k;
-  ta.vmax = vmax_of(Tq, n_entries, q_pos0, m);
-  ta.cand_key[0] = reinterpret_cast<unsigned*>(cb);
-  ta.cand_idx[0] = reinterpret_cast<int*>(cb + w.cand_bytes);
-  ta.cand_key[1] = reinterpret_cast<unsigned*>(cb + 2 * w.cand_bytes);
-  ta.cand_idx[1] = reinterpret_cast<int*>(cb + 3 * w.cand_bytes);
+  ta.nparts = w.plan.nparts;
+  ta.part_tau = ta.part_over = nullptr;
+  ta.part_cnt = nullptr;
+  ta.cand_key = ta.run_key = nullptr;
+  ta.cand_idx = nullptr;
+  if (w.plan.parts) {
+    ta.part_tau = reinterpret_cast<unsigned*>(cb);
+    ta.part_cnt = reinterpret_cast<int*>(cb + w.part_bytes);
+    ta.part_over = reinterpret_cast<unsigned*>(cb + 2 * w.part_bytes);
+    uint8_t* c2 = cb + 3 * w.part_bytes;
+    ta.cand_key = reinterpret_cast<unsigned*>(c2);
+    ta.cand_idx = reinterpret_cast<int*>(c2 + w.cand_bytes);
+    ta.run_key = reinterpret_cast<unsigned*>(c2 + 2 * w.cand_bytes);
+  }
   ta.topk = topk;
   ta.topk_score = topk_score;
   return v4::launch_topk(ta, w.plan, st);
@@ -265,6 +290,7 @@ int v4attn_topk_select(const float* scores, int64_t score_stride, int B, int Tq,
   if (!topk) return fail(V4ATTN_EINVAL, "null topk");
   if (int st = check_index_common(B, Tq, n_entries, q_pos0, m)) return st;
   if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
+  if (int st = check_topk_len(Tq, n_entries, q_pos0, m)) return st;
   const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
   if (vmax > 0 && (!scores || score_stride < vmax))
     return fail(V4ATTN_EINVAL, "scores missing or score_stride %lld < %lld",
@@ -287,6 +313,7 @@ int v4attn_index_topk(const uint16_t* q_idx, const float* w_idx, const uint16_t*
     return st;
   if (!topk) return fail(V4ATTN_EINVAL, "null topk");
   if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
+  if (int st = check_topk_len(Tq, n_entries, q_pos0, m)) return st;
   const IndexWs w = index_ws(B, Tq, n_entries, q_pos0, m, k);
   if (w.total > 0 && (!ws || ws_bytes < w.total))
     return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);

@@ -74,12 +74,14 @@ __device__ __forceinline__ float fp8_to_f32(unsigned code) {
 // near 2^20 keep full fp32 accuracy.
 __device__ __forceinline__ void rope_cos_sin(int64_t pos, int i, int R, float base,
                                              float* c, float* s) {
-  double theta = exp2(-(2.0 * i / R) * log2((double)base));
-  double ang = (double)pos * theta;
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
+  // angle = pos * base^(-2i/R).  It is carried in turns (angle / 2 pi) in
+  // fp64, whose fraction is exact to ~1e-11 turns at a million positions,
+  // and only the reduced angle in [-pi, pi] goes through the fp32 sincos
+  // (about 1e-7 rad), which avoids the large-argument fp64 sincos path.
+  const double theta = exp2(-(2.0 * i / R) * log2((double)base));
+  const double turns = (double)pos * (theta * 0.15915494309189533577);
+  const float r = (float)((turns - rint(turns)) * 6.283185307179586477);
+  sincosf(r, s, c);
 }
 
 template <typename T>

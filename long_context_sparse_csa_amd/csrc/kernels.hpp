@@ -41,15 +41,17 @@ struct IndexScoreArgs {
 int64_t index_keys_per_wave(int B, int Tq, int64_t vmax);
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t st);
 
-// Top-k selection: multi-stage reduction of per-part candidates.
-constexpr int kTopkPart = 16384;  // elements one workgroup selects from in LDS
+// Top-k selection: per-part leaders -> exact per-row select.
+constexpr int kTopkSel = 16384;     // keys the per-row selection holds in LDS
+constexpr int kTopkPartLen = 1024;  // scores per part
+constexpr int kTopkPartCap = 32;    // leaders a part stores
+constexpr int kTopkMaxParts = 4096; // parts per row (entries <= 4M)
 
 struct TopkPlan {
-  int stages;        // number of selection passes (>= 1)
-  int64_t parts0;    // parts of the first pass
-  int64_t cand_elems;  // elements of one candidate buffer (keys and indices)
+  bool parts;        // rows longer than kTopkSel exist: run the part kernel
+  int nparts;        // parts per row (of the longest row)
 };
-TopkPlan topk_plan(int64_t vmax, int k);
+TopkPlan topk_plan(int64_t vmax);
 
 struct TopkArgs {
   const float* scores;     // [B*Tq, score_stride]
@@ -57,9 +59,13 @@ struct TopkArgs {
   int B, Tq;
   int64_t n_entries, q_pos0;
   int m, k;
-  int64_t vmax;
-  unsigned* cand_key[2];   // ping-pong candidate buffers
-  int* cand_idx[2];
+  int nparts;
+  unsigned* part_tau;      // [rows, nparts] the part's leader threshold (0: none)
+  int* part_cnt;           // [rows, nparts] keys >= it in the part
+  unsigned* part_over;     // [rows, nparts] largest of them not stored (0: none)
+  unsigned* cand_key;      // [rows, nparts, kTopkPartCap] the stored ones, position order
+  int* cand_idx;
+  unsigned* run_key;       // [rows, k] keys of a partial selection
   int32_t* topk;           // [B*Tq, k]
   float* topk_score;       // nullable
 };

@@ -6,43 +6,58 @@
 // explained", step 4).  Below the budget nothing is dropped ("DeepSeek-V4,
 // explained", introduction).
 //
-// Design: exact selection in LDS, no sorting.  Scores map to order-preserving
-// 32-bit keys.  A workgroup loads up to 16384 keys of one query into LDS and
-// runs a bucket select: each pass bins the live key range [lo, hi] linearly
-// into at most 2048 LDS-atomic buckets (starting from the part's actual min
-// and max, so a clustered score distribution still spreads over the buckets
-// instead of piling onto a few exponent bins), keeps the bucket holding the
-// k-th key and stops when it is one key wide or needed whole -- at most three
-// passes for 32-bit keys.  A stream compaction in position order then writes every key above
-// tau and the lowest-positioned ties, so the output comes out in ascending
-// index order without a sort.  Longer rows are cut into parts: the union of
-// the parts' exact top-k always contains the row's top-k, so a second pass
-// over the candidates (at most 16384 for a million-token context) finishes
-// the job.  Candidates keep position order, which keeps the tie rule exact.
+// Design: exact selection, no sorting.  Scores map to order-preserving
+// 32-bit keys (NaN -> 0, never selected).  A row of up to 16384 keys is
+// selected by one workgroup in LDS.  A longer row is first cut into parts of
+// 1024 scores, one wave each, over the whole chip: each part takes as its
+// threshold x_p the 16th largest of its 64 lane maxima (a bitwise search over
+// one ballot per bit; x_p is at most the part's 16th largest key) and stores
+// its keys >= x_p in position order, at most 32, recording the largest key it
+// had to leave out.  The per-row workgroup then
+//   1. selects the top-k of the stored keys (in position order); their k-th
+//      largest lo, the k-th largest of a subset of the row, is <= the row's
+//      k-th largest;
+//   2. checks every part: one with x_p <= lo that left out no key >= lo
+//      stored every key >= lo.  If every part passes (the usual case: a part
+//      rarely holds dozens of the row's top 1024) the selection is the
+//      answer;
+//   3. otherwise selects again over the stored keys of the complete parts and
+//      every key >= lo of the others (re-read), which contains the row's
+//      top-k.
+// More than 16384 candidates are taken in chunks: the top-k of what has been
+// seen so far is kept and merged with the next chunk, which keeps position
+// order and so the tie rule.  The exact selection is a bucket select: each
+// pass bins the live key range [lo, hi] linearly into at most 2048 LDS-atomic
+// buckets (from the actual min and max, so clustered scores still spread),
+// keeps the bucket holding the k-th key and stops when it is one key wide or
+// needed whole -- at most three passes for 32-bit keys; a position-ordered
+// stream compaction then writes every key above the bucket and the
+// lowest-positioned keys inside it, so the output comes out in ascending
+// index order.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace v4 {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 2048;
-constexpr int kTopkRounds = kTopkPart / kTopkThreads;
-static_assert(kTopkRounds * kTopkWaves <= kTopkThreads, "one scan entry per thread");
+constexpr int kSelRounds = kTopkSel / kSelThreads;
+static_assert(kSelRounds * kSelWaves <= kSelThreads, "one scan entry per thread");
+constexpr int kBucketsPerThread = kHistBins / kSelThreads;
+static_assert(kTopkPartLen == 16 * 64, "a part is 16 keys per lane of one wave");
 
-TopkPlan topk_plan(int64_t vmax, int k) {
+TopkPlan topk_plan(int64_t vmax) {
   TopkPlan p;
-  p.parts0 = vmax > 0 ? (vmax + kTopkPart - 1) / kTopkPart : 1;
-  p.stages = 1;
-  int64_t parts = p.parts0;
-  p.cand_elems = 0;
-  while (parts > 1) {
-    const int64_t n = parts * (int64_t)k;
-    if (n > p.cand_elems) p.cand_elems = n;
-    parts = (n + kTopkPart - 1) / kTopkPart;
-    p.stages++;
-  }
+  p.parts = vmax > kTopkSel;
+  p.nparts = p.parts ? (int)((vmax + kTopkPartLen - 1) / kTopkPartLen) : 0;
   return p;
+}
+
+__device__ __forceinline__ int64_t visible_of(const TopkArgs& a, int64_t qr) {
+  const int64_t t = a.q_pos0 + (qr % a.Tq);
+  const int64_t v = (t + 1) / a.m;
+  return v < a.n_entries ? v : a.n_entries;
 }
 
 // Exclusive scan of one value per thread across the block; returns the
@@ -59,7 +74,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < kSelWaves; ++w) {
     const int s = s_wave[w];
     before += (w < wave) ? s : 0;
     all += s;
@@ -79,249 +94,404 @@ __device__ __forceinline__ unsigned wave_max_u(unsigned v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o));
   return v;
 }
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
 
-template <bool FIRST>
-__global__ __launch_bounds__(kTopkThreads) void topk_stage_kernel(
-    const float* __restrict__ scores, int64_t score_stride, const unsigned* __restrict__ in_key,
-    const int* __restrict__ in_idx, int64_t in_stride, int Tq, int64_t n_entries,
-    int64_t q_pos0, int m, int k, int last, unsigned* __restrict__ out_key,
-    int* __restrict__ out_idx, int64_t out_stride, int32_t* __restrict__ topk,
-    float* __restrict__ topk_score) {
+// The 16 keys of lane `lane` in the part starting at `base` of row qr:
+// positions base + 64r + lane (absent past the row's visible entries).
+__device__ __forceinline__ void load_part(const TopkArgs& a, int64_t qr, int64_t V, int64_t base,
+                                          int lane, unsigned (&key)[16]) {
+  const float* src = a.scores + qr * a.score_stride;
+  float f[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t i = base + 64 * r + lane;
+    f[r] = src[i < V ? i : (V > 0 ? V - 1 : 0)];
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) key[r] = base + 64 * r + lane < V ? score_key(f[r]) : 0u;
+}
+
+// ---- part leaders: x_p = the 16th largest lane maximum (0 if fewer than 16
+// lanes hold a valid key), then the part's keys >= max(x_p, 1) in position
+// order, the first kTopkPartCap stored, the largest of the rest recorded.
+__global__ __launch_bounds__(256) void topk_part_kernel(TopkArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t qr = blockIdx.y;
+  const int p = blockIdx.x * 4 + wave;
+  if (p >= a.nparts) return;
+  const int64_t V = visible_of(a, qr);
+  if (V <= kTopkSel) return;   // such a row is selected directly
+  const int64_t base = (int64_t)p * kTopkPartLen;
+  unsigned x = 0u, over = 0u;
+  int cnt = 0;
+  if (base < V) {
+    unsigned key[16];
+    load_part(a, qr, V, base, lane, key);
+    unsigned lmax = 0u;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lmax = max(lmax, key[r]);
+    // largest x with at least 16 lane maxima >= x, one bit at a time
+    for (int bit = 31; bit >= 0; --bit) {
+      const unsigned cand = x | (1u << bit);
+      if (__popcll(__ballot(lmax >= cand)) >= 16) x = cand;
+    }
+    const unsigned thr = x > 0u ? x : 1u;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    unsigned* ck = a.cand_key + ((int64_t)qr * a.nparts + p) * kTopkPartCap;
+    int* ci = a.cand_idx + ((int64_t)qr * a.nparts + p) * kTopkPartCap;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool pass = key[r] >= thr;
+      const unsigned long long bl = __ballot(pass);
+      const int pos = cnt + __popcll(bl & lt);
+      if (pass && pos < kTopkPartCap) {
+        ck[pos] = key[r];
+        ci[pos] = (int)(base + 64 * r + lane);
+      } else if (pass) {
+        over = max(over, key[r]);
+      }
+      cnt += __popcll(bl);
+    }
+    over = wave_max_u(over);
+  }
+  if (lane == 0) {
+    a.part_tau[qr * a.nparts + p] = x;
+    a.part_cnt[qr * a.nparts + p] = cnt;
+    a.part_over[qr * a.nparts + p] = over;
+  }
+}
+
+// ---- select: exact top-k of one row in LDS
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   extern __shared__ unsigned smem[];
-  unsigned* s_key = smem;                                   // [kTopkPart]
-  unsigned* s_hist = smem + kTopkPart;                      // [kHistBins]
-  int* s_idx = reinterpret_cast<int*>(s_hist + kHistBins);  // [kTopkPart] (!FIRST)
-  __shared__ int s_wave[kTopkWaves];
-  __shared__ unsigned s_mm[2][kTopkWaves];
-  __shared__ int s_blk[2][kTopkRounds * kTopkWaves];  // per (round, wave) block
+  unsigned* s_key = smem;                                   // [kTopkSel]
+  unsigned* s_hist = smem + kTopkSel;                       // [kHistBins]
+  int* s_idx = reinterpret_cast<int*>(s_hist + kHistBins);  // [kTopkSel]
+  int* s_off = s_idx + kTopkSel;                            // [nparts + 1] (parts path)
+  unsigned* s_raw = reinterpret_cast<unsigned*>(s_off + kTopkMaxParts + 1);  // [nparts / 32]
+  __shared__ int s_wave[kSelWaves];
+  __shared__ unsigned s_mm[2][kSelWaves];
+  __shared__ int s_blk[2][kSelRounds * kSelWaves];  // per (round, wave) block
   __shared__ unsigned s_sel[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t qr = blockIdx.y;
-  const int part = blockIdx.x;
-  int64_t n_in;
-  if (FIRST) {
-    const int64_t t = q_pos0 + (qr % Tq);
-    n_in = (t + 1) / m;
-    if (n_in > n_entries) n_in = n_entries;
-  } else {
-    n_in = in_stride;
-  }
-  const int64_t beg = (int64_t)part * kTopkPart;
-  int len = 0;
-  if (n_in > beg) len = (int)((n_in - beg) < kTopkPart ? (n_in - beg) : kTopkPart);
+  const int64_t qr = blockIdx.x;
+  const int64_t V = visible_of(a, qr);
+  const int k = a.k;
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
 
-  // load keys (and candidate indices) into LDS; count present keys and take
-  // their min and max.  All of a thread's 16-byte loads are issued before any
-  // is consumed (indices past the part re-read its last vector).
-  int nvalid = 0;
-  unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
-  auto note = [&](unsigned key) {
-    nvalid += key != 0u;
-    if (key != 0u) {
-      kmin = min(kmin, key);
+  // Select the top-k of s_key[0, len) (0 = absent) and hand each selected
+  // (position, key, index) to out(), positions in ascending index order.
+  // Returns how many were selected (min(k, present keys)); *lower gets the
+  // k-th largest present key (1 when at most k keys are present).
+  auto select = [&](int len, unsigned* lower, auto out) -> int {
+    // this thread's keys, positions tid + r * threads, held in registers
+    const int nrounds = (len + kSelThreads - 1) / kSelThreads;
+    unsigned kr[kSelRounds];
+#pragma unroll
+    for (int r = 0; r < kSelRounds; ++r) {
+      const int i = r * kSelThreads + tid;
+      kr[r] = (r < nrounds && i < len) ? s_key[i] : 0u;
+    }
+    int nvalid = 0;
+    unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int r = 0; r < kSelRounds; ++r) {
+      const unsigned key = kr[r];
+      nvalid += key != 0u;
+      kmin = key != 0u ? min(kmin, key) : kmin;
       kmax = max(kmax, key);
     }
-  };
-  constexpr int U = kTopkPart / 4 / kTopkThreads;
-  const int64_t src0 = FIRST ? qr * score_stride + beg : qr * in_stride + beg;
-  const bool vec = FIRST ? (score_stride & 3) == 0 : (in_stride & 3) == 0;
-  const int len4 = vec ? (len >> 2) : 0;
-  if (len4 > 0) {
-    u32x4 kv[U];
-    u32x4 iv[FIRST ? 1 : U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i4 = min(tid + u * kTopkThreads, len4 - 1);
-      if (FIRST) {
-        kv[u] = *reinterpret_cast<const u32x4*>(scores + src0 + 4 * i4);
-      } else {
-        kv[u] = *reinterpret_cast<const u32x4*>(in_key + src0 + 4 * i4);
-        iv[FIRST ? 0 : u] = *reinterpret_cast<const u32x4*>(in_idx + src0 + 4 * i4);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i4 = tid + u * kTopkThreads;
-      if (i4 < len4) {
-        u32x4 k4 = kv[u];
-        if (FIRST) {
-          k4.x = score_key(__uint_as_float(k4.x));
-          k4.y = score_key(__uint_as_float(k4.y));
-          k4.z = score_key(__uint_as_float(k4.z));
-          k4.w = score_key(__uint_as_float(k4.w));
-        } else {
-          *reinterpret_cast<u32x4*>(&s_idx[4 * i4]) = iv[FIRST ? 0 : u];
-        }
-        *reinterpret_cast<u32x4*>(&s_key[4 * i4]) = k4;
-        note(k4.x);
-        note(k4.y);
-        note(k4.z);
-        note(k4.w);
-      }
-    }
-  }
-#pragma unroll 8
-  for (int i = 4 * len4 + tid; i < len; i += kTopkThreads) {
-    unsigned key;
-    if (FIRST) {
-      key = score_key(scores[src0 + i]);
-    } else {
-      key = in_key[src0 + i];
-      s_idx[i] = in_idx[src0 + i];
-    }
-    s_key[i] = key;
-    note(key);
-  }
-  kmin = wave_min_u(kmin);
-  kmax = wave_max_u(kmax);
-  if (lane == 0) {
-    s_mm[0][wave] = kmin;
-    s_mm[1][wave] = kmax;
-  }
-  int total_valid;
-  (void)block_excl_scan(nvalid, s_wave, &total_valid);  // also syncs after the LDS writes
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    kmin = min(kmin, s_mm[0][w]);
-    kmax = max(kmax, s_mm[1][w]);
-  }
-
-  // Bucket select: the kept keys form the contiguous key range [lo, hi]; each
-  // pass bins that range linearly into at most 2048 buckets (so the bins
-  // follow the data, not the exponent bits), keeps the bucket holding the
-  // k-th key and accounts for everything above it.  It ends when the bucket
-  // is one key wide (ties by position) or needed whole.
-  const bool all = total_valid <= k;
-  unsigned lo = kmin, hi = kmax;
-  int need = all ? total_valid : k;
-  if (!all) {
-    while (true) {
-      const unsigned span = hi - lo;   // width - 1
-      int shift = 0;
-      while ((span >> shift) >= (unsigned)kHistBins) ++shift;
-      const int nb = (int)(span >> shift) + 1;   // <= kHistBins
-      for (int i = tid; i < nb; i += kTopkThreads) s_hist[i] = 0u;
-      __syncthreads();
-#pragma unroll 4
-      for (int i = tid; i < len; i += kTopkThreads) {
-        const unsigned key = s_key[i];
-        if (key != 0u && key >= lo && key <= hi) atomicAdd(&s_hist[(key - lo) >> shift], 1u);
-      }
-      __syncthreads();
-      // thread t owns buckets nb-1-2t and nb-2-2t (high buckets first)
-      int loc = 0;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int d = nb - 1 - (2 * tid + u);
-        loc += d >= 0 ? (int)s_hist[d] : 0;
-      }
-      int tot;
-      int above = block_excl_scan(loc, s_wave, &tot);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int d = nb - 1 - (2 * tid + u);
-        const int cnt = d >= 0 ? (int)s_hist[d] : 0;
-        if (d >= 0 && above < need && above + cnt >= need) {
-          s_sel[0] = (unsigned)d;
-          s_sel[1] = (unsigned)above;
-          s_sel[2] = (unsigned)cnt;
-        }
-        above += cnt;
-      }
-      __syncthreads();
-      const unsigned d = s_sel[0];
-      const int cnt_gt = (int)s_sel[1], cnt_eq = (int)s_sel[2];
-      __syncthreads();
-      need -= cnt_gt;
-      const unsigned nlo = lo + (d << shift);
-      const uint64_t nhi = (uint64_t)nlo + (1ull << shift) - 1u;
-      hi = nhi < (uint64_t)hi ? (unsigned)nhi : hi;
-      lo = nlo;
-      if (cnt_eq == need || lo == hi) break;
-    }
-  }
-
-  // Stream compaction in position order.  Round r covers positions
-  // [r*threads, (r+1)*threads); (round, wave) blocks are in position order.
-  // Pass A counts each block's keys above the bucket and in it with ballots,
-  // one scan over the (at most 256) blocks turns that into the first output
-  // slot and the first tie rank of every block, and pass B writes.
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
-  const int n_sel_total = all ? total_valid : k;
-  const int nrounds = (len + kTopkThreads - 1) / kTopkThreads;
-  auto classify = [&](int i, unsigned& key, bool& gt, bool& eq) {
-    key = i < len ? s_key[i] : 0u;
-    if (all) {
-      gt = key != 0u;
-      eq = false;
-    } else {
-      gt = key != 0u && key > hi;
-      eq = key != 0u && key >= lo && key <= hi;
-    }
-  };
-#pragma unroll 4
-  for (int rnd = 0; rnd < nrounds; ++rnd) {
-    unsigned key;
-    bool gt, eq;
-    classify(rnd * kTopkThreads + tid, key, gt, eq);
-    const unsigned long long bg = __ballot(gt), be = __ballot(eq);
+    kmin = wave_min_u(kmin);
+    kmax = wave_max_u(kmax);
     if (lane == 0) {
-      s_blk[0][rnd * kTopkWaves + wave] = __popcll(bg);
-      s_blk[1][rnd * kTopkWaves + wave] = __popcll(be);
+      s_mm[0][wave] = kmin;
+      s_mm[1][wave] = kmax;
     }
-  }
-  __syncthreads();
-  {
-    const int e = tid;   // block (round e / waves, wave e % waves), position order
-    const bool own = e < nrounds * kTopkWaves;
-    const int cg = own ? s_blk[0][e] : 0, ce = own ? s_blk[1][e] : 0;
-    int tot;
-    const int eq_before = block_excl_scan(ce, s_wave, &tot);
-    int take = need - eq_before;
-    take = take < 0 ? 0 : (take > ce ? ce : take);
-    const int sel_before = block_excl_scan(cg + take, s_wave, &tot);
-    if (own) {
-      s_blk[0][e] = sel_before;
-      s_blk[1][e] = eq_before;
+    int total_valid;
+    (void)block_excl_scan(nvalid, s_wave, &total_valid);
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      kmin = min(kmin, s_mm[0][w]);
+      kmax = max(kmax, s_mm[1][w]);
     }
-  }
-  __syncthreads();
-#pragma unroll 4
-  for (int rnd = 0; rnd < nrounds; ++rnd) {
-    const int i = rnd * kTopkThreads + tid;
-    unsigned key;
-    bool gt, eq;
-    classify(i, key, gt, eq);
-    const unsigned long long bg = __ballot(gt), be = __ballot(eq);
-    const int e = rnd * kTopkWaves + wave;
-    const int sel_before = s_blk[0][e], eq_before = s_blk[1][e];
-    const int eq_lt = __popcll(be & lt_mask);
-    const bool sel = gt || (eq && eq_before + eq_lt < need);
-    if (sel) {
-      int take_lt = need - eq_before;
-      take_lt = take_lt < 0 ? 0 : (take_lt > eq_lt ? eq_lt : take_lt);
-      const int pos = sel_before + __popcll(bg & lt_mask) + take_lt;
-      const int idx = FIRST ? (int)(beg + i) : s_idx[i];
-      if (last) {
-        topk[qr * k + pos] = idx;
-        if (topk_score) topk_score[qr * k + pos] = key_score(key);
-      } else {
-        out_key[qr * out_stride + (int64_t)part * k + pos] = key;
-        out_idx[qr * out_stride + (int64_t)part * k + pos] = idx;
+    // bucket select: the kept keys form the contiguous key range [lo, hi]
+    const bool all = total_valid <= k;
+    unsigned lo = kmin, hi = kmax;
+    int need = all ? total_valid : k;
+    if (!all) {
+      while (true) {
+        const unsigned span = hi - lo;   // width - 1
+        int shift = 0;
+        while ((span >> shift) >= (unsigned)kHistBins) ++shift;
+        const int nb = (int)(span >> shift) + 1;   // <= kHistBins
+        for (int i = tid; i < nb; i += kSelThreads) s_hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kSelRounds; ++r) {
+          const unsigned key = kr[r];
+          if (key != 0u && key >= lo && key <= hi) atomicAdd(&s_hist[(key - lo) >> shift], 1u);
+        }
+        __syncthreads();
+        // thread t owns buckets nb-1-B*t .. nb-B*t-B (high buckets first)
+        int loc = 0;
+#pragma unroll
+        for (int u = 0; u < kBucketsPerThread; ++u) {
+          const int d = nb - 1 - (kBucketsPerThread * tid + u);
+          loc += d >= 0 ? (int)s_hist[d] : 0;
+        }
+        int tot;
+        int above = block_excl_scan(loc, s_wave, &tot);
+#pragma unroll
+        for (int u = 0; u < kBucketsPerThread; ++u) {
+          const int d = nb - 1 - (kBucketsPerThread * tid + u);
+          const int cnt = d >= 0 ? (int)s_hist[d] : 0;
+          if (d >= 0 && above < need && above + cnt >= need) {
+            s_sel[0] = (unsigned)d;
+            s_sel[1] = (unsigned)above;
+            s_sel[2] = (unsigned)cnt;
+          }
+          above += cnt;
+        }
+        __syncthreads();
+        const unsigned d = s_sel[0];
+        const int cnt_gt = (int)s_sel[1], cnt_eq = (int)s_sel[2];
+        __syncthreads();
+        need -= cnt_gt;
+        const unsigned nlo = lo + (d << shift);
+        const uint64_t nhi = (uint64_t)nlo + (1ull << shift) - 1u;
+        hi = nhi < (uint64_t)hi ? (unsigned)nhi : hi;
+        lo = nlo;
+        if (cnt_eq == need || lo == hi) break;
       }
     }
+    // Stream compaction in position order: round r covers positions
+    // [r*threads, (r+1)*threads); (round, wave) blocks are in position
+    // order.  Pass A counts each block's keys above the bucket and in it,
+    // one scan turns that into first output slots and tie ranks, pass B
+    // hands out the selected keys.
+    auto is_gt = [&](unsigned key) { return all ? key != 0u : (key != 0u && key > hi); };
+    auto is_eq = [&](unsigned key) { return !all && key != 0u && key >= lo && key <= hi; };
+#pragma unroll
+    for (int r = 0; r < kSelRounds; ++r) {
+      if (r < nrounds) {
+        const unsigned long long bg = __ballot(is_gt(kr[r])), be = __ballot(is_eq(kr[r]));
+        if (lane == 0) {
+          s_blk[0][r * kSelWaves + wave] = __popcll(bg);
+          s_blk[1][r * kSelWaves + wave] = __popcll(be);
+        }
+      }
+    }
+    __syncthreads();
+    {
+      const int e = tid;   // block (round e / waves, wave e % waves), position order
+      const bool own = e < nrounds * kSelWaves;
+      const int cg = own ? s_blk[0][e] : 0, ce = own ? s_blk[1][e] : 0;
+      int tot;
+      const int eq_before = block_excl_scan(ce, s_wave, &tot);
+      int take = need - eq_before;
+      take = take < 0 ? 0 : (take > ce ? ce : take);
+      const int sel_before = block_excl_scan(cg + take, s_wave, &tot);
+      if (own) {
+        s_blk[0][e] = sel_before;
+        s_blk[1][e] = eq_before;
+      }
+    }
+    __syncthreads();
+    unsigned smin = 0xFFFFFFFFu;   // smallest selected key
+#pragma unroll
+    for (int r = 0; r < kSelRounds; ++r) {
+      if (r < nrounds) {
+        const unsigned key = kr[r];
+        const bool gt = is_gt(key), eq = is_eq(key);
+        const unsigned long long bg = __ballot(gt), be = __ballot(eq);
+        const int e = r * kSelWaves + wave;
+        const int sel_before = s_blk[0][e], eq_before = s_blk[1][e];
+        const int eq_lt = __popcll(be & lt_mask);
+        if (gt || (eq && eq_before + eq_lt < need)) {
+          int take_lt = need - eq_before;
+          take_lt = take_lt < 0 ? 0 : (take_lt > eq_lt ? eq_lt : take_lt);
+          out(sel_before + __popcll(bg & lt_mask) + take_lt, key, s_idx[r * kSelThreads + tid]);
+          smin = min(smin, key);
+        }
+      }
+    }
+    smin = wave_min_u(smin);
+    if (lane == 0) s_mm[0][wave] = smin;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) smin = min(smin, s_mm[0][w]);
+    *lower = all ? 1u : smin;   // the k-th largest present key
+    __syncthreads();
+    return all ? total_valid : k;
+  };
+
+  int32_t* topk = a.topk + qr * k;
+  float* tks = a.topk_score ? a.topk_score + qr * k : nullptr;
+  auto final_out = [&](int pos, unsigned key, int idx) {
+    topk[pos] = idx;
+    if (tks) tks[pos] = key_score(key);
+  };
+  auto pad = [&](int n_sel) {
+    for (int q = n_sel + tid; q < k; q += kSelThreads) {
+      topk[q] = -1;
+      if (tks) tks[q] = -INFINITY;
+    }
+  };
+  unsigned lower;
+
+  if (V <= kTopkSel) {
+    // the whole row in LDS
+    const int len = (int)(V > 0 ? V : 0);
+    const float* src = a.scores + qr * a.score_stride;
+    for (int i = tid; i < len; i += kSelThreads) {
+      s_key[i] = score_key(src[i]);
+      s_idx[i] = i;
+    }
+    __syncthreads();
+    pad(select(len, &lower, final_out));
+    return;
   }
-  // padding
-  for (int p = n_sel_total + tid; p < k; p += kTopkThreads) {
-    if (last) {
-      topk[qr * k + p] = -1;
-      if (topk_score) topk_score[qr * k + p] = -INFINITY;
-    } else {
-      out_key[qr * out_stride + (int64_t)part * k + p] = 0u;
-      out_idx[qr * out_stride + (int64_t)part * k + p] = -1;
+
+  const int np = a.nparts;
+  const int ppt = (np + kSelThreads - 1) / kSelThreads;   // parts per thread (<= 16)
+  const unsigned* ptau = a.part_tau + qr * np;
+  const int* pcnt = a.part_cnt + qr * np;
+  const unsigned* pover = a.part_over + qr * np;
+  const unsigned* ck = a.cand_key + qr * (int64_t)np * kTopkPartCap;
+  const int* ci = a.cand_idx + qr * (int64_t)np * kTopkPartCap;
+  unsigned* rk = a.run_key + qr * k;
+
+  // Offsets of the parts' candidates given each part's count (cnt_of).
+  auto offsets = [&](auto cnt_of) -> int {
+    int mine = 0;
+    for (int u = 0; u < ppt; ++u) {
+      const int q = tid * ppt + u;
+      mine += q < np ? cnt_of(q) : 0;
+    }
+    int C;
+    int off = block_excl_scan(mine, s_wave, &C);
+    for (int u = 0; u < ppt; ++u) {
+      const int q = tid * ppt + u;
+      if (q < np) {
+        s_off[q] = off;
+        off += cnt_of(q);
+      }
+    }
+    if (tid == 0) s_off[np] = C;
+    __syncthreads();
+    return C;
+  };
+  auto is_raw = [&](int q) { return (s_raw[q >> 5] >> (q & 31)) & 1u; };
+
+  // Select over the candidates s_off describes: a part's candidates are its
+  // stored leaders, or (raw parts) its keys >= thr re-read in position order.
+  // Taken in chunks of what fits beside the running selection.
+  auto run_select = [&](unsigned thr, bool any_raw, unsigned* low) -> int {
+    const int C = s_off[np];
+    int run = 0;   // keys of the partial selection, kept in rk / topk between chunks
+    for (int c0 = 0;;) {
+      const int take = min(C - c0, kTopkSel - run);
+      for (int i = tid; i < run; i += kSelThreads) {
+        s_key[i] = rk[i];
+        s_idx[i] = topk[i];
+      }
+      // stored leaders: thread t copies parts t, t + threads, ..., clipped to
+      // candidates [c0, c0 + take); all 32 slots of a part are loaded at once
+      static_assert(kTopkPartCap == 32, "eight 16-byte loads per part");
+      for (int q = tid; q < np; q += kSelThreads) {
+        const int o0 = s_off[q], cq = s_off[q + 1] - o0;
+        if (is_raw(q) || o0 + cq <= c0 || o0 >= c0 + take) continue;
+        u32x4 kk[8], ii[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          kk[u] = *reinterpret_cast<const u32x4*>(ck + q * kTopkPartCap + 4 * u);
+          ii[u] = *reinterpret_cast<const u32x4*>(ci + q * kTopkPartCap + 4 * u);
+        }
+#pragma unroll
+        for (int j = 0; j < kTopkPartCap; ++j) {
+          const int e = o0 + j;
+          if (j < cq && e >= c0 && e < c0 + take) {
+            s_key[run + e - c0] = kk[j >> 2][j & 3];
+            s_idx[run + e - c0] = (int)ii[j >> 2][j & 3];
+          }
+        }
+      }
+      for (int q = wave; any_raw && q < np; q += kSelWaves) {
+        const int o0 = s_off[q], o1 = s_off[q + 1];
+        if (!is_raw(q) || o1 <= c0 || o0 >= c0 + take) continue;
+        unsigned key[16];
+        const int64_t base = (int64_t)q * kTopkPartLen;
+        load_part(a, qr, V, base, lane, key);
+        int cnt = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool pass = key[r] >= thr;
+          const unsigned long long bl = __ballot(pass);
+          const int e = o0 + cnt + __popcll(bl & lt_mask);
+          if (pass && e >= c0 && e < c0 + take) {
+            s_key[run + e - c0] = key[r];
+            s_idx[run + e - c0] = (int)(base + 64 * r + lane);
+          }
+          cnt += __popcll(bl);
+        }
+      }
+      __syncthreads();
+      const int len = run + take;
+      c0 += take;
+      if (c0 >= C) return select(len, low, final_out);
+      unsigned dummy;
+      run = select(len, &dummy, [&](int pos, unsigned key, int idx) {
+        rk[pos] = key;
+        topk[pos] = idx;
+      });
+      __threadfence_block();
+      __syncthreads();
+    }
+  };
+
+  // 1. the stored leaders of every part
+  for (int w = tid; w < (np + 31) / 32; w += kSelThreads) s_raw[w] = 0u;
+  __syncthreads();
+  (void)offsets([&](int q) { return min(pcnt[q], kTopkPartCap); });
+  int n_sel = run_select(0u, false, &lower);
+  // 2. parts that may hold keys >= lower they did not store (pover is 0 when
+  // nothing was left out, and lower >= 1)
+  int bad = 0;
+  for (int u = 0; u < ppt; ++u) {
+    const int q = tid * ppt + u;
+    if (q < np && (ptau[q] > lower || pover[q] >= lower)) {
+      atomicOr(&s_raw[q >> 5], 1u << (q & 31));
+      ++bad;
     }
   }
+  int nbad;
+  (void)block_excl_scan(bad, s_wave, &nbad);
+  if (nbad == 0) {
+    pad(n_sel);
+    return;
+  }
+  // 3. again over the complete parts' leaders and every key >= lower of the
+  // others (the parts' counts first, in s_idx, one wave per re-read part)
+  const unsigned thr = lower;
+  for (int q = tid; q < np; q += kSelThreads) s_idx[q] = min(pcnt[q], kTopkPartCap);
+  __syncthreads();
+  for (int q = wave; q < np; q += kSelWaves) {
+    if (!is_raw(q)) continue;
+    unsigned key[16];
+    load_part(a, qr, V, (int64_t)q * kTopkPartLen, lane, key);
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c += __popcll(__ballot(key[r] >= thr));
+    if (lane == 0) s_idx[q] = c;
+  }
+  __syncthreads();
+  (void)offsets([&](int q) { return s_idx[q]; });
+  pad(run_select(thr, true, &lower));
 }
 
 static bool g_topk_attr_set = false;
@@ -329,43 +499,20 @@ static bool g_topk_attr_set = false;
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& plan, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.Tq;
   if (rows == 0) return hipSuccess;
-  const size_t lds_first = (kTopkPart + kHistBins) * sizeof(unsigned);
-  const size_t lds_next = lds_first + kTopkPart * sizeof(int);
+  const size_t lds =
+      (size_t)(2 * kTopkSel + kHistBins + kTopkMaxParts + 1 + kTopkMaxParts / 32) * sizeof(unsigned);
   if (!g_topk_attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_stage_kernel<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_first);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)topk_stage_kernel<false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_next);
+    hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     g_topk_attr_set = true;
   }
-  int64_t parts = plan.parts0;
-  int cur = 0;
-  {
-    const int last = plan.stages == 1;
-    dim3 grid((unsigned)parts, (unsigned)rows);
-    topk_stage_kernel<true><<<grid, kTopkThreads, lds_first, st>>>(
-        a.scores, a.score_stride, nullptr, nullptr, 0, a.Tq, a.n_entries, a.q_pos0, a.m, a.k,
-        last, a.cand_key[0], a.cand_idx[0], parts * a.k, a.topk, a.topk_score);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if (plan.parts) {
+    const dim3 grid((unsigned)((plan.nparts + 3) / 4), (unsigned)rows);
+    topk_part_kernel<<<grid, 256, 0, st>>>(a);
   }
-  for (int s = 1; s < plan.stages; ++s) {
-    const int64_t n = parts * (int64_t)a.k;
-    const int64_t nparts = (n + kTopkPart - 1) / kTopkPart;
-    const int last = s == plan.stages - 1;
-    dim3 grid((unsigned)nparts, (unsigned)rows);
-    topk_stage_kernel<false><<<grid, kTopkThreads, lds_next, st>>>(
-        nullptr, 0, a.cand_key[cur], a.cand_idx[cur], n, a.Tq, a.n_entries, a.q_pos0, a.m,
-        a.k, last, a.cand_key[cur ^ 1], a.cand_idx[cur ^ 1], nparts * a.k, a.topk,
-        a.topk_score);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    parts = nparts;
-    cur ^= 1;
-  }
-  return hipSuccess;
+  topk_select_kernel<<<(unsigned)rows, kSelThreads, lds, st>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace v4
