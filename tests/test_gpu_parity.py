@@ -171,6 +171,63 @@ def test_index_topk_bit_exact_on_integer_inputs(case):
             assert np.all(np.isneginf(got_s[b, r, len(sel):]))
 
 
+SCORE_ROWS = [
+    # name, V, k: rows built to reach every path of the selector
+    ("random", 262144, 1024),      # the decode shape: leaders only
+    ("all_equal", 100000, 1024),   # every part overflows: re-read, chunked merge
+    ("ascending", 60000, 4096),    # the top-k sits in the last parts: re-read
+    ("nan_heavy", 50000, 1024),    # 3% valid keys: parts short of leaders
+    ("signed_zero_inf", 40000, 512),  # -0/+0 ties, +-inf
+    ("small_row", 9000, 256),      # one workgroup holds the whole row
+]
+
+
+def _score_row(name, V, seed):
+    g = np.random.default_rng(seed)
+    if name == "random":
+        return g.standard_normal(V).astype(np.float32)
+    if name == "all_equal":
+        return np.full(V, 1.5, dtype=np.float32)
+    if name == "ascending":
+        return np.linspace(-3.0, 3.0, V, dtype=np.float32)
+    if name == "nan_heavy":
+        x = g.standard_normal(V).astype(np.float32)
+        x[g.random(V) < 0.97] = np.nan
+        return x
+    if name == "signed_zero_inf":
+        x = g.choice(np.array([-0.0, 0.0, 1.0, -1.0, np.inf, -np.inf], dtype=np.float32), V)
+        return x.astype(np.float32)
+    return g.standard_normal(V).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", SCORE_ROWS, ids=[c[0] for c in SCORE_ROWS])
+def test_topk_select_paths_bit_exact(case):
+    """Top-k of given score rows against the oracle's (score desc, index asc)
+    rule, on rows built to take each path of the selector.  NaN is never
+    selected (the oracle's rule applied to the non-NaN scores)."""
+    name, V, k = case
+    log(f"topk_select {name} V={V} k={k}")
+    rows = [_score_row(name, V, 11 + r) for r in range(2)]
+    stride = (V + 63) // 64 * 64
+    buf = torch.zeros((2, stride), dtype=torch.float32)
+    for r in range(2):
+        buf[r, :V] = torch.from_numpy(rows[r])
+    buf = buf.to(DEV)
+    topk, ts = ops().topk_select(buf, B=2, Tq=1, n_entries=V, q_pos0=V - 1, m=1, k=k,
+                                 want_scores=True)
+    torch.cuda.synchronize()
+    got, got_s = topk.cpu().numpy(), ts.cpu().numpy()
+    for r in range(2):
+        x = rows[r].astype(np.float64)
+        valid = np.nonzero(~np.isnan(x))[0]
+        sel = valid[oi.topk_select(x[valid], k)[: min(k, len(valid))]]
+        want = np.full(k, -1, dtype=np.int32)
+        want[: len(sel)] = np.sort(sel)
+        np.testing.assert_array_equal(got[r, 0], want)
+        np.testing.assert_array_equal(got_s[r, 0, : len(sel)], x[np.sort(sel)].astype(np.float32))
+        assert np.all(np.isneginf(got_s[r, 0, len(sel):]))
+
+
 def test_index_topk_float_inputs_near_tie_tolerant():
     B, Tq, HI, dI, N, k = 2, 2, 64, 128, 20000, 1024
     log("index_topk float")
