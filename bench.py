@@ -29,6 +29,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+COPY_BYTES = 1 << 30           # calibration copy for the HBM byte counters
+
+# HBM bytes of one index_score launch at the decode shape, from two
+# rocprofv3 --pmc passes over `bench.py --counters` (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
+# for torch's elementwise kernel over 1 GiB in and 1 GiB out (FETCH 524,320
+# KiB -> x2.0; WRITE 1,048,576 KiB -> x1.0).  Valid only for the kernel
+# sources they were taken with (hash below); otherwise reported as null.
+TRAFFIC = {"sources_sha256_16": "f434a9afba727c05",
+           "fetch_kib": 262708.3, "fetch_scale": 2.0,
+           "write_kib": 8195.8, "write_scale": 1.0}
+TRAFFIC_SOURCES = ("long_context_sparse_csa_amd/csrc/indexer.hip",
+                   "long_context_sparse_csa_amd/csrc/common.hpp")
 METRIC = "decode query-tokens/s per layer at 1M ctx (CSA, HCA); % of HBM/MFMA peak"
 
 
@@ -166,6 +179,20 @@ def algorithmic_bytes():
     return out, flops
 
 
+def measured_traffic():
+    """Counter-measured HBM bytes per index_score launch, or None when the
+    kernel sources differ from the ones the counters were taken with."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != TRAFFIC["sources_sha256_16"]:
+        return None
+    return int(1024 * (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] +
+                       TRAFFIC["write_kib"] * TRAFFIC["write_scale"]))
+
+
 def run_timed(launches, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -277,6 +304,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--counters", action="store_true",
+                    help="no timing: run a 1 GiB elementwise copy (known bytes) and a few "
+                         "decode steps for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -294,6 +324,18 @@ def main():
     inp = build_inputs(dev, args.rotate)
     launches, outs = make_step(inp, dev)
     torch.cuda.synchronize()
+    if args.counters:
+        # calibration: torch's elementwise kernel reads and writes COPY_BYTES each
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        for _ in range(3):
+            for _, fn in launches:
+                fn()
+        torch.cuda.synchronize()
+        log("counters pass done")
+        return
     log("timing")
     ms, wall = run_timed(launches, args.steps, args.warmup)
     log(f"step {ms * 1e3:.1f} us")
@@ -317,7 +359,7 @@ def main():
     ach = abytes[dom] / (br[dom] * 1e-6) / 1e9
     roofline = {"kernel": "index_score_kernel<128,4>", "bound": "hbm",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "algorithmic_bytes_per_launch": abytes[dom]}
 
     res = {
