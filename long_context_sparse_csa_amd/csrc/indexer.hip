@@ -6,11 +6,11 @@
 // main attention ("DeepSeek-V4, explained", step 3 of how one query's layer
 // works).  One indexer key per entry is shared by all indexer heads.
 //
-// Design (decode): the dense contraction [HI heads x dI] x [dI x keys] runs on
-// the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with the query's heads as
-// the M dimension, loaded once per wave and held in registers, and the keys as
-// N.  q (all heads of the query) sits in LDS and is read per MFMA, which
-// keeps the registers small; each wave streams one contiguous range of keys
+// Design (decode, few queries): the dense contraction [HI heads x dI] x
+// [dI x keys] runs on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) with
+// the query's heads as the M dimension and the keys as N.  q (all heads of
+// the query) sits in LDS and is read per MFMA, which keeps the registers
+// small; each wave streams one contiguous range of keys
 // in 32-key chunks with streaming (non-temporal) loads, every load
 // instruction covering 1 KiB of contiguous keys (the pattern that measured
 // fastest on this HBM), stages them in its own padded LDS rows and reads them
@@ -20,6 +20,16 @@
 // accumulators in registers (16 heads per lane, then two cross-lane adds), so
 // only 4 bytes per entry leave the kernel.  At 1M tokens this kernel streams
 // 64 MiB of keys per query and is HBM-bound (64 FLOP per byte).
+//
+// Design (prefill, a block of queries of one sequence): every key is shared
+// by all queries, so the contraction is MFMA-bound and the keys are read once
+// per 8 queries (from the Infinity Cache, where a million-token key set fits).
+// A workgroup of 8 waves holds one query per wave (q for 64 heads x 128 dims
+// in registers as the A operands of v_mfma_f32_32x32x16_bf16, the faster bf16
+// shape on this chip) and walks its key range in
+// 128-key tiles copied straight to LDS with global_load_lds (four 1 KiB
+// copies per wave per tile, three tiles in rotation, chunks XOR-swizzled by
+// row so the operand reads are free of bank conflicts).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -128,6 +138,161 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
   }
 }
 
+constexpr int kBlkWaves = 8;    // waves per workgroup
+constexpr int kBlkQPW = 1;      // queries per wave
+constexpr int kBlkQ = kBlkWaves * kBlkQPW;   // queries per workgroup
+constexpr int kBlkKeys = 128;   // keys per LDS tile
+
+// 64 lanes x 16 bytes from per-lane global addresses into 1 KiB of LDS at
+// `dst` (+16 bytes per lane).  Written as asm so that the compiler does not
+// wait for the copy before every LDS read; the tile loop waits for it itself
+// (vmcnt) before the barrier that publishes a tile.  No register result; the
+// address registers are read at issue.
+__device__ __forceinline__ void idx_copy_to_lds16(const void* src, V4_LDS void* dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+__global__ __launch_bounds__(kBlkWaves * 64) void index_score_block_kernel(IndexScoreArgs a,
+                                                                           int64_t key_chunk) {
+  constexpr int DI = 128;
+  constexpr int RB = 2 * DI;               // key row bytes
+  constexpr int CPR = RB / 16;             // 16-byte chunks per row
+  constexpr int TILE = kBlkKeys * RB;      // bytes per tile
+  constexpr int KS = DI / 16;              // 32x32x16 k-steps
+  constexpr int CPW = TILE / 1024 / kBlkWaves;   // 1 KiB copies per wave per tile
+  static_assert(CPW * 1024 * kBlkWaves == TILE, "whole copies per wave");
+  static_assert(CPR == 16, "the row swizzle spans 16 chunks");
+  const int b = blockIdx.z, qg = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = qg * kBlkQ + wave * kBlkQPW;      // this wave's first query
+  auto visible = [&](int rr) {
+    const int64_t t = a.q_pos0 + rr;
+    const int64_t v = (t + 1) / a.m;
+    return v < a.n_entries ? v : a.n_entries;
+  };
+  const int64_t Vlast = visible(min(qg * kBlkQ + kBlkQ - 1, a.Tq - 1));  // largest in group
+  const int64_t kc0 = (int64_t)blockIdx.x * key_chunk;
+  const int64_t kc1 = min(kc0 + key_chunk, Vlast);
+  if (kc0 >= kc1) return;
+  const int ntiles = (int)((kc1 - kc0 + kBlkKeys - 1) / kBlkKeys);
+
+  __shared__ __attribute__((aligned(16))) uint8_t s_k0[TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k1[TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k2[TILE];
+  __shared__ __attribute__((aligned(16))) float s_w[kBlkQ][64];
+
+  const bool wok = r0 < a.Tq;   // the wave has at least one query
+  int64_t qrow[kBlkQPW], jmax[kBlkQPW];
+#pragma unroll
+  for (int u = 0; u < kBlkQPW; ++u) {
+    const int r = r0 + u;
+    qrow[u] = (int64_t)b * a.Tq + min(r, a.Tq - 1);
+    jmax[u] = r < a.Tq ? min(kc1, visible(r)) : 0;   // the query stores keys below it
+    s_w[wave * kBlkQPW + u][lane] = (r < a.Tq && lane < a.HI) ? a.w_idx[qrow[u] * a.HI + lane] : 0.f;
+  }
+
+  // A operands: head hb*32 + (lane & 31), dims 16s + 8(lane >> 5) .. +8
+  bf16x8 qa[kBlkQPW][2][KS];
+#pragma unroll
+  for (int u = 0; u < kBlkQPW; ++u) {
+    const uint16_t* qp = a.q_idx + qrow[u] * a.HI * DI;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = hb * 32 + (lane & 31);
+      const bool hv = r0 + u < a.Tq && h < a.HI;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(qp + (int64_t)min(h, a.HI - 1) * DI + 16 * s +
+                                                  8 * (lane >> 5));
+        if (!hv) v = u32x4{0u, 0u, 0u, 0u};
+        qa[u][hb][s] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  }
+
+  // tile copy: copy i of wave w moves slots 64(CPW w + i) + lane, i.e. row
+  // (64(CPW w + i) + lane) / 16, physical chunk lane % 16 <- logical chunk
+  // (lane % 16) ^ (row & 15)
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_idx + (int64_t)b * a.Ncap * DI);
+  auto issue = [&](int tile, uint8_t* T) {
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int win = CPW * wave + i;
+      const int row = 4 * win + (lane >> 4);   // 64 slots of 16 bytes = 4 rows per copy
+      int64_t j = kc0 + (int64_t)tile * kBlkKeys + row;
+      j = j < kc1 ? j : kc1 - 1;   // past the range: re-read a valid key (score not stored)
+      const int lc = (lane & 15) ^ (row & 15);
+      idx_copy_to_lds16(kbase + j * RB + 16 * lc, (V4_LDS void*)(T + 1024 * win));
+    }
+  };
+
+  auto compute = [&](int tile, const uint8_t* T) {
+#pragma unroll 2
+    for (int kb = 0; kb < kBlkKeys / 32; ++kb) {
+      f32x16 acc[kBlkQPW][2];
+#pragma unroll
+      for (int u = 0; u < kBlkQPW; ++u)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[u][hb][i] = 0.f;
+      const int row = kb * 32 + (lane & 31);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int lc = 2 * s + (lane >> 5);
+        const bf16x8 kv = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(T + row * RB + 16 * (lc ^ (row & 15))));
+#pragma unroll
+        for (int u = 0; u < kBlkQPW; ++u)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            acc[u][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u][hb][s], kv, acc[u][hb], 0, 0, 0);
+      }
+      // lane holds key (lane & 31), heads hb*32 + (i/4)*8 + (lane>>5)*4 + i%4
+      const int64_t j = kc0 + (int64_t)tile * kBlkKeys + kb * 32 + (lane & 31);
+#pragma unroll
+      for (int u = 0; u < kBlkQPW; ++u) {
+        float sc = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(
+                &s_w[wave * kBlkQPW + u][hb * 32 + i4 * 8 + (lane >> 5) * 4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc = fmaf(w4[i], fmaxf(acc[u][hb][4 * i4 + i], 0.f), sc);
+          }
+        sc += __shfl_xor(sc, 32);
+        if (lane < 32 && j < jmax[u]) a.scores[qrow[u] * a.score_stride + j] = sc;
+      }
+    }
+  };
+
+  // Tile t lives in buffer t % 3: a step issues tile t+2, uses tile t, then
+  // waits for its own copies of tile t+1 (t+2's may stay in flight) and meets
+  // the other waves at the barrier.
+  if (ntiles > 0) issue(0, s_k0);
+  if (ntiles > 1) issue(1, s_k1);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  auto step = [&](int tile, const uint8_t* Tr, uint8_t* Ti) {
+    const bool pre = tile + 2 < ntiles;
+    if (pre) issue(tile + 2, Ti);
+    if (wok) compute(tile, Tr);
+    if (pre)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(CPW) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  for (int tile = 0; tile < ntiles; tile += 3) {
+    step(tile, s_k0, s_k2);
+    if (tile + 1 >= ntiles) break;
+    step(tile + 1, s_k1, s_k0);
+    if (tile + 2 >= ntiles) break;
+    step(tile + 2, s_k2, s_k1);
+  }
+}
+
 int64_t index_keys_per_wave(int B, int Tq, int64_t vmax) {
   const int64_t total = (int64_t)B * Tq * vmax;
   const int64_t waves = 256 * 12;                // 256 CUs x 12 waves (three workgroups)
@@ -140,6 +305,17 @@ int64_t index_keys_per_wave(int B, int Tq, int64_t vmax) {
 
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t st) {
   if (a.vmax <= 0 || a.B == 0 || a.Tq == 0) return hipSuccess;
+  if (a.Tq >= kBlkQ && a.dI == 128 && a.HI <= 64) {
+    const int64_t groups = (int64_t)a.B * ((a.Tq + kBlkQ - 1) / kBlkQ);
+    int64_t splits = (512 + groups - 1) / groups;          // about two workgroups per CU
+    int64_t chunk = (a.vmax + splits - 1) / splits;
+    chunk = (chunk + kBlkKeys - 1) / kBlkKeys * kBlkKeys;
+    if (chunk < kBlkKeys) chunk = kBlkKeys;
+    splits = (a.vmax + chunk - 1) / chunk;
+    dim3 grid((unsigned)splits, (unsigned)((a.Tq + kBlkQ - 1) / kBlkQ), (unsigned)a.B);
+    index_score_block_kernel<<<grid, kBlkWaves * 64, 0, st>>>(a, chunk);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((a.vmax + 4 * a.keys_per_wave - 1) / (4 * a.keys_per_wave)), a.Tq, a.B);
   const int mb = (a.HI + 15) / 16;
 #define V4_IDX(DI, MB) index_score_kernel<DI, MB><<<grid, 256, 0, st>>>(a)

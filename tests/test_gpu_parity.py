@@ -149,6 +149,8 @@ INT_CASES = [
     (1, 37, 8, 32, 3000, 3000, 11800, 4, 256),     # causal block: V_t varies per query
     (1, 3, 4, 32, 70000, 70000, 279999, 4, 16),    # five parts, tiny k, heavy ties
     (1, 2, 4, 32, 100, 90, 4, 4, 8),               # V_t = 1 and 1: early positions
+    (1, 40, 64, 128, 6000, 6000, 23900, 4, 256),   # query block (prefill kernel), causal edge
+    (2, 16, 40, 128, 20000, 20000, 79990, 4, 1024),  # query block, 40 heads, two sequences
 ]
 
 
@@ -228,9 +230,10 @@ def test_topk_select_paths_bit_exact(case):
         assert np.all(np.isneginf(got_s[r, 0, len(sel):]))
 
 
-def test_index_topk_float_inputs_near_tie_tolerant():
-    B, Tq, HI, dI, N, k = 2, 2, 64, 128, 20000, 1024
-    log("index_topk float")
+@pytest.mark.parametrize("Tq", [2, 24])
+def test_index_topk_float_inputs_near_tie_tolerant(Tq):
+    B, HI, dI, N, k = 2, 64, 128, 20000, 1024
+    log(f"index_topk float Tq={Tq}")
     q, w, kk = _indexer_inputs(B, Tq, HI, dI, N, 42, False)
     q_pos0 = 4 * N - 2
     topk, ts = ops().index_topk(q, w, kk, n_entries=N, q_pos0=q_pos0, m=4, k=k, want_scores=True)
