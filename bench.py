@@ -16,7 +16,10 @@ query tokens per step / step time), per-layer rates, the per-kernel timing
 breakdown from HIP events, the roofline of the dominant kernel, and the
 float64 oracle timed on the host cores on a bounded sample.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+A "prefill" section times the 4096-token chunk appended to a 2^20-token
+context (both layers) and reports MFMA fractions for scoring and attention.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
 """
 
 import argparse
@@ -231,6 +234,91 @@ def run_breakdown(launches, steps):
     return {n: tot[n] / steps * 1e3 for n in names}   # microseconds
 
 
+def prefill_section(dev, reps):
+    """The 4096-token prefill chunk appended to a 2^20-token context (one
+    sequence): CSA layer = compress the 1024 new m=4 entries, pack the window
+    rows, indexer + top-k over ~263K entries, sparse attention; HCA layer =
+    compress the 32 new m'=128 entries, dense attention over ~8.2K entries.
+    Timed with HIP events on the launching stream."""
+    import torch
+    from long_context_sparse_csa_amd import ops, synth
+    from long_context_sparse_csa_amd.configs import PREFILL_1M as p
+    P, Tq, H, D, R = p.T, p.Tq, p.H, p.D, p.R
+    HI, dI, k, W, mh, seed = p.HI, p.dI, p.k, p.W, p.extra["m_hca"], p.seed
+    Nc, Nh = P // p.m + Tq // p.m, P // mh + Tq // mh
+    ent_c = synth.packed_rows((1, Nc), D, R, seed, "entries", dev, chunk_rows=1 << 18)
+    ent_h = synth.packed_rows((1, Nh), D, R, seed, "entries_h", dev)
+    k_idx = synth.normal((1, Nc, dI), seed, "kI", dev, dtype=torch.bfloat16)
+    q_idx = synth.normal((1, Tq, HI, dI), seed, "qI", dev, dtype=torch.bfloat16)
+    w_idx = synth.normal((1, Tq, HI), seed, "w", dev)
+    q = synth.normal((1, Tq, H, D), seed, "q", dev, dtype=torch.bfloat16)
+    raw_c = synth.normal((1, Tq + p.m, D), seed, "raw", dev, dtype=torch.bfloat16)
+    raw_h = synth.normal((1, Tq + mh, D), seed, "raw_h", dev, dtype=torch.bfloat16)
+    s_c = synth.normal((1, Tq + p.m), seed, "score", dev)
+    s_h = synth.normal((1, Tq + mh), seed, "score_h", dev)
+    b_c = synth.normal((2 * p.m,), seed, "bias", dev, std=0.1)
+    b_h = synth.normal((2 * mh,), seed, "bias_h", dev, std=0.1)
+    raw_w = synth.normal((1, Tq + W - 1, D), seed, "rawwin", dev, dtype=torch.bfloat16)
+    gamma = torch.ones(D, device=dev)
+    sink = synth.normal((H,), seed, "sink", dev)
+    win = torch.empty((1, Tq + W - 1, D + R), dtype=torch.uint8, device=dev)
+    topk = torch.empty((1, Tq, k), dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.index_topk_workspace_bytes(1, Tq, Nc, P, p.m, k), dtype=torch.uint8,
+                     device=dev)
+    calls = {
+        "compress_m4": lambda: ops.compress_pool(raw_c, s_c, b_c, gamma, ent_c, raw_pos0=P - p.m,
+                                                 m=p.m, entry0=P // p.m, n_out=Tq // p.m,
+                                                 out_row0=P // p.m),
+        "pack_window": lambda: ops.compress_pack(raw_w, gamma, win, raw_pos0=P - W + 1),
+        "index_topk": lambda: ops.index_topk(q_idx, w_idx, k_idx, n_entries=Nc, q_pos0=P, m=p.m,
+                                             k=k, topk=topk, workspace=ws),
+        "csa_attend": lambda: ops.csa_attend(q, ent_c, topk, win, gamma, sink, q_pos0=P, W=W),
+        "compress_m128": lambda: ops.compress_pool(raw_h, s_h, b_h, gamma, ent_h, raw_pos0=P - mh,
+                                                   m=mh, entry0=P // mh, n_out=Tq // mh,
+                                                   out_row0=P // mh),
+        "hca_attend": lambda: ops.hca_attend(q, ent_h, win, gamma, sink, n_entries=Nh, m=mh,
+                                             q_pos0=P, W=W),
+    }
+    for fn in calls.values():   # warm-up
+        fn()
+    torch.cuda.synchronize()
+    ms = {}
+    for name, fn in calls.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / reps
+    # algorithmic FLOPs: every (query, visible key) pair once
+    vis_c = sum(min(Nc, (P + r + 1) // p.m) for r in range(Tq))
+    vis_h = sum(min(Nh, (P + r + 1) // mh) for r in range(Tq))
+    fl_idx = 2 * HI * dI * vis_c
+    fl_csa = 4 * H * D * (k + W) * Tq
+    fl_hca = 4 * H * D * (vis_h + W * Tq)
+    mfma_peak = 2500.0   # TFLOP/s, dense bf16, published
+    t_csa = ms["compress_m4"] + ms["pack_window"] + ms["index_topk"] + ms["csa_attend"]
+    t_hca = ms["compress_m128"] + ms["hca_attend"]
+
+    def tf(fl, t):
+        return round(fl / (t * 1e-3) / 1e12, 1)
+    return {
+        "workload": "prefill_4096_on_1m: 4096 new tokens after 2^20 cached, one sequence, "
+                    "H=64 D=512 HI=64 dI=128 k=1024 W=128, m=4 (CSA) and m'=128 (HCA)",
+        "ms": {n: round(v, 3) for n, v in ms.items()},
+        "csa_layer_tokens_per_s": round(Tq / (t_csa * 1e-3), 1),
+        "hca_layer_tokens_per_s": round(Tq / (t_hca * 1e-3), 1),
+        "index_topk_TFLOPs": tf(fl_idx, ms["index_topk"]),
+        "index_topk_mfma_frac": round(tf(fl_idx, ms["index_topk"]) / mfma_peak, 4),
+        "csa_attend_TFLOPs": tf(fl_csa, ms["csa_attend"]),
+        "hca_attend_TFLOPs": tf(fl_hca, ms["hca_attend"]),
+        "hca_attend_mfma_frac": round(tf(fl_hca, ms["hca_attend"]) / mfma_peak, 4),
+        "mfma_peak_TFLOPs": mfma_peak,
+        "reps": reps,
+    }
+
+
 def cpu_baseline(inp, budget_s):
     """The float64 oracle on a bounded sample of the same inputs: whole CSA
     and HCA layers for single sequences, alternating, until the budget."""
@@ -304,6 +392,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 4096-token prefill section")
     ap.add_argument("--counters", action="store_true",
                     help="no timing: run a 1 GiB elementwise copy (known bytes) and a few "
                          "decode steps for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes")
@@ -395,6 +485,10 @@ def main():
         "roofline": roofline,
         "wall_s": round(wall, 3),
     }
+    if not args.no_prefill:
+        log("prefill chunk")
+        res["prefill"] = prefill_section(dev, 3)
+        log("prefill (ms): " + ", ".join(f"{k} {v}" for k, v in res["prefill"]["ms"].items()))
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle)")
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
