@@ -183,9 +183,14 @@ int v4attn_topk_select(const float* scores, int64_t score_stride, int B,
  *                                   positions max(0, t-W+1)..t.
  *   gamma_q f32 [D];  sink f32 [H]
  *   out     bf16 [B, Tq, H, D] out;  lse f32 [B, Tq, H] out, nullable
- *   ws / ws_bytes  >= v4attn_csa_attend_workspace(...) bytes
- * Accumulation is fp32; q~ and the probabilities enter the matrix cores as
- * bf16, FP8 rows are widened exactly to bf16.
+ *   ws / ws_bytes  >= v4attn_csa_attend_workspace(...) bytes (split
+ *              partials of long rows; 0 is possible); contents on entry are
+ *              ignored
+ * Accumulation is fp32.  q~ is rounded to bf16; on the E4M3 dims it enters
+ * the FP8 matrix cores as the exact sum of two E4M3 terms, and so do the
+ * probabilities (each 64-row block of a head scaled by its own power of
+ * two, which the cores undo); on the bf16 dims both are bf16.  Rows are
+ * never widened: the E4M3 bytes go into the matrix cores as stored.
  */
 size_t v4attn_csa_attend_workspace(int B, int Tq, int H, int D, int k, int W);
 int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries,

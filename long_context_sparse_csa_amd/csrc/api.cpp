@@ -93,14 +93,25 @@ IndexWs index_ws(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m, int k)
   return w;
 }
 
-size_t attend_ws(int B, int Tq, int H, int D, int64_t rows_max, int* splits) {
-  const int s = v4::attend_splits(B, Tq, rows_max);
+// Attention workspace (splits > 1): the split partials, O then (max, sum).
+size_t attend_ws(int B, int Tq, int H, int D, int64_t rows_max, bool csa, int* splits) {
+  const int s = v4::attend_splits(B, Tq, rows_max, csa);
   if (splits) *splits = s;
   if (s <= 1) return 0;
   const int64_t q = (int64_t)B * Tq;
   size_t o = (size_t)(q * s * H * D) * sizeof(float);
   o = (o + 255) / 256 * 256;
   return o + (size_t)(q * s * H * 2) * sizeof(float);
+}
+
+// Points the kernel arguments at their parts of the workspace.
+void attend_ws_layout(v4::AttendArgs& a, void* ws) {
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  a.part_o = reinterpret_cast<float*>(w);
+  const int64_t q_rows = (int64_t)a.B * a.Tq;
+  size_t o_bytes = (size_t)(q_rows * a.splits * a.H * a.D) * sizeof(float);
+  o_bytes = (o_bytes + 255) / 256 * 256;
+  a.part_ml = a.splits > 1 ? reinterpret_cast<float*>(w + o_bytes) : nullptr;
 }
 
 int check_attend_common(const uint16_t* q, const uint8_t* entries, const uint8_t* win,
@@ -332,7 +343,7 @@ int v4attn_index_topk(const uint16_t* q_idx, const float* w_idx, const uint16_t*
 
 size_t v4attn_csa_attend_workspace(int B, int Tq, int H, int D, int k, int W) {
   if (B < 0 || Tq < 0 || H < 1 || D < 1 || k < 1 || W < 0) return 0;
-  return attend_ws(B, Tq, H, D, (int64_t)k + W, nullptr);
+  return attend_ws(B, Tq, H, D, (int64_t)k + W, true, nullptr);
 }
 
 int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
@@ -346,7 +357,7 @@ int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries, const int32_t* 
   if (!topk) return fail(V4ATTN_EINVAL, "null topk");
   if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
   int splits = 1;
-  const size_t need = attend_ws(B, Tq, H, D, (int64_t)k + W, &splits);
+  const size_t need = attend_ws(B, Tq, H, D, (int64_t)k + W, true, &splits);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
@@ -355,11 +366,7 @@ int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries, const int32_t* 
   a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R; a.Ncap = Ncap; a.k = k; a.n_entries = 0;
   a.m = 1; a.W = W; a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps; a.rope_base = rope_base;
   a.out = out; a.lse = lse; a.splits = splits;
-  a.part_o = static_cast<float*>(ws);
-  const int64_t q_rows = (int64_t)B * Tq;
-  size_t o_bytes = (size_t)(q_rows * splits * H * D) * sizeof(float);
-  o_bytes = (o_bytes + 255) / 256 * 256;
-  a.part_ml = splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + o_bytes) : nullptr;
+  attend_ws_layout(a, ws);
   a.rows_max = (int64_t)k + W;
   return hip_status(v4::launch_attend(a, (hipStream_t)stream), "CSA attend launch");
 }
@@ -367,7 +374,7 @@ int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries, const int32_t* 
 size_t v4attn_hca_attend_workspace(int B, int Tq, int H, int D, int64_t n_entries, int m,
                                    int64_t q_pos0, int W) {
   if (B < 0 || Tq < 0 || H < 1 || D < 1 || n_entries < 0 || m < 1 || q_pos0 < 0 || W < 0) return 0;
-  return attend_ws(B, Tq, H, D, vmax_of(Tq, n_entries, q_pos0, m) + W, nullptr);
+  return attend_ws(B, Tq, H, D, vmax_of(Tq, n_entries, q_pos0, m) + W, false, nullptr);
 }
 
 int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* win,
@@ -382,7 +389,7 @@ int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
   if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
   const int64_t rows_max = vmax_of(Tq, n_entries, q_pos0, m) + W;
   int splits = 1;
-  const size_t need = attend_ws(B, Tq, H, D, rows_max, &splits);
+  const size_t need = attend_ws(B, Tq, H, D, rows_max, false, &splits);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
@@ -391,11 +398,7 @@ int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
   a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R; a.Ncap = Ncap; a.k = 0; a.n_entries = n_entries;
   a.m = m; a.W = W; a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps; a.rope_base = rope_base;
   a.out = out; a.lse = lse; a.splits = splits;
-  a.part_o = static_cast<float*>(ws);
-  const int64_t q_rows = (int64_t)B * Tq;
-  size_t o_bytes = (size_t)(q_rows * splits * H * D) * sizeof(float);
-  o_bytes = (o_bytes + 255) / 256 * 256;
-  a.part_ml = splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + o_bytes) : nullptr;
+  attend_ws_layout(a, ws);
   a.rows_max = rows_max;
   return hip_status(v4::launch_attend(a, (hipStream_t)stream), "HCA attend launch");
 }

@@ -11,35 +11,36 @@
 // Affordable", section "Two ways to shrink attention, interleaved").  The
 // window, the entries and the sink share one softmax.
 //
-// Design.  One workgroup of eight waves owns one query token and one range of
+// Design.  One workgroup of four waves owns one query token and one range of
 // its rows (entries, then window rows), so every packed row is fetched from
-// HBM once for all 64 heads.  Rows are gathered (CSA: through the top-k list)
-// 64 at a time straight into LDS with global_load_lds (no staging registers,
-// no conversion on the way; four waves move 16 rows each) and kept in their
-// packed form: 576 bytes a row, E4M3 then bf16, 16-byte chunks XOR-swizzled
-// by row so that both LDS read patterns below are free of bank conflicts.
-// Two tile buffers alternate: the next tile lands while the current one is
-// used.
-//   Waves w and w+4 share heads 16(w%4)..+15 and split the dims in halves:
-// each contracts S over its half (holding only that half of q~), the pair
-// adds the two partial S through LDS, both run the same softmax, and each
-// accumulates the output for its half of the dims:
-//   S^T = K q~^T : K rows are the A operand, read 16 bytes a lane (two k-steps
-//                  of E4M3, widened exactly to bf16 in registers); q~ is the B
-//                  operand, held in registers with its dims permuted to match
-//                  the order in which the lanes read the row;
+// HBM once for all heads.  Rows are gathered (CSA: through the top-k list)
+// 128 at a time straight into LDS with global_load_lds (no staging
+// registers, no conversion; each wave moves 32 rows) and kept in their packed
+// form: 576 bytes a row, E4M3 then bf16, 16-byte chunks XOR-swizzled by row
+// so that every LDS read pattern below is free of bank conflicts.  Two tile
+// buffers alternate: the next tile lands while the current one is used.
+//   Wave w owns heads 16w..16w+15 over all dims and all rows, with its own
+// online softmax, so the waves share nothing but the tiles.  Both products
+// run on the 16x16 MFMAs with one head per lane column:
+//   S^T = K q~^T : K rows are the A operand straight from the tile; the E4M3
+//                  dims take the f8f6f4 MFMA (16x16x128) with q~ as two E4M3
+//                  terms (hi + lo), the bf16 dims the bf16 MFMA (16x16x32);
 //   O^T += V^T P^T : V^T comes from the packed rows with the gfx950
 //                  transposing LDS reads (ds_read_b64_tr_b8 for E4M3 dims,
-//                  ds_read_b64_tr_b16 for the bf16 ones), so nothing is stored
-//                  twice; the probabilities stay in the registers the S^T
-//                  accumulators left them in, because the key order of the
-//                  transposing reads is permuted to match (k slot j of lane
-//                  group g = key 4g+j or 16+4g+j-4 of each 32-key half).
-// O^T keeps one head per lane, so the online-softmax rescale needs no
+//                  ds_read_b64_tr_b16 for bf16), so the E4M3 dims go into the
+//                  f8f6f4 MFMA as stored; P stays in the registers the S^T
+//                  accumulators left it in, because the row order of the
+//                  transposing reads is permuted to match.
+// P enters the f8f6f4 product as two E4M3 terms as well.  Each 64-row scale
+// block of one head is exponentiated against its own power of two (its
+// largest p lands in (128, 256]), and the MFMA's per-block E8M0 scale on that
+// operand brings it back to the head's running maximum, so rows far below the
+// maximum keep their relative precision instead of flushing to zero.  O^T
+// keeps one head per lane column, so the online-softmax rescale needs no
 // shuffles, and the running maximum moves only when it grows by more than
-// 2^8 (probabilities stay below 256, exact enough in bf16 and fp32), which
-// skips almost every rescale.  Long rows are split over several workgroups
-// whose (O, max, sum) partials a merge kernel combines with the sink.
+// 2^64 (fp32 and the E8M0 scales hold that range), in practice once, outside
+// the hot loop.  Long rows are split over several workgroups whose
+// (O, max, sum) partials a merge kernel combines with the sink.
 #include <type_traits>
 
 #include "common.hpp"
@@ -47,10 +48,10 @@
 
 namespace v4 {
 
-constexpr int kAttTile = 64;      // rows per LDS tile
-constexpr int kAttThreads = 512;  // eight waves: four head groups x two dim halves
-constexpr int kMaxTopk = 4096;    // largest k the CSA kernel stages in LDS
-constexpr float kLazyMax = 8.0f;  // log2 headroom before the running max moves
+constexpr int kAttRows = 128;      // rows per LDS tile
+constexpr int kAttThreads = 256;   // four waves of 16 heads
+constexpr int kSelCap = 2048;      // CSA: top-k slots of one split staged in LDS
+constexpr float kLazyMax = 64.0f;  // log2 headroom before the running max moves
 constexpr float kNoMax = -1.0e30f; // running-max floor (no key seen yet)
 
 // Source of absent rows (masked out of the softmax; zeros keep 0 * V finite).
@@ -62,25 +63,21 @@ struct AttGeom {
   static constexpr int ROW = D + R;            // packed bytes per row (HBM and LDS)
   static constexpr int CPR = ROW / 16;         // 16-byte chunks per row
   static constexpr int FP8_CPR = (D - R) / 16; // of which E4M3
-  static constexpr int KSTEPS = D / 32;        // 32-dim k-steps of S^T
-  static constexpr int NF8 = (D - 128) / 128;  // 128-dim E4M3 k-steps on the f8f6f4 MFMA
-  static constexpr int NF0 = (NF8 + 1) / 2;    // of which in dim half 0
-  static constexpr int TAIL = D - 128;         // first dim of the bf16-MFMA tail
-  static_assert(D % 128 == 0, "head dim is a multiple of 128");
-  static constexpr int DB = D / 16;            // 16-dim blocks of O^T
-  static constexpr int FB = (D - R) / 16;      // of which over E4M3 dims
-  static constexpr int TILE_BYTES = kAttTile * ROW;
-  static constexpr int DBH = DB / 2;           // output blocks per dim half
-  static constexpr int WPW = CPR / 4;          // 1 KiB copies per staging wave per tile (16 rows)
-  static constexpr int HALF = 32 * ROW;        // byte offset of the second 32-key half
+  static constexpr int NJ = (D - R + 127) / 128; // 128-dim E4M3 k-steps of S^T (the last half full)
+  static constexpr int NB8 = (D - R) / 16;     // 16-dim E4M3 blocks of O^T
+  static constexpr int NB = D / 16;            // all 16-dim blocks (the last four bf16)
+  static constexpr int TILE_BYTES = kAttRows * ROW;
+  static constexpr int WPW = ROW / 32;         // 1 KiB copies per wave per tile (32 rows)
+  static_assert(D >= 128 && (D - R) % 128 == 64, "E4M3 dims end half way through a k-step");
   static_assert(FP8_CPR % 4 == 0 && CPR % 4 == 0, "the chunk swizzle stays inside a region");
-  static_assert(ROW <= 1024, "absent rows read the zero row");
+  static_assert(ROW <= 1024 && ROW % 32 == 0, "absent rows read the zero row");
 };
 
-// Physical chunk = logical chunk ^ swz(row): rows 4i..4i+3 rotate the four
-// chunks of every aligned group differently, which spreads 16 rows of one
-// logical chunk over all 16 chunk slots of a 256-byte bank line.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// Physical chunk = logical chunk ^ swz(row) within aligned groups of four
+// chunks.  swz takes row bit 2 and bits 3 ^ 4: 16 consecutive rows spread one
+// logical chunk over all 16 chunk slots of a 256-byte bank line, and so do
+// the row sets of the transposing reads below.
+__device__ __forceinline__ int swz(int row) { return ((row >> 2) & 1) | ((((row >> 3) ^ (row >> 4)) & 1) << 1); }
 
 // 64 lanes x 16 bytes from per-lane global addresses into 1 KiB of LDS at
 // `dst` (+16 bytes per lane).  Written as asm so that the compiler does not
@@ -91,6 +88,13 @@ __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ void copy_to_lds16(const void* src, V4_LDS void* dst) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// The same copy from a uniform 64-bit base plus a per-lane 32-bit offset
+// (the scalar-base addressing form: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void copy_to_lds16_sbase(const void* base, unsigned off, V4_LDS void* dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 
 struct RowSpace {
@@ -114,41 +118,59 @@ __device__ __forceinline__ RowSpace row_space(const AttendArgs& a, bool csa, int
   return rs;
 }
 
+// Rows of one key range per split: a whole number of tiles.
+__host__ __device__ inline int64_t split_chunk(int64_t n_rows, int splits) {
+  const int64_t c = (n_rows + splits - 1) / splits;
+  return (c + kAttRows - 1) / kAttRows * kAttRows;
+}
+
 template <int D, bool CSA>
 __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
   using G = AttGeom<D>;
-  constexpr int R = G::R;
+  constexpr int R = G::R, NJ = G::NJ, NB8 = G::NB8, NB = G::NB, ROW = G::ROW;
+  constexpr int BFC = G::FP8_CPR;   // first bf16 chunk
   const int qr = blockIdx.y;
   const int split = blockIdx.x;
   const int b = qr / a.Tq, r = qr % a.Tq;
   const int64_t t = a.q_pos0 + r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hg = wave & 3, hf = wave >> 2;   // head group, dim half
-  const int g = lane >> 4, c = lane & 15;
-  const int head = hg * 16 + c;
-  const bool active = hg * 16 < a.H;
+  const int c = lane & 15, g = lane >> 4;   // lane column (head / row / dim), k group
+  const int head = wave * 16 + c;
 
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[2][G::TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) f32x4 s_x[8][4][64];  // partial S^T for the pair
-  __shared__ unsigned s_v[2][4];   // per buffer: row-present bits, 16 rows per staging wave
+  __shared__ unsigned s_v[2][4];   // per buffer: row-present bits, 32 rows per staging wave
   __shared__ float s_cs[R / 2][2];
-  __shared__ __attribute__((aligned(16))) float s_gamma[D];
-  __shared__ int s_sel[CSA ? kMaxTopk : 1];  // this split's slice of the top-k list
+  __shared__ int s_sel[CSA ? kSelCap : 1];  // this split's slice of the top-k list
+  __shared__ __attribute__((aligned(16))) uint8_t s_zero[32];   // K bytes past the E4M3 dims
 
   const RowSpace rs = row_space(a, CSA, t);
-  int64_t chunk = (rs.n_rows + a.splits - 1) / a.splits;
-  chunk = (chunk + kAttTile - 1) / kAttTile * kAttTile;
+  const int64_t chunk = split_chunk(rs.n_rows, a.splits);
   const int64_t row_beg = (int64_t)split * chunk;
   int64_t row_end = row_beg + chunk;
   if (row_end > rs.n_rows) row_end = rs.n_rows;
-  const int ntiles = row_end > row_beg ? (int)((row_end - row_beg + kAttTile - 1) / kAttTile) : 0;
+  const int ntiles = row_end > row_beg ? (int)((row_end - row_beg + kAttRows - 1) / kAttRows) : 0;
   // split-local row numbers fit in 32 bits
   const int nloc = (int)(row_end - row_beg);
   const int ent_loc = (int)max((int64_t)0, min(rs.n_ent, row_end) - row_beg);  // entry rows here
-  const uint8_t* ent_b = a.entries + (int64_t)b * a.Ncap * G::ROW;
+  const uint8_t* ent_b = a.entries + (int64_t)b * a.Ncap * ROW;
   const uint8_t* win_b = a.win + ((int64_t)b * (a.Tq + a.W - 1) +
-                                  (rs.win_lo - (a.q_pos0 - (a.W - 1)))) * G::ROW;
+                                  (rs.win_lo - (a.q_pos0 - (a.W - 1)))) * ROW;
   const int win_first = (int)(rs.n_ent - row_beg);   // split-local row of the first window row
+
+  // q first, so that its loads are not queued behind the first tile's copies
+  constexpr int NSL = 4 * NJ + 2;
+  auto slot_dim = [&](int sl) {
+    return sl < 4 * NJ ? 128 * (sl >> 2) + 32 * g + 8 * (sl & 3) : (D - R) + 32 * (sl - 4 * NJ) + 8 * g;
+  };
+  // slots of the last E4M3 k-step beyond the E4M3 dims stay zero
+  auto slot_ok = [&](int sl) { return sl >= 4 * NJ || slot_dim(sl) < D - R; };
+  const uint16_t* qp = a.q + ((int64_t)qr * a.H + min(head, a.H - 1)) * D;
+  u32x4 qv[NSL];
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) {
+    qv[sl] = u32x4{0u, 0u, 0u, 0u};
+    if (slot_ok(sl)) qv[sl] = *reinterpret_cast<const u32x4*>(qp + slot_dim(sl));
+  }
 
   if (tid < R / 2) {
     float cs, sn;
@@ -156,13 +178,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
     s_cs[tid][0] = cs;
     s_cs[tid][1] = sn;
   }
-  for (int d = 4 * tid; d < D; d += 4 * kAttThreads)
-    *reinterpret_cast<f32x4*>(&s_gamma[d]) = *reinterpret_cast<const f32x4*>(a.gamma_q + d);
   if constexpr (CSA) {
     const int32_t* sel = a.topk + (int64_t)qr * a.k + row_beg;
     for (int x = tid; x < ent_loc; x += kAttThreads) s_sel[x] = sel[x];
   }
-  __syncthreads();
+  if (tid < 8) reinterpret_cast<unsigned*>(s_zero)[tid] = 0u;
+  // LDS writes only: the q loads stay in flight across this barrier
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // split-local row x -> its packed row in HBM, or nullptr if absent
   auto row_ptr = [&](int x) -> const uint8_t* {
@@ -173,83 +195,109 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
       j = s_sel[ent ? x : 0];
       ok = ok && (!ent || (j >= 0 && j < a.Ncap));
     }
-    const uint8_t* p = ent ? ent_b + j * G::ROW : win_b + (int64_t)(x - win_first) * G::ROW;
+    const uint8_t* p = ent ? ent_b + j * ROW : win_b + (int64_t)(x - win_first) * ROW;
     return ok ? p : nullptr;
   };
 
-  // ---- staging (waves 0-3): wave w copies tile rows 16w..16w+15 as WPW
-  // windows of 64 16-byte slots; slot s holds physical chunk s % CPR of row
-  // s / CPR, loaded from logical chunk (s % CPR) ^ swz(row).  Lane l resolves
-  // row 16w + l%16.
+  // ---- staging: wave w copies tile rows 32w..32w+31 as WPW windows of 64
+  // 16-byte slots; slot s holds physical chunk s % CPR of row s / CPR, loaded
+  // from logical chunk (s % CPR) ^ swz(row).  Lane l resolves row 32w + l%32.
   const uint8_t* zero_row = g_zero_row;
+  // Per-lane source offsets of the copies within a run of contiguous rows:
+  // slot 64 i + lane -> row 32w + s / CPR, logical chunk of physical s % CPR.
+  unsigned coff[G::WPW];
+#pragma unroll
+  for (int i = 0; i < G::WPW; ++i) {
+    const int sl = 64 * i + lane;
+    const int rl = sl / G::CPR, pc = sl - rl * G::CPR;
+    coff[i] = (unsigned)((32 * wave + rl) * ROW + 16 * ((pc & ~3) | ((pc & 3) ^ swz(rl))));
+  }
+  // A whole tile of contiguous present rows (HCA entries, or window rows) is
+  // copied from one uniform base, without per-row lookups; its copies are
+  // spread over the S^T steps of the previous tile (contig_base), the rest go
+  // out at once (issue_tile).
+  auto contig_base = [&](int tile) -> const uint8_t* {
+    const int x0 = tile * kAttRows;
+    const bool full = x0 + kAttRows <= nloc;
+    const bool all_ent = x0 + kAttRows <= ent_loc, all_win = x0 >= ent_loc;
+    if (!full || !((!CSA && all_ent) || all_win)) return nullptr;
+    return all_win ? win_b + (int64_t)(x0 - win_first) * ROW : ent_b + (int64_t)(row_beg + x0) * ROW;
+  };
+  auto issue_copy = [&](const uint8_t* base, int buf, int i) {
+    copy_to_lds16_sbase(base, coff[i], (V4_LDS void*)(s_tile[buf] + 32 * wave * ROW + 1024 * i));
+  };
   auto issue_tile = [&](int tile, int buf) {
-    const uint8_t* rp = row_ptr(tile * kAttTile + 16 * wave + (lane & 15));
+    if (const uint8_t* base = contig_base(tile)) {
+      if (lane == 0) s_v[buf][wave] = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < G::WPW; ++i) issue_copy(base, buf, i);
+      return;
+    }
+    const uint8_t* rp = row_ptr(tile * kAttRows + 32 * wave + (lane & 31));
     const bool ok = rp != nullptr;
     const unsigned long long bal = __ballot(ok);
-    if (lane == 0) s_v[buf][wave] = (unsigned)(bal & 0xFFFFull);
+    if (lane == 0) s_v[buf][wave] = (unsigned)(bal & 0xFFFFFFFFull);
     const long long rpl = (long long)(uintptr_t)(ok ? rp : zero_row);
-    uint8_t* Tw = s_tile[buf] + 16 * wave * G::ROW;
+    uint8_t* Tw = s_tile[buf] + 32 * wave * ROW;
+    // the slot arithmetic below is redone per tile (an opaque lane index keeps
+    // the compiler from hoisting ~2 registers per copy out of the tile loop)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < G::WPW; ++i) {
-      const int sl = 64 * i + lane;
+      const int sl = 64 * i + ln;
       const int rl = sl / G::CPR, pc = sl - rl * G::CPR;
-      const uint8_t* src = (const uint8_t*)(uintptr_t)__shfl(rpl, rl) + 16 * (pc ^ swz(rl));
+      const uint8_t* src = (const uint8_t*)(uintptr_t)__shfl(rpl, rl) +
+                           16 * ((pc & ~3) | ((pc & 3) ^ swz(rl)));
       copy_to_lds16(src, (V4_LDS void*)(Tw + 1024 * i));
     }
   };
+  if (ntiles > 0) issue_tile(0, 0);
 
-  if (ntiles > 0 && wave < 4) issue_tile(0, 0);
-
-  // ---- q~ = RoPE_t(RMSNorm(q)) scaled by 2^qe (per head, exact), as the B
-  // operand of S^T.  The E4M3 dims run on the f8f6f4 MFMA with q~ split into
-  // two E4M3 terms (hi + lo: about 2^-8 relative, the scale keeps the lo term
-  // out of the subnormals); the last 64 E4M3 dims and the bf16 dims run on
-  // the bf16 MFMA.  Lane group g owns 8-dim slots: per f8 k-step s the dims
-  // 128s + 32g .. +31 (slots 4s .. 4s+3), then four tail slots t with dims
-  // TAIL + 32t + 8g .. +7 (E4M3 for t < 2, bf16 for t = 2, 3).  Dim half 0
-  // contracts f8 k-steps [0, NF0) and the bf16 tail, half 1 the f8 k-steps
-  // [NF0, NF8) and the E4M3 tail.
-  constexpr int NF8 = G::NF8, NF0 = G::NF0, TAIL = G::TAIL;
-  constexpr int NQ = NF0 > 0 ? NF0 : 1;
-  i32x8 qh[NQ], ql[NQ];
+  // ---- q~ = RoPE_t(RMSNorm(q)), rounded to bf16 and scaled by 2^qe (per
+  // head, exact), as the B operand of S^T.  Lane (c, g) holds head c's dims
+  // 128 j + 32 g + [0, 32) of every E4M3 k-step j (zero past the E4M3 dims)
+  // and dims (D - R) + 32 s + 8 g + [0, 8) of the two bf16 k-steps s.  On the
+  // E4M3 dims the bf16 value goes into the f8f6f4 MFMA as the exact sum of
+  // two E4M3 terms (hi = its E4M3 rounding, lo = the rest, which has at most
+  // four significant bits; qe puts the head's largest |q~| in [128, 256), so
+  // lo stays out of the subnormals for every |q~| above 2^-9 of the largest).
+  // Slots of 8 dims: 4j + v for the E4M3 dims, 4 NJ + s for the bf16 ones
+  // (loaded at the top of the kernel).
+  i32x8 qh[NJ], ql[NJ];
   bf16x8 qt[2];
   float qscale_inv;   // 2^-qe
   {
-    auto slot_dim = [&](int sl) {
-      return sl < 4 * NF8 ? 128 * (sl >> 2) + 32 * g + 8 * (sl & 3) : TAIL + 32 * (sl - 4 * NF8) + 8 * g;
-    };
-    const uint16_t* qp = a.q + ((int64_t)qr * a.H + min(head, a.H - 1)) * D;
-    u32x4 qv[G::KSTEPS];
-#pragma unroll
-    for (int sl = 0; sl < G::KSTEPS; ++sl)
-      qv[sl] = *reinterpret_cast<const u32x4*>(qp + slot_dim(sl));
     if (head >= a.H) {
 #pragma unroll
-      for (int sl = 0; sl < G::KSTEPS; ++sl) qv[sl] = u32x4{0u, 0u, 0u, 0u};
+      for (int sl = 0; sl < NSL; ++sl) qv[sl] = u32x4{0u, 0u, 0u, 0u};
     }
     float ss = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < G::KSTEPS; ++sl) {
-      const unsigned w[4] = {qv[sl].x, qv[sl].y, qv[sl].z, qv[sl].w};
+    for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_bits_to_f32(w[e] & 0xFFFFu), hi = bf16_bits_to_f32(w[e] >> 16);
+        const float lo = bf16_bits_to_f32(qv[sl][e] & 0xFFFFu), hi = bf16_bits_to_f32(qv[sl][e] >> 16);
         ss += lo * lo + hi * hi;
       }
-    }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
     const float rsn = 1.0f / sqrtf(ss / (float)D + a.eps);
-    // q~ of one slot (8 dims), rotated where the dims are rotary
-    auto qtilde = [&](int sl, float (&qf)[8]) {
-      const int d0 = slot_dim(sl);
-      const unsigned w[4] = {qv[sl].x, qv[sl].y, qv[sl].z, qv[sl].w};
+    // q~ of each slot, rotated where the dims are rotary, rounded to bf16 in place
+    float mx = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      const int d0 = slot_ok(sl) ? slot_dim(sl) : 0;
+      const f32x4 ga = *reinterpret_cast<const f32x4*>(a.gamma_q + d0);
+      const f32x4 gb = *reinterpret_cast<const f32x4*>(a.gamma_q + d0 + 4);
+      const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      float qf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qf[2 * e] = s_gamma[d0 + 2 * e] * (bf16_bits_to_f32(w[e] & 0xFFFFu) * rsn);
-        qf[2 * e + 1] = s_gamma[d0 + 2 * e + 1] * (bf16_bits_to_f32(w[e] >> 16) * rsn);
+        qf[2 * e] = gm[2 * e] * (bf16_bits_to_f32(qv[sl][e] & 0xFFFFu) * rsn);
+        qf[2 * e + 1] = gm[2 * e + 1] * (bf16_bits_to_f32(qv[sl][e] >> 16) * rsn);
       }
-      if (d0 >= D - R) {
+      if (sl >= 4 * NJ) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const int i = (d0 + e - (D - R)) >> 1;
@@ -259,289 +307,347 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
           qf[e + 1] = x0 * sn + x1 * cs;
         }
       }
-    };
-    // per-head scale: the largest |q~| lands in [128, 256)
-    float mx = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < G::KSTEPS; ++sl) {
-      float qf[8];
-      qtilde(sl, qf);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qf[e]));
+      for (int e = 0; e < 4; ++e) {
+        qv[sl][e] = pack_bf16x2(qf[2 * e], qf[2 * e + 1]);
+        mx = fmaxf(mx, fmaxf(fabsf(qf[2 * e]), fabsf(qf[2 * e + 1])));
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const int qe = mx > 0.f ? 8 - __builtin_amdgcn_frexp_expf(mx) : 0;
     qscale_inv = ldexpf(1.0f, -qe);
-    // The operands of this wave's half; the half is a compile-time constant
-    // inside so that every slot index is one (no run-time register indexing).
-    auto build = [&](auto half) {
-      constexpr int HF = decltype(half)::value;
-      // f8 k-steps: hi and lo E4M3 terms, 4 bytes per dword in dim order
 #pragma unroll
-      for (int u = 0; u < NQ; ++u) {
-        const int s8 = HF == 0 ? u : NF0 + u;
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float qf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          if (s8 < NF8) qtilde(4 * s8 + v, qf);
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            float x[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = ldexpf(qf[4 * h2 + e], qe);
-            int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-            hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
-            const float r[4] = {x[0] - __builtin_amdgcn_cvt_f32_fp8(hw, 0),
-                                x[1] - __builtin_amdgcn_cvt_f32_fp8(hw, 1),
-                                x[2] - __builtin_amdgcn_cvt_f32_fp8(hw, 2),
-                                x[3] - __builtin_amdgcn_cvt_f32_fp8(hw, 3)};
-            int lw = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
-            lw = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], lw, true);
-            qh[u][2 * v + h2] = hw;
-            ql[u][2 * v + h2] = lw;
-          }
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const unsigned w0 = qv[4 * j + v][2 * h2], w1 = qv[4 * j + v][2 * h2 + 1];
+          const float x0 = ldexpf(bf16_bits_to_f32(w0 & 0xFFFFu), qe), x1 = ldexpf(bf16_bits_to_f32(w0 >> 16), qe);
+          const float x2 = ldexpf(bf16_bits_to_f32(w1 & 0xFFFFu), qe), x3 = ldexpf(bf16_bits_to_f32(w1 >> 16), qe);
+          int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+          hw = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hw, true);
+          const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+          const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+          int lw = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - b01.x, x1 - b01.y, 0, false);
+          lw = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - b23.x, x3 - b23.y, lw, true);
+          qh[j][2 * v + h2] = hw;
+          ql[j][2 * v + h2] = lw;
         }
-      }
-      // tail k-steps: half 0 the bf16 dims (t = 2, 3), half 1 the E4M3 tail (t = 0, 1)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        float qf[8];
-        qtilde(4 * NF8 + (HF == 0 ? 2 : 0) + t2, qf);
-        u32x4 pk = {pack_bf16x2(ldexpf(qf[0], qe), ldexpf(qf[1], qe)),
-                    pack_bf16x2(ldexpf(qf[2], qe), ldexpf(qf[3], qe)),
-                    pack_bf16x2(ldexpf(qf[4], qe), ldexpf(qf[5], qe)),
-                    pack_bf16x2(ldexpf(qf[6], qe), ldexpf(qf[7], qe))};
-        qt[t2] = __builtin_bit_cast(bf16x8, pk);
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned w = qv[4 * NJ + s2][e];
+        pk[e] = pack_bf16x2(ldexpf(bf16_bits_to_f32(w & 0xFFFFu), qe), ldexpf(bf16_bits_to_f32(w >> 16), qe));
       }
-    };
-    if (hf == 0) build(std::integral_constant<int, 0>{});
-    else build(std::integral_constant<int, 1>{});
+      qt[s2] = __builtin_bit_cast(bf16x8, pk);
+    }
   }
 
   const float sl2 = a.scale * kLog2e * qscale_inv;   // undoes the q~ scale
-  // running max starts at a finite floor, so masked keys (-inf) give p = 0
-  // without special cases; an untouched max marks "no row seen"
-  float m_run = kNoMax, l_run = 0.f;  // per head (lane column), log2 units
-  f32x4 o[G::DBH];
+  // running max (log2 units, an integer once set) starts at a finite floor,
+  // so masked keys (-inf) give p = 0 without special cases
+  float m_run = kNoMax, l_run = 0.f;   // per head (lane column); l_run: this lane's rows
+  f32x4 o[NB];
 #pragma unroll
-  for (int db = 0; db < G::DBH; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < NB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // per-lane LDS offsets within a tile (second 32-key half: + HALF)
-  //  K rows of the bf16 tail (A of S^T): row kb*16 + c, chunk FP8_CPR + 4t + g
-  int koff[2];
+  // Per-lane LDS offsets.  Accumulator i of S^T row block rb (16 rows) in
+  // lane group g is row 16 rb + 4 g + i; swz(16 rb + x) = swz(x) ^ 2 (rb & 1).
+  //  K, E4M3 k-step j (A of S^T): row 16 rb + c, chunks 8j + 2g + x:
+  //   koff[rb & 1][x] + 16 rb ROW + 128 j
+  int koff[2][2];
+  //  K, bf16 k-step s: chunk BFC + 4s + g: ktoff[rb & 1] + 16 rb ROW + 64 s
+  int ktoff[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int row = kb * 16 + c;
-    koff[kb] = row * G::ROW + 16 * (g ^ swz(row));
+  for (int p = 0; p < 2; ++p) {
+    const int sw = swz(c) ^ (2 * p);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) koff[p][x] = c * ROW + 64 * (g >> 1) + 16 * ((2 * (g & 1) + x) ^ sw);
+    ktoff[p] = c * ROW + 16 * (BFC + (g ^ sw));
   }
-  //  K rows for the f8f6f4 k-steps: chunks 8s + 2g + i (i = 0, 1) -> + 128s
-  int koff8[2][2];
-  //  K rows for the E4M3 tail: dims TAIL + 32t + 8g, 8 bytes
-  int ktoff[2][2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int row = kb * 16 + c, sw = swz(row);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) koff8[kb][i] = row * G::ROW + 16 * ((2 * g + i) ^ sw);
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-      ktoff[kb][t2] = row * G::ROW + 16 * (TAIL / 16 + ((2 * t2 + (g >> 1)) ^ sw)) + 8 * (g & 1);
-  }
-  //  V^T via tr_b8: source lane (g, j = (lane&15)>>1, h = lane&1) addresses
-  //  key slot j of group g, dims 16db + 8h; chunk 4a + b -> + 64a
+  //  V^T via tr_b8: source lane (G = lane/16, j = (lane%16)/2, h = lane%2) of
+  //  read nn addresses the row of operand byte 8 nn + j of lane group G,
+  //  32 nn + 16 (j/4) + 4G + j%4 (swizzle independent of nn), dims 16 db + 8h:
+  //  v8off[db & 3] + 32 nn ROW + 64 (db >> 2)
   int v8off[4];
   {
     const int j = (lane & 15) >> 1, h = lane & 1;
-    const int row = j < 4 ? 4 * g + j : 16 + 4 * g + j - 4;
+    const int row = 16 * (j >> 2) + 4 * g + (j & 3);
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) v8off[bb] = row * G::ROW + 16 * (bb ^ swz(row)) + 8 * h;
+    for (int d3 = 0; d3 < 4; ++d3) v8off[d3] = row * ROW + 16 * (d3 ^ swz(row)) + 8 * h;
   }
-  //  V^T via tr_b16 (bf16 dims): source lane (g, j = (lane&15)>>2, q = lane&3)
-  //  addresses keys 4g+j (lo) and 16+4g+j (hi), dims (D-R) + 16e + 4q
+  //  V^T via tr_b16 (bf16 dims, 16-dim block e): source lane (G, j = (lane%16)/4,
+  //  q = lane%4) of k-step s, half hl addresses the row of operand element
+  //  4 hl + j of lane group G, 16 (2s + (hl ^ G%2)) + 4G + j, dims
+  //  (D - R) + 16 e + 4q: v16off[hl][e & 1] + 32 s ROW + 64 (e >> 1)
   int v16off[2][2];
   {
     const int j = (lane & 15) >> 2, q = lane & 3;
 #pragma unroll
     for (int hl = 0; hl < 2; ++hl) {
-      const int row = hl * 16 + 4 * g + j;
+      const int row = 16 * (hl ^ (g & 1)) + 4 * g + j;
 #pragma unroll
       for (int e1 = 0; e1 < 2; ++e1)
-        v16off[hl][e1] = row * G::ROW + 16 * (G::FP8_CPR + ((2 * e1 + (q >> 1)) ^ swz(row))) +
-                         8 * (q & 1);
+        v16off[hl][e1] = row * ROW + 16 * (BFC + ((2 * e1 + (q >> 1)) ^ swz(row))) + 8 * (q & 1);
     }
   }
 
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
+  //  qk: S^T for 128 rows x 16 heads, absent rows at -inf, and the logit
+  //      maximum per head of each 64-row scale block, for this lane's pair of
+  //      lane groups (mp) and the other pair (mo).  Row blocks go in pairs
+  //      (two accumulator chains); the operands of each step are read one
+  //      step ahead, and the scheduling fences keep the compiler from
+  //      hoisting every read of the tile.
+  auto qk = [&](const uint8_t* T, int cur, f32x4 (&sacc)[8], float (&mp)[2], float (&mo)[2], auto&& side) {
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int NS = NJ + 2;   // steps per row-block pair: E4M3 k-steps, then bf16
+    static_assert(G::WPW <= 4 * NS, "every copy of the next tile gets a step");
+    auto load = [&](int st, i32x8 (&k8)[2], u32x4 (&kt)[2]) {
+      const int rp = st / NS, ks = st % NS;
+#pragma unroll
+      for (int x2 = 0; x2 < 2; ++x2) {
+        const int rb = 2 * rp + x2;
+        if (ks < NJ) {
+          const uint8_t* kp = T + 16 * rb * ROW + 128 * ks;
+          const uint8_t* p0 = kp + koff[rb & 1][0];
+          const uint8_t* p1 = kp + koff[rb & 1][1];
+          if (ks == NJ - 1 && g >= 2) {   // past the E4M3 dims: zeros (q~ is zero there too)
+            p0 = s_zero;
+            p1 = s_zero + 16;
+          }
+          const u32x4 w0 = *reinterpret_cast<const u32x4*>(p0);
+          const u32x4 w1 = *reinterpret_cast<const u32x4*>(p1);
+          k8[x2] = __builtin_bit_cast(i32x8, u32x8{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w});
+        } else {
+          kt[x2] = *reinterpret_cast<const u32x4*>(T + 16 * rb * ROW + ktoff[rb & 1] + 64 * (ks - NJ));
+        }
+      }
+    };
+    i32x8 k8[2][2];
+    u32x4 kt[2][2];
+    load(0, k8[0], kt[0]);
+#pragma unroll
+    for (int st = 0; st < 4 * NS; ++st) {
+      if (st + 1 < 4 * NS) load(st + 1, k8[(st + 1) & 1], kt[(st + 1) & 1]);
+      const int rp = st / NS, ks = st % NS;
+      if (ks < NJ) {
+#pragma unroll
+        for (int x2 = 0; x2 < 2; ++x2)
+          sacc[2 * rp + x2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              k8[st & 1][x2], qh[ks], sacc[2 * rp + x2], 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int x2 = 0; x2 < 2; ++x2)
+          sacc[2 * rp + x2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              k8[st & 1][x2], ql[ks], sacc[2 * rp + x2], 0, 0, 0, 127, 0, 127);
+      } else {
+#pragma unroll
+        for (int x2 = 0; x2 < 2; ++x2)
+          sacc[2 * rp + x2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, kt[st & 1][x2]), qt[ks - NJ], sacc[2 * rp + x2], 0, 0, 0);
+      }
+      side(st);   // e.g. one copy of the next tile, behind this step's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // row 16 rb + 4g + i is bit 16 (rb & 1) + 4g + i of staging word rb / 2
+    unsigned vm[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) vm[w] = __builtin_amdgcn_readfirstlane(s_v[cur][w]);
+    if ((vm[0] & vm[1] & vm[2] & vm[3]) != 0xFFFFFFFFu) {   // partial tile: mask the absent rows
+#pragma unroll
+      for (int rb = 0; rb < 8; ++rb) {
+        const unsigned vl = vm[rb >> 1] >> (16 * (rb & 1) + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((vl >> i) & 1u)) sacc[rb][i] = -INFINITY;
+      }
+    }
+    // sl2 > 0, so the raw maximum scales to the logit maximum
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float m = sacc[4 * h][0];
+#pragma unroll
+      for (int rb = 4 * h; rb < 4 * h + 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[rb][i]);
+      m *= sl2;
+      mp[h] = fmaxf(m, __shfl_xor(m, 16));
+      mo[h] = __shfl_xor(mp[h], 32);
+    }
+  };
+  //  pv: online softmax of the tile against the running max m_run, then
+  //      O^T += V^T P^T.  Operand byte 4 rb + i of lane group g is row
+  //      16 rb + 4g + i; bytes 0-15 of lane groups {0,1} / {2,3} form one E8M0
+  //      scale block, bytes 16-31 another.  Block (pair, half) is
+  //      exponentiated as p' = 2^(x - c) with c an integer that puts its
+  //      largest p' in (128, 256]; its weight 2^(c - m_run) is the operand's
+  //      E8M0 scale on the E4M3 dims and is applied in fp32 on the bf16 dims.
+  auto pv = [&](const uint8_t* T, f32x4 (&sacc)[8], const float (&mp)[2], const float (&mo)[2]) {
+    float cown[2];
+    int eown[2], eoth[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      cown[h] = fmaxf(ceilf(mp[h]) - 8.0f, m_run - 120.0f);
+      const float coth = fmaxf(ceilf(mo[h]) - 8.0f, m_run - 120.0f);
+      eown[h] = (int)fminf(fmaxf(cown[h] - m_run, -127.0f), 127.0f);
+      eoth[h] = (int)fminf(fmaxf(coth - m_run, -127.0f), 127.0f);
+    }
+    float ls[2] = {0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sacc[rb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[rb][i], sl2, -cown[rb >> 2]));
+        ls[rb >> 2] += sacc[rb][i];
+      }
+    l_run += ldexpf(ls[0], eown[0]) + ldexpf(ls[1], eown[1]);
+    // hi + lo E4M3 terms, dword rb = the four rows of row block rb
+    i32x8 ph, pl;
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) {
+      const float p0 = sacc[rb][0], p1 = sacc[rb][1], p2 = sacc[rb][2], p3 = sacc[rb][3];
+      int hw = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      hw = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, hw, true);
+      const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+      const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+      int lw = __builtin_amdgcn_cvt_pk_fp8_f32(p0 - b01.x, p1 - b01.y, 0, false);
+      lw = __builtin_amdgcn_cvt_pk_fp8_f32(p2 - b23.x, p3 - b23.y, lw, true);
+      ph[rb] = hw;
+      pl[rb] = lw;
+    }
+    // lane group g supplies the scale of block (pair g % 2, half g / 2): its
+    // own pair (g / 2) for g = 0, 3, the other pair for g = 1, 2
+    const int hsel = g >> 1;
+    const int eo = hsel ? eown[1] : eown[0], et = hsel ? eoth[1] : eoth[0];
+    const int sc = 127 + ((g == 0 || g == 3) ? eo : et);
+    __builtin_amdgcn_sched_barrier(0);
+    auto load_v8 = [&](int db, i32x8& v) {
+      i32x2 w[4];
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn)
+        w[nn] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (V4_LDS i32x2*)(T + v8off[db & 3] + 32 * nn * ROW + 64 * (db >> 2)));
+      v = i32x8{w[0].x, w[0].y, w[1].x, w[1].y, w[2].x, w[2].y, w[3].x, w[3].y};
+    };
+    auto load_v16 = [&](int s2, bf16x8 (&v)[4]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u32x2 lo = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                       (V4_LDS i16x4*)(T + v16off[0][e & 1] + 32 * s2 * ROW + 64 * (e >> 1))));
+        const u32x2 hi = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                       (V4_LDS i16x4*)(T + v16off[1][e & 1] + 32 * s2 * ROW + 64 * (e >> 1))));
+        v[e] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      }
+    };
+    // bf16 dims first (p relative to the running max), so p' dies before the
+    // E4M3 dims.  k-step s covers row blocks 2s and 2s + 1: element 4 hl + j
+    // of lane group g is row 16 (2s + (hl ^ g%2)) + 4g + j.
+    bf16x8 vt[2][4];
+    load_v16(0, vt[0]);
+    const bool godd = (g & 1) != 0;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      if (s2 + 1 < 4) load_v16(s2 + 1, vt[(s2 + 1) & 1]);
+      const int es = s2 < 2 ? eown[0] : eown[1];
+      const f32x4 a0 = godd ? sacc[2 * s2 + 1] : sacc[2 * s2];
+      const f32x4 a1 = godd ? sacc[2 * s2] : sacc[2 * s2 + 1];
+      const u32x4 pk = {pack_bf16x2(ldexpf(a0[0], es), ldexpf(a0[1], es)),
+                        pack_bf16x2(ldexpf(a0[2], es), ldexpf(a0[3], es)),
+                        pack_bf16x2(ldexpf(a1[0], es), ldexpf(a1[1], es)),
+                        pack_bf16x2(ldexpf(a1[2], es), ldexpf(a1[3], es))};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[NB8 + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[s2 & 1][e], pb, o[NB8 + e], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // E4M3 dims, two blocks a step (two accumulator chains), operands one step ahead
+    i32x8 vf[2][2];
+    load_v8(0, vf[0][0]);
+    load_v8(1, vf[0][1]);
+#pragma unroll
+    for (int st = 0; st < NB8 / 2; ++st) {
+      if (st + 1 < NB8 / 2) {
+        load_v8(2 * st + 2, vf[(st + 1) & 1][0]);
+        load_v8(2 * st + 3, vf[(st + 1) & 1][1]);
+      }
+#pragma unroll
+      for (int x2 = 0; x2 < 2; ++x2)
+        o[2 * st + x2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vf[st & 1][x2], ph, o[2 * st + x2],
+                                                                          0, 0, 0, 127, 0, sc);
+#pragma unroll
+      for (int x2 = 0; x2 < 2; ++x2)
+        o[2 * st + x2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vf[st & 1][x2], pl, o[2 * st + x2],
+                                                                          0, 0, 0, 127, 0, sc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // Tile t lives in buffer t & 1.  A tile issues the copies of tile t+1 (into
   // the buffer every wave finished reading before the last barrier), uses
   // tile t, waits for its own copies and meets the other waves at the
   // barrier, so tile t+1 is complete in LDS and every read of tile t is done.
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int cur = tile & 1;
-    if (tile + 1 < ntiles && wave < 4) issue_tile(tile + 1, cur ^ 1);
-    const uint8_t* T = s_tile[cur];
-    // partial S^T over this wave's half of the k-steps, 64 keys
-    f32x4 s[2][2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[hh][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (active) {
-      // f8f6f4 k-steps of this half: K straight from the tile, q~ as hi + lo
-#pragma unroll
-      for (int u = 0; u < NQ; ++u) {
-        const int s8 = hf == 0 ? u : NF0 + u;
-        if (s8 < NF8 && (hf == 1 || u < NF0)) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              const u32x4 w0 = *reinterpret_cast<const u32x4*>(T + koff8[kb][0] + hh * G::HALF + 128 * s8);
-              const u32x4 w1 = *reinterpret_cast<const u32x4*>(T + koff8[kb][1] + hh * G::HALF + 128 * s8);
-              const i32x8 ka = __builtin_bit_cast(
-                  i32x8, u32x8{w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w});
-              s[hh][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qh[u], s[hh][kb], 0, 0, 0,
-                                                                           127, 0, 127);
-              s[hh][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, ql[u], s[hh][kb], 0, 0, 0,
-                                                                           127, 0, 127);
-            }
-        }
+  // A tile whose logits pass the running max by more than the headroom
+  // leaves the inner loop, which then never touches the accumulators outside
+  // the MFMAs; the rescale and that tile finish outside it (always once, at
+  // the first tile with a present row).
+  int tile = 0;
+  while (tile < ntiles) {
+    f32x4 sacc[8];
+    float mp[2], mo[2];
+    const uint8_t* T = nullptr;
+    bool grow = false;
+    for (; tile < ntiles; ++tile) {
+      const int cur = tile & 1;
+      const uint8_t* nbase = tile + 1 < ntiles ? contig_base(tile + 1) : nullptr;
+      if (nbase) {
+        if (lane == 0) s_v[cur ^ 1][wave] = 0xFFFFFFFFu;
+      } else if (tile + 1 < ntiles) {
+        issue_tile(tile + 1, cur ^ 1);
       }
-      if (hf == 0) {   // bf16 (rotary) dims
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              const u32x4 w = *reinterpret_cast<const u32x4*>(T + koff[kb] + hh * G::HALF +
-                                                              16 * G::FP8_CPR + 64 * t2);
-              s[hh][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), qt[t2],
-                                                                  s[hh][kb], 0, 0, 0);
-            }
-      } else {         // E4M3 tail, widened to bf16
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              const u32x2 w = *reinterpret_cast<const u32x2*>(T + ktoff[kb][t2] + hh * G::HALF);
-              const u32x2 lo = fp8x4_to_bf16x4(w.x), hi = fp8x4_to_bf16x4(w.y);
-              s[hh][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), qt[t2], s[hh][kb], 0, 0, 0);
-            }
+      T = s_tile[cur];
+      qk(T, cur, sacc, mp, mo, [&](int st) {
+        if (st < G::WPW && nbase) issue_copy(nbase, cur ^ 1, st);
+      });
+      if (__any(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mo[0], mo[1])) > m_run + kLazyMax)) {
+        grow = true;
+        break;
       }
+      pv(T, sacc, mp, mo);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
+    if (!grow) break;
+    const float mt = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mo[0], mo[1]));
+    const float m_new = mt > m_run + kLazyMax ? ceilf(mt) : m_run;
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= corr;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_x[wave][2 * hh + kb][lane] = s[hh][kb];
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (active) {
-      // full S: own half + partner's half (a + b == b + a, so both waves agree)
-      unsigned vmask[2];
-      vmask[0] = __builtin_amdgcn_readfirstlane(s_v[cur][0] | (s_v[cur][1] << 16));
-      vmask[1] = __builtin_amdgcn_readfirstlane(s_v[cur][2] | (s_v[cur][3] << 16));
-      float x[2][2][4];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const f32x4 sk = s[hh][kb] + s_x[wave ^ 4][2 * hh + kb][lane];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[hh][kb][i] = sk[i] * sl2;
-        }
-      // online softmax for head c over this lane's 16 keys: 32hh + 16kb + 4g + i
-      if ((vmask[0] & vmask[1]) != 0xFFFFFFFFu) {   // partial tile: mask the absent rows
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (!((vmask[hh] >> (kb * 16 + 4 * g + i)) & 1u)) x[hh][kb][i] = -INFINITY;
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          mt = fmaxf(mt, fmaxf(fmaxf(x[hh][kb][0], x[hh][kb][1]), fmaxf(x[hh][kb][2], x[hh][kb][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      // move the running max only when it grows past the headroom
-      if (__any(mt > m_run + kLazyMax)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= corr;
-#pragma unroll
-        for (int db = 0; db < G::DBH; ++db) o[db] *= corr;
-        m_run = m_new;
-      }
-      bf16x8 pb[2];
-      float ls = 0.f;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float p[2][4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[kb][i] = __builtin_amdgcn_exp2f(x[hh][kb][i] - m_run);
-            ls += p[kb][i];
-          }
-        const u32x4 pk = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                          pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
-        pb[hh] = __builtin_bit_cast(bf16x8, pk);
-      }
-      l_run += ls;
-      // O^T += V^T P^T for this wave's half of the dim blocks
-#pragma unroll
-      for (int u = 0; u < G::DBH; ++u) {
-        const int db = hf * G::DBH + u;
-        if (db < G::FB) {   // E4M3 dims
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (V4_LDS i32x2*)(T + v8off[db & 3] + hh * G::HALF + 64 * (db >> 2)));
-            const u32x2 lo = fp8x4_to_bf16x4((unsigned)v.x), hi = fp8x4_to_bf16x4((unsigned)v.y);
-            o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), pb[hh], o[u], 0, 0, 0);
-          }
-        } else {            // bf16 dims
-          const int e = db - G::FB;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const u32x2 lo = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                           (V4_LDS i16x4*)(T + v16off[0][e & 1] + hh * G::HALF + 64 * (e >> 1))));
-            const u32x2 hi = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                           (V4_LDS i16x4*)(T + v16off[1][e & 1] + hh * G::HALF + 64 * (e >> 1))));
-            o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), pb[hh], o[u], 0, 0, 0);
-          }
-        }
-      }
-    }
+    for (int db = 0; db < NB; ++db) o[db] *= corr;
+    m_run = m_new;
+    pv(T, sacc, mp, mo);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    ++tile;
   }
 
-  if (!active || head >= a.H) return;
-  // full denominator of this lane's head: sum the four lane groups
+  if (head >= a.H) return;
+  // full denominator of this lane's head: all four lane groups
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  const int db0 = hf * G::DBH;       // this wave's first output dim block
+  // accumulator i of block db holds dim 16 db + 4g + i
   if (a.splits > 1) {
     // unnormalised partial (O, max, sum); the merge kernel adds the sink
     float* po = a.part_o + (((int64_t)qr * a.splits + split) * a.H + head) * D;
 #pragma unroll
-    for (int u = 0; u < G::DBH; ++u)
-      *reinterpret_cast<f32x4*>(po + (db0 + u) * 16 + g * 4) = o[u];
-    if (g == 0 && hf == 0) {
+    for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g) = o[db];
+    if (g == 0) {
       float* pm = a.part_ml + (((int64_t)qr * a.splits + split) * a.H + head) * 2;
       pm[0] = l_run > 0.f ? m_run : -INFINITY;
       pm[1] = l_run;
@@ -561,9 +667,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
   }
   uint16_t* op = a.out + ((int64_t)qr * a.H + head) * D;
 #pragma unroll
-  for (int u = 0; u < G::DBH; ++u) {
-    const int d0 = (db0 + u) * 16 + g * 4;
-    float v[4] = {o[u][0] * scale_o, o[u][1] * scale_o, o[u][2] * scale_o, o[u][3] * scale_o};
+  for (int db = 0; db < NB; ++db) {
+    const int d0 = 16 * db + 4 * g;
+    float v[4] = {o[db][0] * scale_o, o[db][1] * scale_o, o[db][2] * scale_o, o[db][3] * scale_o};
     if (d0 >= D - R) {
 #pragma unroll
       for (int e = 0; e < 4; e += 2) {
@@ -577,7 +683,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
     const u32x2 pkd = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     *reinterpret_cast<u32x2*>(op + d0) = pkd;
   }
-  if (a.lse && g == 0 && hf == 0) a.lse[(int64_t)qr * a.H + head] = lse;
+  if (a.lse && g == 0) a.lse[(int64_t)qr * a.H + head] = lse;
 }
 
 // Combine split partials with the sink, rotate by -t, store bf16 and lse.
@@ -653,14 +759,17 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a) {
   *reinterpret_cast<u32x2*>(a.out + ((int64_t)qr * a.H + h) * D + d) = pk;
 }
 
-int attend_splits(int B, int Tq, int64_t rows_max) {
+int attend_splits(int B, int Tq, int64_t rows_max, bool csa) {
   const int64_t q = (int64_t)B * Tq;
   if (q <= 0 || rows_max <= 0) return 1;
-  int64_t s = (256 + q - 1) / q;                               // about one workgroup per CU
-  const int64_t by_rows = (rows_max + kAttTile - 1) / kAttTile;  // at least one tile per split
+  int64_t s = (256 + q - 1) / q;                                 // about one workgroup per CU
+  const int64_t by_rows = (rows_max + kAttRows - 1) / kAttRows;  // at least one tile per split
   if (s > by_rows) s = by_rows;
   if (s > 64) s = 64;
   if (s < 1) s = 1;
+  // CSA stages a split's top-k slots in LDS: at most kSelCap rows a split
+  if (csa)
+    while (s < 64 && split_chunk(rows_max, (int)s) > kSelCap) ++s;
   return (int)s;
 }
 
@@ -668,6 +777,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   const int64_t q = (int64_t)a.B * a.Tq;
   if (q == 0) return hipSuccess;
   const bool csa = a.topk != nullptr;
+  // every split's slice of the top-k list must fit the kernel's LDS copy
+  if (csa && split_chunk(a.rows_max, a.splits) > kSelCap) return hipErrorInvalidValue;
   dim3 grid(a.splits, (unsigned)q);
 #define V4_ATT(D)                                                             \
   do {                                                                        \

@@ -98,6 +98,6 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 
 // Number of key-range splits the attention uses for a problem (shared by
 // the workspace query and the launch so both agree).
-int attend_splits(int B, int Tq, int64_t rows_max);
+int attend_splits(int B, int Tq, int64_t rows_max, bool csa);
 
 }  // namespace v4

@@ -100,7 +100,7 @@ def test_workspace_sizes_are_host_arithmetic():
     n = L().v4attn_index_topk_workspace(8, 1, 262144, (1 << 20) - 1, 4, 1024)
     assert n >= 8 * 262144 * 4
     assert L().v4attn_index_topk_workspace(-1, 1, 10, 0, 4, 1) == 0
-    # tiny problems need no split partials
+    # many queries need no split partials
     assert L().v4attn_csa_attend_workspace(4096, 1, 64, 512, 1024, 128) == 0
     assert L().v4attn_hca_attend_workspace(32, 1, 64, 512, 8192, 128, (1 << 20) - 1, 128) > 0
 
