@@ -93,24 +93,25 @@ IndexWs index_ws(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m, int k)
   return w;
 }
 
-// Attention workspace (splits > 1): the split partials, O then (max, sum).
+// Attention workspace (splits > 1): the split partials, O (bf16) then
+// (max, sum) (fp32).
+size_t attend_o_bytes(int64_t q, int s, int H, int D) {
+  return ((size_t)(q * s * H * D) * sizeof(uint16_t) + 255) / 256 * 256;
+}
+
 size_t attend_ws(int B, int Tq, int H, int D, int64_t rows_max, bool csa, int* splits) {
   const int s = v4::attend_splits(B, Tq, rows_max, csa);
   if (splits) *splits = s;
   if (s <= 1) return 0;
   const int64_t q = (int64_t)B * Tq;
-  size_t o = (size_t)(q * s * H * D) * sizeof(float);
-  o = (o + 255) / 256 * 256;
-  return o + (size_t)(q * s * H * 2) * sizeof(float);
+  return attend_o_bytes(q, s, H, D) + (size_t)(q * s * H * 2) * sizeof(float);
 }
 
 // Points the kernel arguments at their parts of the workspace.
 void attend_ws_layout(v4::AttendArgs& a, void* ws) {
   uint8_t* w = static_cast<uint8_t*>(ws);
-  a.part_o = reinterpret_cast<float*>(w);
-  const int64_t q_rows = (int64_t)a.B * a.Tq;
-  size_t o_bytes = (size_t)(q_rows * a.splits * a.H * a.D) * sizeof(float);
-  o_bytes = (o_bytes + 255) / 256 * 256;
+  a.part_o = reinterpret_cast<uint16_t*>(w);
+  const size_t o_bytes = attend_o_bytes((int64_t)a.B * a.Tq, a.splits, a.H, a.D);
   a.part_ml = a.splits > 1 ? reinterpret_cast<float*>(w + o_bytes) : nullptr;
 }
 

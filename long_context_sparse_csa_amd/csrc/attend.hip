@@ -643,10 +643,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
   l_run += __shfl_xor(l_run, 32);
   // accumulator i of block db holds dim 16 db + 4g + i
   if (a.splits > 1) {
-    // unnormalised partial (O, max, sum); the merge kernel adds the sink
-    float* po = a.part_o + (((int64_t)qr * a.splits + split) * a.H + head) * D;
+    // unnormalised partial (O as bf16, max, sum); the merge kernel adds the sink
+    uint16_t* po = a.part_o + (((int64_t)qr * a.splits + split) * a.H + head) * D;
 #pragma unroll
-    for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g) = o[db];
+    for (int db = 0; db < NB; ++db)
+      *reinterpret_cast<u32x2*>(po + 16 * db + 4 * g) =
+          u32x2{pack_bf16x2(o[db][0], o[db][1]), pack_bf16x2(o[db][2], o[db][3])};
     if (g == 0) {
       float* pm = a.part_ml + (((int64_t)qr * a.splits + split) * a.H + head) * 2;
       pm[0] = l_run > 0.f ? m_run : -INFINITY;
@@ -730,18 +732,19 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a) {
   const int hh = tid / QPH, d = 4 * (tid % QPH);
   const int h = h0 + hh;
   if (hh >= HPW || h >= a.H) return;
-  const float* po = a.part_o + ((int64_t)qr * S * a.H + h) * D + d;
+  const uint16_t* po = a.part_o + ((int64_t)qr * S * a.H + h) * D + d;
   const int64_t sstride = (int64_t)a.H * D;
   f32x4 x = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 8) {   // eight split partials in flight
-    f32x4 v[8];
+    u32x2 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)min(s0 + u, S - 1) * sstride);
+      v[u] = *reinterpret_cast<const u32x2*>(po + (int64_t)min(s0 + u, S - 1) * sstride);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float w = s0 + u < S ? s_w[hh][s0 + u] : 0.f;
-      x += w * v[u];
+      x += w * f32x4{bf16_bits_to_f32(v[u].x & 0xFFFFu), bf16_bits_to_f32(v[u].x >> 16),
+                     bf16_bits_to_f32(v[u].y & 0xFFFFu), bf16_bits_to_f32(v[u].y >> 16)};
     }
   }
   float y[4] = {x[0], x[1], x[2], x[3]};

@@ -90,7 +90,7 @@ struct AttendArgs {
   uint16_t* out;            // [B, Tq, H, D]
   float* lse;               // [B, Tq, H] or nullptr
   int splits;               // key-range splits per query (1 = no merge pass)
-  float* part_o;            // [B*Tq, splits, H, D]   (splits > 1)
+  uint16_t* part_o;         // [B*Tq, splits, H, D] bf16, unnormalised (splits > 1)
   float* part_ml;           // [B*Tq, splits, H, 2]  (max, sum)
   int64_t rows_max;         // max rows (entries + window) over the block
 };
