@@ -53,111 +53,27 @@ def log(*a):
 
 
 def build_inputs(dev, rotate):
-    import torch
-    from long_context_sparse_csa_amd import synth
+    from long_context_sparse_csa_amd import decode
     from long_context_sparse_csa_amd.configs import CSA_1M, HCA_1M
-
-    c, h = CSA_1M, HCA_1M
-    inp = {"csa": {}, "hca": {}}
-    # ---- CSA layer (cfg: 8 x 1M, m = 4)
-    d = inp["csa"]
-    N = c.T // c.m
-    d["N"] = N
-    d["t"] = c.T - 1
-    d["entries"] = synth.packed_rows((c.B, N), c.D, c.R, c.seed, "entries", dev,
-                                     chunk_rows=1 << 18)
-    d["k_idx"] = synth.normal((c.B, N, c.dI), c.seed, "kI", dev, dtype=torch.bfloat16)
-    d["q_idx"] = synth.normal((c.B, 1, c.HI, c.dI), c.seed, "qI", dev, dtype=torch.bfloat16)
-    d["w_idx"] = synth.normal((c.B, 1, c.HI), c.seed, "w", dev)
-    d["q"] = synth.normal((c.B, 1, c.H, c.D), c.seed, "q", dev, dtype=torch.bfloat16)
-    d["win"] = synth.packed_rows((c.B, c.W), c.D, c.R, c.seed, "win", dev)
-    d["raw"] = synth.normal((c.B, 2 * c.m, c.D), c.seed, "raw", dev, dtype=torch.bfloat16)
-    d["score"] = synth.normal((c.B, 2 * c.m), c.seed, "score", dev)
-    d["bias"] = synth.normal((2 * c.m,), c.seed, "bias", dev, std=0.1)
-    d["sink"] = synth.normal((c.H,), c.seed, "sink", dev)
-    d["gamma"] = torch.ones(c.D, device=dev)
-    # ---- HCA layer (cfg: 32 x 1M, m' = 128)
-    d = inp["hca"]
-    N = h.T // h.m
-    d["N"] = N
-    d["t"] = h.T - 1
-    d["entries"] = [synth.packed_rows((h.B, N), h.D, h.R, h.seed + 100 * i, "entries", dev)
-                    for i in range(rotate)]
-    d["q"] = synth.normal((h.B, 1, h.H, h.D), h.seed, "q", dev, dtype=torch.bfloat16)
-    d["win"] = synth.packed_rows((h.B, h.W), h.D, h.R, h.seed, "win", dev)
-    d["raw"] = synth.normal((h.B, 2 * h.m, h.D), h.seed, "raw", dev, dtype=torch.bfloat16)
-    d["score"] = synth.normal((h.B, 2 * h.m), h.seed, "score", dev)
-    d["bias"] = synth.normal((2 * h.m,), h.seed, "bias", dev, std=0.1)
-    d["sink"] = synth.normal((h.H,), h.seed, "sink", dev)
-    d["gamma"] = torch.ones(h.D, device=dev)
-    return inp
+    return decode.build_inputs(CSA_1M, HCA_1M, dev, rotate)
 
 
 def make_step(inp, dev):
-    """Returns (list of (name, fn) launches for one step, output buffers)."""
-    import torch
-    from long_context_sparse_csa_amd import ops
+    """(name, fn) launches of one eager step (HCA cache copies rotate), and
+    the DecodeStep behind them."""
+    from long_context_sparse_csa_amd import decode
     from long_context_sparse_csa_amd.configs import CSA_1M, HCA_1M
-
-    c, h = CSA_1M, HCA_1M
-    a, b = inp["csa"], inp["hca"]
-    Nc, Nh = a["N"], b["N"]
-    tc, th = a["t"], b["t"]
-    scores = torch.empty((c.B, ops.score_stride(1, Nc, tc, c.m)), dtype=torch.float32, device=dev)
-    topk = torch.empty((c.B, 1, c.k), dtype=torch.int32, device=dev)
-    tk_ws = torch.empty(max(ops.topk_select_workspace_bytes(c.B, 1, Nc, tc, c.m, c.k), 16),
-                        dtype=torch.uint8, device=dev)
-    out_c = torch.empty_like(a["q"])
-    out_h = torch.empty_like(b["q"])
-    csa_ws = torch.empty(max(ops.csa_attend_workspace_bytes(c.B, 1, c.H, c.D, c.k, c.W), 16),
-                         dtype=torch.uint8, device=dev)
-    hca_ws = torch.empty(max(ops.hca_attend_workspace_bytes(h.B, 1, h.H, h.D, Nh, h.m, th, h.W),
-                             16), dtype=torch.uint8, device=dev)
+    st = decode.DecodeStep(inp, CSA_1M, HCA_1M, dev)
     state = {"i": 0}
+    calls = [st.calls(r) for r in range(len(inp["hca"]["entries"]))]
 
-    a["raw_last"] = a["raw"][:, -1:].contiguous()   # the new token's raw latent
-    b["raw_last"] = b["raw"][:, -1:].contiguous()
-
-    def csa_pack():
-        ops.compress_pack(a["raw_last"], a["gamma"], a["win"], raw_pos0=tc, out_row0=c.W - 1)
-
-    def csa_pool():
-        ops.compress_pool(a["raw"], a["score"], a["bias"], a["gamma"], a["entries"],
-                          raw_pos0=tc + 1 - 2 * c.m, m=c.m, entry0=Nc - 1, n_out=1,
-                          out_row0=Nc - 1)
-
-    def csa_score():
-        ops.index_score(a["q_idx"], a["w_idx"], a["k_idx"], n_entries=Nc, q_pos0=tc, m=c.m,
-                        scores=scores)
-
-    def csa_topk():
-        ops.topk_select(scores, B=c.B, Tq=1, n_entries=Nc, q_pos0=tc, m=c.m, k=c.k, topk=topk,
-                        workspace=tk_ws)
-
-    def csa_attend():
-        ops.csa_attend(a["q"], a["entries"], topk, a["win"], a["gamma"], a["sink"], q_pos0=tc,
-                       W=c.W, out=out_c, workspace=csa_ws)
-
-    def hca_ent():
-        return b["entries"][state["i"] % len(b["entries"])]
-
-    def hca_pack():
-        ops.compress_pack(b["raw_last"], b["gamma"], b["win"], raw_pos0=th, out_row0=h.W - 1)
-
-    def hca_pool():
-        ops.compress_pool(b["raw"], b["score"], b["bias"], b["gamma"], hca_ent(),
-                          raw_pos0=th + 1 - 2 * h.m, m=h.m, entry0=Nh - 1, n_out=1,
-                          out_row0=Nh - 1)
-
-    def hca_attend():
-        ops.hca_attend(b["q"], hca_ent(), b["win"], b["gamma"], b["sink"], n_entries=Nh, m=h.m,
-                       q_pos0=th, W=h.W, out=out_h, workspace=hca_ws)
-        state["i"] += 1
-
-    launches = [("csa_pack", csa_pack), ("csa_pool", csa_pool), ("index_score", csa_score),
-                ("topk_select", csa_topk), ("csa_attend", csa_attend), ("hca_pack", hca_pack),
-                ("hca_pool", hca_pool), ("hca_attend", hca_attend)]
-    return launches, {"topk": topk, "out_csa": out_c, "out_hca": out_h, "scores": scores}
+    def mk(name):
+        def fn():
+            calls[state["i"] % len(calls)][name]()
+            if name == "hca_attend":
+                state["i"] += 1
+        return fn
+    return [(n, mk(n)) for n in decode.DecodeStep.NAMES], st
 
 
 def algorithmic_bytes():
@@ -208,6 +124,28 @@ def run_timed(launches, steps, warmup):
     for _ in range(steps):
         for _, fn in launches:
             fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def run_timed_graphs(st, rotate, steps, warmup):
+    """Steps replayed from HIP graphs of the overlapped schedule, one graph
+    per HCA cache copy (used in turn)."""
+    import torch
+    for r in range(rotate):
+        st.run_overlapped(r)
+    torch.cuda.synchronize()
+    graphs = [st.capture(r) for r in range(rotate)]
+    for i in range(warmup):
+        graphs[i % rotate].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        graphs[i % rotate].replay()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -391,6 +329,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of the overlapped schedule (on this stack "
+                         "slower than the calls launched one by one)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 4096-token prefill section")
@@ -412,7 +353,7 @@ def main():
     ops.lib()
     log("generating inputs")
     inp = build_inputs(dev, args.rotate)
-    launches, outs = make_step(inp, dev)
+    launches, st = make_step(inp, dev)
     torch.cuda.synchronize()
     if args.counters:
         # calibration: torch's elementwise kernel reads and writes COPY_BYTES each
@@ -427,8 +368,11 @@ def main():
         log("counters pass done")
         return
     log("timing")
-    ms, wall = run_timed(launches, args.steps, args.warmup)
-    log(f"step {ms * 1e3:.1f} us")
+    if args.graph:
+        ms, wall = run_timed_graphs(st, args.rotate, args.steps, args.warmup)
+    else:
+        ms, wall = run_timed(launches, args.steps, args.warmup)
+    log(f"step {ms * 1e3:.1f} us ({'graph, overlapped' if args.graph else 'eager, sequential'})")
     br = run_breakdown(launches, max(10, min(args.steps, 50)))
     log("breakdown (us): " + ", ".join(f"{k} {v:.1f}" for k, v in br.items()))
     abytes, aflops = algorithmic_bytes()
@@ -460,6 +404,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_schedule": "HIP graph replay, pack and pool on a second stream" if args.graph
+        else "calls launched one by one on one stream",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

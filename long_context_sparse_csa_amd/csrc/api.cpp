@@ -187,7 +187,7 @@ int v4attn_compress(const uint16_t* raw, const float* tok_score, const float* po
     if (n_out > L) return fail(V4ATTN_EINVAL, "PACK n_out %d > L %d", n_out, L);
   }
   v4::CompressArgs a{raw, tok_score, pos_bias, gamma, B, L, D, R, raw_pos0, mode, m, entry0,
-                     n_out, eps, rope_base, out, out_rows};
+                     n_out, eps, rope_base, out, out_rows, v4::rope_turns(rope_base, R)};
   return hip_status(v4::launch_compress(a, (hipStream_t)stream), "compress launch");
 }
 
@@ -366,6 +366,7 @@ int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries, const int32_t* 
   a.q = q; a.entries = entries; a.topk = topk; a.win = win; a.gamma_q = gamma_q; a.sink = sink;
   a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R; a.Ncap = Ncap; a.k = k; a.n_entries = 0;
   a.m = 1; a.W = W; a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps; a.rope_base = rope_base;
+  a.rope = v4::rope_turns(rope_base, R);
   a.out = out; a.lse = lse; a.splits = splits;
   attend_ws_layout(a, ws);
   a.rows_max = (int64_t)k + W;
@@ -398,6 +399,7 @@ int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
   a.q = q; a.entries = entries; a.topk = nullptr; a.win = win; a.gamma_q = gamma_q; a.sink = sink;
   a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R; a.Ncap = Ncap; a.k = 0; a.n_entries = n_entries;
   a.m = m; a.W = W; a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps; a.rope_base = rope_base;
+  a.rope = v4::rope_turns(rope_base, R);
   a.out = out; a.lse = lse; a.splits = splits;
   attend_ws_layout(a, ws);
   a.rows_max = rows_max;

@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
 
   if (tid < R / 2) {
     float cs, sn;
-    rope_cos_sin(t, tid, R, a.rope_base, &cs, &sn);
+    rope_cos_sin(t, a.rope.t[tid], &cs, &sn);
     s_cs[tid][0] = cs;
     s_cs[tid][1] = sn;
   }
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < R / 2) {
     float cs, sn;
-    rope_cos_sin(t, tid, R, a.rope_base, &cs, &sn);
+    rope_cos_sin(t, a.rope.t[tid], &cs, &sn);
     s_cs[tid][0] = cs;
     s_cs[tid][1] = sn;
   }

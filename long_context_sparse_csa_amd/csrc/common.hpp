@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 #include <stdint.h>
 
 namespace v4 {
@@ -70,17 +72,25 @@ __device__ __forceinline__ float fp8_to_f32(unsigned code) {
   return v.x;
 }
 
-// Rotary angle of pair i (of R/2) at absolute position pos, as (cos, sin).
-// The angle pos * base^(-2i/R) is formed and reduced in fp64 so positions
-// near 2^20 keep full fp32 accuracy.
-__device__ __forceinline__ void rope_cos_sin(int64_t pos, int i, int R, float base,
-                                             float* c, float* s) {
-  // angle = pos * base^(-2i/R).  It is carried in turns (angle / 2 pi) in
-  // fp64, whose fraction is exact to ~1e-11 turns at a million positions,
-  // and only the reduced angle in [-pi, pi] goes through the fp32 sincos
-  // (about 1e-7 rad), which avoids the large-argument fp64 sincos path.
-  const double theta = exp2(-(2.0 * i / R) * log2((double)base));
-  const double turns = (double)pos * (theta * 0.15915494309189533577);
+// Rotary frequencies of the R/2 = 32 pairs, in turns per position:
+// base^(-2i/R) / (2 pi), formed once on the host in fp64.
+struct RopeTurns {
+  double t[32];
+};
+
+inline RopeTurns rope_turns(float base, int R) {
+  RopeTurns r{};
+  for (int i = 0; i < 32 && 2 * i < R; ++i)
+    r.t[i] = std::pow((double)base, -2.0 * i / R) * 0.15915494309189533577;
+  return r;
+}
+
+// Rotary angle of a pair at absolute position pos, as (cos, sin).  The angle
+// is carried in turns in fp64, whose fraction is exact to ~1e-11 turns at a
+// million positions; only the reduced angle in [-pi, pi] goes through the
+// fp32 sincos (about 1e-7 rad), which avoids the large-argument fp64 path.
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, double turns_per_pos, float* c, float* s) {
+  const double turns = (double)pos * turns_per_pos;
   const float r = (float)((turns - rint(turns)) * 6.283185307179586477);
   sincosf(r, s, c);
 }

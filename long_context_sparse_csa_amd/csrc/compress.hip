@@ -50,14 +50,14 @@ __device__ __forceinline__ void load_bf16_row(const uint16_t* p, float (&x)[VPL]
 // packed row: E4M3 for channels < D-R, bf16 for the rest.
 template <int VPL>
 __device__ __forceinline__ void rotate_and_pack(uint8_t* row, float (&y)[VPL], int lane, int R,
-                                                int64_t pos, float rope_base) {
+                                                int64_t pos, const RopeTurns& rope) {
   constexpr int D = VPL * 64;
   const int d0 = lane * VPL;
   if (d0 >= D - R) {
 #pragma unroll
     for (int v = 0; v < VPL; v += 2) {
       float c, s;
-      rope_cos_sin(pos, (d0 + v - (D - R)) >> 1, R, rope_base, &c, &s);
+      rope_cos_sin(pos, rope.t[(d0 + v - (D - R)) >> 1], &c, &s);
       float a = y[v], b = y[v + 1];
       y[v] = a * c - b * s;
       y[v + 1] = a * s + b * c;
@@ -108,7 +108,7 @@ template <int VPL>
 __global__ __launch_bounds__(kPoolThreads) void compress_pool_kernel(
     const uint16_t* __restrict__ raw, const float* __restrict__ score,
     const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
-    int64_t raw_pos0, int m, int64_t entry0, float eps, float rope_base,
+    int64_t raw_pos0, int m, int64_t entry0, float eps, const RopeTurns rope,
     uint8_t* __restrict__ out, int64_t out_rows) {
   constexpr int D = VPL * 64;
   const int b = blockIdx.y;
@@ -123,6 +123,22 @@ __global__ __launch_bounds__(kPoolThreads) void compress_pool_kernel(
   const int nw = (int)((j + 1) * (int64_t)m - plo);
   const int64_t r0 = plo - raw_pos0;           // raw row of plo
   const float* srow = score + (int64_t)b * L + r0;
+
+  // rows in batches of U per wave, all loads of a batch in flight together
+  // (loads are unconditional -- rows past the window re-read the last row
+  // with weight 0 -- so the compiler keeps the whole batch in flight); the
+  // first batch is issued before the weights are formed
+  constexpr int U = 64 / VPL;
+  const uint16_t* base = raw + ((int64_t)b * L + r0) * D + lane * VPL;
+  float x[U][VPL];
+  auto load_batch = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(t0 + kPoolWaves * u, nw - 1);
+      load_bf16_row<VPL>(base + (int64_t)t * D, x[u]);
+    }
+  };
+  load_batch(wave);
 
   // weights alpha_t = softmax over the window of (s_t + b_{t - wlo})
   float mx = -INFINITY;
@@ -155,18 +171,7 @@ __global__ __launch_bounds__(kPoolThreads) void compress_pool_kernel(
   float acc[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) acc[v] = 0.f;
-  // rows in batches of U per wave, all loads of a batch in flight together
-  constexpr int U = 64 / VPL;
-  const uint16_t* base = raw + ((int64_t)b * L + r0) * D + lane * VPL;
-  // (loads are unconditional -- rows past the window re-read the last row
-  // with weight 0 -- so the compiler keeps the whole batch in flight)
-  for (int t0 = wave; t0 < nw; t0 += kPoolWaves * U) {
-    float x[U][VPL];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = min(t0 + kPoolWaves * u, nw - 1);
-      load_bf16_row<VPL>(base + (int64_t)t * D, x[u]);
-    }
+  for (int t0 = wave;;) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + kPoolWaves * u;
@@ -174,6 +179,9 @@ __global__ __launch_bounds__(kPoolThreads) void compress_pool_kernel(
 #pragma unroll
       for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, x[u][v], acc[v]);
     }
+    t0 += kPoolWaves * U;
+    if (t0 >= nw) break;
+    load_batch(t0);
   }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) s_part[wave][lane * VPL + v] = acc[v];
@@ -191,14 +199,14 @@ __global__ __launch_bounds__(kPoolThreads) void compress_pool_kernel(
   }
   rmsnorm_wave<VPL>(y, gamma, lane, eps);
   uint8_t* row = out + ((int64_t)b * out_rows + blockIdx.x) * (D + R);
-  rotate_and_pack<VPL>(row, y, lane, R, j * (int64_t)m, rope_base);
+  rotate_and_pack<VPL>(row, y, lane, R, j * (int64_t)m, rope);
 }
 
 // One wave per raw row: RMSNorm, RoPE at the row's own position, pack.
 template <int VPL>
 __global__ __launch_bounds__(256) void compress_pack_kernel(
     const uint16_t* __restrict__ raw, const float* __restrict__ gamma, int L, int R,
-    int64_t raw_pos0, int n_out, float eps, float rope_base, uint8_t* __restrict__ out,
+    int64_t raw_pos0, int n_out, float eps, const RopeTurns rope, uint8_t* __restrict__ out,
     int64_t out_rows) {
   constexpr int D = VPL * 64;
   const int b = blockIdx.y;
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(256) void compress_pack_kernel(
   load_bf16_row<VPL>(raw + ((int64_t)b * L + r) * D + lane * VPL, y);
   rmsnorm_wave<VPL>(y, gamma, lane, eps);
   uint8_t* row = out + ((int64_t)b * out_rows + r) * (D + R);
-  rotate_and_pack<VPL>(row, y, lane, R, raw_pos0 + r, rope_base);
+  rotate_and_pack<VPL>(row, y, lane, R, raw_pos0 + r, rope);
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
@@ -219,7 +227,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
 #define V4_POOL(VPL)                                                                       \
   compress_pool_kernel<VPL><<<grid, kPoolThreads, 0, st>>>(a.raw, a.tok_score, a.pos_bias, a.gamma,  \
                                                   a.L, a.R, a.raw_pos0, a.m, a.entry0,     \
-                                                  a.eps, a.rope_base, a.out, a.out_rows)
+                                                  a.eps, a.rope, a.out, a.out_rows)
     switch (a.D) {
       case 128: V4_POOL(2); break;
       case 256: V4_POOL(4); break;
@@ -230,7 +238,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
     dim3 grid((a.n_out + 3) / 4, a.B);
 #define V4_PACK(VPL)                                                                     \
   compress_pack_kernel<VPL><<<grid, 256, 0, st>>>(a.raw, a.gamma, a.L, a.R, a.raw_pos0,   \
-                                                  a.n_out, a.eps, a.rope_base, a.out,     \
+                                                  a.n_out, a.eps, a.rope, a.out,     \
                                                   a.out_rows)
     switch (a.D) {
       case 128: V4_PACK(2); break;

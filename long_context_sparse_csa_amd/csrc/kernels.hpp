@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace v4 {
 
 struct CompressArgs {
@@ -21,6 +23,7 @@ struct CompressArgs {
   float eps, rope_base;
   uint8_t* out;
   int64_t out_rows;
+  RopeTurns rope;        // from rope_base (host)
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 
@@ -87,6 +90,7 @@ struct AttendArgs {
   int W;
   int64_t q_pos0;
   float scale, eps, rope_base;
+  RopeTurns rope;           // from rope_base (host)
   uint16_t* out;            // [B, Tq, H, D]
   float* lse;               // [B, Tq, H] or nullptr
   int splits;               // key-range splits per query (1 = no merge pass)

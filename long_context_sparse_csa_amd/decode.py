@@ -1,0 +1,151 @@
+"""One decode step of a CSA layer and an HCA layer, as a runnable unit.
+
+Per decode token and sequence, a layer
+  * CSA (compression m, top-k k, window W): packs the new token's window row,
+    pools the compressed entry the token completes, scores every visible
+    entry with the lightning indexer, selects the top-k, and attends over
+    them plus the window;
+  * HCA (compression m'): packs, pools and attends over every entry plus
+    the window.
+Within a layer the window pack and the entry pool do not depend on the
+indexer (nor on each other), so `run_overlapped` puts them on a second
+stream beside the indexer (CSA) or beside each other (HCA); the attention
+waits for both.  `capture` records that schedule in a HIP graph, which
+removes the per-launch gaps of the dozen small and large kernels.
+
+Inputs are seeded synthetic tensors shaped like the workloads in configs.py
+(the random-number recipe is in synth.py).  The HCA caches can rotate over
+several copies, one per graph, so successive steps do not hit the Infinity
+Cache.
+"""
+
+import torch
+
+from . import ops, synth
+
+
+def build_inputs(c, h, dev, rotate=1):
+    """Inputs of the decode step for CSA workload c and HCA workload h."""
+    inp = {"csa": {}, "hca": {}}
+    d = inp["csa"]
+    N = c.T // c.m
+    d["N"], d["t"] = N, c.T - 1
+    d["entries"] = synth.packed_rows((c.B, N), c.D, c.R, c.seed, "entries", dev,
+                                     chunk_rows=1 << 18)
+    d["k_idx"] = synth.normal((c.B, N, c.dI), c.seed, "kI", dev, dtype=torch.bfloat16)
+    d["q_idx"] = synth.normal((c.B, 1, c.HI, c.dI), c.seed, "qI", dev, dtype=torch.bfloat16)
+    d["w_idx"] = synth.normal((c.B, 1, c.HI), c.seed, "w", dev)
+    d["q"] = synth.normal((c.B, 1, c.H, c.D), c.seed, "q", dev, dtype=torch.bfloat16)
+    d["win"] = synth.packed_rows((c.B, c.W), c.D, c.R, c.seed, "win", dev)
+    d["raw"] = synth.normal((c.B, 2 * c.m, c.D), c.seed, "raw", dev, dtype=torch.bfloat16)
+    d["score"] = synth.normal((c.B, 2 * c.m), c.seed, "score", dev)
+    d["bias"] = synth.normal((2 * c.m,), c.seed, "bias", dev, std=0.1)
+    d["sink"] = synth.normal((c.H,), c.seed, "sink", dev)
+    d["gamma"] = torch.ones(c.D, device=dev)
+    d = inp["hca"]
+    N = h.T // h.m
+    d["N"], d["t"] = N, h.T - 1
+    d["entries"] = [synth.packed_rows((h.B, N), h.D, h.R, h.seed + 100 * i, "entries", dev)
+                    for i in range(rotate)]
+    d["q"] = synth.normal((h.B, 1, h.H, h.D), h.seed, "q", dev, dtype=torch.bfloat16)
+    d["win"] = synth.packed_rows((h.B, h.W), h.D, h.R, h.seed, "win", dev)
+    d["raw"] = synth.normal((h.B, 2 * h.m, h.D), h.seed, "raw", dev, dtype=torch.bfloat16)
+    d["score"] = synth.normal((h.B, 2 * h.m), h.seed, "score", dev)
+    d["bias"] = synth.normal((2 * h.m,), h.seed, "bias", dev, std=0.1)
+    d["sink"] = synth.normal((h.H,), h.seed, "sink", dev)
+    d["gamma"] = torch.ones(h.D, device=dev)
+    return inp
+
+
+class DecodeStep:
+    """The library calls of one decode step over fixed buffers."""
+
+    NAMES = ("csa_pack", "csa_pool", "index_score", "topk_select", "csa_attend",
+             "hca_pack", "hca_pool", "hca_attend")
+
+    def __init__(self, inp, c, h, dev):
+        self.inp, self.c, self.h = inp, c, h
+        a, b = inp["csa"], inp["hca"]
+        Nc, Nh, tc, th = a["N"], b["N"], a["t"], b["t"]
+        self.scores = torch.empty((c.B, ops.score_stride(1, Nc, tc, c.m)), dtype=torch.float32,
+                                  device=dev)
+        self.topk = torch.empty((c.B, 1, c.k), dtype=torch.int32, device=dev)
+        self.tk_ws = torch.empty(max(ops.topk_select_workspace_bytes(c.B, 1, Nc, tc, c.m, c.k), 16),
+                                 dtype=torch.uint8, device=dev)
+        self.out_c = torch.empty_like(a["q"])
+        self.out_h = torch.empty_like(b["q"])
+        self.csa_ws = torch.empty(max(ops.csa_attend_workspace_bytes(c.B, 1, c.H, c.D, c.k, c.W), 16),
+                                  dtype=torch.uint8, device=dev)
+        self.hca_ws = torch.empty(max(ops.hca_attend_workspace_bytes(h.B, 1, h.H, h.D, Nh, h.m, th,
+                                                                     h.W), 16),
+                                  dtype=torch.uint8, device=dev)
+        a["raw_last"] = a["raw"][:, -1:].contiguous()   # the new token's raw latent
+        b["raw_last"] = b["raw"][:, -1:].contiguous()
+        self.side = torch.cuda.Stream(device=dev)       # default priority
+        self.ev = [torch.cuda.Event() for _ in range(4)]
+
+    def calls(self, rot=0):
+        """name -> zero-argument launch, HCA cache copy `rot`."""
+        c, h = self.c, self.h
+        a, b = self.inp["csa"], self.inp["hca"]
+        Nc, Nh, tc, th = a["N"], b["N"], a["t"], b["t"]
+        ent_h = b["entries"][rot % len(b["entries"])]
+        return {
+            "csa_pack": lambda: ops.compress_pack(a["raw_last"], a["gamma"], a["win"], raw_pos0=tc,
+                                                  out_row0=c.W - 1),
+            "csa_pool": lambda: ops.compress_pool(a["raw"], a["score"], a["bias"], a["gamma"],
+                                                  a["entries"], raw_pos0=tc + 1 - 2 * c.m, m=c.m,
+                                                  entry0=Nc - 1, n_out=1, out_row0=Nc - 1),
+            "index_score": lambda: ops.index_score(a["q_idx"], a["w_idx"], a["k_idx"], n_entries=Nc,
+                                                   q_pos0=tc, m=c.m, scores=self.scores),
+            "topk_select": lambda: ops.topk_select(self.scores, B=c.B, Tq=1, n_entries=Nc,
+                                                   q_pos0=tc, m=c.m, k=c.k, topk=self.topk,
+                                                   workspace=self.tk_ws),
+            "csa_attend": lambda: ops.csa_attend(a["q"], a["entries"], self.topk, a["win"],
+                                                 a["gamma"], a["sink"], q_pos0=tc, W=c.W,
+                                                 out=self.out_c, workspace=self.csa_ws),
+            "hca_pack": lambda: ops.compress_pack(b["raw_last"], b["gamma"], b["win"], raw_pos0=th,
+                                                  out_row0=h.W - 1),
+            "hca_pool": lambda: ops.compress_pool(b["raw"], b["score"], b["bias"], b["gamma"], ent_h,
+                                                  raw_pos0=th + 1 - 2 * h.m, m=h.m, entry0=Nh - 1,
+                                                  n_out=1, out_row0=Nh - 1),
+            "hca_attend": lambda: ops.hca_attend(b["q"], ent_h, b["win"], b["gamma"], b["sink"],
+                                                 n_entries=Nh, m=h.m, q_pos0=th, W=h.W,
+                                                 out=self.out_h, workspace=self.hca_ws),
+        }
+
+    def run_eager(self, rot=0):
+        """The calls in order on the current stream."""
+        f = self.calls(rot)
+        for n in self.NAMES:
+            f[n]()
+
+    def run_overlapped(self, rot=0):
+        """The step with each layer's pack and pool on a second stream."""
+        f = self.calls(rot)
+        main, side, ev = torch.cuda.current_stream(), self.side, self.ev
+        ev[0].record(main)
+        side.wait_event(ev[0])
+        with torch.cuda.stream(side):
+            f["csa_pack"]()
+            f["csa_pool"]()
+            ev[1].record(side)
+        f["index_score"]()
+        f["topk_select"]()
+        main.wait_event(ev[1])
+        f["csa_attend"]()
+        ev[2].record(main)
+        side.wait_event(ev[2])
+        with torch.cuda.stream(side):
+            f["hca_pack"]()
+            ev[3].record(side)
+        f["hca_pool"]()
+        main.wait_event(ev[3])
+        f["hca_attend"]()
+
+    def capture(self, rot=0):
+        """A HIP graph of run_overlapped(rot) (run it eagerly once first)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_overlapped(rot)
+        return g
