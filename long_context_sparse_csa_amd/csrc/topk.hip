@@ -165,9 +165,10 @@ __global__ __launch_bounds__(256) void topk_part_kernel(TopkArgs a) {
   }
 }
 
-// ---- select: exact top-k of one row in LDS
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
-  extern __shared__ unsigned smem[];
+// ---- select: exact top-k of one row in LDS (every row length; the rows
+// that the fast path in topk_select_kernel settles never get here).  Kept
+// here as a function of its own.
+__device__ __forceinline__ void topk_select_general(const TopkArgs& a, unsigned* smem) {
   unsigned* s_key = smem;                                   // [kTopkSel]
   unsigned* s_hist = smem + kTopkSel;                       // [kHistBins]
   int* s_idx = reinterpret_cast<int*>(s_hist + kHistBins);  // [kTopkSel]
@@ -183,12 +184,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   const int64_t V = visible_of(a, qr);
   const int k = a.k;
   const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  int32_t* topk = a.topk + qr * k;
+  float* tks = a.topk_score ? a.topk_score + qr * k : nullptr;
 
   // Select the top-k of s_key[0, len) (0 = absent) and hand each selected
   // (position, key, index) to out(), positions in ascending index order.
   // Returns how many were selected (min(k, present keys)); *lower gets the
   // k-th largest present key (1 when at most k keys are present).
-  auto select = [&](int len, unsigned* lower, auto out) -> int {
+  // out_key (nullable: then the scores go to topk_score, if given) and
+  // out_idx receive the selection; one instantiation for every use.
+  auto select = [&](int len, unsigned* lower, unsigned* out_key, int32_t* out_idx) -> int {
     // this thread's keys, positions tid + r * threads, held in registers
     const int nrounds = (len + kSelThreads - 1) / kSelThreads;
     unsigned kr[kSelRounds];
@@ -315,7 +320,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
         if (gt || (eq && eq_before + eq_lt < need)) {
           int take_lt = need - eq_before;
           take_lt = take_lt < 0 ? 0 : (take_lt > eq_lt ? eq_lt : take_lt);
-          out(sel_before + __popcll(bg & lt_mask) + take_lt, key, s_idx[r * kSelThreads + tid]);
+          const int pos = sel_before + __popcll(bg & lt_mask) + take_lt;
+          out_idx[pos] = s_idx[r * kSelThreads + tid];
+          if (out_key) out_key[pos] = key;
+          else if (tks) tks[pos] = key_score(key);
           smin = min(smin, key);
         }
       }
@@ -330,8 +338,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
     return all ? total_valid : k;
   };
 
-  int32_t* topk = a.topk + qr * k;
-  float* tks = a.topk_score ? a.topk_score + qr * k : nullptr;
   auto final_out = [&](int pos, unsigned key, int idx) {
     topk[pos] = idx;
     if (tks) tks[pos] = key_score(key);
@@ -353,33 +359,49 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
       s_idx[i] = i;
     }
     __syncthreads();
-    pad(select(len, &lower, final_out));
+    pad(select(len, &lower, nullptr, topk));
     return;
   }
 
   const int np = a.nparts;
-  const int ppt = (np + kSelThreads - 1) / kSelThreads;   // parts per thread (<= 16)
+  const int ppt = (np + kSelThreads - 1) / kSelThreads;   // parts per thread (<= 8)
   const unsigned* ptau = a.part_tau + qr * np;
   const int* pcnt = a.part_cnt + qr * np;
   const unsigned* pover = a.part_over + qr * np;
+  // this thread's parts' records, loaded up front (their latency overlaps
+  // the first selection instead of sitting before the offsets and the check)
+  constexpr int kMaxPpt = (kTopkMaxParts + kSelThreads - 1) / kSelThreads;
+  int my_cnt[kMaxPpt];
+  unsigned my_tau[kMaxPpt], my_over[kMaxPpt];
+#pragma unroll
+  for (int u = 0; u < kMaxPpt; ++u) {
+    const int q = tid * ppt + u;
+    const bool own = u < ppt && q < np;
+    my_cnt[u] = own ? pcnt[q] : 0;
+    my_tau[u] = own ? ptau[q] : 0u;
+    my_over[u] = own ? pover[q] : 0u;
+  }
   const unsigned* ck = a.cand_key + qr * (int64_t)np * kTopkPartCap;
   const int* ci = a.cand_idx + qr * (int64_t)np * kTopkPartCap;
   unsigned* rk = a.run_key + qr * k;
 
   // Offsets of the parts' candidates given each part's count (cnt_of).
+  // cnt_of(u, q): the count of this thread's u-th part q
   auto offsets = [&](auto cnt_of) -> int {
     int mine = 0;
-    for (int u = 0; u < ppt; ++u) {
+#pragma unroll
+    for (int u = 0; u < kMaxPpt; ++u) {
       const int q = tid * ppt + u;
-      mine += q < np ? cnt_of(q) : 0;
+      mine += (u < ppt && q < np) ? cnt_of(u, q) : 0;
     }
     int C;
     int off = block_excl_scan(mine, s_wave, &C);
-    for (int u = 0; u < ppt; ++u) {
+#pragma unroll
+    for (int u = 0; u < kMaxPpt; ++u) {
       const int q = tid * ppt + u;
-      if (q < np) {
+      if (u < ppt && q < np) {
         s_off[q] = off;
-        off += cnt_of(q);
+        off += cnt_of(u, q);
       }
     }
     if (tid == 0) s_off[np] = C;
@@ -403,19 +425,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
       // stored leaders: thread t copies parts t, t + threads, ..., clipped to
       // candidates [c0, c0 + take); all 32 slots of a part are loaded at once
       static_assert(kTopkPartCap == 32, "eight 16-byte loads per part");
-      for (int q = tid; q < np; q += kSelThreads) {
+      // two threads a part, 16 slots each
+      for (int h2 = tid; h2 < 2 * np; h2 += kSelThreads) {
+        const int q = h2 >> 1, half = h2 & 1;
         const int o0 = s_off[q], cq = s_off[q + 1] - o0;
-        if (is_raw(q) || o0 + cq <= c0 || o0 >= c0 + take) continue;
-        u32x4 kk[8], ii[8];
+        if (is_raw(q) || o0 + cq <= c0 || o0 >= c0 + take || 16 * half >= cq) continue;
+        u32x4 kk[4], ii[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          kk[u] = *reinterpret_cast<const u32x4*>(ck + q * kTopkPartCap + 4 * u);
-          ii[u] = *reinterpret_cast<const u32x4*>(ci + q * kTopkPartCap + 4 * u);
+        for (int u = 0; u < 4; ++u) {
+          kk[u] = *reinterpret_cast<const u32x4*>(ck + q * kTopkPartCap + 16 * half + 4 * u);
+          ii[u] = *reinterpret_cast<const u32x4*>(ci + q * kTopkPartCap + 16 * half + 4 * u);
         }
 #pragma unroll
-        for (int j = 0; j < kTopkPartCap; ++j) {
-          const int e = o0 + j;
-          if (j < cq && e >= c0 && e < c0 + take) {
+        for (int j = 0; j < 16; ++j) {
+          const int e = o0 + 16 * half + j;
+          if (16 * half + j < cq && e >= c0 && e < c0 + take) {
             s_key[run + e - c0] = kk[j >> 2][j & 3];
             s_idx[run + e - c0] = (int)ii[j >> 2][j & 3];
           }
@@ -443,12 +467,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
       __syncthreads();
       const int len = run + take;
       c0 += take;
-      if (c0 >= C) return select(len, low, final_out);
+      if (c0 >= C) return select(len, low, nullptr, topk);
       unsigned dummy;
-      run = select(len, &dummy, [&](int pos, unsigned key, int idx) {
-        rk[pos] = key;
-        topk[pos] = idx;
-      });
+      run = select(len, &dummy, rk, topk);
       __threadfence_block();
       __syncthreads();
     }
@@ -457,14 +478,15 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   // 1. the stored leaders of every part
   for (int w = tid; w < (np + 31) / 32; w += kSelThreads) s_raw[w] = 0u;
   __syncthreads();
-  (void)offsets([&](int q) { return min(pcnt[q], kTopkPartCap); });
+  (void)offsets([&](int u, int) { return min(my_cnt[u], kTopkPartCap); });
   int n_sel = run_select(0u, false, &lower);
   // 2. parts that may hold keys >= lower they did not store (pover is 0 when
   // nothing was left out, and lower >= 1)
   int bad = 0;
-  for (int u = 0; u < ppt; ++u) {
+#pragma unroll
+  for (int u = 0; u < kMaxPpt; ++u) {
     const int q = tid * ppt + u;
-    if (q < np && (ptau[q] > lower || pover[q] >= lower)) {
+    if (u < ppt && q < np && (my_tau[u] > lower || my_over[u] >= lower)) {
       atomicOr(&s_raw[q >> 5], 1u << (q & 31));
       ++bad;
     }
@@ -490,9 +512,184 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
     if (lane == 0) s_idx[q] = c;
   }
   __syncthreads();
-  (void)offsets([&](int q) { return s_idx[q]; });
+  (void)offsets([&](int, int q) { return s_idx[q]; });
   pad(run_select(thr, true, &lower));
 }
+
+// ---- the per-row kernel.  Fast path (rows of at most kSelThreads parts):
+// thread q holds part q's stored leaders in registers, in position order, so
+// (part, slot) order is the row's position order.  A bucket select over the
+// registers finds the k-th largest leader lo; one scan over the parts then
+// places each part's selected leaders.  If every part stored all its keys
+// >= lo (the check of step 2 of the general path) this is the answer;
+// otherwise, and for every other row, the general path runs.
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
+  extern __shared__ unsigned smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t qr = blockIdx.x;
+  const int64_t V = visible_of(a, qr);
+  const int np = a.nparts;
+  if (V > kTopkSel && np <= kSelThreads) {
+    unsigned* s_key = smem;                                   // [kTopkSel + 64]
+    unsigned* s_hist = smem + kTopkSel;                       // [kHistBins]
+    int* s_idx = reinterpret_cast<int*>(s_hist + kHistBins);  // [kTopkSel + 64]
+    __shared__ int s_wave[kSelWaves];
+    __shared__ unsigned s_mm[2][kSelWaves];
+    __shared__ unsigned s_sel[4];
+    const int k = a.k;
+    int32_t* topk = a.topk + qr * k;
+    float* tks = a.topk_score ? a.topk_score + qr * k : nullptr;
+    const unsigned* ck = a.cand_key + qr * (int64_t)np * kTopkPartCap;
+    const int* ci = a.cand_idx + qr * (int64_t)np * kTopkPartCap;
+    const int q = tid;
+    const bool own = q < np;
+    const int cq = own ? min(a.part_cnt[qr * np + q], kTopkPartCap) : 0;
+    const unsigned tau = own ? a.part_tau[qr * np + q] : 0u;
+    const unsigned over = own ? a.part_over[qr * np + q] : 0u;
+    unsigned key[kTopkPartCap];
+    int idx[kTopkPartCap];
+    if (own) {
+#pragma unroll
+      for (int u = 0; u < kTopkPartCap / 4; ++u) {
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(ck + q * kTopkPartCap + 4 * u);
+        const u32x4 ii = *reinterpret_cast<const u32x4*>(ci + q * kTopkPartCap + 4 * u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          key[4 * u + e] = 4 * u + e < cq ? kk[e] : 0u;
+          idx[4 * u + e] = (int)ii[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kTopkPartCap; ++j) key[j] = 0u;
+    }
+    // range of the present leaders and their number
+    unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < kTopkPartCap; ++j) {
+      kmin = key[j] != 0u ? min(kmin, key[j]) : kmin;
+      kmax = max(kmax, key[j]);
+    }
+    kmin = wave_min_u(kmin);
+    kmax = wave_max_u(kmax);
+    if (lane == 0) {
+      s_mm[0][wave] = kmin;
+      s_mm[1][wave] = kmax;
+    }
+    int total;
+    (void)block_excl_scan(cq, s_wave, &total);
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      kmin = min(kmin, s_mm[0][w]);
+      kmax = max(kmax, s_mm[1][w]);
+    }
+    // bucket select: the kept keys form the contiguous key range [lo, hi]
+    const bool all = total <= k;
+    unsigned lo = kmin, hi = kmax;
+    int need = all ? total : k;
+    if (!all) {
+      while (true) {
+        const unsigned span = hi - lo;
+        int shift = 0;
+        while ((span >> shift) >= (unsigned)kHistBins) ++shift;
+        const int nb = (int)(span >> shift) + 1;
+        for (int i = tid; i < nb; i += kSelThreads) s_hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kTopkPartCap; ++j)
+          if (key[j] != 0u && key[j] >= lo && key[j] <= hi) atomicAdd(&s_hist[(key[j] - lo) >> shift], 1u);
+        __syncthreads();
+        int loc = 0;
+#pragma unroll
+        for (int u = 0; u < kBucketsPerThread; ++u) {
+          const int d = nb - 1 - (kBucketsPerThread * tid + u);
+          loc += d >= 0 ? (int)s_hist[d] : 0;
+        }
+        int tot;
+        int above = block_excl_scan(loc, s_wave, &tot);
+#pragma unroll
+        for (int u = 0; u < kBucketsPerThread; ++u) {
+          const int d = nb - 1 - (kBucketsPerThread * tid + u);
+          const int cnt = d >= 0 ? (int)s_hist[d] : 0;
+          if (d >= 0 && above < need && above + cnt >= need) {
+            s_sel[0] = (unsigned)d;
+            s_sel[1] = (unsigned)above;
+            s_sel[2] = (unsigned)cnt;
+          }
+          above += cnt;
+        }
+        __syncthreads();
+        const unsigned d = s_sel[0];
+        const int cnt_gt = (int)s_sel[1], cnt_eq = (int)s_sel[2];
+        __syncthreads();
+        need -= cnt_gt;
+        const unsigned nlo = lo + (d << shift);
+        const uint64_t nhi = (uint64_t)nlo + (1ull << shift) - 1u;
+        hi = nhi < (uint64_t)hi ? (unsigned)nhi : hi;
+        lo = nlo;
+        if (cnt_eq == need || lo == hi) break;
+      }
+    }
+    // per part: keys above the bucket (key > hi_e) and in it
+    // (lo_e <= key <= hi); in-bucket keys go to the lowest positions first.
+    // With every leader kept, hi_e = 0 (present keys are >= 1) and no key is
+    // in the bucket.  Branch-free: a key that is not taken is written to a
+    // per-lane slot past the selection area (in the histogram, unused now).
+    const unsigned hi_e = all ? 0u : hi, lo_e = all ? 0xFFFFFFFFu : lo;
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int j = 0; j < kTopkPartCap; ++j) {
+      ngt += key[j] > hi_e ? 1 : 0;
+      neq += (key[j] >= lo_e && key[j] <= hi) ? 1 : 0;
+    }
+    int tot;
+    const int eq_before = block_excl_scan(neq, s_wave, &tot);
+    int take = need - eq_before;
+    take = take < 0 ? 0 : (take > neq ? neq : take);
+    int pos = block_excl_scan(ngt + take, s_wave, &tot);
+    // the selection goes to LDS first (a part's slots are contiguous there),
+    // then out in coalesced rows
+    const int dummy = kTopkSel + lane;   // s_key / s_idx slots past the selection
+    unsigned smin = 0xFFFFFFFFu;
+    int taken = 0;
+#pragma unroll
+    for (int j = 0; j < kTopkPartCap; ++j) {
+      const bool eq = key[j] >= lo_e && key[j] <= hi;
+      const bool sel = key[j] > hi_e || (eq && taken < take);
+      const int slot = sel ? pos : dummy;
+      s_key[slot] = key[j];
+      s_idx[slot] = idx[j];
+      pos += sel ? 1 : 0;
+      taken += eq ? 1 : 0;
+      smin = sel ? min(smin, key[j]) : smin;
+    }
+    smin = wave_min_u(smin);
+    if (lane == 0) s_mm[0][wave] = smin;
+    __syncthreads();
+    const int n_out = all ? total : k;
+    for (int i = tid; i < n_out; i += kSelThreads) {
+      topk[i] = s_idx[i];
+      if (tks) tks[i] = key_score(s_key[i]);
+    }
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) smin = min(smin, s_mm[0][w]);
+    const unsigned low = all ? 1u : smin;   // the k-th largest leader
+    // step 2's check
+    const int bad = (own && (tau > low || over >= low)) ? 1 : 0;
+    int nbad;
+    (void)block_excl_scan(bad, s_wave, &nbad);
+    if (nbad == 0) {
+      for (int i = n_out + tid; i < k; i += kSelThreads) {
+        topk[i] = -1;
+        if (tks) tks[i] = -INFINITY;
+      }
+      return;
+    }
+    __syncthreads();
+  }
+  topk_select_general(a, smem);
+}
+
 
 static bool g_topk_attr_set = false;
 
