@@ -20,6 +20,7 @@ A "prefill" section times the 4096-token chunk appended to a 2^20-token
 context (both layers) and reports MFMA fractions for scoring and attention.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
+                    [--prefill-only] [--graph] [--counters]
 """
 
 import argparse
@@ -37,12 +38,12 @@ COPY_BYTES = 1 << 30           # calibration copy for the HBM byte counters
 # HBM bytes of one index_score launch at the decode shape, from two
 # rocprofv3 --pmc passes over `bench.py --counters` (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
-# for torch's elementwise kernel over 1 GiB in and 1 GiB out (FETCH 524,320
+# for torch's elementwise kernel over 1 GiB in and 1 GiB out (FETCH 524,319
 # KiB -> x2.0; WRITE 1,048,576 KiB -> x1.0).  Valid only for the kernel
 # sources they were taken with (hash below); otherwise reported as null.
-TRAFFIC = {"sources_sha256_16": "f434a9afba727c05",
-           "fetch_kib": 262708.3, "fetch_scale": 2.0,
-           "write_kib": 8195.8, "write_scale": 1.0}
+TRAFFIC = {"sources_sha256_16": "408a3e7f48ae5d1e",
+           "fetch_kib": 262711.9, "fetch_scale": 2.0,
+           "write_kib": 8195.0, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("long_context_sparse_csa_amd/csrc/indexer.hip",
                    "long_context_sparse_csa_amd/csrc/common.hpp")
 METRIC = "decode query-tokens/s per layer at 1M ctx (CSA, HCA); % of HBM/MFMA peak"
@@ -333,6 +334,8 @@ def main():
                     help="time HIP-graph replays of the overlapped schedule (on this stack "
                          "slower than the calls launched one by one)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill chunk (prints its section as the JSON line)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 4096-token prefill section")
     ap.add_argument("--counters", action="store_true",
@@ -351,6 +354,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
     ops.lib()
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_section(dev, 3)}), flush=True)
+        return
     log("generating inputs")
     inp = build_inputs(dev, args.rotate)
     launches, st = make_step(inp, dev)
