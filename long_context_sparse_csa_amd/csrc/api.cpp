@@ -244,7 +244,7 @@ hipError_t run_score(const uint16_t* q_idx, const float* w_idx, const uint16_t* 
                      int m, float* scores, int64_t stride, hipStream_t st) {
   const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
   v4::IndexScoreArgs ia{q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m,
-                        vmax, scores, stride, v4::index_keys_per_wave(B, Tq, vmax)};
+                        vmax, scores, stride, v4::index_row_waves(B, Tq, vmax)};
   return v4::launch_index_score(ia, st);
 }
 

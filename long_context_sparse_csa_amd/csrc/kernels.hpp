@@ -38,10 +38,10 @@ struct IndexScoreArgs {
   int64_t vmax;           // max visible entries over the query block
   float* scores;          // [B*Tq, score_stride]
   int64_t score_stride;
-  int64_t keys_per_wave;  // contiguous keys one wave scores (multiple of 32)
+  int64_t row_waves;      // waves sharing one query row (multiple of 4)
 };
-// Keys per wave that spread a launch over three workgroups per CU.
-int64_t index_keys_per_wave(int B, int Tq, int64_t vmax);
+// Waves per query row that spread a launch over three workgroups per CU.
+int64_t index_row_waves(int B, int Tq, int64_t vmax);
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t st);
 
 // Top-k selection: per-part leaders -> exact per-row select.
