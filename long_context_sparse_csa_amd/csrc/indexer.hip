@@ -29,12 +29,22 @@
 // in registers as the A operands of v_mfma_f32_32x32x16_bf16, the faster bf16
 // shape on this chip) and walks its key range in
 // 128-key tiles copied straight to LDS with global_load_lds (four 1 KiB
-// copies per wave per tile, three tiles in rotation, chunks XOR-swizzled by
-// row so the operand reads are free of bank conflicts).
+// copies per wave per tile, two tiles in turn, chunks XOR-swizzled by row so
+// the operand reads are free of bank conflicts).  The vector ALU work per
+// MFMA (ReLU and weighted head sum) is about half the MFMA time, so it is
+// kept lean: the ReLU is one integer max, and the scores of a tile are stored
+// at the start of the next step, off the path of the copy wait.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace v4 {
+
+// max(x, 0) as one integer max on the bits: a negative float (sign bit set)
+// is a negative int and becomes +0, a non-negative one is unchanged (fmaxf
+// would first quiet a possible signalling NaN, a second instruction).
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
 
 template <int DI, int MB>
 __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
@@ -127,7 +137,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
       for (int i4 = 0; i4 < 4; ++i4) {
         const f32x4 w4 = *reinterpret_cast<const f32x4*>(&s_w[hb * 32 + i4 * 8 + (lane >> 5) * 4]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc = fmaf(w4[i], fmaxf(acc[hb][4 * i4 + i], 0.f), sc);
+        for (int i = 0; i < 4; ++i) sc = fmaf(w4[i], relu(acc[hb][4 * i4 + i]), sc);
       }
     sc += __shfl_xor(sc, 32);
     const int64_t j = ch * 32 + (lane & 31);
@@ -152,10 +162,12 @@ __device__ __forceinline__ void idx_copy_to_lds16(const void* src, V4_LDS void* 
 
 __global__ __launch_bounds__(kBlkWaves * 64) void index_score_block_kernel(IndexScoreArgs a,
                                                                            int64_t key_chunk) {
+  constexpr int KEYS = kBlkKeys;
+  constexpr int NBUF = 2;                  // tiles in LDS
   constexpr int DI = 128;
   constexpr int RB = 2 * DI;               // key row bytes
   constexpr int CPR = RB / 16;             // 16-byte chunks per row
-  constexpr int TILE = kBlkKeys * RB;      // bytes per tile
+  constexpr int TILE = KEYS * RB;      // bytes per tile
   constexpr int KS = DI / 16;              // 32x32x16 k-steps
   constexpr int CPW = TILE / 1024 / kBlkWaves;   // 1 KiB copies per wave per tile
   static_assert(CPW * 1024 * kBlkWaves == TILE, "whole copies per wave");
@@ -172,11 +184,9 @@ __global__ __launch_bounds__(kBlkWaves * 64) void index_score_block_kernel(Index
   const int64_t kc0 = (int64_t)blockIdx.x * key_chunk;
   const int64_t kc1 = min(kc0 + key_chunk, Vlast);
   if (kc0 >= kc1) return;
-  const int ntiles = (int)((kc1 - kc0 + kBlkKeys - 1) / kBlkKeys);
+  const int ntiles = (int)((kc1 - kc0 + KEYS - 1) / KEYS);
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_k0[TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t s_k1[TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t s_k2[TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[NBUF][TILE];
   __shared__ __attribute__((aligned(16))) float s_w[kBlkQ][64];
 
   const bool wok = r0 < a.Tq;   // the wave has at least one query
@@ -217,16 +227,17 @@ __global__ __launch_bounds__(kBlkWaves * 64) void index_score_block_kernel(Index
     for (int i = 0; i < CPW; ++i) {
       const int win = CPW * wave + i;
       const int row = 4 * win + (lane >> 4);   // 64 slots of 16 bytes = 4 rows per copy
-      int64_t j = kc0 + (int64_t)tile * kBlkKeys + row;
+      int64_t j = kc0 + (int64_t)tile * KEYS + row;
       j = j < kc1 ? j : kc1 - 1;   // past the range: re-read a valid key (score not stored)
       const int lc = (lane & 15) ^ (row & 15);
       idx_copy_to_lds16(kbase + j * RB + 16 * lc, (V4_LDS void*)(T + 1024 * win));
     }
   };
 
-  auto compute = [&](int tile, const uint8_t* T) {
-#pragma unroll 2
-    for (int kb = 0; kb < kBlkKeys / 32; ++kb) {
+  constexpr int NKB = KEYS / 32;
+  auto compute = [&](int tile, const uint8_t* T, float* scv) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
       f32x16 acc[kBlkQPW][2];
 #pragma unroll
       for (int u = 0; u < kBlkQPW; ++u)
@@ -247,7 +258,7 @@ __global__ __launch_bounds__(kBlkWaves * 64) void index_score_block_kernel(Index
             acc[u][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u][hb][s], kv, acc[u][hb], 0, 0, 0);
       }
       // lane holds key (lane & 31), heads hb*32 + (i/4)*8 + (lane>>5)*4 + i%4
-      const int64_t j = kc0 + (int64_t)tile * kBlkKeys + kb * 32 + (lane & 31);
+      const int64_t j = kc0 + (int64_t)tile * KEYS + kb * 32 + (lane & 31);
 #pragma unroll
       for (int u = 0; u < kBlkQPW; ++u) {
         float sc = 0.f;
@@ -258,36 +269,41 @@ __global__ __launch_bounds__(kBlkWaves * 64) void index_score_block_kernel(Index
             const f32x4 w4 = *reinterpret_cast<const f32x4*>(
                 &s_w[wave * kBlkQPW + u][hb * 32 + i4 * 8 + (lane >> 5) * 4]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc = fmaf(w4[i], fmaxf(acc[u][hb][4 * i4 + i], 0.f), sc);
+            for (int i = 0; i < 4; ++i) sc = fmaf(w4[i], relu(acc[u][hb][4 * i4 + i]), sc);
           }
         sc += __shfl_xor(sc, 32);
-        if (lane < 32 && j < jmax[u]) a.scores[qrow[u] * a.score_stride + j] = sc;
+        scv[kb] = sc;
       }
     }
   };
+  auto flush = [&](int tile, const float* scv) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int64_t j = kc0 + (int64_t)tile * KEYS + kb * 32 + (lane & 31);
+      if (lane < 32 && j < jmax[0]) a.scores[qrow[0] * a.score_stride + j] = scv[kb];
+    }
+  };
 
-  // Tile t lives in buffer t % 3: a step issues tile t+2, uses tile t, then
-  // waits for its own copies of tile t+1 (t+2's may stay in flight) and meets
-  // the other waves at the barrier.
-  if (ntiles > 0) issue(0, s_k0);
-  if (ntiles > 1) issue(1, s_k1);
+  // Tile t lives in buffer t % NBUF.  A step first stores the previous
+  // tile's scores (held in registers, so that the store latency overlaps a
+  // whole step and the copies issued after them are the newest memory
+  // operations), issues tile t + NBUF - 1, uses tile t, then waits for its own
+  // copies of tile t+1 (later tiles may stay in flight) and meets the other
+  // waves at the barrier.
+  for (int p = 0; p < NBUF - 1 && p < ntiles; ++p) issue(p, s_k[p]);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  auto step = [&](int tile, const uint8_t* Tr, uint8_t* Ti) {
-    const bool pre = tile + 2 < ntiles;
-    if (pre) issue(tile + 2, Ti);
-    if (wok) compute(tile, Tr);
+  float scv[NKB];
+  for (int tile = 0; tile < ntiles; ++tile) {
+    if (tile > 0 && wok) flush(tile - 1, scv);
+    const bool pre = tile + NBUF - 1 < ntiles;
+    if (pre) issue(tile + NBUF - 1, s_k[(tile + NBUF - 1) % NBUF]);
+    if (wok) compute(tile, s_k[tile % NBUF], scv);
     if (pre)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(CPW) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(CPW * (NBUF - 2)) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
-  for (int tile = 0; tile < ntiles; tile += 3) {
-    step(tile, s_k0, s_k2);
-    if (tile + 1 >= ntiles) break;
-    step(tile + 1, s_k1, s_k0);
-    if (tile + 2 >= ntiles) break;
-    step(tile + 2, s_k2, s_k1);
   }
+  if (ntiles > 0 && wok) flush(ntiles - 1, scv);
 }
 
 int64_t index_row_waves(int B, int Tq, int64_t vmax) {
