@@ -45,6 +45,35 @@ def integers(shape, lo, hi, seed, name, device="cpu", dtype=torch.float32):
     return x.to(dtype)
 
 
+def e4m3_codes(shape, seed, name, device="cpu"):
+    """Uniform random finite OCP E4M3FN codes, uint8 (the NaN codes 0x7F and
+    0xFF are never drawn)."""
+    g = _gen(seed, name, device)
+    x = torch.randint(0, 254, shape, generator=g, device=device)
+    x = x + (x >= 0x7F).to(x.dtype)
+    return x.to(torch.uint8)
+
+
+def e4m3_rows(shape, seed, name, device="cpu", chunk_rows=1 << 20):
+    """N(0,1) rows stored as E4M3FN codes with one fp32 scale per row (the
+    row's largest magnitude / 448, so the largest value maps to 448): codes
+    uint8 [*shape], scales float32 [*shape[:-1]] (torch casts)."""
+    d = shape[-1]
+    rows = 1
+    for s in shape[:-1]:
+        rows *= s
+    codes = torch.empty((rows, d), dtype=torch.uint8, device=device)
+    scales = torch.empty((rows,), dtype=torch.float32, device=device)
+    g = _gen(seed, name, device)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        v = torch.randn((r1 - r0, d), generator=g, device=device)
+        sc = v.abs().amax(dim=1).clamp_min(1e-30) / 448.0
+        codes[r0:r1] = (v / sc[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        scales[r0:r1] = sc
+    return codes.view(*shape), scales.view(*shape[:-1])
+
+
 def pack_values(vals, R):
     """float32 [..., D] -> uint8 [..., D+R]: E4M3FN codes of dims [0, D-R)
     followed by little-endian bf16 of dims [D-R, D) (torch casts)."""

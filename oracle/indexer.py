@@ -12,6 +12,10 @@ Readings (the pages print no formula for the score):
     entry shared by all heads; no extra scale (it folds into w);
   * query at position t sees entries j < V_t = min(n_entries, floor((t+1)/m))
     (entry j exists once token (j+1)m-1 is cached);
+  * FP8 indexer ([P1] step 3: the indexer's few heads run in FP8; [P5] same
+    section: the indexer's attention runs at reduced precision): queries and
+    keys are OCP E4M3FN codes with one positive scale per row (per query
+    head, per key); the score is the score above of the dequantised rows;
   * top-k order is (score descending, index ascending): ties go to the lower
     entry index.  The first min(k, V_t) entries in that order form the set;
     it is returned in ascending index order, padded with -1 to length k.
@@ -20,6 +24,8 @@ Readings (the pages print no formula for the score):
 """
 
 import numpy as np
+
+from .codecs import e4m3_decode
 
 
 def visible_entries(t, n_entries, m):
@@ -61,6 +67,31 @@ def index_topk(q_idx, w, k_idx, n_entries, q_pos, m, k):
     for r in range(Tq):
         V = visible_entries(int(q_pos[r]), n_entries, m)
         sc = index_scores(q_idx[r], w[r], k_idx, V)
+        topk[r] = topk_select(sc, k)
+        scores.append(sc)
+    return topk, scores
+
+
+def index_scores_fp8(q8, q_scale, w, k8, k_scale, V):
+    """FP8 indexer scores of one query against entries 0..V-1, float64 [V].
+
+    q8: uint8 E4M3 codes [H_I, d_I]; q_scale: [H_I]; w: [H_I];
+    k8: uint8 E4M3 codes [>=V, d_I]; k_scale: [>=V].  Query head h is
+    q_scale[h] * decode(q8[h]) and key j is k_scale[j] * decode(k8[j])."""
+    q = e4m3_decode(np.asarray(q8)) * np.asarray(q_scale, dtype=np.float64)[:, None]
+    k = e4m3_decode(np.asarray(k8[:V])) * np.asarray(k_scale[:V], dtype=np.float64)[:, None]
+    return index_scores(q, w, k, V)
+
+
+def index_topk_fp8(q8, q_scale, w, k8, k_scale, n_entries, q_pos, m, k):
+    """index_topk for the FP8 indexer: q8 [Tq, H_I, d_I], q_scale and w
+    [Tq, H_I], k8 [>= n_entries, d_I], k_scale [>= n_entries]."""
+    Tq = q8.shape[0]
+    topk = np.full((Tq, k), -1, dtype=np.int32)
+    scores = []
+    for r in range(Tq):
+        V = visible_entries(int(q_pos[r]), n_entries, m)
+        sc = index_scores_fp8(q8[r], q_scale[r], w[r], k8, k_scale, V)
         topk[r] = topk_select(sc, k)
         scores.append(sc)
     return topk, scores

@@ -40,6 +40,60 @@ def test_index_scores_integer_bruteforce():
     assert oi.index_scores(q, w, k, 17).shape == (17,)
 
 
+# E4M3FN codes of a few exact values (sign bit 0x80; 1.0 = exponent 7, bias 7)
+_E4M3 = {0.0: 0x00, 0.5: 0x30, 1.0: 0x38, 1.5: 0x3C, 2.0: 0x40, 3.0: 0x44}
+
+
+def _code(v):
+    return _E4M3[abs(v)] | (0x80 if v < 0 else 0)
+
+
+def test_index_scores_fp8_hand_example():
+    # q = q_scale * q8 = [[2, 4], [-0.5, 0.25]];  k = k_scale * k8 =
+    # [[1, -1], [2.25, 1.125], [2, 8]];  w = [1, -2]:
+    # j=0: dots -2, -0.75 -> 0;  j=1: 9, -0.84375 -> 9;  j=2: 36, 1 -> 36 - 2 = 34
+    q8 = np.array([[_code(1.0), _code(2.0)], [_code(-1.0), _code(0.5)]], dtype=np.uint8)
+    k8 = np.array([[_code(1.0), _code(-1.0)], [_code(3.0), _code(1.5)],
+                   [_code(0.5), _code(2.0)]], dtype=np.uint8)
+    got = oi.index_scores_fp8(q8, np.array([2.0, 0.5]), np.array([1.0, -2.0]), k8,
+                              np.array([1.0, 0.75, 4.0]), 3)
+    assert got.tolist() == [0.0, 9.0, 34.0]
+
+
+def test_index_scores_fp8_integer_codes_equal_integer_scores():
+    # unit scales and integer codes reduce to the integer indexer above
+    g = np.random.default_rng(3)
+    HI, dI, N = 4, 64, 40
+    q = g.integers(-3, 4, (HI, dI))
+    k = g.integers(-3, 4, (N, dI))
+    w = g.integers(-3, 4, HI).astype(np.float64)
+    enc = np.vectorize(lambda v: _code(float(v)))
+    got = oi.index_scores_fp8(enc(q).astype(np.uint8), np.ones(HI), w,
+                              enc(k).astype(np.uint8), np.ones(N), N)
+    assert np.array_equal(got, oi.index_scores(q, w, k, N))
+
+
+def test_index_scores_fp8_scales_are_per_row():
+    g = np.random.default_rng(4)
+    HI, dI, N = 3, 64, 20
+    q8 = g.integers(0, 0x7F, (HI, dI)).astype(np.uint8) | (g.integers(0, 2, (HI, dI)) * 0x80).astype(np.uint8)
+    k8 = g.integers(0, 0x7F, (N, dI)).astype(np.uint8) | (g.integers(0, 2, (N, dI)) * 0x80).astype(np.uint8)
+    qs, ks, w = g.uniform(0.5, 2, HI), g.uniform(0.5, 2, N), g.normal(size=HI)
+    base = oi.index_scores_fp8(q8, qs, w, k8, ks, N)
+    # a key's scale multiplies its score (positive homogeneity of ReLU)
+    ks2 = ks.copy()
+    ks2[5] *= 4.0
+    s2 = oi.index_scores_fp8(q8, qs, w, k8, ks2, N)
+    assert np.isclose(s2[5], 4.0 * base[5], rtol=1e-12)
+    assert np.array_equal(np.delete(s2, 5), np.delete(base, 5))
+    # a query head's scale acts like a factor on that head's weight
+    qs2, w2 = qs.copy(), w.copy()
+    qs2[1] *= 8.0
+    w2[1] *= 8.0
+    assert np.allclose(oi.index_scores_fp8(q8, qs2, w, k8, ks, N),
+                       oi.index_scores_fp8(q8, qs, w2, k8, ks, N), rtol=1e-12, atol=0)
+
+
 def test_visible_entries():
     assert oi.visible_entries(4095, 1024, 4) == 1024
     assert oi.visible_entries(4094, 1024, 4) == 1023
