@@ -161,6 +161,41 @@ int v4attn_topk_select(const float* scores, int64_t score_stride, int B,
                        size_t ws_bytes, void* stream);
 
 /*
+ * v4attn_index_score_fp8 / v4attn_index_topk_fp8 -- the lightning indexer
+ * with FP8 inputs.
+ *
+ * Defines: the indexer is a few small heads run in FP8 ("DeepSeek-V4,
+ * explained", step 3 of how one query's layer works; "DeepSeek-V4: Making a
+ * Million Tokens Affordable", section "Two ways to shrink attention,
+ * interleaved", on the indexer's reduced precision).  Queries and keys are OCP
+ * E4M3FN codes, each row with a positive fp32 scale:
+ *   score_{t,j} = sum_h w_{t,h} ReLU((sq_{t,h} q8_{t,h}) . (sk_j k8_j)),
+ * formed on the FP8 matrix cores as sk_j * sum_h (w_{t,h} sq_{t,h})
+ * ReLU(q8_{t,h} . k8_j) (exact E4M3 products, fp32 accumulation; w sq is one
+ * fp32 product).  Visibility, top-k rule and outputs are those of
+ * v4attn_index_topk / v4attn_index_score.
+ *
+ *   q8       u8  [B, Tq, HI, dI]  E4M3 indexer queries (16-byte aligned)
+ *   q_scale  f32 [B, Tq, HI]      per query head, > 0
+ *   w_idx    f32 [B, Tq, HI]      per-query head weights
+ *   k8       u8  [B, Ncap, dI]    E4M3 indexer keys (16-byte aligned)
+ *   k_scale  f32 [B, Ncap]        per key, > 0 (a scale <= 0 or not finite
+ *                                 gives scores the formula above does not)
+ *   dI in {64, 128}; HI <= 64.  The workspace of v4attn_index_topk_fp8 is
+ *   v4attn_index_topk_workspace(...) bytes; contents on entry are ignored.
+ * q8 and k8 must hold finite codes (0x7F and 0xFF are NaN in E4M3FN).
+ */
+int v4attn_index_score_fp8(const uint8_t* q8, const float* q_scale, const float* w_idx,
+                           const uint8_t* k8, const float* k_scale, int B, int Tq, int HI,
+                           int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m,
+                           float* scores, int64_t score_stride, void* stream);
+int v4attn_index_topk_fp8(const uint8_t* q8, const float* q_scale, const float* w_idx,
+                          const uint8_t* k8, const float* k_scale, int B, int Tq, int HI,
+                          int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m,
+                          int k, int32_t* topk, float* topk_score, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
  * v4attn_csa_attend -- CSA core attention: shared-KV multi-query attention
  * over the selected entries plus the uncompressed window, with sink.
  *

@@ -44,6 +44,25 @@ struct IndexScoreArgs {
 int64_t index_row_waves(int B, int Tq, int64_t vmax);
 hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t st);
 
+// FP8 lightning-indexer scoring: q and k as OCP E4M3 codes with positive
+// fp32 scales (one per query head, one per key); same score buffer.
+struct IndexScoreFp8Args {
+  const uint8_t* q8;       // [B, Tq, HI, dI] E4M3
+  const float* q_scale;    // [B, Tq, HI]
+  const float* w_idx;      // [B, Tq, HI]
+  const uint8_t* k8;       // [B, Ncap, dI] E4M3
+  const float* k_scale;    // [B, Ncap]
+  int B, Tq, HI, dI;
+  int64_t Ncap, n_entries, q_pos0;
+  int m;
+  int64_t vmax;            // max visible entries over the query block
+  float* scores;           // [B*Tq, score_stride]
+  int64_t score_stride;
+  int64_t row_waves;       // waves sharing one query row (multiple of 4)
+};
+int64_t index_fp8_row_waves(int B, int Tq, int64_t vmax);
+hipError_t launch_index_score_fp8(const IndexScoreFp8Args& a, hipStream_t st);
+
 // Top-k selection: per-part leaders -> exact per-row select.
 constexpr int kTopkSel = 16384;     // keys the per-row selection holds in LDS
 constexpr int kTopkPartLen = 1024;  // scores per part

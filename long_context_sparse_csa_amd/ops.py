@@ -41,6 +41,10 @@ _SIGS = {
     "v4attn_index_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _I, _P, _P, _P, _Z,
                                _P]),
     "v4attn_index_score": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _P, _L, _P]),
+    "v4attn_index_score_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _P, _L,
+                                    _P]),
+    "v4attn_index_topk_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _I, _P,
+                                   _P, _P, _Z, _P]),
     "v4attn_topk_select_workspace": (_Z, [_I, _I, _L, _L, _I, _I]),
     "v4attn_topk_select": (_I, [_P, _L, _I, _I, _L, _L, _I, _I, _P, _P, _P, _Z, _P]),
     "v4attn_csa_attend_workspace": (_Z, [_I, _I, _I, _I, _I, _I]),
@@ -217,6 +221,53 @@ def index_score(q_idx, w_idx, k_idx, *, n_entries, q_pos0, m, scores=None):
                                    k_idx.shape[1], int(n_entries), int(q_pos0), int(m),
                                    _ptr(scores), scores.shape[1], _stream(q_idx)))
     return scores
+
+
+def _fp8_inputs(q8, q_scale, w_idx, k8, k_scale):
+    _need(q8, "q8", torch.uint8, 4)
+    _need(q_scale, "q_scale", torch.float32, 3)
+    _need(w_idx, "w_idx", torch.float32, 3)
+    _need(k8, "k8", torch.uint8, 3)
+    _need(k_scale, "k_scale", torch.float32, 2)
+    B, Tq, HI, dI = q8.shape
+    if tuple(q_scale.shape) != (B, Tq, HI) or tuple(w_idx.shape) != (B, Tq, HI) \
+            or k8.shape[0] != B or k8.shape[2] != dI or tuple(k_scale.shape) != tuple(k8.shape[:2]):
+        raise ValueError("shape mismatch")
+    return B, Tq, HI, dI, k8.shape[1]
+
+
+def index_score_fp8(q8, q_scale, w_idx, k8, k_scale, *, n_entries, q_pos0, m, scores=None):
+    """FP8 indexer scores f32 [B*Tq, stride] from E4M3 codes (uint8) and
+    per-row fp32 scales; row b*Tq+r is valid for j < V_t."""
+    B, Tq, HI, dI, Ncap = _fp8_inputs(q8, q_scale, w_idx, k8, k_scale)
+    if scores is None:
+        scores = torch.empty((B * Tq, max(score_stride(Tq, n_entries, q_pos0, m), 1)),
+                             dtype=torch.float32, device=q8.device)
+    _need(scores, "scores", torch.float32, 2)
+    check(lib().v4attn_index_score_fp8(_ptr(q8), _ptr(q_scale), _ptr(w_idx), _ptr(k8),
+                                       _ptr(k_scale), B, Tq, HI, dI, Ncap, int(n_entries),
+                                       int(q_pos0), int(m), _ptr(scores), scores.shape[1],
+                                       _stream(q8)))
+    return scores
+
+
+def index_topk_fp8(q8, q_scale, w_idx, k8, k_scale, *, n_entries, q_pos0, m, k, topk=None,
+                   topk_score=None, want_scores=False, workspace=None):
+    """Top-k entry indices per query from the FP8 indexer (int32 [B, Tq, k])."""
+    B, Tq, HI, dI, Ncap = _fp8_inputs(q8, q_scale, w_idx, k8, k_scale)
+    dev = q8.device
+    if topk is None:
+        topk = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
+    _need(topk, "topk", torch.int32, 3)
+    if want_scores and topk_score is None:
+        topk_score = torch.empty((B, Tq, k), dtype=torch.float32, device=dev)
+    nbytes = index_topk_workspace_bytes(B, Tq, n_entries, q_pos0, m, k)
+    workspace = _workspace(nbytes, dev, workspace)
+    check(lib().v4attn_index_topk_fp8(_ptr(q8), _ptr(q_scale), _ptr(w_idx), _ptr(k8),
+                                      _ptr(k_scale), B, Tq, HI, dI, Ncap, int(n_entries),
+                                      int(q_pos0), int(m), int(k), _ptr(topk), _ptr(topk_score),
+                                      _ptr(workspace), nbytes, _stream(q8)))
+    return topk, topk_score
 
 
 def topk_select_workspace_bytes(B, Tq, n_entries, q_pos0, m, k):
