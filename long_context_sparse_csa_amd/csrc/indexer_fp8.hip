@@ -20,10 +20,12 @@
 // Design (decode, few queries): as the bf16 decode kernel, at half the bytes
 // per key.  q (all heads, E4M3) sits in registers as the MFMA's A operands
 // (32 heads x 64 dims per operand), the folded weights w sq in LDS.  A row's
-// keys are cut into 32-key chunks dealt round-robin over the row's waves; a
-// chunk is read with non-temporal loads, 1 KiB of contiguous keys per
-// instruction, with its 32 key scales, staged in the wave's padded LDS rows
-// and read back as the B operand while the next chunk is in flight.
+// keys are cut into 64-key chunks (8 KiB, the bytes per wave in flight of the
+// bf16 kernel; 32-key chunks measured 1% slower, 128-key ones 15%) dealt
+// round-robin over the row's waves; a chunk is read with non-temporal loads,
+// 1 KiB of contiguous keys per instruction, with its key scales, staged in
+// the wave's padded LDS rows and read back as the B operand of two 32-key
+// blocks while the next chunk is in flight.
 //
 // Design (prefill, a block of queries of one sequence): eight waves, one
 // query each (q in registers), share 128-key tiles (16 KiB) copied straight
@@ -72,31 +74,32 @@ __device__ __forceinline__ void load_q8(const IndexScoreFp8Args& a, int64_t qrow
 
 }  // namespace
 
-template <int DI>
+template <int DI, int CK>
 __global__ __launch_bounds__(256) void index_score_fp8_kernel(IndexScoreFp8Args a) {
   constexpr int KS = DI / 64;        // 32x32x64 k-steps
   constexpr int RB = DI;             // key row bytes
   constexpr int P = RB / 16;         // 16-byte pieces per key
   constexpr int KPI = 64 / P;        // keys per load instruction
-  constexpr int NL = 32 / KPI;       // load instructions per 32-key chunk
+  constexpr int NL = CK / KPI;       // load instructions per CK-key chunk
+  constexpr int NB = CK / 32;        // 32-key MFMA blocks per chunk
   constexpr int KSTR = RB + 16;      // padded LDS row: the operand reads hit distinct banks
   const int b = blockIdx.z, r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = a.q_pos0 + r;
   int64_t V = (t + 1) / a.m;
   if (V > a.n_entries) V = a.n_entries;
-  const int64_t nch = (V + 31) / 32;
+  const int64_t nch = (V + CK - 1) / CK;
   const int64_t NW = (int64_t)gridDim.x * 4;
   const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
   if ((int64_t)blockIdx.x * 4 >= nch) return;   // the whole block is past the visible keys
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[4][32 * KSTR];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[4][CK * KSTR];
   __shared__ __attribute__((aligned(16))) float s_w[64];
 
   const uint8_t* kbase = a.k8 + (int64_t)b * a.Ncap * DI;
   const float* sbase = a.k_scale + (int64_t)b * a.Ncap;
   u32x4 kv[NL];
-  float ks_n = 0.f;   // scale of key lane % 32 of the chunk in flight
+  float ks_n[NB];   // scales of keys 32 nb + lane % 32 of the chunk in flight
   auto load = [&](int64_t j0) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -104,9 +107,10 @@ __global__ __launch_bounds__(256) void index_score_fp8_kernel(IndexScoreFp8Args 
       kv[i] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4*>(kbase + j * RB + 16 * (lane % P)));
     }
-    ks_n = sbase[min(j0 + (lane & 31), V - 1)];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) ks_n[nb] = sbase[min(j0 + 32 * nb + (lane & 31), V - 1)];
   };
-  if (gw < nch) load(gw * 32);   // in flight while q and the weights load
+  if (gw < nch) load(gw * CK);   // in flight while q and the weights load
 
   const int64_t qrow = (int64_t)b * a.Tq + r;
   i32x8 qa[2][KS];
@@ -121,36 +125,45 @@ __global__ __launch_bounds__(256) void index_score_fp8_kernel(IndexScoreFp8Args 
 #pragma unroll
     for (int i = 0; i < NL; ++i)
       *reinterpret_cast<u32x4*>(kst + (i * KPI + lane / P) * KSTR + 16 * (lane % P)) = kv[i];
-    const float ksc = ks_n;
-    if (ch + NW < nch) load((ch + NW) * 32);
-    f32x16 acc[2];
+    float ksc[NB];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int nb = 0; nb < NB; ++nb) ksc[nb] = ks_n[nb];
+    if (ch + NW < nch) load((ch + NW) * CK);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[hb][i] = 0.f;
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x16 acc[2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint8_t* kp = kst + (lane & 31) * KSTR + 64 * ks + 32 * (lane >> 5);
-      const i32x8 kb = cat8(*reinterpret_cast<const u32x4*>(kp), *reinterpret_cast<const u32x4*>(kp + 16));
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) acc[hb] = mfma_e4m3(qa[hb][ks], kb, acc[hb]);
-    }
-    // lane holds key lane % 32, heads hb*32 + (i/4)*8 + (lane/32)*4 + i%4
-    float sc = 0.f;
+        for (int i = 0; i < 16; ++i) acc[hb][i] = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint8_t* kp = kst + (32 * nb + (lane & 31)) * KSTR + 64 * ks + 32 * (lane >> 5);
+        const i32x8 kb = cat8(*reinterpret_cast<const u32x4*>(kp), *reinterpret_cast<const u32x4*>(kp + 16));
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 w4 = *reinterpret_cast<const f32x4*>(&s_w[hb * 32 + i4 * 8 + (lane >> 5) * 4]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc = fmaf(w4[i], relu8(acc[hb][4 * i4 + i]), sc);
+        for (int hb = 0; hb < 2; ++hb) acc[hb] = mfma_e4m3(qa[hb][ks], kb, acc[hb]);
       }
-    sc += __shfl_xor(sc, 32);
-    const int64_t j = ch * 32 + (lane & 31);
-    if (lane < 32 && j < V) sp[j] = ksc * sc;
+      // lane holds key 32 nb + lane % 32, heads hb*32 + (i/4)*8 + (lane/32)*4 + i%4
+      float sc = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 w4 = *reinterpret_cast<const f32x4*>(&s_w[hb * 32 + i4 * 8 + (lane >> 5) * 4]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc = fmaf(w4[i], relu8(acc[hb][4 * i4 + i]), sc);
+        }
+      sc += __shfl_xor(sc, 32);
+      const int64_t j = ch * CK + 32 * nb + (lane & 31);
+      if (lane < 32 && j < V) sp[j] = ksc[nb] * sc;
+    }
   }
 }
 
+#ifndef V4_F8_CHUNK
+#define V4_F8_CHUNK 64
+#endif
+constexpr int kF8Chunk = V4_F8_CHUNK;   // keys per decode chunk (a multiple of 32)
 constexpr int kF8Waves = 8;      // waves (queries) per workgroup
 constexpr int kF8Keys = 128;     // keys per LDS tile
 
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(kF8Waves * 64) void index_score_fp8_block_kernel(In
 
 int64_t index_fp8_row_waves(int B, int Tq, int64_t vmax) {
   const int64_t rows = (int64_t)B * Tq;
-  const int64_t nch = (vmax + 31) / 32;
+  const int64_t nch = (vmax + kF8Chunk - 1) / kF8Chunk;
   int64_t per_row = (256 * 12 + rows - 1) / rows;   // 256 CUs x 12 waves (three workgroups)
   const int64_t cpw = (nch + per_row - 1) / per_row;
   per_row = (nch + cpw - 1) / cpw;
@@ -295,9 +308,9 @@ hipError_t launch_index_score_fp8(const IndexScoreFp8Args& a, hipStream_t st) {
   }
   dim3 grid((unsigned)(a.row_waves / 4), a.Tq, a.B);
   if (a.dI == 64)
-    index_score_fp8_kernel<64><<<grid, 256, 0, st>>>(a);
+    index_score_fp8_kernel<64, kF8Chunk><<<grid, 256, 0, st>>>(a);
   else
-    index_score_fp8_kernel<128><<<grid, 256, 0, st>>>(a);
+    index_score_fp8_kernel<128, kF8Chunk><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
