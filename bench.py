@@ -3,10 +3,11 @@
 
 One step is one decode token per sequence through
   * a CSA layer (compression m = 4, top-k 1024, window 128), 8 sequences of
-    2^20 tokens: pack the new token's window row, pool the entry it completes,
+    2^20 tokens: pack the new token's window row and pool the entry it completes
+    (one fused compress step),
     indexer scores over all 262,144 entries, top-k, sparse attention;
   * an HCA layer (compression m' = 128, window 128), 32 sequences of 2^20
-    tokens: pack, pool, dense attention over all 8,192 entries.
+    tokens: the compress step, dense attention over all 8,192 entries.
 All inputs are seeded synthetic N(0,1) data resident in HBM before timing.
 The HCA caches rotate over several copies so successive steps do not hit the
 256 MB Infinity Cache (each model layer has its own cache).
@@ -90,10 +91,8 @@ def algorithmic_bytes():
         "index_score": c.B * (Nc * c.dI * 2 + c.HI * c.dI * 2 + c.HI * 4),
         "csa_attend": c.B * ((c.k + c.W) * row + c.H * c.D * 2 * 2 + c.k * 4),
         "hca_attend": h.B * ((Nh + h.W) * row + h.H * h.D * 2 * 2),
-        "csa_pool": c.B * (2 * c.m * (c.D * 2 + 4) + row),
-        "hca_pool": h.B * (2 * h.m * (h.D * 2 + 4) + row),
-        "csa_pack": c.B * (c.D * 2 + row),
-        "hca_pack": h.B * (h.D * 2 + row),
+        "csa_compress": c.B * (2 * c.m * (c.D * 2 + 4) + row + c.D * 2 + row),
+        "hca_compress": h.B * (2 * h.m * (h.D * 2 + 4) + row + h.D * 2 + row),
     }
     flops = {
         "index_score": c.B * 2 * c.HI * c.dI * Nc,
@@ -278,7 +277,7 @@ def fp8_indexer_section(dev, st, launches, reps):
     fn = dict(launches)
     fn["index_score"] = lambda: ops.index_score_fp8(q8, qs, a["w_idx"], k8, ks, n_entries=Nc,
                                                     q_pos0=tc, m=c.m, scores=st.scores)
-    names = ("csa_pack", "csa_pool", "index_score", "topk_select", "csa_attend")
+    names = ("csa_compress", "index_score", "topk_select", "csa_attend")
     csa = [(n, fn[n]) for n in names]
     for _ in range(3):
         for _, f in csa:
@@ -456,9 +455,9 @@ def main():
     log("breakdown (us): " + ", ".join(f"{k} {v:.1f}" for k, v in br.items()))
     abytes, aflops = algorithmic_bytes()
 
-    t_csa_us = sum(br[k] for k in ("csa_pack", "csa_pool", "index_score", "topk_select",
+    t_csa_us = sum(br[k] for k in ("csa_compress", "index_score", "topk_select",
                                    "csa_attend"))
-    t_hca_us = sum(br[k] for k in ("hca_pack", "hca_pool", "hca_attend"))
+    t_hca_us = sum(br[k] for k in ("hca_compress", "hca_attend"))
     kernels = {}
     for k, us in br.items():
         ent = {"us": round(us, 2)}
@@ -483,7 +482,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "step_schedule": "HIP graph replay, pack and pool on a second stream" if args.graph
+        "step_schedule": "HIP graph replay, the CSA compress step on a second stream" if args.graph
         else "calls launched one by one on one stream",
         "higher_is_better": True,
         "scaling": "weak",

@@ -103,6 +103,30 @@ int v4attn_compress(const uint16_t* raw, const float* tok_score,
                     uint8_t* out, int64_t out_rows, void* stream);
 
 /*
+ * v4attn_compress_step -- one decode step of the compressor, in one launch:
+ * the window row of the new token at position t (as V4ATTN_PACK) and, when
+ * t completes a group ((t+1) % m == 0), the compressed entry j = (t+1)/m - 1
+ * it completes (as V4ATTN_POOL).  Same definitions and bytes as the two
+ * v4attn_compress calls (the pooling over [(j-1)m, (j+1)m), RMSNorm, RoPE,
+ * packing: "Two ways to shrink attention, interleaved").
+ *
+ *   raw        bf16 [B, L, D]  positions raw_pos0 .. raw_pos0+L-1; must hold
+ *                              t and, for a completed entry, its window
+ *   tok_score  f32 [B, L], pos_bias f32 [2m]  (needed only for an entry)
+ *   gamma      f32 [D]
+ *   entries    u8 [B, ent_rows, D+R] out: entry j at row j (nullable when
+ *              no entry completes)
+ *   win        u8 [B, win_rows, D+R] out: the new token's row at win_row
+ * Errors: EINVAL for null/misaligned buffers, t outside the raw rows, a
+ * window that starts before raw_pos0, j >= ent_rows or win_row out of range.
+ */
+int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const float* pos_bias,
+                         const float* gamma, int B, int L, int D, int R, int64_t raw_pos0,
+                         int m, int64_t t, float eps, float rope_base, uint8_t* entries,
+                         int64_t ent_rows, uint8_t* win, int64_t win_rows, int64_t win_row,
+                         void* stream);
+
+/*
  * v4attn_index_topk -- lightning-indexer scores and top-k selection.
  *
  * Defines: a lightweight indexer scores each query against every compressed

@@ -191,6 +191,43 @@ int v4attn_compress(const uint16_t* raw, const float* tok_score, const float* po
   return hip_status(v4::launch_compress(a, (hipStream_t)stream), "compress launch");
 }
 
+int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const float* pos_bias,
+                         const float* gamma, int B, int L, int D, int R, int64_t raw_pos0, int m,
+                         int64_t t, float eps, float rope_base, uint8_t* entries,
+                         int64_t ent_rows, uint8_t* win, int64_t win_rows, int64_t win_row,
+                         void* stream) {
+  if (!raw || !gamma || !win) return fail(V4ATTN_EINVAL, "null raw, gamma or win");
+  if (B < 0 || L < 0 || ent_rows < 0 || win_rows < 0)
+    return fail(V4ATTN_EINVAL, "negative B, L, ent_rows or win_rows");
+  if (int st = check_dr(D, R)) return st;
+  if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
+  if (!(eps >= 0.f) || !std::isfinite(eps) || !(rope_base > 0.f))
+    return fail(V4ATTN_EINVAL, "bad eps or rope_base");
+  if (t < 0 || t < raw_pos0 || t >= raw_pos0 + L)
+    return fail(V4ATTN_EINVAL, "position %lld is not in the raw rows [%lld, %lld)", (long long)t,
+                (long long)raw_pos0, (long long)(raw_pos0 + L));
+  if (win_row < 0 || win_row >= win_rows)
+    return fail(V4ATTN_EINVAL, "win_row %lld outside [0, %lld)", (long long)win_row,
+                (long long)win_rows);
+  if (!aligned16(raw) || !aligned16(win)) return fail(V4ATTN_EINVAL, "raw and win must be 16-byte aligned");
+  if ((t + 1) % m == 0) {
+    const int64_t j = (t + 1) / m - 1;
+    const int64_t lo = (j - 1) * (int64_t)m;
+    const int64_t first = lo > 0 ? lo : 0;
+    if (!tok_score || !pos_bias || !entries)
+      return fail(V4ATTN_EINVAL, "a completed entry needs tok_score, pos_bias and entries");
+    if (!aligned16(entries)) return fail(V4ATTN_EINVAL, "entries must be 16-byte aligned");
+    if (j >= ent_rows)
+      return fail(V4ATTN_EINVAL, "entry %lld outside %lld entry rows", (long long)j, (long long)ent_rows);
+    if (first < raw_pos0)
+      return fail(V4ATTN_EINVAL, "entry %lld needs positions from %lld but rows start at %lld",
+                  (long long)j, (long long)first, (long long)raw_pos0);
+  }
+  v4::CompressStepArgs a{raw, tok_score, pos_bias, gamma, B, L, D, R, raw_pos0, m, t, eps,
+                         v4::rope_turns(rope_base, R), entries, ent_rows, win, win_rows, win_row};
+  return hip_status(v4::launch_compress_step(a, (hipStream_t)stream), "compress step launch");
+}
+
 size_t v4attn_index_topk_workspace(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m,
                                    int k) {
   if (B < 0 || Tq < 0 || n_entries < 0 || q_pos0 < 0 || m < 1 || k < 1) return 0;

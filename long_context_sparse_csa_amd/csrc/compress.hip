@@ -104,15 +104,14 @@ __device__ __forceinline__ void rmsnorm_wave(float (&y)[VPL], const float* __res
 constexpr int kPoolThreads = 1024;   // sixteen waves pool one entry's window
 constexpr int kPoolWaves = kPoolThreads / 64;
 
+// Entry j of sequence b, written to `row`: the whole 1024-thread workgroup.
 template <int VPL>
-__global__ __launch_bounds__(kPoolThreads) void compress_pool_kernel(
+__device__ __forceinline__ void pool_entry(
     const uint16_t* __restrict__ raw, const float* __restrict__ score,
     const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
-    int64_t raw_pos0, int m, int64_t entry0, float eps, const RopeTurns rope,
-    uint8_t* __restrict__ out, int64_t out_rows) {
+    int64_t raw_pos0, int m, int64_t j, int b, float eps, const RopeTurns& rope,
+    uint8_t* __restrict__ row) {
   constexpr int D = VPL * 64;
-  const int b = blockIdx.y;
-  const int64_t j = entry0 + blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float s_alpha[512];
   __shared__ float s_part[kPoolWaves][D];
@@ -198,8 +197,19 @@ __global__ __launch_bounds__(kPoolThreads) void compress_pool_kernel(
     y[v] = z * inv;
   }
   rmsnorm_wave<VPL>(y, gamma, lane, eps);
-  uint8_t* row = out + ((int64_t)b * out_rows + blockIdx.x) * (D + R);
   rotate_and_pack<VPL>(row, y, lane, R, j * (int64_t)m, rope);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(kPoolThreads) void compress_pool_kernel(
+    const uint16_t* __restrict__ raw, const float* __restrict__ score,
+    const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
+    int64_t raw_pos0, int m, int64_t entry0, float eps, const RopeTurns rope,
+    uint8_t* __restrict__ out, int64_t out_rows) {
+  constexpr int D = VPL * 64;
+  const int b = blockIdx.y;
+  pool_entry<VPL>(raw, score, bias, gamma, L, R, raw_pos0, m, entry0 + blockIdx.x, b, eps, rope,
+                  out + ((int64_t)b * out_rows + blockIdx.x) * (D + R));
 }
 
 // One wave per raw row: RMSNorm, RoPE at the row's own position, pack.
@@ -218,6 +228,49 @@ __global__ __launch_bounds__(256) void compress_pack_kernel(
   rmsnorm_wave<VPL>(y, gamma, lane, eps);
   uint8_t* row = out + ((int64_t)b * out_rows + r) * (D + R);
   rotate_and_pack<VPL>(row, y, lane, R, raw_pos0 + r, rope);
+}
+
+// One decode step of the compressor: block 0 of each sequence pools the entry
+// the new token completes (if any), the last block packs the token's window
+// row; both run side by side in one launch.
+template <int VPL>
+__global__ __launch_bounds__(kPoolThreads) void compress_step_kernel(
+    const uint16_t* __restrict__ raw, const float* __restrict__ score,
+    const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
+    int64_t raw_pos0, int m, int64_t t, float eps, const RopeTurns rope,
+    uint8_t* __restrict__ ent, int64_t ent_rows, uint8_t* __restrict__ win, int64_t win_rows,
+    int64_t win_row) {
+  constexpr int D = VPL * 64;
+  const int b = blockIdx.y;
+  if (blockIdx.x == gridDim.x - 1) {
+    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x;
+    float y[VPL];
+    load_bf16_row<VPL>(raw + ((int64_t)b * L + (t - raw_pos0)) * D + lane * VPL, y);
+    rmsnorm_wave<VPL>(y, gamma, lane, eps);
+    rotate_and_pack<VPL>(win + ((int64_t)b * win_rows + win_row) * (D + R), y, lane, R, t, rope);
+    return;
+  }
+  const int64_t j = (t + 1) / m - 1;
+  pool_entry<VPL>(raw, score, bias, gamma, L, R, raw_pos0, m, j, b, eps, rope,
+                  ent + ((int64_t)b * ent_rows + j) * (D + R));
+}
+
+hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  const bool pool = (a.t + 1) % a.m == 0;
+  dim3 grid(pool ? 2 : 1, a.B);
+#define V4_STEP(VPL)                                                                        \
+  compress_step_kernel<VPL><<<grid, kPoolThreads, 0, st>>>(                                 \
+      a.raw, a.tok_score, a.pos_bias, a.gamma, a.L, a.R, a.raw_pos0, a.m, a.t, a.eps, a.rope, \
+      a.ent, a.ent_rows, a.win, a.win_rows, a.win_row)
+  switch (a.D) {
+    case 128: V4_STEP(2); break;
+    case 256: V4_STEP(4); break;
+    default: V4_STEP(8); break;
+  }
+#undef V4_STEP
+  return hipGetLastError();
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {

@@ -27,6 +27,26 @@ struct CompressArgs {
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 
+// One decode step of the compressor: the window row of the token at t and,
+// when (t+1) % m == 0, the entry (t+1)/m - 1 it completes, in one launch.
+struct CompressStepArgs {
+  const uint16_t* raw;     // [B, L, D], positions raw_pos0 ..
+  const float* tok_score;  // [B, L]
+  const float* pos_bias;   // [2m]
+  const float* gamma;      // [D]
+  int B, L, D, R;
+  int64_t raw_pos0;
+  int m;
+  int64_t t;
+  float eps;
+  RopeTurns rope;
+  uint8_t* ent;            // [B, ent_rows, D+R], entry j at row j
+  int64_t ent_rows;
+  uint8_t* win;            // [B, win_rows, D+R]
+  int64_t win_rows, win_row;
+};
+hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st);
+
 // Lightning-indexer scoring into a dense fp32 score buffer.
 struct IndexScoreArgs {
   const uint16_t* q_idx;  // [B, Tq, HI, dI]

@@ -1,17 +1,15 @@
 """One decode step of a CSA layer and an HCA layer, as a runnable unit.
 
 Per decode token and sequence, a layer
-  * CSA (compression m, top-k k, window W): packs the new token's window row,
-    pools the compressed entry the token completes, scores every visible
-    entry with the lightning indexer, selects the top-k, and attends over
-    them plus the window;
-  * HCA (compression m'): packs, pools and attends over every entry plus
-    the window.
-Within a layer the window pack and the entry pool do not depend on the
-indexer (nor on each other), so `run_overlapped` puts them on a second
-stream beside the indexer (CSA) or beside each other (HCA); the attention
-waits for both.  `capture` records that schedule in a HIP graph, which
-removes the per-launch gaps of the dozen small and large kernels.
+  * CSA (compression m, top-k k, window W): packs the new token's window row
+    and pools the compressed entry the token completes (one fused compress
+    step), scores every visible entry with the lightning indexer, selects the
+    top-k, and attends over them plus the window;
+  * HCA (compression m'): the compress step, then attention over every entry
+    plus the window.
+Within the CSA layer the compress step does not depend on the indexer, so
+`run_overlapped` puts it on a second stream beside the indexer; the attention
+waits for both.  `capture` records that schedule in a HIP graph.
 
 Inputs are seeded synthetic tensors shaped like the workloads in configs.py
 (the random-number recipe is in synth.py).  The HCA caches can rotate over
@@ -60,8 +58,8 @@ def build_inputs(c, h, dev, rotate=1):
 class DecodeStep:
     """The library calls of one decode step over fixed buffers."""
 
-    NAMES = ("csa_pack", "csa_pool", "index_score", "topk_select", "csa_attend",
-             "hca_pack", "hca_pool", "hca_attend")
+    NAMES = ("csa_compress", "index_score", "topk_select", "csa_attend",
+             "hca_compress", "hca_attend")
 
     def __init__(self, inp, c, h, dev):
         self.inp, self.c, self.h = inp, c, h
@@ -91,11 +89,10 @@ class DecodeStep:
         Nc, Nh, tc, th = a["N"], b["N"], a["t"], b["t"]
         ent_h = b["entries"][rot % len(b["entries"])]
         return {
-            "csa_pack": lambda: ops.compress_pack(a["raw_last"], a["gamma"], a["win"], raw_pos0=tc,
-                                                  out_row0=c.W - 1),
-            "csa_pool": lambda: ops.compress_pool(a["raw"], a["score"], a["bias"], a["gamma"],
-                                                  a["entries"], raw_pos0=tc + 1 - 2 * c.m, m=c.m,
-                                                  entry0=Nc - 1, n_out=1, out_row0=Nc - 1),
+            "csa_compress": lambda: ops.compress_step(a["raw"], a["score"], a["bias"], a["gamma"],
+                                                      a["entries"], a["win"],
+                                                      raw_pos0=tc + 1 - 2 * c.m, m=c.m, t=tc,
+                                                      win_row=c.W - 1),
             "index_score": lambda: ops.index_score(a["q_idx"], a["w_idx"], a["k_idx"], n_entries=Nc,
                                                    q_pos0=tc, m=c.m, scores=self.scores),
             "topk_select": lambda: ops.topk_select(self.scores, B=c.B, Tq=1, n_entries=Nc,
@@ -104,11 +101,9 @@ class DecodeStep:
             "csa_attend": lambda: ops.csa_attend(a["q"], a["entries"], self.topk, a["win"],
                                                  a["gamma"], a["sink"], q_pos0=tc, W=c.W,
                                                  out=self.out_c, workspace=self.csa_ws),
-            "hca_pack": lambda: ops.compress_pack(b["raw_last"], b["gamma"], b["win"], raw_pos0=th,
-                                                  out_row0=h.W - 1),
-            "hca_pool": lambda: ops.compress_pool(b["raw"], b["score"], b["bias"], b["gamma"], ent_h,
-                                                  raw_pos0=th + 1 - 2 * h.m, m=h.m, entry0=Nh - 1,
-                                                  n_out=1, out_row0=Nh - 1),
+            "hca_compress": lambda: ops.compress_step(b["raw"], b["score"], b["bias"], b["gamma"],
+                                                      ent_h, b["win"], raw_pos0=th + 1 - 2 * h.m,
+                                                      m=h.m, t=th, win_row=h.W - 1),
             "hca_attend": lambda: ops.hca_attend(b["q"], ent_h, b["win"], b["gamma"], b["sink"],
                                                  n_entries=Nh, m=h.m, q_pos0=th, W=h.W,
                                                  out=self.out_h, workspace=self.hca_ws),
@@ -121,26 +116,20 @@ class DecodeStep:
             f[n]()
 
     def run_overlapped(self, rot=0):
-        """The step with each layer's pack and pool on a second stream."""
+        """The step with the CSA layer's compress step on a second stream,
+        beside the indexer and the top-k."""
         f = self.calls(rot)
         main, side, ev = torch.cuda.current_stream(), self.side, self.ev
         ev[0].record(main)
         side.wait_event(ev[0])
         with torch.cuda.stream(side):
-            f["csa_pack"]()
-            f["csa_pool"]()
+            f["csa_compress"]()
             ev[1].record(side)
         f["index_score"]()
         f["topk_select"]()
         main.wait_event(ev[1])
         f["csa_attend"]()
-        ev[2].record(main)
-        side.wait_event(ev[2])
-        with torch.cuda.stream(side):
-            f["hca_pack"]()
-            ev[3].record(side)
-        f["hca_pool"]()
-        main.wait_event(ev[3])
+        f["hca_compress"]()
         f["hca_attend"]()
 
     def capture(self, rot=0):

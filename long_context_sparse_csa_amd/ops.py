@@ -37,6 +37,8 @@ _SIGS = {
     "v4attn_last_error": (_c.c_char_p, []),
     "v4attn_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _I, _L, _I, _F, _F, _P, _L,
                              _P]),
+    "v4attn_compress_step": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _L, _F, _F, _P, _L, _P,
+                                  _L, _L, _P]),
     "v4attn_index_topk_workspace": (_Z, [_I, _I, _L, _L, _I, _I]),
     "v4attn_index_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _I, _P, _P, _P, _Z,
                                _P]),
@@ -149,6 +151,29 @@ def compress_pool(raw, tok_score, pos_bias, gamma, out, *, raw_pos0, m, entry0, 
                                 float(eps), float(rope_base), _row_ptr(out, out_row0, D + R),
                                 out.shape[1], _stream(raw)))
     return out
+
+
+def compress_step(raw, tok_score, pos_bias, gamma, entries, win, *, raw_pos0, m, t, win_row,
+                  eps=1e-6, rope_base=10000.0, R=64):
+    """One decode step of the compressor in one launch: the window row of the
+    token at position t -> win[b, win_row], and, when (t+1) % m == 0, the
+    entry j = (t+1)/m - 1 it completes -> entries[b, j]."""
+    _need(raw, "raw", torch.bfloat16, 3)
+    _need(tok_score, "tok_score", torch.float32, 2)
+    _need(pos_bias, "pos_bias", torch.float32, 1)
+    _need(gamma, "gamma", torch.float32, 1)
+    _need(entries, "entries", torch.uint8, 3)
+    _need(win, "win", torch.uint8, 3)
+    B, L, D = raw.shape
+    if tuple(tok_score.shape) != (B, L) or pos_bias.numel() != 2 * m or gamma.numel() != D \
+            or entries.shape[0] != B or entries.shape[2] != D + R or win.shape[0] != B \
+            or win.shape[2] != D + R:
+        raise ValueError("shape mismatch")
+    check(lib().v4attn_compress_step(_ptr(raw), _ptr(tok_score), _ptr(pos_bias), _ptr(gamma), B, L,
+                                     D, R, int(raw_pos0), int(m), int(t), float(eps),
+                                     float(rope_base), _ptr(entries), entries.shape[1], _ptr(win),
+                                     win.shape[1], int(win_row), _stream(raw)))
+    return entries, win
 
 
 def compress_pack(raw, gamma, out, *, raw_pos0, n_out=None, out_row0=0, eps=1e-6,

@@ -32,7 +32,7 @@ MISALIGNED = ctypes.c_void_p(0x100008)
 def test_exports_every_header_function():
     names = ops().header_functions()
     assert "v4attn_compress" in names and "v4attn_hca_attend" in names
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L(), n), n
     assert L().v4attn_version() == 1
@@ -69,6 +69,37 @@ def _compress(**kw):
 def test_compress_rejects(kw, status):
     assert _compress(**kw) == status
     assert L().v4attn_last_error() != b""
+
+
+def _step(**kw):
+    a = dict(raw=FAKE, s=FAKE, b=FAKE, g=FAKE, B=2, L=8, D=512, R=64, raw_pos0=100, m=4, t=107,
+             ent=FAKE, ent_rows=27, win=FAKE, win_rows=128, win_row=127)
+    a.update(kw)
+    return L().v4attn_compress_step(a["raw"], a["s"], a["b"], a["g"], a["B"], a["L"], a["D"],
+                                    a["R"], a["raw_pos0"], a["m"], a["t"], 1e-6, 1e4, a["ent"],
+                                    a["ent_rows"], a["win"], a["win_rows"], a["win_row"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(raw=None), -1),
+    (dict(win=None), -1),
+    (dict(t=108), -1),                 # t outside the raw rows [100, 108)
+    (dict(t=99), -1),
+    (dict(raw_pos0=101, L=7), -1),     # entry 26's window starts at 100 < raw_pos0
+    (dict(ent_rows=26), -1),           # entry 26 needs 27 rows
+    (dict(ent=None), -1),              # an entry completes at t = 107
+    (dict(win_row=128), -1),
+    (dict(m=0), -2),
+    (dict(D=384), -2),
+])
+def test_compress_step_rejects(kw, status):
+    assert _step(**kw) == status
+
+
+def test_compress_step_pack_only_needs_no_entry_buffers():
+    # t = 106 completes no group: scores, biases and entries may be null.  A
+    # bad win_row is rejected on the host before any launch.
+    assert _step(t=106, s=None, b=None, ent=None, win_row=-1) == -1
 
 
 def _index(**kw):

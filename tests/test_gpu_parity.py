@@ -116,6 +116,47 @@ def test_compress_pack_matches_oracle(D):
         assert_rows_within_one_ulp(out[bb].cpu().numpy(), e, D, R)
 
 
+@pytest.mark.parametrize("D,m,t", [(512, 4, (1 << 20) - 1), (512, 128, (1 << 20) - 1),
+                                   (512, 4, (1 << 20) - 2), (128, 4, 3), (256, 3, 2),
+                                   (512, 128, 127)])
+def test_compress_step_matches_pool_and_pack(D, m, t):
+    """The fused decode-step compressor writes the same bytes as a PACK call
+    for the token at t and, when t completes a group, a POOL call for the
+    entry it completes; both against the oracle too.  Includes entry 0 (no
+    previous group) and a step that completes no group."""
+    log(f"compress_step D={D} m={m} t={t}")
+    B, R, W = 2, 64, 128
+    raw_pos0 = max(0, t + 1 - 2 * m)
+    L = t + 1 - raw_pos0
+    raw, score, bias, gamma = _compress_inputs(B, L, D, m, 31 + D + m)
+    j = (t + 1) // m - 1
+    done = (t + 1) % m == 0
+    rows = j + 1 if done else 1
+    ent = torch.zeros((B, rows, D + R), dtype=torch.uint8, device=DEV)
+    win = torch.zeros((B, W, D + R), dtype=torch.uint8, device=DEV)
+    ops().compress_step(raw, score, bias, gamma, ent, win, raw_pos0=raw_pos0, m=m, t=t,
+                        win_row=W - 1)
+    ent2 = torch.zeros_like(ent)
+    win2 = torch.zeros_like(win)
+    ops().compress_pack(raw[:, L - 1:].contiguous(), gamma, win2, raw_pos0=t, out_row0=W - 1)
+    if done:
+        ops().compress_pool(raw, score, bias, gamma, ent2, raw_pos0=raw_pos0, m=m, entry0=j,
+                            n_out=1, out_row0=j)
+    torch.cuda.synchronize()
+    assert torch.equal(win, win2)
+    assert torch.equal(ent, ent2)   # all zero when no group completes
+    c = bf16_to_f64(raw)
+    gm = gamma.cpu().double().numpy()
+    for bb in range(B):
+        e = oc.compress_pack(c[bb, L - 1:], t, gm, 1e-6, R, 1e4)
+        assert_rows_within_one_ulp(win[bb, W - 1:].cpu().numpy(), e, D, R)
+        if done:
+            js, e = oc.compress_pool(c[bb], score[bb].cpu().double().numpy(), raw_pos0, m,
+                                     bias.cpu().double().numpy(), gm, 1e-6, R, 1e4, j0=j, n=1)
+            assert list(js) == [j]
+            assert_rows_within_one_ulp(ent[bb, j:j + 1].cpu().numpy(), e, D, R)
+
+
 def test_compress_rejects_missing_window_rows():
     B, D, m = 1, 128, 4
     raw, score, bias, gamma = _compress_inputs(B, 16, D, m, 3)
