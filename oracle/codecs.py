@@ -13,6 +13,14 @@ Everything is written from the format definitions:
   bf16: the upper 16 bits of an IEEE binary32, i.e. 8 exponent bits (bias
         127) and 7 fraction bits.
 
+The MXFP4 indexer (a next-row variant; [P5] "Two ways to shrink attention,
+interleaved": the indexer's attention runs in FP4) reads OCP MX FP4 data:
+blocks of 32 E2M1 elements sharing one E8M0 scale,
+  e2m1: value = (-1)^s * 2^(e-1) * (1 + m/2)   for e in 1..3
+        value = (-1)^s * (m/2)                 for e == 0   (4 bits: s e e m)
+  e8m0: scale = 2^(x-127) for x in 0..254 (x = 255 is NaN).
+Two E2M1 codes share a byte, the lower-indexed element in the low nibble.
+
 Packed row layout (D dims, last R rotary): bytes [0, D-R) hold E4M3 codes of
 dims 0..D-R-1; bytes [D-R, D+R) hold little-endian bf16 of dims D-R..D-1.
 """
@@ -64,6 +72,34 @@ def e4m3_encode(x):
     assert np.all(_POS_VALUES[idx] == r), "rounded value not on the E4M3 grid"
     code = idx.astype(np.uint8) | np.where(sign, 0x80, 0).astype(np.uint8)
     return np.where(nan, np.uint8(_E4M3_NAN), code).astype(np.uint8)
+
+
+def e2m1_decode(nibbles):
+    """4-bit E2M1 codes (ints 0..15) -> float64 values (exact)."""
+    c = np.asarray(nibbles).astype(np.int64)
+    sign = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    v = np.where(e == 0, m / 2.0, np.ldexp(1.0 + m / 2.0, e - 1))
+    return np.where(sign == 1, -v, v)
+
+
+def e8m0_decode(x):
+    """uint8 E8M0 scale codes -> float64 2^(x-127) (NaN for 255)."""
+    x = np.asarray(x, dtype=np.uint8).astype(np.int64)
+    return np.where(x == 255, np.nan, np.ldexp(1.0, x - 127))
+
+
+def mxfp4_decode(packed, scales):
+    """MXFP4 rows -> float64 [..., d]: packed uint8 [..., d/2] (element 2i in
+    the low nibble of byte i) and E8M0 scales uint8 [..., d/32], one per
+    block of 32 consecutive elements."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lo, hi = p & 0xF, p >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(*p.shape[:-1], 2 * p.shape[-1])
+    v = e2m1_decode(nib)
+    s = e8m0_decode(scales)
+    return v * np.repeat(s, 32, axis=-1)
 
 
 def bf16_decode(bits):

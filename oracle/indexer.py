@@ -16,6 +16,9 @@ Readings (the pages print no formula for the score):
     section: the indexer's attention runs at reduced precision): queries and
     keys are OCP E4M3FN codes with one positive scale per row (per query
     head, per key); the score is the score above of the dequantised rows;
+  * MXFP4 indexer ([P5] same section: the indexer's attention runs in FP4):
+    queries and keys in the OCP MX FP4 format (E2M1 elements, one E8M0 scale
+    per 32 consecutive dims); again the score of the dequantised rows;
   * top-k order is (score descending, index ascending): ties go to the lower
     entry index.  The first min(k, V_t) entries in that order form the set;
     it is returned in ascending index order, padded with -1 to length k.
@@ -25,7 +28,7 @@ Readings (the pages print no formula for the score):
 
 import numpy as np
 
-from .codecs import e4m3_decode
+from .codecs import e4m3_decode, mxfp4_decode
 
 
 def visible_entries(t, n_entries, m):
@@ -92,6 +95,31 @@ def index_topk_fp8(q8, q_scale, w, k8, k_scale, n_entries, q_pos, m, k):
     for r in range(Tq):
         V = visible_entries(int(q_pos[r]), n_entries, m)
         sc = index_scores_fp8(q8[r], q_scale[r], w[r], k8, k_scale, V)
+        topk[r] = topk_select(sc, k)
+        scores.append(sc)
+    return topk, scores
+
+
+def index_scores_mxfp4(q4, q_sc, w, k4, k_sc, V):
+    """MXFP4 indexer scores of one query against entries 0..V-1, float64 [V].
+
+    q4: uint8 [H_I, d_I/2] packed E2M1; q_sc: uint8 [H_I, d_I/32] E8M0;
+    w: [H_I]; k4: uint8 [>=V, d_I/2]; k_sc: uint8 [>=V, d_I/32]."""
+    q = mxfp4_decode(q4, q_sc)
+    k = mxfp4_decode(k4[:V], k_sc[:V])
+    return index_scores(q, w, k, V)
+
+
+def index_topk_mxfp4(q4, q_sc, w, k4, k_sc, n_entries, q_pos, m, k):
+    """index_topk for the MXFP4 indexer: q4 [Tq, H_I, d_I/2], q_sc
+    [Tq, H_I, d_I/32], w [Tq, H_I], k4 [>= n_entries, d_I/2], k_sc
+    [>= n_entries, d_I/32]."""
+    Tq = q4.shape[0]
+    topk = np.full((Tq, k), -1, dtype=np.int32)
+    scores = []
+    for r in range(Tq):
+        V = visible_entries(int(q_pos[r]), n_entries, m)
+        sc = index_scores_mxfp4(q4[r], q_sc[r], w[r], k4, k_sc, V)
         topk[r] = topk_select(sc, k)
         scores.append(sc)
     return topk, scores

@@ -103,3 +103,36 @@ def test_pack_unpack_roundtrip(D, R):
     # layout: bf16 little-endian after the D-R fp8 bytes
     lo_byte, hi_byte = rows[0, D - R], rows[0, D - R + 1]
     assert (int(hi_byte) << 8 | int(lo_byte)) == codecs.bf16_encode(v[0, D - R])
+
+
+# ---------------------------------------------------------------- MXFP4 --
+# The OCP Microscaling (MX) v1.0 element table for FP4 E2M1 (magnitudes of
+# codes 0..7; bit 3 is the sign) and the E8M0 scale (2^(x-127), 255 = NaN).
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_matches_the_element_table():
+    v = codecs.e2m1_decode(np.arange(16))
+    assert v[:8].tolist() == E2M1_TABLE
+    assert v[8:].tolist() == [-x for x in E2M1_TABLE]
+    assert np.signbit(v[8])          # code 8 is -0
+
+
+def test_e8m0_decode():
+    v = codecs.e8m0_decode(np.array([0, 1, 126, 127, 128, 254, 255], dtype=np.uint8))
+    assert v[:6].tolist() == [2.0 ** -127, 2.0 ** -126, 0.5, 1.0, 2.0, 2.0 ** 127]
+    assert np.isnan(v[6])
+
+
+def test_mxfp4_decode_nibble_order_and_block_scales():
+    # 64 elements: bytes 0..31; element 2i is the low nibble of byte i.
+    # Block 0 (elements 0..31) scaled by 2^1, block 1 (32..63) by 2^-2.
+    packed = np.zeros(32, dtype=np.uint8)
+    packed[0] = 0x72      # elements 0, 1 = 1.0, 6.0
+    packed[15] = 0xA3     # elements 30, 31 = 1.5, -1.0
+    packed[16] = 0x0D     # elements 32, 33 = -3.0, 0.0
+    got = codecs.mxfp4_decode(packed, np.array([128, 125], dtype=np.uint8))
+    want = np.zeros(64)
+    want[0], want[1], want[30], want[31] = 2.0, 12.0, 3.0, -2.0
+    want[32] = -0.75
+    assert np.array_equal(got, want)

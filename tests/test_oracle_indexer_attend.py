@@ -94,6 +94,41 @@ def test_index_scores_fp8_scales_are_per_row():
                        oi.index_scores_fp8(q8, qs, w2, k8, ks, N), rtol=1e-12, atol=0)
 
 
+# E2M1 codes of exact values (bit 3 is the sign)
+_E2M1 = {0.0: 0x0, 0.5: 0x1, 1.0: 0x2, 1.5: 0x3, 2.0: 0x4, 3.0: 0x5, 4.0: 0x6, 6.0: 0x7}
+
+
+def _pack_e2m1(vals):
+    c = np.array([_E2M1[abs(v)] | (8 if v < 0 else 0) for v in np.ravel(vals)], dtype=np.uint8)
+    c = c.reshape(*np.shape(vals))
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def test_index_scores_mxfp4_hand_example():
+    # d_I = 32 (one block).  q head 0 = 2^1 * [1, 2, 0...], head 1 = 2^0 * [-1, 0.5, 0...];
+    # keys (scale 2^-1): k0 = 0.5 * [3, 1, 0...] = [1.5, 0.5], k1 = 0.5 * [-4, 6] = [-2, 3]
+    # w = [1, 2]:  j=0: dots 2*1.5 + 4*0.5 = 5, -1.5 + 0.25 -> 0  => 5
+    #             j=1: -4 + 12 = 8, 2 + 1.5 = 3.5 => 8 + 7 = 15
+    q = np.zeros((2, 32)); q[0, :2] = [1.0, 2.0]; q[1, :2] = [-1.0, 0.5]
+    k = np.zeros((2, 32)); k[0, :2] = [3.0, 1.0]; k[1, :2] = [-4.0, 6.0]
+    got = oi.index_scores_mxfp4(_pack_e2m1(q), np.array([[128], [127]], dtype=np.uint8),
+                                np.array([1.0, 2.0]), _pack_e2m1(k),
+                                np.array([[126], [126]], dtype=np.uint8), 2)
+    assert got.tolist() == [5.0, 15.0]
+
+
+def test_index_scores_mxfp4_integer_codes_equal_integer_scores():
+    g = np.random.default_rng(5)
+    HI, dI, N = 4, 64, 30
+    vals = np.array([0.0, 1.0, -1.0, 2.0, -2.0, 3.0, -3.0, 4.0, -4.0, 6.0, -6.0])
+    q = g.choice(vals, (HI, dI))
+    k = g.choice(vals, (N, dI))
+    w = g.integers(-3, 4, HI).astype(np.float64)
+    got = oi.index_scores_mxfp4(_pack_e2m1(q), np.full((HI, 2), 127, np.uint8), w,
+                                _pack_e2m1(k), np.full((N, 2), 127, np.uint8), N)
+    assert np.array_equal(got, oi.index_scores(q, w, k, N))
+
+
 def test_visible_entries():
     assert oi.visible_entries(4095, 1024, 4) == 1024
     assert oi.visible_entries(4094, 1024, 4) == 1023
