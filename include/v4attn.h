@@ -220,6 +220,38 @@ int v4attn_index_topk_fp8(const uint8_t* q8, const float* q_scale, const float* 
                           size_t ws_bytes, void* stream);
 
 /*
+ * v4attn_index_score_mxfp4 / v4attn_index_topk_mxfp4 -- the lightning
+ * indexer with MXFP4 inputs.
+ *
+ * Defines: V4 runs the indexer's attention in FP4 ("DeepSeek-V4: Making a
+ * Million Tokens Affordable", section "Two ways to shrink attention,
+ * interleaved").  Queries and keys are in the OCP MX FP4 format: E2M1
+ * elements, two per byte (the lower-indexed one in the low nibble), one
+ * E8M0 scale byte (2^(x-127)) per 32 consecutive dims.  The score is the one
+ * of v4attn_index_topk on the dequantised rows, sum_h w_h ReLU(q_h . k_j),
+ * formed on the FP4 matrix cores (the MX blocks go in as stored; fp32
+ * accumulation).  Visibility, top-k rule and outputs as v4attn_index_topk.
+ *
+ *   q4    u8  [B, Tq, HI, dI/2]   packed E2M1 queries (16-byte aligned)
+ *   q_sc  u8  [B, Tq, HI, dI/32]  E8M0 scales of the queries
+ *   w_idx f32 [B, Tq, HI]         per-query head weights
+ *   k4    u8  [B, Ncap, dI/2]     packed E2M1 keys (16-byte aligned)
+ *   k_sc  u8  [B, Ncap, dI/32]    E8M0 scales of the keys (dI/32-byte aligned)
+ *   dI in {64, 128}; HI <= 64.  Scale byte 255 (NaN) gives unspecified
+ *   scores.  The workspace of v4attn_index_topk_mxfp4 is
+ *   v4attn_index_topk_workspace(...) bytes; contents on entry are ignored.
+ */
+int v4attn_index_score_mxfp4(const uint8_t* q4, const uint8_t* q_sc, const float* w_idx,
+                             const uint8_t* k4, const uint8_t* k_sc, int B, int Tq, int HI,
+                             int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m,
+                             float* scores, int64_t score_stride, void* stream);
+int v4attn_index_topk_mxfp4(const uint8_t* q4, const uint8_t* q_sc, const float* w_idx,
+                            const uint8_t* k4, const uint8_t* k_sc, int B, int Tq, int HI,
+                            int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m,
+                            int k, int32_t* topk, float* topk_score, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
  * v4attn_csa_attend -- CSA core attention: shared-KV multi-query attention
  * over the selected entries plus the uncompressed window, with sink.
  *

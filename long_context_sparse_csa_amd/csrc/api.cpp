@@ -341,6 +341,32 @@ hipError_t run_score_fp8(const uint8_t* q8, const float* q_scale, const float* w
   return v4::launch_index_score_fp8(ia, st);
 }
 
+int check_score_mxfp4_args(const uint8_t* q4, const uint8_t* q_sc, const float* w_idx,
+                           const uint8_t* k4, const uint8_t* k_sc, int B, int Tq, int HI, int dI,
+                           int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m) {
+  if (!q4 || !q_sc || !w_idx) return fail(V4ATTN_EINVAL, "null q4, q_sc or w_idx");
+  if (int st = check_index_common(B, Tq, n_entries, q_pos0, m)) return st;
+  if (HI < 1 || HI > 64) return fail(V4ATTN_EUNSUPPORTED, "HI = %d: 1 <= HI <= 64 is built", HI);
+  if (dI != 64 && dI != 128)
+    return fail(V4ATTN_EUNSUPPORTED, "dI = %d: the MXFP4 indexer builds dI in {64, 128}", dI);
+  if (Ncap < 0 || n_entries > Ncap) return fail(V4ATTN_EINVAL, "need 0 <= n_entries <= Ncap");
+  if (n_entries > 0 && (!k4 || !k_sc)) return fail(V4ATTN_EINVAL, "null k4 or k_sc");
+  if (!aligned16(q4) || !aligned16(k4)) return fail(V4ATTN_EINVAL, "q4 and k4 must be 16-byte aligned");
+  if (((uintptr_t)k_sc) % (dI / 32) != 0)
+    return fail(V4ATTN_EINVAL, "k_sc must be %d-byte aligned", dI / 32);
+  return V4ATTN_OK;
+}
+
+hipError_t run_score_mxfp4(const uint8_t* q4, const uint8_t* q_sc, const float* w_idx,
+                           const uint8_t* k4, const uint8_t* k_sc, int B, int Tq, int HI, int dI,
+                           int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m, float* scores,
+                           int64_t stride, hipStream_t st) {
+  const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
+  v4::IndexScoreMxfp4Args ia{q4, q_sc, w_idx, k4, k_sc, B, Tq, HI, dI, Ncap, n_entries,
+                             q_pos0, m, vmax, scores, stride, v4::index_mxfp4_row_waves(B, Tq, vmax)};
+  return v4::launch_index_score_mxfp4(ia, st);
+}
+
 }  // namespace
 
 int v4attn_index_score(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx, int B,
@@ -441,6 +467,49 @@ int v4attn_index_topk_fp8(const uint8_t* q8, const float* q_scale, const float* 
   hipError_t e = run_score_fp8(q8, q_scale, w_idx, k8, k_scale, B, Tq, HI, dI, Ncap, n_entries,
                                q_pos0, m, scores, w.score_stride, st);
   if (e != hipSuccess) return hip_status(e, "FP8 index score launch");
+  return hip_status(run_topk(scores, w.score_stride, B, Tq, n_entries, q_pos0, m, k, topk,
+                             topk_score, base + w.scores_bytes, w.tk, st),
+                    "top-k launch");
+}
+
+int v4attn_index_score_mxfp4(const uint8_t* q4, const uint8_t* q_sc, const float* w_idx,
+                             const uint8_t* k4, const uint8_t* k_sc, int B, int Tq, int HI,
+                             int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m,
+                             float* scores, int64_t score_stride, void* stream) {
+  if (int st = check_score_mxfp4_args(q4, q_sc, w_idx, k4, k_sc, B, Tq, HI, dI, Ncap, n_entries,
+                                      q_pos0, m))
+    return st;
+  const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
+  if (vmax > 0 && (!scores || score_stride < vmax))
+    return fail(V4ATTN_EINVAL, "scores missing or score_stride %lld < %lld",
+                (long long)score_stride, (long long)vmax);
+  return hip_status(run_score_mxfp4(q4, q_sc, w_idx, k4, k_sc, B, Tq, HI, dI, Ncap, n_entries,
+                                    q_pos0, m, scores, score_stride, (hipStream_t)stream),
+                    "MXFP4 index score launch");
+}
+
+int v4attn_index_topk_mxfp4(const uint8_t* q4, const uint8_t* q_sc, const float* w_idx,
+                            const uint8_t* k4, const uint8_t* k_sc, int B, int Tq, int HI, int dI,
+                            int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m, int k,
+                            int32_t* topk, float* topk_score, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (int st = check_score_mxfp4_args(q4, q_sc, w_idx, k4, k_sc, B, Tq, HI, dI, Ncap, n_entries,
+                                      q_pos0, m))
+    return st;
+  if (!topk) return fail(V4ATTN_EINVAL, "null topk");
+  if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
+  if (int st = check_topk_len(Tq, n_entries, q_pos0, m)) return st;
+  const IndexWs w = index_ws(B, Tq, n_entries, q_pos0, m, k);
+  if (w.total > 0 && (!ws || ws_bytes < w.total))
+    return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
+  if ((int64_t)B * Tq == 0) return hip_status(hipSuccess, "");
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* scores = reinterpret_cast<float*>(base);
+  hipError_t e = run_score_mxfp4(q4, q_sc, w_idx, k4, k_sc, B, Tq, HI, dI, Ncap, n_entries,
+                                 q_pos0, m, scores, w.score_stride, st);
+  if (e != hipSuccess) return hip_status(e, "MXFP4 index score launch");
   return hip_status(run_topk(scores, w.score_stride, B, Tq, n_entries, q_pos0, m, k, topk,
                              topk_score, base + w.scores_bytes, w.tk, st),
                     "top-k launch");

@@ -83,6 +83,25 @@ struct IndexScoreFp8Args {
 int64_t index_fp8_row_waves(int B, int Tq, int64_t vmax);
 hipError_t launch_index_score_fp8(const IndexScoreFp8Args& a, hipStream_t st);
 
+// MXFP4 lightning-indexer scoring: q and k as OCP MX FP4 rows (packed E2M1
+// codes, one E8M0 scale byte per 32 dims); same score buffer.
+struct IndexScoreMxfp4Args {
+  const uint8_t* q4;       // [B, Tq, HI, dI/2]
+  const uint8_t* q_sc;     // [B, Tq, HI, dI/32]
+  const float* w_idx;      // [B, Tq, HI]
+  const uint8_t* k4;       // [B, Ncap, dI/2]
+  const uint8_t* k_sc;     // [B, Ncap, dI/32]
+  int B, Tq, HI, dI;
+  int64_t Ncap, n_entries, q_pos0;
+  int m;
+  int64_t vmax;
+  float* scores;
+  int64_t score_stride;
+  int64_t row_waves;
+};
+int64_t index_mxfp4_row_waves(int B, int Tq, int64_t vmax);
+hipError_t launch_index_score_mxfp4(const IndexScoreMxfp4Args& a, hipStream_t st);
+
 // Top-k selection: per-part leaders -> exact per-row select.
 constexpr int kTopkSel = 16384;     // keys the per-row selection holds in LDS
 constexpr int kTopkPartLen = 1024;  // scores per part

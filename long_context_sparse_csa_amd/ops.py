@@ -47,6 +47,10 @@ _SIGS = {
                                     _P]),
     "v4attn_index_topk_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _I, _P,
                                    _P, _P, _Z, _P]),
+    "v4attn_index_score_mxfp4": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _P,
+                                      _L, _P]),
+    "v4attn_index_topk_mxfp4": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _I, _P,
+                                     _P, _P, _Z, _P]),
     "v4attn_topk_select_workspace": (_Z, [_I, _I, _L, _L, _I, _I]),
     "v4attn_topk_select": (_I, [_P, _L, _I, _I, _L, _L, _I, _I, _P, _P, _P, _Z, _P]),
     "v4attn_csa_attend_workspace": (_Z, [_I, _I, _I, _I, _I, _I]),
@@ -292,6 +296,54 @@ def index_topk_fp8(q8, q_scale, w_idx, k8, k_scale, *, n_entries, q_pos0, m, k, 
                                       _ptr(k_scale), B, Tq, HI, dI, Ncap, int(n_entries),
                                       int(q_pos0), int(m), int(k), _ptr(topk), _ptr(topk_score),
                                       _ptr(workspace), nbytes, _stream(q8)))
+    return topk, topk_score
+
+
+def _mxfp4_inputs(q4, q_sc, w_idx, k4, k_sc):
+    _need(q4, "q4", torch.uint8, 4)
+    _need(q_sc, "q_sc", torch.uint8, 4)
+    _need(w_idx, "w_idx", torch.float32, 3)
+    _need(k4, "k4", torch.uint8, 3)
+    _need(k_sc, "k_sc", torch.uint8, 3)
+    B, Tq, HI, half = q4.shape
+    dI = 2 * half
+    if tuple(q_sc.shape) != (B, Tq, HI, dI // 32) or tuple(w_idx.shape) != (B, Tq, HI) \
+            or k4.shape[0] != B or k4.shape[2] != half \
+            or tuple(k_sc.shape) != (B, k4.shape[1], dI // 32):
+        raise ValueError("shape mismatch")
+    return B, Tq, HI, dI, k4.shape[1]
+
+
+def index_score_mxfp4(q4, q_sc, w_idx, k4, k_sc, *, n_entries, q_pos0, m, scores=None):
+    """MXFP4 indexer scores f32 [B*Tq, stride] from packed E2M1 codes (uint8,
+    two per byte) and E8M0 block scales (uint8, one per 32 dims)."""
+    B, Tq, HI, dI, Ncap = _mxfp4_inputs(q4, q_sc, w_idx, k4, k_sc)
+    if scores is None:
+        scores = torch.empty((B * Tq, max(score_stride(Tq, n_entries, q_pos0, m), 1)),
+                             dtype=torch.float32, device=q4.device)
+    _need(scores, "scores", torch.float32, 2)
+    check(lib().v4attn_index_score_mxfp4(_ptr(q4), _ptr(q_sc), _ptr(w_idx), _ptr(k4), _ptr(k_sc),
+                                         B, Tq, HI, dI, Ncap, int(n_entries), int(q_pos0), int(m),
+                                         _ptr(scores), scores.shape[1], _stream(q4)))
+    return scores
+
+
+def index_topk_mxfp4(q4, q_sc, w_idx, k4, k_sc, *, n_entries, q_pos0, m, k, topk=None,
+                     topk_score=None, want_scores=False, workspace=None):
+    """Top-k entry indices per query from the MXFP4 indexer (int32 [B, Tq, k])."""
+    B, Tq, HI, dI, Ncap = _mxfp4_inputs(q4, q_sc, w_idx, k4, k_sc)
+    dev = q4.device
+    if topk is None:
+        topk = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
+    _need(topk, "topk", torch.int32, 3)
+    if want_scores and topk_score is None:
+        topk_score = torch.empty((B, Tq, k), dtype=torch.float32, device=dev)
+    nbytes = index_topk_workspace_bytes(B, Tq, n_entries, q_pos0, m, k)
+    workspace = _workspace(nbytes, dev, workspace)
+    check(lib().v4attn_index_topk_mxfp4(_ptr(q4), _ptr(q_sc), _ptr(w_idx), _ptr(k4), _ptr(k_sc),
+                                        B, Tq, HI, dI, Ncap, int(n_entries), int(q_pos0), int(m),
+                                        int(k), _ptr(topk), _ptr(topk_score), _ptr(workspace),
+                                        nbytes, _stream(q4)))
     return topk, topk_score
 
 

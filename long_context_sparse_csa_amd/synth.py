@@ -74,6 +74,48 @@ def e4m3_rows(shape, seed, name, device="cpu", chunk_rows=1 << 20):
     return codes.view(*shape), scales.view(*shape[:-1])
 
 
+def mxfp4_codes(shape, d, seed, name, device="cpu", scale_lo=120, scale_hi=134):
+    """Uniform random MXFP4 rows: packed E2M1 codes uint8 [*shape, d/2] (every
+    nibble is a valid code) and E8M0 scales uint8 [*shape, d/32] uniform in
+    [scale_lo, scale_hi]."""
+    g = _gen(seed, name, device)
+    codes = torch.randint(0, 256, (*shape, d // 2), generator=g, device=device).to(torch.uint8)
+    scales = torch.randint(scale_lo, scale_hi + 1, (*shape, d // 32), generator=g,
+                           device=device).to(torch.uint8)
+    return codes, scales
+
+
+def mxfp4_rows(shape, seed, name, device="cpu", chunk_rows=1 << 18):
+    """N(0,1) rows [*shape] (last dim d) in the OCP MX FP4 format: per block of
+    32 values the E8M0 scale 2^(floor(log2(amax)) - 2) (the largest magnitude
+    lands in [4, 8) and saturates at 6), elements rounded half-to-even onto
+    the E2M1 grid.  Returns packed codes uint8 [..., d/2] and scales uint8
+    [..., d/32]."""
+    d = shape[-1]
+    rows = 1
+    for s_ in shape[:-1]:
+        rows *= s_
+    codes = torch.empty((rows, d // 2), dtype=torch.uint8, device=device)
+    scales = torch.empty((rows, d // 32), dtype=torch.uint8, device=device)
+    g = _gen(seed, name, device)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        v = torch.randn((r1 - r0, d // 32, 32), generator=g, device=device)
+        amax = v.abs().amax(dim=2).clamp_min(2.0 ** -100)
+        x = torch.floor(torch.log2(amax)) - 2.0
+        a = (v.abs() / torch.exp2(x)[..., None]).clamp_max(6.0)
+        q = torch.where(a < 2.0, torch.round(a * 2.0) / 2.0,
+                        torch.where(a < 4.0, torch.round(a), torch.round(a / 2.0) * 2.0))
+        q = q.clamp_max(6.0)
+        # magnitude -> code: 0, .5, 1, 1.5 -> 0..3; 2, 3 -> 4, 5; 4, 6 -> 6, 7
+        mag = torch.where(q < 2.0, q * 2.0, torch.where(q < 4.0, q + 2.0, q / 2.0 + 4.0))
+        c = mag.to(torch.int32) | ((v < 0) & (mag > 0)).to(torch.int32) * 8
+        c = c.view(r1 - r0, d)
+        codes[r0:r1] = (c[:, 0::2] | (c[:, 1::2] << 4)).to(torch.uint8)
+        scales[r0:r1] = (x + 127.0).to(torch.uint8)
+    return codes.view(*shape[:-1], d // 2), scales.view(*shape[:-1], d // 32)
+
+
 def pack_values(vals, R):
     """float32 [..., D] -> uint8 [..., D+R]: E4M3FN codes of dims [0, D-R)
     followed by little-endian bf16 of dims [D-R, D) (torch casts)."""

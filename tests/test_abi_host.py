@@ -32,7 +32,7 @@ MISALIGNED = ctypes.c_void_p(0x100008)
 def test_exports_every_header_function():
     names = ops().header_functions()
     assert "v4attn_compress" in names and "v4attn_hca_attend" in names
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(L(), n), n
     assert L().v4attn_version() == 1
@@ -155,6 +155,30 @@ def test_index_score_fp8_rejects_short_stride():
     st = L().v4attn_index_score_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 128, 1000, 1000,
                                     3999, 4, FAKE, 999, None)
     assert st == -1
+
+
+def _index_mxfp4(**kw):
+    a = dict(q=FAKE, qs=FAKE, w=FAKE, k=FAKE, ks=FAKE, B=2, Tq=1, HI=64, dI=128, Ncap=1000,
+             n=1000, q_pos0=3999, m=4, k_=64, topk=FAKE, ts=None, ws=FAKE, ws_bytes=0)
+    a.update(kw)
+    return L().v4attn_index_topk_mxfp4(a["q"], a["qs"], a["w"], a["k"], a["ks"], a["B"], a["Tq"],
+                                       a["HI"], a["dI"], a["Ncap"], a["n"], a["q_pos0"], a["m"],
+                                       a["k_"], a["topk"], a["ts"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1),
+    (dict(qs=None), -1),
+    (dict(ks=None), -1),
+    (dict(k=MISALIGNED), -1),
+    (dict(ks=ctypes.c_void_p(0x100002)), -1),   # 4 scale bytes per key: 4-byte aligned
+    (dict(HI=65), -2),
+    (dict(dI=32), -2),
+    (dict(n=1001), -1),
+    (dict(ws_bytes=10), -3),
+])
+def test_index_topk_mxfp4_rejects(kw, status):
+    assert _index_mxfp4(**kw) == status
 
 
 def test_workspace_sizes_are_host_arithmetic():
