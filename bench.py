@@ -19,9 +19,10 @@ float64 oracle timed on the host cores on a bounded sample.
 
 A "prefill" section times the 4096-token chunk appended to a 2^20-token
 context (both layers) and reports MFMA fractions for scoring and attention.
-An "fp8_indexer" section runs the same CSA decode layer and prefill indexer
-with the FP8 (E4M3, one scale per row) lightning indexer; the headline value
-keeps the bf16 indexer keys of the workload definition.
+"fp8_indexer" and "mxfp4_indexer" sections run the same CSA decode layer and
+prefill indexer with the FP8 (E4M3, one scale per row) and MXFP4 lightning
+indexers; the headline value keeps the bf16 indexer keys of the workload
+definition.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
                     [--no-fp8] [--prefill-only] [--graph] [--counters]
@@ -38,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak, published
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4/FP6 matrix peak, published
 COPY_BYTES = 1 << 30           # calibration copy for the HBM byte counters
 
 # HBM bytes of one index_score launch at the decode shape, from two
@@ -261,22 +263,32 @@ def prefill_section(dev, reps):
     }
 
 
-def fp8_indexer_section(dev, st, launches, reps):
-    """The FP8 lightning indexer (E4M3 queries and keys, one scale per row)
-    on the same workloads: the decode CSA layer with index_score_fp8 in place
-    of the bf16 indexer (8 x 262,144 entries), and the 4096-query prefill
-    indexer + top-k over ~263K entries.  Inputs: N(0,1) rows quantised with
-    one scale per row (synth.e4m3_rows)."""
+def low_precision_indexer_section(dev, st, launches, reps, fmt):
+    """The lightning indexer with FP8 (E4M3, one fp32 scale per row) or MXFP4
+    (E2M1 with an E8M0 scale per 32 dims) queries and keys, on the same
+    workloads: the decode CSA layer with it in place of the bf16 indexer
+    (8 x 262,144 entries), and the 4096-query prefill indexer + top-k over
+    ~263K entries.  Inputs: N(0,1) rows quantised by synth.e4m3_rows /
+    synth.mxfp4_rows."""
     import torch
     from long_context_sparse_csa_amd import ops, synth
     from long_context_sparse_csa_amd.configs import CSA_1M as c, PREFILL_1M as p
+    fp8 = fmt == "fp8"
     a = st.inp["csa"]
     Nc, tc = a["N"], a["t"]
-    q8, qs = synth.e4m3_rows((c.B, 1, c.HI, c.dI), c.seed, "q8", dev)
-    k8, ks = synth.e4m3_rows((c.B, Nc, c.dI), c.seed, "k8", dev, chunk_rows=1 << 18)
+    if fp8:
+        q, qs = synth.e4m3_rows((c.B, 1, c.HI, c.dI), c.seed, "q8", dev)
+        kk, ks = synth.e4m3_rows((c.B, Nc, c.dI), c.seed, "k8", dev, chunk_rows=1 << 18)
+        score, topk_fn, peak = ops.index_score_fp8, ops.index_topk_fp8, FP8_PEAK_TFLOPS
+        key_bytes = c.dI + 4
+    else:
+        q, qs = synth.mxfp4_rows((c.B, 1, c.HI, c.dI), c.seed, "q4", dev)
+        kk, ks = synth.mxfp4_rows((c.B, Nc, c.dI), c.seed, "k4", dev)
+        score, topk_fn, peak = ops.index_score_mxfp4, ops.index_topk_mxfp4, FP4_PEAK_TFLOPS
+        key_bytes = c.dI // 2 + c.dI // 32
     fn = dict(launches)
-    fn["index_score"] = lambda: ops.index_score_fp8(q8, qs, a["w_idx"], k8, ks, n_entries=Nc,
-                                                    q_pos0=tc, m=c.m, scores=st.scores)
+    fn["index_score"] = lambda: score(q, qs, a["w_idx"], kk, ks, n_entries=Nc, q_pos0=tc, m=c.m,
+                                      scores=st.scores)
     names = ("csa_compress", "index_score", "topk_select", "csa_attend")
     csa = [(n, fn[n]) for n in names]
     for _ in range(3):
@@ -284,27 +296,31 @@ def fp8_indexer_section(dev, st, launches, reps):
             f()
     br = run_breakdown(csa, 20)
     t_layer = sum(br.values())
-    idx_bytes = c.B * Nc * (c.dI + 4) + c.B * c.HI * (c.dI + 8)
+    idx_bytes = c.B * Nc * key_bytes + q.numel() + qs.numel() * qs.element_size() + c.B * c.HI * 4
     dec = {
-        "index_score_fp8_us": round(br["index_score"], 2),
-        "index_score_fp8_GBps": round(idx_bytes / (br["index_score"] * 1e-6) / 1e9, 1),
-        "index_score_fp8_hbm_frac": round(idx_bytes / (br["index_score"] * 1e-6) / 1e9 /
-                                          HBM_PEAK_GBS, 4),
+        "index_score_us": round(br["index_score"], 2),
+        "index_score_GBps": round(idx_bytes / (br["index_score"] * 1e-6) / 1e9, 1),
+        "index_score_hbm_frac": round(idx_bytes / (br["index_score"] * 1e-6) / 1e9 /
+                                      HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_launch": idx_bytes,
         "csa_layer_us": round(t_layer, 2),
         "csa_query_tokens_per_s": round(c.B / (t_layer * 1e-6), 1),
     }
-    del k8, ks
+    del kk, ks
     P, Tq, HI, dI, k = p.T, p.Tq, p.HI, p.dI, p.k
     Np = P // p.m + Tq // p.m
-    pq8, pqs = synth.e4m3_rows((1, Tq, HI, dI), p.seed, "q8", dev)
-    pk8, pks = synth.e4m3_rows((1, Np, dI), p.seed, "k8", dev)
+    if fp8:
+        pq, pqs = synth.e4m3_rows((1, Tq, HI, dI), p.seed, "q8", dev)
+        pk, pks = synth.e4m3_rows((1, Np, dI), p.seed, "k8", dev)
+    else:
+        pq, pqs = synth.mxfp4_rows((1, Tq, HI, dI), p.seed, "q4", dev)
+        pk, pks = synth.mxfp4_rows((1, Np, dI), p.seed, "k4", dev)
     pw = synth.normal((1, Tq, HI), p.seed, "w", dev)
     topk = torch.empty((1, Tq, k), dtype=torch.int32, device=dev)
     ws = torch.empty(ops.index_topk_workspace_bytes(1, Tq, Np, P, p.m, k), dtype=torch.uint8,
                      device=dev)
-    call = lambda: ops.index_topk_fp8(pq8, pqs, pw, pk8, pks, n_entries=Np, q_pos0=P, m=p.m, k=k,
-                                      topk=topk, workspace=ws)
+    call = lambda: topk_fn(pq, pqs, pw, pk, pks, n_entries=Np, q_pos0=P, m=p.m, k=k, topk=topk,
+                           workspace=ws)
     call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -317,14 +333,15 @@ def fp8_indexer_section(dev, st, launches, reps):
     vis = sum(min(Np, (P + r + 1) // p.m) for r in range(Tq))
     tf = 2 * HI * dI * vis / (ms * 1e-3) / 1e12
     return {
-        "workload": "indexer keys and queries E4M3 with one fp32 scale per row; decode: the "
-                    "CSA layer of decode_1m_csa_hca with the FP8 indexer; prefill: "
+        "workload": ("indexer keys and queries E4M3 with one fp32 scale per row" if fp8 else
+                     "indexer keys and queries MXFP4 (E2M1, E8M0 scale per 32 dims)") +
+                    "; decode: the CSA layer of decode_1m_csa_hca with this indexer; prefill: "
                     "prefill_4096_on_1m indexer + top-k",
         "decode": dec,
         "prefill_index_topk_ms": round(ms, 3),
         "prefill_index_topk_TFLOPs": round(tf, 1),
-        "prefill_index_topk_mfma_frac_fp8": round(tf / FP8_PEAK_TFLOPS, 4),
-        "fp8_peak_TFLOPs": FP8_PEAK_TFLOPS,
+        "prefill_index_topk_mfma_frac": round(tf / peak, 4),
+        "mfma_peak_TFLOPs": peak,
     }
 
 
@@ -407,7 +424,7 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill chunk (prints its section as the JSON line)")
     ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the FP8-indexer section")
+                    help="skip the FP8 and MXFP4 indexer sections")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 4096-token prefill section")
     ap.add_argument("--counters", action="store_true",
@@ -514,10 +531,12 @@ def main():
         res["prefill"] = prefill_section(dev, 3)
         log("prefill (ms): " + ", ".join(f"{k} {v}" for k, v in res["prefill"]["ms"].items()))
     if not args.no_fp8:
-        log("fp8 indexer")
-        res["fp8_indexer"] = fp8_indexer_section(dev, st, launches, 3)
-        log("fp8 indexer: " + json.dumps(res["fp8_indexer"]["decode"]) +
-            f", prefill index_topk {res['fp8_indexer']['prefill_index_topk_ms']} ms")
+        for fmt in ("fp8", "mxfp4"):
+            log(f"{fmt} indexer")
+            sec = low_precision_indexer_section(dev, st, launches, 3, fmt)
+            res[f"{fmt}_indexer"] = sec
+            log(f"{fmt} indexer: " + json.dumps(sec["decode"]) +
+                f", prefill index_topk {sec['prefill_index_topk_ms']} ms")
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle)")
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
