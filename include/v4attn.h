@@ -272,7 +272,7 @@ int v4attn_index_topk_mxfp4(const uint8_t* q4, const uint8_t* q_sc, const float*
  *   win     u8   [B, Tq+W-1, D+R]   packed window rows; row r is position
  *                                   q_pos0-(W-1)+r.  The query at t uses
  *                                   positions max(0, t-W+1)..t.
- *   gamma_q f32 [D];  sink f32 [H]
+ *   gamma_q f32 [D] (16-byte aligned);  sink f32 [H]
  *   out     bf16 [B, Tq, H, D] out;  lse f32 [B, Tq, H] out, nullable
  *   ws / ws_bytes  >= v4attn_csa_attend_workspace(...) bytes (split
  *              partials of long rows; 0 is possible); contents on entry are

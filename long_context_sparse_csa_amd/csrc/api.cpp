@@ -132,8 +132,9 @@ int check_attend_common(const uint16_t* q, const uint8_t* entries, const uint8_t
   if (Ncap > 0 && !entries) return fail(V4ATTN_EINVAL, "null entries with Ncap > 0");
   if (!std::isfinite(scale) || !(eps >= 0.f) || !std::isfinite(eps) || !(rope_base > 0.f))
     return fail(V4ATTN_EINVAL, "bad scale, eps or rope_base");
-  if (!aligned16(q) || !aligned16(entries) || !aligned16(win) || !aligned16(out))
-    return fail(V4ATTN_EINVAL, "q, entries, win and out must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(entries) || !aligned16(win) || !aligned16(out) ||
+      !aligned16(gamma_q))
+    return fail(V4ATTN_EINVAL, "q, entries, win, gamma_q and out must be 16-byte aligned");
   return V4ATTN_OK;
 }
 

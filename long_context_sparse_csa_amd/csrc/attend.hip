@@ -142,6 +142,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
   __shared__ float s_cs[R / 2][2];
   __shared__ int s_sel[CSA ? kSelCap : 1];  // this split's slice of the top-k list
   __shared__ __attribute__((aligned(16))) uint8_t s_zero[32];   // K bytes past the E4M3 dims
+  __shared__ __attribute__((aligned(16))) float s_gamma[D];      // gamma_q, read per q~ slot
 
   const RowSpace rs = row_space(a, CSA, t);
   const int64_t chunk = split_chunk(rs.n_rows, a.splits);
@@ -157,7 +158,24 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
                                   (rs.win_lo - (a.q_pos0 - (a.W - 1)))) * ROW;
   const int win_first = (int)(rs.n_ent - row_beg);   // split-local row of the first window row
 
-  // q first, so that its loads are not queued behind the first tile's copies
+  // The loads the first barrier waits for go out first (a wave's vector loads
+  // complete in order): this split's slice of the top-k list (CSA), the
+  // rotary frequency and gamma_q.  Then q, before the first tile's copies,
+  // so that its loads are not queued behind them; they stay in flight across
+  // the barrier.
+  constexpr int SELR = CSA ? kSelCap / kAttThreads : 1;
+  int selv[SELR];
+  if constexpr (CSA) {
+    const int32_t* sel = a.topk + (int64_t)qr * a.k + row_beg;
+#pragma unroll
+    for (int i = 0; i < SELR; ++i) {
+      const int x = tid + i * kAttThreads;
+      selv[i] = x < ent_loc ? sel[x] : 0;
+    }
+  }
+  const double rturn = tid < R / 2 ? a.rope.t[tid] : 0.0;
+  f32x4 gv = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (tid < D / 4) gv = reinterpret_cast<const f32x4*>(a.gamma_q)[tid];
   constexpr int NSL = 4 * NJ + 2;
   auto slot_dim = [&](int sl) {
     return sl < 4 * NJ ? 128 * (sl >> 2) + 32 * g + 8 * (sl & 3) : (D - R) + 32 * (sl - 4 * NJ) + 8 * g;
@@ -174,15 +192,19 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
 
   if (tid < R / 2) {
     float cs, sn;
-    rope_cos_sin(t, a.rope.t[tid], &cs, &sn);
+    rope_cos_sin(t, rturn, &cs, &sn);
     s_cs[tid][0] = cs;
     s_cs[tid][1] = sn;
   }
   if constexpr (CSA) {
-    const int32_t* sel = a.topk + (int64_t)qr * a.k + row_beg;
-    for (int x = tid; x < ent_loc; x += kAttThreads) s_sel[x] = sel[x];
+#pragma unroll
+    for (int i = 0; i < SELR; ++i) {
+      const int x = tid + i * kAttThreads;
+      if (x < ent_loc) s_sel[x] = selv[i];
+    }
   }
   if (tid < 8) reinterpret_cast<unsigned*>(s_zero)[tid] = 0u;
+  if (tid < D / 4) reinterpret_cast<f32x4*>(s_gamma)[tid] = gv;
   // LDS writes only: the q loads stay in flight across this barrier
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -288,8 +310,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
       const int d0 = slot_ok(sl) ? slot_dim(sl) : 0;
-      const f32x4 ga = *reinterpret_cast<const f32x4*>(a.gamma_q + d0);
-      const f32x4 gb = *reinterpret_cast<const f32x4*>(a.gamma_q + d0 + 4);
+      const f32x4 ga = *reinterpret_cast<const f32x4*>(s_gamma + d0);
+      const f32x4 gb = *reinterpret_cast<const f32x4*>(s_gamma + d0 + 4);
       const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
       float qf[8];
 #pragma unroll
