@@ -22,10 +22,11 @@ context (both layers) and reports MFMA fractions for scoring and attention.
 "fp8_indexer" and "mxfp4_indexer" sections run the same CSA decode layer and
 prefill indexer with the FP8 (E4M3, one scale per row) and MXFP4 lightning
 indexers; the headline value keeps the bf16 indexer keys of the workload
-definition.
+definition.  An "nsa_variant" section times the NSA-style compress-select-
+window layer at the same 1M-token decode shape.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
-                    [--no-fp8] [--prefill-only] [--graph] [--counters]
+                    [--no-fp8] [--no-nsa] [--nsa-only] [--prefill-only] [--graph] [--counters]
 """
 
 import argparse
@@ -345,6 +346,58 @@ def low_precision_indexer_section(dev, st, launches, reps, fmt):
     }
 
 
+def nsa_section(dev, reps):
+    """The NSA-style variant at the 1M-token decode shape: 8 sequences, 64
+    heads x 512 dims, 16,384 compressed entries of 64-token blocks, 16 blocks
+    (1,024 tokens) selected, 128-token window, gates U(0,1).  One call =
+    compressed branch (logits kept), block scores, top-16, selected branch,
+    window branch, gated sum; timed with HIP events on the launching stream.
+    Inputs: N(0,1) packed rows for entries and the full token cache."""
+    import torch
+    from long_context_sparse_csa_amd import ops, synth
+    from long_context_sparse_csa_amd.configs import NSA_1M as c
+    B, H, D, R, m, W, n_sel = c.B, c.H, c.D, c.R, c.m, c.W, c.extra["n_sel"]
+    V, t = c.n_entries, c.q_pos0
+    q = synth.normal((B, 1, H, D), c.seed, "q", dev, dtype=torch.bfloat16)
+    ent = synth.packed_rows((B, V), D, R, c.seed, "entries", dev)
+    tok = synth.packed_rows((B, c.T), D, R, c.seed, "tokens", dev)
+    win = tok[:, t - (W - 1): t + 1].contiguous()
+    gq = synth.normal((D,), c.seed, "gamma_q", dev, mean=1.0, std=0.1)
+    gates = torch.rand((B, 1, H, 3), generator=torch.Generator().manual_seed(c.seed)).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(ops.nsa_attend_workspace_bytes(B, 1, H, D, V, m, t, W, n_sel),
+                     dtype=torch.uint8, device=dev)
+    call = lambda: ops.nsa_attend(q, ent, tok, win, gq, gates, n_entries=V, m=m, q_pos0=t, W=W,
+                                  n_sel=n_sel, out=out, workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    row = D + R
+    # per query: entries, logits written and read back, block scores written
+    # and read, selected token rows, window rows, q, three branch outputs
+    # written and read, out
+    per_q = (V * row + 2 * H * V * 4 + 2 * V * 4 + n_sel * m * row + W * row + H * D * 2 +
+             6 * H * D * 2 + H * D * 2)
+    gbs = B * per_q / (us * 1e-6) / 1e9
+    del tok
+    return {
+        "workload": f"nsa_decode_1m: B={B} T=2^20 m={m} N={V} n_sel={n_sel} "
+                    f"(selected tokens {n_sel * m}) H={H} D={D} R={R} W={W}",
+        "layer_us": round(us, 2),
+        "query_tokens_per_s": round(B / (us * 1e-6), 1),
+        "algorithmic_bytes_per_call": B * per_q,
+        "GBps": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+    }
+
+
 def cpu_baseline(inp, budget_s):
     """The float64 oracle on a bounded sample of the same inputs: whole CSA
     and HCA layers for single sequences, alternating, until the budget."""
@@ -427,6 +480,10 @@ def main():
                     help="skip the FP8 and MXFP4 indexer sections")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 4096-token prefill section")
+    ap.add_argument("--no-nsa", action="store_true",
+                    help="skip the NSA-style variant section")
+    ap.add_argument("--nsa-only", action="store_true",
+                    help="time only the NSA-style variant (prints its section as the JSON line)")
     ap.add_argument("--counters", action="store_true",
                     help="no timing: run a 1 GiB elementwise copy (known bytes) and a few "
                          "decode steps for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes")
@@ -445,6 +502,9 @@ def main():
     ops.lib()
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_section(dev, 3)}), flush=True)
+        return
+    if args.nsa_only:
+        print(json.dumps({"nsa_variant": nsa_section(dev, 20)}), flush=True)
         return
     log("generating inputs")
     inp = build_inputs(dev, args.rotate)
@@ -537,6 +597,10 @@ def main():
             res[f"{fmt}_indexer"] = sec
             log(f"{fmt} indexer: " + json.dumps(sec["decode"]) +
                 f", prefill index_topk {sec['prefill_index_topk_ms']} ms")
+    if not args.no_nsa:
+        log("nsa variant")
+        res["nsa_variant"] = nsa_section(dev, 20)
+        log("nsa variant: " + json.dumps(res["nsa_variant"]))
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle)")
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

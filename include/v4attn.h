@@ -315,6 +315,62 @@ int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries,
                       uint16_t* out, float* lse,
                       void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * v4attn_nsa_attend -- the NSA-style compress-select-window variant: a
+ * compressed branch over the visible compressed entries, a selected branch
+ * over the full-fidelity tokens of the n_sel best blocks, a window branch,
+ * mixed per query and head by three gates.
+ *
+ * Defines: NSA scores blocks with attention over compressed block
+ * representations, keeps the k best blocks at full fidelity plus a sliding
+ * window of recent tokens, and mixes the compressed, selected and window
+ * outputs with learned gates ("DeepSeek-V4, explained", the numbered steps of
+ * how a compress-then-select layer handles one query: scoring, top-k,
+ * combining branches).  The page gives no formulas; this library reads them
+ * as follows, with q~, logits, the -t output rotation and the packed row
+ * format exactly as v4attn_csa_attend, and NO sink in any branch:
+ *   V_t    = min(n_entries, floor((t+1)/m)) visible entries;
+ *   o_cmp  = attention over entries 0..V_t-1, probabilities p_{h,j};
+ *   block j = tokens [j m, (j+1) m) (the tokens entry j summarises);
+ *   s_j    = sum_h p_{h,j};  the n_sel best blocks by s (ties to the lower
+ *            block; fewer than n_sel visible -> all of them, -1 padded);
+ *   o_slc  = attention over the tokens of the selected blocks;
+ *   o_win  = attention over the window positions max(0, t-W+1)..t;
+ *   out    = g0 o_cmp + g1 o_slc + g2 o_win  (a branch with no rows is 0).
+ *
+ *   q       bf16 [B, Tq, H, D]        query r at position t = q_pos0 + r
+ *   entries u8   [B, Ncap, D+R]       packed compressed entries
+ *   tokens  u8   [B, Ntok, D+R]       packed full-fidelity rows, row i =
+ *                                     position i; Ntok >= V_t m for every
+ *                                     query of the block
+ *   win     u8   [B, Tq+W-1, D+R]     packed window rows (as csa_attend)
+ *   gamma_q f32 [D] (16-byte aligned)
+ *   gates   f32  [B, Tq, H, 3]        (compressed, selected, window)
+ *   out     bf16 [B, Tq, H, D] out
+ *   blocks  i32  [B, Tq, n_sel] out, nullable: the selected blocks,
+ *           ascending, -1 padded
+ *   block_score f32 [B, Tq, n_sel] out, nullable: their scores s_j
+ *   ws / ws_bytes  >= v4attn_nsa_attend_workspace(...) bytes, 16-byte
+ *           aligned; holds the compressed branch's logits (B Tq H V_max
+ *           floats) and every intermediate; contents on entry are ignored
+ * 1 <= n_sel, n_sel m <= 4096, 1 <= m <= 256.  Accumulation is fp32; the
+ * branch outputs are rounded to bf16 before the gated sum (in fp32).
+ * Errors: V4ATTN_EINVAL / EUNSUPPORTED / EWORKSPACE as the other calls; on an
+ * error nothing is launched.
+ */
+size_t v4attn_nsa_attend_workspace(int B, int Tq, int H, int D,
+                                   int64_t n_entries, int m, int64_t q_pos0,
+                                   int W, int n_sel);
+int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries,
+                      const uint8_t* tokens, const uint8_t* win,
+                      const float* gamma_q, const float* gates,
+                      int B, int Tq, int H, int D, int R, int64_t Ncap,
+                      int64_t n_entries, int m, int64_t Ntok, int W,
+                      int n_sel, int64_t q_pos0, float scale, float eps,
+                      float rope_base, uint16_t* out, int32_t* blocks,
+                      float* block_score, void* ws, size_t ws_bytes,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

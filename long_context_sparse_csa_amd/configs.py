@@ -66,5 +66,11 @@ CSA_1M = Workload("csa_decode_1m", "csa_decode", B=8, Tq=1, T=1 << 20, m=4,
 PREFILL_1M = Workload("prefill_4096_on_1m", "prefill", B=1, Tq=4096,
                       T=1 << 20, m=4, seed=5, extra={"m_hca": 128})
 
-ALL = [TINY_CSA, CSA_128K, HCA_1M, CSA_1M, PREFILL_1M]
+# The NSA-style variant ("DeepSeek-V4, explained", the numbered steps of how a
+# compress-then-select layer handles one query): 64-token blocks, one
+# compressed entry each, 16 blocks selected, the same 128-token window.
+NSA_1M = Workload("nsa_decode_1m", "nsa_decode", B=8, Tq=1, T=1 << 20, m=64,
+                  seed=6, extra={"n_sel": 16})
+
+ALL = [TINY_CSA, CSA_128K, HCA_1M, CSA_1M, PREFILL_1M, NSA_1M]
 BY_NAME = {w.name: w for w in ALL}

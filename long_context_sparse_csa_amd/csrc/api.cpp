@@ -3,6 +3,7 @@
 // so invalid calls return an error without touching the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -578,6 +579,138 @@ int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
   attend_ws_layout(a, ws);
   a.rows_max = rows_max;
   return hip_status(v4::launch_attend(a, (hipStream_t)stream), "HCA attend launch");
+}
+
+namespace {
+
+// NSA-style variant workspace: the compressed branch's logits and lse, the
+// three branch outputs, block scores, the top-k scratch, the selected blocks
+// and their tokens, then the attention partials (reused by the three
+// branches in turn: they run in order on one stream).
+struct NsaWs {
+  int64_t vmax, lstride, sstride;
+  size_t logits, lse, o[3], score, topk, blocks, tok, att, total;
+  TopkWs tk;
+};
+
+NsaWs nsa_ws(int B, int Tq, int H, int D, int64_t n_entries, int m, int64_t q_pos0, int W,
+             int n_sel) {
+  NsaWs w;
+  const int64_t q = (int64_t)B * Tq;
+  w.vmax = vmax_of(Tq, n_entries, q_pos0, m);
+  w.lstride = (w.vmax + 127) / 128 * 128;   // the kernel writes whole 128-row tiles
+  w.sstride = (w.vmax + 63) / 64 * 64;
+  size_t o = 0;
+  w.logits = o; o += align256((size_t)(q * H * w.lstride) * sizeof(float));
+  w.lse = o;    o += align256((size_t)(q * H) * sizeof(float));
+  for (int b = 0; b < 3; ++b) { w.o[b] = o; o += align256((size_t)(q * H * D) * sizeof(uint16_t)); }
+  w.score = o;  o += align256((size_t)(q * w.sstride) * sizeof(float));
+  w.tk = topk_ws(B, Tq, n_entries, q_pos0, m, n_sel);
+  w.topk = o;   o += align256(w.tk.total);
+  w.blocks = o; o += align256((size_t)(q * n_sel) * sizeof(int32_t));
+  w.tok = o;    o += align256((size_t)(q * n_sel * m) * sizeof(int32_t));
+  w.att = o;
+  size_t att = attend_ws(B, Tq, H, D, w.vmax, false, nullptr);
+  att = std::max(att, attend_ws(B, Tq, H, D, (int64_t)n_sel * m, true, nullptr));
+  att = std::max(att, attend_ws(B, Tq, H, D, W, false, nullptr));
+  w.total = o + att;
+  return w;
+}
+
+}  // namespace
+
+size_t v4attn_nsa_attend_workspace(int B, int Tq, int H, int D, int64_t n_entries, int m,
+                                   int64_t q_pos0, int W, int n_sel) {
+  if (B < 0 || Tq < 0 || H < 1 || D < 1 || n_entries < 0 || m < 1 || q_pos0 < 0 || W < 0 ||
+      n_sel < 1)
+    return 0;
+  return nsa_ws(B, Tq, H, D, n_entries, m, q_pos0, W, n_sel).total;
+}
+
+int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* tokens,
+                      const uint8_t* win, const float* gamma_q, const float* gates, int B,
+                      int Tq, int H, int D, int R, int64_t Ncap, int64_t n_entries, int m,
+                      int64_t Ntok, int W, int n_sel, int64_t q_pos0, float scale, float eps,
+                      float rope_base, uint16_t* out, int32_t* blocks, float* block_score,
+                      void* ws, size_t ws_bytes, void* stream) {
+  static const float kNoSinkCheck = 0.f;   // the common check wants a sink; no branch has one
+  if (int st = check_attend_common(q, entries, win, gamma_q, &kNoSinkCheck, B, Tq, H, D, R, Ncap,
+                                   W, q_pos0, scale, eps, rope_base, out))
+    return st;
+  if (!gates) return fail(V4ATTN_EINVAL, "null gates");
+  if (n_entries < 0 || n_entries > Ncap) return fail(V4ATTN_EINVAL, "need 0 <= n_entries <= Ncap");
+  if (n_entries >= (int64_t)1 << 31) return fail(V4ATTN_EUNSUPPORTED, "n_entries >= 2^31");
+  if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
+  if (n_sel < 1 || (int64_t)n_sel * m > kMaxK)
+    return fail(V4ATTN_EUNSUPPORTED, "n_sel = %d, m = %d: 1 <= n_sel and n_sel m <= %d are built",
+                n_sel, m, kMaxK);
+  if (int st = check_topk_len(Tq, n_entries, q_pos0, m)) return st;
+  const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
+  if (Ntok < vmax * m)
+    return fail(V4ATTN_EINVAL, "Ntok %lld < %lld: the tokens of every visible block are needed",
+                (long long)Ntok, (long long)(vmax * m));
+  if (Ntok * (int64_t)(D + R) >= ((int64_t)1 << 32))
+    return fail(V4ATTN_EUNSUPPORTED, "one sequence's token cache must be below 4 GiB");
+  if (Ntok > 0 && !tokens) return fail(V4ATTN_EINVAL, "null tokens with Ntok > 0");
+  if (!aligned16(tokens)) return fail(V4ATTN_EINVAL, "tokens must be 16-byte aligned");
+  const NsaWs w = nsa_ws(B, Tq, H, D, n_entries, m, q_pos0, W, n_sel);
+  if (w.total > 0 && (!ws || ws_bytes < w.total))
+    return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
+  const int64_t nq = (int64_t)B * Tq;
+  if (nq == 0) return hip_status(hipSuccess, "");
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* logits = reinterpret_cast<float*>(base + w.logits);
+  float* lse = reinterpret_cast<float*>(base + w.lse);
+  uint16_t* o_b[3];
+  for (int b = 0; b < 3; ++b) o_b[b] = reinterpret_cast<uint16_t*>(base + w.o[b]);
+  float* score = reinterpret_cast<float*>(base + w.score);
+  int32_t* blk = blocks ? blocks : reinterpret_cast<int32_t*>(base + w.blocks);
+  int32_t* tok = reinterpret_cast<int32_t*>(base + w.tok);
+  void* att_ws = base + w.att;
+
+  v4::AttendArgs a{};
+  a.q = q; a.win = win; a.gamma_q = gamma_q; a.sink = nullptr;
+  a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R;
+  a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps; a.rope_base = rope_base;
+  a.rope = v4::rope_turns(rope_base, R);
+  auto run_branch = [&](v4::AttendArgs& x, bool csa, const char* what) {
+    x.splits = v4::attend_splits(B, Tq, x.rows_max, csa);
+    attend_ws_layout(x, att_ws);
+    return hip_status(v4::launch_attend(x, st), what);
+  };
+
+  // 1. compressed branch: every visible entry, its logits and lse kept
+  v4::AttendArgs c = a;
+  c.entries = entries; c.topk = nullptr; c.Ncap = Ncap; c.n_entries = n_entries; c.m = m;
+  c.W = 0; c.out = o_b[0]; c.lse = lse; c.rows_max = vmax;
+  c.logits2 = logits; c.logits_stride = w.lstride;
+  if (int s = run_branch(c, false, "NSA compressed branch launch")) return s;
+  // 2. block scores and the top n_sel blocks
+  v4::NsaBlockScoreArgs bs{logits, lse, B, Tq, H, w.lstride, n_entries, q_pos0, m, vmax,
+                           score, w.sstride};
+  hipError_t e = v4::launch_nsa_block_score(bs, st);
+  if (e != hipSuccess) return hip_status(e, "NSA block score launch");
+  e = run_topk(score, w.sstride, B, Tq, n_entries, q_pos0, m, n_sel, blk, block_score,
+               base + w.topk, w.tk, st);
+  if (e != hipSuccess) return hip_status(e, "NSA block top-k launch");
+  // 3. selected branch: the tokens of the selected blocks
+  v4::NsaExpandArgs ex{blk, (int)nq, n_sel, m, tok};
+  e = v4::launch_nsa_expand(ex, st);
+  if (e != hipSuccess) return hip_status(e, "NSA expand launch");
+  v4::AttendArgs sl = a;
+  sl.entries = tokens; sl.topk = tok; sl.Ncap = Ntok; sl.k = n_sel * m; sl.W = 0;
+  sl.out = o_b[1]; sl.rows_max = (int64_t)n_sel * m;
+  if (int s = run_branch(sl, true, "NSA selected branch launch")) return s;
+  // 4. window branch
+  v4::AttendArgs wn = a;
+  wn.entries = entries; wn.topk = nullptr; wn.Ncap = Ncap; wn.n_entries = 0; wn.m = 1;
+  wn.W = W; wn.out = o_b[2]; wn.rows_max = W;
+  if (int s = run_branch(wn, false, "NSA window branch launch")) return s;
+  // 5. gated sum
+  v4::NsaCombineArgs cb{o_b[0], o_b[1], o_b[2], gates, nq * H, D, out};
+  return hip_status(v4::launch_nsa_combine(cb, st), "NSA combine launch");
 }
 
 }  // extern "C"

@@ -639,6 +639,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
       qk(T, cur, sacc, mp, mo, [&](int st) {
         if (st < G::WPW && nbase) issue_copy(nbase, cur ^ 1, st);
       });
+      if (a.logits2 && head < a.H) {   // the tile's logits (log2 units; absent rows -inf)
+        float* lp = a.logits2 + ((int64_t)qr * a.H + head) * a.logits_stride + row_beg +
+                    (int64_t)tile * kAttRows + 4 * g;
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb) *reinterpret_cast<f32x4*>(lp + 16 * rb) = sacc[rb] * sl2;
+      }
       if (__any(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mo[0], mo[1])) > m_run + kLazyMax)) {
         grow = true;
         break;
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
   }
   const bool seen = l_run > 0.f;
   const float mr = seen ? m_run : -INFINITY;
-  const float z2 = a.sink[head] * kLog2e;
+  const float z2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;   // no sink: -inf
   const float M = fmaxf(mr, z2);
   float scale_o = 0.f, lse = -INFINITY;
   if (M != -INFINITY) {
@@ -740,7 +746,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a) {
     const bool own = lane < S;
     const f32x2 ml = own ? *reinterpret_cast<const f32x2*>(pm + (int64_t)lane * a.H * 2)
                          : f32x2{-INFINITY, 0.f};
-    const float z2 = a.sink[h] * kLog2e;
+    const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
     const float M = fmaxf(wave_max(ml.x), z2);
     const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
     float den = wave_sum(ml.y * w);

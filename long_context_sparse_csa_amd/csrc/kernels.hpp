@@ -139,7 +139,7 @@ struct AttendArgs {
   const int32_t* topk;      // [B, Tq, k] or nullptr
   const uint8_t* win;       // [B, Tq+W-1, D+R]
   const float* gamma_q;
-  const float* sink;
+  const float* sink;        // [H], or nullptr for no sink
   int B, Tq, H, D, R;
   int64_t Ncap;
   int k;                    // CSA: top-k slots
@@ -155,11 +155,49 @@ struct AttendArgs {
   uint16_t* part_o;         // [B*Tq, splits, H, D] bf16, unnormalised (splits > 1)
   float* part_ml;           // [B*Tq, splits, H, 2]  (max, sum)
   int64_t rows_max;         // max rows (entries + window) over the block
+  float* logits2;           // nullptr, or [B*Tq, H, logits_stride]: every row's logit
+                            // times log2(e) (absent rows -inf); logits_stride >= rows
+                            // rounded up to 128
+  int64_t logits_stride;
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 
 // Number of key-range splits the attention uses for a problem (shared by
 // the workspace query and the launch so both agree).
 int attend_splits(int B, int Tq, int64_t rows_max, bool csa);
+
+// NSA-style variant: block scores from the compressed branch's logits.
+struct NsaBlockScoreArgs {
+  const float* logits2;     // [B*Tq, H, logits_stride], log2 units
+  const float* lse;         // [B*Tq, H], natural log
+  int B, Tq, H;
+  int64_t logits_stride;
+  int64_t n_entries, q_pos0;
+  int m;
+  int64_t vmax;             // max visible entries over the block
+  float* score;             // [B*Tq, score_stride]
+  int64_t score_stride;
+};
+hipError_t launch_nsa_block_score(const NsaBlockScoreArgs& a, hipStream_t st);
+
+// Selected blocks -> their tokens.
+struct NsaExpandArgs {
+  const int32_t* blocks;    // [rows, n_sel], -1 = empty
+  int rows, n_sel, m;
+  int32_t* tok;             // [rows, n_sel * m]
+};
+hipError_t launch_nsa_expand(const NsaExpandArgs& a, hipStream_t st);
+
+// out = g0 o_cmp + g1 o_slc + g2 o_win (bf16 in and out, fp32 arithmetic).
+struct NsaCombineArgs {
+  const uint16_t* o_cmp;    // [rows, D]   (rows = B*Tq*H)
+  const uint16_t* o_slc;
+  const uint16_t* o_win;
+  const float* gates;       // [rows, 3]
+  int64_t rows;
+  int D;
+  uint16_t* out;
+};
+hipError_t launch_nsa_combine(const NsaCombineArgs& a, hipStream_t st);
 
 }  // namespace v4

@@ -59,6 +59,9 @@ _SIGS = {
     "v4attn_hca_attend_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I]),
     "v4attn_hca_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I, _L, _F,
                                _F, _F, _P, _P, _P, _Z, _P]),
+    "v4attn_nsa_attend_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I, _I]),
+    "v4attn_nsa_attend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _L, _I,
+                               _I, _L, _F, _F, _F, _P, _P, _P, _P, _Z, _P]),
 }
 
 _lib = None
@@ -438,3 +441,41 @@ def hca_attend(q, entries, win, gamma_q, sink, *, n_entries, m, q_pos0, W, scale
                                   int(q_pos0), float(scale), float(eps), float(rope_base),
                                   _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(q)))
     return out, lse
+
+
+def nsa_attend_workspace_bytes(B, Tq, H, D, n_entries, m, q_pos0, W, n_sel):
+    return lib().v4attn_nsa_attend_workspace(B, Tq, H, D, n_entries, m, q_pos0, W, n_sel)
+
+
+def nsa_attend(q, entries, tokens, win, gamma_q, gates, *, n_entries, m, q_pos0, W, n_sel,
+               scale=None, eps=1e-6, rope_base=10000.0, R=64, out=None, want_blocks=False,
+               workspace=None):
+    """NSA-style variant: compressed, selected-block and window branches mixed
+    by per-head gates.  Returns (out, blocks, block_score); the last two are
+    None unless want_blocks."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(entries, "entries", torch.uint8, 3)
+    _need(tokens, "tokens", torch.uint8, 3)
+    _need(win, "win", torch.uint8, 3)
+    _need(gamma_q, "gamma_q", torch.float32, 1)
+    _need(gates, "gates", torch.float32, 4)
+    B, Tq, H, D = q.shape
+    if entries.shape[0] != B or entries.shape[2] != D + R or tokens.shape[0] != B \
+            or tokens.shape[2] != D + R or tuple(win.shape) != (B, Tq + W - 1, D + R) \
+            or gamma_q.numel() != D or tuple(gates.shape) != (B, Tq, H, 3):
+        raise ValueError("shape mismatch")
+    scale = D ** -0.5 if scale is None else scale
+    out, _ = _attend_io(q, out, None, False)
+    blocks = block_score = None
+    if want_blocks:
+        blocks = torch.empty((B, Tq, n_sel), dtype=torch.int32, device=q.device)
+        block_score = torch.empty((B, Tq, n_sel), dtype=torch.float32, device=q.device)
+    nbytes = nsa_attend_workspace_bytes(B, Tq, H, D, n_entries, m, q_pos0, W, n_sel)
+    workspace = _workspace(nbytes, q.device, workspace)
+    check(lib().v4attn_nsa_attend(_ptr(q), _ptr(entries), _ptr(tokens), _ptr(win), _ptr(gamma_q),
+                                  _ptr(gates), B, Tq, H, D, R, entries.shape[1], int(n_entries),
+                                  int(m), tokens.shape[1], int(W), int(n_sel), int(q_pos0),
+                                  float(scale), float(eps), float(rope_base), _ptr(out),
+                                  _ptr(blocks), _ptr(block_score), _ptr(workspace), nbytes,
+                                  _stream(q)))
+    return out, blocks, block_score

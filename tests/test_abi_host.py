@@ -32,7 +32,7 @@ MISALIGNED = ctypes.c_void_p(0x100008)
 def test_exports_every_header_function():
     names = ops().header_functions()
     assert "v4attn_compress" in names and "v4attn_hca_attend" in names
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(L(), n), n
     assert L().v4attn_version() == 1
@@ -232,3 +232,39 @@ def test_hca_attend_rejects():
     # 32 sequences at 1M need split partials: workspace too small
     args[5], args[10], args[11], args[14] = 32, 8192, 8192, (1 << 20) - 1
     assert f(*args) == -3
+
+
+def _nsa(**kw):
+    a = dict(q=FAKE, e=FAKE, tok=FAKE, w=FAKE, g=FAKE, gates=FAKE, B=1, Tq=1, H=64, D=512, R=64,
+             Ncap=100, n_entries=100, m=4, Ntok=400, W=128, n_sel=16, q_pos0=500, scale=0.04,
+             eps=1e-6, base=1e4, out=FAKE, blocks=None, bscore=None, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return L().v4attn_nsa_attend(a["q"], a["e"], a["tok"], a["w"], a["g"], a["gates"], a["B"],
+                                 a["Tq"], a["H"], a["D"], a["R"], a["Ncap"], a["n_entries"],
+                                 a["m"], a["Ntok"], a["W"], a["n_sel"], a["q_pos0"], a["scale"],
+                                 a["eps"], a["base"], a["out"], a["blocks"], a["bscore"], a["ws"],
+                                 a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gates=None), -1),
+    (dict(tok=None), -1),
+    (dict(tok=MISALIGNED), -1),
+    (dict(n_entries=101), -1),            # more entries than the cache holds
+    (dict(m=0), -2),
+    (dict(n_sel=0), -2),
+    (dict(n_sel=2048, m=4), -2),          # n_sel m > 4096 token slots
+    (dict(Ntok=399), -1),                 # the last visible block's tokens are missing
+    (dict(H=65), -2),
+    (dict(ws_bytes=16), -3),
+    (dict(ws=MISALIGNED), -1),
+])
+def test_nsa_attend_rejects(kw, status):
+    assert _nsa(**kw) == status
+
+
+def test_nsa_workspace_holds_the_compressed_logits():
+    # 8 queries x 64 heads x 8192 visible entries (1M context, m = 128) of fp32 logits
+    n = L().v4attn_nsa_attend_workspace(8, 1, 64, 512, 8192, 128, (1 << 20) - 1, 128, 16)
+    assert n >= 8 * 64 * 8192 * 4
+    assert L().v4attn_nsa_attend_workspace(8, 1, 64, 512, 8192, 128, 0, 128, 0) == 0
