@@ -64,7 +64,7 @@ size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 TopkWs topk_ws(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m, int k) {
   TopkWs w;
   const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
-  w.plan = v4::topk_plan(vmax);
+  w.plan = v4::topk_plan(vmax, k);
   const int64_t rows = (int64_t)B * Tq;
   const int64_t np = w.plan.nparts;
   w.part_bytes = align256((size_t)(rows * np) * sizeof(int));
@@ -300,6 +300,7 @@ hipError_t run_topk(const float* scores, int64_t stride, int B, int Tq, int64_t 
   ta.q_pos0 = q_pos0;
   ta.m = m;
   ta.k = k;
+  ta.direct_max = w.plan.direct_max;
   ta.nparts = w.plan.nparts;
   ta.part_tau = ta.part_over = nullptr;
   ta.part_cnt = nullptr;
@@ -583,15 +584,24 @@ int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
 
 namespace {
 
-// NSA-style variant workspace: the compressed branch's logits and lse, the
-// three branch outputs, block scores, the top-k scratch, the selected blocks
-// and their tokens, then the attention partials (reused by the three
-// branches in turn: they run in order on one stream).
+// NSA-style variant workspace: the compressed branch's logits and lse, its
+// output and the window branch's, block scores, the top-k scratch, the
+// selected blocks, then the attention partials: the compressed and window
+// branches run in one launch (separate regions); the selected branch reuses
+// the compressed branch's region after it.
 struct NsaWs {
   int64_t vmax, lstride, sstride;
-  size_t logits, lse, o[3], score, topk, blocks, tok, att, total;
+  size_t logits, lse, o_cmp, o_win, score, topk, blocks, att_cmp, att_win, total;
   TopkWs tk;
 };
+
+// Where the window branch runs.  One attention workgroup fills a CU, so it
+// goes beside the selected branch (few workgroups) when that branch merges
+// split partials in a later pass, which then reads the finished window
+// output for the gated sum; otherwise beside the compressed branch.
+bool nsa_win_with_selected(int B, int Tq, int n_sel, int m) {
+  return v4::attend_splits(B, Tq, (int64_t)n_sel * m, true) > 1;
+}
 
 NsaWs nsa_ws(int B, int Tq, int H, int D, int64_t n_entries, int m, int64_t q_pos0, int W,
              int n_sel) {
@@ -600,20 +610,22 @@ NsaWs nsa_ws(int B, int Tq, int H, int D, int64_t n_entries, int m, int64_t q_po
   w.vmax = vmax_of(Tq, n_entries, q_pos0, m);
   w.lstride = (w.vmax + 127) / 128 * 128;   // the kernel writes whole 128-row tiles
   w.sstride = (w.vmax + 63) / 64 * 64;
+  const size_t o_bytes = align256((size_t)(q * H * D) * sizeof(uint16_t));
   size_t o = 0;
-  w.logits = o; o += align256((size_t)(q * H * w.lstride) * sizeof(float));
+  w.logits = o; o += align256((size_t)(q * w.lstride * 64) * sizeof(float));
   w.lse = o;    o += align256((size_t)(q * H) * sizeof(float));
-  for (int b = 0; b < 3; ++b) { w.o[b] = o; o += align256((size_t)(q * H * D) * sizeof(uint16_t)); }
+  w.o_cmp = o;  o += o_bytes;
+  w.o_win = o;  o += o_bytes;
   w.score = o;  o += align256((size_t)(q * w.sstride) * sizeof(float));
   w.tk = topk_ws(B, Tq, n_entries, q_pos0, m, n_sel);
   w.topk = o;   o += align256(w.tk.total);
   w.blocks = o; o += align256((size_t)(q * n_sel) * sizeof(int32_t));
-  w.tok = o;    o += align256((size_t)(q * n_sel * m) * sizeof(int32_t));
-  w.att = o;
-  size_t att = attend_ws(B, Tq, H, D, w.vmax, false, nullptr);
-  att = std::max(att, attend_ws(B, Tq, H, D, (int64_t)n_sel * m, true, nullptr));
-  att = std::max(att, attend_ws(B, Tq, H, D, W, false, nullptr));
-  w.total = o + att;
+  const size_t a_cmp = align256(attend_ws(B, Tq, H, D, w.vmax, false, nullptr));
+  const size_t a_win = align256(attend_ws(B, Tq, H, D, W, false, nullptr));
+  const size_t a_sel = align256(attend_ws(B, Tq, H, D, (int64_t)n_sel * m, true, nullptr));
+  w.att_cmp = o;
+  w.att_win = o + std::max(a_cmp, a_sel);
+  w.total = w.att_win + a_win;
   return w;
 }
 
@@ -663,54 +675,60 @@ int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
   uint8_t* base = static_cast<uint8_t*>(ws);
   float* logits = reinterpret_cast<float*>(base + w.logits);
   float* lse = reinterpret_cast<float*>(base + w.lse);
-  uint16_t* o_b[3];
-  for (int b = 0; b < 3; ++b) o_b[b] = reinterpret_cast<uint16_t*>(base + w.o[b]);
+  uint16_t* o_cmp = reinterpret_cast<uint16_t*>(base + w.o_cmp);
+  uint16_t* o_win = reinterpret_cast<uint16_t*>(base + w.o_win);
   float* score = reinterpret_cast<float*>(base + w.score);
   int32_t* blk = blocks ? blocks : reinterpret_cast<int32_t*>(base + w.blocks);
-  int32_t* tok = reinterpret_cast<int32_t*>(base + w.tok);
-  void* att_ws = base + w.att;
 
   v4::AttendArgs a{};
   a.q = q; a.win = win; a.gamma_q = gamma_q; a.sink = nullptr;
   a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R;
   a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps; a.rope_base = rope_base;
   a.rope = v4::rope_turns(rope_base, R);
-  auto run_branch = [&](v4::AttendArgs& x, bool csa, const char* what) {
-    x.splits = v4::attend_splits(B, Tq, x.rows_max, csa);
-    attend_ws_layout(x, att_ws);
-    return hip_status(v4::launch_attend(x, st), what);
-  };
 
-  // 1. compressed branch: every visible entry, its logits and lse kept
-  v4::AttendArgs c = a;
-  c.entries = entries; c.topk = nullptr; c.Ncap = Ncap; c.n_entries = n_entries; c.m = m;
-  c.W = 0; c.out = o_b[0]; c.lse = lse; c.rows_max = vmax;
+  const bool win_late = nsa_win_with_selected(B, Tq, n_sel, m);
+  // window branch: the window rows only (as an HCA problem with no entries,
+  // or a CSA problem with no top-k slots)
+  v4::AttendArgs wn = a;
+  wn.entries = entries; wn.Ncap = Ncap; wn.n_entries = 0; wn.m = 1; wn.W = W;
+  wn.out = o_win; wn.rows_max = W;
+  if (win_late) { wn.topk = blk; wn.k = 0; }
+  wn.splits = v4::attend_splits(B, Tq, wn.rows_max, win_late);
+  attend_ws_layout(wn, base + w.att_win);
+
+  // 1. compressed branch: every visible entry, logits and lse kept
+  v4::AttendBatch ab{};
+  v4::AttendArgs& c = ab.p[0];
+  c = a;
+  c.entries = entries; c.Ncap = Ncap; c.n_entries = n_entries; c.m = m; c.W = 0;
+  c.out = o_cmp; c.lse = lse; c.rows_max = vmax;
   c.logits2 = logits; c.logits_stride = w.lstride;
-  if (int s = run_branch(c, false, "NSA compressed branch launch")) return s;
+  c.splits = v4::attend_splits(B, Tq, c.rows_max, false);
+  attend_ws_layout(c, base + w.att_cmp);
+  if (!win_late) ab.p[1] = wn;
+  hipError_t e = v4::launch_attend_batch(ab, win_late ? 1 : 2, st);
+  if (e != hipSuccess) return hip_status(e, "NSA compressed branch launch");
   // 2. block scores and the top n_sel blocks
   v4::NsaBlockScoreArgs bs{logits, lse, B, Tq, H, w.lstride, n_entries, q_pos0, m, vmax,
                            score, w.sstride};
-  hipError_t e = v4::launch_nsa_block_score(bs, st);
+  e = v4::launch_nsa_block_score(bs, st);
   if (e != hipSuccess) return hip_status(e, "NSA block score launch");
   e = run_topk(score, w.sstride, B, Tq, n_entries, q_pos0, m, n_sel, blk, block_score,
                base + w.topk, w.tk, st);
   if (e != hipSuccess) return hip_status(e, "NSA block top-k launch");
-  // 3. selected branch: the tokens of the selected blocks
-  v4::NsaExpandArgs ex{blk, (int)nq, n_sel, m, tok};
-  e = v4::launch_nsa_expand(ex, st);
-  if (e != hipSuccess) return hip_status(e, "NSA expand launch");
-  v4::AttendArgs sl = a;
-  sl.entries = tokens; sl.topk = tok; sl.Ncap = Ntok; sl.k = n_sel * m; sl.W = 0;
-  sl.out = o_b[1]; sl.rows_max = (int64_t)n_sel * m;
-  if (int s = run_branch(sl, true, "NSA selected branch launch")) return s;
-  // 4. window branch
-  v4::AttendArgs wn = a;
-  wn.entries = entries; wn.topk = nullptr; wn.Ncap = Ncap; wn.n_entries = 0; wn.m = 1;
-  wn.W = W; wn.out = o_b[2]; wn.rows_max = W;
-  if (int s = run_branch(wn, false, "NSA window branch launch")) return s;
-  // 5. gated sum
-  v4::NsaCombineArgs cb{o_b[0], o_b[1], o_b[2], gates, nq * H, D, out};
-  return hip_status(v4::launch_nsa_combine(cb, st), "NSA combine launch");
+  // 3. selected branch over the tokens of the selected blocks; its final
+  //    store forms the gated sum with the other two branches
+  v4::AttendBatch sb{};
+  v4::AttendArgs& sl = sb.p[0];
+  sl = a;
+  sl.entries = tokens; sl.topk = blk; sl.sel_m = m; sl.Ncap = Ntok; sl.k = n_sel * m; sl.W = 0;
+  sl.out = out; sl.rows_max = (int64_t)n_sel * m;
+  sl.mix_gates = gates; sl.mix_o0 = o_cmp; sl.mix_o2 = o_win;
+  sl.splits = v4::attend_splits(B, Tq, sl.rows_max, true);
+  attend_ws_layout(sl, base + w.att_cmp);
+  if (win_late) sb.p[1] = wn;
+  return hip_status(v4::launch_attend_batch(sb, win_late ? 2 : 1, st),
+                    "NSA selected branch launch");
 }
 
 }  // extern "C"

@@ -124,13 +124,33 @@ __host__ __device__ inline int64_t split_chunk(int64_t n_rows, int splits) {
   return (c + kAttRows - 1) / kAttRows * kAttRows;
 }
 
+// out = g1 * y + g0 * o0 + g2 * o2 for four dims (the gated sum of the
+// NSA-style variant, applied where the last branch is finalised), else y.
+__device__ __forceinline__ u32x2 final_bf16x4(const AttendArgs& a, int64_t off, int64_t qh,
+                                              const float (&y)[4]) {
+  if (!a.mix_gates) return u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  const float g0 = a.mix_gates[3 * qh], g1 = a.mix_gates[3 * qh + 1], g2 = a.mix_gates[3 * qh + 2];
+  const u32x2 u0 = *reinterpret_cast<const u32x2*>(a.mix_o0 + off);
+  const u32x2 u2 = *reinterpret_cast<const u32x2*>(a.mix_o2 + off);
+  const float x0[4] = {bf16_bits_to_f32(u0.x & 0xFFFFu), bf16_bits_to_f32(u0.x >> 16),
+                       bf16_bits_to_f32(u0.y & 0xFFFFu), bf16_bits_to_f32(u0.y >> 16)};
+  const float x2[4] = {bf16_bits_to_f32(u2.x & 0xFFFFu), bf16_bits_to_f32(u2.x >> 16),
+                       bf16_bits_to_f32(u2.y & 0xFFFFu), bf16_bits_to_f32(u2.y >> 16)};
+  float z[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = fmaf(g2, x2[e], fmaf(g0, x0[e], g1 * y[e]));
+  return u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+}
+
 template <int D, bool CSA>
-__global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   using G = AttGeom<D>;
   constexpr int R = G::R, NJ = G::NJ, NB8 = G::NB8, NB = G::NB, ROW = G::ROW;
   constexpr int BFC = G::FP8_CPR;   // first bf16 chunk
+  const AttendArgs& a = ab.p[blockIdx.z];   // the problem of this grid layer
   const int qr = blockIdx.y;
   const int split = blockIdx.x;
+  if (split >= a.splits) return;   // a layer with fewer splits than the grid
   const int b = qr / a.Tq, r = qr % a.Tq;
   const int64_t t = a.q_pos0 + r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -166,11 +186,22 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
   constexpr int SELR = CSA ? kSelCap / kAttThreads : 1;
   int selv[SELR];
   if constexpr (CSA) {
-    const int32_t* sel = a.topk + (int64_t)qr * a.k + row_beg;
+    if (a.sel_m > 1) {   // slots hold blocks of sel_m consecutive rows
+      const int32_t* sel = a.topk + (int64_t)qr * (a.k / a.sel_m);
 #pragma unroll
-    for (int i = 0; i < SELR; ++i) {
-      const int x = tid + i * kAttThreads;
-      selv[i] = x < ent_loc ? sel[x] : 0;
+      for (int i = 0; i < SELR; ++i) {
+        const int x = tid + i * kAttThreads;
+        const int p = (int)row_beg + x;
+        const int blk = x < ent_loc ? sel[p / a.sel_m] : -1;
+        selv[i] = blk >= 0 ? blk * a.sel_m + p % a.sel_m : -1;
+      }
+    } else {
+      const int32_t* sel = a.topk + (int64_t)qr * a.k + row_beg;
+#pragma unroll
+      for (int i = 0; i < SELR; ++i) {
+        const int x = tid + i * kAttThreads;
+        selv[i] = x < ent_loc ? sel[x] : 0;
+      }
     }
   }
   const double rturn = tid < R / 2 ? a.rope.t[tid] : 0.0;
@@ -640,10 +671,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
         if (st < G::WPW && nbase) issue_copy(nbase, cur ^ 1, st);
       });
       if (a.logits2 && head < a.H) {   // the tile's logits (log2 units; absent rows -inf)
-        float* lp = a.logits2 + ((int64_t)qr * a.H + head) * a.logits_stride + row_beg +
-                    (int64_t)tile * kAttRows + 4 * g;
+        float* lp = a.logits2 + ((int64_t)qr * a.logits_stride + row_beg +
+                                 (int64_t)tile * kAttRows + 4 * g) * 64 + head;
 #pragma unroll
-        for (int rb = 0; rb < 8; ++rb) *reinterpret_cast<f32x4*>(lp + 16 * rb) = sacc[rb] * sl2;
+        for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lp[(16 * rb + i) * 64] = sacc[rb][i] * sl2;
       }
       if (__any(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mo[0], mo[1])) > m_run + kLazyMax)) {
         grow = true;
@@ -710,8 +743,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
         v[e + 1] = -x0 * sn + x1 * cs;
       }
     }
-    const u32x2 pkd = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    *reinterpret_cast<u32x2*>(op + d0) = pkd;
+    const int64_t qh = (int64_t)qr * a.H + head;
+    *reinterpret_cast<u32x2*>(op + d0) = final_bf16x4(a, qh * D + d0, qh, v);
   }
   if (a.lse && g == 0) a.lse[(int64_t)qr * a.H + head] = lse;
 }
@@ -722,7 +755,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs a) {
 // .. into one weight per split (splits <= 64: one lane each); then every thread merges
 // four dims of one head, all of its split loads in flight together.
 template <int D>
-__global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a) {
+__global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
+  const AttendArgs& a = ab.p[blockIdx.z];
+  if (a.splits <= 1) return;   // this layer's kernel stored its output itself
   constexpr int R = 64;
   constexpr int QPH = D / 4;          // threads per head (four dims each)
   constexpr int HPW = 256 / QPH;      // heads per workgroup
@@ -786,14 +821,16 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a) {
       y[e + 1] = -x0 * sn + x1 * cs;
     }
   }
-  const u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-  *reinterpret_cast<u32x2*>(a.out + ((int64_t)qr * a.H + h) * D + d) = pk;
+  const int64_t qh = (int64_t)qr * a.H + h;
+  *reinterpret_cast<u32x2*>(a.out + qh * D + d) = final_bf16x4(a, qh * D + d, qh, y);
 }
 
-int attend_splits(int B, int Tq, int64_t rows_max, bool csa) {
+int attend_splits(int B, int Tq, int64_t rows_max, bool csa, int wg_budget) {
   const int64_t q = (int64_t)B * Tq;
   if (q <= 0 || rows_max <= 0) return 1;
-  int64_t s = (256 + q - 1) / q;                                 // about one workgroup per CU
+  // about one workgroup per CU (one fits a CU); within a smaller budget, at
+  // most the budget
+  int64_t s = wg_budget >= 256 ? (256 + q - 1) / q : wg_budget / q;
   const int64_t by_rows = (rows_max + kAttRows - 1) / kAttRows;  // at least one tile per split
   if (s > by_rows) s = by_rows;
   if (s > 64) s = 64;
@@ -804,19 +841,31 @@ int attend_splits(int B, int Tq, int64_t rows_max, bool csa) {
   return (int)s;
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
+hipError_t launch_attend_batch(const AttendBatch& ab, int n, hipStream_t st) {
+  const AttendArgs& a = ab.p[0];
   const int64_t q = (int64_t)a.B * a.Tq;
   if (q == 0) return hipSuccess;
   const bool csa = a.topk != nullptr;
-  // every split's slice of the top-k list must fit the kernel's LDS copy
-  if (csa && split_chunk(a.rows_max, a.splits) > kSelCap) return hipErrorInvalidValue;
-  dim3 grid(a.splits, (unsigned)q);
+  int gx = 1;
+  bool merge = false;
+  for (int z = 0; z < n; ++z) {
+    const AttendArgs& x = ab.p[z];
+    // one kernel instance serves the batch: same kind, shapes and query block
+    if ((x.topk != nullptr) != csa || x.D != a.D || x.H != a.H || x.B != a.B || x.Tq != a.Tq)
+      return hipErrorInvalidValue;
+    // every split's slice of the top-k list must fit the kernel's LDS copy
+    if (csa && split_chunk(x.rows_max, x.splits) > kSelCap) return hipErrorInvalidValue;
+    if (csa && x.sel_m > 1 && x.k % x.sel_m != 0) return hipErrorInvalidValue;
+    gx = x.splits > gx ? x.splits : gx;
+    merge = merge || x.splits > 1;
+  }
+  dim3 grid(gx, (unsigned)q, n);
 #define V4_ATT(D)                                                             \
   do {                                                                        \
-    if (csa) attend_kernel<D, true><<<grid, kAttThreads, 0, st>>>(a);         \
-    else attend_kernel<D, false><<<grid, kAttThreads, 0, st>>>(a);            \
-    if (a.splits > 1)                                                         \
-      attend_merge_kernel<D><<<dim3((a.H + 1024 / (D) - 1) / (1024 / (D)), (unsigned)q), 256, 0, st>>>(a); \
+    if (csa) attend_kernel<D, true><<<grid, kAttThreads, 0, st>>>(ab);        \
+    else attend_kernel<D, false><<<grid, kAttThreads, 0, st>>>(ab);           \
+    if (merge)                                                                \
+      attend_merge_kernel<D><<<dim3((a.H + 1024 / (D) - 1) / (1024 / (D)), (unsigned)q, n), 256, 0, st>>>(ab); \
   } while (0)
   switch (a.D) {
     case 128: V4_ATT(128); break;
@@ -825,6 +874,12 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   }
 #undef V4_ATT
   return hipGetLastError();
+}
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
+  AttendBatch ab{};
+  ab.p[0] = a;
+  return launch_attend_batch(ab, 1, st);
 }
 
 }  // namespace v4

@@ -109,10 +109,11 @@ constexpr int kTopkPartCap = 32;    // leaders a part stores
 constexpr int kTopkMaxParts = 4096; // parts per row (entries <= 4M)
 
 struct TopkPlan {
-  bool parts;        // rows longer than kTopkSel exist: run the part kernel
-  int nparts;        // parts per row (of the longest row)
+  int64_t direct_max;  // rows of at most this many entries are selected directly
+  bool parts;          // longer rows exist: run the part kernel
+  int nparts;          // parts per row (of the longest row)
 };
-TopkPlan topk_plan(int64_t vmax);
+TopkPlan topk_plan(int64_t vmax, int k);
 
 struct TopkArgs {
   const float* scores;     // [B*Tq, score_stride]
@@ -120,6 +121,7 @@ struct TopkArgs {
   int B, Tq;
   int64_t n_entries, q_pos0;
   int m, k;
+  int64_t direct_max;      // TopkPlan::direct_max
   int nparts;
   unsigned* part_tau;      // [rows, nparts] the part's leader threshold (0: none)
   int* part_cnt;           // [rows, nparts] keys >= it in the part
@@ -155,20 +157,36 @@ struct AttendArgs {
   uint16_t* part_o;         // [B*Tq, splits, H, D] bf16, unnormalised (splits > 1)
   float* part_ml;           // [B*Tq, splits, H, 2]  (max, sum)
   int64_t rows_max;         // max rows (entries + window) over the block
-  float* logits2;           // nullptr, or [B*Tq, H, logits_stride]: every row's logit
-                            // times log2(e) (absent rows -inf); logits_stride >= rows
+  float* logits2;           // nullptr, or [B*Tq, logits_stride, 64]: every row's logit
+                            // per head (heads innermost, slots >= H unused) times
+                            // log2(e), absent rows -inf; logits_stride >= rows
                             // rounded up to 128
   int64_t logits_stride;
+  int sel_m;                // CSA: 0 or 1 = topk holds row indices; > 1 = topk
+                            // [B*Tq, k / sel_m] holds blocks of sel_m rows
+                            // (row b sel_m + u), -1 = empty
+  const float* mix_gates;   // nullptr, or [B*Tq, H, 3]: the stored output is
+                            // g1 * this + g0 * mix_o0 + g2 * mix_o2
+  const uint16_t* mix_o0;   // bf16 [B*Tq, H, D]
+  const uint16_t* mix_o2;
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 
+// Up to two problems of the same kind, head count, head dim and query block
+// in one launch (grid layer z runs p[z]); each keeps its own splits and
+// workspace.
+struct AttendBatch {
+  AttendArgs p[2];
+};
+hipError_t launch_attend_batch(const AttendBatch& ab, int n, hipStream_t st);
+
 // Number of key-range splits the attention uses for a problem (shared by
 // the workspace query and the launch so both agree).
-int attend_splits(int B, int Tq, int64_t rows_max, bool csa);
+int attend_splits(int B, int Tq, int64_t rows_max, bool csa, int wg_budget = 256);
 
 // NSA-style variant: block scores from the compressed branch's logits.
 struct NsaBlockScoreArgs {
-  const float* logits2;     // [B*Tq, H, logits_stride], log2 units
+  const float* logits2;     // [B*Tq, logits_stride, 64], log2 units
   const float* lse;         // [B*Tq, H], natural log
   int B, Tq, H;
   int64_t logits_stride;
@@ -179,25 +197,5 @@ struct NsaBlockScoreArgs {
   int64_t score_stride;
 };
 hipError_t launch_nsa_block_score(const NsaBlockScoreArgs& a, hipStream_t st);
-
-// Selected blocks -> their tokens.
-struct NsaExpandArgs {
-  const int32_t* blocks;    // [rows, n_sel], -1 = empty
-  int rows, n_sel, m;
-  int32_t* tok;             // [rows, n_sel * m]
-};
-hipError_t launch_nsa_expand(const NsaExpandArgs& a, hipStream_t st);
-
-// out = g0 o_cmp + g1 o_slc + g2 o_win (bf16 in and out, fp32 arithmetic).
-struct NsaCombineArgs {
-  const uint16_t* o_cmp;    // [rows, D]   (rows = B*Tq*H)
-  const uint16_t* o_slc;
-  const uint16_t* o_win;
-  const float* gates;       // [rows, 3]
-  int64_t rows;
-  int D;
-  uint16_t* out;
-};
-hipError_t launch_nsa_combine(const NsaCombineArgs& a, hipStream_t st);
 
 }  // namespace v4

@@ -1,7 +1,7 @@
-// The small kernels of the NSA-style variant: block scores from the
-// compressed branch's logits, block -> token expansion, and the gated sum of
-// the three branch outputs.  The branches themselves run on the attention
-// kernel (attend.hip).
+// Block scores of the NSA-style variant from the compressed branch's logits.
+// The branches themselves run on the attention kernel (attend.hip), which
+// also expands the selected blocks into their tokens and forms the gated sum
+// of the three branch outputs.
 //
 // Pages: in NSA the block scores come from attention over compressed block
 // representations, the k best blocks are attended at full fidelity beside a
@@ -15,6 +15,7 @@
 // probability of entry j summed over the heads (one shared KV); no sink in any
 // branch.
 
+#include "common.hpp"
 #include "kernels.hpp"
 
 namespace v4 {
@@ -23,75 +24,45 @@ namespace {
 
 constexpr float kLog2eN = 1.4426950408889634f;
 
-// score[q, j] = sum_h 2^(l2[q, h, j] - lse[q, h] log2 e) for j < V_t.  One
-// thread per entry; the head loop reads one coalesced row of logits per head.
+// score[q, j] = sum_h 2^(l2[q, j, h] - lse[q, h] log2 e) for j < V_t.  The
+// heads of one row are 256 contiguous bytes: 16 lanes read them as float4s
+// and add across lanes; a wave covers 16 rows, all its loads in flight
+// together.
 __global__ __launch_bounds__(256) void nsa_block_score_kernel(NsaBlockScoreArgs a) {
-  __shared__ float s_lse2[64];
   const int q = blockIdx.y;
   const int64_t t = a.q_pos0 + q % a.Tq;
   int64_t v = (t + 1) / a.m;
   if (v > a.n_entries) v = a.n_entries;
-  if (threadIdx.x < a.H) s_lse2[threadIdx.x] = a.lse[(int64_t)q * a.H + threadIdx.x] * kLog2eN;
-  __syncthreads();
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= v) return;
-  const float* lp = a.logits2 + (int64_t)q * a.H * a.logits_stride + j;
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
-  int h = 0;
-  for (; h + 4 <= a.H; h += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      s[u] += exp2f(lp[(int64_t)(h + u) * a.logits_stride] - s_lse2[h + u]);
-  }
-  for (; h < a.H; ++h) s[0] += exp2f(lp[(int64_t)h * a.logits_stride] - s_lse2[h]);
-  a.score[(int64_t)q * a.score_stride + j] = (s[0] + s[1]) + (s[2] + s[3]);
-}
-
-// tok[q, i m + u] = blk[q, i] m + u, or -1 where the block slot is empty.
-__global__ __launch_bounds__(256) void nsa_expand_kernel(NsaExpandArgs a) {
-  const int q = blockIdx.y;
-  const int n = a.n_sel * a.m;
-  const int x = blockIdx.x * 256 + threadIdx.x;
-  if (x >= n) return;
-  const int i = x / a.m, u = x - i * a.m;
-  const int32_t blk = a.blocks[(int64_t)q * a.n_sel + i];
-  a.tok[(int64_t)q * n + x] = blk >= 0 ? blk * a.m + u : -1;
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-  // round to nearest even (finite inputs)
-  auto rn = [](float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  };
-  return rn(x) | (rn(y) << 16);
-}
-
-// out = g0 o_cmp + g1 o_slc + g2 o_win in fp32, stored as bf16.  One thread
-// per 8 dims of one (query, head).
-__global__ __launch_bounds__(256) void nsa_combine_kernel(NsaCombineArgs a) {
-  const int64_t n8 = (int64_t)a.rows * a.D / 8;
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (x >= n8) return;
-  const int64_t qh = x / (a.D / 8);
-  const float g0 = a.gates[3 * qh], g1 = a.gates[3 * qh + 1], g2 = a.gates[3 * qh + 2];
-  const uint4 u0 = reinterpret_cast<const uint4*>(a.o_cmp)[x];
-  const uint4 u1 = reinterpret_cast<const uint4*>(a.o_slc)[x];
-  const uint4 u2 = reinterpret_cast<const uint4*>(a.o_win)[x];
-  const uint32_t w0[4] = {u0.x, u0.y, u0.z, u0.w};
-  const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w};
-  const uint32_t w2[4] = {u2.x, u2.y, u2.z, u2.w};
-  uint32_t r[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hq = lane & 15, rsub = lane >> 4;   // heads 4 hq .. 4 hq + 3; row in a group of 4
+  const int64_t j0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  if (j0 >= v) return;
+  float l2s[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float lo = fmaf(g2, bf16_lo(w2[e]), fmaf(g1, bf16_lo(w1[e]), g0 * bf16_lo(w0[e])));
-    const float hi = fmaf(g2, bf16_hi(w2[e]), fmaf(g1, bf16_hi(w1[e]), g0 * bf16_hi(w0[e])));
-    r[e] = pack2(lo, hi);
+    const int h = 4 * hq + e;
+    l2s[e] = h < a.H ? a.lse[(int64_t)q * a.H + h] * kLog2eN : 0.f;
   }
-  reinterpret_cast<uint4*>(a.out)[x] = uint4{r[0], r[1], r[2], r[3]};
+  const float* lp = a.logits2 + (int64_t)q * a.logits_stride * 64 + 4 * hq;
+  f32x4 x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t j = j0 + 4 * u + rsub;
+    x[u] = j < v ? *reinterpret_cast<const f32x4*>(lp + j * 64) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * hq + e < a.H) s += exp2f(x[u][e] - l2s[e]);   // slots >= H hold no logit
+    s += __shfl_xor(s, 8);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 1);
+    const int64_t j = j0 + 4 * u + rsub;
+    if (hq == 0 && j < v) a.score[(int64_t)q * a.score_stride + j] = s;
+  }
 }
 
 }  // namespace
@@ -99,21 +70,7 @@ __global__ __launch_bounds__(256) void nsa_combine_kernel(NsaCombineArgs a) {
 hipError_t launch_nsa_block_score(const NsaBlockScoreArgs& a, hipStream_t st) {
   const int64_t q = (int64_t)a.B * a.Tq;
   if (q == 0 || a.vmax == 0) return hipSuccess;
-  nsa_block_score_kernel<<<dim3((unsigned)((a.vmax + 255) / 256), (unsigned)q), 256, 0, st>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_nsa_expand(const NsaExpandArgs& a, hipStream_t st) {
-  const int n = a.n_sel * a.m;
-  if (a.rows == 0 || n == 0) return hipSuccess;
-  nsa_expand_kernel<<<dim3((unsigned)((n + 255) / 256), (unsigned)a.rows), 256, 0, st>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_nsa_combine(const NsaCombineArgs& a, hipStream_t st) {
-  const int64_t n8 = (int64_t)a.rows * a.D / 8;
-  if (n8 == 0) return hipSuccess;
-  nsa_combine_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(a);
+  nsa_block_score_kernel<<<dim3((unsigned)((a.vmax + 63) / 64), (unsigned)q), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

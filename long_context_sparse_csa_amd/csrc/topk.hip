@@ -47,9 +47,14 @@ static_assert(kSelRounds * kSelWaves <= kSelThreads, "one scan entry per thread"
 constexpr int kBucketsPerThread = kHistBins / kSelThreads;
 static_assert(kTopkPartLen == 16 * 64, "a part is 16 keys per lane of one wave");
 
-TopkPlan topk_plan(int64_t vmax) {
+// Rows up to kTopkSel keys are selected by one workgroup straight from the
+// scores; for a small k a row of more than 2048 keys is spread over part
+// waves first (each part's leaders hold every one of its keys in the row's
+// top 16, so the per-row step sees ~32 keys a part instead of 1024).
+TopkPlan topk_plan(int64_t vmax, int k) {
   TopkPlan p;
-  p.parts = vmax > kTopkSel;
+  p.direct_max = k <= 32 ? 2048 : kTopkSel;
+  p.parts = vmax > p.direct_max;
   p.nparts = p.parts ? (int)((vmax + kTopkPartLen - 1) / kTopkPartLen) : 0;
   return p;
 }
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(256) void topk_part_kernel(TopkArgs a) {
   const int p = blockIdx.x * 4 + wave;
   if (p >= a.nparts) return;
   const int64_t V = visible_of(a, qr);
-  if (V <= kTopkSel) return;   // such a row is selected directly
+  if (V <= a.direct_max) return;   // such a row is selected directly
   const int64_t base = (int64_t)p * kTopkPartLen;
   unsigned x = 0u, over = 0u;
   int cnt = 0;
@@ -350,13 +355,25 @@ __device__ __forceinline__ void topk_select_general(const TopkArgs& a, unsigned*
   };
   unsigned lower;
 
-  if (V <= kTopkSel) {
+  if (V <= a.direct_max) {
     // the whole row in LDS
     const int len = (int)(V > 0 ? V : 0);
     const float* src = a.scores + qr * a.score_stride;
-    for (int i = tid; i < len; i += kSelThreads) {
-      s_key[i] = score_key(src[i]);
-      s_idx[i] = i;
+    // every load in flight before the first use (a loop of load -> store
+    // would wait out the memory latency once per round)
+    float sv[kSelRounds];
+#pragma unroll
+    for (int r = 0; r < kSelRounds; ++r) {
+      const int i = r * kSelThreads + tid;
+      sv[r] = i < len ? src[i] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < kSelRounds; ++r) {
+      const int i = r * kSelThreads + tid;
+      if (i < len) {
+        s_key[i] = score_key(sv[r]);
+        s_idx[i] = i;
+      }
     }
     __syncthreads();
     pad(select(len, &lower, nullptr, topk));
@@ -529,7 +546,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   const int64_t qr = blockIdx.x;
   const int64_t V = visible_of(a, qr);
   const int np = a.nparts;
-  if (V > kTopkSel && np <= kSelThreads) {
+  if (V > a.direct_max && np <= kSelThreads) {
     unsigned* s_key = smem;                                   // [kTopkSel + 64]
     unsigned* s_hist = smem + kTopkSel;                       // [kHistBins]
     int* s_idx = reinterpret_cast<int*>(s_hist + kHistBins);  // [kTopkSel + 64]

@@ -222,11 +222,18 @@ SCORE_ROWS = [
     ("nan_heavy", 50000, 1024),    # 3% valid keys: parts short of leaders
     ("signed_zero_inf", 40000, 512),  # -0/+0 ties, +-inf
     ("small_row", 9000, 256),      # one workgroup holds the whole row
+    # k <= 32: rows above 2048 keys go through the part leaders
+    ("random_small_k", 16384, 16),
+    ("all_equal_small_k", 5000, 16),    # every part overflows: re-read
+    ("ascending_small_k", 3000, 32),    # the top-k fills the last part's leaders
+    ("nan_heavy_small_k", 20000, 4),
+    ("small_row_small_k", 2048, 8),     # the longest row selected directly
 ]
 
 
 def _score_row(name, V, seed):
     g = np.random.default_rng(seed)
+    name = name.replace("_small_k", "")
     if name == "random":
         return g.standard_normal(V).astype(np.float32)
     if name == "all_equal":
