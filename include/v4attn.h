@@ -371,6 +371,62 @@ int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries,
                       float* block_score, void* ws, size_t ws_bytes,
                       void* stream);
 
+/*
+ * v4attn_csa_attend_backward / v4attn_hca_attend_backward -- gradients of
+ * v4attn_csa_attend / v4attn_hca_attend.
+ *
+ * Defines: the attention step is trained end to end except the top-k choice,
+ * a hard selection with no gradient ("DeepSeek-V4, explained", step 7); the
+ * selected set and the window are therefore constants here.  The chain rule
+ * of the forward's definition (q~ = RoPE_t(RMSNorm_gamma_q(q)), l = scale
+ * q~ . x, one softmax with the sink, out = RoPE_{-t}(sum p x)):
+ *   do = RoPE_t(dout),  D_h = dout_h . out_h,  dl_x = p_x (do . x - D_h),
+ *   d x     += scale sum_h dl_hx q~_h + sum_h p_hx do_h   (key and value)
+ *   d sink_h += -exp(sink_h - lse_h) D_h
+ *   dq       = RMSNorm backward of RoPE_t^T(scale sum_x dl_x x);
+ *   d gamma_q += its gamma part.
+ * A row's gradient is taken with respect to its stored (dequantised) value.
+ *
+ *   q, entries, topk, win, gamma_q, sink, sizes: as the forward call
+ *   out  bf16 [B, Tq, H, D], lse f32 [B, Tq, H]: the forward's outputs
+ *   dout bf16 [B, Tq, H, D]: gradient of out (16-byte aligned)
+ *   dq   f32  [B, Tq, H, D] out (written, 16-byte aligned)
+ *   d_entries f32 [B, Ncap, D], d_win f32 [B, Tq+W-1, D]: ADDED to (the
+ *            caller zeroes them); required when Ncap > 0 / W > 0
+ *   d_sink f32 [H], d_gamma_q f32 [D]: added to; nullable
+ *   ws / ws_bytes >= the matching *_backward_workspace(...) bytes
+ * Arithmetic: every attended row is gathered as bf16 (exact); q~, do and the
+ * probabilities and dl enter bf16 matrix-core products with fp32
+ * accumulation.  Row gradients use fp32 atomics, so their summation order
+ * (and last bits) vary from run to run when rows are shared.
+ */
+size_t v4attn_csa_attend_backward_workspace(int B, int Tq, int H, int D,
+                                            int k, int W);
+int v4attn_csa_attend_backward(const uint16_t* q, const uint8_t* entries,
+                               const int32_t* topk, const uint8_t* win,
+                               const float* gamma_q, const float* sink,
+                               int B, int Tq, int H, int D, int R,
+                               int64_t Ncap, int k, int W, int64_t q_pos0,
+                               float scale, float eps, float rope_base,
+                               const uint16_t* out, const float* lse,
+                               const uint16_t* dout, float* dq,
+                               float* d_entries, float* d_win, float* d_sink,
+                               float* d_gamma_q, void* ws, size_t ws_bytes,
+                               void* stream);
+size_t v4attn_hca_attend_backward_workspace(int B, int Tq, int H, int D,
+                                            int64_t n_entries, int m,
+                                            int64_t q_pos0, int W);
+int v4attn_hca_attend_backward(const uint16_t* q, const uint8_t* entries,
+                               const uint8_t* win, const float* gamma_q,
+                               const float* sink, int B, int Tq, int H, int D,
+                               int R, int64_t Ncap, int64_t n_entries, int m,
+                               int W, int64_t q_pos0, float scale, float eps,
+                               float rope_base, const uint16_t* out,
+                               const float* lse, const uint16_t* dout,
+                               float* dq, float* d_entries, float* d_win,
+                               float* d_sink, float* d_gamma_q, void* ws,
+                               size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libv4attn.so")
 
-SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "indexer_fp8.hip", "indexer_mxfp4.hip", "topk.hip", "attend.hip", "nsa.hip"]
+SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "indexer_fp8.hip", "indexer_mxfp4.hip", "topk.hip", "attend.hip", "nsa.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

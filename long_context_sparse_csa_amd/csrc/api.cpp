@@ -731,4 +731,99 @@ int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
                     "NSA selected branch launch");
 }
 
+namespace {
+
+// Attention backward: queries are processed in chunks whose per-query
+// buffers (gathered rows, [S; dP], [scale dL; P], ...) fit about 1 GiB.
+int bwd_chunk(int64_t nq, int D, int64_t np) {
+  const size_t per = v4::bwd_query_bytes(D, np);
+  int64_t c = (int64_t)(((size_t)1 << 30) / per);
+  if (c < 1) c = 1;
+  if (c > 64) c = 64;
+  return (int)(c < nq ? c : (nq > 0 ? nq : 1));
+}
+
+size_t bwd_ws(int B, int Tq, int D, int64_t rows_max) {
+  const int64_t nq = (int64_t)B * Tq;
+  const int64_t np = v4::bwd_rows_padded(rows_max > 0 ? rows_max : 1);
+  return (size_t)bwd_chunk(nq, D, np) * v4::bwd_query_bytes(D, np);
+}
+
+int run_backward(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
+                 const uint8_t* win, const float* gamma_q, const float* sink, int B, int Tq, int H,
+                 int D, int R, int64_t Ncap, int k, int64_t n_entries, int m, int W,
+                 int64_t q_pos0, float scale, float eps, float rope_base, const uint16_t* out,
+                 const float* lse, const uint16_t* dout, float* dq, float* d_entries,
+                 float* d_win, float* d_sink, float* d_gamma_q, int64_t rows_max, void* ws,
+                 size_t ws_bytes, void* stream) {
+  if (!out || !lse || !dout || !dq) return fail(V4ATTN_EINVAL, "null out, lse, dout or dq");
+  if (Ncap > 0 && !d_entries) return fail(V4ATTN_EINVAL, "null d_entries with Ncap > 0");
+  if (W > 0 && !d_win) return fail(V4ATTN_EINVAL, "null d_win with W > 0");
+  if (!aligned16(dout) || !aligned16(dq)) return fail(V4ATTN_EINVAL, "dout and dq must be 16-byte aligned");
+  const size_t need = bwd_ws(B, Tq, D, rows_max);
+  if (!ws || ws_bytes < need)
+    return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
+  const int64_t nq = (int64_t)B * Tq;
+  if (nq == 0) return hip_status(hipSuccess, "");
+  v4::BwdArgs a{};
+  a.q = q; a.entries = entries; a.topk = topk; a.win = win; a.gamma_q = gamma_q; a.sink = sink;
+  a.out = out; a.lse = lse; a.dout = dout;
+  a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R; a.Ncap = Ncap; a.k = k; a.n_entries = n_entries;
+  a.m = m; a.W = W; a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps;
+  a.rope = v4::rope_turns(rope_base, R);
+  a.np = v4::bwd_rows_padded(rows_max > 0 ? rows_max : 1);
+  a.dq = dq; a.d_entries = d_entries; a.d_win = d_win; a.d_sink = d_sink; a.d_gamma_q = d_gamma_q;
+  return hip_status(v4::launch_attend_backward(a, bwd_chunk(nq, D, a.np), ws, (hipStream_t)stream),
+                    "attention backward launch");
+}
+
+}  // namespace
+
+size_t v4attn_csa_attend_backward_workspace(int B, int Tq, int H, int D, int k, int W) {
+  if (B < 0 || Tq < 0 || H < 1 || D < 1 || k < 1 || W < 0) return 0;
+  return bwd_ws(B, Tq, D, (int64_t)k + W);
+}
+
+int v4attn_csa_attend_backward(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
+                               const uint8_t* win, const float* gamma_q, const float* sink, int B,
+                               int Tq, int H, int D, int R, int64_t Ncap, int k, int W,
+                               int64_t q_pos0, float scale, float eps, float rope_base,
+                               const uint16_t* out, const float* lse, const uint16_t* dout,
+                               float* dq, float* d_entries, float* d_win, float* d_sink,
+                               float* d_gamma_q, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_attend_common(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, W,
+                                   q_pos0, scale, eps, rope_base, out))
+    return st;
+  if (!topk) return fail(V4ATTN_EINVAL, "null topk");
+  if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
+  return run_backward(q, entries, topk, win, gamma_q, sink, B, Tq, H, D, R, Ncap, k, 0, 1, W,
+                      q_pos0, scale, eps, rope_base, out, lse, dout, dq, d_entries, d_win,
+                      d_sink, d_gamma_q, (int64_t)k + W, ws, ws_bytes, stream);
+}
+
+size_t v4attn_hca_attend_backward_workspace(int B, int Tq, int H, int D, int64_t n_entries, int m,
+                                            int64_t q_pos0, int W) {
+  if (B < 0 || Tq < 0 || H < 1 || D < 1 || n_entries < 0 || m < 1 || q_pos0 < 0 || W < 0) return 0;
+  return bwd_ws(B, Tq, D, vmax_of(Tq, n_entries, q_pos0, m) + W);
+}
+
+int v4attn_hca_attend_backward(const uint16_t* q, const uint8_t* entries, const uint8_t* win,
+                               const float* gamma_q, const float* sink, int B, int Tq, int H,
+                               int D, int R, int64_t Ncap, int64_t n_entries, int m, int W,
+                               int64_t q_pos0, float scale, float eps, float rope_base,
+                               const uint16_t* out, const float* lse, const uint16_t* dout,
+                               float* dq, float* d_entries, float* d_win, float* d_sink,
+                               float* d_gamma_q, void* ws, size_t ws_bytes, void* stream) {
+  if (int st = check_attend_common(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, W,
+                                   q_pos0, scale, eps, rope_base, out))
+    return st;
+  if (n_entries < 0 || n_entries > Ncap) return fail(V4ATTN_EINVAL, "need 0 <= n_entries <= Ncap");
+  if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
+  return run_backward(q, entries, nullptr, win, gamma_q, sink, B, Tq, H, D, R, Ncap, 0, n_entries,
+                      m, W, q_pos0, scale, eps, rope_base, out, lse, dout, dq, d_entries, d_win,
+                      d_sink, d_gamma_q, vmax_of(Tq, n_entries, q_pos0, m) + W, ws, ws_bytes,
+                      stream);
+}
+
 }  // extern "C"

@@ -1,0 +1,367 @@
+// Backward of the core attention (CSA and HCA): gradients with respect to
+// the raw queries, every attended row (entries and window rows), the sinks
+// and gamma_q.
+//
+// Pages: the attention step is trained end to end except the hard top-k
+// choice ("DeepSeek-V4, explained", step 7).  The forward is the one of
+// attend.hip: q~ = RoPE_t(RMSNorm(q)), one softmax over the rows and the
+// sink, out = RoPE_{-t}(sum p x).
+//
+// Design: per chunk of queries, every attended row is gathered once as bf16
+// (the E4M3 and bf16 stored values are exact in bf16) into X [q, n, D]; the
+// query side [q~; do] (do = RoPE_t(dout)) is Y [q, 128, D] (64 head slots
+// each).  Then, per query, three batched bf16 matrix-core products
+//     [S; dP]   = Y X^T                     (logits / scale, and do . x)
+//     dq~       = (scale dL) X
+//     dX        = [scale dL; P]^T Y        (key and value paths at once)
+// with P = exp(scale S - lse) and dL = P (dP - D), D_h = dout_h . out_h, in
+// between (an elementwise kernel).  dX rows are added into the caller's
+// row gradients with atomics (a row may be attended by many queries); dq~
+// goes back through RoPE_t and the RMSNorm.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace v4 {
+
+namespace {
+
+constexpr float kL2e = 1.4426950408889634f;
+constexpr int kLdsK = 40;   // padded k stride of the staged tiles (bf16)
+
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {   // round to nearest even (finite)
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// C[z] = alpha A[z] B[z] on 64 x 64 tiles, K in steps of 32 (all multiples:
+// the caller pads).  A is M x K (AT: stored K x M), B is K x N (BT: stored
+// N x K); bf16 in, fp32 accumulate.  Four waves, 32 x 32 each.
+template <bool AT, bool BT>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[64][kLdsK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[64][kLdsK];
+  const int z = blockIdx.z;
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  const uint16_t* A = g.a + (int64_t)z * g.a_batch;
+  const uint16_t* B = g.b + (int64_t)z * g.b_batch;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, c = lane & 15, gq = lane >> 4;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // a tile [64 rows][32 k] from a row-major (rows x k) matrix, or from a
+  // (k x rows) one, transposed on the way into LDS
+  auto stage = [&](uint16_t (*s)[kLdsK], const uint16_t* p, int64_t ld, int r0, int k0, bool tr) {
+    if (!tr) {
+      const int r = tid >> 2, ch = tid & 3;
+      *reinterpret_cast<uint4*>(&s[r][8 * ch]) =
+          *reinterpret_cast<const uint4*>(p + (int64_t)(r0 + r) * ld + k0 + 8 * ch);
+    } else {
+      const int kk = tid >> 3, ch = tid & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(p + (int64_t)(k0 + kk) * ld + r0 + 8 * ch);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[8 * ch + 2 * e][kk] = (uint16_t)(w[e] & 0xFFFFu);
+        s[8 * ch + 2 * e + 1][kk] = (uint16_t)(w[e] >> 16);
+      }
+    }
+  };
+  for (int k0 = 0; k0 < g.K; k0 += 32) {
+    stage(sA, A, g.lda, m0, k0, AT);
+    stage(sB, B, g.ldb, n0, k0, !BT);
+    __syncthreads();
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(&sA[wm * 32 + 16 * i + c][8 * gq]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8*>(&sB[wn * 32 + 16 * j + c][8 * gq]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    __syncthreads();
+  }
+  // lane (c, gq) holds rows 4 gq + v, column c of each 16 x 16 block
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * 32 + 16 * i + 4 * gq + v;
+        const int n = n0 + wn * 32 + 16 * j + c;
+        const float x = g.alpha * acc[i][j][v];
+        if (!g.rowmap) {
+          g.c[(int64_t)z * g.c_batch + (int64_t)m * g.ldc + n] = x;
+        } else {
+          const int64_t r = g.rowmap[(int64_t)z * g.rowmap_batch + m];
+          if (r >= 0) atomicAdd(g.c + r * g.ldc + n, x);
+          else if (r <= -2) atomicAdd(g.c2 + (-2 - r) * g.ldc + n, x);
+        }
+      }
+}
+
+// X[qc, x, :] = the query's row x as bf16 (zeros if absent), rowmap = where
+// its gradient goes: entry b Ncap + j (>= 0), window row -2 - (b (Tq+W-1) + r),
+// or -1.  One wave per row slot.
+__global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a, int q0) {
+  const int qc = blockIdx.y, qr = q0 + qc;
+  const int b = qr / a.Tq, r = qr % a.Tq;
+  const int64_t t = a.q_pos0 + r;
+  const int x = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (x >= a.np) return;
+  int64_t n_ent;
+  if (a.topk) {
+    n_ent = a.k;
+  } else {
+    const int64_t v = (t + 1) / a.m;
+    n_ent = v < a.n_entries ? v : a.n_entries;
+  }
+  const int64_t lo = t - a.W + 1 > 0 ? t - a.W + 1 : 0;
+  const int64_t n_win = a.W > 0 ? t - lo + 1 : 0;
+  const int ROW = a.D + a.R;
+  const uint8_t* src = nullptr;
+  int64_t map = -1;
+  if (x < n_ent) {
+    const int64_t j = a.topk ? (int64_t)a.topk[(int64_t)qr * a.k + x] : (int64_t)x;
+    if (j >= 0 && j < a.Ncap) {
+      src = a.entries + ((int64_t)b * a.Ncap + j) * ROW;
+      map = (int64_t)b * a.Ncap + j;
+    }
+  } else if (x < n_ent + n_win) {
+    const int64_t wrow = lo + (x - n_ent) - (a.q_pos0 - (a.W - 1));
+    const int64_t grow = (int64_t)b * (a.Tq + a.W - 1) + wrow;
+    src = a.win + grow * ROW;
+    map = -2 - grow;
+  }
+  uint16_t* dst = a.X + ((int64_t)qc * a.np + x) * a.D;
+  const int E = a.D - a.R;
+  for (int d = lane; d < a.D; d += 64) {
+    float v = 0.f;
+    if (src) {
+      if (d < E) {
+        v = __builtin_amdgcn_cvt_pk_f32_fp8((int)src[d], false)[0];
+      } else {
+        v = bf16f(reinterpret_cast<const uint16_t*>(src + E)[d - E]);
+      }
+    }
+    dst[d] = f2bf(v);
+  }
+  if (lane == 0) a.rowmap[(int64_t)qc * a.np + x] = map;
+}
+
+// Y[qc] = [q~ (64 head slots); do = RoPE_t(dout) (64 slots)] as bf16, Dh =
+// dout . out, dsink += -p_sink Dh.  One wave per head; lane holds the dim
+// pairs (2 lane + 128 e, +1).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int q0) {
+  const int qc = blockIdx.y, qr = q0 + qc;
+  const int r = qr % a.Tq;
+  const int64_t t = a.q_pos0 + r;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  uint16_t* yq = a.Y + ((int64_t)qc * 128 + h) * a.D;
+  uint16_t* yd = a.Y + ((int64_t)qc * 128 + 64 + h) * a.D;
+  if (h >= a.H) {
+    for (int d = lane; d < a.D; d += 64) yq[d] = yd[d] = 0;
+    return;
+  }
+  const uint16_t* qp = a.q + ((int64_t)qr * a.H + h) * a.D;
+  const uint16_t* gp = a.dout + ((int64_t)qr * a.H + h) * a.D;
+  const uint16_t* op = a.out + ((int64_t)qr * a.H + h) * a.D;
+  const int NP = a.D / 128;   // pairs per lane
+  float ss = 0.f, dd = 0.f;
+  for (int e = 0; e < NP; ++e) {
+    const int d = 2 * lane + 128 * e;
+    const float q0v = bf16f(qp[d]), q1v = bf16f(qp[d + 1]);
+    ss += q0v * q0v + q1v * q1v;
+    dd += bf16f(gp[d]) * bf16f(op[d]) + bf16f(gp[d + 1]) * bf16f(op[d + 1]);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    ss += __shfl_xor(ss, o);
+    dd += __shfl_xor(dd, o);
+  }
+  const float rsn = 1.0f / sqrtf(ss / (float)a.D + a.eps);
+  for (int e = 0; e < NP; ++e) {
+    const int d = 2 * lane + 128 * e;
+    float x0 = a.gamma_q[d] * (bf16f(qp[d]) * rsn), x1 = a.gamma_q[d + 1] * (bf16f(qp[d + 1]) * rsn);
+    float g0 = bf16f(gp[d]), g1 = bf16f(gp[d + 1]);
+    if (d >= a.D - a.R) {
+      float cs, sn;
+      rope_cos_sin(t, a.rope.t[(d - (a.D - a.R)) >> 1], &cs, &sn);
+      const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+      x0 = y0;
+      x1 = y1;
+      const float u0 = g0 * cs - g1 * sn, u1 = g0 * sn + g1 * cs;   // do = RoPE_t(dout)
+      g0 = u0;
+      g1 = u1;
+    }
+    yq[d] = f2bf(x0);
+    yq[d + 1] = f2bf(x1);
+    yd[d] = f2bf(g0);
+    yd[d + 1] = f2bf(g1);
+  }
+  if (lane == 0) {
+    a.Dh[(int64_t)qc * 64 + h] = dd;
+    if (a.sink && a.d_sink) {
+      const float lse = a.lse[(int64_t)qr * a.H + h];
+      const float pz = lse == -INFINITY ? 0.f : expf(a.sink[h] - lse);
+      atomicAdd(a.d_sink + h, -pz * dd);
+    }
+  }
+}
+
+// T[qc] = [scale dL; P] (bf16, 64 head slots each) from [S; dP]: P =
+// exp(scale S - lse), dL = P (dP - Dh); absent rows and head slots >= H: 0.
+__global__ __launch_bounds__(256) void bwd_softmax_kernel(BwdArgs a, int q0) {
+  const int qc = blockIdx.z, qr = q0 + qc;
+  const int h = blockIdx.y;
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= a.np) return;
+  const float* sp = a.SP + (int64_t)qc * 128 * a.np;
+  float p = 0.f, dl = 0.f;
+  if (h < a.H && a.rowmap[(int64_t)qc * a.np + x] != -1) {
+    const float lse = a.lse[(int64_t)qr * a.H + h];
+    if (lse != -INFINITY) {
+      p = exp2f((a.scale * sp[(int64_t)h * a.np + x] - lse) * kL2e);
+      dl = p * (sp[(int64_t)(64 + h) * a.np + x] - a.Dh[(int64_t)qc * 64 + h]);
+    }
+  }
+  uint16_t* tp = a.T + (int64_t)qc * 128 * a.np;
+  tp[(int64_t)h * a.np + x] = f2bf(a.scale * dl);
+  tp[(int64_t)(64 + h) * a.np + x] = f2bf(p);
+}
+
+// dq = RMSNorm backward of RoPE_t^T(dq~); d_gamma_q += sum over heads.  One
+// workgroup per query, wave w takes heads w, w+4, ..; lane holds dim pairs.
+__global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a, int q0) {
+  __shared__ float s_dg[4][512];
+  const int qc = blockIdx.x, qr = q0 + qc;
+  const int r = qr % a.Tq;
+  const int64_t t = a.q_pos0 + r;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int NP = a.D / 128;
+  float dg[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dg[i] = 0.f;
+  for (int h = wave; h < a.H; h += 4) {
+    const uint16_t* qp = a.q + ((int64_t)qr * a.H + h) * a.D;
+    const float* gq = a.DQT + ((int64_t)qc * 64 + h) * a.D;
+    float ss = 0.f;
+    for (int e = 0; e < NP; ++e) {
+      const int d = 2 * lane + 128 * e;
+      ss += bf16f(qp[d]) * bf16f(qp[d]) + bf16f(qp[d + 1]) * bf16f(qp[d + 1]);
+    }
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const float rsn = 1.0f / sqrtf(ss / (float)a.D + a.eps);
+    float gx[8], xq[8];
+    float dot = 0.f;
+    for (int e = 0; e < NP; ++e) {
+      const int d = 2 * lane + 128 * e;
+      float u0 = gq[d], u1 = gq[d + 1];
+      if (d >= a.D - a.R) {   // RoPE_t transposed = rotation by -t
+        float cs, sn;
+        rope_cos_sin(t, a.rope.t[(d - (a.D - a.R)) >> 1], &cs, &sn);
+        const float v0 = u0 * cs + u1 * sn, v1 = -u0 * sn + u1 * cs;
+        u0 = v0;
+        u1 = v1;
+      }
+      xq[2 * e] = bf16f(qp[d]);
+      xq[2 * e + 1] = bf16f(qp[d + 1]);
+      dg[2 * e] += u0 * xq[2 * e] * rsn;
+      dg[2 * e + 1] += u1 * xq[2 * e + 1] * rsn;
+      gx[2 * e] = u0 * a.gamma_q[d];
+      gx[2 * e + 1] = u1 * a.gamma_q[d + 1];
+      dot += gx[2 * e] * xq[2 * e] + gx[2 * e + 1] * xq[2 * e + 1];
+    }
+    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+    const float c3 = dot * rsn * rsn * rsn / (float)a.D;
+    float* dqp = a.dq + ((int64_t)qr * a.H + h) * a.D;
+    for (int e = 0; e < NP; ++e) {
+      const int d = 2 * lane + 128 * e;
+      dqp[d] = gx[2 * e] * rsn - xq[2 * e] * c3;
+      dqp[d + 1] = gx[2 * e + 1] * rsn - xq[2 * e + 1] * c3;
+    }
+  }
+  if (!a.d_gamma_q) return;
+  for (int e = 0; e < NP; ++e) {
+    const int d = 2 * lane + 128 * e;
+    s_dg[wave][d] = dg[2 * e];
+    s_dg[wave][d + 1] = dg[2 * e + 1];
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < a.D; d += 256)
+    atomicAdd(a.d_gamma_q + d, s_dg[0][d] + s_dg[1][d] + s_dg[2][d] + s_dg[3][d]);
+}
+
+template <bool AT, bool BT>
+hipError_t gemm(const GemmArgs& g, int M, int N, int Z, hipStream_t st) {
+  gemm_bf16_kernel<AT, BT><<<dim3(N / 64, M / 64, Z), 256, 0, st>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t bwd_rows_padded(int64_t rows_max) { return (rows_max + 63) / 64 * 64; }
+
+size_t bwd_query_bytes(int D, int64_t np) {
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  return al((size_t)np * D * 2)          // X
+         + al((size_t)np * 8)            // rowmap
+         + al((size_t)128 * D * 2)       // Y
+         + al((size_t)64 * 4)            // Dh
+         + al((size_t)128 * np * 4)      // [S; dP]
+         + al((size_t)128 * np * 2)      // T
+         + al((size_t)64 * D * 4);       // dq~
+}
+
+hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t st) {
+  const int nq = a.B * a.Tq;
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  const int64_t np = a.np;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  a.X = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * np * a.D * 2);
+  a.rowmap = reinterpret_cast<int64_t*>(w);    w += al((size_t)qchunk * np * 8);
+  a.Y = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * 128 * a.D * 2);
+  a.Dh = reinterpret_cast<float*>(w);          w += al((size_t)qchunk * 64 * 4);
+  a.SP = reinterpret_cast<float*>(w);          w += al((size_t)qchunk * 128 * np * 4);
+  a.T = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * 128 * np * 2);
+  a.DQT = reinterpret_cast<float*>(w);
+  for (int q0 = 0; q0 < nq; q0 += qchunk) {
+    const int qc = nq - q0 < qchunk ? nq - q0 : qchunk;
+    bwd_gather_kernel<<<dim3((unsigned)((np + 3) / 4), qc), 256, 0, st>>>(a, q0);
+    bwd_prep_kernel<<<dim3(16, qc), 256, 0, st>>>(a, q0);
+    // [S; dP] = Y X^T: M = 128, N = np, K = D
+    GemmArgs g1{};
+    g1.a = a.Y; g1.lda = a.D; g1.a_batch = 128 * (int64_t)a.D;
+    g1.b = a.X; g1.ldb = a.D; g1.b_batch = np * a.D;
+    g1.c = a.SP; g1.ldc = np; g1.c_batch = 128 * np; g1.K = a.D; g1.alpha = 1.f;
+    hipError_t e = gemm<false, true>(g1, 128, (int)np, qc, st);
+    if (e != hipSuccess) return e;
+    bwd_softmax_kernel<<<dim3((unsigned)((np + 255) / 256), 64, qc), 256, 0, st>>>(a, q0);
+    // dq~ = (scale dL) X: M = 64, N = D, K = np
+    GemmArgs g2{};
+    g2.a = a.T; g2.lda = np; g2.a_batch = 128 * np;
+    g2.b = a.X; g2.ldb = a.D; g2.b_batch = np * a.D;
+    g2.c = a.DQT; g2.ldc = a.D; g2.c_batch = 64 * (int64_t)a.D; g2.K = (int)np; g2.alpha = 1.f;
+    e = gemm<false, false>(g2, 64, a.D, qc, st);
+    if (e != hipSuccess) return e;
+    // dX = T^T Y, added into the row gradients: M = np, N = D, K = 128
+    GemmArgs g3{};
+    g3.a = a.T; g3.lda = np; g3.a_batch = 128 * np;
+    g3.b = a.Y; g3.ldb = a.D; g3.b_batch = 128 * (int64_t)a.D;
+    g3.c = a.d_entries; g3.c2 = a.d_win; g3.ldc = a.D; g3.K = 128; g3.alpha = 1.f;
+    g3.rowmap = a.rowmap; g3.rowmap_batch = np;
+    e = gemm<true, false>(g3, (int)np, a.D, qc, st);
+    if (e != hipSuccess) return e;
+    bwd_q_kernel<<<qc, 256, 0, st>>>(a, q0);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace v4

@@ -198,4 +198,60 @@ struct NsaBlockScoreArgs {
 };
 hipError_t launch_nsa_block_score(const NsaBlockScoreArgs& a, hipStream_t st);
 
+// Batched bf16 matrix-core product C[z] = alpha A[z] B[z] (fp32 out; M, N
+// multiples of 64, K of 32).  With rowmap, row m of C[z] is instead added
+// (atomically) into c row rowmap[z, m] (>= 0), c2 row -2 - rowmap (<= -2),
+// or dropped (-1).
+struct GemmArgs {
+  const uint16_t* a;
+  int64_t lda, a_batch;
+  const uint16_t* b;
+  int64_t ldb, b_batch;
+  float* c;
+  float* c2;
+  int64_t ldc, c_batch;
+  const int64_t* rowmap;
+  int64_t rowmap_batch;
+  int K;
+  float alpha;
+};
+
+// Attention backward (both kinds: CSA when topk != nullptr).
+struct BwdArgs {
+  const uint16_t* q;         // [B, Tq, H, D]
+  const uint8_t* entries;    // [B, Ncap, D+R]
+  const int32_t* topk;       // [B, Tq, k] or nullptr (dense visible entries)
+  const uint8_t* win;        // [B, Tq+W-1, D+R]
+  const float* gamma_q;      // [D]
+  const float* sink;         // [H] or nullptr
+  const uint16_t* out;       // forward output [B, Tq, H, D]
+  const float* lse;          // forward lse [B, Tq, H]
+  const uint16_t* dout;      // [B, Tq, H, D]
+  int B, Tq, H, D, R;
+  int64_t Ncap;
+  int k;
+  int64_t n_entries;
+  int m, W;
+  int64_t q_pos0;
+  float scale, eps;
+  RopeTurns rope;
+  int64_t np;                // row slots per query, padded to 64
+  float* dq;                 // [B, Tq, H, D] (written)
+  float* d_entries;          // [B, Ncap, D] (added)
+  float* d_win;              // [B, Tq+W-1, D] (added)
+  float* d_sink;             // [H] (added), nullable
+  float* d_gamma_q;          // [D] (added), nullable
+  // workspace views (set by the launcher)
+  uint16_t* X;
+  int64_t* rowmap;
+  uint16_t* Y;
+  float* Dh;
+  float* SP;
+  uint16_t* T;
+  float* DQT;
+};
+int64_t bwd_rows_padded(int64_t rows_max);
+size_t bwd_query_bytes(int D, int64_t np);
+hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t st);
+
 }  // namespace v4

@@ -59,6 +59,14 @@ _SIGS = {
     "v4attn_hca_attend_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I]),
     "v4attn_hca_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I, _L, _F,
                                _F, _F, _P, _P, _P, _Z, _P]),
+    "v4attn_csa_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "v4attn_csa_attend_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _I, _I,
+                                        _L, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                                        _P]),
+    "v4attn_hca_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I]),
+    "v4attn_hca_attend_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I,
+                                        _L, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                                        _P]),
     "v4attn_nsa_attend_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I, _I]),
     "v4attn_nsa_attend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _L, _I,
                                _I, _L, _F, _F, _F, _P, _P, _P, _P, _Z, _P]),
@@ -479,3 +487,71 @@ def nsa_attend(q, entries, tokens, win, gamma_q, gates, *, n_entries, m, q_pos0,
                                   _ptr(blocks), _ptr(block_score), _ptr(workspace), nbytes,
                                   _stream(q)))
     return out, blocks, block_score
+
+
+def _bwd_outputs(q, entries, win, H, D, grads):
+    """Gradient buffers: dq written, the rest zeroed here unless given."""
+    B, Tq = q.shape[:2]
+    dev = q.device
+    g = dict(grads or {})
+    dq = g.get("dq")
+    if dq is None:
+        dq = torch.empty((B, Tq, H, D), dtype=torch.float32, device=dev)
+    d_ent = g.get("d_entries")
+    if d_ent is None:
+        d_ent = torch.zeros((B, entries.shape[1], D), dtype=torch.float32, device=dev)
+    d_win = g.get("d_win")
+    if d_win is None:
+        d_win = torch.zeros((B, win.shape[1], D), dtype=torch.float32, device=dev)
+    d_sink = g.get("d_sink")
+    if d_sink is None:
+        d_sink = torch.zeros(H, dtype=torch.float32, device=dev)
+    d_gamma = g.get("d_gamma_q")
+    if d_gamma is None:
+        d_gamma = torch.zeros(D, dtype=torch.float32, device=dev)
+    for t, n in ((dq, "dq"), (d_ent, "d_entries"), (d_win, "d_win"), (d_sink, "d_sink"),
+                 (d_gamma, "d_gamma_q")):
+        _need(t, n, torch.float32)
+    return dq, d_ent, d_win, d_sink, d_gamma
+
+
+def csa_attend_backward(q, entries, topk, win, gamma_q, sink, out, lse, dout, *, q_pos0, W,
+                        scale=None, eps=1e-6, rope_base=10000.0, R=64, grads=None,
+                        workspace=None):
+    """Gradients of csa_attend.  Returns (dq, d_entries, d_win, d_sink,
+    d_gamma_q); the last four are added into `grads` entries if given."""
+    _need(dout, "dout", torch.bfloat16, 4)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Tq, H, D = q.shape
+    k = topk.shape[2]
+    scale = D ** -0.5 if scale is None else scale
+    dq, d_ent, d_win, d_sink, d_gamma = _bwd_outputs(q, entries, win, H, D, grads)
+    nbytes = lib().v4attn_csa_attend_backward_workspace(B, Tq, H, D, k, W)
+    workspace = _workspace(nbytes, q.device, workspace)
+    check(lib().v4attn_csa_attend_backward(
+        _ptr(q), _ptr(entries), _ptr(topk), _ptr(win), _ptr(gamma_q), _ptr(sink), B, Tq, H, D, R,
+        entries.shape[1], k, int(W), int(q_pos0), float(scale), float(eps), float(rope_base),
+        _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(d_ent), _ptr(d_win), _ptr(d_sink),
+        _ptr(d_gamma), _ptr(workspace), nbytes, _stream(q)))
+    return dq, d_ent, d_win, d_sink, d_gamma
+
+
+def hca_attend_backward(q, entries, win, gamma_q, sink, out, lse, dout, *, n_entries, m, q_pos0,
+                        W, scale=None, eps=1e-6, rope_base=10000.0, R=64, grads=None,
+                        workspace=None):
+    """Gradients of hca_attend (see csa_attend_backward)."""
+    _need(dout, "dout", torch.bfloat16, 4)
+    _need(out, "out", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Tq, H, D = q.shape
+    scale = D ** -0.5 if scale is None else scale
+    dq, d_ent, d_win, d_sink, d_gamma = _bwd_outputs(q, entries, win, H, D, grads)
+    nbytes = lib().v4attn_hca_attend_backward_workspace(B, Tq, H, D, n_entries, m, q_pos0, W)
+    workspace = _workspace(nbytes, q.device, workspace)
+    check(lib().v4attn_hca_attend_backward(
+        _ptr(q), _ptr(entries), _ptr(win), _ptr(gamma_q), _ptr(sink), B, Tq, H, D, R,
+        entries.shape[1], int(n_entries), int(m), int(W), int(q_pos0), float(scale), float(eps),
+        float(rope_base), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(d_ent), _ptr(d_win),
+        _ptr(d_sink), _ptr(d_gamma), _ptr(workspace), nbytes, _stream(q)))
+    return dq, d_ent, d_win, d_sink, d_gamma
