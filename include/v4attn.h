@@ -394,6 +394,8 @@ int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries,
  *   d_entries f32 [B, Ncap, D], d_win f32 [B, Tq+W-1, D]: ADDED to (the
  *            caller zeroes them); required when Ncap > 0 / W > 0
  *   d_sink f32 [H], d_gamma_q f32 [D]: added to; nullable
+ *   p_sel f32 [B, Tq, k] (CSA only, nullable): written with sum_h p_hx of
+ *            every top-k slot (0 for -1 slots): the indexer loss's target
  *   ws / ws_bytes >= the matching *_backward_workspace(...) bytes
  * Arithmetic: every attended row is gathered as bf16 (exact); q~, do and the
  * probabilities and dl enter bf16 matrix-core products with fp32
@@ -411,8 +413,8 @@ int v4attn_csa_attend_backward(const uint16_t* q, const uint8_t* entries,
                                const uint16_t* out, const float* lse,
                                const uint16_t* dout, float* dq,
                                float* d_entries, float* d_win, float* d_sink,
-                               float* d_gamma_q, void* ws, size_t ws_bytes,
-                               void* stream);
+                               float* d_gamma_q, float* p_sel, void* ws,
+                               size_t ws_bytes, void* stream);
 size_t v4attn_hca_attend_backward_workspace(int B, int Tq, int H, int D,
                                             int64_t n_entries, int m,
                                             int64_t q_pos0, int W);
@@ -426,6 +428,62 @@ int v4attn_hca_attend_backward(const uint16_t* q, const uint8_t* entries,
                                float* dq, float* d_entries, float* d_win,
                                float* d_sink, float* d_gamma_q, void* ws,
                                size_t ws_bytes, void* stream);
+
+/*
+ * v4attn_compress_backward -- gradient of v4attn_compress (POOL) for entries
+ * entry0 .. entry0+n_out-1 with respect to the raw latents, token scores,
+ * positional biases and gamma.
+ *
+ * Defines: as v4attn_compress (weights softmax(s_t + b_{t-(j-1)m}) over
+ * [(j-1)m, (j+1)m), pool, RMSNorm, RoPE at j m); trained end to end
+ * ("DeepSeek-V4, explained", step 7).  d_entries is the gradient with
+ * respect to the entries' stored values: the E4M3 / bf16 rounding is passed
+ * straight through.
+ *   raw, tok_score, pos_bias, gamma, sizes, raw_pos0, m, entry0, n_out: as
+ *        the forward (the windows must lie in the rows)
+ *   d_entries f32 [B, n_out, D]
+ *   d_raw f32 [B, L, D], d_score f32 [B, L]: added to
+ *   d_bias f32 [2m], d_gamma f32 [D]: added to, nullable
+ * fp32 arithmetic; a token is in two windows, so its gradients are added
+ * with atomics (the last bits vary from run to run).
+ */
+int v4attn_compress_backward(const uint16_t* raw, const float* tok_score,
+                             const float* pos_bias, const float* gamma, int B,
+                             int L, int D, int R, int64_t raw_pos0, int m,
+                             int64_t entry0, int n_out, float eps,
+                             float rope_base, const float* d_entries,
+                             float* d_raw, float* d_score, float* d_bias,
+                             float* d_gamma, void* stream);
+
+/*
+ * v4attn_index_kl_backward -- the indexer's KL alignment loss over one entry
+ * set per query and its gradients with respect to q^I, w and k^I.
+ *
+ * Defines: DSA trains its lightning indexer with a KL-divergence loss that
+ * pulls the indexer's scores toward the main attention's distribution, with
+ * the indexer's input detached, first over every entry, then over the
+ * selected ones ("DeepSeek-V4, explained", step 7).  Reading: over the set
+ * S of a query (sel, -1 slots excluded), P_j = target_j / sum_S target
+ * (target: the attention probabilities of the entries summed over heads,
+ * e.g. p_sel of v4attn_csa_attend_backward), Q = softmax_S(score) with the
+ * score of v4attn_index_score, loss = sum_j P_j (log P_j - log Q_j);
+ * d score_j = Q_j - P_j; P is a constant.
+ *   q_idx bf16 [B, Tq, HI, dI], w_idx f32 [B, Tq, HI], k_idx bf16 [B, Ncap, dI]
+ *   sel i32 [B, Tq, ns], target f32 [B, Tq, ns]
+ *   loss f32 [B, Tq] (written, nullable); dq_idx f32 [B, Tq, HI, dI] and
+ *   dw_idx f32 [B, Tq, HI] (written); dk_idx f32 [B, Ncap, dI] (added to)
+ *   ws / ws_bytes >= v4attn_index_kl_backward_workspace(B, Tq, dI, ns)
+ * 1 <= ns <= 4096, dI in {32, 64, 128}, HI <= 64.  q^I.k^I in fp32 from the
+ * bf16 inputs (exact products); ds w [q.k > 0] enters the dq and dk
+ * products as bf16; dk rows use fp32 atomics.
+ */
+size_t v4attn_index_kl_backward_workspace(int B, int Tq, int dI, int ns);
+int v4attn_index_kl_backward(const uint16_t* q_idx, const float* w_idx,
+                             const uint16_t* k_idx, const int32_t* sel,
+                             const float* target, int B, int Tq, int HI,
+                             int dI, int64_t Ncap, int ns, float* loss,
+                             float* dq_idx, float* dw_idx, float* dk_idx,
+                             void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -754,8 +754,8 @@ int run_backward(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
                  int D, int R, int64_t Ncap, int k, int64_t n_entries, int m, int W,
                  int64_t q_pos0, float scale, float eps, float rope_base, const uint16_t* out,
                  const float* lse, const uint16_t* dout, float* dq, float* d_entries,
-                 float* d_win, float* d_sink, float* d_gamma_q, int64_t rows_max, void* ws,
-                 size_t ws_bytes, void* stream) {
+                 float* d_win, float* d_sink, float* d_gamma_q, float* p_sel, int64_t rows_max,
+                 void* ws, size_t ws_bytes, void* stream) {
   if (!out || !lse || !dout || !dq) return fail(V4ATTN_EINVAL, "null out, lse, dout or dq");
   if (Ncap > 0 && !d_entries) return fail(V4ATTN_EINVAL, "null d_entries with Ncap > 0");
   if (W > 0 && !d_win) return fail(V4ATTN_EINVAL, "null d_win with W > 0");
@@ -774,6 +774,7 @@ int run_backward(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
   a.rope = v4::rope_turns(rope_base, R);
   a.np = v4::bwd_rows_padded(rows_max > 0 ? rows_max : 1);
   a.dq = dq; a.d_entries = d_entries; a.d_win = d_win; a.d_sink = d_sink; a.d_gamma_q = d_gamma_q;
+  a.p_sel = p_sel; a.k_sel = topk ? k : 0;
   return hip_status(v4::launch_attend_backward(a, bwd_chunk(nq, D, a.np), ws, (hipStream_t)stream),
                     "attention backward launch");
 }
@@ -791,7 +792,8 @@ int v4attn_csa_attend_backward(const uint16_t* q, const uint8_t* entries, const 
                                int64_t q_pos0, float scale, float eps, float rope_base,
                                const uint16_t* out, const float* lse, const uint16_t* dout,
                                float* dq, float* d_entries, float* d_win, float* d_sink,
-                               float* d_gamma_q, void* ws, size_t ws_bytes, void* stream) {
+                               float* d_gamma_q, float* p_sel, void* ws, size_t ws_bytes,
+                               void* stream) {
   if (int st = check_attend_common(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, W,
                                    q_pos0, scale, eps, rope_base, out))
     return st;
@@ -799,7 +801,7 @@ int v4attn_csa_attend_backward(const uint16_t* q, const uint8_t* entries, const 
   if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
   return run_backward(q, entries, topk, win, gamma_q, sink, B, Tq, H, D, R, Ncap, k, 0, 1, W,
                       q_pos0, scale, eps, rope_base, out, lse, dout, dq, d_entries, d_win,
-                      d_sink, d_gamma_q, (int64_t)k + W, ws, ws_bytes, stream);
+                      d_sink, d_gamma_q, p_sel, (int64_t)k + W, ws, ws_bytes, stream);
 }
 
 size_t v4attn_hca_attend_backward_workspace(int B, int Tq, int H, int D, int64_t n_entries, int m,
@@ -822,8 +824,92 @@ int v4attn_hca_attend_backward(const uint16_t* q, const uint8_t* entries, const 
   if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
   return run_backward(q, entries, nullptr, win, gamma_q, sink, B, Tq, H, D, R, Ncap, 0, n_entries,
                       m, W, q_pos0, scale, eps, rope_base, out, lse, dout, dq, d_entries, d_win,
-                      d_sink, d_gamma_q, vmax_of(Tq, n_entries, q_pos0, m) + W, ws, ws_bytes,
-                      stream);
+                      d_sink, d_gamma_q, nullptr, vmax_of(Tq, n_entries, q_pos0, m) + W, ws,
+                      ws_bytes, stream);
+}
+
+int v4attn_compress_backward(const uint16_t* raw, const float* tok_score, const float* pos_bias,
+                             const float* gamma, int B, int L, int D, int R, int64_t raw_pos0,
+                             int m, int64_t entry0, int n_out, float eps, float rope_base,
+                             const float* d_entries, float* d_raw, float* d_score, float* d_bias,
+                             float* d_gamma, void* stream) {
+  if (!raw || !tok_score || !pos_bias || !gamma || !d_entries || !d_raw || !d_score)
+    return fail(V4ATTN_EINVAL, "null raw, tok_score, pos_bias, gamma, d_entries, d_raw or d_score");
+  if (B < 0 || L < 0 || n_out < 0) return fail(V4ATTN_EINVAL, "negative B, L or n_out");
+  if (int st = check_dr(D, R)) return st;
+  if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
+  if (entry0 < 0) return fail(V4ATTN_EINVAL, "negative entry0");
+  if (!(eps >= 0.f) || !std::isfinite(eps) || !(rope_base > 0.f))
+    return fail(V4ATTN_EINVAL, "bad eps or rope_base");
+  if (n_out > 0) {
+    const int64_t lo = (entry0 - 1) * (int64_t)m;
+    const int64_t first = lo > 0 ? lo : 0;
+    const int64_t last = (entry0 + n_out) * (int64_t)m;
+    if (first < raw_pos0 || last > raw_pos0 + L)
+      return fail(V4ATTN_EINVAL, "entries %lld..%lld need positions [%lld, %lld) but rows hold [%lld, %lld)",
+                  (long long)entry0, (long long)(entry0 + n_out - 1), (long long)first,
+                  (long long)last, (long long)raw_pos0, (long long)(raw_pos0 + L));
+  }
+  if (!aligned16(raw)) return fail(V4ATTN_EINVAL, "raw must be 16-byte aligned");
+  v4::CompressBwdArgs a{raw, tok_score, pos_bias, gamma, B, L, D, R, raw_pos0, m, entry0, n_out,
+                        eps, v4::rope_turns(rope_base, R), d_entries, d_raw, d_score, d_bias,
+                        d_gamma};
+  return hip_status(v4::launch_compress_backward(a, (hipStream_t)stream), "compress backward launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+int kl_chunk(int64_t nq, int64_t nsp, int dIp) {
+  int64_t c = (int64_t)(((size_t)1 << 30) / v4::kl_query_bytes(nsp, dIp));
+  if (c < 1) c = 1;
+  if (c > 256) c = 256;
+  return (int)(c < nq ? c : (nq > 0 ? nq : 1));
+}
+
+size_t kl_ws(int B, int Tq, int dI, int ns) {
+  const int64_t nsp = (ns + 63) / 64 * 64;
+  const int dIp = (dI + 63) / 64 * 64;
+  return (size_t)kl_chunk((int64_t)B * Tq, nsp, dIp) * v4::kl_query_bytes(nsp, dIp);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t v4attn_index_kl_backward_workspace(int B, int Tq, int dI, int ns) {
+  if (B < 0 || Tq < 0 || dI < 1 || ns < 1) return 0;
+  return kl_ws(B, Tq, dI, ns);
+}
+
+int v4attn_index_kl_backward(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx,
+                             const int32_t* sel, const float* target, int B, int Tq, int HI,
+                             int dI, int64_t Ncap, int ns, float* loss, float* dq_idx,
+                             float* dw_idx, float* dk_idx, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!q_idx || !w_idx || !sel || !target || !dq_idx || !dw_idx || !dk_idx)
+    return fail(V4ATTN_EINVAL, "null q_idx, w_idx, sel, target, dq_idx, dw_idx or dk_idx");
+  if (Ncap > 0 && !k_idx) return fail(V4ATTN_EINVAL, "null k_idx");
+  if (B < 0 || Tq < 0 || Ncap < 0) return fail(V4ATTN_EINVAL, "negative B, Tq or Ncap");
+  if (HI < 1 || HI > 64) return fail(V4ATTN_EUNSUPPORTED, "HI = %d: 1 <= HI <= 64 is built", HI);
+  if (dI != 32 && dI != 64 && dI != 128)
+    return fail(V4ATTN_EUNSUPPORTED, "dI = %d: dI in {32, 64, 128} is built", dI);
+  if (ns < 1 || ns > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "ns = %d: 1 <= ns <= %d is built", ns, kMaxK);
+  const size_t need = kl_ws(B, Tq, dI, ns);
+  if (!ws || ws_bytes < need)
+    return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
+  const int64_t nq = (int64_t)B * Tq;
+  if (nq == 0) return hip_status(hipSuccess, "");
+  v4::KlArgs a{};
+  a.q_idx = q_idx; a.w_idx = w_idx; a.k_idx = k_idx; a.sel = sel; a.target = target;
+  a.B = B; a.Tq = Tq; a.HI = HI; a.dI = dI; a.dIp = (dI + 63) / 64 * 64; a.Ncap = Ncap;
+  a.ns = ns; a.nsp = (ns + 63) / 64 * 64;
+  a.loss = loss; a.dq = dq_idx; a.dw = dw_idx; a.dk = dk_idx;
+  return hip_status(v4::launch_index_kl_backward(a, kl_chunk(nq, a.nsp, a.dIp), ws,
+                                                 (hipStream_t)stream),
+                    "indexer KL backward launch");
 }
 
 }  // extern "C"

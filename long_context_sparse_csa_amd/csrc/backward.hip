@@ -98,6 +98,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
         const int m = m0 + wm * 32 + 16 * i + 4 * gq + v;
         const int n = n0 + wn * 32 + 16 * j + c;
         const float x = g.alpha * acc[i][j][v];
+        if (n >= g.n_valid) continue;
         if (!g.rowmap) {
           g.c[(int64_t)z * g.c_batch + (int64_t)m * g.ldc + n] = x;
         } else {
@@ -299,6 +300,243 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a, int q0) {
     atomicAdd(a.d_gamma_q + d, s_dg[0][d] + s_dg[1][d] + s_dg[2][d] + s_dg[3][d]);
 }
 
+// p_sel[q, x] = sum_h p_hx for the entry slots x < n_ent (the indexer loss's
+// target weights); 0 for absent slots.
+__global__ __launch_bounds__(256) void bwd_psel_kernel(BwdArgs a, int q0) {
+  const int qc = blockIdx.y, qr = q0 + qc;
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= a.k_sel) return;
+  float s = 0.f;
+  if (a.rowmap[(int64_t)qc * a.np + x] != -1) {
+    const float* sp = a.SP + (int64_t)qc * 128 * a.np;
+    for (int h = 0; h < a.H; ++h) {
+      const float lse = a.lse[(int64_t)qr * a.H + h];
+      if (lse != -INFINITY) s += exp2f((a.scale * sp[(int64_t)h * a.np + x] - lse) * kL2e);
+    }
+  }
+  a.p_sel[(int64_t)qr * a.k_sel + x] = s;
+}
+
+// ---- compressor backward: one workgroup per (sequence, entry).  Recomputes
+// the window weights alpha and the pooled vector, then
+//   dy = RoPE_{jm}^T(de), RMSNorm backward -> dpooled and d gamma,
+//   d c_t += alpha_t dpooled,  dalpha_t = c_t . dpooled,
+//   dlogit_t = alpha_t (dalpha_t - sum alpha dalpha) -> d s_t and d b.
+// Thread i owns the dim pair (2i, 2i+1); a token is in two windows, so the
+// latent and score gradients are added with atomics.
+__global__ __launch_bounds__(256) void compress_bwd_kernel(CompressBwdArgs a) {
+  __shared__ float s_alpha[512];
+  __shared__ float s_dp[512];
+  __shared__ float s_red[8];
+  __shared__ float s_da[512];
+  const int b = blockIdx.y;
+  const int64_t j = a.entry0 + blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int D = a.D, m = a.m;
+  const int64_t wlo = (j - 1) * (int64_t)m;
+  const int64_t plo = wlo > 0 ? wlo : 0;
+  const int nw = (int)((j + 1) * (int64_t)m - plo);
+  const int64_t r0 = plo - a.raw_pos0;
+  auto block_sum = [&](float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    __syncthreads();
+    if (lane == 0) s_red[wave] = v;
+    __syncthreads();
+    return s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  };
+  auto block_max = [&](float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    __syncthreads();
+    if (lane == 0) s_red[wave] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  };
+  // window weights
+  float mx = -INFINITY;
+  for (int t = tid; t < nw; t += 256) {
+    const float lg = a.tok_score[(int64_t)b * a.L + r0 + t] + a.pos_bias[plo - wlo + t];
+    s_alpha[t] = lg;
+    mx = fmaxf(mx, lg);
+  }
+  mx = block_max(mx);
+  float sum = 0.f;
+  for (int t = tid; t < nw; t += 256) {
+    const float e = expf(s_alpha[t] - mx);
+    s_alpha[t] = e;
+    sum += e;
+  }
+  sum = block_sum(sum);
+  const float inv = 1.0f / sum;
+  for (int t = tid; t < nw; t += 256) s_alpha[t] *= inv;
+  __syncthreads();
+  // pooled vector (this thread's pair)
+  const bool own = 2 * tid < D;
+  const int d = 2 * tid;
+  const uint16_t* rb = a.raw + ((int64_t)b * a.L + r0) * D;
+  float p0 = 0.f, p1 = 0.f;
+  if (own)
+    for (int t = 0; t < nw; ++t) {
+      const uint32_t w2 = *reinterpret_cast<const uint32_t*>(rb + (int64_t)t * D + d);
+      p0 += s_alpha[t] * bf16f((uint16_t)(w2 & 0xFFFFu));
+      p1 += s_alpha[t] * bf16f((uint16_t)(w2 >> 16));
+    }
+  const float ms = block_sum(own ? p0 * p0 + p1 * p1 : 0.f) / (float)D;
+  const float rsn = 1.0f / sqrtf(ms + a.eps);
+  // dy = RoPE at j m, transposed
+  float g0 = 0.f, g1 = 0.f;
+  if (own) {
+    g0 = a.de[((int64_t)b * a.n_out + blockIdx.x) * D + d];
+    g1 = a.de[((int64_t)b * a.n_out + blockIdx.x) * D + d + 1];
+    if (d >= D - a.R) {
+      float cs, sn;
+      rope_cos_sin(j * m, a.rope.t[(d - (D - a.R)) >> 1], &cs, &sn);
+      const float u0 = g0 * cs + g1 * sn, u1 = -g0 * sn + g1 * cs;
+      g0 = u0;
+      g1 = u1;
+    }
+  }
+  const float ga = own ? g0 * a.gamma[d] : 0.f, gb = own ? g1 * a.gamma[d + 1] : 0.f;
+  const float dot = block_sum(ga * p0 + gb * p1);
+  const float c3 = dot * rsn * rsn * rsn / (float)D;
+  if (own) {
+    s_dp[d] = ga * rsn - p0 * c3;
+    s_dp[d + 1] = gb * rsn - p1 * c3;
+    if (a.d_gamma) {
+      atomicAdd(a.d_gamma + d, g0 * p0 * rsn);
+      atomicAdd(a.d_gamma + d + 1, g1 * p1 * rsn);
+    }
+  }
+  __syncthreads();
+  // per token: latent gradient and dalpha (one wave per token)
+  for (int t = wave; t < nw; t += 4) {
+    const uint16_t* ct = rb + (int64_t)t * D;
+    float* dct = a.d_raw + ((int64_t)b * a.L + r0 + t) * D;
+    const float al = s_alpha[t];
+    float da = 0.f;
+    for (int e = lane; e < D; e += 64) {
+      da += bf16f(ct[e]) * s_dp[e];
+      atomicAdd(dct + e, al * s_dp[e]);
+    }
+    for (int o = 32; o > 0; o >>= 1) da += __shfl_xor(da, o);
+    if (lane == 0) s_da[t] = da;
+  }
+  __syncthreads();
+  float sad = 0.f;
+  for (int t = tid; t < nw; t += 256) sad += s_alpha[t] * s_da[t];
+  sad = block_sum(sad);
+  for (int t = tid; t < nw; t += 256) {
+    const float dl = s_alpha[t] * (s_da[t] - sad);
+    atomicAdd(a.d_score + (int64_t)b * a.L + r0 + t, dl);
+    if (a.d_bias) atomicAdd(a.d_bias + (plo - wlo + t), dl);
+  }
+}
+
+// ---- indexer KL backward, per query: from A = q^I K^T (64 head slots x
+// set), s_j = sum_h w_h relu(A_hj), Q = softmax(s) over the valid slots, P
+// the normalised target; loss = sum P (log P - log Q); ds = Q - P;
+// G_hj = ds_j w_h [A_hj > 0] (bf16) and dw_h = sum_j ds_j relu(A_hj).
+__global__ __launch_bounds__(256) void kl_elem_kernel(KlArgs a, int q0) {
+  __shared__ float s_s[4096];
+  __shared__ float s_p[4096];
+  __shared__ float s_red[8];
+  const int qc = blockIdx.x, qr = q0 + qc;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ns = a.ns, nsp = a.nsp;
+  const float* A = a.Am + (int64_t)qc * 64 * nsp;
+  const float* w = a.w_idx + (int64_t)qr * a.HI;
+  auto block_sum = [&](float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    __syncthreads();
+    if (lane == 0) s_red[wave] = v;
+    __syncthreads();
+    return s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  };
+  auto block_max = [&](float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    __syncthreads();
+    if (lane == 0) s_red[wave] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  };
+  float mx = -INFINITY, ptot = 0.f;
+  for (int x = tid; x < ns; x += 256) {
+    const bool valid = a.rowmap[(int64_t)qc * nsp + x] >= 0;
+    float sc = 0.f;
+    for (int h = 0; h < a.HI; ++h) sc += w[h] * fmaxf(A[(int64_t)h * nsp + x], 0.f);
+    s_s[x] = valid ? sc : -INFINITY;
+    const float pv = valid ? a.target[(int64_t)qr * ns + x] : 0.f;
+    s_p[x] = pv;
+    ptot += pv;
+    mx = fmaxf(mx, s_s[x]);
+  }
+  mx = block_max(mx);
+  ptot = block_sum(ptot);
+  float se = 0.f;
+  for (int x = tid; x < ns; x += 256) se += mx == -INFINITY ? 0.f : expf(s_s[x] - mx);
+  se = block_sum(se);
+  const float lz = mx + logf(se);   // log sum exp
+  const float pin = ptot > 0.f ? 1.0f / ptot : 0.f;
+  float loss = 0.f;
+  for (int x = tid; x < ns; x += 256) {
+    const float P = s_p[x] * pin;
+    const float lq = s_s[x] - lz;
+    const float Q = s_s[x] == -INFINITY ? 0.f : expf(lq);
+    if (P > 0.f) loss += P * (logf(P) - lq);
+    s_s[x] = Q * (ptot > 0.f ? 1.f : 0.f) - P;   // ds
+  }
+  loss = block_sum(loss);
+  if (tid == 0 && a.loss) a.loss[qr] = loss;
+  __syncthreads();
+  // G (bf16) and dw: wave w takes heads w, w+4, ..
+  uint16_t* G = a.Gm + (int64_t)qc * 64 * nsp;
+  for (int h = wave; h < 64; h += 4) {
+    float dw = 0.f;
+    const float wh = h < a.HI ? w[h] : 0.f;
+    for (int x = lane; x < nsp; x += 64) {
+      float gv = 0.f;
+      if (h < a.HI && x < ns) {
+        const float av = A[(int64_t)h * nsp + x];
+        dw += s_s[x] * fmaxf(av, 0.f);
+        gv = av > 0.f ? s_s[x] * wh : 0.f;
+      }
+      G[(int64_t)h * nsp + x] = f2bf(gv);
+    }
+    for (int o = 32; o > 0; o >>= 1) dw += __shfl_xor(dw, o);
+    if (lane == 0 && h < a.HI) a.dw[(int64_t)qr * a.HI + h] = dw;
+  }
+}
+
+// Gathers a query's set of indexer keys as bf16 (dims padded to dIp with
+// zeros) and the query's heads (64 slots); rowmap = b Ncap + j or -1.
+__global__ __launch_bounds__(256) void kl_gather_kernel(KlArgs a, int q0) {
+  const int qc = blockIdx.y, qr = q0 + qc;
+  const int b = qr / a.Tq;
+  const int x = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (x < a.nsp) {
+    const int32_t j = x < a.ns ? a.sel[(int64_t)qr * a.ns + x] : -1;
+    const bool ok = j >= 0 && j < a.Ncap;
+    uint16_t* dst = a.K + ((int64_t)qc * a.nsp + x) * a.dIp;
+    const uint16_t* src = a.k_idx + ((int64_t)b * a.Ncap + (ok ? j : 0)) * a.dI;
+    for (int e = lane; e < a.dIp; e += 64) dst[e] = ok && e < a.dI ? src[e] : 0;
+    if (lane == 0) a.rowmap[(int64_t)qc * a.nsp + x] = ok ? (int64_t)b * a.Ncap + j : -1;
+  }
+  if (blockIdx.x < 16) {   // 64 head slots of q^I, four a workgroup
+    const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+    uint16_t* dst = a.Qi + ((int64_t)qc * 64 + h) * a.dIp;
+    const uint16_t* src = a.q_idx + ((int64_t)qr * a.HI + (h < a.HI ? h : 0)) * a.dI;
+    for (int e = lane; e < a.dIp; e += 64) dst[e] = h < a.HI && e < a.dI ? src[e] : 0;
+  }
+}
+
+// dq^I rows of the query (the first HI slots, dI dims) from the padded product
+__global__ __launch_bounds__(256) void kl_dq_kernel(KlArgs a, int q0) {
+  const int qc = blockIdx.x, qr = q0 + qc;
+  for (int i = threadIdx.x; i < a.HI * a.dI; i += 256) {
+    const int h = i / a.dI, e = i - h * a.dI;
+    a.dq[(int64_t)qr * a.HI * a.dI + i] = a.DQ[((int64_t)qc * 64 + h) * a.dIp + e];
+  }
+}
+
 template <bool AT, bool BT>
 hipError_t gemm(const GemmArgs& g, int M, int N, int Z, hipStream_t st) {
   gemm_bf16_kernel<AT, BT><<<dim3(N / 64, M / 64, Z), 256, 0, st>>>(g);
@@ -340,26 +578,86 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t s
     GemmArgs g1{};
     g1.a = a.Y; g1.lda = a.D; g1.a_batch = 128 * (int64_t)a.D;
     g1.b = a.X; g1.ldb = a.D; g1.b_batch = np * a.D;
-    g1.c = a.SP; g1.ldc = np; g1.c_batch = 128 * np; g1.K = a.D; g1.alpha = 1.f;
+    g1.c = a.SP; g1.ldc = np; g1.c_batch = 128 * np; g1.K = a.D; g1.alpha = 1.f; g1.n_valid = (int)np;
     hipError_t e = gemm<false, true>(g1, 128, (int)np, qc, st);
     if (e != hipSuccess) return e;
     bwd_softmax_kernel<<<dim3((unsigned)((np + 255) / 256), 64, qc), 256, 0, st>>>(a, q0);
+    if (a.p_sel && a.k_sel > 0)
+      bwd_psel_kernel<<<dim3((unsigned)((a.k_sel + 255) / 256), qc), 256, 0, st>>>(a, q0);
     // dq~ = (scale dL) X: M = 64, N = D, K = np
     GemmArgs g2{};
     g2.a = a.T; g2.lda = np; g2.a_batch = 128 * np;
     g2.b = a.X; g2.ldb = a.D; g2.b_batch = np * a.D;
     g2.c = a.DQT; g2.ldc = a.D; g2.c_batch = 64 * (int64_t)a.D; g2.K = (int)np; g2.alpha = 1.f;
+    g2.n_valid = a.D;
     e = gemm<false, false>(g2, 64, a.D, qc, st);
     if (e != hipSuccess) return e;
     // dX = T^T Y, added into the row gradients: M = np, N = D, K = 128
     GemmArgs g3{};
     g3.a = a.T; g3.lda = np; g3.a_batch = 128 * np;
     g3.b = a.Y; g3.ldb = a.D; g3.b_batch = 128 * (int64_t)a.D;
-    g3.c = a.d_entries; g3.c2 = a.d_win; g3.ldc = a.D; g3.K = 128; g3.alpha = 1.f;
+    g3.c = a.d_entries; g3.c2 = a.d_win; g3.ldc = a.D; g3.K = 128; g3.alpha = 1.f; g3.n_valid = a.D;
     g3.rowmap = a.rowmap; g3.rowmap_batch = np;
     e = gemm<true, false>(g3, (int)np, a.D, qc, st);
     if (e != hipSuccess) return e;
     bwd_q_kernel<<<qc, 256, 0, st>>>(a, q0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_backward(const CompressBwdArgs& a, hipStream_t st) {
+  if (a.B == 0 || a.n_out == 0) return hipSuccess;
+  compress_bwd_kernel<<<dim3((unsigned)a.n_out, (unsigned)a.B), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+size_t kl_query_bytes(int64_t nsp, int dIp) {
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  return al((size_t)nsp * dIp * 2) + al((size_t)nsp * 8) + al((size_t)64 * dIp * 2) +
+         al((size_t)64 * nsp * 4) + al((size_t)64 * nsp * 2) + al((size_t)64 * dIp * 4);
+}
+
+hipError_t launch_index_kl_backward(KlArgs a, int qchunk, void* ws, hipStream_t st) {
+  const int nq = a.B * a.Tq;
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const int64_t nsp = a.nsp;
+  a.K = reinterpret_cast<uint16_t*>(w);      w += al((size_t)qchunk * nsp * a.dIp * 2);
+  a.rowmap = reinterpret_cast<int64_t*>(w);  w += al((size_t)qchunk * nsp * 8);
+  a.Qi = reinterpret_cast<uint16_t*>(w);     w += al((size_t)qchunk * 64 * a.dIp * 2);
+  a.Am = reinterpret_cast<float*>(w);        w += al((size_t)qchunk * 64 * nsp * 4);
+  a.Gm = reinterpret_cast<uint16_t*>(w);     w += al((size_t)qchunk * 64 * nsp * 2);
+  a.DQ = reinterpret_cast<float*>(w);
+  for (int q0 = 0; q0 < nq; q0 += qchunk) {
+    const int qc = nq - q0 < qchunk ? nq - q0 : qchunk;
+    const unsigned gx = (unsigned)((nsp + 3) / 4 > 16 ? (nsp + 3) / 4 : 16);
+    kl_gather_kernel<<<dim3(gx, qc), 256, 0, st>>>(a, q0);
+    // A = Qi K^T: M = 64, N = nsp, K = dIp
+    GemmArgs g1{};
+    g1.a = a.Qi; g1.lda = a.dIp; g1.a_batch = 64 * (int64_t)a.dIp;
+    g1.b = a.K; g1.ldb = a.dIp; g1.b_batch = nsp * a.dIp;
+    g1.c = a.Am; g1.ldc = nsp; g1.c_batch = 64 * nsp; g1.K = a.dIp; g1.alpha = 1.f;
+    g1.n_valid = (int)nsp;
+    hipError_t e = gemm<false, true>(g1, 64, (int)nsp, qc, st);
+    if (e != hipSuccess) return e;
+    kl_elem_kernel<<<qc, 256, 0, st>>>(a, q0);
+    // dq = G K: M = 64, N = dIp, K = nsp
+    GemmArgs g2{};
+    g2.a = a.Gm; g2.lda = nsp; g2.a_batch = 64 * nsp;
+    g2.b = a.K; g2.ldb = a.dIp; g2.b_batch = nsp * a.dIp;
+    g2.c = a.DQ; g2.ldc = a.dIp; g2.c_batch = 64 * (int64_t)a.dIp; g2.K = (int)nsp; g2.alpha = 1.f;
+    g2.n_valid = a.dIp;
+    e = gemm<false, false>(g2, 64, a.dIp, qc, st);
+    if (e != hipSuccess) return e;
+    kl_dq_kernel<<<qc, 256, 0, st>>>(a, q0);
+    // dK = G^T Qi, added into dk rows: M = nsp, N = dIp (first dI kept), K = 64
+    GemmArgs g3{};
+    g3.a = a.Gm; g3.lda = nsp; g3.a_batch = 64 * nsp;
+    g3.b = a.Qi; g3.ldb = a.dIp; g3.b_batch = 64 * (int64_t)a.dIp;
+    g3.c = a.dk; g3.ldc = a.dI; g3.K = 64; g3.alpha = 1.f; g3.n_valid = a.dI;
+    g3.rowmap = a.rowmap; g3.rowmap_batch = nsp;
+    e = gemm<true, false>(g3, (int)nsp, a.dIp, qc, st);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }

@@ -214,6 +214,7 @@ struct GemmArgs {
   int64_t rowmap_batch;
   int K;
   float alpha;
+  int n_valid;               // columns >= n_valid are not stored
 };
 
 // Attention backward (both kinds: CSA when topk != nullptr).
@@ -241,6 +242,9 @@ struct BwdArgs {
   float* d_win;              // [B, Tq+W-1, D] (added)
   float* d_sink;             // [H] (added), nullable
   float* d_gamma_q;          // [D] (added), nullable
+  float* p_sel;              // [B, Tq, k_sel] sum over heads of p of the entry
+                             // slots (written), nullable
+  int k_sel;
   // workspace views (set by the launcher)
   uint16_t* X;
   int64_t* rowmap;
@@ -253,5 +257,51 @@ struct BwdArgs {
 int64_t bwd_rows_padded(int64_t rows_max);
 size_t bwd_query_bytes(int D, int64_t np);
 hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t st);
+
+// Compressor (POOL) backward for entries entry0 .. entry0+n_out-1.
+struct CompressBwdArgs {
+  const uint16_t* raw;       // [B, L, D], positions raw_pos0 ..
+  const float* tok_score;    // [B, L]
+  const float* pos_bias;     // [2m]
+  const float* gamma;        // [D]
+  int B, L, D, R;
+  int64_t raw_pos0;
+  int m;
+  int64_t entry0;
+  int n_out;
+  float eps;
+  RopeTurns rope;
+  const float* de;           // [B, n_out, D] gradient of the entries' values
+  float* d_raw;              // [B, L, D] (added)
+  float* d_score;            // [B, L] (added)
+  float* d_bias;             // [2m] (added), nullable
+  float* d_gamma;            // [D] (added), nullable
+};
+hipError_t launch_compress_backward(const CompressBwdArgs& a, hipStream_t st);
+
+// Indexer KL loss backward over one entry set per query.
+struct KlArgs {
+  const uint16_t* q_idx;     // [B, Tq, HI, dI]
+  const float* w_idx;        // [B, Tq, HI]
+  const uint16_t* k_idx;     // [B, Ncap, dI]
+  const int32_t* sel;        // [B, Tq, ns] entry indices, -1 = empty
+  const float* target;       // [B, Tq, ns] target weights (normalised here)
+  int B, Tq, HI, dI, dIp;
+  int64_t Ncap;
+  int ns;
+  int64_t nsp;               // ns padded to 64
+  float* loss;               // [B, Tq] (written), nullable
+  float* dq;                 // [B, Tq, HI, dI] (written)
+  float* dw;                 // [B, Tq, HI] (written)
+  float* dk;                 // [B, Ncap, dI] (added)
+  uint16_t* K;
+  int64_t* rowmap;
+  uint16_t* Qi;
+  float* Am;
+  uint16_t* Gm;
+  float* DQ;
+};
+size_t kl_query_bytes(int64_t nsp, int dIp);
+hipError_t launch_index_kl_backward(KlArgs a, int qchunk, void* ws, hipStream_t st);
 
 }  // namespace v4

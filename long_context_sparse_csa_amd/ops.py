@@ -61,8 +61,13 @@ _SIGS = {
                                _F, _F, _P, _P, _P, _Z, _P]),
     "v4attn_csa_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _I, _I]),
     "v4attn_csa_attend_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _I, _I,
-                                        _L, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
-                                        _P]),
+                                        _L, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _Z, _P]),
+    "v4attn_compress_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _L, _I, _F, _F, _P,
+                                      _P, _P, _P, _P, _P]),
+    "v4attn_index_kl_backward_workspace": (_Z, [_I, _I, _I, _I]),
+    "v4attn_index_kl_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _P, _P, _P, _P,
+                                      _P, _Z, _P]),
     "v4attn_hca_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I]),
     "v4attn_hca_attend_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I,
                                         _L, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
@@ -517,9 +522,10 @@ def _bwd_outputs(q, entries, win, H, D, grads):
 
 def csa_attend_backward(q, entries, topk, win, gamma_q, sink, out, lse, dout, *, q_pos0, W,
                         scale=None, eps=1e-6, rope_base=10000.0, R=64, grads=None,
-                        workspace=None):
+                        p_sel=None, workspace=None):
     """Gradients of csa_attend.  Returns (dq, d_entries, d_win, d_sink,
-    d_gamma_q); the last four are added into `grads` entries if given."""
+    d_gamma_q); the last four are added into `grads` entries if given.
+    p_sel (f32 [B, Tq, k], optional) receives sum_h p of every top-k slot."""
     _need(dout, "dout", torch.bfloat16, 4)
     _need(out, "out", torch.bfloat16, 4)
     _need(lse, "lse", torch.float32, 3)
@@ -533,7 +539,7 @@ def csa_attend_backward(q, entries, topk, win, gamma_q, sink, out, lse, dout, *,
         _ptr(q), _ptr(entries), _ptr(topk), _ptr(win), _ptr(gamma_q), _ptr(sink), B, Tq, H, D, R,
         entries.shape[1], k, int(W), int(q_pos0), float(scale), float(eps), float(rope_base),
         _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(d_ent), _ptr(d_win), _ptr(d_sink),
-        _ptr(d_gamma), _ptr(workspace), nbytes, _stream(q)))
+        _ptr(d_gamma), _ptr(p_sel), _ptr(workspace), nbytes, _stream(q)))
     return dq, d_ent, d_win, d_sink, d_gamma
 
 
@@ -555,3 +561,50 @@ def hca_attend_backward(q, entries, win, gamma_q, sink, out, lse, dout, *, n_ent
         float(rope_base), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(d_ent), _ptr(d_win),
         _ptr(d_sink), _ptr(d_gamma), _ptr(workspace), nbytes, _stream(q)))
     return dq, d_ent, d_win, d_sink, d_gamma
+
+
+def compress_backward(raw, tok_score, pos_bias, gamma, d_entries, *, raw_pos0, m, entry0,
+                      eps=1e-6, rope_base=10000.0, R=64, grads=None):
+    """Gradients of compress_pool for entries entry0 .. entry0 + n_out - 1
+    (n_out = d_entries.shape[1]).  Returns (d_raw, d_score, d_bias, d_gamma),
+    added into `grads` entries if given, else into fresh zeros."""
+    _need(raw, "raw", torch.bfloat16, 3)
+    _need(d_entries, "d_entries", torch.float32, 3)
+    B, L, D = raw.shape
+    n_out = d_entries.shape[1]
+    g = dict(grads or {})
+    dev = raw.device
+    d_raw = g.get("d_raw", torch.zeros((B, L, D), dtype=torch.float32, device=dev))
+    d_score = g.get("d_score", torch.zeros((B, L), dtype=torch.float32, device=dev))
+    d_bias = g.get("d_bias", torch.zeros(2 * m, dtype=torch.float32, device=dev))
+    d_gamma = g.get("d_gamma", torch.zeros(D, dtype=torch.float32, device=dev))
+    check(lib().v4attn_compress_backward(
+        _ptr(raw), _ptr(tok_score), _ptr(pos_bias), _ptr(gamma), B, L, D, R, int(raw_pos0), int(m),
+        int(entry0), n_out, float(eps), float(rope_base), _ptr(d_entries), _ptr(d_raw),
+        _ptr(d_score), _ptr(d_bias), _ptr(d_gamma), _stream(raw)))
+    return d_raw, d_score, d_bias, d_gamma
+
+
+def index_kl_backward(q_idx, w_idx, k_idx, sel, target, *, dk=None, workspace=None):
+    """Indexer KL loss over the entry set `sel` (int32 [B, Tq, ns]) with target
+    weights (f32 [B, Tq, ns]).  Returns (loss [B, Tq], dq_idx, dw_idx, dk_idx);
+    dk_idx is added into `dk` if given."""
+    _need(q_idx, "q_idx", torch.bfloat16, 4)
+    _need(k_idx, "k_idx", torch.bfloat16, 3)
+    _need(sel, "sel", torch.int32, 3)
+    _need(target, "target", torch.float32, 3)
+    B, Tq, HI, dI = q_idx.shape
+    ns = sel.shape[2]
+    dev = q_idx.device
+    loss = torch.empty((B, Tq), dtype=torch.float32, device=dev)
+    dq = torch.empty((B, Tq, HI, dI), dtype=torch.float32, device=dev)
+    dw = torch.empty((B, Tq, HI), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.zeros((B, k_idx.shape[1], dI), dtype=torch.float32, device=dev)
+    nbytes = lib().v4attn_index_kl_backward_workspace(B, Tq, dI, ns)
+    workspace = _workspace(nbytes, dev, workspace)
+    check(lib().v4attn_index_kl_backward(
+        _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(sel), _ptr(target), B, Tq, HI, dI,
+        k_idx.shape[1], ns, _ptr(loss), _ptr(dq), _ptr(dw), _ptr(dk), _ptr(workspace), nbytes,
+        _stream(q_idx)))
+    return loss, dq, dw, dk

@@ -201,3 +201,134 @@ def test_backward_adds_into_given_gradients():
     assert torch.equal(a[0], b[0])                        # dq is written, not added
     for x, y in zip(a[1:], b[1:]):
         assert torch.allclose(y, 2 * x, rtol=1e-5, atol=1e-6)
+
+
+# ------------------------------------------------------- compressor backward --
+# Every input is exact in fp32 (bf16 latents); the kernel works in fp32, so
+# each gradient is the float64 one up to fp32 rounding of sums of at most
+# D + 2m terms: rel-L2 and max-abs (of the tensor's largest) within 1e-4.
+
+POOL_BWD_CASES = [
+    # B, L, D, m, pos0
+    (2, 40, 512, 4, 0),        # entry 0 (half window) included
+    (1, 4 * 128, 256, 128, 128),
+    (2, 96, 128, 16, 32),      # rows start mid-sequence
+]
+
+
+@pytest.mark.parametrize("case", POOL_BWD_CASES)
+def test_compress_backward_matches_oracle(case):
+    from oracle import compress as oc
+    B, L, D, m, pos0 = case
+    log(f"compress backward {case}")
+    seed = sum(case) % 977
+    raw = synth.normal((B, L, D), seed, "raw", DEV, dtype=torch.bfloat16)
+    sc = synth.normal((B, L), seed, "score", DEV)
+    bias = synth.normal((2 * m,), seed, "bias", DEV, std=0.3)
+    gam = synth.normal((D,), seed, "gamma", DEV, mean=1.0, std=0.1)
+    j_lo, j_hi = oc.entries_written(pos0, L, m)
+    js = np.arange(j_lo, j_hi)
+    de = synth.normal((B, len(js), D), seed, "de", DEV)
+    got = ops().compress_backward(raw, sc, bias, gam, de, raw_pos0=pos0, m=m, entry0=int(j_lo))
+    torch.cuda.synchronize()
+    rn, sn = bf16_to_f64(raw), sc.cpu().double().numpy()
+    bn, gn, den = bias.cpu().double().numpy(), gam.cpu().double().numpy(), de.cpu().double().numpy()
+    d_raw, d_sc = np.zeros((B, L, D)), np.zeros((B, L))
+    d_b, d_g = np.zeros(2 * m), np.zeros(D)
+    for b in range(B):
+        dc, ds, db, dg = ob.compress_pool_backward(rn[b], sn[b], pos0, m, bn, gn, EPS, R, BASE, js,
+                                                   den[b])
+        d_raw[b], d_sc[b] = dc, ds
+        d_b += db
+        d_g += dg
+    for n, g_, w_ in zip(("d_raw", "d_score", "d_bias", "d_gamma"), got, (d_raw, d_sc, d_b, d_g)):
+        g_ = g_.cpu().double().numpy()
+        rel = np.linalg.norm(g_ - w_) / np.linalg.norm(w_)
+        mx = np.abs(g_ - w_).max() / np.abs(w_).max()
+        log(f"  {n}: rel-L2 {rel:.2e}, max-abs/max {mx:.2e}")
+        assert rel <= 1e-4 and mx <= 1e-4, n
+
+
+# ------------------------------------------------------ indexer KL backward --
+# q^I.k^I is exact up to fp32 summation (bf16 inputs), so the scores, Q, the
+# loss and dw are fp32-accurate (rel 1e-4 allows sums over 4096 entries);
+# ds w [q.k > 0] enters the dq and dk products rounded to bf16 (2^-9), so
+# dq and dk are within rel-L2 4 * 2^-9 and 3e-2 of their largest element.
+
+KL_CASES = [
+    # B, Tq, HI, dI, Ncap, ns, n_valid
+    (2, 3, 64, 128, 3000, 1024, 1000),   # -1 padded sets, keys shared across queries
+    (1, 4, 40, 64, 500, 256, None),
+    (2, 2, 4, 32, 200, 64, 50),          # the tiny indexer shape
+]
+
+
+@pytest.mark.parametrize("case", KL_CASES)
+def test_index_kl_backward_matches_oracle(case):
+    B, Tq, HI, dI, Ncap, ns, nv = case
+    log(f"indexer KL backward {case}")
+    seed = sum(case[:6]) % 953
+    qi = synth.normal((B, Tq, HI, dI), seed, "qI", DEV, dtype=torch.bfloat16)
+    wi = synth.normal((B, Tq, HI), seed, "w", DEV)
+    ki = synth.normal((B, Ncap, dI), seed, "kI", DEV, dtype=torch.bfloat16)
+    g = torch.Generator().manual_seed(seed)
+    sel = torch.full((B, Tq, ns), -1, dtype=torch.int32)
+    for b in range(B):
+        for r in range(Tq):
+            n = ns if nv is None else nv
+            sel[b, r, :n] = torch.randperm(Ncap, generator=g)[:n].sort().values.to(torch.int32)
+    tgt = torch.rand((B, Tq, ns), generator=g)
+    tgt[tgt < 0.1] = 0.0
+    sel, tgt = sel.to(DEV), tgt.to(DEV)
+    loss, dq, dw, dk = ops().index_kl_backward(qi, wi, ki, sel, tgt)
+    torch.cuda.synchronize()
+    qn, kn = bf16_to_f64(qi), bf16_to_f64(ki)
+    wn, seln, tn = wi.cpu().double().numpy(), sel.cpu().numpy(), tgt.cpu().double().numpy()
+    r_loss, r_dq, r_dw = np.zeros((B, Tq)), np.zeros((B, Tq, HI, dI)), np.zeros((B, Tq, HI))
+    r_dk = np.zeros((B, Ncap, dI))
+    for b in range(B):
+        for r in range(Tq):
+            v = seln[b, r] >= 0
+            idx = seln[b, r][v]
+            P = tn[b, r][v] / tn[b, r][v].sum()
+            l_, dq_, dw_, dk_ = ob.indexer_kl(qn[b, r], wn[b, r], kn[b][idx], P)
+            r_loss[b, r], r_dq[b, r], r_dw[b, r] = l_, dq_, dw_
+            np.add.at(r_dk[b], idx, dk_)
+    np.testing.assert_allclose(loss.cpu().double().numpy(), r_loss, rtol=1e-4, atol=1e-6)
+    for n, g_, w_, tol in (("dw", dw, r_dw, 1e-4), ("dq", dq, r_dq, REL_L2), ("dk", dk, r_dk, REL_L2)):
+        g_ = g_.cpu().double().numpy()
+        rel = np.linalg.norm(g_ - w_) / np.linalg.norm(w_)
+        mx = np.abs(g_ - w_).max() / np.abs(w_).max()
+        log(f"  {n}: rel-L2 {rel:.2e}, max-abs/max {mx:.2e}")
+        assert rel <= tol and mx <= max(tol, MAX_REL if n != "dw" else 1e-4), n
+
+
+def test_attention_backward_p_sel_is_the_kl_target():
+    """p_sel of the CSA backward = sum over heads of the attention
+    probabilities of the top-k slots (bf16 q~ in the logits: rel-L2 4 * 2^-9)."""
+    B, Tq, H, D, Ncap, k, W, q_pos0 = 2, 2, 64, 512, 2000, 256, 128, 9000
+    q, ent, win, gq, sink, dout = _inputs(B, Tq, H, D, Ncap, W, 77)
+    g = torch.Generator().manual_seed(7)
+    topk = torch.stack([torch.stack([torch.randperm(Ncap, generator=g)[:k].sort().values
+                                     for _ in range(Tq)]) for _ in range(B)]).to(torch.int32)
+    topk[0, 0, -10:] = -1
+    topk = topk.to(DEV)
+    out, lse = ops().csa_attend(q, ent, topk, win, gq, sink, q_pos0=q_pos0, W=W, want_lse=True)
+    p_sel = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    ops().csa_attend_backward(q, ent, topk, win, gq, sink, out, lse, dout, q_pos0=q_pos0, W=W,
+                              p_sel=p_sel)
+    torch.cuda.synchronize()
+    qn, en, wn = bf16_to_f64(q), rows_to_f64(ent, D, R), rows_to_f64(win, D, R)
+    tk = topk.cpu().numpy()
+    for b in range(B):
+        for r in range(Tq):
+            t = q_pos0 + r
+            sel = tk[b, r]
+            rows = np.concatenate([en[b][sel[sel >= 0]], wn[b][_win_rows(t, q_pos0, W)]])
+            _, p, _ = oa.attend_rows(qn[b, r], gq.cpu().double().numpy(), t, rows,
+                                     sink.cpu().double().numpy(), D ** -0.5, EPS, R, BASE)
+            want = np.zeros(k)
+            want[sel >= 0] = p[:, : int((sel >= 0).sum())].sum(axis=0)
+            got = p_sel[b, r].cpu().double().numpy()
+            assert np.all(got[sel < 0] == 0)
+            assert np.linalg.norm(got - want) <= REL_L2 * np.linalg.norm(want)
