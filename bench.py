@@ -23,10 +23,12 @@ context (both layers) and reports MFMA fractions for scoring and attention.
 prefill indexer with the FP8 (E4M3, one scale per row) and MXFP4 lightning
 indexers; the headline value keeps the bf16 indexer keys of the workload
 definition.  An "nsa_variant" section times the NSA-style compress-select-
-window layer at the same 1M-token decode shape.
+window layer at the same 1M-token decode shape.  A "backward" section times
+the CSA layer's training step on the prefill chunk (attention, indexer KL
+and compressor backward).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
-                    [--no-fp8] [--no-nsa] [--nsa-only] [--prefill-only] [--graph] [--counters]
+                    [--no-fp8] [--no-nsa] [--nsa-only] [--no-backward] [--backward-only] [--prefill-only] [--graph] [--counters]
 """
 
 import argparse
@@ -398,6 +400,91 @@ def nsa_section(dev, reps):
     }
 
 
+def backward_section(dev, reps):
+    """Training step of the CSA layer on the 4096-token prefill chunk of a
+    2^20-token context (one sequence): attention backward over each query's
+    1024 selected entries + its 128-token window (64 heads x 512 dims), the
+    indexer KL loss backward over the same 1024 entries (64 x 128 indexer
+    heads), and the compressor backward for the chunk's 1024 new entries
+    (m = 4).  Inputs: N(0,1) packed rows and latents, random sorted top-k
+    sets, dout N(0,1).  Timed with HIP events; the attention backward is
+    reported against the bf16 matrix peak with its algorithmic FLOPs
+    10 H n D per query (n = k + W rows): [S; dP] 4, dq 2, dX 4."""
+    import torch
+    from long_context_sparse_csa_amd import ops, synth
+    from long_context_sparse_csa_amd.configs import PREFILL_1M as p
+    P, Tq, H, D, R, W, k, seed = p.T, p.Tq, p.H, p.D, p.R, p.W, p.k, p.seed
+    HI, dI, m = p.HI, p.dI, p.m
+    Nc = P // m + Tq // m
+    q = synth.normal((1, Tq, H, D), seed, "q", dev, dtype=torch.bfloat16)
+    ent = synth.packed_rows((1, Nc), D, R, seed, "entries", dev, chunk_rows=1 << 18)
+    win = synth.packed_rows((1, Tq + W - 1), D, R, seed, "win", dev)
+    gq = torch.ones(D, device=dev)
+    sink = synth.normal((H,), seed, "sink", dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    # sorted random k-subsets of each query's visible entries
+    vis = torch.minimum(torch.full((Tq,), Nc, device=dev),
+                        (P + torch.arange(Tq, device=dev) + 1) // m)
+    r = torch.rand((Tq, k), generator=g, device=dev)
+    topk = (r * vis[:, None].float()).long().clamp(max=Nc - 1)
+    topk = torch.sort(topk, dim=1).values.to(torch.int32)[None].contiguous()
+    out, lse = ops.csa_attend(q, ent, topk, win, gq, sink, q_pos0=P, W=W, want_lse=True)
+    dout = synth.normal((1, Tq, H, D), seed, "dout", dev, dtype=torch.bfloat16)
+    p_sel = torch.empty((1, Tq, k), dtype=torch.float32, device=dev)
+    grads = {"dq": torch.empty((1, Tq, H, D), dtype=torch.float32, device=dev),
+             "d_entries": torch.zeros((1, Nc, D), dtype=torch.float32, device=dev),
+             "d_win": torch.zeros((1, Tq + W - 1, D), dtype=torch.float32, device=dev),
+             "d_sink": torch.zeros(H, dtype=torch.float32, device=dev),
+             "d_gamma_q": torch.zeros(D, dtype=torch.float32, device=dev)}
+    ws = torch.empty(ops.lib().v4attn_csa_attend_backward_workspace(1, Tq, H, D, k, W),
+                     dtype=torch.uint8, device=dev)
+    att = lambda: ops.csa_attend_backward(q, ent, topk, win, gq, sink, out, lse, dout, q_pos0=P,
+                                          W=W, grads=grads, p_sel=p_sel, workspace=ws)
+    qi = synth.normal((1, Tq, HI, dI), seed, "qI", dev, dtype=torch.bfloat16)
+    wi = synth.normal((1, Tq, HI), seed, "w", dev)
+    ki = synth.normal((1, Nc, dI), seed, "kI", dev, dtype=torch.bfloat16)
+    dk = torch.zeros((1, Nc, dI), dtype=torch.float32, device=dev)
+    kws = torch.empty(ops.lib().v4attn_index_kl_backward_workspace(1, Tq, dI, k),
+                      dtype=torch.uint8, device=dev)
+    kl = lambda: ops.index_kl_backward(qi, wi, ki, topk, p_sel, dk=dk, workspace=kws)
+    raw = synth.normal((1, Tq + m, D), seed, "raw", dev, dtype=torch.bfloat16)
+    sc = synth.normal((1, Tq + m), seed, "score", dev)
+    bias = synth.normal((2 * m,), seed, "bias", dev, std=0.1)
+    de = synth.normal((1, Tq // m, D), seed, "de", dev)
+    cgr = {"d_raw": torch.zeros((1, Tq + m, D), dtype=torch.float32, device=dev),
+           "d_score": torch.zeros((1, Tq + m), dtype=torch.float32, device=dev),
+           "d_bias": torch.zeros(2 * m, dtype=torch.float32, device=dev),
+           "d_gamma": torch.zeros(D, dtype=torch.float32, device=dev)}
+    cmp = lambda: ops.compress_backward(raw, sc, bias, gq, de, raw_pos0=P - m, m=m,
+                                        entry0=P // m, grads=cgr)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_att, ms_kl, ms_cmp = timed(att), timed(kl), timed(cmp)
+    flops = 10.0 * H * (k + W) * D * Tq
+    tf = flops / (ms_att * 1e-3) / 1e12
+    return {
+        "workload": f"csa_layer_backward_4096_on_1m: Tq={Tq} k={k} W={W} H={H} D={D} "
+                    f"HI={HI} dI={dI} m={m}",
+        "ms": {"attend_backward": round(ms_att, 3), "index_kl_backward": round(ms_kl, 3),
+               "compress_backward": round(ms_cmp, 3)},
+        "layer_backward_ms": round(ms_att + ms_kl + ms_cmp, 3),
+        "tokens_per_s": round(Tq / ((ms_att + ms_kl + ms_cmp) * 1e-3), 1),
+        "attend_backward_TFLOPs": round(tf, 1),
+        "attend_backward_mfma_frac": round(tf / 2500.0, 4),
+    }
+
+
 def cpu_baseline(inp, budget_s):
     """The float64 oracle on a bounded sample of the same inputs: whole CSA
     and HCA layers for single sequences, alternating, until the budget."""
@@ -482,6 +569,10 @@ def main():
                     help="skip the 4096-token prefill section")
     ap.add_argument("--no-nsa", action="store_true",
                     help="skip the NSA-style variant section")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the CSA layer backward section")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the CSA layer backward (prints its section as the JSON line)")
     ap.add_argument("--nsa-only", action="store_true",
                     help="time only the NSA-style variant (prints its section as the JSON line)")
     ap.add_argument("--counters", action="store_true",
@@ -505,6 +596,9 @@ def main():
         return
     if args.nsa_only:
         print(json.dumps({"nsa_variant": nsa_section(dev, 20)}), flush=True)
+        return
+    if args.backward_only:
+        print(json.dumps({"backward": backward_section(dev, 3)}), flush=True)
         return
     log("generating inputs")
     inp = build_inputs(dev, args.rotate)
@@ -601,6 +695,10 @@ def main():
         log("nsa variant")
         res["nsa_variant"] = nsa_section(dev, 20)
         log("nsa variant: " + json.dumps(res["nsa_variant"]))
+    if not args.no_backward:
+        log("csa layer backward")
+        res["backward"] = backward_section(dev, 3)
+        log("backward: " + json.dumps(res["backward"]))
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle)")
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

@@ -144,16 +144,27 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a, int q0) {
   }
   uint16_t* dst = a.X + ((int64_t)qc * a.np + x) * a.D;
   const int E = a.D - a.R;
-  for (int d = lane; d < a.D; d += 64) {
-    float v = 0.f;
+  const int d = 8 * lane;   // this lane's 8 dims (E and D are multiples of 8)
+  if (d < a.D) {
+    uint4 o = {0u, 0u, 0u, 0u};
     if (src) {
-      if (d < E) {
-        v = __builtin_amdgcn_cvt_pk_f32_fp8((int)src[d], false)[0];
-      } else {
-        v = bf16f(reinterpret_cast<const uint16_t*>(src + E)[d - E]);
+      if (d < E) {   // 8 E4M3 bytes -> 8 bf16 (exact)
+        const uint2 b8 = *reinterpret_cast<const uint2*>(src + d);
+        const uint32_t w2[2] = {b8.x, b8.y};
+        uint32_t r[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w2[h], false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w2[h], true);
+          r[2 * h] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
+          r[2 * h + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+        }
+        o = uint4{r[0], r[1], r[2], r[3]};
+      } else {       // bf16 dims as stored
+        o = *reinterpret_cast<const uint4*>(src + E + 2 * (d - E));
       }
     }
-    dst[d] = f2bf(v);
+    *reinterpret_cast<uint4*>(dst + d) = o;
   }
   if (lane == 0) a.rowmap[(int64_t)qc * a.np + x] = map;
 }
@@ -219,30 +230,42 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int q0) {
 
 // T[qc] = [scale dL; P] (bf16, 64 head slots each) from [S; dP]: P =
 // exp(scale S - lse), dL = P (dP - Dh); absent rows and head slots >= H: 0.
+// One thread per row slot, all heads; p_sel (entry slots) is the head sum.
 __global__ __launch_bounds__(256) void bwd_softmax_kernel(BwdArgs a, int q0) {
-  const int qc = blockIdx.z, qr = q0 + qc;
-  const int h = blockIdx.y;
+  __shared__ float s_l2[64], s_dh[64];
+  const int qc = blockIdx.y, qr = q0 + qc;
+  if (threadIdx.x < 64) {
+    const int h = threadIdx.x;
+    const float lse = h < a.H ? a.lse[(int64_t)qr * a.H + h] : -INFINITY;
+    s_l2[h] = lse * kL2e;
+    s_dh[h] = a.Dh[(int64_t)qc * 64 + h];
+  }
+  __syncthreads();
   const int x = blockIdx.x * 256 + threadIdx.x;
   if (x >= a.np) return;
-  const float* sp = a.SP + (int64_t)qc * 128 * a.np;
-  float p = 0.f, dl = 0.f;
-  if (h < a.H && a.rowmap[(int64_t)qc * a.np + x] != -1) {
-    const float lse = a.lse[(int64_t)qr * a.H + h];
-    if (lse != -INFINITY) {
-      p = exp2f((a.scale * sp[(int64_t)h * a.np + x] - lse) * kL2e);
-      dl = p * (sp[(int64_t)(64 + h) * a.np + x] - a.Dh[(int64_t)qc * 64 + h]);
+  const float* sp = a.SP + (int64_t)qc * 128 * a.np + x;
+  uint16_t* tp = a.T + (int64_t)qc * 128 * a.np + x;
+  const bool present = a.rowmap[(int64_t)qc * a.np + x] != -1;
+  const float sl2 = a.scale * kL2e;
+  float psum = 0.f;
+  for (int h = 0; h < 64; ++h) {
+    float p = 0.f, dl = 0.f;
+    if (present && s_l2[h] != -INFINITY) {
+      p = exp2f(sp[(int64_t)h * a.np] * sl2 - s_l2[h]);
+      dl = p * (sp[(int64_t)(64 + h) * a.np] - s_dh[h]);
     }
+    psum += p;
+    tp[(int64_t)h * a.np] = f2bf(a.scale * dl);
+    tp[(int64_t)(64 + h) * a.np] = f2bf(p);
   }
-  uint16_t* tp = a.T + (int64_t)qc * 128 * a.np;
-  tp[(int64_t)h * a.np + x] = f2bf(a.scale * dl);
-  tp[(int64_t)(64 + h) * a.np + x] = f2bf(p);
+  if (a.p_sel && x < a.k_sel) a.p_sel[(int64_t)qr * a.k_sel + x] = psum;
 }
 
-// dq = RMSNorm backward of RoPE_t^T(dq~); d_gamma_q += sum over heads.  One
-// workgroup per query, wave w takes heads w, w+4, ..; lane holds dim pairs.
+// dq = RMSNorm backward of RoPE_t^T(dq~); d_gamma_q += sum over heads.  A
+// workgroup takes four heads of one query (one a wave); lane holds dim pairs.
 __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a, int q0) {
   __shared__ float s_dg[4][512];
-  const int qc = blockIdx.x, qr = q0 + qc;
+  const int qc = blockIdx.y, qr = q0 + qc;
   const int r = qr % a.Tq;
   const int64_t t = a.q_pos0 + r;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -250,7 +273,8 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a, int q0) {
   float dg[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) dg[i] = 0.f;
-  for (int h = wave; h < a.H; h += 4) {
+  if (blockIdx.x * 4 >= a.H) return;
+  for (int h = blockIdx.x * 4 + wave; h < a.H && h < blockIdx.x * 4 + 4; h += 4) {
     const uint16_t* qp = a.q + ((int64_t)qr * a.H + h) * a.D;
     const float* gq = a.DQT + ((int64_t)qc * 64 + h) * a.D;
     float ss = 0.f;
@@ -298,23 +322,6 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a, int q0) {
   __syncthreads();
   for (int d = threadIdx.x; d < a.D; d += 256)
     atomicAdd(a.d_gamma_q + d, s_dg[0][d] + s_dg[1][d] + s_dg[2][d] + s_dg[3][d]);
-}
-
-// p_sel[q, x] = sum_h p_hx for the entry slots x < n_ent (the indexer loss's
-// target weights); 0 for absent slots.
-__global__ __launch_bounds__(256) void bwd_psel_kernel(BwdArgs a, int q0) {
-  const int qc = blockIdx.y, qr = q0 + qc;
-  const int x = blockIdx.x * 256 + threadIdx.x;
-  if (x >= a.k_sel) return;
-  float s = 0.f;
-  if (a.rowmap[(int64_t)qc * a.np + x] != -1) {
-    const float* sp = a.SP + (int64_t)qc * 128 * a.np;
-    for (int h = 0; h < a.H; ++h) {
-      const float lse = a.lse[(int64_t)qr * a.H + h];
-      if (lse != -INFINITY) s += exp2f((a.scale * sp[(int64_t)h * a.np + x] - lse) * kL2e);
-    }
-  }
-  a.p_sel[(int64_t)qr * a.k_sel + x] = s;
 }
 
 // ---- compressor backward: one workgroup per (sequence, entry).  Recomputes
@@ -435,15 +442,28 @@ __global__ __launch_bounds__(256) void compress_bwd_kernel(CompressBwdArgs a) {
 // set), s_j = sum_h w_h relu(A_hj), Q = softmax(s) over the valid slots, P
 // the normalised target; loss = sum P (log P - log Q); ds = Q - P;
 // G_hj = ds_j w_h [A_hj > 0] (bf16) and dw_h = sum_j ds_j relu(A_hj).
-__global__ __launch_bounds__(256) void kl_elem_kernel(KlArgs a, int q0) {
-  __shared__ float s_s[4096];
-  __shared__ float s_p[4096];
+// Three kernels: scores (a thread per slot), the per-query softmax and loss
+// (a workgroup per query), G and dw (a thread per slot).
+__global__ __launch_bounds__(256) void kl_score_kernel(KlArgs a, int q0) {
+  __shared__ float s_w[64];
+  const int qc = blockIdx.y, qr = q0 + qc;
+  if (threadIdx.x < 64) s_w[threadIdx.x] = threadIdx.x < a.HI ? a.w_idx[(int64_t)qr * a.HI + threadIdx.x] : 0.f;
+  __syncthreads();
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= a.nsp) return;
+  const float* A = a.Am + (int64_t)qc * 64 * a.nsp + x;
+  float sc = 0.f;
+  for (int h = 0; h < a.HI; ++h) sc += s_w[h] * fmaxf(A[(int64_t)h * a.nsp], 0.f);
+  const bool valid = x < a.ns && a.rowmap[(int64_t)qc * a.nsp + x] >= 0;
+  a.Sb[(int64_t)qc * a.nsp + x] = valid ? sc : -INFINITY;
+}
+
+__global__ __launch_bounds__(256) void kl_reduce_kernel(KlArgs a, int q0) {
   __shared__ float s_red[8];
   const int qc = blockIdx.x, qr = q0 + qc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ns = a.ns, nsp = a.nsp;
-  const float* A = a.Am + (int64_t)qc * 64 * nsp;
-  const float* w = a.w_idx + (int64_t)qr * a.HI;
+  float* S = a.Sb + (int64_t)qc * a.nsp;
+  const float* tg = a.target + (int64_t)qr * a.ns;
   auto block_sum = [&](float v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     __syncthreads();
@@ -459,50 +479,52 @@ __global__ __launch_bounds__(256) void kl_elem_kernel(KlArgs a, int q0) {
     return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   };
   float mx = -INFINITY, ptot = 0.f;
-  for (int x = tid; x < ns; x += 256) {
-    const bool valid = a.rowmap[(int64_t)qc * nsp + x] >= 0;
-    float sc = 0.f;
-    for (int h = 0; h < a.HI; ++h) sc += w[h] * fmaxf(A[(int64_t)h * nsp + x], 0.f);
-    s_s[x] = valid ? sc : -INFINITY;
-    const float pv = valid ? a.target[(int64_t)qr * ns + x] : 0.f;
-    s_p[x] = pv;
-    ptot += pv;
-    mx = fmaxf(mx, s_s[x]);
+  for (int x = tid; x < a.ns; x += 256) {
+    mx = fmaxf(mx, S[x]);
+    ptot += S[x] == -INFINITY ? 0.f : tg[x];
   }
   mx = block_max(mx);
   ptot = block_sum(ptot);
   float se = 0.f;
-  for (int x = tid; x < ns; x += 256) se += mx == -INFINITY ? 0.f : expf(s_s[x] - mx);
+  for (int x = tid; x < a.ns; x += 256) se += S[x] == -INFINITY ? 0.f : expf(S[x] - mx);
   se = block_sum(se);
-  const float lz = mx + logf(se);   // log sum exp
+  const float lz = mx + logf(se);
   const float pin = ptot > 0.f ? 1.0f / ptot : 0.f;
   float loss = 0.f;
-  for (int x = tid; x < ns; x += 256) {
-    const float P = s_p[x] * pin;
-    const float lq = s_s[x] - lz;
-    const float Q = s_s[x] == -INFINITY ? 0.f : expf(lq);
-    if (P > 0.f) loss += P * (logf(P) - lq);
-    s_s[x] = Q * (ptot > 0.f ? 1.f : 0.f) - P;   // ds
+  for (int x = tid; x < a.nsp; x += 256) {
+    float ds = 0.f;
+    if (x < a.ns && S[x] != -INFINITY) {
+      const float P = tg[x] * pin;
+      const float lq = S[x] - lz;
+      if (P > 0.f) loss += P * (logf(P) - lq);
+      ds = (ptot > 0.f ? expf(lq) : 0.f) - P;
+    }
+    S[x] = ds;
   }
   loss = block_sum(loss);
   if (tid == 0 && a.loss) a.loss[qr] = loss;
+  if (tid < a.HI) a.dw[(int64_t)qr * a.HI + tid] = 0.f;
+}
+
+__global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int q0) {
+  __shared__ float s_w[64];
+  const int qc = blockIdx.y, qr = q0 + qc;
+  if (threadIdx.x < 64) s_w[threadIdx.x] = threadIdx.x < a.HI ? a.w_idx[(int64_t)qr * a.HI + threadIdx.x] : 0.f;
   __syncthreads();
-  // G (bf16) and dw: wave w takes heads w, w+4, ..
-  uint16_t* G = a.Gm + (int64_t)qc * 64 * nsp;
-  for (int h = wave; h < 64; h += 4) {
-    float dw = 0.f;
-    const float wh = h < a.HI ? w[h] : 0.f;
-    for (int x = lane; x < nsp; x += 64) {
-      float gv = 0.f;
-      if (h < a.HI && x < ns) {
-        const float av = A[(int64_t)h * nsp + x];
-        dw += s_s[x] * fmaxf(av, 0.f);
-        gv = av > 0.f ? s_s[x] * wh : 0.f;
-      }
-      G[(int64_t)h * nsp + x] = f2bf(gv);
+  const int lane = threadIdx.x & 63;
+  const int x = blockIdx.x * 256 + threadIdx.x;   // nsp is a multiple of 64: whole waves
+  if (x >= a.nsp) return;
+  const float ds = a.Sb[(int64_t)qc * a.nsp + x];
+  const float* A = a.Am + (int64_t)qc * 64 * a.nsp + x;
+  uint16_t* G = a.Gm + (int64_t)qc * 64 * a.nsp + x;
+  for (int h = 0; h < 64; ++h) {
+    const float av = h < a.HI ? A[(int64_t)h * a.nsp] : 0.f;
+    G[(int64_t)h * a.nsp] = f2bf(av > 0.f ? ds * s_w[h] : 0.f);
+    if (h < a.HI) {
+      float dw = ds * fmaxf(av, 0.f);
+      for (int o = 32; o > 0; o >>= 1) dw += __shfl_xor(dw, o);
+      if (lane == 0) atomicAdd(a.dw + (int64_t)qr * a.HI + h, dw);
     }
-    for (int o = 32; o > 0; o >>= 1) dw += __shfl_xor(dw, o);
-    if (lane == 0 && h < a.HI) a.dw[(int64_t)qr * a.HI + h] = dw;
   }
 }
 
@@ -581,9 +603,7 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t s
     g1.c = a.SP; g1.ldc = np; g1.c_batch = 128 * np; g1.K = a.D; g1.alpha = 1.f; g1.n_valid = (int)np;
     hipError_t e = gemm<false, true>(g1, 128, (int)np, qc, st);
     if (e != hipSuccess) return e;
-    bwd_softmax_kernel<<<dim3((unsigned)((np + 255) / 256), 64, qc), 256, 0, st>>>(a, q0);
-    if (a.p_sel && a.k_sel > 0)
-      bwd_psel_kernel<<<dim3((unsigned)((a.k_sel + 255) / 256), qc), 256, 0, st>>>(a, q0);
+    bwd_softmax_kernel<<<dim3((unsigned)((np + 255) / 256), qc), 256, 0, st>>>(a, q0);
     // dq~ = (scale dL) X: M = 64, N = D, K = np
     GemmArgs g2{};
     g2.a = a.T; g2.lda = np; g2.a_batch = 128 * np;
@@ -600,7 +620,7 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t s
     g3.rowmap = a.rowmap; g3.rowmap_batch = np;
     e = gemm<true, false>(g3, (int)np, a.D, qc, st);
     if (e != hipSuccess) return e;
-    bwd_q_kernel<<<qc, 256, 0, st>>>(a, q0);
+    bwd_q_kernel<<<dim3((unsigned)((a.H + 3) / 4), qc), 256, 0, st>>>(a, q0);
   }
   return hipGetLastError();
 }
@@ -614,7 +634,8 @@ hipError_t launch_compress_backward(const CompressBwdArgs& a, hipStream_t st) {
 size_t kl_query_bytes(int64_t nsp, int dIp) {
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
   return al((size_t)nsp * dIp * 2) + al((size_t)nsp * 8) + al((size_t)64 * dIp * 2) +
-         al((size_t)64 * nsp * 4) + al((size_t)64 * nsp * 2) + al((size_t)64 * dIp * 4);
+         al((size_t)64 * nsp * 4) + al((size_t)64 * nsp * 2) + al((size_t)64 * dIp * 4) +
+         al((size_t)nsp * 4);
 }
 
 hipError_t launch_index_kl_backward(KlArgs a, int qchunk, void* ws, hipStream_t st) {
@@ -627,7 +648,8 @@ hipError_t launch_index_kl_backward(KlArgs a, int qchunk, void* ws, hipStream_t 
   a.Qi = reinterpret_cast<uint16_t*>(w);     w += al((size_t)qchunk * 64 * a.dIp * 2);
   a.Am = reinterpret_cast<float*>(w);        w += al((size_t)qchunk * 64 * nsp * 4);
   a.Gm = reinterpret_cast<uint16_t*>(w);     w += al((size_t)qchunk * 64 * nsp * 2);
-  a.DQ = reinterpret_cast<float*>(w);
+  a.DQ = reinterpret_cast<float*>(w);        w += al((size_t)qchunk * 64 * a.dIp * 4);
+  a.Sb = reinterpret_cast<float*>(w);
   for (int q0 = 0; q0 < nq; q0 += qchunk) {
     const int qc = nq - q0 < qchunk ? nq - q0 : qchunk;
     const unsigned gx = (unsigned)((nsp + 3) / 4 > 16 ? (nsp + 3) / 4 : 16);
@@ -640,7 +662,9 @@ hipError_t launch_index_kl_backward(KlArgs a, int qchunk, void* ws, hipStream_t 
     g1.n_valid = (int)nsp;
     hipError_t e = gemm<false, true>(g1, 64, (int)nsp, qc, st);
     if (e != hipSuccess) return e;
-    kl_elem_kernel<<<qc, 256, 0, st>>>(a, q0);
+    kl_score_kernel<<<dim3((unsigned)((nsp + 255) / 256), qc), 256, 0, st>>>(a, q0);
+    kl_reduce_kernel<<<qc, 256, 0, st>>>(a, q0);
+    kl_grad_kernel<<<dim3((unsigned)((nsp + 255) / 256), qc), 256, 0, st>>>(a, q0);
     // dq = G K: M = 64, N = dIp, K = nsp
     GemmArgs g2{};
     g2.a = a.Gm; g2.lda = nsp; g2.a_batch = 64 * nsp;

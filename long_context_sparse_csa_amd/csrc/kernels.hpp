@@ -300,6 +300,7 @@ struct KlArgs {
   float* Am;
   uint16_t* Gm;
   float* DQ;
+  float* Sb;                 // [chunk, nsp] scores, then d loss / d score
 };
 size_t kl_query_bytes(int64_t nsp, int dIp);
 hipError_t launch_index_kl_backward(KlArgs a, int qchunk, void* ws, hipStream_t st);
