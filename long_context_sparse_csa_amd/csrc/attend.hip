@@ -126,9 +126,10 @@ __host__ __device__ inline int64_t split_chunk(int64_t n_rows, int splits) {
 
 // out = g1 * y + g0 * o0 + g2 * o2 for four dims (the gated sum of the
 // NSA-style variant, applied where the last branch is finalised), else y.
+template <bool MIX>
 __device__ __forceinline__ u32x2 final_bf16x4(const AttendArgs& a, int64_t off, int64_t qh,
                                               const float (&y)[4]) {
-  if (!a.mix_gates) return u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  if (!MIX || !a.mix_gates) return u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
   const float g0 = a.mix_gates[3 * qh], g1 = a.mix_gates[3 * qh + 1], g2 = a.mix_gates[3 * qh + 2];
   const u32x2 u0 = *reinterpret_cast<const u32x2*>(a.mix_o0 + off);
   const u32x2 u2 = *reinterpret_cast<const u32x2*>(a.mix_o2 + off);
@@ -670,7 +671,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
       qk(T, cur, sacc, mp, mo, [&](int st) {
         if (st < G::WPW && nbase) issue_copy(nbase, cur ^ 1, st);
       });
-      if (a.logits2 && head < a.H) {   // the tile's logits (log2 units; absent rows -inf)
+      if (!CSA && a.logits2 && head < a.H) {   // the tile's logits (log2 units; absent rows -inf)
         float* lp = a.logits2 + ((int64_t)qr * a.logits_stride + row_beg +
                                  (int64_t)tile * kAttRows + 4 * g) * 64 + head;
 #pragma unroll
@@ -744,7 +745,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
       }
     }
     const int64_t qh = (int64_t)qr * a.H + head;
-    *reinterpret_cast<u32x2*>(op + d0) = final_bf16x4(a, qh * D + d0, qh, v);
+    *reinterpret_cast<u32x2*>(op + d0) = final_bf16x4<CSA>(a, qh * D + d0, qh, v);   // mix: CSA only
   }
   if (a.lse && g == 0) a.lse[(int64_t)qr * a.H + head] = lse;
 }
@@ -822,7 +823,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
     }
   }
   const int64_t qh = (int64_t)qr * a.H + h;
-  *reinterpret_cast<u32x2*>(a.out + qh * D + d) = final_bf16x4(a, qh * D + d, qh, y);
+  *reinterpret_cast<u32x2*>(a.out + qh * D + d) = final_bf16x4<true>(a, qh * D + d, qh, y);
 }
 
 int attend_splits(int B, int Tq, int64_t rows_max, bool csa, int wg_budget) {

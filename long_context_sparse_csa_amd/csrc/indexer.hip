@@ -306,10 +306,13 @@ __global__ __launch_bounds__(kBlkWaves * 64) void index_score_block_kernel(Index
   if (ntiles > 0 && wok) flush(ntiles - 1, scv);
 }
 
+#ifndef V4_ROW_WAVES
+#define V4_ROW_WAVES (256 * 12)   // 256 CUs x 12 waves (three workgroups)
+#endif
 int64_t index_row_waves(int B, int Tq, int64_t vmax) {
   const int64_t rows = (int64_t)B * Tq;
   const int64_t nch = (vmax + 31) / 32;
-  int64_t per_row = (256 * 12 + rows - 1) / rows;   // 256 CUs x 12 waves (three workgroups)
+  int64_t per_row = (V4_ROW_WAVES + rows - 1) / rows;
   const int64_t cpw = (nch + per_row - 1) / per_row; // chunks per wave, then as few waves as that needs
   per_row = (nch + cpw - 1) / cpw;
   return (per_row + 3) / 4 * 4;

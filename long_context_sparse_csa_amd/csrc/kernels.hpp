@@ -157,7 +157,7 @@ struct AttendArgs {
   uint16_t* part_o;         // [B*Tq, splits, H, D] bf16, unnormalised (splits > 1)
   float* part_ml;           // [B*Tq, splits, H, 2]  (max, sum)
   int64_t rows_max;         // max rows (entries + window) over the block
-  float* logits2;           // nullptr, or [B*Tq, logits_stride, 64]: every row's logit
+  float* logits2;           // HCA only: nullptr, or [B*Tq, logits_stride, 64]: every row's logit
                             // per head (heads innermost, slots >= H unused) times
                             // log2(e), absent rows -inf; logits_stride >= rows
                             // rounded up to 128
@@ -165,7 +165,7 @@ struct AttendArgs {
   int sel_m;                // CSA: 0 or 1 = topk holds row indices; > 1 = topk
                             // [B*Tq, k / sel_m] holds blocks of sel_m rows
                             // (row b sel_m + u), -1 = empty
-  const float* mix_gates;   // nullptr, or [B*Tq, H, 3]: the stored output is
+  const float* mix_gates;   // CSA only: nullptr, or [B*Tq, H, 3]: the stored output is
                             // g1 * this + g0 * mix_o0 + g2 * mix_o2
   const uint16_t* mix_o0;   // bf16 [B*Tq, H, D]
   const uint16_t* mix_o2;
