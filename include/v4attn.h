@@ -117,14 +117,28 @@ int v4attn_compress(const uint16_t* raw, const float* tok_score,
  *   entries    u8 [B, ent_rows, D+R] out: entry j at row j (nullable when
  *              no entry completes)
  *   win        u8 [B, win_rows, D+R] out: the new token's row at win_row
+ *   seq_pos    host i64 [B], nullable: per-sequence token positions (a ragged
+ *              batch, B <= 64); then t must be their largest, sequence b's
+ *              raw rows are the L positions ending at seq_pos[b] (raw_pos0
+ *              is ignored) and each sequence pools its own completed entry
  * Errors: EINVAL for null/misaligned buffers, t outside the raw rows, a
  * window that starts before raw_pos0, j >= ent_rows or win_row out of range.
  */
 int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const float* pos_bias,
                          const float* gamma, int B, int L, int D, int R, int64_t raw_pos0,
-                         int m, int64_t t, float eps, float rope_base, uint8_t* entries,
+                         int m, int64_t t, const int64_t* seq_pos, float eps,
+                         float rope_base, uint8_t* entries,
                          int64_t ent_rows, uint8_t* win, int64_t win_rows, int64_t win_row,
                          void* stream);
+
+/*
+ * Ragged batches (v4attn_index_topk, v4attn_index_score,
+ * v4attn_topk_select, v4attn_csa_attend, v4attn_hca_attend): seq_pos is a
+ * nullable HOST array i64 [B] (B <= 64) of per-sequence positions; sequence
+ * b's query r is then at seq_pos[b] + r (its window buffer rows relative to
+ * seq_pos[b]), and q_pos0 must equal the largest of them (it sizes the
+ * workspaces and is validated as before).  NULL: every sequence at q_pos0.
+ */
 
 /*
  * v4attn_index_topk -- lightning-indexer scores and top-k selection.
@@ -155,7 +169,8 @@ size_t v4attn_index_topk_workspace(int B, int Tq, int64_t n_entries,
                                    int64_t q_pos0, int m, int k);
 int v4attn_index_topk(const uint16_t* q_idx, const float* w_idx,
                       const uint16_t* k_idx, int B, int Tq, int HI, int dI,
-                      int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m,
+                      int64_t Ncap, int64_t n_entries, int64_t q_pos0,
+                      const int64_t* seq_pos, int m,
                       int k, int32_t* topk, float* topk_score,
                       void* ws, size_t ws_bytes, void* stream);
 
@@ -175,12 +190,14 @@ int v4attn_index_topk(const uint16_t* q_idx, const float* w_idx,
  */
 int v4attn_index_score(const uint16_t* q_idx, const float* w_idx,
                        const uint16_t* k_idx, int B, int Tq, int HI, int dI,
-                       int64_t Ncap, int64_t n_entries, int64_t q_pos0, int m,
+                       int64_t Ncap, int64_t n_entries, int64_t q_pos0,
+                       const int64_t* seq_pos, int m,
                        float* scores, int64_t score_stride, void* stream);
 size_t v4attn_topk_select_workspace(int B, int Tq, int64_t n_entries,
                                     int64_t q_pos0, int m, int k);
 int v4attn_topk_select(const float* scores, int64_t score_stride, int B,
-                       int Tq, int64_t n_entries, int64_t q_pos0, int m, int k,
+                       int Tq, int64_t n_entries, int64_t q_pos0,
+                       const int64_t* seq_pos, int m, int k,
                        int32_t* topk, float* topk_score, void* ws,
                        size_t ws_bytes, void* stream);
 
@@ -288,7 +305,8 @@ int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries,
                       const int32_t* topk, const uint8_t* win,
                       const float* gamma_q, const float* sink,
                       int B, int Tq, int H, int D, int R, int64_t Ncap,
-                      int k, int W, int64_t q_pos0, float scale, float eps,
+                      int k, int W, int64_t q_pos0,
+                      const int64_t* seq_pos, float scale, float eps,
                       float rope_base, uint16_t* out, float* lse,
                       void* ws, size_t ws_bytes, void* stream);
 
@@ -311,7 +329,7 @@ int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries,
                       const uint8_t* win, const float* gamma_q,
                       const float* sink, int B, int Tq, int H, int D, int R,
                       int64_t Ncap, int64_t n_entries, int m, int W,
-                      int64_t q_pos0, float scale, float eps, float rope_base,
+                      int64_t q_pos0, const int64_t* seq_pos, float scale, float eps, float rope_base,
                       uint16_t* out, float* lse,
                       void* ws, size_t ws_bytes, void* stream);
 

@@ -54,6 +54,27 @@ int64_t vmax_of(int Tq, int64_t n_entries, int64_t q_pos0, int m) {
   return min64(n_entries, (q_pos0 + Tq) / m);
 }
 
+// Per-sequence positions (host array, nullable): every p >= 0 and their
+// largest equal to q_pos0, which sizes workspaces and is validated as
+// before.  Passed to the kernels by value.
+int load_seq_pos(const int64_t* seq_pos, int B, int64_t q_pos0, v4::SeqPos* sp, bool* ragged) {
+  *ragged = seq_pos != nullptr;
+  if (!seq_pos) return V4ATTN_OK;
+  if (B > v4::kMaxRagged)
+    return fail(V4ATTN_EUNSUPPORTED, "B = %d: per-sequence positions are built for B <= %d", B,
+                v4::kMaxRagged);
+  int64_t mx = -1;
+  for (int b = 0; b < B; ++b) {
+    if (seq_pos[b] < 0) return fail(V4ATTN_EINVAL, "negative position of sequence %d", b);
+    sp->p[b] = seq_pos[b];
+    mx = seq_pos[b] > mx ? seq_pos[b] : mx;
+  }
+  if (B > 0 && mx != q_pos0)
+    return fail(V4ATTN_EINVAL, "q_pos0 %lld must be the largest sequence position (%lld)",
+                (long long)q_pos0, (long long)mx);
+  return V4ATTN_OK;
+}
+
 struct TopkWs {
   v4::TopkPlan plan;
   size_t part_bytes, cand_bytes, run_bytes, total;
@@ -195,9 +216,9 @@ int v4attn_compress(const uint16_t* raw, const float* tok_score, const float* po
 
 int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const float* pos_bias,
                          const float* gamma, int B, int L, int D, int R, int64_t raw_pos0, int m,
-                         int64_t t, float eps, float rope_base, uint8_t* entries,
-                         int64_t ent_rows, uint8_t* win, int64_t win_rows, int64_t win_row,
-                         void* stream) {
+                         int64_t t, const int64_t* seq_pos, float eps, float rope_base,
+                         uint8_t* entries, int64_t ent_rows, uint8_t* win, int64_t win_rows,
+                         int64_t win_row, void* stream) {
   if (!raw || !gamma || !win) return fail(V4ATTN_EINVAL, "null raw, gamma or win");
   if (B < 0 || L < 0 || ent_rows < 0 || win_rows < 0)
     return fail(V4ATTN_EINVAL, "negative B, L, ent_rows or win_rows");
@@ -205,15 +226,23 @@ int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const floa
   if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
   if (!(eps >= 0.f) || !std::isfinite(eps) || !(rope_base > 0.f))
     return fail(V4ATTN_EINVAL, "bad eps or rope_base");
-  if (t < 0 || t < raw_pos0 || t >= raw_pos0 + L)
-    return fail(V4ATTN_EINVAL, "position %lld is not in the raw rows [%lld, %lld)", (long long)t,
-                (long long)raw_pos0, (long long)(raw_pos0 + L));
+  v4::SeqPos sp;
+  bool ragged;
+  if (int st = load_seq_pos(seq_pos, B, t, &sp, &ragged)) return st;
   if (win_row < 0 || win_row >= win_rows)
     return fail(V4ATTN_EINVAL, "win_row %lld outside [0, %lld)", (long long)win_row,
                 (long long)win_rows);
   if (!aligned16(raw) || !aligned16(win)) return fail(V4ATTN_EINVAL, "raw and win must be 16-byte aligned");
-  if ((t + 1) % m == 0) {
-    const int64_t j = (t + 1) / m - 1;
+  // every sequence's token (with per-sequence positions its raw rows are the
+  // L positions ending at it)
+  for (int b = 0; b < (ragged ? B : 1); ++b) {
+    const int64_t tb = ragged ? sp.p[b] : t;
+    const int64_t p0 = ragged ? tb - L + 1 : raw_pos0;
+    if (tb < 0 || tb < p0 || tb >= p0 + L)
+      return fail(V4ATTN_EINVAL, "position %lld is not in the raw rows [%lld, %lld)", (long long)tb,
+                  (long long)p0, (long long)(p0 + L));
+    if ((tb + 1) % m != 0) continue;
+    const int64_t j = (tb + 1) / m - 1;
     const int64_t lo = (j - 1) * (int64_t)m;
     const int64_t first = lo > 0 ? lo : 0;
     if (!tok_score || !pos_bias || !entries)
@@ -221,12 +250,14 @@ int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const floa
     if (!aligned16(entries)) return fail(V4ATTN_EINVAL, "entries must be 16-byte aligned");
     if (j >= ent_rows)
       return fail(V4ATTN_EINVAL, "entry %lld outside %lld entry rows", (long long)j, (long long)ent_rows);
-    if (first < raw_pos0)
+    if (first < p0)
       return fail(V4ATTN_EINVAL, "entry %lld needs positions from %lld but rows start at %lld",
-                  (long long)j, (long long)first, (long long)raw_pos0);
+                  (long long)j, (long long)first, (long long)p0);
   }
   v4::CompressStepArgs a{raw, tok_score, pos_bias, gamma, B, L, D, R, raw_pos0, m, t, eps,
                          v4::rope_turns(rope_base, R), entries, ent_rows, win, win_rows, win_row};
+  a.ragged = ragged;
+  if (ragged) a.pos = sp;
   return hip_status(v4::launch_compress_step(a, (hipStream_t)stream), "compress step launch");
 }
 
@@ -280,18 +311,22 @@ int check_score_args(const uint16_t* q_idx, const float* w_idx, const uint16_t* 
 
 hipError_t run_score(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx, int B,
                      int Tq, int HI, int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0,
-                     int m, float* scores, int64_t stride, hipStream_t st) {
+                     int m, float* scores, int64_t stride, const v4::SeqPos* sp, hipStream_t st) {
   const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
   v4::IndexScoreArgs ia{q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m,
                         vmax, scores, stride, v4::index_row_waves(B, Tq, vmax)};
+  ia.ragged = sp != nullptr;
+  if (sp) ia.pos = *sp;
   return v4::launch_index_score(ia, st);
 }
 
 hipError_t run_topk(const float* scores, int64_t stride, int B, int Tq, int64_t n_entries,
                     int64_t q_pos0, int m, int k, int32_t* topk, float* topk_score, void* ws,
-                    const TopkWs& w, hipStream_t st) {
+                    const TopkWs& w, hipStream_t st, const v4::SeqPos* sp = nullptr) {
   uint8_t* cb = static_cast<uint8_t*>(ws);
   v4::TopkArgs ta;
+  ta.ragged = sp != nullptr;
+  if (sp) ta.pos = *sp;
   ta.scores = scores;
   ta.score_stride = stride;
   ta.B = B;
@@ -374,23 +409,31 @@ hipError_t run_score_mxfp4(const uint8_t* q4, const uint8_t* q_sc, const float* 
 
 int v4attn_index_score(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx, int B,
                        int Tq, int HI, int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0,
-                       int m, float* scores, int64_t score_stride, void* stream) {
+                       const int64_t* seq_pos, int m, float* scores, int64_t score_stride,
+                       void* stream) {
   if (int st = check_score_args(q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m))
     return st;
+  v4::SeqPos sp;
+  bool ragged;
+  if (int st = load_seq_pos(seq_pos, B, q_pos0, &sp, &ragged)) return st;
   const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
   if (vmax > 0 && (!scores || score_stride < vmax))
     return fail(V4ATTN_EINVAL, "scores missing or score_stride %lld < %lld",
                 (long long)score_stride, (long long)vmax);
   return hip_status(run_score(q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m,
-                              scores, score_stride, (hipStream_t)stream),
+                              scores, score_stride, ragged ? &sp : nullptr, (hipStream_t)stream),
                     "index score launch");
 }
 
 int v4attn_topk_select(const float* scores, int64_t score_stride, int B, int Tq,
-                       int64_t n_entries, int64_t q_pos0, int m, int k, int32_t* topk,
-                       float* topk_score, void* ws, size_t ws_bytes, void* stream) {
+                       int64_t n_entries, int64_t q_pos0, const int64_t* seq_pos, int m, int k,
+                       int32_t* topk, float* topk_score, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (!topk) return fail(V4ATTN_EINVAL, "null topk");
   if (int st = check_index_common(B, Tq, n_entries, q_pos0, m)) return st;
+  v4::SeqPos sp;
+  bool ragged;
+  if (int st = load_seq_pos(seq_pos, B, q_pos0, &sp, &ragged)) return st;
   if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
   if (int st = check_topk_len(Tq, n_entries, q_pos0, m)) return st;
   const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
@@ -403,16 +446,19 @@ int v4attn_topk_select(const float* scores, int64_t score_stride, int B, int Tq,
   if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
   if ((int64_t)B * Tq == 0) return hip_status(hipSuccess, "");
   return hip_status(run_topk(scores, score_stride, B, Tq, n_entries, q_pos0, m, k, topk,
-                             topk_score, ws, w, (hipStream_t)stream),
+                             topk_score, ws, w, (hipStream_t)stream, ragged ? &sp : nullptr),
                     "top-k launch");
 }
 
 int v4attn_index_topk(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx, int B,
                       int Tq, int HI, int dI, int64_t Ncap, int64_t n_entries, int64_t q_pos0,
-                      int m, int k, int32_t* topk, float* topk_score, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      const int64_t* seq_pos, int m, int k, int32_t* topk, float* topk_score,
+                      void* ws, size_t ws_bytes, void* stream) {
   if (int st = check_score_args(q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m))
     return st;
+  v4::SeqPos sp;
+  bool ragged;
+  if (int st = load_seq_pos(seq_pos, B, q_pos0, &sp, &ragged)) return st;
   if (!topk) return fail(V4ATTN_EINVAL, "null topk");
   if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
   if (int st = check_topk_len(Tq, n_entries, q_pos0, m)) return st;
@@ -425,10 +471,10 @@ int v4attn_index_topk(const uint16_t* q_idx, const float* w_idx, const uint16_t*
   uint8_t* base = static_cast<uint8_t*>(ws);
   float* scores = reinterpret_cast<float*>(base);
   hipError_t e = run_score(q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m,
-                           scores, w.score_stride, st);
+                           scores, w.score_stride, ragged ? &sp : nullptr, st);
   if (e != hipSuccess) return hip_status(e, "index score launch");
   return hip_status(run_topk(scores, w.score_stride, B, Tq, n_entries, q_pos0, m, k, topk,
-                             topk_score, base + w.scores_bytes, w.tk, st),
+                             topk_score, base + w.scores_bytes, w.tk, st, ragged ? &sp : nullptr),
                     "top-k launch");
 }
 
@@ -526,11 +572,14 @@ size_t v4attn_csa_attend_workspace(int B, int Tq, int H, int D, int k, int W) {
 int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
                       const uint8_t* win, const float* gamma_q, const float* sink, int B, int Tq,
                       int H, int D, int R, int64_t Ncap, int k, int W, int64_t q_pos0,
-                      float scale, float eps, float rope_base, uint16_t* out, float* lse,
-                      void* ws, size_t ws_bytes, void* stream) {
+                      const int64_t* seq_pos, float scale, float eps, float rope_base,
+                      uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (int st = check_attend_common(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, W,
                                    q_pos0, scale, eps, rope_base, out))
     return st;
+  v4::SeqPos sp;
+  bool ragged;
+  if (int st = load_seq_pos(seq_pos, B, q_pos0, &sp, &ragged)) return st;
   if (!topk) return fail(V4ATTN_EINVAL, "null topk");
   if (k < 1 || k > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "k = %d: 1 <= k <= %d is built", k, kMaxK);
   int splits = 1;
@@ -546,6 +595,8 @@ int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries, const int32_t* 
   a.out = out; a.lse = lse; a.splits = splits;
   attend_ws_layout(a, ws);
   a.rows_max = (int64_t)k + W;
+  a.ragged = ragged;
+  if (ragged) a.pos = sp;
   return hip_status(v4::launch_attend(a, (hipStream_t)stream), "CSA attend launch");
 }
 
@@ -557,12 +608,15 @@ size_t v4attn_hca_attend_workspace(int B, int Tq, int H, int D, int64_t n_entrie
 
 int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* win,
                       const float* gamma_q, const float* sink, int B, int Tq, int H, int D, int R,
-                      int64_t Ncap, int64_t n_entries, int m, int W, int64_t q_pos0, float scale,
-                      float eps, float rope_base, uint16_t* out, float* lse, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      int64_t Ncap, int64_t n_entries, int m, int W, int64_t q_pos0,
+                      const int64_t* seq_pos, float scale, float eps, float rope_base,
+                      uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (int st = check_attend_common(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, W,
                                    q_pos0, scale, eps, rope_base, out))
     return st;
+  v4::SeqPos sp;
+  bool ragged;
+  if (int st = load_seq_pos(seq_pos, B, q_pos0, &sp, &ragged)) return st;
   if (n_entries < 0 || n_entries > Ncap) return fail(V4ATTN_EINVAL, "need 0 <= n_entries <= Ncap");
   if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
   const int64_t rows_max = vmax_of(Tq, n_entries, q_pos0, m) + W;
@@ -579,6 +633,8 @@ int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
   a.out = out; a.lse = lse; a.splits = splits;
   attend_ws_layout(a, ws);
   a.rows_max = rows_max;
+  a.ragged = ragged;
+  if (ragged) a.pos = sp;
   return hip_status(v4::launch_attend(a, (hipStream_t)stream), "HCA attend launch");
 }
 

@@ -153,7 +153,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   const int split = blockIdx.x;
   if (split >= a.splits) return;   // a layer with fewer splits than the grid
   const int b = qr / a.Tq, r = qr % a.Tq;
-  const int64_t t = a.q_pos0 + r;
+  const int64_t qpos = a.ragged ? a.pos.p[b] : a.q_pos0;   // this sequence's first query
+  const int64_t t = qpos + r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;   // lane column (head / row / dim), k group
   const int head = wave * 16 + c;
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   const int ent_loc = (int)max((int64_t)0, min(rs.n_ent, row_end) - row_beg);  // entry rows here
   const uint8_t* ent_b = a.entries + (int64_t)b * a.Ncap * ROW;
   const uint8_t* win_b = a.win + ((int64_t)b * (a.Tq + a.W - 1) +
-                                  (rs.win_lo - (a.q_pos0 - (a.W - 1)))) * ROW;
+                                  (rs.win_lo - (qpos - (a.W - 1)))) * ROW;
   const int win_first = (int)(rs.n_ent - row_beg);   // split-local row of the first window row
 
   // The loads the first barrier waits for go out first (a wave's vector loads
@@ -764,7 +765,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   constexpr int HPW = 256 / QPH;      // heads per workgroup
   const int qr = blockIdx.y;
   const int h0 = blockIdx.x * HPW;
-  const int64_t t = a.q_pos0 + (qr % a.Tq);
+  const int64_t t = (a.ragged ? a.pos.p[qr / a.Tq] : a.q_pos0) + (qr % a.Tq);
   const int S = a.splits;
   __shared__ float s_w[HPW][64];
   __shared__ float s_cs[R / 2][2];

@@ -239,9 +239,14 @@ __global__ __launch_bounds__(kPoolThreads) void compress_step_kernel(
     const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
     int64_t raw_pos0, int m, int64_t t, float eps, const RopeTurns rope,
     uint8_t* __restrict__ ent, int64_t ent_rows, uint8_t* __restrict__ win, int64_t win_rows,
-    int64_t win_row) {
+    int64_t win_row, const bool ragged, const SeqPos pos) {
   constexpr int D = VPL * 64;
   const int b = blockIdx.y;
+  if (ragged) {   // this sequence's token; its raw rows end at it
+    t = pos.p[b];
+    raw_pos0 = t - L + 1;
+    if (blockIdx.x == 0 && gridDim.x == 2 && (t + 1) % m != 0) return;   // no entry completes
+  }
   if (blockIdx.x == gridDim.x - 1) {
     if (threadIdx.x >= 64) return;
     const int lane = threadIdx.x;
@@ -258,12 +263,16 @@ __global__ __launch_bounds__(kPoolThreads) void compress_step_kernel(
 
 hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
-  const bool pool = (a.t + 1) % a.m == 0;
+  bool pool = (a.t + 1) % a.m == 0;
+  if (a.ragged) {
+    pool = false;
+    for (int b = 0; b < a.B; ++b) pool = pool || (a.pos.p[b] + 1) % a.m == 0;
+  }
   dim3 grid(pool ? 2 : 1, a.B);
 #define V4_STEP(VPL)                                                                        \
   compress_step_kernel<VPL><<<grid, kPoolThreads, 0, st>>>(                                 \
       a.raw, a.tok_score, a.pos_bias, a.gamma, a.L, a.R, a.raw_pos0, a.m, a.t, a.eps, a.rope, \
-      a.ent, a.ent_rows, a.win, a.win_rows, a.win_row)
+      a.ent, a.ent_rows, a.win, a.win_rows, a.win_row, a.ragged, a.pos)
   switch (a.D) {
     case 128: V4_STEP(2); break;
     case 256: V4_STEP(4); break;

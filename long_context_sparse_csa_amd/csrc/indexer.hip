@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
   constexpr int NL = 32 / KPI;       // load instructions per 32-key chunk
   const int b = blockIdx.z, r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t = a.q_pos0 + r;
+  const int64_t t = (a.ragged ? a.pos.p[b] : a.q_pos0) + r;
   int64_t V = (t + 1) / a.m;
   if (V > a.n_entries) V = a.n_entries;
   // 32-key chunks are dealt round-robin over the row's waves, so at any time
@@ -175,8 +175,9 @@ __global__ __launch_bounds__(kBlkWaves * 64) void index_score_block_kernel(Index
   const int b = blockIdx.z, qg = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = qg * kBlkQ + wave * kBlkQPW;      // this wave's first query
+  const int64_t qpos = a.ragged ? a.pos.p[b] : a.q_pos0;
   auto visible = [&](int rr) {
-    const int64_t t = a.q_pos0 + rr;
+    const int64_t t = qpos + rr;
     const int64_t v = (t + 1) / a.m;
     return v < a.n_entries ? v : a.n_entries;
   };

@@ -10,6 +10,13 @@
 
 namespace v4 {
 
+// Per-sequence positions of a ragged batch (decode path), passed by value
+// with the kernel arguments: sequence b's first query is at p[b].
+constexpr int kMaxRagged = 64;
+struct SeqPos {
+  int64_t p[kMaxRagged];
+};
+
 struct CompressArgs {
   const uint16_t* raw;
   const float* tok_score;
@@ -44,6 +51,8 @@ struct CompressStepArgs {
   int64_t ent_rows;
   uint8_t* win;            // [B, win_rows, D+R]
   int64_t win_rows, win_row;
+  bool ragged;             // token of sequence b at pos.p[b]; raw rows hold its
+  SeqPos pos;              // positions p[b]-L+1 .. p[b] (t, raw_pos0 unused)
 };
 hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st);
 
@@ -59,6 +68,8 @@ struct IndexScoreArgs {
   float* scores;          // [B*Tq, score_stride]
   int64_t score_stride;
   int64_t row_waves;      // waves sharing one query row (multiple of 4)
+  bool ragged;            // query block of sequence b starts at pos.p[b]
+  SeqPos pos;
 };
 // Waves per query row that spread a launch over three workgroups per CU.
 int64_t index_row_waves(int B, int Tq, int64_t vmax);
@@ -131,6 +142,8 @@ struct TopkArgs {
   unsigned* run_key;       // [rows, k] keys of a partial selection
   int32_t* topk;           // [B*Tq, k]
   float* topk_score;       // nullable
+  bool ragged;             // query block of sequence b starts at pos.p[b]
+  SeqPos pos;
 };
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& plan, hipStream_t st);
 
@@ -169,6 +182,8 @@ struct AttendArgs {
                             // g1 * this + g0 * mix_o0 + g2 * mix_o2
   const uint16_t* mix_o0;   // bf16 [B*Tq, H, D]
   const uint16_t* mix_o2;
+  bool ragged;              // query block of sequence b starts at pos.p[b]
+  SeqPos pos;               // (its window buffer rows are relative to it)
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 

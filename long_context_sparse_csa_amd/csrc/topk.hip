@@ -60,7 +60,7 @@ TopkPlan topk_plan(int64_t vmax, int k) {
 }
 
 __device__ __forceinline__ int64_t visible_of(const TopkArgs& a, int64_t qr) {
-  const int64_t t = a.q_pos0 + (qr % a.Tq);
+  const int64_t t = (a.ragged ? a.pos.p[qr / a.Tq] : a.q_pos0) + (qr % a.Tq);
   const int64_t v = (t + 1) / a.m;
   return v < a.n_entries ? v : a.n_entries;
 }

@@ -37,12 +37,12 @@ _SIGS = {
     "v4attn_last_error": (_c.c_char_p, []),
     "v4attn_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _I, _L, _I, _F, _F, _P, _L,
                              _P]),
-    "v4attn_compress_step": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _L, _F, _F, _P, _L, _P,
-                                  _L, _L, _P]),
+    "v4attn_compress_step": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _L, _P, _F, _F, _P, _L,
+                                  _P, _L, _L, _P]),
     "v4attn_index_topk_workspace": (_Z, [_I, _I, _L, _L, _I, _I]),
-    "v4attn_index_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _I, _P, _P, _P, _Z,
+    "v4attn_index_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _P, _I, _I, _P, _P, _P, _Z,
                                _P]),
-    "v4attn_index_score": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _P, _L, _P]),
+    "v4attn_index_score": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _P, _I, _P, _L, _P]),
     "v4attn_index_score_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _P, _L,
                                     _P]),
     "v4attn_index_topk_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _I, _P,
@@ -52,13 +52,13 @@ _SIGS = {
     "v4attn_index_topk_mxfp4": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _I, _I, _P,
                                      _P, _P, _Z, _P]),
     "v4attn_topk_select_workspace": (_Z, [_I, _I, _L, _L, _I, _I]),
-    "v4attn_topk_select": (_I, [_P, _L, _I, _I, _L, _L, _I, _I, _P, _P, _P, _Z, _P]),
+    "v4attn_topk_select": (_I, [_P, _L, _I, _I, _L, _L, _P, _I, _I, _P, _P, _P, _Z, _P]),
     "v4attn_csa_attend_workspace": (_Z, [_I, _I, _I, _I, _I, _I]),
-    "v4attn_csa_attend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _I, _I, _L, _F,
-                               _F, _F, _P, _P, _P, _Z, _P]),
+    "v4attn_csa_attend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _I, _I, _L, _P,
+                               _F, _F, _F, _P, _P, _P, _Z, _P]),
     "v4attn_hca_attend_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I]),
-    "v4attn_hca_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I, _L, _F,
-                               _F, _F, _P, _P, _P, _Z, _P]),
+    "v4attn_hca_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I, _L, _P,
+                               _F, _F, _F, _P, _P, _P, _Z, _P]),
     "v4attn_csa_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _I, _I]),
     "v4attn_csa_attend_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _I, _I,
                                         _L, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -137,6 +137,21 @@ def _need(t, name, dtype, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
+def _seq_pos(seq_pos, B, q_pos0):
+    """Per-sequence positions as a host int64 array (kept alive by the
+    caller for the call) and the q_pos0 the library expects with it (their
+    largest)."""
+    if seq_pos is None:
+        if q_pos0 is None:
+            raise ValueError("q_pos0 (or seq_pos) is required")
+        return None, None, int(q_pos0)
+    sp = [int(x) for x in seq_pos]
+    if len(sp) != B:
+        raise ValueError(f"seq_pos has {len(sp)} positions for {B} sequences")
+    arr = (_c.c_int64 * max(B, 1))(*sp)
+    return arr, _c.cast(arr, _c.c_void_p), max(sp) if sp else int(q_pos0 or 0)
+
+
 def _workspace(nbytes, device, ws):
     if nbytes == 0:
         return ws
@@ -173,11 +188,13 @@ def compress_pool(raw, tok_score, pos_bias, gamma, out, *, raw_pos0, m, entry0, 
     return out
 
 
-def compress_step(raw, tok_score, pos_bias, gamma, entries, win, *, raw_pos0, m, t, win_row,
-                  eps=1e-6, rope_base=10000.0, R=64):
+def compress_step(raw, tok_score, pos_bias, gamma, entries, win, *, m, win_row, raw_pos0=None,
+                  t=None, seq_pos=None, eps=1e-6, rope_base=10000.0, R=64):
     """One decode step of the compressor in one launch: the window row of the
     token at position t -> win[b, win_row], and, when (t+1) % m == 0, the
-    entry j = (t+1)/m - 1 it completes -> entries[b, j]."""
+    entry j = (t+1)/m - 1 it completes -> entries[b, j].  With seq_pos (one
+    position per sequence) each sequence's raw rows are the L positions
+    ending at its own token."""
     _need(raw, "raw", torch.bfloat16, 3)
     _need(tok_score, "tok_score", torch.float32, 2)
     _need(pos_bias, "pos_bias", torch.float32, 1)
@@ -189,8 +206,10 @@ def compress_step(raw, tok_score, pos_bias, gamma, entries, win, *, raw_pos0, m,
             or entries.shape[0] != B or entries.shape[2] != D + R or win.shape[0] != B \
             or win.shape[2] != D + R:
         raise ValueError("shape mismatch")
+    arr, sp, t = _seq_pos(seq_pos, B, t)
+    raw_pos0 = t - L + 1 if raw_pos0 is None else raw_pos0
     check(lib().v4attn_compress_step(_ptr(raw), _ptr(tok_score), _ptr(pos_bias), _ptr(gamma), B, L,
-                                     D, R, int(raw_pos0), int(m), int(t), float(eps),
+                                     D, R, int(raw_pos0), int(m), int(t), sp, float(eps),
                                      float(rope_base), _ptr(entries), entries.shape[1], _ptr(win),
                                      win.shape[1], int(win_row), _stream(raw)))
     return entries, win
@@ -220,8 +239,8 @@ def index_topk_workspace_bytes(B, Tq, n_entries, q_pos0, m, k):
     return lib().v4attn_index_topk_workspace(B, Tq, n_entries, q_pos0, m, k)
 
 
-def index_topk(q_idx, w_idx, k_idx, *, n_entries, q_pos0, m, k, topk=None, topk_score=None,
-               want_scores=False, workspace=None):
+def index_topk(q_idx, w_idx, k_idx, *, n_entries, m, k, q_pos0=None, seq_pos=None, topk=None,
+               topk_score=None, want_scores=False, workspace=None):
     """Top-k entry indices per query (int32 [B, Tq, k], ascending, -1 padded)."""
     _need(q_idx, "q_idx", torch.bfloat16, 4)
     _need(w_idx, "w_idx", torch.float32, 3)
@@ -236,10 +255,11 @@ def index_topk(q_idx, w_idx, k_idx, *, n_entries, q_pos0, m, k, topk=None, topk_
     _need(topk, "topk", torch.int32, 3)
     if want_scores and topk_score is None:
         topk_score = torch.empty((B, Tq, k), dtype=torch.float32, device=dev)
+    arr, sp, q_pos0 = _seq_pos(seq_pos, B, q_pos0)
     nbytes = index_topk_workspace_bytes(B, Tq, n_entries, q_pos0, m, k)
     workspace = _workspace(nbytes, dev, workspace)
     check(lib().v4attn_index_topk(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, Tq, HI, dI, Ncap,
-                                  int(n_entries), int(q_pos0), int(m), int(k), _ptr(topk),
+                                  int(n_entries), int(q_pos0), sp, int(m), int(k), _ptr(topk),
                                   _ptr(topk_score), _ptr(workspace), nbytes, _stream(q_idx)))
     return topk, topk_score
 
@@ -250,7 +270,7 @@ def score_stride(Tq, n_entries, q_pos0, m):
     return (v + 63) // 64 * 64
 
 
-def index_score(q_idx, w_idx, k_idx, *, n_entries, q_pos0, m, scores=None):
+def index_score(q_idx, w_idx, k_idx, *, n_entries, m, q_pos0=None, seq_pos=None, scores=None):
     """Indexer scores f32 [B*Tq, stride]; row b*Tq+r is valid for j < V_t."""
     _need(q_idx, "q_idx", torch.bfloat16, 4)
     _need(w_idx, "w_idx", torch.float32, 3)
@@ -258,12 +278,13 @@ def index_score(q_idx, w_idx, k_idx, *, n_entries, q_pos0, m, scores=None):
     B, Tq, HI, dI = q_idx.shape
     if tuple(w_idx.shape) != (B, Tq, HI) or k_idx.shape[0] != B or k_idx.shape[2] != dI:
         raise ValueError("shape mismatch")
+    arr, sp, q_pos0 = _seq_pos(seq_pos, B, q_pos0)
     if scores is None:
         scores = torch.empty((B * Tq, max(score_stride(Tq, n_entries, q_pos0, m), 1)),
                              dtype=torch.float32, device=q_idx.device)
     _need(scores, "scores", torch.float32, 2)
     check(lib().v4attn_index_score(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), B, Tq, HI, dI,
-                                   k_idx.shape[1], int(n_entries), int(q_pos0), int(m),
+                                   k_idx.shape[1], int(n_entries), int(q_pos0), sp, int(m),
                                    _ptr(scores), scores.shape[1], _stream(q_idx)))
     return scores
 
@@ -367,8 +388,8 @@ def topk_select_workspace_bytes(B, Tq, n_entries, q_pos0, m, k):
     return lib().v4attn_topk_select_workspace(B, Tq, n_entries, q_pos0, m, k)
 
 
-def topk_select(scores, *, B, Tq, n_entries, q_pos0, m, k, topk=None, topk_score=None,
-                want_scores=False, workspace=None):
+def topk_select(scores, *, B, Tq, n_entries, m, k, q_pos0=None, seq_pos=None, topk=None,
+                topk_score=None, want_scores=False, workspace=None):
     """Top-k selection from an index_score buffer."""
     _need(scores, "scores", torch.float32, 2)
     dev = scores.device
@@ -377,10 +398,11 @@ def topk_select(scores, *, B, Tq, n_entries, q_pos0, m, k, topk=None, topk_score
     _need(topk, "topk", torch.int32, 3)
     if want_scores and topk_score is None:
         topk_score = torch.empty((B, Tq, k), dtype=torch.float32, device=dev)
+    arr, sp, q_pos0 = _seq_pos(seq_pos, B, q_pos0)
     nbytes = topk_select_workspace_bytes(B, Tq, n_entries, q_pos0, m, k)
     workspace = _workspace(nbytes, dev, workspace)
     check(lib().v4attn_topk_select(_ptr(scores), scores.shape[1], B, Tq, int(n_entries),
-                                   int(q_pos0), int(m), int(k), _ptr(topk), _ptr(topk_score),
+                                   int(q_pos0), sp, int(m), int(k), _ptr(topk), _ptr(topk_score),
                                    _ptr(workspace), nbytes, _stream(scores)))
     return topk, topk_score
 
@@ -405,8 +427,9 @@ def hca_attend_workspace_bytes(B, Tq, H, D, n_entries, m, q_pos0, W):
     return lib().v4attn_hca_attend_workspace(B, Tq, H, D, n_entries, m, q_pos0, W)
 
 
-def csa_attend(q, entries, topk, win, gamma_q, sink, *, q_pos0, W, scale=None, eps=1e-6,
-               rope_base=10000.0, R=64, out=None, lse=None, want_lse=False, workspace=None):
+def csa_attend(q, entries, topk, win, gamma_q, sink, *, W, q_pos0=None, seq_pos=None,
+               scale=None, eps=1e-6, rope_base=10000.0, R=64, out=None, lse=None,
+               want_lse=False, workspace=None):
     """Sparse shared-KV attention over the top-k entries plus the window."""
     _need(q, "q", torch.bfloat16, 4)
     _need(entries, "entries", torch.uint8, 3)
@@ -422,18 +445,19 @@ def csa_attend(q, entries, topk, win, gamma_q, sink, *, q_pos0, W, scale=None, e
         raise ValueError("shape mismatch")
     scale = D ** -0.5 if scale is None else scale
     out, lse = _attend_io(q, out, lse, want_lse)
+    arr, sp, q_pos0 = _seq_pos(seq_pos, B, q_pos0)
     nbytes = csa_attend_workspace_bytes(B, Tq, H, D, k, W)
     workspace = _workspace(nbytes, q.device, workspace)
     check(lib().v4attn_csa_attend(_ptr(q), _ptr(entries), _ptr(topk), _ptr(win), _ptr(gamma_q),
                                   _ptr(sink), B, Tq, H, D, R, entries.shape[1], k, int(W),
-                                  int(q_pos0), float(scale), float(eps), float(rope_base),
+                                  int(q_pos0), sp, float(scale), float(eps), float(rope_base),
                                   _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(q)))
     return out, lse
 
 
-def hca_attend(q, entries, win, gamma_q, sink, *, n_entries, m, q_pos0, W, scale=None,
-               eps=1e-6, rope_base=10000.0, R=64, out=None, lse=None, want_lse=False,
-               workspace=None):
+def hca_attend(q, entries, win, gamma_q, sink, *, n_entries, m, W, q_pos0=None, seq_pos=None,
+               scale=None, eps=1e-6, rope_base=10000.0, R=64, out=None, lse=None,
+               want_lse=False, workspace=None):
     """Dense shared-KV attention over every visible entry plus the window."""
     _need(q, "q", torch.bfloat16, 4)
     _need(entries, "entries", torch.uint8, 3)
@@ -447,11 +471,12 @@ def hca_attend(q, entries, win, gamma_q, sink, *, n_entries, m, q_pos0, W, scale
         raise ValueError("shape mismatch")
     scale = D ** -0.5 if scale is None else scale
     out, lse = _attend_io(q, out, lse, want_lse)
+    arr, sp, q_pos0 = _seq_pos(seq_pos, B, q_pos0)
     nbytes = hca_attend_workspace_bytes(B, Tq, H, D, n_entries, m, q_pos0, W)
     workspace = _workspace(nbytes, q.device, workspace)
     check(lib().v4attn_hca_attend(_ptr(q), _ptr(entries), _ptr(win), _ptr(gamma_q), _ptr(sink), B,
                                   Tq, H, D, R, entries.shape[1], int(n_entries), int(m), int(W),
-                                  int(q_pos0), float(scale), float(eps), float(rope_base),
+                                  int(q_pos0), sp, float(scale), float(eps), float(rope_base),
                                   _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(q)))
     return out, lse
 

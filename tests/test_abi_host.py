@@ -71,12 +71,17 @@ def test_compress_rejects(kw, status):
     assert L().v4attn_last_error() != b""
 
 
+def _positions(*p):
+    return ctypes.cast((ctypes.c_int64 * len(p))(*p), ctypes.c_void_p)
+
+
 def _step(**kw):
     a = dict(raw=FAKE, s=FAKE, b=FAKE, g=FAKE, B=2, L=8, D=512, R=64, raw_pos0=100, m=4, t=107,
-             ent=FAKE, ent_rows=27, win=FAKE, win_rows=128, win_row=127)
+             ent=FAKE, ent_rows=27, win=FAKE, win_rows=128, win_row=127, sp=None)
     a.update(kw)
     return L().v4attn_compress_step(a["raw"], a["s"], a["b"], a["g"], a["B"], a["L"], a["D"],
-                                    a["R"], a["raw_pos0"], a["m"], a["t"], 1e-6, 1e4, a["ent"],
+                                    a["R"], a["raw_pos0"], a["m"], a["t"], a["sp"], 1e-6, 1e4,
+                                    a["ent"],
                                     a["ent_rows"], a["win"], a["win_rows"], a["win_row"], None)
 
 
@@ -91,6 +96,11 @@ def _step(**kw):
     (dict(win_row=128), -1),
     (dict(m=0), -2),
     (dict(D=384), -2),
+    # per-sequence positions: t must be the largest; each sequence's entry checked
+    (dict(sp=_positions(107, 99), t=106), -1),
+    (dict(sp=_positions(107, -1)), -1),
+    (dict(sp=_positions(107, 103), ent_rows=26), -1),   # sequence 0 completes entry 26
+    (dict(sp=_positions(107, 103), L=7), -1),           # window of entry 26 needs 8 rows
 ])
 def test_compress_step_rejects(kw, status):
     assert _step(**kw) == status
@@ -107,7 +117,8 @@ def _index(**kw):
              m=4, k_=64, topk=FAKE, ts=None, ws=FAKE, ws_bytes=0)
     a.update(kw)
     return L().v4attn_index_topk(a["q"], a["w"], a["k"], a["B"], a["Tq"], a["HI"], a["dI"],
-                                 a["Ncap"], a["n"], a["q_pos0"], a["m"], a["k_"], a["topk"],
+                                 a["Ncap"], a["n"], a["q_pos0"], a.get("sp"), a["m"], a["k_"],
+                                 a["topk"],
                                  a["ts"], a["ws"], a["ws_bytes"], None)
 
 
@@ -198,7 +209,8 @@ def _csa(**kw):
     a.update(kw)
     return L().v4attn_csa_attend(a["q"], a["e"], a["t"], a["w"], a["g"], a["s"], a["B"], a["Tq"],
                                  a["H"], a["D"], a["R"], a["Ncap"], a["k"], a["W"], a["q_pos0"],
-                                 a["scale"], a["eps"], a["base"], a["out"], a["lse"], a["ws"],
+                                 a.get("sp"), a["scale"], a["eps"], a["base"], a["out"], a["lse"],
+                                 a["ws"],
                                  a["ws_bytes"], None)
 
 
@@ -214,6 +226,8 @@ def _csa(**kw):
     (dict(scale=float("nan")), -1),
     (dict(out=MISALIGNED), -1),
     (dict(q_pos0=-5), -1),
+    (dict(sp=_positions(500, 501), B=2), -1),  # q_pos0 is not the largest position
+    (dict(sp=_positions(*range(65)), B=65, q_pos0=64), -2),   # more sequences than built
 ])
 def test_csa_attend_rejects(kw, status):
     assert _csa(**kw) == status
@@ -221,14 +235,14 @@ def test_csa_attend_rejects(kw, status):
 
 def test_hca_attend_rejects():
     f = L().v4attn_hca_attend
-    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 512, 64, 10, 11, 128, 128, 5000, 0.04, 1e-6,
-            1e4, FAKE, None, FAKE, 0, None]
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 512, 64, 10, 11, 128, 128, 5000, None, 0.04,
+            1e-6, 1e4, FAKE, None, FAKE, 0, None]
     assert f(*args) == -1          # n_entries > Ncap
     args[11] = 10
     args[12] = 0
     assert f(*args) == -2          # m = 0
     args[12] = 128
-    args[21] = 0
+    args[22] = 0
     # 32 sequences at 1M need split partials: workspace too small
     args[5], args[10], args[11], args[14] = 32, 8192, 8192, (1 << 20) - 1
     assert f(*args) == -3
