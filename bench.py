@@ -23,12 +23,14 @@ context (both layers) and reports MFMA fractions for scoring and attention.
 prefill indexer with the FP8 (E4M3, one scale per row) and MXFP4 lightning
 indexers; the headline value keeps the bf16 indexer keys of the workload
 definition.  An "nsa_variant" section times the NSA-style compress-select-
-window layer at the same 1M-token decode shape.  A "backward" section times
+window layer at the same 1M-token decode shape.  A "ragged_decode" section runs the same step with each
+sequence at its own position (128K to 1M).  A "backward" section times
 the CSA layer's training step on the prefill chunk (attention, indexer KL
 and compressor backward).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
-                    [--no-fp8] [--no-nsa] [--nsa-only] [--no-backward] [--backward-only] [--prefill-only] [--graph] [--counters]
+                    [--no-fp8] [--no-nsa] [--nsa-only] [--no-ragged]
+                    [--no-backward] [--backward-only] [--prefill-only] [--graph] [--counters]
 """
 
 import argparse
@@ -69,12 +71,12 @@ def build_inputs(dev, rotate):
     return decode.build_inputs(CSA_1M, HCA_1M, dev, rotate)
 
 
-def make_step(inp, dev):
+def make_step(inp, dev, csa_pos=None, hca_pos=None):
     """(name, fn) launches of one eager step (HCA cache copies rotate), and
-    the DecodeStep behind them."""
+    the DecodeStep behind them (optionally a ragged batch)."""
     from long_context_sparse_csa_amd import decode
     from long_context_sparse_csa_amd.configs import CSA_1M, HCA_1M
-    st = decode.DecodeStep(inp, CSA_1M, HCA_1M, dev)
+    st = decode.DecodeStep(inp, CSA_1M, HCA_1M, dev, csa_pos=csa_pos, hca_pos=hca_pos)
     state = {"i": 0}
     calls = [st.calls(r) for r in range(len(inp["hca"]["entries"]))]
 
@@ -485,6 +487,35 @@ def backward_section(dev, reps):
     }
 
 
+def ragged_section(dev, inp, reps):
+    """The decode step with a ragged batch: the same caches and calls, each
+    sequence's new token at its own position -- CSA sequence b at
+    (b + 1) 2^17 - 1, HCA sequence b at (b + 1) 2^15 - 1 (lengths 128K to 1M,
+    mean 0.56M) -- timed like the headline (calls launched one by one).
+    The indexer reads only each sequence's visible keys, so its algorithmic
+    bytes are sum_b V_b (256 + ...) per step."""
+    from long_context_sparse_csa_amd.configs import CSA_1M as c, HCA_1M as h
+    csa_pos = [(b + 1) * (1 << 17) - 1 for b in range(c.B)]
+    hca_pos = [(b + 1) * (1 << 15) - 1 for b in range(h.B)]
+    launches, _ = make_step(inp, dev, csa_pos=csa_pos, hca_pos=hca_pos)
+    ms, _ = run_timed(launches, reps, 5)
+    br = run_breakdown(launches, 20)
+    vis = sum(min(c.T // c.m, (p + 1) // c.m) for p in csa_pos)
+    idx_bytes = vis * c.dI * 2 + c.B * (c.HI * c.dI * 2 + c.HI * 4 + 0)
+    t_csa = sum(br[k] for k in ("csa_compress", "index_score", "topk_select", "csa_attend"))
+    t_hca = sum(br[k] for k in ("hca_compress", "hca_attend"))
+    return {
+        "workload": "decode_ragged: CSA B=8 at positions (b+1) 2^17 - 1, HCA B=32 at "
+                    "(b+1) 2^15 - 1 (the decode_1m_csa_hca caches)",
+        "step_us": round(ms * 1e3, 2),
+        "query_token_layers_per_s": round((c.B + h.B) / (ms * 1e-3), 1),
+        "csa_layer_us": round(t_csa, 2), "hca_layer_us": round(t_hca, 2),
+        "kernels_us": {k: round(v, 2) for k, v in br.items()},
+        "index_score_GBps": round(idx_bytes / (br["index_score"] * 1e-6) / 1e9, 1),
+        "index_score_hbm_frac": round(idx_bytes / (br["index_score"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def cpu_baseline(inp, budget_s):
     """The float64 oracle on a bounded sample of the same inputs: whole CSA
     and HCA layers for single sequences, alternating, until the budget."""
@@ -569,6 +600,8 @@ def main():
                     help="skip the 4096-token prefill section")
     ap.add_argument("--no-nsa", action="store_true",
                     help="skip the NSA-style variant section")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged-batch decode section")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the CSA layer backward section")
     ap.add_argument("--backward-only", action="store_true",
@@ -680,6 +713,10 @@ def main():
         "roofline": roofline,
         "wall_s": round(wall, 3),
     }
+    if not args.no_ragged:
+        log("ragged decode")
+        res["ragged_decode"] = ragged_section(dev, inp, args.steps)
+        log("ragged decode: " + json.dumps(res["ragged_decode"]))
     if not args.no_prefill:
         log("prefill chunk")
         res["prefill"] = prefill_section(dev, 3)

@@ -316,7 +316,30 @@ hipError_t run_score(const uint16_t* q_idx, const float* w_idx, const uint16_t* 
   v4::IndexScoreArgs ia{q_idx, w_idx, k_idx, B, Tq, HI, dI, Ncap, n_entries, q_pos0, m,
                         vmax, scores, stride, v4::index_row_waves(B, Tq, vmax)};
   ia.ragged = sp != nullptr;
-  if (sp) ia.pos = *sp;
+  if (sp) {
+    ia.pos = *sp;
+    if (Tq == 1) {
+      // workgroups in proportion to each sequence's visible entries (the
+      // launch's total as for B rows of the longest), whole multiples of 4 waves
+      int64_t tot = 0, vis[v4::kMaxRagged];
+      for (int b = 0; b < B; ++b) {
+        const int64_t v = min64(n_entries, (sp->p[b] + 1) / m);
+        vis[b] = v;
+        tot += v;
+      }
+      const int64_t budget = (int64_t)B * (ia.row_waves / 4);
+      int acc = 0;
+      for (int b = 0; b < B; ++b) {
+        ia.wg_start[b] = acc;
+        int64_t n = tot > 0 ? (budget * vis[b] + tot - 1) / tot : 1;
+        const int64_t need = (vis[b] + 127) / 128;   // at least one chunk per wave
+        if (n > need) n = need;
+        if (n < 1) n = 1;
+        acc += (int)n;
+      }
+      ia.wg_start[B] = acc;
+    }
+  }
   return v4::launch_index_score(ia, st);
 }
 

@@ -55,7 +55,14 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
   constexpr int P = RB / 16;         // 16-byte pieces per key row
   constexpr int KPI = 64 / P;        // keys per load instruction
   constexpr int NL = 32 / KPI;       // load instructions per 32-key chunk
-  const int b = blockIdx.z, r = blockIdx.y;
+  int b = blockIdx.z, blk = blockIdx.x, nblk = gridDim.x;
+  const int r = blockIdx.y;
+  if (a.ragged && a.Tq == 1) {   // flat grid: find this workgroup's sequence
+    b = 0;
+    while (b + 1 < a.B && (int)blockIdx.x >= a.wg_start[b + 1]) ++b;
+    blk = blockIdx.x - a.wg_start[b];
+    nblk = a.wg_start[b + 1] - a.wg_start[b];
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = (a.ragged ? a.pos.p[b] : a.q_pos0) + r;
   int64_t V = (t + 1) / a.m;
@@ -63,9 +70,9 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
   // 32-key chunks are dealt round-robin over the row's waves, so at any time
   // the waves of a row read one compact front of the key array
   const int64_t nch = (V + 31) / 32;
-  const int64_t NW = (int64_t)gridDim.x * 4;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
-  if ((int64_t)blockIdx.x * 4 >= nch) return;   // the whole block is past the visible keys
+  const int64_t NW = (int64_t)nblk * 4;
+  const int64_t gw = (int64_t)blk * 4 + wave;
+  if ((int64_t)blk * 4 >= nch) return;   // the whole block is past the visible keys
 
   __shared__ __attribute__((aligned(16))) uint8_t s_q[M2 * 32 * QSTR];
   __shared__ __attribute__((aligned(16))) uint8_t s_k[4][32 * KSTR];
@@ -333,6 +340,7 @@ hipError_t launch_index_score(const IndexScoreArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   dim3 grid((unsigned)(a.row_waves / 4), a.Tq, a.B);
+  if (a.ragged && a.Tq == 1) grid = dim3((unsigned)a.wg_start[a.B], 1, 1);
   const int mb = (a.HI + 15) / 16;
 #define V4_IDX(DI, MB) index_score_kernel<DI, MB><<<grid, 256, 0, st>>>(a)
 #define V4_IDX_MB(DI)          \

@@ -70,6 +70,9 @@ struct IndexScoreArgs {
   int64_t row_waves;      // waves sharing one query row (multiple of 4)
   bool ragged;            // query block of sequence b starts at pos.p[b]
   SeqPos pos;
+  // ragged decode (Tq = 1): a flat grid, sequence b owning workgroups
+  // wg_start[b] .. wg_start[b+1]-1 (in proportion to its visible entries)
+  int wg_start[kMaxRagged + 1];
 };
 // Waves per query row that spread a launch over three workgroups per CU.
 int64_t index_row_waves(int B, int Tq, int64_t vmax);

@@ -61,10 +61,17 @@ class DecodeStep:
     NAMES = ("csa_compress", "index_score", "topk_select", "csa_attend",
              "hca_compress", "hca_attend")
 
-    def __init__(self, inp, c, h, dev):
+    def __init__(self, inp, c, h, dev, csa_pos=None, hca_pos=None):
+        """csa_pos / hca_pos: optional per-sequence positions of the new
+        tokens (a ragged batch); by default every sequence is at T - 1."""
         self.inp, self.c, self.h = inp, c, h
+        self.csa_pos, self.hca_pos = csa_pos, hca_pos
         a, b = inp["csa"], inp["hca"]
         Nc, Nh, tc, th = a["N"], b["N"], a["t"], b["t"]
+        if csa_pos is not None:
+            tc = max(csa_pos)
+        if hca_pos is not None:
+            th = max(hca_pos)
         self.scores = torch.empty((c.B, ops.score_stride(1, Nc, tc, c.m)), dtype=torch.float32,
                                   device=dev)
         self.topk = torch.empty((c.B, 1, c.k), dtype=torch.int32, device=dev)
@@ -87,25 +94,34 @@ class DecodeStep:
         c, h = self.c, self.h
         a, b = self.inp["csa"], self.inp["hca"]
         Nc, Nh, tc, th = a["N"], b["N"], a["t"], b["t"]
+        cp, hp = self.csa_pos, self.hca_pos
+        if cp is not None:
+            tc = max(cp)
+        if hp is not None:
+            th = max(hp)
         ent_h = b["entries"][rot % len(b["entries"])]
         return {
             "csa_compress": lambda: ops.compress_step(a["raw"], a["score"], a["bias"], a["gamma"],
                                                       a["entries"], a["win"],
                                                       raw_pos0=tc + 1 - 2 * c.m, m=c.m, t=tc,
-                                                      win_row=c.W - 1),
+                                                      seq_pos=cp, win_row=c.W - 1),
             "index_score": lambda: ops.index_score(a["q_idx"], a["w_idx"], a["k_idx"], n_entries=Nc,
-                                                   q_pos0=tc, m=c.m, scores=self.scores),
+                                                   q_pos0=tc, seq_pos=cp, m=c.m,
+                                                   scores=self.scores),
             "topk_select": lambda: ops.topk_select(self.scores, B=c.B, Tq=1, n_entries=Nc,
-                                                   q_pos0=tc, m=c.m, k=c.k, topk=self.topk,
+                                                   q_pos0=tc, seq_pos=cp, m=c.m, k=c.k,
+                                                   topk=self.topk,
                                                    workspace=self.tk_ws),
             "csa_attend": lambda: ops.csa_attend(a["q"], a["entries"], self.topk, a["win"],
-                                                 a["gamma"], a["sink"], q_pos0=tc, W=c.W,
+                                                 a["gamma"], a["sink"], q_pos0=tc, seq_pos=cp,
+                                                 W=c.W,
                                                  out=self.out_c, workspace=self.csa_ws),
             "hca_compress": lambda: ops.compress_step(b["raw"], b["score"], b["bias"], b["gamma"],
                                                       ent_h, b["win"], raw_pos0=th + 1 - 2 * h.m,
-                                                      m=h.m, t=th, win_row=h.W - 1),
+                                                      m=h.m, t=th, seq_pos=hp, win_row=h.W - 1),
             "hca_attend": lambda: ops.hca_attend(b["q"], ent_h, b["win"], b["gamma"], b["sink"],
-                                                 n_entries=Nh, m=h.m, q_pos0=th, W=h.W,
+                                                 n_entries=Nh, m=h.m, q_pos0=th, seq_pos=hp,
+                                                 W=h.W,
                                                  out=self.out_h, workspace=self.hca_ws),
         }
 
