@@ -118,14 +118,23 @@ hipError_t launch_index_score_mxfp4(const IndexScoreMxfp4Args& a, hipStream_t st
 
 // Top-k selection: per-part leaders -> exact per-row select.
 constexpr int kTopkSel = 16384;     // keys the per-row selection holds in LDS
-constexpr int kTopkPartLen = 1024;  // scores per part
+constexpr int kTopkPartLen = 1024;  // scores per part (the longest; 256 or 512 for short rows)
 constexpr int kTopkPartCap = 32;    // leaders a part stores
 constexpr int kTopkMaxParts = 4096; // parts per row (entries <= 4M)
+
+// Scores per part of a row of V entries: short enough that a part holds
+// about k/8 or fewer of the row's top k on average (its leaders then
+// rarely overflow); 256, 512 or 1024.
+__host__ __device__ inline int topk_part_len(int64_t V, int k) {
+  int P = kTopkPartLen;
+  while (P > 256 && (int64_t)k * P > 8 * V) P >>= 1;
+  return P;
+}
 
 struct TopkPlan {
   int64_t direct_max;  // rows of at most this many entries are selected directly
   bool parts;          // longer rows exist: run the part kernel
-  int nparts;          // parts per row (of the longest row)
+  int nparts;          // part slots per row (the most any row of the launch has)
 };
 TopkPlan topk_plan(int64_t vmax, int k);
 
@@ -136,7 +145,7 @@ struct TopkArgs {
   int64_t n_entries, q_pos0;
   int m, k;
   int64_t direct_max;      // TopkPlan::direct_max
-  int nparts;
+  int nparts;              // part slots per row (a row uses topk_part_len of its own V)
   unsigned* part_tau;      // [rows, nparts] the part's leader threshold (0: none)
   int* part_cnt;           // [rows, nparts] keys >= it in the part
   unsigned* part_over;     // [rows, nparts] largest of them not stored (0: none)

@@ -34,6 +34,8 @@
 // stream compaction then writes every key above the bucket and the
 // lowest-positioned keys inside it, so the output comes out in ascending
 // index order.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -45,7 +47,7 @@ constexpr int kHistBins = 2048;
 constexpr int kSelRounds = kTopkSel / kSelThreads;
 static_assert(kSelRounds * kSelWaves <= kSelThreads, "one scan entry per thread");
 constexpr int kBucketsPerThread = kHistBins / kSelThreads;
-static_assert(kTopkPartLen == 16 * 64, "a part is 16 keys per lane of one wave");
+static_assert(kTopkPartLen == 16 * 64, "a part is at most 16 keys per lane of one wave");
 
 // Rows up to kTopkSel keys are selected by one workgroup straight from the
 // scores; for a small k a row of more than 2048 keys is spread over part
@@ -55,7 +57,15 @@ TopkPlan topk_plan(int64_t vmax, int k) {
   TopkPlan p;
   p.direct_max = k <= 32 ? 2048 : kTopkSel;
   p.parts = vmax > p.direct_max;
-  p.nparts = p.parts ? (int)((vmax + kTopkPartLen - 1) / kTopkPartLen) : 0;
+  // a row's part count is largest at its own length or just below a length
+  // where the part length halves (rows of a launch may be shorter than vmax)
+  int64_t np = 0;
+  for (int64_t V : {vmax, std::min(vmax, (int64_t)k * 128 - 1), std::min(vmax, (int64_t)k * 64 - 1)}) {
+    if (V <= 0) continue;
+    const int P = topk_part_len(V, k);
+    np = std::max(np, (V + P - 1) / P);
+  }
+  p.nparts = p.parts ? (int)np : 0;
   return p;
 }
 
@@ -105,19 +115,23 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
-// The 16 keys of lane `lane` in the part starting at `base` of row qr:
-// positions base + 64r + lane (absent past the row's visible entries).
+// The keys of lane `lane` in the part starting at `base` of row qr:
+// positions base + 64r + lane for r < P / 64 (absent past the part
+// and past the row's visible entries).
 __device__ __forceinline__ void load_part(const TopkArgs& a, int64_t qr, int64_t V, int64_t base,
-                                          int lane, unsigned (&key)[16]) {
+                                          int P, int lane, unsigned (&key)[16]) {
   const float* src = a.scores + qr * a.score_stride;
+  const int kpl = P >> 6;
+  int64_t end = base + P;
+  if (end > V) end = V;
   float f[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t i = base + 64 * r + lane;
-    f[r] = src[i < V ? i : (V > 0 ? V - 1 : 0)];
+    f[r] = r < kpl ? src[i < V ? i : (V > 0 ? V - 1 : 0)] : 0.f;
   }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) key[r] = base + 64 * r + lane < V ? score_key(f[r]) : 0u;
+  for (int r = 0; r < 16; ++r) key[r] = base + 64 * r + lane < end ? score_key(f[r]) : 0u;
 }
 
 // ---- part leaders: x_p = the 16th largest lane maximum (0 if fewer than 16
@@ -127,15 +141,16 @@ __global__ __launch_bounds__(256) void topk_part_kernel(TopkArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t qr = blockIdx.y;
   const int p = blockIdx.x * 4 + wave;
-  if (p >= a.nparts) return;
   const int64_t V = visible_of(a, qr);
   if (V <= a.direct_max) return;   // such a row is selected directly
-  const int64_t base = (int64_t)p * kTopkPartLen;
+  const int P = topk_part_len(V, a.k);
+  if (p >= (V + P - 1) / P) return;   // past this row's parts
+  const int64_t base = (int64_t)p * P;
   unsigned x = 0u, over = 0u;
   int cnt = 0;
   if (base < V) {
     unsigned key[16];
-    load_part(a, qr, V, base, lane, key);
+    load_part(a, qr, V, base, P, lane, key);
     unsigned lmax = 0u;
 #pragma unroll
     for (int r = 0; r < 16; ++r) lmax = max(lmax, key[r]);
@@ -380,11 +395,13 @@ __device__ __forceinline__ void topk_select_general(const TopkArgs& a, unsigned*
     return;
   }
 
-  const int np = a.nparts;
+  const int ns = a.nparts;                       // part slots per row (strides)
+  const int P = topk_part_len(V, a.k);
+  const int np = (int)((V + P - 1) / P);          // this row's parts
   const int ppt = (np + kSelThreads - 1) / kSelThreads;   // parts per thread (<= 8)
-  const unsigned* ptau = a.part_tau + qr * np;
-  const int* pcnt = a.part_cnt + qr * np;
-  const unsigned* pover = a.part_over + qr * np;
+  const unsigned* ptau = a.part_tau + qr * ns;
+  const int* pcnt = a.part_cnt + qr * ns;
+  const unsigned* pover = a.part_over + qr * ns;
   // this thread's parts' records, loaded up front (their latency overlaps
   // the first selection instead of sitting before the offsets and the check)
   constexpr int kMaxPpt = (kTopkMaxParts + kSelThreads - 1) / kSelThreads;
@@ -398,8 +415,8 @@ __device__ __forceinline__ void topk_select_general(const TopkArgs& a, unsigned*
     my_tau[u] = own ? ptau[q] : 0u;
     my_over[u] = own ? pover[q] : 0u;
   }
-  const unsigned* ck = a.cand_key + qr * (int64_t)np * kTopkPartCap;
-  const int* ci = a.cand_idx + qr * (int64_t)np * kTopkPartCap;
+  const unsigned* ck = a.cand_key + qr * (int64_t)ns * kTopkPartCap;
+  const int* ci = a.cand_idx + qr * (int64_t)ns * kTopkPartCap;
   unsigned* rk = a.run_key + qr * k;
 
   // Offsets of the parts' candidates given each part's count (cnt_of).
@@ -466,8 +483,8 @@ __device__ __forceinline__ void topk_select_general(const TopkArgs& a, unsigned*
         const int o0 = s_off[q], o1 = s_off[q + 1];
         if (!is_raw(q) || o1 <= c0 || o0 >= c0 + take) continue;
         unsigned key[16];
-        const int64_t base = (int64_t)q * kTopkPartLen;
-        load_part(a, qr, V, base, lane, key);
+        const int64_t base = (int64_t)q * P;
+        load_part(a, qr, V, base, P, lane, key);
         int cnt = 0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -522,7 +539,7 @@ __device__ __forceinline__ void topk_select_general(const TopkArgs& a, unsigned*
   for (int q = wave; q < np; q += kSelWaves) {
     if (!is_raw(q)) continue;
     unsigned key[16];
-    load_part(a, qr, V, (int64_t)q * kTopkPartLen, lane, key);
+    load_part(a, qr, V, (int64_t)q * P, P, lane, key);
     int c = 0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) c += __popcll(__ballot(key[r] >= thr));
@@ -545,7 +562,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t qr = blockIdx.x;
   const int64_t V = visible_of(a, qr);
-  const int np = a.nparts;
+  const int ns = a.nparts;                                        // part slots per row
+  const int np = V > a.direct_max ? (int)((V + topk_part_len(V, a.k) - 1) / topk_part_len(V, a.k)) : 0;
   if (V > a.direct_max && np <= kSelThreads) {
     unsigned* s_key = smem;                                   // [kTopkSel + 64]
     unsigned* s_hist = smem + kTopkSel;                       // [kHistBins]
@@ -556,13 +574,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
     const int k = a.k;
     int32_t* topk = a.topk + qr * k;
     float* tks = a.topk_score ? a.topk_score + qr * k : nullptr;
-    const unsigned* ck = a.cand_key + qr * (int64_t)np * kTopkPartCap;
-    const int* ci = a.cand_idx + qr * (int64_t)np * kTopkPartCap;
+    const unsigned* ck = a.cand_key + qr * (int64_t)ns * kTopkPartCap;
+    const int* ci = a.cand_idx + qr * (int64_t)ns * kTopkPartCap;
     const int q = tid;
     const bool own = q < np;
-    const int cq = own ? min(a.part_cnt[qr * np + q], kTopkPartCap) : 0;
-    const unsigned tau = own ? a.part_tau[qr * np + q] : 0u;
-    const unsigned over = own ? a.part_over[qr * np + q] : 0u;
+    const int cq = own ? min(a.part_cnt[qr * ns + q], kTopkPartCap) : 0;
+    const unsigned tau = own ? a.part_tau[qr * ns + q] : 0u;
+    const unsigned over = own ? a.part_over[qr * ns + q] : 0u;
     unsigned key[kTopkPartCap];
     int idx[kTopkPartCap];
     if (own) {
