@@ -21,7 +21,11 @@ Readings (the pages are silent on these):
   * order of operations: pool -> RMSNorm (over all D dims, with gain gamma and
     epsilon eps) -> RoPE at position j*m on the last R dims -> quantise;
   * window (uncompressed) rows are the per-token latents with the same
-    RMSNorm and RoPE at their own position ("PACK" below).
+    RMSNorm and RoPE at their own position ("PACK" below);
+  * indexer keys of the compressed entries: the per-token indexer-key stream
+    pooled by the same compressor, i.e. with entry j's own window weights
+    alpha_{j,t}; no RMSNorm and no RoPE (the indexer's score uses the keys
+    as they are), stored as bf16 ("pool_index_keys" below).
 """
 
 import numpy as np
@@ -106,3 +110,23 @@ def compress_pack(c, pos0, gamma, eps, R, base):
     c = np.asarray(c, dtype=np.float64)
     pos = pos0 + np.arange(c.shape[0])
     return rope(rmsnorm(c, gamma, eps), pos, R, base)
+
+
+def pool_index_keys(kI, s, pos0, m, bias, js):
+    """Indexer keys of entries js: sum_t alpha_{j,t} kI_t over entry j's
+    window, with the weights of the entry itself (pool_weights).
+
+    kI: [L, d_I] per-token indexer keys for positions pos0..; s: [L].
+    Returns float64 [len(js), d_I] (not rounded)."""
+    kI = np.asarray(kI, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+
+    class _ByPos:
+        def __getitem__(self, p):
+            return s[p - pos0]
+
+    out = np.zeros((len(js), kI.shape[1]))
+    for r, j in enumerate(js):
+        pos, alpha = pool_weights(_ByPos(), bias, j, m)
+        out[r] = alpha @ kI[pos - pos0]
+    return out

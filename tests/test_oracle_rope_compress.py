@@ -177,3 +177,34 @@ def test_page_counting_examples():
         assert abs(case["tokens"] / case["m"] - case["entries"]) < 1
     ws = gold["window_share"]
     assert round(100 * ws["window"] / ws["tokens"], 3) == ws["percent"]
+
+
+def test_index_key_pooling_weights_are_the_entry_weights():
+    # pooling a constant key stream gives the constant (weights sum to 1);
+    # a one-hot stream at position p gives entry j's weight of p, read from
+    # the pinned pool_weights; adding a constant to every score changes
+    # nothing
+    from oracle import compress as occ
+    g = np.random.default_rng(3)
+    m, L, dI = 4, 24, 8
+    s = g.normal(size=L)
+    bias = g.normal(0, 0.3, size=2 * m)
+    js = np.arange(0, L // m)
+    const = np.tile(g.normal(size=dI), (L, 1))
+    assert np.allclose(occ.pool_index_keys(const, s, 0, m, bias, js), const[: len(js)], atol=1e-13)
+
+    class _S:
+        def __getitem__(self, q):
+            return s[q]
+
+    for p in (0, 5, 11):
+        onehot = np.zeros((L, dI))
+        onehot[p, 0] = 1.0
+        got = occ.pool_index_keys(onehot, s, 0, m, bias, js)[:, 0]
+        for r, j in enumerate(js):
+            pos, alpha = occ.pool_weights(_S(), bias, j, m)
+            want = alpha[list(pos).index(p)] if p in pos else 0.0
+            assert abs(got[r] - want) < 1e-15
+    kI = g.normal(size=(L, dI))
+    assert np.allclose(occ.pool_index_keys(kI, s + 3.0, 0, m, bias, js),
+                       occ.pool_index_keys(kI, s, 0, m, bias, js), atol=1e-13)
