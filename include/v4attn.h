@@ -94,13 +94,20 @@ const char* v4attn_last_error(void);
  *   out       u8 [B, out_rows, D+R]: output i of sequence b goes to row
  *             b*out_rows + i (i = j - entry0 for POOL).  n_out <= out_rows.
  * FP8 values are rounded to nearest-even after clamping to +-448.
+ *   raw_idx    bf16 [B, L, dI], nullable (POOL only): the tokens' indexer
+ *              keys, pooled by the same compressor: entry j's indexer key is
+ *              sum_t alpha_{j,t} kI_t with the entry's own weights, no norm,
+ *              no rotation, bf16 (RNE) -> k_idx_out [B, out_rows, dI], rows
+ *              as out (dI in {32, 64, 128})
  */
 int v4attn_compress(const uint16_t* raw, const float* tok_score,
                     const float* pos_bias, const float* gamma,
                     int B, int L, int D, int R, int64_t raw_pos0,
                     int mode, int m, int64_t entry0, int n_out,
                     float eps, float rope_base,
-                    uint8_t* out, int64_t out_rows, void* stream);
+                    uint8_t* out, int64_t out_rows,
+                    const uint16_t* raw_idx, int dI, uint16_t* k_idx_out,
+                    void* stream);
 
 /*
  * v4attn_compress_step -- one decode step of the compressor, in one launch:
@@ -121,6 +128,9 @@ int v4attn_compress(const uint16_t* raw, const float* tok_score,
  *              batch, B <= 64); then t must be their largest, sequence b's
  *              raw rows are the L positions ending at seq_pos[b] (raw_pos0
  *              is ignored) and each sequence pools its own completed entry
+ *   raw_idx    bf16 [B, L, dI], nullable: token indexer keys; a completed
+ *              entry's pooled key (as v4attn_compress) -> k_idx [B, ent_rows,
+ *              dI] row j
  * Errors: EINVAL for null/misaligned buffers, t outside the raw rows, a
  * window that starts before raw_pos0, j >= ent_rows or win_row out of range.
  */
@@ -129,6 +139,7 @@ int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const floa
                          int m, int64_t t, const int64_t* seq_pos, float eps,
                          float rope_base, uint8_t* entries,
                          int64_t ent_rows, uint8_t* win, int64_t win_rows, int64_t win_row,
+                         const uint16_t* raw_idx, int dI, uint16_t* k_idx,
                          void* stream);
 
 /*

@@ -182,7 +182,8 @@ const char* v4attn_last_error(void) { return g_err.c_str(); }
 int v4attn_compress(const uint16_t* raw, const float* tok_score, const float* pos_bias,
                     const float* gamma, int B, int L, int D, int R, int64_t raw_pos0, int mode,
                     int m, int64_t entry0, int n_out, float eps, float rope_base, uint8_t* out,
-                    int64_t out_rows, void* stream) {
+                    int64_t out_rows, const uint16_t* raw_idx, int dI, uint16_t* k_idx_out,
+                    void* stream) {
   if (!raw || !gamma || !out) return fail(V4ATTN_EINVAL, "null raw, gamma or out");
   if (B < 0 || L < 0 || n_out < 0 || out_rows < 0)
     return fail(V4ATTN_EINVAL, "negative B, L, n_out or out_rows");
@@ -209,8 +210,12 @@ int v4attn_compress(const uint16_t* raw, const float* tok_score, const float* po
   } else {
     if (n_out > L) return fail(V4ATTN_EINVAL, "PACK n_out %d > L %d", n_out, L);
   }
+  if (raw_idx && (!k_idx_out || (dI != 32 && dI != 64 && dI != 128)))
+    return fail(V4ATTN_EINVAL, "indexer keys need k_idx_out and dI in {32, 64, 128}");
   v4::CompressArgs a{raw, tok_score, pos_bias, gamma, B, L, D, R, raw_pos0, mode, m, entry0,
-                     n_out, eps, rope_base, out, out_rows, v4::rope_turns(rope_base, R)};
+                     n_out, eps, rope_base, out, out_rows, v4::rope_turns(rope_base, R),
+                     mode == V4ATTN_POOL ? raw_idx : nullptr, dI,
+                     mode == V4ATTN_POOL && raw_idx ? k_idx_out : nullptr};
   return hip_status(v4::launch_compress(a, (hipStream_t)stream), "compress launch");
 }
 
@@ -218,7 +223,8 @@ int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const floa
                          const float* gamma, int B, int L, int D, int R, int64_t raw_pos0, int m,
                          int64_t t, const int64_t* seq_pos, float eps, float rope_base,
                          uint8_t* entries, int64_t ent_rows, uint8_t* win, int64_t win_rows,
-                         int64_t win_row, void* stream) {
+                         int64_t win_row, const uint16_t* raw_idx, int dI, uint16_t* k_idx,
+                         void* stream) {
   if (!raw || !gamma || !win) return fail(V4ATTN_EINVAL, "null raw, gamma or win");
   if (B < 0 || L < 0 || ent_rows < 0 || win_rows < 0)
     return fail(V4ATTN_EINVAL, "negative B, L, ent_rows or win_rows");
@@ -258,6 +264,11 @@ int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const floa
                          v4::rope_turns(rope_base, R), entries, ent_rows, win, win_rows, win_row};
   a.ragged = ragged;
   if (ragged) a.pos = sp;
+  if (raw_idx && (!k_idx || (dI != 32 && dI != 64 && dI != 128)))
+    return fail(V4ATTN_EINVAL, "indexer keys need k_idx and dI in {32, 64, 128}");
+  a.raw_idx = raw_idx;
+  a.dI = dI;
+  a.kidx = raw_idx ? k_idx : nullptr;
   return hip_status(v4::launch_compress_step(a, (hipStream_t)stream), "compress step launch");
 }
 

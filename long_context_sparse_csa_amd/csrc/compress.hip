@@ -110,7 +110,8 @@ __device__ __forceinline__ void pool_entry(
     const uint16_t* __restrict__ raw, const float* __restrict__ score,
     const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
     int64_t raw_pos0, int m, int64_t j, int b, float eps, const RopeTurns& rope,
-    uint8_t* __restrict__ row) {
+    uint8_t* __restrict__ row,
+    const uint16_t* __restrict__ raw_idx, int dI, uint16_t* __restrict__ kidx_row) {
   constexpr int D = VPL * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float s_alpha[512];
@@ -185,6 +186,26 @@ __device__ __forceinline__ void pool_entry(
 #pragma unroll
   for (int v = 0; v < VPL; ++v) s_part[wave][lane * VPL + v] = acc[v];
   __syncthreads();
+  if (kidx_row) {
+    // the entry's indexer key: the token indexer keys pooled with the same
+    // weights (no norm, no rotation), bf16; wave w takes rows w, w+16, ..
+    __shared__ float s_kp[kPoolWaves][128];
+    const uint16_t* kb = raw_idx + ((int64_t)b * L + r0) * dI;
+    for (int d = lane; d < 128; d += 64) {
+      float z = 0.f;
+      if (d < dI)
+        for (int t = wave; t < nw; t += kPoolWaves)
+          z = fmaf(s_alpha[t], __uint_as_float((uint32_t)kb[(int64_t)t * dI + d] << 16), z);
+      s_kp[wave][d] = z;
+    }
+    __syncthreads();
+    if (tid < dI) {
+      float z = 0.f;
+#pragma unroll
+      for (int w = 0; w < kPoolWaves; ++w) z += s_kp[w][tid];
+      kidx_row[tid] = (uint16_t)(pack_bf16x2(z * inv, 0.f) & 0xFFFFu);
+    }
+  }
   if (wave != 0) return;
 
   float y[VPL];
@@ -205,11 +226,13 @@ __global__ __launch_bounds__(kPoolThreads) void compress_pool_kernel(
     const uint16_t* __restrict__ raw, const float* __restrict__ score,
     const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
     int64_t raw_pos0, int m, int64_t entry0, float eps, const RopeTurns rope,
-    uint8_t* __restrict__ out, int64_t out_rows) {
+    uint8_t* __restrict__ out, int64_t out_rows, const uint16_t* __restrict__ raw_idx, int dI,
+    uint16_t* __restrict__ kidx_out) {
   constexpr int D = VPL * 64;
   const int b = blockIdx.y;
   pool_entry<VPL>(raw, score, bias, gamma, L, R, raw_pos0, m, entry0 + blockIdx.x, b, eps, rope,
-                  out + ((int64_t)b * out_rows + blockIdx.x) * (D + R));
+                  out + ((int64_t)b * out_rows + blockIdx.x) * (D + R), raw_idx, dI,
+                  kidx_out ? kidx_out + ((int64_t)b * out_rows + blockIdx.x) * dI : nullptr);
 }
 
 // One wave per raw row: RMSNorm, RoPE at the row's own position, pack.
@@ -239,7 +262,8 @@ __global__ __launch_bounds__(kPoolThreads) void compress_step_kernel(
     const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
     int64_t raw_pos0, int m, int64_t t, float eps, const RopeTurns rope,
     uint8_t* __restrict__ ent, int64_t ent_rows, uint8_t* __restrict__ win, int64_t win_rows,
-    int64_t win_row, const bool ragged, const SeqPos pos) {
+    int64_t win_row, const bool ragged, const SeqPos pos, const uint16_t* __restrict__ raw_idx,
+    int dI, uint16_t* __restrict__ kidx) {
   constexpr int D = VPL * 64;
   const int b = blockIdx.y;
   if (ragged) {   // this sequence's token; its raw rows end at it
@@ -258,7 +282,8 @@ __global__ __launch_bounds__(kPoolThreads) void compress_step_kernel(
   }
   const int64_t j = (t + 1) / m - 1;
   pool_entry<VPL>(raw, score, bias, gamma, L, R, raw_pos0, m, j, b, eps, rope,
-                  ent + ((int64_t)b * ent_rows + j) * (D + R));
+                  ent + ((int64_t)b * ent_rows + j) * (D + R), raw_idx, dI,
+                  kidx ? kidx + ((int64_t)b * ent_rows + j) * dI : nullptr);
 }
 
 hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st) {
@@ -272,7 +297,7 @@ hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st) {
 #define V4_STEP(VPL)                                                                        \
   compress_step_kernel<VPL><<<grid, kPoolThreads, 0, st>>>(                                 \
       a.raw, a.tok_score, a.pos_bias, a.gamma, a.L, a.R, a.raw_pos0, a.m, a.t, a.eps, a.rope, \
-      a.ent, a.ent_rows, a.win, a.win_rows, a.win_row, a.ragged, a.pos)
+      a.ent, a.ent_rows, a.win, a.win_rows, a.win_row, a.ragged, a.pos, a.raw_idx, a.dI, a.kidx)
   switch (a.D) {
     case 128: V4_STEP(2); break;
     case 256: V4_STEP(4); break;
@@ -289,7 +314,8 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
 #define V4_POOL(VPL)                                                                       \
   compress_pool_kernel<VPL><<<grid, kPoolThreads, 0, st>>>(a.raw, a.tok_score, a.pos_bias, a.gamma,  \
                                                   a.L, a.R, a.raw_pos0, a.m, a.entry0,     \
-                                                  a.eps, a.rope, a.out, a.out_rows)
+                                                  a.eps, a.rope, a.out, a.out_rows, a.raw_idx, \
+                                                  a.dI, a.kidx)
     switch (a.D) {
       case 128: V4_POOL(2); break;
       case 256: V4_POOL(4); break;

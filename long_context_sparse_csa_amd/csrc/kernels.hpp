@@ -31,6 +31,9 @@ struct CompressArgs {
   uint8_t* out;
   int64_t out_rows;
   RopeTurns rope;        // from rope_base (host)
+  const uint16_t* raw_idx;  // POOL, nullable: [B, L, dI] token indexer keys
+  int dI;
+  uint16_t* kidx;           // [B, out_rows, dI] pooled indexer keys (rows as out)
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 
@@ -53,6 +56,9 @@ struct CompressStepArgs {
   int64_t win_rows, win_row;
   bool ragged;             // token of sequence b at pos.p[b]; raw rows hold its
   SeqPos pos;              // positions p[b]-L+1 .. p[b] (t, raw_pos0 unused)
+  const uint16_t* raw_idx; // nullable: [B, L, dI] token indexer keys
+  int dI;
+  uint16_t* kidx;          // [B, ent_rows, dI]: the entry's pooled indexer key at row j
 };
 hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st);
 

@@ -36,9 +36,9 @@ _SIGS = {
     "v4attn_status_string": (_c.c_char_p, [_I]),
     "v4attn_last_error": (_c.c_char_p, []),
     "v4attn_compress": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _I, _L, _I, _F, _F, _P, _L,
-                             _P]),
+                             _P, _I, _P, _P]),
     "v4attn_compress_step": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _L, _P, _F, _F, _P, _L,
-                                  _P, _L, _L, _P]),
+                                  _P, _L, _L, _P, _I, _P, _P]),
     "v4attn_index_topk_workspace": (_Z, [_I, _I, _L, _L, _I, _I]),
     "v4attn_index_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _P, _I, _I, _P, _P, _P, _Z,
                                _P]),
@@ -168,10 +168,24 @@ def _row_ptr(out, row0, row_bytes):
     return _c.c_void_p(out.data_ptr() + row0 * row_bytes)
 
 
+def _kidx_args(raw_idx, k_idx, B, L, row0):
+    """(raw_idx ptr, dI, k_idx row pointer) for the pooled indexer keys."""
+    if raw_idx is None:
+        return None, 0, None
+    _need(raw_idx, "raw_idx", torch.bfloat16, 3)
+    _need(k_idx, "k_idx", torch.bfloat16, 3)
+    dI = raw_idx.shape[2]
+    if tuple(raw_idx.shape[:2]) != (B, L) or k_idx.shape[0] != B or k_idx.shape[2] != dI:
+        raise ValueError("shape mismatch")
+    return _ptr(raw_idx), dI, _c.c_void_p(k_idx.data_ptr() + row0 * dI * 2)
+
+
 def compress_pool(raw, tok_score, pos_bias, gamma, out, *, raw_pos0, m, entry0, n_out,
-                  out_row0=0, eps=1e-6, rope_base=10000.0, R=64):
+                  out_row0=0, eps=1e-6, rope_base=10000.0, R=64, raw_idx=None, k_idx=None):
     """Pool 2m-token windows of raw bf16 latents [B, L, D] into packed entries
-    entry0..entry0+n_out-1, written to out[b, out_row0 + i] (uint8 [B, rows, D+R])."""
+    entry0..entry0+n_out-1, written to out[b, out_row0 + i] (uint8 [B, rows, D+R]).
+    With raw_idx (bf16 [B, L, dI], the tokens' indexer keys) the entries'
+    indexer keys, pooled with the same weights, go to k_idx[b, out_row0 + i]."""
     _need(raw, "raw", torch.bfloat16, 3)
     _need(tok_score, "tok_score", torch.float32, 2)
     _need(pos_bias, "pos_bias", torch.float32, 1)
@@ -181,20 +195,25 @@ def compress_pool(raw, tok_score, pos_bias, gamma, out, *, raw_pos0, m, entry0, 
     if tuple(tok_score.shape) != (B, L) or pos_bias.numel() != 2 * m or gamma.numel() != D \
             or out.shape[0] != B or out.shape[2] != D + R or out_row0 + n_out > out.shape[1]:
         raise ValueError("shape mismatch")
+    ri, dI, kp = _kidx_args(raw_idx, k_idx, B, L, out_row0)
+    if raw_idx is not None and k_idx.shape[1] != out.shape[1]:
+        raise ValueError("k_idx must have out's rows")
     check(lib().v4attn_compress(_ptr(raw), _ptr(tok_score), _ptr(pos_bias), _ptr(gamma), B, L, D,
                                 R, int(raw_pos0), POOL, int(m), int(entry0), int(n_out),
                                 float(eps), float(rope_base), _row_ptr(out, out_row0, D + R),
-                                out.shape[1], _stream(raw)))
+                                out.shape[1], ri, dI, kp, _stream(raw)))
     return out
 
 
 def compress_step(raw, tok_score, pos_bias, gamma, entries, win, *, m, win_row, raw_pos0=None,
-                  t=None, seq_pos=None, eps=1e-6, rope_base=10000.0, R=64):
+                  t=None, seq_pos=None, eps=1e-6, rope_base=10000.0, R=64, raw_idx=None,
+                  k_idx=None):
     """One decode step of the compressor in one launch: the window row of the
     token at position t -> win[b, win_row], and, when (t+1) % m == 0, the
     entry j = (t+1)/m - 1 it completes -> entries[b, j].  With seq_pos (one
     position per sequence) each sequence's raw rows are the L positions
-    ending at its own token."""
+    ending at its own token.  With raw_idx (bf16 [B, L, dI]) a completed
+    entry's pooled indexer key goes to k_idx[b, j] (bf16 [B, rows, dI])."""
     _need(raw, "raw", torch.bfloat16, 3)
     _need(tok_score, "tok_score", torch.float32, 2)
     _need(pos_bias, "pos_bias", torch.float32, 1)
@@ -208,10 +227,13 @@ def compress_step(raw, tok_score, pos_bias, gamma, entries, win, *, m, win_row, 
         raise ValueError("shape mismatch")
     arr, sp, t = _seq_pos(seq_pos, B, t)
     raw_pos0 = t - L + 1 if raw_pos0 is None else raw_pos0
+    ri, dI, kp = _kidx_args(raw_idx, k_idx, B, L, 0)
+    if raw_idx is not None and k_idx.shape[1] != entries.shape[1]:
+        raise ValueError("k_idx must have the entries' rows")
     check(lib().v4attn_compress_step(_ptr(raw), _ptr(tok_score), _ptr(pos_bias), _ptr(gamma), B, L,
                                      D, R, int(raw_pos0), int(m), int(t), sp, float(eps),
                                      float(rope_base), _ptr(entries), entries.shape[1], _ptr(win),
-                                     win.shape[1], int(win_row), _stream(raw)))
+                                     win.shape[1], int(win_row), ri, dI, kp, _stream(raw)))
     return entries, win
 
 
@@ -229,7 +251,8 @@ def compress_pack(raw, gamma, out, *, raw_pos0, n_out=None, out_row0=0, eps=1e-6
         raise ValueError("shape mismatch")
     check(lib().v4attn_compress(_ptr(raw), None, None, _ptr(gamma), B, L, D, R, int(raw_pos0),
                                 PACK, 1, 0, int(n_out), float(eps), float(rope_base),
-                                _row_ptr(out, out_row0, D + R), out.shape[1], _stream(raw)))
+                                _row_ptr(out, out_row0, D + R), out.shape[1], None, 0, None,
+                                _stream(raw)))
     return out
 
 

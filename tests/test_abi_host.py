@@ -47,7 +47,8 @@ def _compress(**kw):
     return L().v4attn_compress(a["raw"], a["tok_score"], a["pos_bias"], a["gamma"], a["B"],
                                a["L"], a["D"], a["R"], a["raw_pos0"], a["mode"], a["m"],
                                a["entry0"], a["n_out"], a["eps"], a["base"], a["out"],
-                               a["out_rows"], a["stream"])
+                               a["out_rows"], a.get("ri"), a.get("dI", 0), a.get("ko"),
+                               a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -65,6 +66,8 @@ def _compress(**kw):
     (dict(raw=MISALIGNED), -1),
     (dict(eps=-1.0), -1),
     (dict(mode=1, n_out=17, out_rows=20), -1),   # PACK beyond L
+    (dict(ri=FAKE, dI=128, ko=None), -1),        # pooled indexer keys need an output
+    (dict(ri=FAKE, dI=96, ko=FAKE), -1),         # dI not built
 ])
 def test_compress_rejects(kw, status):
     assert _compress(**kw) == status
@@ -82,7 +85,8 @@ def _step(**kw):
     return L().v4attn_compress_step(a["raw"], a["s"], a["b"], a["g"], a["B"], a["L"], a["D"],
                                     a["R"], a["raw_pos0"], a["m"], a["t"], a["sp"], 1e-6, 1e4,
                                     a["ent"],
-                                    a["ent_rows"], a["win"], a["win_rows"], a["win_row"], None)
+                                    a["ent_rows"], a["win"], a["win_rows"], a["win_row"],
+                                    a.get("ri"), a.get("dI", 0), a.get("ko"), None)
 
 
 @pytest.mark.parametrize("kw,status", [

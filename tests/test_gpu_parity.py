@@ -480,3 +480,42 @@ def test_tiny_csa_decode_pipeline_end_to_end():
                          sink.cpu().double().numpy(), t, w.W, w.scale, 1e-6, R, 1e4)
     ma, rl = assert_attn_close(bf16_to_f64(out)[0], o, "tiny pipeline")
     log(f"  max_abs {ma:.2e} rel_l2 {rl:.2e}")
+
+
+@pytest.mark.parametrize("m,dI,D", [(4, 128, 512), (128, 64, 512), (16, 32, 128)])
+def test_compress_pools_indexer_keys(m, dI, D):
+    """The compressor pools the tokens' indexer keys with each entry's own
+    window weights (POOL call and decode step, uniform and per-sequence
+    positions); every bf16 key within one ulp of the exact pooled value (fp32
+    sums of exact bf16 products, then one rounding)."""
+    from helpers import quantum_bf16
+    B, R, W = 2, 64, 16
+    log(f"pooled indexer keys m={m} dI={dI} D={D}")
+    L = 6 * m
+    raw, score, bias, gamma = _compress_inputs(B, L, D, m, 57 + m)
+    kraw = synth.normal((B, L, dI), 57, "kraw", DEV, dtype=torch.bfloat16)
+    n_out = L // m
+    ent = torch.zeros((B, n_out, D + R), dtype=torch.uint8, device=DEV)
+    kid = torch.zeros((B, n_out, dI), dtype=torch.bfloat16, device=DEV)
+    ops().compress_pool(raw, score, bias, gamma, ent, raw_pos0=0, m=m, entry0=0, n_out=n_out,
+                        raw_idx=kraw, k_idx=kid)
+    # decode steps: sequence 0 at 4m - 1 (completes entry 3), sequence 1 at 3m - 1
+    pos = [4 * m - 1, 3 * m - 1]
+    raw_s = torch.stack([raw[b, p + 1 - 2 * m: p + 1] for b, p in enumerate(pos)]).contiguous()
+    sc_s = torch.stack([score[b, p + 1 - 2 * m: p + 1] for b, p in enumerate(pos)]).contiguous()
+    kr_s = torch.stack([kraw[b, p + 1 - 2 * m: p + 1] for b, p in enumerate(pos)]).contiguous()
+    ent2 = torch.zeros_like(ent)
+    kid2 = torch.zeros_like(kid)
+    win = torch.zeros((B, W, D + R), dtype=torch.uint8, device=DEV)
+    ops().compress_step(raw_s, sc_s, bias, gamma, ent2, win, m=m, seq_pos=pos, win_row=W - 1,
+                        raw_idx=kr_s, k_idx=kid2)
+    torch.cuda.synchronize()
+    kn, sn, bn = bf16_to_f64(kraw), score.cpu().double().numpy(), bias.cpu().double().numpy()
+    for b in range(B):
+        want = oc.pool_index_keys(kn[b], sn[b], 0, m, bn, np.arange(n_out))
+        got = bf16_to_f64(kid[b])
+        assert np.all(np.abs(got - want) <= quantum_bf16(want) + 1e-30), b
+        j = (pos[b] + 1) // m - 1
+        got2 = bf16_to_f64(kid2[b])
+        assert np.array_equal(got2[j], got[j])              # the step writes the same key
+        assert np.all(got2[np.arange(n_out) != j] == 0)     # and nothing else
