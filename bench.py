@@ -4,7 +4,7 @@
 One step is one decode token per sequence through
   * a CSA layer (compression m = 4, top-k 1024, window 128), 8 sequences of
     2^20 tokens: pack the new token's window row and pool the entry it completes
-    (one fused compress step),
+    and that entry's indexer key (one fused compress step),
     indexer scores over all 262,144 entries, top-k, sparse attention;
   * an HCA layer (compression m' = 128, window 128), 32 sequences of 2^20
     tokens: the compress step, dense attention over all 8,192 entries.
@@ -98,7 +98,7 @@ def algorithmic_bytes():
         "index_score": c.B * (Nc * c.dI * 2 + c.HI * c.dI * 2 + c.HI * 4),
         "csa_attend": c.B * ((c.k + c.W) * row + c.H * c.D * 2 * 2 + c.k * 4),
         "hca_attend": h.B * ((Nh + h.W) * row + h.H * h.D * 2 * 2),
-        "csa_compress": c.B * (2 * c.m * (c.D * 2 + 4) + row + c.D * 2 + row),
+        "csa_compress": c.B * (2 * c.m * (c.D * 2 + 4 + c.dI * 2) + row + c.D * 2 + row + c.dI * 2),
         "hca_compress": h.B * (2 * h.m * (h.D * 2 + 4) + row + h.D * 2 + row),
     }
     flops = {

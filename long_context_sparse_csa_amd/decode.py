@@ -36,6 +36,8 @@ def build_inputs(c, h, dev, rotate=1):
     d["q"] = synth.normal((c.B, 1, c.H, c.D), c.seed, "q", dev, dtype=torch.bfloat16)
     d["win"] = synth.packed_rows((c.B, c.W), c.D, c.R, c.seed, "win", dev)
     d["raw"] = synth.normal((c.B, 2 * c.m, c.D), c.seed, "raw", dev, dtype=torch.bfloat16)
+    # the tokens' indexer keys: the compressor pools them into k_idx
+    d["raw_idx"] = synth.normal((c.B, 2 * c.m, c.dI), c.seed, "rawI", dev, dtype=torch.bfloat16)
     d["score"] = synth.normal((c.B, 2 * c.m), c.seed, "score", dev)
     d["bias"] = synth.normal((2 * c.m,), c.seed, "bias", dev, std=0.1)
     d["sink"] = synth.normal((c.H,), c.seed, "sink", dev)
@@ -104,7 +106,8 @@ class DecodeStep:
             "csa_compress": lambda: ops.compress_step(a["raw"], a["score"], a["bias"], a["gamma"],
                                                       a["entries"], a["win"],
                                                       raw_pos0=tc + 1 - 2 * c.m, m=c.m, t=tc,
-                                                      seq_pos=cp, win_row=c.W - 1),
+                                                      seq_pos=cp, win_row=c.W - 1,
+                                                      raw_idx=a["raw_idx"], k_idx=a["k_idx"]),
             "index_score": lambda: ops.index_score(a["q_idx"], a["w_idx"], a["k_idx"], n_entries=Nc,
                                                    q_pos0=tc, seq_pos=cp, m=c.m,
                                                    scores=self.scores),
