@@ -53,8 +53,8 @@ COPY_BYTES = 1 << 30           # calibration copy for the HBM byte counters
 # for torch's elementwise kernel over 1 GiB in and 1 GiB out (FETCH 524,319
 # KiB -> x2.0; WRITE 1,048,576 KiB -> x1.0).  Valid only for the kernel
 # sources they were taken with (hash below); otherwise reported as null.
-TRAFFIC = {"sources_sha256_16": "f97dc679ac2f5a24",
-           "fetch_kib": 262699.2, "fetch_scale": 2.0,
+TRAFFIC = {"sources_sha256_16": "bfeba9f6fe104e16",
+           "fetch_kib": 262708.2, "fetch_scale": 2.0,
            "write_kib": 8192.0, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("long_context_sparse_csa_amd/csrc/indexer.hip",
                    "long_context_sparse_csa_amd/csrc/common.hpp")
