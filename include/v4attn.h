@@ -143,6 +143,36 @@ int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const floa
                          void* stream);
 
 /*
+ * v4attn_compress_steps -- v4attn_compress_step for n layers (1 <= n <= 2,
+ * the same D) in one launch: each descriptor holds one layer's arguments,
+ * with the meaning, checks and errors of v4attn_compress_step (the first
+ * failing layer's status is returned and nothing is launched).  For a
+ * decode step over an interleaved stack, whose layers' compress steps are
+ * independent of each other.
+ */
+typedef struct {
+  const uint16_t* raw;
+  const float* tok_score;
+  const float* pos_bias;
+  const float* gamma;
+  int B, L, D, R;
+  int64_t raw_pos0;
+  int m;
+  int64_t t;
+  const int64_t* seq_pos;
+  float eps, rope_base;
+  uint8_t* entries;
+  int64_t ent_rows;
+  uint8_t* win;
+  int64_t win_rows, win_row;
+  const uint16_t* raw_idx;
+  int dI;
+  uint16_t* k_idx;
+} v4attn_compress_step_desc;
+int v4attn_compress_steps(const v4attn_compress_step_desc* steps, int n,
+                          void* stream);
+
+/*
  * Ragged batches (v4attn_index_topk, v4attn_index_score,
  * v4attn_topk_select, v4attn_csa_attend, v4attn_hca_attend): seq_pos is a
  * nullable HOST array i64 [B] (B <= 64) of per-sequence positions; sequence

@@ -219,12 +219,16 @@ int v4attn_compress(const uint16_t* raw, const float* tok_score, const float* po
   return hip_status(v4::launch_compress(a, (hipStream_t)stream), "compress launch");
 }
 
-int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const float* pos_bias,
-                         const float* gamma, int B, int L, int D, int R, int64_t raw_pos0, int m,
-                         int64_t t, const int64_t* seq_pos, float eps, float rope_base,
-                         uint8_t* entries, int64_t ent_rows, uint8_t* win, int64_t win_rows,
-                         int64_t win_row, const uint16_t* raw_idx, int dI, uint16_t* k_idx,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates one layer's decode-step arguments and fills the kernel's.
+int step_args(const uint16_t* raw, const float* tok_score, const float* pos_bias,
+              const float* gamma, int B, int L, int D, int R, int64_t raw_pos0, int m, int64_t t,
+              const int64_t* seq_pos, float eps, float rope_base, uint8_t* entries,
+              int64_t ent_rows, uint8_t* win, int64_t win_rows, int64_t win_row,
+              const uint16_t* raw_idx, int dI, uint16_t* k_idx, v4::CompressStepArgs* out) {
   if (!raw || !gamma || !win) return fail(V4ATTN_EINVAL, "null raw, gamma or win");
   if (B < 0 || L < 0 || ent_rows < 0 || win_rows < 0)
     return fail(V4ATTN_EINVAL, "negative B, L, ent_rows or win_rows");
@@ -269,7 +273,43 @@ int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const floa
   a.raw_idx = raw_idx;
   a.dI = dI;
   a.kidx = raw_idx ? k_idx : nullptr;
+  *out = a;
+  return V4ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int v4attn_compress_step(const uint16_t* raw, const float* tok_score, const float* pos_bias,
+                         const float* gamma, int B, int L, int D, int R, int64_t raw_pos0, int m,
+                         int64_t t, const int64_t* seq_pos, float eps, float rope_base,
+                         uint8_t* entries, int64_t ent_rows, uint8_t* win, int64_t win_rows,
+                         int64_t win_row, const uint16_t* raw_idx, int dI, uint16_t* k_idx,
+                         void* stream) {
+  v4::CompressStepArgs a;
+  if (int st = step_args(raw, tok_score, pos_bias, gamma, B, L, D, R, raw_pos0, m, t, seq_pos, eps,
+                         rope_base, entries, ent_rows, win, win_rows, win_row, raw_idx, dI, k_idx,
+                         &a))
+    return st;
   return hip_status(v4::launch_compress_step(a, (hipStream_t)stream), "compress step launch");
+}
+
+int v4attn_compress_steps(const v4attn_compress_step_desc* steps, int n, void* stream) {
+  if (!steps) return fail(V4ATTN_EINVAL, "null steps");
+  if (n < 1 || n > v4::kMaxSteps)
+    return fail(V4ATTN_EUNSUPPORTED, "n = %d: 1 <= n <= %d layers are built", n, v4::kMaxSteps);
+  v4::CompressStepArgs a[v4::kMaxSteps];
+  for (int z = 0; z < n; ++z) {
+    const v4attn_compress_step_desc& d = steps[z];
+    if (int st = step_args(d.raw, d.tok_score, d.pos_bias, d.gamma, d.B, d.L, d.D, d.R,
+                           d.raw_pos0, d.m, d.t, d.seq_pos, d.eps, d.rope_base, d.entries,
+                           d.ent_rows, d.win, d.win_rows, d.win_row, d.raw_idx, d.dI, d.k_idx,
+                           &a[z]))
+      return st;
+    if (d.D != steps[0].D) return fail(V4ATTN_EUNSUPPORTED, "every layer of one call needs the same D");
+  }
+  return hip_status(v4::launch_compress_steps(a, n, (hipStream_t)stream), "compress steps launch");
 }
 
 size_t v4attn_index_topk_workspace(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m,

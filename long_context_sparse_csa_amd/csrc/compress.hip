@@ -256,55 +256,66 @@ __global__ __launch_bounds__(256) void compress_pack_kernel(
 // One decode step of the compressor: block 0 of each sequence pools the entry
 // the new token completes (if any), the last block packs the token's window
 // row; both run side by side in one launch.
+// One decode step of one or more layers' compressors (grid layer z runs
+// layer z): block 0 of each sequence pools the entry its token completes
+// (if any), the last block packs the token's window row.
 template <int VPL>
-__global__ __launch_bounds__(kPoolThreads) void compress_step_kernel(
-    const uint16_t* __restrict__ raw, const float* __restrict__ score,
-    const float* __restrict__ bias, const float* __restrict__ gamma, int L, int R,
-    int64_t raw_pos0, int m, int64_t t, float eps, const RopeTurns rope,
-    uint8_t* __restrict__ ent, int64_t ent_rows, uint8_t* __restrict__ win, int64_t win_rows,
-    int64_t win_row, const bool ragged, const SeqPos pos, const uint16_t* __restrict__ raw_idx,
-    int dI, uint16_t* __restrict__ kidx) {
+__global__ __launch_bounds__(kPoolThreads) void compress_step_kernel(CompressStepBatch bt) {
   constexpr int D = VPL * 64;
+  const CompressStepArgs& a = bt.s[blockIdx.z];
   const int b = blockIdx.y;
-  if (ragged) {   // this sequence's token; its raw rows end at it
-    t = pos.p[b];
-    raw_pos0 = t - L + 1;
-    if (blockIdx.x == 0 && gridDim.x == 2 && (t + 1) % m != 0) return;   // no entry completes
+  if (b >= a.B) return;   // a layer with fewer sequences than the grid
+  int64_t t = a.t, raw_pos0 = a.raw_pos0;
+  if (a.ragged) {   // this sequence's token; its raw rows end at it
+    t = a.pos.p[b];
+    raw_pos0 = t - a.L + 1;
   }
+  if (blockIdx.x == 0 && gridDim.x == 2 && (t + 1) % a.m != 0) return;   // no entry completes
   if (blockIdx.x == gridDim.x - 1) {
     if (threadIdx.x >= 64) return;
     const int lane = threadIdx.x;
     float y[VPL];
-    load_bf16_row<VPL>(raw + ((int64_t)b * L + (t - raw_pos0)) * D + lane * VPL, y);
-    rmsnorm_wave<VPL>(y, gamma, lane, eps);
-    rotate_and_pack<VPL>(win + ((int64_t)b * win_rows + win_row) * (D + R), y, lane, R, t, rope);
+    load_bf16_row<VPL>(a.raw + ((int64_t)b * a.L + (t - raw_pos0)) * D + lane * VPL, y);
+    rmsnorm_wave<VPL>(y, a.gamma, lane, a.eps);
+    rotate_and_pack<VPL>(a.win + ((int64_t)b * a.win_rows + a.win_row) * (D + a.R), y, lane, a.R, t,
+                         a.rope);
     return;
   }
-  const int64_t j = (t + 1) / m - 1;
-  pool_entry<VPL>(raw, score, bias, gamma, L, R, raw_pos0, m, j, b, eps, rope,
-                  ent + ((int64_t)b * ent_rows + j) * (D + R), raw_idx, dI,
-                  kidx ? kidx + ((int64_t)b * ent_rows + j) * dI : nullptr);
+  const int64_t j = (t + 1) / a.m - 1;
+  pool_entry<VPL>(a.raw, a.tok_score, a.pos_bias, a.gamma, a.L, a.R, raw_pos0, a.m, j, b, a.eps,
+                  a.rope, a.ent + ((int64_t)b * a.ent_rows + j) * (D + a.R), a.raw_idx, a.dI,
+                  a.kidx ? a.kidx + ((int64_t)b * a.ent_rows + j) * a.dI : nullptr);
 }
 
-hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st) {
-  if (a.B == 0) return hipSuccess;
-  bool pool = (a.t + 1) % a.m == 0;
-  if (a.ragged) {
-    pool = false;
-    for (int b = 0; b < a.B; ++b) pool = pool || (a.pos.p[b] + 1) % a.m == 0;
+hipError_t launch_compress_steps(const CompressStepArgs* a, int n, hipStream_t st) {
+  if (n < 1 || n > kMaxSteps) return hipErrorInvalidValue;
+  CompressStepBatch bt{};
+  bool pool = false;
+  int maxB = 0;
+  for (int z = 0; z < n; ++z) {
+    if (a[z].D != a[0].D) return hipErrorInvalidValue;   // one kernel instance
+    bt.s[z] = a[z];
+    maxB = a[z].B > maxB ? a[z].B : maxB;
+    if (a[z].ragged) {
+      for (int b = 0; b < a[z].B; ++b) pool = pool || (a[z].pos.p[b] + 1) % a[z].m == 0;
+    } else {
+      pool = pool || (a[z].B > 0 && (a[z].t + 1) % a[z].m == 0);
+    }
   }
-  dim3 grid(pool ? 2 : 1, a.B);
-#define V4_STEP(VPL)                                                                        \
-  compress_step_kernel<VPL><<<grid, kPoolThreads, 0, st>>>(                                 \
-      a.raw, a.tok_score, a.pos_bias, a.gamma, a.L, a.R, a.raw_pos0, a.m, a.t, a.eps, a.rope, \
-      a.ent, a.ent_rows, a.win, a.win_rows, a.win_row, a.ragged, a.pos, a.raw_idx, a.dI, a.kidx)
-  switch (a.D) {
+  if (maxB == 0) return hipSuccess;
+  dim3 grid(pool ? 2 : 1, maxB, n);
+#define V4_STEP(VPL) compress_step_kernel<VPL><<<grid, kPoolThreads, 0, st>>>(bt)
+  switch (a[0].D) {
     case 128: V4_STEP(2); break;
     case 256: V4_STEP(4); break;
     default: V4_STEP(8); break;
   }
 #undef V4_STEP
   return hipGetLastError();
+}
+
+hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st) {
+  return launch_compress_steps(&a, 1, st);
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {

@@ -61,6 +61,12 @@ struct CompressStepArgs {
   uint16_t* kidx;          // [B, ent_rows, dI]: the entry's pooled indexer key at row j
 };
 hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st);
+// Several layers' decode steps (same D) in one launch.
+constexpr int kMaxSteps = 2;   // the arguments of every layer travel in the kernel arguments
+struct CompressStepBatch {
+  CompressStepArgs s[kMaxSteps];
+};
+hipError_t launch_compress_steps(const CompressStepArgs* a, int n, hipStream_t st);
 
 // Lightning-indexer scoring into a dense fp32 score buffer.
 struct IndexScoreArgs {

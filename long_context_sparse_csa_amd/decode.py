@@ -60,8 +60,9 @@ def build_inputs(c, h, dev, rotate=1):
 class DecodeStep:
     """The library calls of one decode step over fixed buffers."""
 
-    NAMES = ("csa_compress", "index_score", "topk_select", "csa_attend",
-             "hca_compress", "hca_attend")
+    # both layers' compress steps go out in one launch ("compress"); the
+    # per-layer calls remain available as "csa_compress" / "hca_compress"
+    NAMES = ("compress", "index_score", "topk_select", "csa_attend", "hca_attend")
 
     def __init__(self, inp, c, h, dev, csa_pos=None, hca_pos=None):
         """csa_pos / hca_pos: optional per-sequence positions of the new
@@ -102,7 +103,14 @@ class DecodeStep:
         if hp is not None:
             th = max(hp)
         ent_h = b["entries"][rot % len(b["entries"])]
+        csa_step = dict(raw=a["raw"], tok_score=a["score"], pos_bias=a["bias"], gamma=a["gamma"],
+                        entries=a["entries"], win=a["win"], raw_pos0=tc + 1 - 2 * c.m, m=c.m, t=tc,
+                        seq_pos=cp, win_row=c.W - 1, raw_idx=a["raw_idx"], k_idx=a["k_idx"])
+        hca_step = dict(raw=b["raw"], tok_score=b["score"], pos_bias=b["bias"], gamma=b["gamma"],
+                        entries=ent_h, win=b["win"], raw_pos0=th + 1 - 2 * h.m, m=h.m, t=th,
+                        seq_pos=hp, win_row=h.W - 1)
         return {
+            "compress": lambda: ops.compress_steps([csa_step, hca_step]),
             "csa_compress": lambda: ops.compress_step(a["raw"], a["score"], a["bias"], a["gamma"],
                                                       a["entries"], a["win"],
                                                       raw_pos0=tc + 1 - 2 * c.m, m=c.m, t=tc,

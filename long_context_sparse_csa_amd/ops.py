@@ -39,6 +39,7 @@ _SIGS = {
                              _P, _I, _P, _P]),
     "v4attn_compress_step": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _L, _P, _F, _F, _P, _L,
                                   _P, _L, _L, _P, _I, _P, _P]),
+    "v4attn_compress_steps": (_I, [_P, _I, _P]),
     "v4attn_index_topk_workspace": (_Z, [_I, _I, _L, _L, _I, _I]),
     "v4attn_index_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _L, _L, _L, _P, _I, _I, _P, _P, _P, _Z,
                                _P]),
@@ -76,6 +77,17 @@ _SIGS = {
     "v4attn_nsa_attend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _L, _I,
                                _I, _L, _F, _F, _F, _P, _P, _P, _P, _Z, _P]),
 }
+
+class CompressStepDesc(_c.Structure):
+    """v4attn_compress_step_desc: one layer's decode-step arguments."""
+    _fields_ = [("raw", _c.c_void_p), ("tok_score", _c.c_void_p), ("pos_bias", _c.c_void_p),
+                ("gamma", _c.c_void_p), ("B", _c.c_int), ("L", _c.c_int), ("D", _c.c_int),
+                ("R", _c.c_int), ("raw_pos0", _c.c_int64), ("m", _c.c_int), ("t", _c.c_int64),
+                ("seq_pos", _c.c_void_p), ("eps", _c.c_float), ("rope_base", _c.c_float),
+                ("entries", _c.c_void_p), ("ent_rows", _c.c_int64), ("win", _c.c_void_p),
+                ("win_rows", _c.c_int64), ("win_row", _c.c_int64), ("raw_idx", _c.c_void_p),
+                ("dI", _c.c_int), ("k_idx", _c.c_void_p)]
+
 
 _lib = None
 
@@ -235,6 +247,40 @@ def compress_step(raw, tok_score, pos_bias, gamma, entries, win, *, m, win_row, 
                                      float(rope_base), _ptr(entries), entries.shape[1], _ptr(win),
                                      win.shape[1], int(win_row), ri, dI, kp, _stream(raw)))
     return entries, win
+
+
+def compress_steps(layers):
+    """compress_step for several layers (each a dict of compress_step's
+    arguments; same D) in one launch."""
+    descs = (CompressStepDesc * len(layers))()
+    keep = []
+    for z, kw in enumerate(layers):
+        kw = dict(kw)
+        raw, ts, pb, gm = kw.pop("raw"), kw.pop("tok_score"), kw.pop("pos_bias"), kw.pop("gamma")
+        ent, win = kw.pop("entries"), kw.pop("win")
+        m, win_row = kw.pop("m"), kw.pop("win_row")
+        R = kw.pop("R", 64)
+        B, L, D = raw.shape
+        arr, sp, t = _seq_pos(kw.pop("seq_pos", None), B, kw.pop("t", None))
+        raw_pos0 = kw.pop("raw_pos0", None)
+        raw_pos0 = t - L + 1 if raw_pos0 is None else raw_pos0
+        raw_idx, k_idx = kw.pop("raw_idx", None), kw.pop("k_idx", None)
+        eps, base = kw.pop("eps", 1e-6), kw.pop("rope_base", 10000.0)
+        if kw:
+            raise ValueError(f"unknown arguments {sorted(kw)}")
+        ri, dI, kp = _kidx_args(raw_idx, k_idx, B, L, 0)
+        keep.append(arr)
+        d = descs[z]
+        d.raw, d.tok_score, d.pos_bias, d.gamma = (raw.data_ptr(), ts.data_ptr(), pb.data_ptr(),
+                                                   gm.data_ptr())
+        d.B, d.L, d.D, d.R = B, L, D, R
+        d.raw_pos0, d.m, d.t, d.seq_pos = int(raw_pos0), int(m), int(t), sp
+        d.eps, d.rope_base = float(eps), float(base)
+        d.entries, d.ent_rows, d.win, d.win_rows = (ent.data_ptr(), ent.shape[1], win.data_ptr(),
+                                                    win.shape[1])
+        d.win_row, d.raw_idx, d.dI, d.k_idx = int(win_row), ri, dI, kp
+    check(lib().v4attn_compress_steps(_c.cast(descs, _c.c_void_p), len(layers),
+                                      _stream(layers[0]["raw"])))
 
 
 def compress_pack(raw, gamma, out, *, raw_pos0, n_out=None, out_row0=0, eps=1e-6,

@@ -32,7 +32,7 @@ MISALIGNED = ctypes.c_void_p(0x100008)
 def test_exports_every_header_function():
     names = ops().header_functions()
     assert "v4attn_compress" in names and "v4attn_hca_attend" in names
-    assert len(names) == 27
+    assert len(names) == 28
     for n in names:
         assert hasattr(L(), n), n
     assert L().v4attn_version() == 1

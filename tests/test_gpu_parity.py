@@ -519,3 +519,44 @@ def test_compress_pools_indexer_keys(m, dI, D):
         got2 = bf16_to_f64(kid2[b])
         assert np.array_equal(got2[j], got[j])              # the step writes the same key
         assert np.all(got2[np.arange(n_out) != j] == 0)     # and nothing else
+
+
+def test_compress_steps_of_two_layers_in_one_launch():
+    """compress_steps runs a CSA-style (m = 4, 8 sequences, pooled indexer
+    keys) and an HCA-style (m = 128, 3 sequences, per-sequence positions)
+    layer in one launch: the same bytes as the two compress_step calls, and
+    the CSA layer's entry within one ulp of the oracle."""
+    D, R, W = 512, 64, 16
+    mc, mh, Bc, Bh = 4, 128, 8, 3
+    tc, ph = 4095, [128 * 9 - 1, 128 * 4 + 3, 127]
+    rc, sc, bc, gc = _compress_inputs(Bc, 2 * mc, D, mc, 71)
+    rh, sh, bh, gh = _compress_inputs(Bh, 2 * mh, D, mh, 72)
+    kr = synth.normal((Bc, 2 * mc, 128), 71, "kraw", DEV, dtype=torch.bfloat16)
+
+    def bufs():
+        return (torch.zeros((Bc, tc // mc + 1, D + R), dtype=torch.uint8, device=DEV),
+                torch.zeros((Bc, W, D + R), dtype=torch.uint8, device=DEV),
+                torch.zeros((Bc, tc // mc + 1, 128), dtype=torch.bfloat16, device=DEV),
+                torch.zeros((Bh, 10, D + R), dtype=torch.uint8, device=DEV),
+                torch.zeros((Bh, W, D + R), dtype=torch.uint8, device=DEV))
+
+    def layers(ec, wc, kc, eh, wh):
+        return [dict(raw=rc, tok_score=sc, pos_bias=bc, gamma=gc, entries=ec, win=wc, m=mc, t=tc,
+                     win_row=W - 1, raw_idx=kr, k_idx=kc),
+                dict(raw=rh, tok_score=sh, pos_bias=bh, gamma=gh, entries=eh, win=wh, m=mh,
+                     seq_pos=ph, win_row=W - 1)]
+    one = bufs()
+    ops().compress_steps(layers(*one))
+    two = bufs()
+    for kw in layers(*two):
+        ops().compress_step(**kw)
+    torch.cuda.synchronize()
+    for x, y in zip(one, two):
+        assert torch.equal(x, y)
+    j = (tc + 1) // mc - 1
+    c = bf16_to_f64(rc)
+    for b in range(Bc):
+        js, e = oc.compress_pool(c[b], sc[b].cpu().double().numpy(), tc + 1 - 2 * mc, mc,
+                                 bc.cpu().double().numpy(), gc.cpu().double().numpy(), 1e-6, R,
+                                 1e4, j0=j, n=1)
+        assert_rows_within_one_ulp(one[0][b, j:j + 1].cpu().numpy(), e, D, R)
