@@ -90,6 +90,7 @@ class DecodeStep:
         a["raw_last"] = a["raw"][:, -1:].contiguous()   # the new token's raw latent
         b["raw_last"] = b["raw"][:, -1:].contiguous()
         self.side = torch.cuda.Stream(device=dev)       # default priority
+        self._calls = {}
         self.ev = [torch.cuda.Event() for _ in range(4)]
 
     def calls(self, rot=0):
@@ -141,6 +142,26 @@ class DecodeStep:
         f = self.calls(rot)
         for n in self.NAMES:
             f[n]()
+
+    def run_concurrent(self, rot=0):
+        """The step with the HCA layer's attention on a second stream beside
+        the CSA layer's indexer, top-k and attention: the HCA attention is
+        bound by its matrix-core issue, the indexer by HBM, so they overlap.
+        The current stream waits for both before it goes on."""
+        if rot not in self._calls:      # built once per cache copy (host time per step)
+            self._calls[rot] = self.calls(rot)
+        f = self._calls[rot]
+        main, side, ev = torch.cuda.current_stream(), self.side, self.ev
+        f["compress"]()
+        ev[2].record(main)
+        f["index_score"]()
+        side.wait_event(ev[2])
+        with torch.cuda.stream(side):
+            f["hca_attend"]()
+            ev[3].record(side)
+        f["topk_select"]()
+        f["csa_attend"]()
+        main.wait_event(ev[3])
 
     def run_overlapped(self, rot=0):
         """The step with the CSA layer's compress step on a second stream,

@@ -1,5 +1,6 @@
-"""The decode step replayed from HIP graphs (the schedule bench.py times)
-gives exactly the outputs of the calls launched one by one.
+"""The decode step's other schedules (HCA attention on a second stream, the
+one bench.py times; HIP-graph replays) give exactly the outputs of the
+calls launched one by one.
 
 The step's kernels are deterministic and its writes (window row, pooled
 entry) are idempotent, so every run must reproduce the eager outputs bit for
@@ -39,6 +40,10 @@ def test_decode_step_graph_replays_match_eager():
     for r in range(2):
         st.run_overlapped(r)
         assert _same(_snap(st), ref[r]), f"overlapped schedule, cache {r}"
+    for i in range(4):   # concurrent schedule, back to back without syncs in between
+        st.run_concurrent(i % 2)
+        st.run_concurrent((i + 1) % 2)
+        assert _same(_snap(st), ref[(i + 1) % 2]), f"concurrent schedule, round {i}"
     graphs = [st.capture(r) for r in range(2)]
     for i in range(6):
         r = i % 2
