@@ -518,8 +518,8 @@ def ragged_section(dev, inp, reps):
     from long_context_sparse_csa_amd.configs import CSA_1M as c, HCA_1M as h
     csa_pos = [(b + 1) * (1 << 17) - 1 for b in range(c.B)]
     hca_pos = [(b + 1) * (1 << 15) - 1 for b in range(h.B)]
-    launches, _ = make_step(inp, dev, csa_pos=csa_pos, hca_pos=hca_pos)
-    ms, _ = run_timed(launches, reps, 5)
+    launches, st = make_step(inp, dev, csa_pos=csa_pos, hca_pos=hca_pos)
+    ms, _ = run_timed_concurrent(st, len(inp["hca"]["entries"]), reps, 5)
     br = run_breakdown(launches, 20)
     vis = sum(min(c.T // c.m, (p + 1) // c.m) for p in csa_pos)
     idx_bytes = vis * c.dI * 2 + c.B * (c.HI * c.dI * 2 + c.HI * 4 + 0)
