@@ -137,11 +137,14 @@ void attend_ws_layout(v4::AttendArgs& a, void* ws) {
   a.part_ml = a.splits > 1 ? reinterpret_cast<float*>(w + o_bytes) : nullptr;
 }
 
+// need_sink: the call takes a per-head sink (every attention call but the
+// NSA-style variant, whose branches have none).
 int check_attend_common(const uint16_t* q, const uint8_t* entries, const uint8_t* win,
                         const float* gamma_q, const float* sink, int B, int Tq, int H, int D,
                         int R, int64_t Ncap, int W, int64_t q_pos0, float scale, float eps,
-                        float rope_base, const uint16_t* out) {
-  if (!q || !gamma_q || !sink || !out) return fail(V4ATTN_EINVAL, "null q, gamma_q, sink or out");
+                        float rope_base, const uint16_t* out, bool need_sink = true) {
+  if (!q || !gamma_q || (need_sink && !sink) || !out)
+    return fail(V4ATTN_EINVAL, "null q, gamma_q, sink or out");
   if (B < 0 || Tq < 0) return fail(V4ATTN_EINVAL, "negative B or Tq");
   if (int st = check_dr(D, R)) return st;
   if (H < 1 || H > 64) return fail(V4ATTN_EUNSUPPORTED, "H = %d: 1 <= H <= 64 is built", H);
@@ -775,9 +778,8 @@ int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
                       int64_t Ntok, int W, int n_sel, int64_t q_pos0, float scale, float eps,
                       float rope_base, uint16_t* out, int32_t* blocks, float* block_score,
                       void* ws, size_t ws_bytes, void* stream) {
-  static const float kNoSinkCheck = 0.f;   // the common check wants a sink; no branch has one
-  if (int st = check_attend_common(q, entries, win, gamma_q, &kNoSinkCheck, B, Tq, H, D, R, Ncap,
-                                   W, q_pos0, scale, eps, rope_base, out))
+  if (int st = check_attend_common(q, entries, win, gamma_q, nullptr, B, Tq, H, D, R, Ncap, W,
+                                   q_pos0, scale, eps, rope_base, out, false))
     return st;
   if (!gates) return fail(V4ATTN_EINVAL, "null gates");
   if (n_entries < 0 || n_entries > Ncap) return fail(V4ATTN_EINVAL, "need 0 <= n_entries <= Ncap");

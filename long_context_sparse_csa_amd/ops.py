@@ -668,10 +668,17 @@ def compress_backward(raw, tok_score, pos_bias, gamma, d_entries, *, raw_pos0, m
     n_out = d_entries.shape[1]
     g = dict(grads or {})
     dev = raw.device
-    d_raw = g.get("d_raw", torch.zeros((B, L, D), dtype=torch.float32, device=dev))
-    d_score = g.get("d_score", torch.zeros((B, L), dtype=torch.float32, device=dev))
-    d_bias = g.get("d_bias", torch.zeros(2 * m, dtype=torch.float32, device=dev))
-    d_gamma = g.get("d_gamma", torch.zeros(D, dtype=torch.float32, device=dev))
+
+    def buf(name, shape):
+        t = g.get(name)
+        if t is None:
+            t = torch.zeros(shape, dtype=torch.float32, device=dev)
+        _need(t, name, torch.float32)
+        return t
+    d_raw = buf("d_raw", (B, L, D))
+    d_score = buf("d_score", (B, L))
+    d_bias = buf("d_bias", (2 * m,))
+    d_gamma = buf("d_gamma", (D,))
     check(lib().v4attn_compress_backward(
         _ptr(raw), _ptr(tok_score), _ptr(pos_bias), _ptr(gamma), B, L, D, R, int(raw_pos0), int(m),
         int(entry0), n_out, float(eps), float(rope_base), _ptr(d_entries), _ptr(d_raw),
