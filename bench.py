@@ -638,7 +638,7 @@ def main():
                          "decode steps for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
 

@@ -12,7 +12,7 @@ from long_context_sparse_csa_amd import LIB_PATH
 import os
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH),
-                                reason="libv4attn.so not built (run __graft_entry__.build())")
+                                reason="libv4attn.so not built (python -m long_context_sparse_csa_amd.build)")
 
 
 def L():
