@@ -55,15 +55,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // a tile [64 rows][32 k] from a row-major (rows x k) matrix, or from a
-  // (k x rows) one, transposed on the way into LDS
-  auto stage = [&](uint16_t (*s)[kLdsK], const uint16_t* p, int64_t ld, int r0, int k0, bool tr) {
+  // (k x rows) one, transposed on the way into LDS; the next k-tile's global
+  // loads are in flight while the current one's MFMAs run
+  auto fetch = [&](const uint16_t* p, int64_t ld, int r0, int k0, bool tr) -> uint4 {
     if (!tr) {
       const int r = tid >> 2, ch = tid & 3;
-      *reinterpret_cast<uint4*>(&s[r][8 * ch]) =
-          *reinterpret_cast<const uint4*>(p + (int64_t)(r0 + r) * ld + k0 + 8 * ch);
+      return *reinterpret_cast<const uint4*>(p + (int64_t)(r0 + r) * ld + k0 + 8 * ch);
+    }
+    const int kk = tid >> 3, ch = tid & 7;
+    return *reinterpret_cast<const uint4*>(p + (int64_t)(k0 + kk) * ld + r0 + 8 * ch);
+  };
+  auto put = [&](uint16_t (*s)[kLdsK], uint4 v, bool tr) {
+    if (!tr) {
+      const int r = tid >> 2, ch = tid & 3;
+      *reinterpret_cast<uint4*>(&s[r][8 * ch]) = v;
     } else {
       const int kk = tid >> 3, ch = tid & 7;
-      const uint4 v = *reinterpret_cast<const uint4*>(p + (int64_t)(k0 + kk) * ld + r0 + 8 * ch);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -72,10 +79,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
       }
     }
   };
+  uint4 ra = fetch(A, g.lda, m0, 0, AT), rb = fetch(B, g.ldb, n0, 0, !BT);
   for (int k0 = 0; k0 < g.K; k0 += 32) {
-    stage(sA, A, g.lda, m0, k0, AT);
-    stage(sB, B, g.ldb, n0, k0, !BT);
+    put(sA, ra, AT);
+    put(sB, rb, !BT);
     __syncthreads();
+    if (k0 + 32 < g.K) {
+      ra = fetch(A, g.lda, m0, k0 + 32, AT);
+      rb = fetch(B, g.ldb, n0, k0 + 32, !BT);
+    }
     bf16x8 a[2], b[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(&sA[wm * 32 + 16 * i + c][8 * gq]);
