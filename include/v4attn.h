@@ -528,6 +528,7 @@ int v4attn_compress_backward(const uint16_t* raw, const float* tok_score,
  * score of v4attn_index_score, loss = sum_j P_j (log P_j - log Q_j);
  * d score_j = Q_j - P_j; P is a constant.
  *   q_idx bf16 [B, Tq, HI, dI], w_idx f32 [B, Tq, HI], k_idx bf16 [B, Ncap, dI]
+ *   (q_idx and k_idx 16-byte aligned)
  *   sel i32 [B, Tq, ns], target f32 [B, Tq, ns]
  *   loss f32 [B, Tq] (written, nullable); dq_idx f32 [B, Tq, HI, dI] and
  *   dw_idx f32 [B, Tq, HI] (written); dk_idx f32 [B, Ncap, dI] (added to)

@@ -1028,6 +1028,7 @@ int v4attn_index_kl_backward(const uint16_t* q_idx, const float* w_idx, const ui
   if (dI != 32 && dI != 64 && dI != 128)
     return fail(V4ATTN_EUNSUPPORTED, "dI = %d: dI in {32, 64, 128} is built", dI);
   if (ns < 1 || ns > kMaxK) return fail(V4ATTN_EUNSUPPORTED, "ns = %d: 1 <= ns <= %d is built", ns, kMaxK);
+  if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(V4ATTN_EINVAL, "q_idx and k_idx must be 16-byte aligned");
   const size_t need = kl_ws(B, Tq, dI, ns);
   if (!ws || ws_bytes < need)
     return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);

@@ -551,14 +551,18 @@ __global__ __launch_bounds__(256) void kl_gather_kernel(KlArgs a, int q0) {
     const bool ok = j >= 0 && j < a.Ncap;
     uint16_t* dst = a.K + ((int64_t)qc * a.nsp + x) * a.dIp;
     const uint16_t* src = a.k_idx + ((int64_t)b * a.Ncap + (ok ? j : 0)) * a.dI;
-    for (int e = lane; e < a.dIp; e += 64) dst[e] = ok && e < a.dI ? src[e] : 0;
+    for (int e = 8 * lane; e < a.dIp; e += 512)   // 16-byte pieces
+      *reinterpret_cast<uint4*>(dst + e) =
+          ok && e < a.dI ? *reinterpret_cast<const uint4*>(src + e) : uint4{0u, 0u, 0u, 0u};
     if (lane == 0) a.rowmap[(int64_t)qc * a.nsp + x] = ok ? (int64_t)b * a.Ncap + j : -1;
   }
   if (blockIdx.x < 16) {   // 64 head slots of q^I, four a workgroup
     const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
     uint16_t* dst = a.Qi + ((int64_t)qc * 64 + h) * a.dIp;
     const uint16_t* src = a.q_idx + ((int64_t)qr * a.HI + (h < a.HI ? h : 0)) * a.dI;
-    for (int e = lane; e < a.dIp; e += 64) dst[e] = h < a.HI && e < a.dI ? src[e] : 0;
+    for (int e = 8 * lane; e < a.dIp; e += 512)
+      *reinterpret_cast<uint4*>(dst + e) =
+          h < a.HI && e < a.dI ? *reinterpret_cast<const uint4*>(src + e) : uint4{0u, 0u, 0u, 0u};
   }
 }
 
