@@ -512,14 +512,20 @@ def ragged_section(dev, inp, reps):
     """The decode step with a ragged batch: the same caches and calls, each
     sequence's new token at its own position -- CSA sequence b at
     (b + 1) 2^17 - 1, HCA sequence b at (b + 1) 2^15 - 1 (lengths 128K to 1M,
-    mean 0.56M) -- timed like the headline (calls launched one by one).
+    mean 0.56M) -- timed like the headline (HCA attention on a second stream).
     The indexer reads only each sequence's visible keys, so its algorithmic
     bytes are sum_b V_b (256 + ...) per step."""
     from long_context_sparse_csa_amd.configs import CSA_1M as c, HCA_1M as h
     csa_pos = [(b + 1) * (1 << 17) - 1 for b in range(c.B)]
     hca_pos = [(b + 1) * (1 << 15) - 1 for b in range(h.B)]
     launches, st = make_step(inp, dev, csa_pos=csa_pos, hca_pos=hca_pos)
-    ms, _ = run_timed_concurrent(st, len(inp["hca"]["entries"]), reps, 5)
+    # The first block timed after the ragged step is set up runs host-bound
+    # and 3-5x slower, whichever schedule goes first (cause not found); the
+    # step is timed as three blocks a schedule, the steady-state figure is the
+    # fastest block and the first block is reported beside it.
+    rot = len(inp["hca"]["entries"])
+    blocks = [run_timed_concurrent(st, rot, reps, 5)[0] for _ in range(3)]
+    ms, ms_seq = min(blocks), min(run_timed(launches, reps, 5)[0] for _ in range(3))
     br = run_breakdown(launches, 20)
     vis = sum(min(c.T // c.m, (p + 1) // c.m) for p in csa_pos)
     idx_bytes = vis * c.dI * 2 + c.B * (c.HI * c.dI * 2 + c.HI * 4 + 0)
@@ -530,6 +536,8 @@ def ragged_section(dev, inp, reps):
         "workload": "decode_ragged: CSA B=8 at positions (b+1) 2^17 - 1, HCA B=32 at "
                     "(b+1) 2^15 - 1 (the decode_1m_csa_hca caches)",
         "step_us": round(ms * 1e3, 2),
+        "one_stream_step_us": round(ms_seq * 1e3, 2),
+        "first_block_step_us": round(blocks[0] * 1e3, 2),
         "query_token_layers_per_s": round((c.B + h.B) / (ms * 1e-3), 1),
         "csa_layer_us": round(t_csa, 2), "hca_layer_us": round(t_hca, 2),
         "kernels_us": {k: round(v, 2) for k, v in br.items()},
