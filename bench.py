@@ -163,11 +163,11 @@ def run_timed_concurrent(st, rotate, steps, warmup):
 
 
 def run_timed_graphs(st, rotate, steps, warmup):
-    """Steps replayed from HIP graphs of the overlapped schedule, one graph
+    """Steps replayed from HIP graphs of the concurrent schedule, one graph
     per HCA cache copy (used in turn)."""
     import torch
     for r in range(rotate):
-        st.run_overlapped(r)
+        st.run_concurrent(r)
     torch.cuda.synchronize()
     graphs = [st.capture(r) for r in range(rotate)]
     for i in range(warmup):
@@ -622,8 +622,7 @@ def main():
                     help="time the calls launched one by one on one stream (the default runs "
                          "the HCA attention on a second stream beside the CSA chain)")
     ap.add_argument("--graph", action="store_true",
-                    help="time HIP-graph replays of the overlapped schedule (on this stack "
-                         "slower than the calls launched one by one)")
+                    help="time HIP-graph replays of the concurrent schedule")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill chunk (prints its section as the JSON line)")
@@ -685,7 +684,7 @@ def main():
     log("timing")
     if args.graph:
         ms, wall = run_timed_graphs(st, args.rotate, args.steps, args.warmup)
-        sched = "HIP graph replay, the CSA compress step on a second stream"
+        sched = "HIP graph replay of the concurrent schedule (HCA attention on a second stream)"
     elif args.sequential:
         ms, wall = run_timed(launches, args.steps, args.warmup)
         sched = "calls launched one by one on one stream"

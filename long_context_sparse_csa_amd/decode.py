@@ -7,9 +7,11 @@ Per decode token and sequence, a layer
     top-k, and attends over them plus the window;
   * HCA (compression m'): the compress step, then attention over every entry
     plus the window.
-Within the CSA layer the compress step does not depend on the indexer, so
-`run_overlapped` puts it on a second stream beside the indexer; the attention
-waits for both.  `capture` records that schedule in a HIP graph.
+`run_concurrent` issues both layers' compress steps in one launch, then
+the CSA layer's indexer, top-k and attention on the launching stream and the
+HCA layer's attention on a second stream beside them (every kernel that
+reads an entry, an indexer key or a window row runs after the compress step
+that writes it).  `capture` records that schedule in a HIP graph.
 
 Inputs are seeded synthetic tensors shaped like the workloads in configs.py
 (the random-number recipe is in synth.py).  The HCA caches can rotate over
@@ -163,26 +165,10 @@ class DecodeStep:
         f["csa_attend"]()
         main.wait_event(ev[3])
 
-    def run_overlapped(self, rot=0):
-        """The step with the CSA layer's compress step on a second stream,
-        beside the indexer and the top-k."""
-        f = self.calls(rot)
-        main, side, ev = torch.cuda.current_stream(), self.side, self.ev
-        ev[0].record(main)
-        side.wait_event(ev[0])
-        with torch.cuda.stream(side):
-            f["csa_compress"]()
-            ev[1].record(side)
-        f["index_score"]()
-        f["topk_select"]()
-        main.wait_event(ev[1])
-        f["csa_attend"]()
-        f["hca_compress"]()
-        f["hca_attend"]()
-
     def capture(self, rot=0):
-        """A HIP graph of run_overlapped(rot) (run it eagerly once first)."""
+        """A HIP graph of run_concurrent(rot) (run it eagerly once first, so
+        that nothing is allocated during the capture)."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.run_overlapped(rot)
+            self.run_concurrent(rot)
         return g
