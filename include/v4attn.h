@@ -335,11 +335,13 @@ int v4attn_index_topk_mxfp4(const uint8_t* q4, const uint8_t* q_sc, const float*
  *   ws / ws_bytes  >= v4attn_csa_attend_workspace(...) bytes (split
  *              partials of long rows; 0 is possible); contents on entry are
  *              ignored
- * Accumulation is fp32.  q~ is rounded to bf16; on the E4M3 dims it enters
- * the FP8 matrix cores as the exact sum of two E4M3 terms, and so do the
- * probabilities (each 64-row block of a head scaled by its own power of
- * two, which the cores undo); on the bf16 dims both are bf16.  Rows are
- * never widened: the E4M3 bytes go into the matrix cores as stored.
+ * Accumulation is fp32, split partials included.  On the E4M3 dims q~ (fp32)
+ * enters the FP8 matrix cores as the sum of two E4M3 terms (its rounding and
+ * the rounding of the remainder: at least bf16's eight significant bits), and
+ * so do the probabilities (each 64-row block of a head scaled by its own
+ * power of two, which the cores undo); on the bf16 dims both are rounded to
+ * bf16.  Rows are never widened: the E4M3 bytes go into the matrix cores as
+ * stored.
  */
 size_t v4attn_csa_attend_workspace(int B, int Tq, int H, int D, int k, int W);
 int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries,

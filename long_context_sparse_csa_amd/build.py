@@ -6,6 +6,7 @@ Every call recompiles (a build check must see the current sources).  The
 result is long_context_sparse_csa_amd/libv4attn.so.
 """
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -36,13 +37,19 @@ FLAGS = [
 def build(verbose=False):
     objs = []
     with tempfile.TemporaryDirectory(prefix="v4attn_build_") as tmp:
+        cmds = []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
             if src.endswith(".cpp"):
                 cmd.insert(1, "-xhip")
-            _run(cmd, verbose)
+            cmds.append(cmd)
             objs.append(obj)
+        # one hipcc per source, compiled side by side (at most 16 at once)
+        jobs = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
         tmp_out = OUT + ".tmp"
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_out], verbose)
         os.replace(tmp_out, OUT)

@@ -309,14 +309,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   };
   if (ntiles > 0) issue_tile(0, 0);
 
-  // ---- q~ = RoPE_t(RMSNorm(q)), rounded to bf16 and scaled by 2^qe (per
-  // head, exact), as the B operand of S^T.  Lane (c, g) holds head c's dims
-  // 128 j + 32 g + [0, 32) of every E4M3 k-step j (zero past the E4M3 dims)
-  // and dims (D - R) + 32 s + 8 g + [0, 8) of the two bf16 k-steps s.  On the
-  // E4M3 dims the bf16 value goes into the f8f6f4 MFMA as the exact sum of
-  // two E4M3 terms (hi = its E4M3 rounding, lo = the rest, which has at most
-  // four significant bits; qe puts the head's largest |q~| in [128, 256), so
-  // lo stays out of the subnormals for every |q~| above 2^-9 of the largest).
+  // ---- q~ = RoPE_t(RMSNorm(q)) in fp32, scaled by 2^qe (per head, exact;
+  // qe puts the head's largest |q~| in [128, 256)), as the B operand of S^T.
+  // Lane (c, g) holds head c's dims 128 j + 32 g + [0, 32) of every E4M3
+  // k-step j (zero past the E4M3 dims) and dims (D - R) + 32 s + 8 g + [0, 8)
+  // of the two bf16 k-steps s.  On the E4M3 dims the fp32 value goes into the
+  // f8f6f4 MFMA as the sum of two E4M3 terms: hi = its E4M3 rounding, lo = the
+  // E4M3 rounding of the exact remainder x - hi.  The pair carries at least
+  // the eight significant bits of a bf16 rounding and, because the remainder
+  // is usually well inside hi's half-ulp, about 2.6x less rounding error on
+  // average.  The rotary dims enter the bf16 MFMA rounded to bf16.
   // Slots of 8 dims: 4j + v for the E4M3 dims, 4 NJ + s for the bf16 ones
   // (loaded at the top of the kernel).
   i32x8 qh[NJ], ql[NJ];
@@ -338,21 +340,28 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
     const float rsn = 1.0f / sqrtf(ss / (float)D + a.eps);
-    // q~ of each slot, rotated where the dims are rotary, rounded to bf16 in place
-    float mx = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) {
+    // gamma_q * q * rsn of slot sl, element e (the same fp32 operations in
+    // both passes below, so the E4M3 split sees the values the maximum saw)
+    auto qnorm = [&](int sl, float (&qf)[8]) {
       const int d0 = slot_ok(sl) ? slot_dim(sl) : 0;
       const f32x4 ga = *reinterpret_cast<const f32x4*>(s_gamma + d0);
       const f32x4 gb = *reinterpret_cast<const f32x4*>(s_gamma + d0 + 4);
       const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-      float qf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         qf[2 * e] = gm[2 * e] * (bf16_bits_to_f32(qv[sl][e] & 0xFFFFu) * rsn);
         qf[2 * e + 1] = gm[2 * e + 1] * (bf16_bits_to_f32(qv[sl][e] >> 16) * rsn);
       }
+    };
+    // the largest |q~| of the head; the rotary slots are rotated and rounded
+    // to bf16 in place, the E4M3 slots keep the raw q
+    float mx = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      float qf[8];
+      qnorm(sl, qf);
       if (sl >= 4 * NJ) {
+        const int d0 = slot_dim(sl);
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const int i = (d0 + e - (D - R)) >> 1;
@@ -361,12 +370,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
           qf[e] = x0 * cs - x1 * sn;
           qf[e + 1] = x0 * sn + x1 * cs;
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[sl][e] = pack_bf16x2(qf[2 * e], qf[2 * e + 1]);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[sl][e] = pack_bf16x2(qf[2 * e], qf[2 * e + 1]);
-        mx = fmaxf(mx, fmaxf(fabsf(qf[2 * e]), fabsf(qf[2 * e + 1])));
-      }
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qf[e]));
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -375,21 +383,23 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int v = 0; v < 4; ++v) {
+        float qf[8];
+        qnorm(4 * j + v, qf);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const unsigned w0 = qv[4 * j + v][2 * h2], w1 = qv[4 * j + v][2 * h2 + 1];
-          const float x0 = ldexpf(bf16_bits_to_f32(w0 & 0xFFFFu), qe), x1 = ldexpf(bf16_bits_to_f32(w0 >> 16), qe);
-          const float x2 = ldexpf(bf16_bits_to_f32(w1 & 0xFFFFu), qe), x3 = ldexpf(bf16_bits_to_f32(w1 >> 16), qe);
+          const float x0 = ldexpf(qf[4 * h2], qe), x1 = ldexpf(qf[4 * h2 + 1], qe);
+          const float x2 = ldexpf(qf[4 * h2 + 2], qe), x3 = ldexpf(qf[4 * h2 + 3], qe);
           int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
           hw = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hw, true);
           const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
           const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
           int lw = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - b01.x, x1 - b01.y, 0, false);
           lw = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - b23.x, x3 - b23.y, lw, true);
-          qh[j][2 * v + h2] = hw;
-          ql[j][2 * v + h2] = lw;
+          qh[j][2 * v + h2] = slot_ok(4 * j + v) ? hw : 0;
+          ql[j][2 * v + h2] = slot_ok(4 * j + v) ? lw : 0;
         }
+      }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       u32x4 pk;
@@ -706,12 +716,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   l_run += __shfl_xor(l_run, 32);
   // accumulator i of block db holds dim 16 db + 4g + i
   if (a.splits > 1) {
-    // unnormalised partial (O as bf16, max, sum); the merge kernel adds the sink
-    uint16_t* po = a.part_o + (((int64_t)qr * a.splits + split) * a.H + head) * D;
+    // unnormalised partial (O, max, sum) in fp32; the merge kernel adds the sink
+    float* po = a.part_o + (((int64_t)qr * a.splits + split) * a.H + head) * D;
 #pragma unroll
-    for (int db = 0; db < NB; ++db)
-      *reinterpret_cast<u32x2*>(po + 16 * db + 4 * g) =
-          u32x2{pack_bf16x2(o[db][0], o[db][1]), pack_bf16x2(o[db][2], o[db][3])};
+    for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g) = o[db];
     if (g == 0) {
       float* pm = a.part_ml + (((int64_t)qr * a.splits + split) * a.H + head) * 2;
       pm[0] = l_run > 0.f ? m_run : -INFINITY;
@@ -797,19 +805,18 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   const int hh = tid / QPH, d = 4 * (tid % QPH);
   const int h = h0 + hh;
   if (hh >= HPW || h >= a.H) return;
-  const uint16_t* po = a.part_o + ((int64_t)qr * S * a.H + h) * D + d;
+  const float* po = a.part_o + ((int64_t)qr * S * a.H + h) * D + d;
   const int64_t sstride = (int64_t)a.H * D;
   f32x4 x = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 8) {   // eight split partials in flight
-    u32x2 v[8];
+    f32x4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      v[u] = *reinterpret_cast<const u32x2*>(po + (int64_t)min(s0 + u, S - 1) * sstride);
+      v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)min(s0 + u, S - 1) * sstride);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float w = s0 + u < S ? s_w[hh][s0 + u] : 0.f;
-      x += w * f32x4{bf16_bits_to_f32(v[u].x & 0xFFFFu), bf16_bits_to_f32(v[u].x >> 16),
-                     bf16_bits_to_f32(v[u].y & 0xFFFFu), bf16_bits_to_f32(v[u].y >> 16)};
+      x += w * v[u];
     }
   }
   float y[4] = {x[0], x[1], x[2], x[3]};

@@ -33,21 +33,34 @@ MAX_ABS = 2e-2
 REL_L2 = 5e-3
 
 
-def assert_attn_close(got, want, what="", logit_mult=1.0):
-    """Spec bars (max-abs 2e-2, rel-L2 5e-3) at the standard logit scale
-    1/sqrt(D).  Stress cases use logits `logit_mult` times sharper.  The part
-    of the error that comes from feeding the matrix cores a bf16 q~ grows
-    linearly with the logit scale, while the bf16 rounding of P and of the
-    output does not.  A float64 simulation of one 64-head query (bf16 q~, bf16
-    P, bf16 output) gives rel-L2 2.6e-3 at 1x and 3.8e-3 at 4x, of which q~
-    alone is 3.6e-3, and max-abs 1.5e-2 at 4x, of which the output's own
-    rounding is 7.7e-3.  So for stress cases max-abs scales with the
-    multiplier and rel-L2 with its square root."""
+def bf16_half_spacing(x):
+    """Half the bf16 spacing at magnitude |x|: the largest error of rounding
+    an exact value of that size to a bf16 output."""
+    a = float(np.max(np.abs(x))) if np.size(x) else 0.0
+    if a == 0.0:
+        return 0.0
+    return 2.0 ** (np.floor(np.log2(a)) - 8)
+
+
+def assert_attn_close(got, want, what=""):
+    """Attention outputs: rel-L2 <= 5e-3 and max-abs <= 2e-2 + half the bf16
+    spacing at the largest |out| of the case.
+
+    The output is bf16, so even the exact result rounded to an output is off
+    by up to half a spacing; the second term grants exactly that and leaves
+    the 2e-2 to the arithmetic.  At the workloads' 1/sqrt(D) logit scale
+    |out| stays below 0.5 and the term is at most 1e-3.  With 4x sharper
+    logits a few rows dominate, |out| reaches 4-5 (spacing 2^-5), and the
+    term is 1.6e-2: measured max-abs 1.5e-2 on 2 queries and 2.0e-2 on 256
+    queries (an element whose exact value lies within the kernel's ~1e-3
+    relative logit-path error of a rounding midpoint lands on the far
+    neighbour), against a float64 model of the kernel's roundings (two-term
+    E4M3 q~, bf16 rotary q~, two-term E4M3 probabilities, fp32 partials,
+    bf16 output) that gives 1.3-1.5e-2 per query."""
     max_abs, rel_l2 = err_stats(got, want)
-    m = max(1.0, logit_mult)
-    bar_abs, bar_rel = MAX_ABS * m, REL_L2 * m ** 0.5
-    assert max_abs <= bar_abs and rel_l2 <= bar_rel, \
-        f"{what}: max_abs {max_abs:.3e} (<= {bar_abs}), rel_l2 {rel_l2:.3e} (<= {bar_rel})"
+    bar_abs = MAX_ABS + bf16_half_spacing(want)
+    assert max_abs <= bar_abs and rel_l2 <= REL_L2, \
+        f"{what}: max_abs {max_abs:.3e} (<= {bar_abs:.3e}), rel_l2 {rel_l2:.3e} (<= {REL_L2})"
     return max_abs, rel_l2
 
 
