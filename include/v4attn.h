@@ -54,6 +54,11 @@ extern "C" {
 #define V4ATTN_EWORKSPACE   (-3) /* workspace missing or too small          */
 #define V4ATTN_EHIP         (-4) /* HIP runtime error (no device, launch)   */
 
+/* Bytes of the fixed device scratch v4attn_hca_attend_noalloc uses on each
+ * GPU (40 MiB: the split partials of 32 decode queries x 64 heads x 512 dims
+ * over 8 splits take 33.7 MB). */
+#define V4ATTN_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+
 /* v4attn_compress modes. */
 #define V4ATTN_POOL 0 /* pool 2m-token windows into compressed entries     */
 #define V4ATTN_PACK 1 /* one window row per raw token (no pooling)          */
@@ -375,6 +380,30 @@ int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries,
                       int64_t q_pos0, const int64_t* seq_pos, float scale, float eps, float rope_base,
                       uint16_t* out, float* lse,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * v4attn_hca_attend_noalloc -- v4attn_hca_attend without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments, results and errors as v4attn_hca_attend (the outputs are
+ * identical to its); the split partials go to a fixed scratch array the
+ * library holds on each GPU (V4ATTN_NOALLOC_SCRATCH_BYTES, kept until the
+ * process ends) instead of a caller's workspace.  The call allocates and
+ * frees nothing.  A call whose partials need more than the scratch holds
+ * returns V4ATTN_EWORKSPACE and launches nothing.  Every call on one GPU
+ * shares that GPU's scratch, which keeps the last call's contents (nothing
+ * in it needs to start at zero): calls that overlap on one GPU (e.g. on two
+ * streams) race and must be serialised by the caller.  The first call on a
+ * device looks up that device's copy of the scratch (hipGetSymbolAddress).
+ */
+int v4attn_hca_attend_noalloc(const uint16_t* q, const uint8_t* entries,
+                              const uint8_t* win, const float* gamma_q,
+                              const float* sink, int B, int Tq, int H, int D,
+                              int R, int64_t Ncap, int64_t n_entries, int m,
+                              int W, int64_t q_pos0, const int64_t* seq_pos,
+                              float scale, float eps, float rope_base,
+                              uint16_t* out, float* lse, void* stream);
 
 /*
  * v4attn_nsa_attend -- the NSA-style compress-select-window variant: a

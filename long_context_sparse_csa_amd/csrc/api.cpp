@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/v4attn.h"
@@ -677,6 +678,84 @@ int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries, const int32_t* 
   return hip_status(v4::launch_attend(a, (hipStream_t)stream), "CSA attend launch");
 }
 
+}  // extern "C"
+
+// The fixed device scratch of v4attn_hca_attend_noalloc: the split partials
+// go here instead of into a caller's workspace.  Each GPU the library runs
+// on holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, so the device address of each GPU's copy is
+// looked up once (with that GPU current) and only that address is used.
+static __device__ __align__(256) uint8_t scratch[V4ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Validates an HCA attention call and fills its kernel arguments (all but
+// the workspace views); *need = the split partials' bytes.
+int hca_attend_args(const uint16_t* q, const uint8_t* entries, const uint8_t* win,
+                    const float* gamma_q, const float* sink, int B, int Tq, int H, int D, int R,
+                    int64_t Ncap, int64_t n_entries, int m, int W, int64_t q_pos0,
+                    const int64_t* seq_pos, float scale, float eps, float rope_base,
+                    uint16_t* out, float* lse, v4::AttendArgs* ap, size_t* need) {
+  if (int st = check_attend_common(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, W,
+                                   q_pos0, scale, eps, rope_base, out))
+    return st;
+  v4::SeqPos sp;
+  bool ragged;
+  if (int st = load_seq_pos(seq_pos, B, q_pos0, &sp, &ragged)) return st;
+  if (n_entries < 0 || n_entries > Ncap) return fail(V4ATTN_EINVAL, "need 0 <= n_entries <= Ncap");
+  if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
+  const int64_t rows_max = vmax_of(Tq, n_entries, q_pos0, m) + W;
+  int splits = 1;
+  *need = attend_ws(B, Tq, H, D, rows_max, false, &splits);
+  v4::AttendArgs& a = *ap;
+  a.q = q; a.entries = entries; a.topk = nullptr; a.win = win; a.gamma_q = gamma_q; a.sink = sink;
+  a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R; a.Ncap = Ncap; a.k = 0; a.n_entries = n_entries;
+  a.m = m; a.W = W; a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps; a.rope_base = rope_base;
+  a.rope = v4::rope_turns(rope_base, R);
+  a.out = out; a.lse = lse; a.splits = splits;
+  a.rows_max = rows_max;
+  a.ragged = ragged;
+  if (ragged) a.pos = sp;
+  return V4ATTN_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of the scratch on the stream's device.
+int scratch_of_stream_device(hipStream_t stream, void** out) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(V4ATTN_EUNSUPPORTED, "device %d: devices 0..%d are supported", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) return hip_status(e2, "hipSetDevice");
+    }
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(V4ATTN_EHIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return V4ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t v4attn_hca_attend_workspace(int B, int Tq, int H, int D, int64_t n_entries, int m,
                                    int64_t q_pos0, int W) {
   if (B < 0 || Tq < 0 || H < 1 || D < 1 || n_entries < 0 || m < 1 || q_pos0 < 0 || W < 0) return 0;
@@ -688,30 +767,37 @@ int v4attn_hca_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
                       int64_t Ncap, int64_t n_entries, int m, int W, int64_t q_pos0,
                       const int64_t* seq_pos, float scale, float eps, float rope_base,
                       uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  if (int st = check_attend_common(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, W,
-                                   q_pos0, scale, eps, rope_base, out))
+  v4::AttendArgs a{};
+  size_t need = 0;
+  if (int st = hca_attend_args(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, n_entries, m,
+                               W, q_pos0, seq_pos, scale, eps, rope_base, out, lse, &a, &need))
     return st;
-  v4::SeqPos sp;
-  bool ragged;
-  if (int st = load_seq_pos(seq_pos, B, q_pos0, &sp, &ragged)) return st;
-  if (n_entries < 0 || n_entries > Ncap) return fail(V4ATTN_EINVAL, "need 0 <= n_entries <= Ncap");
-  if (m < 1 || m > 256) return fail(V4ATTN_EUNSUPPORTED, "m = %d: 1 <= m <= 256 is built", m);
-  const int64_t rows_max = vmax_of(Tq, n_entries, q_pos0, m) + W;
-  int splits = 1;
-  const size_t need = attend_ws(B, Tq, H, D, rows_max, false, &splits);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
-  v4::AttendArgs a{};
-  a.q = q; a.entries = entries; a.topk = nullptr; a.win = win; a.gamma_q = gamma_q; a.sink = sink;
-  a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.R = R; a.Ncap = Ncap; a.k = 0; a.n_entries = n_entries;
-  a.m = m; a.W = W; a.q_pos0 = q_pos0; a.scale = scale; a.eps = eps; a.rope_base = rope_base;
-  a.rope = v4::rope_turns(rope_base, R);
-  a.out = out; a.lse = lse; a.splits = splits;
   attend_ws_layout(a, ws);
-  a.rows_max = rows_max;
-  a.ragged = ragged;
-  if (ragged) a.pos = sp;
+  return hip_status(v4::launch_attend(a, (hipStream_t)stream), "HCA attend launch");
+}
+
+int v4attn_hca_attend_noalloc(const uint16_t* q, const uint8_t* entries, const uint8_t* win,
+                              const float* gamma_q, const float* sink, int B, int Tq, int H, int D,
+                              int R, int64_t Ncap, int64_t n_entries, int m, int W, int64_t q_pos0,
+                              const int64_t* seq_pos, float scale, float eps, float rope_base,
+                              uint16_t* out, float* lse, void* stream) {
+  v4::AttendArgs a{};
+  size_t need = 0;
+  if (int st = hca_attend_args(q, entries, win, gamma_q, sink, B, Tq, H, D, R, Ncap, n_entries, m,
+                               W, q_pos0, seq_pos, scale, eps, rope_base, out, lse, &a, &need))
+    return st;
+  if (need > V4ATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(V4ATTN_EWORKSPACE,
+                "the split partials need %zu bytes; the fixed scratch holds %zu (use "
+                "v4attn_hca_attend with a workspace)",
+                need, (size_t)V4ATTN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0)
+    if (int st = scratch_of_stream_device((hipStream_t)stream, &ws)) return st;
+  attend_ws_layout(a, ws);
   return hip_status(v4::launch_attend(a, (hipStream_t)stream), "HCA attend launch");
 }
 

@@ -60,6 +60,8 @@ _SIGS = {
     "v4attn_hca_attend_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I]),
     "v4attn_hca_attend": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I, _L, _P,
                                _F, _F, _F, _P, _P, _P, _Z, _P]),
+    "v4attn_hca_attend_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I, _L,
+                                       _P, _F, _F, _F, _P, _P, _P]),
     "v4attn_csa_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _I, _I]),
     "v4attn_csa_attend_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _I, _I,
                                         _L, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -547,6 +549,32 @@ def hca_attend(q, entries, win, gamma_q, sink, *, n_entries, m, W, q_pos0=None, 
                                   Tq, H, D, R, entries.shape[1], int(n_entries), int(m), int(W),
                                   int(q_pos0), sp, float(scale), float(eps), float(rope_base),
                                   _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream(q)))
+    return out, lse
+
+
+def hca_attend_noalloc(q, entries, win, gamma_q, sink, *, n_entries, m, W, q_pos0=None,
+                       seq_pos=None, scale=None, eps=1e-6, rope_base=10000.0, R=64, out=None,
+                       lse=None, want_lse=False):
+    """hca_attend with the split partials in the library's fixed device
+    scratch (no workspace; out and lse must be given to allocate nothing)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(entries, "entries", torch.uint8, 3)
+    _need(win, "win", torch.uint8, 3)
+    _need(gamma_q, "gamma_q", torch.float32, 1)
+    _need(sink, "sink", torch.float32, 1)
+    B, Tq, H, D = q.shape
+    if entries.shape[0] != B or entries.shape[2] != D + R \
+            or tuple(win.shape) != (B, Tq + W - 1, D + R) or gamma_q.numel() != D \
+            or sink.numel() != H:
+        raise ValueError("shape mismatch")
+    scale = D ** -0.5 if scale is None else scale
+    out, lse = _attend_io(q, out, lse, want_lse)
+    arr, sp, q_pos0 = _seq_pos(seq_pos, B, q_pos0)
+    check(lib().v4attn_hca_attend_noalloc(_ptr(q), _ptr(entries), _ptr(win), _ptr(gamma_q),
+                                          _ptr(sink), B, Tq, H, D, R, entries.shape[1],
+                                          int(n_entries), int(m), int(W), int(q_pos0), sp,
+                                          float(scale), float(eps), float(rope_base), _ptr(out),
+                                          _ptr(lse), _stream(q)))
     return out, lse
 
 

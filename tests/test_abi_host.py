@@ -32,7 +32,7 @@ MISALIGNED = ctypes.c_void_p(0x100008)
 def test_exports_every_header_function():
     names = ops().header_functions()
     assert "v4attn_compress" in names and "v4attn_hca_attend" in names
-    assert len(names) == 28
+    assert len(names) == 29
     for n in names:
         assert hasattr(L(), n), n
     assert L().v4attn_version() == 1
@@ -250,6 +250,21 @@ def test_hca_attend_rejects():
     # 32 sequences at 1M need split partials: workspace too small
     args[5], args[10], args[11], args[14] = 32, 8192, 8192, (1 << 20) - 1
     assert f(*args) == -3
+
+
+def test_hca_attend_noalloc_rejects_before_any_device_call():
+    f = L().v4attn_hca_attend_noalloc
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 512, 64, 10, 11, 128, 128, 5000, None, 0.04,
+            1e-6, 1e4, FAKE, None, None]
+    assert f(*args) == -1          # n_entries > Ncap
+    args[11] = 10
+    args[12] = 0
+    assert f(*args) == -2          # m = 0
+    args[12] = 128
+    # 255 queries over 328 rows: two splits of fp32 partials, 67 MB > the 40 MiB scratch
+    args[5], args[10], args[11], args[14] = 255, 200, 200, 200 * 128 + 5
+    assert f(*args) == -3
+    assert b"scratch" in L().v4attn_last_error()
 
 
 def _nsa(**kw):
