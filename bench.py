@@ -1,22 +1,28 @@
 #!/usr/bin/env python3
-"""Decode throughput at a 1M-token context on one MI355X.
+"""Decode throughput per layer at a 1M-token context on one MI355X.
 
 One step is one decode token per sequence through
   * a CSA layer (compression m = 4, top-k 1024, window 128), 8 sequences of
-    2^20 tokens: pack the new token's window row and pool the entry it completes
-    and that entry's indexer key (a compress step, in one launch with the HCA
-    layer's),
-    indexer scores over all 262,144 entries, top-k, sparse attention;
-  * an HCA layer (compression m' = 128, window 128), 32 sequences of 2^20
-    tokens: the compress step, dense attention over all 8,192 entries.
-All inputs are seeded synthetic N(0,1) data resident in HBM before timing.
-The HCA caches rotate over several copies so successive steps do not hit the
-256 MB Infinity Cache (each model layer has its own cache).
+    2^20 tokens: the compress step (the new token's window row, the entry it
+    completes and that entry's pooled indexer key), indexer scores over all
+    262,144 entries, top-k, sparse attention;
+  * then an HCA layer (compression m' = 128, window 128), 32 sequences of
+    2^20 tokens: the compress step, dense attention over all 8,192 entries;
+the calls in that order on one stream, as layers of a stack run.  All inputs
+are seeded synthetic N(0,1) data resident in HBM before timing.  The HCA
+caches rotate over several copies so successive steps do not hit the 256 MB
+Infinity Cache (each model layer has its own cache).
 
-Prints ONE JSON line: value = query-token-layers per second (8 CSA + 32 HCA
-query tokens per step / step time), per-layer rates, the per-kernel timing
-breakdown from HIP events, the roofline of the dominant kernel, and the
-float64 oracle timed on the host cores on a bounded sample.
+Prints ONE JSON line: value = query-token-layers per second ((8 + 32) query
+tokens / (CSA layer time + HCA layer time)); per_layer = each layer's query
+tokens/s, algorithmic bytes and fraction of the HBM roofline; the per-kernel
+timing breakdown from HIP events; the roofline of the dominant kernel; the
+same calls with the two independent batches overlapped on two streams (and
+as a HIP graph replay), labelled as such; the CSA layer at a 128K context
+(16 sequences); 8 sequences through an alternating CSA/HCA layer stack; and
+the float64 oracle timed on the host cores on bounded samples (decode with
+the thread pool and with one thread, the prefill chunk extrapolated from a
+stratified sample).
 
 A "prefill" section times the 4096-token chunk appended to a 2^20-token
 context (both layers) and reports MFMA fractions for scoring and attention.
@@ -24,14 +30,14 @@ context (both layers) and reports MFMA fractions for scoring and attention.
 prefill indexer with the FP8 (E4M3, one scale per row) and MXFP4 lightning
 indexers; the headline value keeps the bf16 indexer keys of the workload
 definition.  An "nsa_variant" section times the NSA-style compress-select-
-window layer at the same 1M-token decode shape.  A "ragged_decode" section runs the same step with each
-sequence at its own position (128K to 1M).  A "backward" section times
-the CSA layer's training step on the prefill chunk (attention, indexer KL
-and compressor backward).
+window layer at the same 1M-token decode shape.  A "ragged_decode" section
+runs the same step with each sequence at its own position (128K to 1M).  A
+"backward" section times the CSA layer's training step on the prefill chunk
+(attention, indexer KL and compressor backward).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
-                    [--no-fp8] [--no-nsa] [--nsa-only] [--no-ragged]
-                    [--no-backward] [--backward-only] [--prefill-only] [--graph] [--counters]
+                    [--no-fp8] [--no-nsa] [--nsa-only] [--no-ragged] [--no-extra-decode]
+                    [--no-backward] [--backward-only] [--prefill-only] [--counters]
 """
 
 import argparse
@@ -72,9 +78,16 @@ def build_inputs(dev, rotate):
     return decode.build_inputs(CSA_1M, HCA_1M, dev, rotate)
 
 
-def make_step(inp, dev, csa_pos=None, hca_pos=None):
-    """(name, fn) launches of one eager step (HCA cache copies rotate), and
-    the DecodeStep behind them (optionally a ragged batch)."""
+# The calls of one layer, in dependency order: a layer's compress step
+# writes the rows its indexer and attention read.
+CSA_LAYER = ("csa_compress", "index_score", "topk_select", "csa_attend")
+HCA_LAYER = ("hca_compress", "hca_attend")
+
+
+def make_step(inp, dev, csa_pos=None, hca_pos=None, names=CSA_LAYER + HCA_LAYER):
+    """(name, fn) launches of one eager step -- the CSA layer's calls, then
+    the HCA layer's, one stream (HCA cache copies rotate) -- and the
+    DecodeStep behind them (optionally a ragged batch)."""
     from long_context_sparse_csa_amd import decode
     from long_context_sparse_csa_amd.configs import CSA_1M, HCA_1M
     st = decode.DecodeStep(inp, CSA_1M, HCA_1M, dev, csa_pos=csa_pos, hca_pos=hca_pos)
@@ -87,7 +100,7 @@ def make_step(inp, dev, csa_pos=None, hca_pos=None):
             if name == "hca_attend":
                 state["i"] += 1
         return fn
-    return [(n, mk(n)) for n in decode.DecodeStep.NAMES], st
+    return [(n, mk(n)) for n in names], st
 
 
 def algorithmic_bytes():
@@ -512,46 +525,149 @@ def ragged_section(dev, inp, reps):
     """The decode step with a ragged batch: the same caches and calls, each
     sequence's new token at its own position -- CSA sequence b at
     (b + 1) 2^17 - 1, HCA sequence b at (b + 1) 2^15 - 1 (lengths 128K to 1M,
-    mean 0.56M) -- timed like the headline (HCA attention on a second stream).
-    The indexer reads only each sequence's visible keys, so its algorithmic
-    bytes are sum_b V_b (256 + ...) per step."""
+    mean 0.56M) -- timed like the headline (one stream, CSA layer then HCA
+    layer) and with the two batches overlapped on two streams.  The indexer
+    reads only each sequence's visible keys, so its algorithmic bytes are
+    sum_b V_b (256 + ...) per step."""
     from long_context_sparse_csa_amd.configs import CSA_1M as c, HCA_1M as h
     csa_pos = [(b + 1) * (1 << 17) - 1 for b in range(c.B)]
     hca_pos = [(b + 1) * (1 << 15) - 1 for b in range(h.B)]
     launches, st = make_step(inp, dev, csa_pos=csa_pos, hca_pos=hca_pos)
-    # The first block timed after the ragged step is set up runs host-bound
-    # and 3-5x slower, whichever schedule goes first (cause not found); the
-    # step is timed as three blocks a schedule, the steady-state figure is the
-    # fastest block and the first block is reported beside it.
     rot = len(inp["hca"]["entries"])
-    blocks = [run_timed_concurrent(st, rot, reps, 5)[0] for _ in range(3)]
-    ms, ms_seq = min(blocks), min(run_timed(launches, reps, 5)[0] for _ in range(3))
+    blocks = [run_timed(launches, reps, 5)[0] for _ in range(3)]
+    blocks2 = [run_timed_concurrent(st, rot, reps, 5)[0] for _ in range(3)]
     br = run_breakdown(launches, 20)
     vis = sum(min(c.T // c.m, (p + 1) // c.m) for p in csa_pos)
     idx_bytes = vis * c.dI * 2 + c.B * (c.HI * c.dI * 2 + c.HI * 4 + 0)
-    # the one launch of both layers' compress steps counts half to each layer
-    t_csa = br["compress"] / 2 + sum(br[k] for k in ("index_score", "topk_select", "csa_attend"))
-    t_hca = br["compress"] / 2 + br["hca_attend"]
+    t_csa = sum(br[k] for k in CSA_LAYER)
+    t_hca = sum(br[k] for k in HCA_LAYER)
+    ms = sum(blocks) / 3
     return {
         "workload": "decode_ragged: CSA B=8 at positions (b+1) 2^17 - 1, HCA B=32 at "
                     "(b+1) 2^15 - 1 (the decode_1m_csa_hca caches)",
         "step_us": round(ms * 1e3, 2),
-        "one_stream_step_us": round(ms_seq * 1e3, 2),
-        "first_block_step_us": round(blocks[0] * 1e3, 2),
+        "step_us_blocks": [round(x * 1e3, 2) for x in blocks],
         "query_token_layers_per_s": round((c.B + h.B) / (ms * 1e-3), 1),
+        "two_stream_overlap_step_us_blocks": [round(x * 1e3, 2) for x in blocks2],
         "csa_layer_us": round(t_csa, 2), "hca_layer_us": round(t_hca, 2),
+        "csa_query_tokens_per_s": round(c.B / (t_csa * 1e-6), 1),
+        "hca_query_tokens_per_s": round(h.B / (t_hca * 1e-6), 1),
         "kernels_us": {k: round(v, 2) for k, v in br.items()},
         "index_score_GBps": round(idx_bytes / (br["index_score"] * 1e-6) / 1e9, 1),
         "index_score_hbm_frac": round(idx_bytes / (br["index_score"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
     }
 
 
-def cpu_baseline(inp, budget_s):
-    """The float64 oracle on a bounded sample of the same inputs: whole CSA
-    and HCA layers for single sequences, alternating, until the budget."""
+def csa_128k_section(dev, steps, rotate=4):
+    """The CSA layer at a 128K context (16 sequences, 32,768 entries each):
+    compress step with the pooled indexer key, indexer over every entry,
+    top-1024, sparse attention; one stream.  One step's bytes (~147 MB) fit
+    the 256 MB Infinity Cache, so the entry and indexer-key caches rotate
+    over `rotate` copies."""
+    import torch
+    from long_context_sparse_csa_amd import ops, synth
+    from long_context_sparse_csa_amd.configs import CSA_128K as c
+    B, N, t, m = c.B, c.T // c.m, c.T - 1, c.m
+    ents = [synth.packed_rows((B, N), c.D, c.R, c.seed + 100 * i, "entries", dev) for i in range(rotate)]
+    kids = [synth.normal((B, N, c.dI), c.seed + 100 * i, "kI", dev, dtype=torch.bfloat16)
+            for i in range(rotate)]
+    qI = synth.normal((B, 1, c.HI, c.dI), c.seed, "qI", dev, dtype=torch.bfloat16)
+    wI = synth.normal((B, 1, c.HI), c.seed, "w", dev)
+    q = synth.normal((B, 1, c.H, c.D), c.seed, "q", dev, dtype=torch.bfloat16)
+    win = synth.packed_rows((B, c.W), c.D, c.R, c.seed, "win", dev)
+    raw = synth.normal((B, 2 * m, c.D), c.seed, "raw", dev, dtype=torch.bfloat16)
+    raw_idx = synth.normal((B, 2 * m, c.dI), c.seed, "rawI", dev, dtype=torch.bfloat16)
+    score = synth.normal((B, 2 * m), c.seed, "score", dev)
+    bias = synth.normal((2 * m,), c.seed, "bias", dev, std=0.1)
+    sink = synth.normal((c.H,), c.seed, "sink", dev)
+    gamma = torch.ones(c.D, device=dev)
+    scores = torch.empty((B, ops.score_stride(1, N, t, m)), dtype=torch.float32, device=dev)
+    topk = torch.empty((B, 1, c.k), dtype=torch.int32, device=dev)
+    tk_ws = torch.empty(max(ops.topk_select_workspace_bytes(B, 1, N, t, m, c.k), 16),
+                        dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    a_ws = torch.empty(max(ops.csa_attend_workspace_bytes(B, 1, c.H, c.D, c.k, c.W), 16),
+                       dtype=torch.uint8, device=dev)
+    state = {"i": 0}
+
+    def copy():
+        return state["i"] % rotate
+    calls = [
+        ("csa_compress", lambda: ops.compress_step(raw, score, bias, gamma, ents[copy()], win,
+                                                   raw_pos0=t + 1 - 2 * m, m=m, t=t,
+                                                   win_row=c.W - 1, raw_idx=raw_idx,
+                                                   k_idx=kids[copy()])),
+        ("index_score", lambda: ops.index_score(qI, wI, kids[copy()], n_entries=N, q_pos0=t, m=m,
+                                                scores=scores)),
+        ("topk_select", lambda: ops.topk_select(scores, B=B, Tq=1, n_entries=N, q_pos0=t, m=m,
+                                                k=c.k, topk=topk, workspace=tk_ws)),
+        ("csa_attend", lambda: ops.csa_attend(q, ents[copy()], topk, win, gamma, sink, q_pos0=t,
+                                              W=c.W, out=out, workspace=a_ws)),
+    ]
+
+    def bump():
+        state["i"] += 1
+    launches = calls + [("next_copy", bump)]
+    ms, _ = run_timed(launches, steps, 5)
+    br = run_breakdown(launches, 20)
+    br.pop("next_copy")
+    row = c.D + c.R
+    per_q = (N * c.dI * 2 + c.HI * c.dI * 2 + c.HI * 4 + (c.k + c.W) * row + c.H * c.D * 2 * 2 +
+             c.k * 4)
+    gbs = B * per_q / (ms * 1e-3) / 1e9
+    return {
+        "workload": f"csa_decode_128k: B={B} T=2^17 m={m} N={N} H={c.H} D={c.D} HI={c.HI} "
+                    f"dI={c.dI} k={c.k} W={c.W}; entry and indexer-key caches rotate over "
+                    f"{rotate} copies",
+        "layer_us": round(ms * 1e3, 2),
+        "query_tokens_per_s": round(B / (ms * 1e-3), 1),
+        "algorithmic_bytes_per_query": per_q,
+        "GBps": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline_query_tokens_per_s": round(HBM_PEAK_GBS * 1e9 / per_q, 1),
+        "kernels_us": {k: round(v, 2) for k, v in br.items()},
+    }
+
+
+def stack_section(dev, steps, pairs=2):
+    """8 sequences at a 2^20-token context through an alternating stack of
+    CSA and HCA layers (2 x `pairs` layers, each with its own caches), one
+    decode token: every layer's calls in order on one stream, as a dependent
+    stack would run them (a layer's compress step needs that layer's input)."""
+    import torch
+    from long_context_sparse_csa_amd import decode
+    from long_context_sparse_csa_amd.configs import CSA_1M, HCA_1M
+    launches = []
+    for i in range(pairs):
+        c = CSA_1M.with_(seed=CSA_1M.seed + 1000 * (i + 1))
+        h = HCA_1M.with_(B=CSA_1M.B, seed=HCA_1M.seed + 1000 * (i + 1))
+        st = decode.DecodeStep(decode.build_inputs(c, h, dev), c, h, dev)
+        f = st.calls(0)
+        launches += [(f"L{2 * i}_{n}", f[n]) for n in CSA_LAYER]
+        launches += [(f"L{2 * i + 1}_{n}", f[n]) for n in HCA_LAYER]
+    torch.cuda.synchronize()
+    ms, _ = run_timed(launches, steps, 5)
+    br = run_breakdown(launches, 20)
+    B, L = CSA_1M.B, 2 * pairs
+    t_csa = sum(v for k, v in br.items() if k.split("_", 1)[1] in CSA_LAYER) / pairs
+    t_hca = sum(v for k, v in br.items() if k.split("_", 1)[1] in HCA_LAYER) / pairs
+    return {
+        "workload": f"decode_stack_1m: B={B} sequences at T=2^20 through {L} alternating layers "
+                    f"(CSA m=4 k=1024, HCA m'=128; W=128, H=64, D=512), each with its own caches",
+        "stack_us": round(ms * 1e3, 2),
+        "query_token_layers_per_s": round(B * L / (ms * 1e-3), 1),
+        "csa_layer_us": round(t_csa, 2),
+        "hca_layer_us": round(t_hca, 2),
+    }
+
+
+
+def _oracle_decode_queries(inp, budget_s, max_pairs):
+    """Whole CSA-layer and HCA-layer queries of the decode workloads through
+    the float64 oracle, alternating, until the budget: (seconds per CSA
+    query, seconds per HCA query, counts)."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
     from long_context_sparse_csa_amd.configs import CSA_1M as c, HCA_1M as h
     from oracle import attend as oa, codecs, compress as oc, indexer as oi
 
@@ -562,7 +678,7 @@ def cpu_baseline(inp, budget_s):
     t_csa, t_hca, n_csa, n_hca = 0.0, 0.0, 0, 0
     t0 = time.perf_counter()
     s = 0
-    while time.perf_counter() - t0 < budget_s and s < 64:
+    while s < max_pairs and (s == 0 or time.perf_counter() - t0 < budget_s):
         bb = s % c.B
         # host copies of the sequence's bytes (not timed: the oracle's input)
         kI = a["k_idx"][bb].cpu()
@@ -582,9 +698,8 @@ def cpu_baseline(inp, budget_s):
                        c.scale, c.eps, c.R, c.rope_base)
         t_csa += time.perf_counter() - x0
         n_csa += 1
-        # HCA sequence
         hb = s % h.B
-        ent = inp["hca"]["entries"][0][hb].cpu().numpy()
+        ent = b["entries"][0][hb].cpu().numpy()
         win = b["win"][hb].cpu().numpy()
         q = b["q"][hb]
         x0 = time.perf_counter()
@@ -594,21 +709,100 @@ def cpu_baseline(inp, budget_s):
         t_hca += time.perf_counter() - x0
         n_hca += 1
         s += 1
-    per_csa, per_hca = t_csa / n_csa, t_hca / n_hca
+    return t_csa / n_csa, t_hca / n_hca, n_csa, n_hca
+
+
+def _oracle_prefill_queries(dev, n_sample, budget_s):
+    """Float64 oracle on a stratified sample of the prefill chunk's 4096
+    queries (evenly spaced, first and last included): per query, the CSA
+    layer (indexer over every visible entry, top-1024, attention over the
+    selection and the causal window) and the HCA layer (attention over every
+    visible entry and the window).  Seconds per query, extrapolated to the
+    chunk by the caller."""
+    import numpy as np
+    import torch
+    from long_context_sparse_csa_amd import synth
+    from long_context_sparse_csa_amd.configs import PREFILL_1M as p
+    from oracle import attend as oa, codecs, indexer as oi
+    P, Tq, H, D, R, W, k, m, mh = p.T, p.Tq, p.H, p.D, p.R, p.W, p.k, p.m, p.extra["m_hca"]
+    Nc, Nh = P // m + Tq // m, P // mh + Tq // mh
+
+    def f64(t):
+        return codecs.bf16_decode(t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+    kI = f64(synth.normal((1, Nc, p.dI), p.seed, "kI", dev, dtype=torch.bfloat16)[0])
+    ent_c = synth.packed_rows((1, Nc), D, R, p.seed, "entries", dev, chunk_rows=1 << 18)[0] \
+        .cpu().numpy()
+    ent_h = codecs.unpack_rows(synth.packed_rows((1, Nh), D, R, p.seed, "entries_h", dev)[0]
+                               .cpu().numpy(), D, R)
+    win = codecs.unpack_rows(synth.packed_rows((1, Tq + W - 1), D, R, p.seed, "win", dev)[0]
+                             .cpu().numpy(), D, R)
+    qI = synth.normal((1, Tq, p.HI, p.dI), p.seed, "qI", dev, dtype=torch.bfloat16)[0]
+    wI = synth.normal((1, Tq, p.HI), p.seed, "w", dev)[0]
+    q = synth.normal((1, Tq, H, D), p.seed, "q", dev, dtype=torch.bfloat16)[0]
+    sink = synth.normal((H,), p.seed, "sink", dev).cpu().double().numpy()
+    gq = np.ones(D)
+    t_csa = t_hca = 0.0
+    n = 0
+    t0 = time.perf_counter()
+    for r in np.linspace(0, Tq - 1, n_sample).round().astype(int):
+        if n and time.perf_counter() - t0 > budget_s:
+            break
+        t = P + int(r)
+        qn, qIn, wn = f64(q[r]), f64(qI[r]), wI[r].cpu().double().numpy()
+        x0 = time.perf_counter()
+        V = oi.visible_entries(t, Nc, m)
+        sel = oi.topk_select(oi.index_scores(qIn, wn, kI, V), k)
+        rows = codecs.unpack_rows(ent_c[sel[sel >= 0]], D, R)
+        oa.attend_rows(qn, gq, t, np.concatenate([rows, oa.window_rows(win, t, P, W)]), sink,
+                       p.scale, p.eps, R, p.rope_base)
+        t_csa += time.perf_counter() - x0
+        x0 = time.perf_counter()
+        Vh = min(Nh, (t + 1) // mh)
+        oa.attend_rows(qn, gq, t, np.concatenate([ent_h[:Vh], oa.window_rows(win, t, P, W)]), sink,
+                       p.scale, p.eps, R, p.rope_base)
+        t_hca += time.perf_counter() - x0
+        n += 1
+    return t_csa / n, t_hca / n, n
+
+
+def cpu_baseline(inp, dev, budget_s, prefill):
+    """The float64 oracle (never tuned) on bounded samples of the same
+    workloads: decode queries with the BLAS thread pool as it is and with
+    one thread, and a stratified sample of the prefill chunk's queries
+    extrapolated to the chunk."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from long_context_sparse_csa_amd.configs import CSA_1M as c, HCA_1M as h, PREFILL_1M as p
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    per_csa, per_hca, n_csa, n_hca = _oracle_decode_queries(inp, budget_s * 0.5, 64)
     step = c.B * per_csa + h.B * per_hca
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {
+    with threadpool_limits(limits=1):
+        one_csa, one_hca, n1c, n1h = _oracle_decode_queries(inp, budget_s * 0.2, 2)
+    res = {
         "value": (c.B + h.B) / step,
-        "unit": "query-tokens/s",
+        "unit": "query-token-layers/s",
         "cores": threads,
         "kind": "oracle",
         "sample": (f"{n_csa} CSA-layer queries (compress of one entry, float64 indexer over "
                    f"262,144 entries, top-1024, attention over 1152 rows) and {n_hca} HCA-layer "
-                   f"queries (attention over 8320 rows) at 1M context, extrapolated to the "
-                   f"8 + 32-query step"),
-        "csa_query_s": per_csa,
-        "hca_query_s": per_hca,
+                   f"queries (attention over 8320 rows) at 1M context, extrapolated to one CSA "
+                   f"layer of 8 sequences followed by one HCA layer of 32"),
+        "csa_query_tokens_per_s": 1.0 / per_csa,
+        "hca_query_tokens_per_s": 1.0 / per_hca,
+        "one_thread": {"value": (c.B + h.B) / (c.B * one_csa + h.B * one_hca), "cores": 1,
+                       "csa_query_tokens_per_s": 1.0 / one_csa,
+                       "hca_query_tokens_per_s": 1.0 / one_hca,
+                       "sample": f"{n1c} CSA-layer and {n1h} HCA-layer queries, one BLAS thread"},
     }
+    if prefill:
+        pc, ph, npf = _oracle_prefill_queries(dev, 16, budget_s * 0.4)
+        res["prefill_extrapolated"] = {
+            "csa_layer_tokens_per_s": 1.0 / pc, "hca_layer_tokens_per_s": 1.0 / ph,
+            "chunk_s_extrapolated": {"csa": pc * p.Tq, "hca": ph * p.Tq},
+            "cores": threads,
+            "sample": f"{npf} of the 4096 prefill queries (evenly spaced, first and last "
+                      f"included), timed one by one and extrapolated linearly to the chunk",
+        }
+    return res
 
 
 def main():
@@ -618,12 +812,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sequential", action="store_true",
-                    help="time the calls launched one by one on one stream (the default runs "
-                         "the HCA attention on a second stream beside the CSA chain)")
-    ap.add_argument("--graph", action="store_true",
-                    help="time HIP-graph replays of the concurrent schedule")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-extra-decode", action="store_true",
+                    help="skip the 128K CSA layer and the alternating layer stack")
+    ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill chunk (prints its section as the JSON line)")
     ap.add_argument("--no-fp8", action="store_true",
@@ -682,25 +873,16 @@ def main():
         log("counters pass done")
         return
     log("timing")
-    if args.graph:
-        ms, wall = run_timed_graphs(st, args.rotate, args.steps, args.warmup)
-        sched = "HIP graph replay of the concurrent schedule (HCA attention on a second stream)"
-    elif args.sequential:
-        ms, wall = run_timed(launches, args.steps, args.warmup)
-        sched = "calls launched one by one on one stream"
-    else:
-        ms, wall = run_timed_concurrent(st, args.rotate, args.steps, args.warmup)
-        sched = ("one stream, the HCA attention on a second stream beside the CSA indexer, "
-                 "top-k and attention")
+    # headline: the CSA layer's calls, then the HCA layer's, on one stream
+    ms, wall = run_timed(launches, args.steps, args.warmup)
+    sched = ("one stream: the CSA layer (compress step, indexer, top-k, attention), then the "
+             "HCA layer (compress step, attention)")
     log(f"step {ms * 1e3:.1f} us ({sched})")
     br = run_breakdown(launches, max(10, min(args.steps, 50)))
     log("breakdown (us): " + ", ".join(f"{k} {v:.1f}" for k, v in br.items()))
     abytes, aflops = algorithmic_bytes()
-
-    # the one launch of both layers' compress steps counts half to each layer
-    t_csa_us = br["compress"] / 2 + sum(br[k] for k in ("index_score", "topk_select",
-                                                        "csa_attend"))
-    t_hca_us = br["compress"] / 2 + br["hca_attend"]
+    t_csa_us = sum(br[k] for k in CSA_LAYER)
+    t_hca_us = sum(br[k] for k in HCA_LAYER)
     kernels = {}
     for k, us in br.items():
         ent = {"us": round(us, 2)}
@@ -717,10 +899,21 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "algorithmic_bytes_per_launch": abytes[dom]}
 
+    def layer(nq, us, names):
+        by = sum(abytes.get(n, 0) for n in names)
+        gbs = by / (us * 1e-6) / 1e9
+        return {"query_tokens_per_s": round(nq / (us * 1e-6), 1), "layer_us": round(us, 2),
+                "algorithmic_bytes": by, "GBps": round(gbs, 1),
+                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "roofline_query_tokens_per_s": round(nq * HBM_PEAK_GBS * 1e9 / by, 1)}
     res = {
         "metric": METRIC,
         "value": round((c.B + h.B) / (ms * 1e-3), 1),
-        "unit": "query-tokens/s",
+        "unit": "query-token-layers/s",
+        "per_layer": {
+            "csa": layer(c.B, t_csa_us, CSA_LAYER),
+            "hca": layer(h.B, t_hca_us, HCA_LAYER),
+        },
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -738,19 +931,36 @@ def main():
             "hca": f"B={h.B} T=2^20 m={h.m} N={h.T // h.m} H={h.H} D={h.D} R={h.R} W={h.W}",
             "storage": "entries E4M3 (448 dims) + bf16 (64 rotary dims) = 576 B/row; "
                        "indexer keys bf16",
-            "value_is": "query-token-layers/s: (8 CSA + 32 HCA query tokens) per step",
+            "value_is": "query-token-layers/s: (8 CSA + 32 HCA query tokens) / (CSA layer time "
+                        "+ HCA layer time), the two layers one after the other",
             "hca_cache_copies": args.rotate,
-        },
-        "per_layer": {
-            "csa_query_tokens_per_s": round(c.B / (t_csa_us * 1e-6), 1),
-            "hca_query_tokens_per_s": round(h.B / (t_hca_us * 1e-6), 1),
-            "csa_layer_us": round(t_csa_us, 2),
-            "hca_layer_us": round(t_hca_us, 2),
         },
         "kernels": kernels,
         "roofline": roofline,
         "wall_s": round(wall, 3),
     }
+    log("per layer: " + json.dumps(res["per_layer"]))
+    # the same calls with the two layers' independent batches overlapped: both
+    # compress steps in one launch, the HCA attention on a second stream
+    # beside the CSA indexer, top-k and attention (not open to a dependent
+    # stack, where each layer waits for the previous one)
+    ms2, _ = run_timed_concurrent(st, args.rotate, args.steps, args.warmup)
+    msg, _ = run_timed_graphs(st, args.rotate, args.steps, args.warmup)
+    res["two_stream_overlap"] = {
+        "what": "independent CSA and HCA batches overlapped on two streams (both compress steps "
+                "in one launch, HCA attention beside the CSA chain)",
+        "step_us": round(ms2 * 1e3, 2),
+        "query_token_layers_per_s": round((c.B + h.B) / (ms2 * 1e-3), 1),
+        "hip_graph_replay_step_us": round(msg * 1e3, 2),
+    }
+    log("two-stream overlap: " + json.dumps(res["two_stream_overlap"]))
+    if not args.no_extra_decode:
+        log("csa decode 128k")
+        res["csa_decode_128k"] = csa_128k_section(dev, args.steps)
+        log("csa decode 128k: " + json.dumps(res["csa_decode_128k"]))
+        log("layer stack")
+        res["decode_stack"] = stack_section(dev, max(10, args.steps // 2))
+        log("layer stack: " + json.dumps(res["decode_stack"]))
     if not args.no_ragged:
         log("ragged decode")
         res["ragged_decode"] = ragged_section(dev, inp, args.steps)
@@ -776,7 +986,7 @@ def main():
         log("backward: " + json.dumps(res["backward"]))
     if not args.no_cpu_baseline:
         log("cpu baseline (float64 oracle)")
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(inp, dev, args.cpu_seconds, not args.no_prefill)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

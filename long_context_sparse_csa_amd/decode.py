@@ -59,6 +59,20 @@ def build_inputs(c, h, dev, rotate=1):
     return inp
 
 
+_SIDE = {}
+
+
+def side_stream(dev):
+    """One second stream per device (default priority), shared by every
+    DecodeStep: a new stream per step object would take a hardware queue of
+    its own the first time it is used."""
+    d = torch.device(dev)
+    key = d.index if d.index is not None else torch.cuda.current_device()
+    if key not in _SIDE:
+        _SIDE[key] = torch.cuda.Stream(device=d)
+    return _SIDE[key]
+
+
 class DecodeStep:
     """The library calls of one decode step over fixed buffers."""
 
@@ -91,7 +105,7 @@ class DecodeStep:
                                   dtype=torch.uint8, device=dev)
         a["raw_last"] = a["raw"][:, -1:].contiguous()   # the new token's raw latent
         b["raw_last"] = b["raw"][:, -1:].contiguous()
-        self.side = torch.cuda.Stream(device=dev)       # default priority
+        self.side = side_stream(dev)
         self._calls = {}
         self.ev = [torch.cuda.Event() for _ in range(4)]
 

@@ -151,6 +151,29 @@ def _need(t, name, dtype, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
+_ARRAY_TYPES = {}
+
+
+def _int64_array(n):
+    """The ctypes type int64[n], made once per n: a new array type per call
+    is a class object with reference cycles, and the garbage it leaves sets
+    off the interpreter's full garbage collections (tens of milliseconds
+    each, inside whatever loop is launching)."""
+    t = _ARRAY_TYPES.get(n)
+    if t is None:
+        t = _ARRAY_TYPES[n] = _c.c_int64 * n
+    return t
+
+
+def _desc_array(n):
+    """CompressStepDesc[n], made once per n (see _int64_array)."""
+    key = ("desc", n)
+    t = _ARRAY_TYPES.get(key)
+    if t is None:
+        t = _ARRAY_TYPES[key] = CompressStepDesc * n
+    return t
+
+
 def _seq_pos(seq_pos, B, q_pos0):
     """Per-sequence positions as a host int64 array (kept alive by the
     caller for the call) and the q_pos0 the library expects with it (their
@@ -162,7 +185,7 @@ def _seq_pos(seq_pos, B, q_pos0):
     sp = [int(x) for x in seq_pos]
     if len(sp) != B:
         raise ValueError(f"seq_pos has {len(sp)} positions for {B} sequences")
-    arr = (_c.c_int64 * max(B, 1))(*sp)
+    arr = _int64_array(max(B, 1))(*sp)
     return arr, _c.cast(arr, _c.c_void_p), max(sp) if sp else int(q_pos0 or 0)
 
 
@@ -254,7 +277,7 @@ def compress_step(raw, tok_score, pos_bias, gamma, entries, win, *, m, win_row, 
 def compress_steps(layers):
     """compress_step for several layers (each a dict of compress_step's
     arguments; same D) in one launch."""
-    descs = (CompressStepDesc * len(layers))()
+    descs = _desc_array(len(layers))()
     keep = []
     for z, kw in enumerate(layers):
         kw = dict(kw)
