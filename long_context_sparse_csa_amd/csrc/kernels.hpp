@@ -130,16 +130,18 @@ hipError_t launch_index_score_mxfp4(const IndexScoreMxfp4Args& a, hipStream_t st
 
 // Top-k selection: per-part leaders -> exact per-row select.
 constexpr int kTopkSel = 16384;     // keys the per-row selection holds in LDS
-constexpr int kTopkPartLen = 1024;  // scores per part (the longest; 256 or 512 for short rows)
+constexpr int kTopkPartLen = 1024;  // scores per part (the longest; 128 to 512 for short rows)
+constexpr int kTopkPartMin = 128;   // the shortest part
 constexpr int kTopkPartCap = 32;    // leaders a part stores
 constexpr int kTopkMaxParts = 4096; // parts per row (entries <= 4M)
 
 // Scores per part of a row of V entries: short enough that a part holds
-// about k/8 or fewer of the row's top k on average (its leaders then
-// rarely overflow); 256, 512 or 1024.
+// on average at most 4 of the row's top k (a part stores its keys from the
+// 16th largest of its 64 lane maxima up, so it rarely misses one of the
+// row's top k: a miss sends the row to the re-read path); 128 to 1024.
 __host__ __device__ inline int topk_part_len(int64_t V, int k) {
   int P = kTopkPartLen;
-  while (P > 256 && (int64_t)k * P > 8 * V) P >>= 1;
+  while (P > kTopkPartMin && (int64_t)k * P > 4 * V) P >>= 1;
   return P;
 }
 

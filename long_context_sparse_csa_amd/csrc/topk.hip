@@ -60,11 +60,14 @@ TopkPlan topk_plan(int64_t vmax, int k) {
   // a row's part count is largest at its own length or just below a length
   // where the part length halves (rows of a launch may be shorter than vmax)
   int64_t np = 0;
-  for (int64_t V : {vmax, std::min(vmax, (int64_t)k * 128 - 1), std::min(vmax, (int64_t)k * 64 - 1)}) {
-    if (V <= 0) continue;
+  auto consider = [&](int64_t V) {
+    if (V <= 0) return;
     const int P = topk_part_len(V, k);
     np = std::max(np, (V + P - 1) / P);
-  }
+  };
+  consider(vmax);
+  for (int P = kTopkPartLen; P > kTopkPartMin; P >>= 1)   // P halves below V = k P / 4
+    consider(std::min(vmax, (int64_t)k * P / 4 - 1));
   p.nparts = p.parts ? (int)np : 0;
   return p;
 }

@@ -217,6 +217,7 @@ def test_index_topk_bit_exact_on_integer_inputs(case):
 SCORE_ROWS = [
     # name, V, k: rows built to reach every path of the selector
     ("random", 262144, 1024),      # the decode shape: leaders only
+    ("random_128k", 32768, 1024),  # the 128K decode shape: 128-score parts
     ("all_equal", 100000, 1024),   # every part overflows: re-read, chunked merge
     ("ascending", 60000, 4096),    # the top-k sits in the last parts: re-read
     ("nan_heavy", 50000, 1024),    # 3% valid keys: parts short of leaders
@@ -233,7 +234,7 @@ SCORE_ROWS = [
 
 def _score_row(name, V, seed):
     g = np.random.default_rng(seed)
-    name = name.replace("_small_k", "")
+    name = name.replace("_small_k", "").replace("_128k", "")
     if name == "random":
         return g.standard_normal(V).astype(np.float32)
     if name == "all_equal":
