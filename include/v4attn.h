@@ -55,9 +55,9 @@ extern "C" {
 #define V4ATTN_EHIP         (-4) /* HIP runtime error (no device, launch)   */
 
 /* Bytes of the fixed device scratch v4attn_hca_attend_noalloc uses on each
- * GPU (40 MiB: the split partials of 32 decode queries x 64 heads x 512 dims
- * over 8 splits take 33.7 MB). */
-#define V4ATTN_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+ * GPU (24 MiB: the split partials of 32 decode queries x 64 heads x 512 dims
+ * over 8 splits take 17.0 MB). */
+#define V4ATTN_NOALLOC_SCRATCH_BYTES ((size_t)24 << 20)
 
 /* v4attn_compress modes. */
 #define V4ATTN_POOL 0 /* pool 2m-token windows into compressed entries     */
@@ -340,7 +340,9 @@ int v4attn_index_topk_mxfp4(const uint8_t* q4, const uint8_t* q_sc, const float*
  *   ws / ws_bytes  >= v4attn_csa_attend_workspace(...) bytes (split
  *              partials of long rows; 0 is possible); contents on entry are
  *              ignored
- * Accumulation is fp32, split partials included.  On the E4M3 dims q~ (fp32)
+ * Accumulation is fp32; a long row's split partials are kept as 16-bit
+ * integers with one power-of-two scale per split and head (every element
+ * within 2^-15 of the head's largest).  On the E4M3 dims q~ (fp32)
  * enters the FP8 matrix cores as the sum of two E4M3 terms (its rounding and
  * the rounding of the remainder: at least bf16's eight significant bits), and
  * so do the probabilities (each 64-row block of a head scaled by its own

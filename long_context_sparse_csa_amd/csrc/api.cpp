@@ -116,10 +116,11 @@ IndexWs index_ws(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m, int k)
   return w;
 }
 
-// Attention workspace (splits > 1): the split partials, O then (max, sum),
-// all fp32.
+// Attention workspace (splits > 1): the split partials, O (16-bit integers
+// with a power-of-two scale per split and head), then (max, sum, scale
+// exponent, unused) in fp32.
 size_t attend_o_bytes(int64_t q, int s, int H, int D) {
-  return ((size_t)(q * s * H * D) * sizeof(float) + 255) / 256 * 256;
+  return ((size_t)(q * s * H * D) * sizeof(uint16_t) + 255) / 256 * 256;
 }
 
 size_t attend_ws(int B, int Tq, int H, int D, int64_t rows_max, bool csa, int* splits) {
@@ -127,13 +128,13 @@ size_t attend_ws(int B, int Tq, int H, int D, int64_t rows_max, bool csa, int* s
   if (splits) *splits = s;
   if (s <= 1) return 0;
   const int64_t q = (int64_t)B * Tq;
-  return attend_o_bytes(q, s, H, D) + (size_t)(q * s * H * 2) * sizeof(float);
+  return attend_o_bytes(q, s, H, D) + (size_t)(q * s * H * 4) * sizeof(float);
 }
 
 // Points the kernel arguments at their parts of the workspace.
 void attend_ws_layout(v4::AttendArgs& a, void* ws) {
   uint8_t* w = static_cast<uint8_t*>(ws);
-  a.part_o = reinterpret_cast<float*>(w);
+  a.part_o = reinterpret_cast<uint16_t*>(w);
   const size_t o_bytes = attend_o_bytes((int64_t)a.B * a.Tq, a.splits, a.H, a.D);
   a.part_ml = a.splits > 1 ? reinterpret_cast<float*>(w + o_bytes) : nullptr;
 }

@@ -716,14 +716,34 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   l_run += __shfl_xor(l_run, 32);
   // accumulator i of block db holds dim 16 db + 4g + i
   if (a.splits > 1) {
-    // unnormalised partial (O, max, sum) in fp32; the merge kernel adds the sink
-    float* po = a.part_o + (((int64_t)qr * a.splits + split) * a.H + head) * D;
+    // unnormalised partial O in block floating point: 16-bit integers and
+    // one power-of-two scale per (split, head), 2^e the head's largest |O|
+    // rounded up, so every element lands within 2^-15 of that largest value
+    // (bf16's bytes, fp32-like precision where it matters: the dominant
+    // elements of the dominant split); (max, sum, e - 15) in fp32.  The merge
+    // kernel adds the sink.
+    float amax = 0.f;
 #pragma unroll
-    for (int db = 0; db < NB; ++db) *reinterpret_cast<f32x4*>(po + 16 * db + 4 * g) = o[db];
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[db][i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;   // amax < 2^ex
+    const float to_int = ldexpf(1.0f, 15 - ex);
+    auto q16 = [&](float v) {
+      const int x = (int)rintf(v * to_int);   // |v * to_int| < 2^15: rounds to at most 2^15
+      return (unsigned)min(max(x, -32767), 32767) & 0xFFFFu;
+    };
+    uint16_t* po = a.part_o + (((int64_t)qr * a.splits + split) * a.H + head) * D;
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+      *reinterpret_cast<u32x2*>(po + 16 * db + 4 * g) =
+          u32x2{q16(o[db][0]) | (q16(o[db][1]) << 16), q16(o[db][2]) | (q16(o[db][3]) << 16)};
     if (g == 0) {
-      float* pm = a.part_ml + (((int64_t)qr * a.splits + split) * a.H + head) * 2;
-      pm[0] = l_run > 0.f ? m_run : -INFINITY;
-      pm[1] = l_run;
+      float* pm = a.part_ml + (((int64_t)qr * a.splits + split) * a.H + head) * 4;
+      *reinterpret_cast<f32x4*>(pm) =
+          f32x4{l_run > 0.f ? m_run : -INFINITY, l_run, (float)(ex - 15), 0.f};
     }
     return;
   }
@@ -787,17 +807,17 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   for (int hw = wave; hw < HPW; hw += 4) {
     const int h = h0 + hw;
     if (h >= a.H) break;
-    const float* pm = a.part_ml + ((int64_t)qr * S * a.H + h) * 2;
+    const float* pm = a.part_ml + ((int64_t)qr * S * a.H + h) * 4;
     const bool own = lane < S;
-    const f32x2 ml = own ? *reinterpret_cast<const f32x2*>(pm + (int64_t)lane * a.H * 2)
-                         : f32x2{-INFINITY, 0.f};
+    const f32x4 ml = own ? *reinterpret_cast<const f32x4*>(pm + (int64_t)lane * a.H * 4)
+                         : f32x4{-INFINITY, 0.f, 0.f, 0.f};
     const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
     const float M = fmaxf(wave_max(ml.x), z2);
     const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
     float den = wave_sum(ml.y * w);
     if (M != -INFINITY) den += exp2f(z2 - M);
     const float inv = den > 0.f ? 1.0f / den : 0.f;
-    s_w[hw][lane] = w * inv;
+    s_w[hw][lane] = ldexpf(w * inv, (int)ml.z);   // also undoes the partial's integer scale
     if (a.lse && lane == 0)
       a.lse[(int64_t)qr * a.H + h] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
   }
@@ -805,18 +825,19 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   const int hh = tid / QPH, d = 4 * (tid % QPH);
   const int h = h0 + hh;
   if (hh >= HPW || h >= a.H) return;
-  const float* po = a.part_o + ((int64_t)qr * S * a.H + h) * D + d;
+  const uint16_t* po = a.part_o + ((int64_t)qr * S * a.H + h) * D + d;
   const int64_t sstride = (int64_t)a.H * D;
   f32x4 x = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 8) {   // eight split partials in flight
-    f32x4 v[8];
+    u32x2 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)min(s0 + u, S - 1) * sstride);
+      v[u] = *reinterpret_cast<const u32x2*>(po + (int64_t)min(s0 + u, S - 1) * sstride);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float w = s0 + u < S ? s_w[hh][s0 + u] : 0.f;
-      x += w * v[u];
+      x += w * f32x4{(float)(int)(short)(v[u].x & 0xFFFFu), (float)((int)v[u].x >> 16),
+                     (float)(int)(short)(v[u].y & 0xFFFFu), (float)((int)v[u].y >> 16)};
     }
   }
   float y[4] = {x[0], x[1], x[2], x[3]};

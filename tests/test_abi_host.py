@@ -261,7 +261,7 @@ def test_hca_attend_noalloc_rejects_before_any_device_call():
     args[12] = 0
     assert f(*args) == -2          # m = 0
     args[12] = 128
-    # 255 queries over 328 rows: two splits of fp32 partials, 67 MB > the 40 MiB scratch
+    # 255 queries over 328 rows: two splits of partials, 33.5 MB > the 24 MiB scratch
     args[5], args[10], args[11], args[14] = 255, 200, 200, 200 * 128 + 5
     assert f(*args) == -3
     assert b"scratch" in L().v4attn_last_error()

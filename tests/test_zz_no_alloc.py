@@ -71,13 +71,13 @@ def test_noalloc_matches_workspace_call_twice():
 
 
 def test_noalloc_rejects_partials_beyond_the_scratch():
-    """255 queries over 328 rows need two splits of fp32 partials (67 MB),
-    more than the 40 MiB scratch: an error, nothing launched."""
+    """255 queries over 328 rows need two splits of partials (33.5 MB), more
+    than the 24 MiB scratch: an error, nothing launched."""
     B, H, D, N, m, t, W = 255, 64, 512, 200, 128, 200 * 128 + 5, 128
     q, ent, win, gq, sink = _inputs(B, H, D, N, W, 7)
     need = ops().hca_attend_workspace_bytes(B, 1, H, D, N, m, t, W)
     assert need > ops().lib().v4attn_hca_attend_workspace(32, 1, H, D, N, m, t, W)
-    assert need > (40 << 20)
+    assert need > (24 << 20)
     with pytest.raises(ops().V4AttnError) as ei:
         ops().hca_attend_noalloc(q, ent, win, gq, sink, n_entries=N, m=m, q_pos0=t, W=W)
     assert ei.value.status == ops().V4ATTN_EWORKSPACE
