@@ -116,9 +116,9 @@ IndexWs index_ws(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m, int k)
   return w;
 }
 
-// Attention workspace (splits > 1): the split partials, O (16-bit integers
-// with a power-of-two scale per split and head), then (max, sum, scale
-// exponent, unused) in fp32.
+// Attention workspace (splits > 1): the split partials, O (signed
+// normalised 16-bit integers with a power-of-two scale per split and head),
+// then (max, sum, scale exponent, unused) in fp32.
 size_t attend_o_bytes(int64_t q, int s, int H, int D) {
   return ((size_t)(q * s * H * D) * sizeof(uint16_t) + 255) / 256 * 256;
 }

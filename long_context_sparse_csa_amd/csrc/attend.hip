@@ -329,86 +329,75 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl) qv[sl] = u32x4{0u, 0u, 0u, 0u};
     }
-    float ss = 0.f;
+    // one pass over q: the sum of squares, and a bound on the largest |q~|
+    // before the RMS scale (|gamma q| on the E4M3 dims; on the rotary dims
+    // the length of each rotated pair, which bounds both of its components)
+    float ss = 0.f, mb = 0.f, mr2 = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < NSL; ++sl)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_bits_to_f32(qv[sl][e] & 0xFFFFu), hi = bf16_bits_to_f32(qv[sl][e] >> 16);
-        ss += lo * lo + hi * hi;
-      }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    const float rsn = 1.0f / sqrtf(ss / (float)D + a.eps);
-    // gamma_q * q * rsn of slot sl, element e (the same fp32 operations in
-    // both passes below, so the E4M3 split sees the values the maximum saw)
-    auto qnorm = [&](int sl, float (&qf)[8]) {
+    for (int sl = 0; sl < NSL; ++sl) {
       const int d0 = slot_ok(sl) ? slot_dim(sl) : 0;
       const f32x4 ga = *reinterpret_cast<const f32x4*>(s_gamma + d0);
       const f32x4 gb = *reinterpret_cast<const f32x4*>(s_gamma + d0 + 4);
       const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qf[2 * e] = gm[2 * e] * (bf16_bits_to_f32(qv[sl][e] & 0xFFFFu) * rsn);
-        qf[2 * e + 1] = gm[2 * e + 1] * (bf16_bits_to_f32(qv[sl][e] >> 16) * rsn);
+        const float lo = bf16_bits_to_f32(qv[sl][e] & 0xFFFFu), hi = bf16_bits_to_f32(qv[sl][e] >> 16);
+        ss += lo * lo + hi * hi;
+        const float glo = gm[2 * e] * lo, ghi = gm[2 * e + 1] * hi;
+        if (sl >= 4 * NJ) mr2 = fmaxf(mr2, glo * glo + ghi * ghi);
+        else mb = fmaxf(mb, fmaxf(fabsf(glo), fabsf(ghi)));
       }
-    };
-    // the largest |q~| of the head; the rotary slots are rotated and rounded
-    // to bf16 in place, the E4M3 slots keep the raw q
-    float mx = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) {
-      float qf[8];
-      qnorm(sl, qf);
-      if (sl >= 4 * NJ) {
-        const int d0 = slot_dim(sl);
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int i = (d0 + e - (D - R)) >> 1;
-          const float cs = s_cs[i][0], sn = s_cs[i][1];
-          const float x0 = qf[e], x1 = qf[e + 1];
-          qf[e] = x0 * cs - x1 * sn;
-          qf[e + 1] = x0 * sn + x1 * cs;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qv[sl][e] = pack_bf16x2(qf[2 * e], qf[2 * e + 1]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(qf[e]));
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    mb = fmaxf(mb, sqrtf(mr2));
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float rsn = 1.0f / sqrtf(ss / (float)D + a.eps);
+    // 2^qe puts the bound (so every |q~|) at most 256, the largest near it
+    const float mx = mb * rsn;
     const int qe = mx > 0.f ? 8 - __builtin_amdgcn_frexp_expf(mx) : 0;
     qscale_inv = ldexpf(1.0f, -qe);
+    const float rs2 = ldexpf(rsn, qe);
+    // second pass: q~ 2^qe = gamma q rsn 2^qe; the E4M3 slots split into
+    // hi + lo, the rotary slots rotated and rounded to bf16
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int sl = 0; sl < NSL; ++sl) {
+      const int d0 = slot_ok(sl) ? slot_dim(sl) : 0;
+      const f32x4 ga = *reinterpret_cast<const f32x4*>(s_gamma + d0);
+      const f32x4 gb = *reinterpret_cast<const f32x4*>(s_gamma + d0 + 4);
+      const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      float x[8];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float qf[8];
-        qnorm(4 * j + v, qf);
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = (gm[2 * e] * bf16_bits_to_f32(qv[sl][e] & 0xFFFFu)) * rs2;
+        x[2 * e + 1] = (gm[2 * e + 1] * bf16_bits_to_f32(qv[sl][e] >> 16)) * rs2;
+      }
+      if (sl < 4 * NJ) {
+        const int j = sl >> 2, v = sl & 3;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const float x0 = ldexpf(qf[4 * h2], qe), x1 = ldexpf(qf[4 * h2 + 1], qe);
-          const float x2 = ldexpf(qf[4 * h2 + 2], qe), x3 = ldexpf(qf[4 * h2 + 3], qe);
+          const float x0 = x[4 * h2], x1 = x[4 * h2 + 1], x2 = x[4 * h2 + 2], x3 = x[4 * h2 + 3];
           int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
           hw = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hw, true);
           const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
           const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
           int lw = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - b01.x, x1 - b01.y, 0, false);
           lw = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - b23.x, x3 - b23.y, lw, true);
-          qh[j][2 * v + h2] = slot_ok(4 * j + v) ? hw : 0;
-          ql[j][2 * v + h2] = slot_ok(4 * j + v) ? lw : 0;
+          qh[j][2 * v + h2] = slot_ok(sl) ? hw : 0;
+          ql[j][2 * v + h2] = slot_ok(sl) ? lw : 0;
         }
-      }
+      } else {
+        u32x4 pk;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4 pk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned w = qv[4 * NJ + s2][e];
-        pk[e] = pack_bf16x2(ldexpf(bf16_bits_to_f32(w & 0xFFFFu), qe), ldexpf(bf16_bits_to_f32(w >> 16), qe));
+        for (int e = 0; e < 8; e += 2) {
+          const int i = (d0 + e - (D - R)) >> 1;
+          const float cs = s_cs[i][0], sn = s_cs[i][1];
+          const float x0 = x[e], x1 = x[e + 1];
+          pk[e >> 1] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+        }
+        qt[sl - 4 * NJ] = __builtin_bit_cast(bf16x8, pk);
       }
-      qt[s2] = __builtin_bit_cast(bf16x8, pk);
     }
   }
 
@@ -716,12 +705,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   l_run += __shfl_xor(l_run, 32);
   // accumulator i of block db holds dim 16 db + 4g + i
   if (a.splits > 1) {
-    // unnormalised partial O in block floating point: 16-bit integers and
-    // one power-of-two scale per (split, head), 2^e the head's largest |O|
-    // rounded up, so every element lands within 2^-15 of that largest value
-    // (bf16's bytes, fp32-like precision where it matters: the dominant
-    // elements of the dominant split); (max, sum, e - 15) in fp32.  The merge
-    // kernel adds the sink.
+    // unnormalised partial O in block floating point: 16-bit signed
+    // normalised integers and one power-of-two scale per (split, head), 2^e
+    // the head's largest |O| rounded up, so every element lands within
+    // 2^-15 of that largest value (bf16's bytes, fp32-like precision where
+    // it matters: the dominant elements of the dominant split); (max, sum,
+    // e) in fp32.  The merge kernel adds the sink.
     float amax = 0.f;
 #pragma unroll
     for (int db = 0; db < NB; ++db)
@@ -730,20 +719,19 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     const int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;   // amax < 2^ex
-    const float to_int = ldexpf(1.0f, 15 - ex);
-    auto q16 = [&](float v) {
-      const int x = (int)rintf(v * to_int);   // |v * to_int| < 2^15: rounds to at most 2^15
-      return (unsigned)min(max(x, -32767), 32767) & 0xFFFFu;
-    };
+    const float to_unit = ldexpf(1.0f, -ex);   // |O| 2^-ex < 1: snorm16 = round(32767 |O| 2^-ex)
     uint16_t* po = a.part_o + (((int64_t)qr * a.splits + split) * a.H + head) * D;
 #pragma unroll
-    for (int db = 0; db < NB; ++db)
+    for (int db = 0; db < NB; ++db) {
+      const s16x2 lo = __builtin_amdgcn_cvt_pknorm_i16(o[db][0] * to_unit, o[db][1] * to_unit);
+      const s16x2 hi = __builtin_amdgcn_cvt_pknorm_i16(o[db][2] * to_unit, o[db][3] * to_unit);
       *reinterpret_cast<u32x2*>(po + 16 * db + 4 * g) =
-          u32x2{q16(o[db][0]) | (q16(o[db][1]) << 16), q16(o[db][2]) | (q16(o[db][3]) << 16)};
+          u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+    }
     if (g == 0) {
       float* pm = a.part_ml + (((int64_t)qr * a.splits + split) * a.H + head) * 4;
       *reinterpret_cast<f32x4*>(pm) =
-          f32x4{l_run > 0.f ? m_run : -INFINITY, l_run, (float)(ex - 15), 0.f};
+          f32x4{l_run > 0.f ? m_run : -INFINITY, l_run, (float)ex, 0.f};
     }
     return;
   }
@@ -817,7 +805,8 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
     float den = wave_sum(ml.y * w);
     if (M != -INFINITY) den += exp2f(z2 - M);
     const float inv = den > 0.f ? 1.0f / den : 0.f;
-    s_w[hw][lane] = ldexpf(w * inv, (int)ml.z);   // also undoes the partial's integer scale
+    // also undoes the partial's scale: O = q 2^e / 32767
+    s_w[hw][lane] = ldexpf(w * inv, (int)ml.z) * (1.0f / 32767.0f);
     if (a.lse && lane == 0)
       a.lse[(int64_t)qr * a.H + h] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
   }

@@ -193,8 +193,8 @@ struct AttendArgs {
   uint16_t* out;            // [B, Tq, H, D]
   float* lse;               // [B, Tq, H] or nullptr
   int splits;               // key-range splits per query (1 = no merge pass)
-  uint16_t* part_o;         // [B*Tq, splits, H, D] int16, unnormalised O times 2^-(exponent)
-  float* part_ml;           // [B*Tq, splits, H, 4]  (max, sum, exponent, unused)
+  uint16_t* part_o;         // [B*Tq, splits, H, D] snorm16 q: unnormalised O = q 2^e / 32767
+  float* part_ml;           // [B*Tq, splits, H, 4]  (max, sum, e, unused)
   int64_t rows_max;         // max rows (entries + window) over the block
   float* logits2;           // HCA only: nullptr, or [B*Tq, logits_stride, 64]: every row's logit
                             // per head (heads innermost, slots >= H unused) times
