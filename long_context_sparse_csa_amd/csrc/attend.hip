@@ -223,6 +223,42 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
     if (slot_ok(sl)) qv[sl] = *reinterpret_cast<const u32x4*>(qp + slot_dim(sl));
   }
 
+  // ---- staging: wave w copies tile rows 32w..32w+31 as WPW windows of 64
+  // 16-byte slots; slot s holds physical chunk s % CPR of row s / CPR, loaded
+  // from logical chunk (s % CPR) ^ swz(row).  Lane l resolves row 32w + l%32.
+  const uint8_t* zero_row = g_zero_row;
+  // Per-lane source offsets of the copies within a run of contiguous rows:
+  // slot 64 i + lane -> row 32w + s / CPR, logical chunk of physical s % CPR.
+  unsigned coff[G::WPW];
+#pragma unroll
+  for (int i = 0; i < G::WPW; ++i) {
+    const int sl = 64 * i + lane;
+    const int rl = sl / G::CPR, pc = sl - rl * G::CPR;
+    coff[i] = (unsigned)((32 * wave + rl) * ROW + 16 * ((pc & ~3) | ((pc & 3) ^ swz(rl))));
+  }
+  // A whole tile of contiguous present rows (HCA entries, or window rows) is
+  // copied from one uniform base, without per-row lookups; its copies are
+  // spread over the S^T steps of the previous tile (contig_base), the rest go
+  // out at once (issue_tile).
+  auto contig_base = [&](int tile) -> const uint8_t* {
+    const int x0 = tile * kAttRows;
+    const bool full = x0 + kAttRows <= nloc;
+    const bool all_ent = x0 + kAttRows <= ent_loc, all_win = x0 >= ent_loc;
+    if (!full || !((!CSA && all_ent) || all_win)) return nullptr;
+    return all_win ? win_b + (int64_t)(x0 - win_first) * ROW : ent_b + (int64_t)(row_beg + x0) * ROW;
+  };
+  auto issue_copy = [&](const uint8_t* base, int buf, int i) {
+    copy_to_lds16_sbase(base, coff[i], (V4_LDS void*)(s_tile[buf] + 32 * wave * ROW + 1024 * i));
+  };
+  // A contiguous tile 0 goes out now, behind only the loads above, so its
+  // HBM latency overlaps the rest of the prologue.
+  const uint8_t* base0 = ntiles > 0 ? contig_base(0) : nullptr;
+  if (base0) {
+    if (lane == 0) s_v[0][wave] = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < G::WPW; ++i) issue_copy(base0, 0, i);
+  }
+
   if (tid < R / 2) {
     float cs, sn;
     rope_cos_sin(t, rturn, &cs, &sn);
@@ -254,33 +290,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
     return ok ? p : nullptr;
   };
 
-  // ---- staging: wave w copies tile rows 32w..32w+31 as WPW windows of 64
-  // 16-byte slots; slot s holds physical chunk s % CPR of row s / CPR, loaded
-  // from logical chunk (s % CPR) ^ swz(row).  Lane l resolves row 32w + l%32.
-  const uint8_t* zero_row = g_zero_row;
-  // Per-lane source offsets of the copies within a run of contiguous rows:
-  // slot 64 i + lane -> row 32w + s / CPR, logical chunk of physical s % CPR.
-  unsigned coff[G::WPW];
-#pragma unroll
-  for (int i = 0; i < G::WPW; ++i) {
-    const int sl = 64 * i + lane;
-    const int rl = sl / G::CPR, pc = sl - rl * G::CPR;
-    coff[i] = (unsigned)((32 * wave + rl) * ROW + 16 * ((pc & ~3) | ((pc & 3) ^ swz(rl))));
-  }
-  // A whole tile of contiguous present rows (HCA entries, or window rows) is
-  // copied from one uniform base, without per-row lookups; its copies are
-  // spread over the S^T steps of the previous tile (contig_base), the rest go
-  // out at once (issue_tile).
-  auto contig_base = [&](int tile) -> const uint8_t* {
-    const int x0 = tile * kAttRows;
-    const bool full = x0 + kAttRows <= nloc;
-    const bool all_ent = x0 + kAttRows <= ent_loc, all_win = x0 >= ent_loc;
-    if (!full || !((!CSA && all_ent) || all_win)) return nullptr;
-    return all_win ? win_b + (int64_t)(x0 - win_first) * ROW : ent_b + (int64_t)(row_beg + x0) * ROW;
-  };
-  auto issue_copy = [&](const uint8_t* base, int buf, int i) {
-    copy_to_lds16_sbase(base, coff[i], (V4_LDS void*)(s_tile[buf] + 32 * wave * ROW + 1024 * i));
-  };
   auto issue_tile = [&](int tile, int buf) {
     if (const uint8_t* base = contig_base(tile)) {
       if (lane == 0) s_v[buf][wave] = 0xFFFFFFFFu;
@@ -307,7 +316,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
       copy_to_lds16(src, (V4_LDS void*)(Tw + 1024 * i));
     }
   };
-  if (ntiles > 0) issue_tile(0, 0);
+  if (ntiles > 0 && !base0) issue_tile(0, 0);
 
   // ---- q~ = RoPE_t(RMSNorm(q)) in fp32, scaled by 2^qe (per head, exact;
   // qe puts the head's largest |q~| in [128, 256)), as the B operand of S^T.
@@ -689,10 +698,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
     if (!grow) break;
     const float mt = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mo[0], mo[1]));
     const float m_new = mt > m_run + kLazyMax ? ceilf(mt) : m_run;
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= corr;
+    if (m_run != kNoMax) {   // before the first present row O and l are still zero
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= corr;
 #pragma unroll
-    for (int db = 0; db < NB; ++db) o[db] *= corr;
+      for (int db = 0; db < NB; ++db) o[db] *= corr;
+    }
     m_run = m_new;
     pv(T, sacc, mp, mo);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
