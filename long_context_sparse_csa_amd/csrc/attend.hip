@@ -250,6 +250,27 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   auto issue_copy = [&](const uint8_t* base, int buf, int i) {
     copy_to_lds16_sbase(base, coff[i], (V4_LDS void*)(s_tile[buf] + 32 * wave * ROW + 1024 * i));
   };
+  // Copies of one tile whose rows are gathered: lane l of wave w holds the
+  // packed row pointer of tile row 32w + l % 32 (nullptr: absent).
+  auto issue_rows = [&](const uint8_t* rp, int buf) {
+    const bool ok = rp != nullptr;
+    const unsigned long long bal = __ballot(ok);
+    if (lane == 0) s_v[buf][wave] = (unsigned)(bal & 0xFFFFFFFFull);
+    const long long rpl = (long long)(uintptr_t)(ok ? rp : zero_row);
+    uint8_t* Tw = s_tile[buf] + 32 * wave * ROW;
+    // the slot arithmetic below is redone per tile (an opaque lane index keeps
+    // the compiler from hoisting ~2 registers per copy out of the tile loop)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < G::WPW; ++i) {
+      const int sl = 64 * i + ln;
+      const int rl = sl / G::CPR, pc = sl - rl * G::CPR;
+      const uint8_t* src = (const uint8_t*)(uintptr_t)__shfl(rpl, rl) +
+                           16 * ((pc & ~3) | ((pc & 3) ^ swz(rl)));
+      copy_to_lds16(src, (V4_LDS void*)(Tw + 1024 * i));
+    }
+  };
   // A contiguous tile 0 goes out now, behind only the loads above, so its
   // HBM latency overlaps the rest of the prologue.
   const uint8_t* base0 = ntiles > 0 ? contig_base(0) : nullptr;
@@ -257,6 +278,25 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
     if (lane == 0) s_v[0][wave] = 0xFFFFFFFFu;
 #pragma unroll
     for (int i = 0; i < G::WPW; ++i) issue_copy(base0, 0, i);
+  }
+  // CSA: a gathered tile 0 too, its row indices read straight from the top-k
+  // list (the LDS copy of the split's slice serves the later tiles).
+  bool early0 = false;
+  if constexpr (CSA) {
+    if (!base0 && ntiles > 0 && a.sel_m <= 1) {
+      const int x = 32 * wave + (lane & 31);
+      const uint8_t* rp = nullptr;
+      if (x < nloc) {
+        if (x < ent_loc) {
+          const int64_t j = a.topk[(int64_t)qr * a.k + row_beg + x];
+          if (j >= 0 && j < a.Ncap) rp = ent_b + j * ROW;
+        } else {
+          rp = win_b + (int64_t)(x - win_first) * ROW;
+        }
+      }
+      issue_rows(rp, 0);
+      early0 = true;
+    }
   }
 
   if (tid < R / 2) {
@@ -297,26 +337,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
       for (int i = 0; i < G::WPW; ++i) issue_copy(base, buf, i);
       return;
     }
-    const uint8_t* rp = row_ptr(tile * kAttRows + 32 * wave + (lane & 31));
-    const bool ok = rp != nullptr;
-    const unsigned long long bal = __ballot(ok);
-    if (lane == 0) s_v[buf][wave] = (unsigned)(bal & 0xFFFFFFFFull);
-    const long long rpl = (long long)(uintptr_t)(ok ? rp : zero_row);
-    uint8_t* Tw = s_tile[buf] + 32 * wave * ROW;
-    // the slot arithmetic below is redone per tile (an opaque lane index keeps
-    // the compiler from hoisting ~2 registers per copy out of the tile loop)
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-#pragma unroll
-    for (int i = 0; i < G::WPW; ++i) {
-      const int sl = 64 * i + ln;
-      const int rl = sl / G::CPR, pc = sl - rl * G::CPR;
-      const uint8_t* src = (const uint8_t*)(uintptr_t)__shfl(rpl, rl) +
-                           16 * ((pc & ~3) | ((pc & 3) ^ swz(rl)));
-      copy_to_lds16(src, (V4_LDS void*)(Tw + 1024 * i));
-    }
+    issue_rows(row_ptr(tile * kAttRows + 32 * wave + (lane & 31)), buf);
   };
-  if (ntiles > 0 && !base0) issue_tile(0, 0);
+  if (ntiles > 0 && !base0 && !early0) issue_tile(0, 0);
 
   // ---- q~ = RoPE_t(RMSNorm(q)) in fp32, scaled by 2^qe (per head, exact;
   // qe puts the head's largest |q~| in [128, 256)), as the B operand of S^T.
