@@ -139,6 +139,22 @@ void attend_ws_layout(v4::AttendArgs& a, void* ws) {
   a.part_ml = a.splits > 1 ? reinterpret_cast<float*>(w + o_bytes) : nullptr;
 }
 
+// Ragged decode batches (Tq = 1): each sequence gets its own split count
+// (about the same tiles per workgroup everywhere) instead of the longest
+// sequence's.  csa: rows = k + window rows; else visible entries + window.
+void plan_ragged_attend(v4::AttendArgs& a, bool csa) {
+  if (!a.ragged || a.Tq != 1 || a.B < 1) return;
+  int64_t rows[v4::kMaxRagged];
+  for (int b = 0; b < a.B; ++b) {
+    const int64_t t = a.pos.p[b];
+    const int64_t lo = t - a.W + 1 > 0 ? t - a.W + 1 : 0;
+    const int64_t n_win = a.W > 0 ? t - lo + 1 : 0;
+    const int64_t v = (t + 1) / a.m < a.n_entries ? (t + 1) / a.m : a.n_entries;
+    rows[b] = (csa ? (int64_t)a.k : v) + n_win;
+  }
+  v4::plan_flat_splits(a, rows, csa);
+}
+
 // need_sink: the call takes a per-head sink (every attention call but the
 // NSA-style variant, whose branches have none).
 int check_attend_common(const uint16_t* q, const uint8_t* entries, const uint8_t* win,
@@ -676,6 +692,7 @@ int v4attn_csa_attend(const uint16_t* q, const uint8_t* entries, const int32_t* 
   a.rows_max = (int64_t)k + W;
   a.ragged = ragged;
   if (ragged) a.pos = sp;
+  plan_ragged_attend(a, true);
   return hip_status(v4::launch_attend(a, (hipStream_t)stream), "CSA attend launch");
 }
 
@@ -717,6 +734,7 @@ int hca_attend_args(const uint16_t* q, const uint8_t* entries, const uint8_t* wi
   a.rows_max = rows_max;
   a.ragged = ragged;
   if (ragged) a.pos = sp;
+  plan_ragged_attend(a, false);
   return V4ATTN_OK;
 }
 

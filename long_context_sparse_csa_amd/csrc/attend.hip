@@ -149,9 +149,24 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   constexpr int R = G::R, NJ = G::NJ, NB8 = G::NB8, NB = G::NB, ROW = G::ROW;
   constexpr int BFC = G::FP8_CPR;   // first bf16 chunk
   const AttendArgs& a = ab.p[blockIdx.z];   // the problem of this grid layer
-  const int qr = blockIdx.y;
-  const int split = blockIdx.x;
-  if (split >= a.splits) return;   // a layer with fewer splits than the grid
+  int qr, split, nsplit;
+  int64_t slot;   // this split's partial slot
+  if (a.flat) {   // ragged decode: workgroup x is slot x of sequence b
+    const int x = blockIdx.x;
+    if (x >= a.slot0[a.B]) return;
+    int bb = 0;
+    while (bb + 1 < a.B && x >= a.slot0[bb + 1]) ++bb;
+    qr = bb;
+    split = x - a.slot0[bb];
+    nsplit = a.slot0[bb + 1] - a.slot0[bb];
+    slot = x;
+  } else {
+    qr = blockIdx.y;
+    split = blockIdx.x;
+    if (split >= a.splits) return;   // a layer with fewer splits than the grid
+    nsplit = a.splits;
+    slot = (int64_t)qr * a.splits + split;
+  }
   const int b = qr / a.Tq, r = qr % a.Tq;
   const int64_t qpos = a.ragged ? a.pos.p[b] : a.q_pos0;   // this sequence's first query
   const int64_t t = qpos + r;
@@ -167,7 +182,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   __shared__ __attribute__((aligned(16))) float s_gamma[D];      // gamma_q, read per q~ slot
 
   const RowSpace rs = row_space(a, CSA, t);
-  const int64_t chunk = split_chunk(rs.n_rows, a.splits);
+  const int64_t chunk = split_chunk(rs.n_rows, nsplit);
   const int64_t row_beg = (int64_t)split * chunk;
   int64_t row_end = row_beg + chunk;
   if (row_end > rs.n_rows) row_end = rs.n_rows;
@@ -738,7 +753,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   // accumulator i of block db holds dim 16 db + 4g + i
-  if (a.splits > 1) {
+  if (nsplit > 1) {
     // unnormalised partial O in block floating point: 16-bit signed
     // normalised integers and one power-of-two scale per (split, head), 2^e
     // the head's largest |O| rounded up, so every element lands within
@@ -754,7 +769,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     const int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;   // amax < 2^ex
     const float to_unit = ldexpf(1.0f, -ex);   // |O| 2^-ex < 1: snorm16 = round(32767 |O| 2^-ex)
-    uint16_t* po = a.part_o + (((int64_t)qr * a.splits + split) * a.H + head) * D;
+    uint16_t* po = a.part_o + (slot * a.H + head) * D;
 #pragma unroll
     for (int db = 0; db < NB; ++db) {
       const s16x2 lo = __builtin_amdgcn_cvt_pknorm_i16(o[db][0] * to_unit, o[db][1] * to_unit);
@@ -763,7 +778,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
           u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
     }
     if (g == 0) {
-      float* pm = a.part_ml + (((int64_t)qr * a.splits + split) * a.H + head) * 4;
+      float* pm = a.part_ml + (slot * a.H + head) * 4;
       *reinterpret_cast<f32x4*>(pm) =
           f32x4{l_run > 0.f ? m_run : -INFINITY, l_run, (float)ex, 0.f};
     }
@@ -809,14 +824,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
 template <int D>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   const AttendArgs& a = ab.p[blockIdx.z];
-  if (a.splits <= 1) return;   // this layer's kernel stored its output itself
+  const int qr = blockIdx.y;
+  if (qr >= a.B * a.Tq) return;
+  const int S = a.flat ? a.slot0[qr + 1] - a.slot0[qr] : a.splits;
+  if (S <= 1) return;   // the attention kernel stored this query's output itself
+  const int64_t slot0 = a.flat ? a.slot0[qr] : (int64_t)qr * S;   // its first partial slot
   constexpr int R = 64;
   constexpr int QPH = D / 4;          // threads per head (four dims each)
   constexpr int HPW = 256 / QPH;      // heads per workgroup
-  const int qr = blockIdx.y;
   const int h0 = blockIdx.x * HPW;
   const int64_t t = (a.ragged ? a.pos.p[qr / a.Tq] : a.q_pos0) + (qr % a.Tq);
-  const int S = a.splits;
   __shared__ float s_w[HPW][64];
   __shared__ float s_cs[R / 2][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -829,7 +846,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   for (int hw = wave; hw < HPW; hw += 4) {
     const int h = h0 + hw;
     if (h >= a.H) break;
-    const float* pm = a.part_ml + ((int64_t)qr * S * a.H + h) * 4;
+    const float* pm = a.part_ml + (slot0 * a.H + h) * 4;
     const bool own = lane < S;
     const f32x4 ml = own ? *reinterpret_cast<const f32x4*>(pm + (int64_t)lane * a.H * 4)
                          : f32x4{-INFINITY, 0.f, 0.f, 0.f};
@@ -848,7 +865,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   const int hh = tid / QPH, d = 4 * (tid % QPH);
   const int h = h0 + hh;
   if (hh >= HPW || h >= a.H) return;
-  const uint16_t* po = a.part_o + ((int64_t)qr * S * a.H + h) * D + d;
+  const uint16_t* po = a.part_o + (slot0 * a.H + h) * D + d;
   const int64_t sstride = (int64_t)a.H * D;
   f32x4 x = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 8) {   // eight split partials in flight
@@ -903,16 +920,19 @@ hipError_t launch_attend_batch(const AttendBatch& ab, int n, hipStream_t st) {
   bool merge = false;
   for (int z = 0; z < n; ++z) {
     const AttendArgs& x = ab.p[z];
-    // one kernel instance serves the batch: same kind, shapes and query block
-    if ((x.topk != nullptr) != csa || x.D != a.D || x.H != a.H || x.B != a.B || x.Tq != a.Tq)
+    // one kernel instance serves the batch: same kind, shapes, query block
+    // and grid form
+    if ((x.topk != nullptr) != csa || x.D != a.D || x.H != a.H || x.B != a.B || x.Tq != a.Tq ||
+        x.flat != a.flat)
       return hipErrorInvalidValue;
     // every split's slice of the top-k list must fit the kernel's LDS copy
-    if (csa && split_chunk(x.rows_max, x.splits) > kSelCap) return hipErrorInvalidValue;
+    if (csa && !x.flat && split_chunk(x.rows_max, x.splits) > kSelCap) return hipErrorInvalidValue;
     if (csa && x.sel_m > 1 && x.k % x.sel_m != 0) return hipErrorInvalidValue;
-    gx = x.splits > gx ? x.splits : gx;
-    merge = merge || x.splits > 1;
+    const int xs = x.flat ? x.slot0[x.B] : x.splits;
+    gx = xs > gx ? xs : gx;
+    merge = merge || (x.flat ? x.slot0[x.B] > x.B : x.splits > 1);
   }
-  dim3 grid(gx, (unsigned)q, n);
+  dim3 grid(gx, a.flat ? 1u : (unsigned)q, n);
 #define V4_ATT(D)                                                             \
   do {                                                                        \
     if (csa) attend_kernel<D, true><<<grid, kAttThreads, 0, st>>>(ab);        \
@@ -927,6 +947,40 @@ hipError_t launch_attend_batch(const AttendBatch& ab, int n, hipStream_t st) {
   }
 #undef V4_ATT
   return hipGetLastError();
+}
+
+void plan_flat_splits(AttendArgs& a, const int64_t* rows, bool csa) {
+  const int B = a.B;
+  a.flat = false;
+  if (B < 1 || B > kMaxRagged || a.Tq != 1) return;
+  const int64_t cap = (int64_t)B * a.splits;          // the partial slots the workspace holds
+  const int64_t want = cap < 256 ? cap : (B > 256 ? B : 256);   // about one workgroup per CU
+  int64_t tiles[kMaxRagged], total = 0;
+  for (int b = 0; b < B; ++b) {
+    tiles[b] = (rows[b] + kAttRows - 1) / kAttRows;
+    total += tiles[b] > 0 ? tiles[b] : 1;
+  }
+  auto splits_of = [&](int b, int64_t per) {
+    int64_t s = (tiles[b] + per - 1) / per;
+    if (csa)   // a split's slice of the top-k list fits the kernel's LDS copy
+      while (split_chunk(rows[b], (int)s) > kSelCap) ++s;
+    s = s < 1 ? 1 : (s > 64 ? 64 : s);
+    return s;
+  };
+  for (int64_t per = (total + want - 1) / want; per <= (1 << 20); ++per) {
+    int64_t sum = 0;
+    for (int b = 0; b < B; ++b) sum += splits_of(b, per);
+    if (sum <= cap) {
+      int acc = 0;
+      for (int b = 0; b < B; ++b) {
+        a.slot0[b] = acc;
+        acc += (int)splits_of(b, per);
+      }
+      a.slot0[B] = acc;
+      a.flat = true;
+      return;
+    }
+  }
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {

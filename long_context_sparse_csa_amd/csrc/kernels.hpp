@@ -210,8 +210,18 @@ struct AttendArgs {
   const uint16_t* mix_o2;
   bool ragged;              // query block of sequence b starts at pos.p[b]
   SeqPos pos;               // (its window buffer rows are relative to it)
+  // ragged decode (Tq = 1) with its own split count per sequence: sequence b
+  // owns split slots slot0[b] .. slot0[b+1]-1 (a flat grid of slot0[B]
+  // workgroups; partials at those slots); false: `splits` for every query
+  bool flat;
+  int slot0[kMaxRagged + 1];
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+// Per-sequence split counts for a ragged decode batch (rows[b] rows for
+// sequence b): about the same number of tiles per workgroup everywhere,
+// within the B * a.splits partial slots of the uniform plan.  Sets a.flat
+// and a.slot0.
+void plan_flat_splits(AttendArgs& a, const int64_t* rows, bool csa);
 
 // Up to two problems of the same kind, head count, head dim and query block
 // in one launch (grid layer z runs p[z]); each keeps its own splits and

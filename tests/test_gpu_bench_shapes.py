@@ -10,7 +10,9 @@ on sampled outputs the float64 oracle computes one by one.
   * the bf16 lightning indexer at the 1M decode shape (8 x 262,144 entries)
     and its top-k;
   * the prefill indexer + top-k at 4096 queries x ~263K entries, whose fp32
-    score buffer passes 2^32 bytes (rows beyond it are sampled).
+    score buffer passes 2^32 bytes (rows beyond it are sampled);
+  * the ragged HCA decode batch (32 sequences of 256 to 8,192 visible
+    entries, each with its own split count).
 
 Bars as everywhere: attention max-abs <= 2e-2 and rel-L2 <= 5e-3 per
 sampled query; scores within fp32 rounding of the float64 sum; top-k sets
@@ -233,3 +235,31 @@ def test_prefill_index_topk_4096_on_1m_sampled_past_4gib():
         got_s = ts[0, r].cpu().double().numpy()
         assert np.all(np.abs(got_s - sc[g]) <= 2.0 ** -12 * bound[g]), f"row {r}: scores"
         log(f"  r={r} V={V} byte offset {r * stride * 4}: {n_diff} near-tie swaps")
+
+
+def test_hca_ragged_decode_sampled():
+    """The ragged decode batch the benchmark times: 32 sequences at positions
+    (b + 1) 2^15 - 1 (256 to 8,192 visible entries), each with its own split
+    count; sampled sequences against the oracle."""
+    h = HCA_1M
+    B, H, D, R, W, m = h.B, h.H, h.D, h.R, h.W, h.m
+    N = h.T // m
+    pos = [(b + 1) * (1 << 15) - 1 for b in range(B)]
+    log(f"hca ragged decode B={B}")
+    ent = synth.packed_rows((B, N), D, R, h.seed, "entries", DEV)
+    win = synth.packed_rows((B, W), D, R, h.seed, "win", DEV)
+    q = synth.normal((B, 1, H, D), h.seed, "q", DEV, dtype=torch.bfloat16)
+    gq = synth.normal((D,), h.seed, "gamma_q", DEV, mean=1.0, std=0.1)
+    sink = synth.normal((H,), h.seed, "sink", DEV)
+    out, lse = ops().hca_attend(q, ent, win, gq, sink, n_entries=N, m=m, W=W, seq_pos=pos,
+                                want_lse=True)
+    torch.cuda.synchronize()
+    gqn, sk = gq.cpu().double().numpy(), sink.cpu().double().numpy()
+    for b in (0, 1, 15, 31):
+        t = pos[b]
+        V = min(N, (t + 1) // m)
+        rows = np.concatenate([rows_to_f64(ent[b, :V], D, R), rows_to_f64(win[b], D, R)])
+        o, l = _attend_one(bf16_to_f64(q[b, 0]), rows, gqn, sk, t, h.scale, D)
+        ma, rl = assert_attn_close(bf16_to_f64(out[b, 0]), o, f"hca ragged b={b}")
+        log(f"  b={b} V={V} max_abs {ma:.2e} rel_l2 {rl:.2e}")
+        np.testing.assert_allclose(lse[b, 0].cpu().numpy(), l, rtol=2e-3, atol=2e-3)
