@@ -554,176 +554,191 @@ __device__ __forceinline__ void topk_select_general(const TopkArgs& a, unsigned*
 }
 
 // ---- the per-row kernel.  Fast path (rows of at most kSelThreads parts):
-// thread q holds part q's stored leaders in registers, in position order, so
-// (part, slot) order is the row's position order.  A bucket select over the
-// registers finds the k-th largest leader lo; one scan over the parts then
-// places each part's selected leaders.  If every part stored all its keys
+// the parts' stored leaders sit in registers, part q's slots with threads
+// q*TPP .. q*TPP+TPP-1 (KPT = 32/TPP slots each, in position order), so
+// thread order is the row's position order.  A bucket select over the
+// registers finds the k-th largest leader lo; one scan over the threads then
+// places each thread's selected leaders.  If every part stored all its keys
 // >= lo (the check of step 2 of the general path) this is the answer;
-// otherwise, and for every other row, the general path runs.
+// otherwise, and for every other row, the general path runs.  Rows of at
+// most kSelThreads/2 parts take two threads a part (half the serial work
+// per thread).
+template <int KPT>
+__device__ __forceinline__ bool topk_select_fast(const TopkArgs& a, unsigned* smem, int64_t qr,
+                                                 int np) {
+  constexpr int TPP = kTopkPartCap / KPT;   // threads per part
+  unsigned* s_key = smem;                                   // [kTopkSel + 64]
+  unsigned* s_hist = smem + kTopkSel;                       // [kHistBins]
+  int* s_idx = reinterpret_cast<int*>(s_hist + kHistBins);  // [kTopkSel + 64]
+  __shared__ int s_wave[kSelWaves];
+  __shared__ unsigned s_mm[2][kSelWaves];
+  __shared__ unsigned s_sel[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ns = a.nparts;   // part slots per row
+  const int k = a.k;
+  int32_t* topk = a.topk + qr * k;
+  float* tks = a.topk_score ? a.topk_score + qr * k : nullptr;
+  const unsigned* ck = a.cand_key + qr * (int64_t)ns * kTopkPartCap;
+  const int* ci = a.cand_idx + qr * (int64_t)ns * kTopkPartCap;
+  const int q = tid / TPP, s0 = (tid % TPP) * KPT;   // part, first slot
+  const bool own = q < np;
+  const int cpart = own ? min(a.part_cnt[qr * ns + q], kTopkPartCap) : 0;
+  const int cq = max(0, min(cpart - s0, KPT));          // this thread's stored leaders
+  const bool lead = own && s0 == 0;                     // the part's record holder
+  const unsigned tau = lead ? a.part_tau[qr * ns + q] : 0u;
+  const unsigned over = lead ? a.part_over[qr * ns + q] : 0u;
+  unsigned key[KPT];
+  int idx[KPT];
+  if (own) {
+#pragma unroll
+    for (int u = 0; u < KPT / 4; ++u) {
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(ck + q * kTopkPartCap + s0 + 4 * u);
+      const u32x4 ii = *reinterpret_cast<const u32x4*>(ci + q * kTopkPartCap + s0 + 4 * u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        key[4 * u + e] = 4 * u + e < cq ? kk[e] : 0u;
+        idx[4 * u + e] = (int)ii[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = 0u;
+  }
+  // range of the present leaders and their number
+  unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    kmin = key[j] != 0u ? min(kmin, key[j]) : kmin;
+    kmax = max(kmax, key[j]);
+  }
+  kmin = wave_min_u(kmin);
+  kmax = wave_max_u(kmax);
+  if (lane == 0) {
+    s_mm[0][wave] = kmin;
+    s_mm[1][wave] = kmax;
+  }
+  int total;
+  (void)block_excl_scan(cq, s_wave, &total);
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    kmin = min(kmin, s_mm[0][w]);
+    kmax = max(kmax, s_mm[1][w]);
+  }
+  // bucket select: the kept keys form the contiguous key range [lo, hi]
+  const bool all = total <= k;
+  unsigned lo = kmin, hi = kmax;
+  int need = all ? total : k;
+  if (!all) {
+    while (true) {
+      const unsigned span = hi - lo;
+      int shift = 0;
+      while ((span >> shift) >= (unsigned)kHistBins) ++shift;
+      const int nb = (int)(span >> shift) + 1;
+      for (int i = tid; i < nb; i += kSelThreads) s_hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (key[j] != 0u && key[j] >= lo && key[j] <= hi) atomicAdd(&s_hist[(key[j] - lo) >> shift], 1u);
+      __syncthreads();
+      int loc = 0;
+#pragma unroll
+      for (int u = 0; u < kBucketsPerThread; ++u) {
+        const int d = nb - 1 - (kBucketsPerThread * tid + u);
+        loc += d >= 0 ? (int)s_hist[d] : 0;
+      }
+      int tot;
+      int above = block_excl_scan(loc, s_wave, &tot);
+#pragma unroll
+      for (int u = 0; u < kBucketsPerThread; ++u) {
+        const int d = nb - 1 - (kBucketsPerThread * tid + u);
+        const int cnt = d >= 0 ? (int)s_hist[d] : 0;
+        if (d >= 0 && above < need && above + cnt >= need) {
+          s_sel[0] = (unsigned)d;
+          s_sel[1] = (unsigned)above;
+          s_sel[2] = (unsigned)cnt;
+        }
+        above += cnt;
+      }
+      __syncthreads();
+      const unsigned d = s_sel[0];
+      const int cnt_gt = (int)s_sel[1], cnt_eq = (int)s_sel[2];
+      __syncthreads();
+      need -= cnt_gt;
+      const unsigned nlo = lo + (d << shift);
+      const uint64_t nhi = (uint64_t)nlo + (1ull << shift) - 1u;
+      hi = nhi < (uint64_t)hi ? (unsigned)nhi : hi;
+      lo = nlo;
+      if (cnt_eq == need || lo == hi) break;
+    }
+  }
+  // per thread: keys above the bucket (key > hi_e) and in it
+  // (lo_e <= key <= hi); in-bucket keys go to the lowest positions first.
+  // With every leader kept, hi_e = 0 (present keys are >= 1) and no key is
+  // in the bucket.  Branch-free: a key that is not taken is written to a
+  // per-lane slot past the selection area.
+  const unsigned hi_e = all ? 0u : hi, lo_e = all ? 0xFFFFFFFFu : lo;
+  int ngt = 0, neq = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    ngt += key[j] > hi_e ? 1 : 0;
+    neq += (key[j] >= lo_e && key[j] <= hi) ? 1 : 0;
+  }
+  int tot;
+  const int eq_before = block_excl_scan(neq, s_wave, &tot);
+  int take = need - eq_before;
+  take = take < 0 ? 0 : (take > neq ? neq : take);
+  int pos = block_excl_scan(ngt + take, s_wave, &tot);
+  // the selection goes to LDS first (a part's slots are contiguous there),
+  // then out in coalesced rows
+  const int dummy = kTopkSel + lane;   // s_key / s_idx slots past the selection
+  unsigned smin = 0xFFFFFFFFu;
+  int taken = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool eq = key[j] >= lo_e && key[j] <= hi;
+    const bool sel = key[j] > hi_e || (eq && taken < take);
+    const int slot = sel ? pos : dummy;
+    s_key[slot] = key[j];
+    s_idx[slot] = idx[j];
+    pos += sel ? 1 : 0;
+    taken += eq ? 1 : 0;
+    smin = sel ? min(smin, key[j]) : smin;
+  }
+  smin = wave_min_u(smin);
+  if (lane == 0) s_mm[0][wave] = smin;
+  __syncthreads();
+  const int n_out = all ? total : k;
+  for (int i = tid; i < n_out; i += kSelThreads) {
+    topk[i] = s_idx[i];
+    if (tks) tks[i] = key_score(s_key[i]);
+  }
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) smin = min(smin, s_mm[0][w]);
+  const unsigned low = all ? 1u : smin;   // the k-th largest leader
+  // step 2's check
+  const int bad = (lead && (tau > low || over >= low)) ? 1 : 0;
+  int nbad;
+  (void)block_excl_scan(bad, s_wave, &nbad);
+  if (nbad == 0) {
+    for (int i = n_out + tid; i < k; i += kSelThreads) {
+      topk[i] = -1;
+      if (tks) tks[i] = -INFINITY;
+    }
+    return true;
+  }
+  __syncthreads();
+  return false;
+}
+
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   extern __shared__ unsigned smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t qr = blockIdx.x;
   const int64_t V = visible_of(a, qr);
-  const int ns = a.nparts;                                        // part slots per row
   const int np = V > a.direct_max ? (int)((V + topk_part_len(V, a.k) - 1) / topk_part_len(V, a.k)) : 0;
-  if (V > a.direct_max && np <= kSelThreads) {
-    unsigned* s_key = smem;                                   // [kTopkSel + 64]
-    unsigned* s_hist = smem + kTopkSel;                       // [kHistBins]
-    int* s_idx = reinterpret_cast<int*>(s_hist + kHistBins);  // [kTopkSel + 64]
-    __shared__ int s_wave[kSelWaves];
-    __shared__ unsigned s_mm[2][kSelWaves];
-    __shared__ unsigned s_sel[4];
-    const int k = a.k;
-    int32_t* topk = a.topk + qr * k;
-    float* tks = a.topk_score ? a.topk_score + qr * k : nullptr;
-    const unsigned* ck = a.cand_key + qr * (int64_t)ns * kTopkPartCap;
-    const int* ci = a.cand_idx + qr * (int64_t)ns * kTopkPartCap;
-    const int q = tid;
-    const bool own = q < np;
-    const int cq = own ? min(a.part_cnt[qr * ns + q], kTopkPartCap) : 0;
-    const unsigned tau = own ? a.part_tau[qr * ns + q] : 0u;
-    const unsigned over = own ? a.part_over[qr * ns + q] : 0u;
-    unsigned key[kTopkPartCap];
-    int idx[kTopkPartCap];
-    if (own) {
-#pragma unroll
-      for (int u = 0; u < kTopkPartCap / 4; ++u) {
-        const u32x4 kk = *reinterpret_cast<const u32x4*>(ck + q * kTopkPartCap + 4 * u);
-        const u32x4 ii = *reinterpret_cast<const u32x4*>(ci + q * kTopkPartCap + 4 * u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          key[4 * u + e] = 4 * u + e < cq ? kk[e] : 0u;
-          idx[4 * u + e] = (int)ii[e];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kTopkPartCap; ++j) key[j] = 0u;
-    }
-    // range of the present leaders and their number
-    unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-    for (int j = 0; j < kTopkPartCap; ++j) {
-      kmin = key[j] != 0u ? min(kmin, key[j]) : kmin;
-      kmax = max(kmax, key[j]);
-    }
-    kmin = wave_min_u(kmin);
-    kmax = wave_max_u(kmax);
-    if (lane == 0) {
-      s_mm[0][wave] = kmin;
-      s_mm[1][wave] = kmax;
-    }
-    int total;
-    (void)block_excl_scan(cq, s_wave, &total);
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) {
-      kmin = min(kmin, s_mm[0][w]);
-      kmax = max(kmax, s_mm[1][w]);
-    }
-    // bucket select: the kept keys form the contiguous key range [lo, hi]
-    const bool all = total <= k;
-    unsigned lo = kmin, hi = kmax;
-    int need = all ? total : k;
-    if (!all) {
-      while (true) {
-        const unsigned span = hi - lo;
-        int shift = 0;
-        while ((span >> shift) >= (unsigned)kHistBins) ++shift;
-        const int nb = (int)(span >> shift) + 1;
-        for (int i = tid; i < nb; i += kSelThreads) s_hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kTopkPartCap; ++j)
-          if (key[j] != 0u && key[j] >= lo && key[j] <= hi) atomicAdd(&s_hist[(key[j] - lo) >> shift], 1u);
-        __syncthreads();
-        int loc = 0;
-#pragma unroll
-        for (int u = 0; u < kBucketsPerThread; ++u) {
-          const int d = nb - 1 - (kBucketsPerThread * tid + u);
-          loc += d >= 0 ? (int)s_hist[d] : 0;
-        }
-        int tot;
-        int above = block_excl_scan(loc, s_wave, &tot);
-#pragma unroll
-        for (int u = 0; u < kBucketsPerThread; ++u) {
-          const int d = nb - 1 - (kBucketsPerThread * tid + u);
-          const int cnt = d >= 0 ? (int)s_hist[d] : 0;
-          if (d >= 0 && above < need && above + cnt >= need) {
-            s_sel[0] = (unsigned)d;
-            s_sel[1] = (unsigned)above;
-            s_sel[2] = (unsigned)cnt;
-          }
-          above += cnt;
-        }
-        __syncthreads();
-        const unsigned d = s_sel[0];
-        const int cnt_gt = (int)s_sel[1], cnt_eq = (int)s_sel[2];
-        __syncthreads();
-        need -= cnt_gt;
-        const unsigned nlo = lo + (d << shift);
-        const uint64_t nhi = (uint64_t)nlo + (1ull << shift) - 1u;
-        hi = nhi < (uint64_t)hi ? (unsigned)nhi : hi;
-        lo = nlo;
-        if (cnt_eq == need || lo == hi) break;
-      }
-    }
-    // per part: keys above the bucket (key > hi_e) and in it
-    // (lo_e <= key <= hi); in-bucket keys go to the lowest positions first.
-    // With every leader kept, hi_e = 0 (present keys are >= 1) and no key is
-    // in the bucket.  Branch-free: a key that is not taken is written to a
-    // per-lane slot past the selection area (in the histogram, unused now).
-    const unsigned hi_e = all ? 0u : hi, lo_e = all ? 0xFFFFFFFFu : lo;
-    int ngt = 0, neq = 0;
-#pragma unroll
-    for (int j = 0; j < kTopkPartCap; ++j) {
-      ngt += key[j] > hi_e ? 1 : 0;
-      neq += (key[j] >= lo_e && key[j] <= hi) ? 1 : 0;
-    }
-    int tot;
-    const int eq_before = block_excl_scan(neq, s_wave, &tot);
-    int take = need - eq_before;
-    take = take < 0 ? 0 : (take > neq ? neq : take);
-    int pos = block_excl_scan(ngt + take, s_wave, &tot);
-    // the selection goes to LDS first (a part's slots are contiguous there),
-    // then out in coalesced rows
-    const int dummy = kTopkSel + lane;   // s_key / s_idx slots past the selection
-    unsigned smin = 0xFFFFFFFFu;
-    int taken = 0;
-#pragma unroll
-    for (int j = 0; j < kTopkPartCap; ++j) {
-      const bool eq = key[j] >= lo_e && key[j] <= hi;
-      const bool sel = key[j] > hi_e || (eq && taken < take);
-      const int slot = sel ? pos : dummy;
-      s_key[slot] = key[j];
-      s_idx[slot] = idx[j];
-      pos += sel ? 1 : 0;
-      taken += eq ? 1 : 0;
-      smin = sel ? min(smin, key[j]) : smin;
-    }
-    smin = wave_min_u(smin);
-    if (lane == 0) s_mm[0][wave] = smin;
-    __syncthreads();
-    const int n_out = all ? total : k;
-    for (int i = tid; i < n_out; i += kSelThreads) {
-      topk[i] = s_idx[i];
-      if (tks) tks[i] = key_score(s_key[i]);
-    }
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) smin = min(smin, s_mm[0][w]);
-    const unsigned low = all ? 1u : smin;   // the k-th largest leader
-    // step 2's check
-    const int bad = (own && (tau > low || over >= low)) ? 1 : 0;
-    int nbad;
-    (void)block_excl_scan(bad, s_wave, &nbad);
-    if (nbad == 0) {
-      for (int i = n_out + tid; i < k; i += kSelThreads) {
-        topk[i] = -1;
-        if (tks) tks[i] = -INFINITY;
-      }
-      return;
-    }
-    __syncthreads();
+  if (V > a.direct_max && np <= kSelThreads / 2) {
+    if (topk_select_fast<kTopkPartCap / 2>(a, smem, qr, np)) return;
+  } else if (V > a.direct_max && np <= kSelThreads) {
+    if (topk_select_fast<kTopkPartCap>(a, smem, qr, np)) return;
   }
   topk_select_general(a, smem);
 }
