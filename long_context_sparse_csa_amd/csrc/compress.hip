@@ -45,19 +45,65 @@ __device__ __forceinline__ void load_bf16_row(const uint16_t* p, float (&x)[VPL]
   }
 }
 
-// y holds this lane's VPL channels (lane*VPL ..) of an RMSNorm'd row.  Rotate
-// the channels that fall in the last R dims by position `pos` and store the
-// packed row: E4M3 for channels < D-R, bf16 for the rest.
+// A lane's VPL bf16 channels of a row as they are loaded (one 4, 8 or 16
+// byte load), converted to fp32 when used.
+template <int VPL> struct RawRow;
+template <> struct RawRow<8> {
+  using T = u32x4;
+  __device__ static void to_f32(const T& w, float (&x)[8]) {
+    const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(ws[i] & 0xFFFFu);
+      x[2 * i + 1] = bf16_bits_to_f32(ws[i] >> 16);
+    }
+  }
+};
+template <> struct RawRow<4> {
+  using T = u32x2;
+  __device__ static void to_f32(const T& w, float (&x)[4]) {
+    x[0] = bf16_bits_to_f32(w.x & 0xFFFFu);
+    x[1] = bf16_bits_to_f32(w.x >> 16);
+    x[2] = bf16_bits_to_f32(w.y & 0xFFFFu);
+    x[3] = bf16_bits_to_f32(w.y >> 16);
+  }
+};
+template <> struct RawRow<2> {
+  using T = unsigned;
+  __device__ static void to_f32(const T& w, float (&x)[2]) {
+    x[0] = bf16_bits_to_f32(w & 0xFFFFu);
+    x[1] = bf16_bits_to_f32(w >> 16);
+  }
+};
+
+// (cos, sin) of the rotary pairs among this lane's VPL channels (lane*VPL ..)
+// at position `pos` (lanes without rotary channels get (1, 0)).
 template <int VPL>
-__device__ __forceinline__ void rotate_and_pack(uint8_t* row, float (&y)[VPL], int lane, int R,
-                                                int64_t pos, const RopeTurns& rope) {
+__device__ __forceinline__ void lane_rope(int lane, int R, int64_t pos, const RopeTurns& rope,
+                                          float (&cs)[VPL / 2], float (&sn)[VPL / 2]) {
+  constexpr int D = VPL * 64;
+  const int d0 = lane * VPL;
+#pragma unroll
+  for (int v = 0; v < VPL; v += 2) {
+    cs[v / 2] = 1.f;
+    sn[v / 2] = 0.f;
+    if (d0 >= D - R) rope_cos_sin(pos, rope.t[(d0 + v - (D - R)) >> 1], &cs[v / 2], &sn[v / 2]);
+  }
+}
+
+// y holds this lane's VPL channels (lane*VPL ..) of an RMSNorm'd row.  Rotate
+// the channels that fall in the last R dims by the given (cos, sin) of their
+// pairs and store the packed row: E4M3 for channels < D-R, bf16 for the rest.
+template <int VPL>
+__device__ __forceinline__ void rotate_and_pack_cs(uint8_t* row, float (&y)[VPL], int lane, int R,
+                                                   const float (&cs)[VPL / 2],
+                                                   const float (&sn)[VPL / 2]) {
   constexpr int D = VPL * 64;
   const int d0 = lane * VPL;
   if (d0 >= D - R) {
 #pragma unroll
     for (int v = 0; v < VPL; v += 2) {
-      float c, s;
-      rope_cos_sin(pos, rope.t[(d0 + v - (D - R)) >> 1], &c, &s);
+      const float c = cs[v / 2], s = sn[v / 2];
       float a = y[v], b = y[v + 1];
       y[v] = a * c - b * s;
       y[v + 1] = a * s + b * c;
@@ -85,6 +131,15 @@ __device__ __forceinline__ void rotate_and_pack(uint8_t* row, float (&y)[VPL], i
       *reinterpret_cast<unsigned short*>(dst) = (unsigned short)pack_fp8x2(y[0], y[1]);
     }
   }
+}
+
+// As rotate_and_pack_cs, with the rotation of position `pos`.
+template <int VPL>
+__device__ __forceinline__ void rotate_and_pack(uint8_t* row, float (&y)[VPL], int lane, int R,
+                                                int64_t pos, const RopeTurns& rope) {
+  float cs[VPL / 2], sn[VPL / 2];
+  lane_rope<VPL>(lane, R, pos, rope, cs, sn);
+  rotate_and_pack_cs<VPL>(row, y, lane, R, cs, sn);
 }
 
 // RMSNorm of a row held as VPL channels per lane across one wave.
@@ -124,21 +179,41 @@ __device__ __forceinline__ void pool_entry(
   const int64_t r0 = plo - raw_pos0;           // raw row of plo
   const float* srow = score + (int64_t)b * L + r0;
 
-  // rows in batches of U per wave, all loads of a batch in flight together
-  // (loads are unconditional -- rows past the window re-read the last row
-  // with weight 0 -- so the compiler keeps the whole batch in flight); the
-  // first batch is issued before the weights are formed
-  constexpr int U = 64 / VPL;
+  // Every load the entry needs goes out first, before any barrier: the rows
+  // this wave pools (rows wave, wave + 16, .., as packed bf16, U at a time)
+  // and the first of its token indexer keys; wave 0, which packs the row,
+  // also works out the rotation of the entry's position.  The row loads are
+  // unconditional (past the window they re-read the last row, weighted 0), so
+  // the whole batch stays in flight.
+  constexpr int U = VPL >= 8 ? 8 : 16;   // 32 registers of rows in flight
+  using Raw = typename RawRow<VPL>::T;
   const uint16_t* base = raw + ((int64_t)b * L + r0) * D + lane * VPL;
-  float x[U][VPL];
+  Raw x[U];
   auto load_batch = [&](int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = min(t0 + kPoolWaves * u, nw - 1);
-      load_bf16_row<VPL>(base + (int64_t)t * D, x[u]);
+      x[u] = *reinterpret_cast<const Raw*>(base + (int64_t)t * D);
     }
   };
   load_batch(wave);
+  const uint16_t* kb = kidx_row ? raw_idx + ((int64_t)b * L + r0) * dI : nullptr;
+  uint16_t k0[2] = {0, 0};   // the key dims lane, lane + 64 of row `wave`
+  if (kb && wave < nw) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (lane + 64 * h < dI) k0[h] = kb[(int64_t)wave * dI + lane + 64 * h];
+  }
+  __shared__ float s_rot[2][D / 2];   // (cos, sin) per channel pair, kept in LDS
+  if (wave == 0) {
+    float cs[VPL / 2], sn[VPL / 2];
+    lane_rope<VPL>(lane, R, j * (int64_t)m, rope, cs, sn);
+#pragma unroll
+    for (int v = 0; v < VPL / 2; ++v) {
+      s_rot[0][lane * (VPL / 2) + v] = cs[v];
+      s_rot[1][lane * (VPL / 2) + v] = sn[v];
+    }
+  }
 
   // weights alpha_t = softmax over the window of (s_t + b_{t - wlo})
   float mx = -INFINITY;
@@ -176,8 +251,10 @@ __device__ __forceinline__ void pool_entry(
     for (int u = 0; u < U; ++u) {
       const int t = t0 + kPoolWaves * u;
       const float a = t < nw ? s_alpha[t] : 0.f;
+      float xf[VPL];
+      RawRow<VPL>::to_f32(x[u], xf);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, x[u][v], acc[v]);
+      for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, xf[v], acc[v]);
     }
     t0 += kPoolWaves * U;
     if (t0 >= nw) break;
@@ -190,12 +267,14 @@ __device__ __forceinline__ void pool_entry(
     // the entry's indexer key: the token indexer keys pooled with the same
     // weights (no norm, no rotation), bf16; wave w takes rows w, w+16, ..
     __shared__ float s_kp[kPoolWaves][128];
-    const uint16_t* kb = raw_idx + ((int64_t)b * L + r0) * dI;
-    for (int d = lane; d < 128; d += 64) {
+    for (int h = 0; h < 2; ++h) {
+      const int d = lane + 64 * h;
       float z = 0.f;
-      if (d < dI)
-        for (int t = wave; t < nw; t += kPoolWaves)
+      if (d < dI) {
+        if (wave < nw) z = s_alpha[wave] * __uint_as_float((uint32_t)k0[h] << 16);
+        for (int t = wave + kPoolWaves; t < nw; t += kPoolWaves)
           z = fmaf(s_alpha[t], __uint_as_float((uint32_t)kb[(int64_t)t * dI + d] << 16), z);
+      }
       s_kp[wave][d] = z;
     }
     __syncthreads();
@@ -218,7 +297,13 @@ __device__ __forceinline__ void pool_entry(
     y[v] = z * inv;
   }
   rmsnorm_wave<VPL>(y, gamma, lane, eps);
-  rotate_and_pack<VPL>(row, y, lane, R, j * (int64_t)m, rope);
+  float cs[VPL / 2], sn[VPL / 2];
+#pragma unroll
+  for (int v = 0; v < VPL / 2; ++v) {
+    cs[v] = s_rot[0][lane * (VPL / 2) + v];
+    sn[v] = s_rot[1][lane * (VPL / 2) + v];
+  }
+  rotate_and_pack_cs<VPL>(row, y, lane, R, cs, sn);
 }
 
 template <int VPL>

@@ -156,9 +156,9 @@ _ARRAY_TYPES = {}
 
 def _int64_array(n):
     """The ctypes type int64[n], made once per n: a new array type per call
-    is a class object with reference cycles, and the garbage it leaves sets
-    off the interpreter's full garbage collections (tens of milliseconds
-    each, inside whatever loop is launching)."""
+    is a class object with reference cycles, and cyclic garbage sets off the
+    interpreter's full garbage collections (tens of milliseconds each, inside
+    whatever loop is launching)."""
     t = _ARRAY_TYPES.get(n)
     if t is None:
         t = _ARRAY_TYPES[n] = _c.c_int64 * n
@@ -186,7 +186,9 @@ def _seq_pos(seq_pos, B, q_pos0):
     if len(sp) != B:
         raise ValueError(f"seq_pos has {len(sp)} positions for {B} sequences")
     arr = _int64_array(max(B, 1))(*sp)
-    return arr, _c.cast(arr, _c.c_void_p), max(sp) if sp else int(q_pos0 or 0)
+    # the address, not ctypes.cast (which ties the two objects in a reference
+    # cycle); the caller keeps arr alive for the call
+    return arr, _c.c_void_p(_c.addressof(arr)), max(sp) if sp else int(q_pos0 or 0)
 
 
 def _workspace(nbytes, device, ws):
@@ -304,7 +306,7 @@ def compress_steps(layers):
         d.entries, d.ent_rows, d.win, d.win_rows = (ent.data_ptr(), ent.shape[1], win.data_ptr(),
                                                     win.shape[1])
         d.win_row, d.raw_idx, d.dI, d.k_idx = int(win_row), ri, dI, kp
-    check(lib().v4attn_compress_steps(_c.cast(descs, _c.c_void_p), len(layers),
+    check(lib().v4attn_compress_steps(_c.c_void_p(_c.addressof(descs)), len(layers),
                                       _stream(layers[0]["raw"])))
 
 
