@@ -15,34 +15,23 @@
 // contiguous channels (coalesced 16-byte loads at D = 512, eight rows in
 // flight per wave, so a 256-row window is two rounds of loads), the partial
 // sums meet in LDS and wave 0 normalises, rotates and packs the 576-byte row.
-// Each entry depends only on its own window, so streaming (one entry per
-// call) and batch calls produce identical bytes.
+// A window row is one wave's work, with the row, gamma and the rotary turn
+// all requested before any is used.  Each entry depends only on its own
+// window, so streaming (one entry per call) and batch calls produce
+// identical bytes.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace v4 {
 
-template <int VPL>
-__device__ __forceinline__ void load_bf16_row(const uint16_t* p, float (&x)[VPL]) {
-  if constexpr (VPL == 8) {
-    u32x4 w = *reinterpret_cast<const u32x4*>(p);
-    unsigned ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16_bits_to_f32(ws[i] & 0xFFFFu);
-      x[2 * i + 1] = bf16_bits_to_f32(ws[i] >> 16);
-    }
-  } else if constexpr (VPL == 4) {
-    u32x2 w = *reinterpret_cast<const u32x2*>(p);
-    x[0] = bf16_bits_to_f32(w.x & 0xFFFFu);
-    x[1] = bf16_bits_to_f32(w.x >> 16);
-    x[2] = bf16_bits_to_f32(w.y & 0xFFFFu);
-    x[3] = bf16_bits_to_f32(w.y >> 16);
-  } else {
-    unsigned w = *reinterpret_cast<const unsigned*>(p);
-    x[0] = bf16_bits_to_f32(w & 0xFFFFu);
-    x[1] = bf16_bits_to_f32(w >> 16);
-  }
+// A raw buffer resource over the n bytes at p (a load at an offset past n
+// returns 0 and touches no memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
 // A lane's VPL bf16 channels of a row as they are loaded (one 4, 8 or 16
@@ -50,6 +39,9 @@ __device__ __forceinline__ void load_bf16_row(const uint16_t* p, float (&x)[VPL]
 template <int VPL> struct RawRow;
 template <> struct RawRow<8> {
   using T = u32x4;
+  __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  }
   __device__ static void to_f32(const T& w, float (&x)[8]) {
     const unsigned ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -61,6 +53,10 @@ template <> struct RawRow<8> {
 };
 template <> struct RawRow<4> {
   using T = u32x2;
+  __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return u32x2{v[0], v[1]};
+  }
   __device__ static void to_f32(const T& w, float (&x)[4]) {
     x[0] = bf16_bits_to_f32(w.x & 0xFFFFu);
     x[1] = bf16_bits_to_f32(w.x >> 16);
@@ -70,6 +66,9 @@ template <> struct RawRow<4> {
 };
 template <> struct RawRow<2> {
   using T = unsigned;
+  __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
   __device__ static void to_f32(const T& w, float (&x)[2]) {
     x[0] = bf16_bits_to_f32(w & 0xFFFFu);
     x[1] = bf16_bits_to_f32(w >> 16);
@@ -133,15 +132,6 @@ __device__ __forceinline__ void rotate_and_pack_cs(uint8_t* row, float (&y)[VPL]
   }
 }
 
-// As rotate_and_pack_cs, with the rotation of position `pos`.
-template <int VPL>
-__device__ __forceinline__ void rotate_and_pack(uint8_t* row, float (&y)[VPL], int lane, int R,
-                                                int64_t pos, const RopeTurns& rope) {
-  float cs[VPL / 2], sn[VPL / 2];
-  lane_rope<VPL>(lane, R, pos, rope, cs, sn);
-  rotate_and_pack_cs<VPL>(row, y, lane, R, cs, sn);
-}
-
 // RMSNorm of a row held as VPL channels per lane across one wave.
 template <int VPL>
 __device__ __forceinline__ void rmsnorm_wave(float (&y)[VPL], const float* __restrict__ gamma,
@@ -154,6 +144,44 @@ __device__ __forceinline__ void rmsnorm_wave(float (&y)[VPL], const float* __res
   const float rs = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
   for (int v = 0; v < VPL; ++v) y[v] = gamma[lane * VPL + v] * (y[v] * rs);
+}
+
+// One wave packs one window row: the raw bf16 row at src, RMSNorm'd with
+// gamma, its last R channels rotated at position pos, stored at dst.  The
+// row, gamma and the rotary turns are all requested before any is used.
+template <int VPL>
+__device__ __forceinline__ void pack_row_wave(const uint16_t* src, const float* gamma,
+                                              uint8_t* dst, int64_t pos, const RopeTurns& rope,
+                                              int R, float eps, int lane) {
+  constexpr int D = VPL * 64;
+  using Raw = typename RawRow<VPL>::T;
+  const double tv = rope.t[lane & 31];   // pair lane mod 32's turns per position
+  const Raw w = RawRow<VPL>::load(buf_rsrc(src, D * 2), lane * VPL * 2);
+  const __amdgpu_buffer_rsrc_t rs_g = buf_rsrc(gamma, D * 4);
+  float g[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) g[v] = buf_f32(rs_g, (lane * VPL + v) * 4);
+  float y[VPL];
+  RawRow<VPL>::to_f32(w, y);
+  float ss = 0.f;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) ss += y[v] * y[v];
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) y[v] = g[v] * (y[v] * rs);
+  // lane i < R/2 rotates pair i; the lanes holding the pair's channels fetch it
+  float c0, s0;
+  rope_cos_sin(pos, tv, &c0, &s0);
+  float cs[VPL / 2], sn[VPL / 2];
+#pragma unroll
+  for (int v = 0; v < VPL; v += 2) {
+    const int pr = (lane * VPL + v - (D - R)) >> 1;
+    const float c = __shfl(c0, pr & 63), sv = __shfl(s0, pr & 63);
+    cs[v / 2] = pr >= 0 ? c : 1.f;
+    sn[v / 2] = pr >= 0 ? sv : 0.f;
+  }
+  rotate_and_pack_cs<VPL>(dst, y, lane, R, cs, sn);
 }
 
 constexpr int kPoolThreads = 1024;   // sixteen waves pool one entry's window
@@ -331,55 +359,81 @@ __global__ __launch_bounds__(256) void compress_pack_kernel(
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n_out) return;
-  float y[VPL];
-  load_bf16_row<VPL>(raw + ((int64_t)b * L + r) * D + lane * VPL, y);
-  rmsnorm_wave<VPL>(y, gamma, lane, eps);
-  uint8_t* row = out + ((int64_t)b * out_rows + r) * (D + R);
-  rotate_and_pack<VPL>(row, y, lane, R, raw_pos0 + r, rope);
+  pack_row_wave<VPL>(raw + ((int64_t)b * L + r) * D, gamma,
+                     out + ((int64_t)b * out_rows + r) * (D + R), raw_pos0 + r, rope, R, eps, lane);
 }
 
-// One decode step of the compressor: block 0 of each sequence pools the entry
-// the new token completes (if any), the last block packs the token's window
-// row; both run side by side in one launch.
-// One decode step of one or more layers' compressors (grid layer z runs
-// layer z): block 0 of each sequence pools the entry its token completes
-// (if any), the last block packs the token's window row.
+// One decode step of one or more layers' compressors.  Workgroup (b, k, 0)
+// pools the entry that sequence b's token completes in the k-th layer in
+// launch order (if it completes one), workgroup (b, k, 1) packs the token's
+// window row (wave 0; the grid is one deep when no token completes an entry).
+// The host puts the layers with the longest windows first and the pooling
+// workgroups go out before the window rows: they take the longest.
 template <int VPL>
 __global__ __launch_bounds__(kPoolThreads) void compress_step_kernel(CompressStepBatch bt) {
   constexpr int D = VPL * 64;
-  const CompressStepArgs& a = bt.s[blockIdx.z];
-  const int b = blockIdx.y;
-  if (b >= a.B) return;   // a layer with fewer sequences than the grid
+  const CompressStepArgs& a = bt.s[blockIdx.y];
+  const int b = blockIdx.x;
+  const bool win_block = blockIdx.z == gridDim.z - 1;
+  // every argument read up front, before any branch, so the reads go out
+  // together (each round trip to the argument segment costs a memory
+  // latency; the empty asm keeps the compiler from sinking them into the
+  // branches that use them)
+  const int B = a.B, L = a.L, m = a.m, R = a.R, dI = a.dI;
+  const bool ragged = a.ragged;
+  const int64_t pb = a.pos.p[b & (kMaxRagged - 1)];
+  const uint16_t* raw = a.raw;
+  const float* tok_score = a.tok_score;
+  const float* pos_bias = a.pos_bias;
+  const uint16_t* raw_idx = a.raw_idx;
+  uint16_t* kidx = a.kidx;
+  uint8_t* win = a.win;
+  uint8_t* ent = a.ent;
+  const int64_t win_rows = a.win_rows, win_row = a.win_row, ent_rows = a.ent_rows;
+  const float* gamma = a.gamma;
+  const float eps = a.eps;
   int64_t t = a.t, raw_pos0 = a.raw_pos0;
-  if (a.ragged) {   // this sequence's token; its raw rows end at it
-    t = a.pos.p[b];
-    raw_pos0 = t - a.L + 1;
+  asm volatile("" ::"s"(raw), "s"(tok_score), "s"(pos_bias), "s"(raw_idx), "s"(kidx), "s"(win),
+               "s"(ent), "s"(gamma), "s"(pb), "s"(t), "s"(raw_pos0), "s"(win_rows), "s"(win_row),
+               "s"(ent_rows));
+  asm volatile("" ::"s"(B), "s"(L), "s"(m), "s"(R), "s"(dI), "s"(eps), "s"((int)ragged));
+  if (b >= B) return;   // a layer with fewer sequences than the grid
+  if (ragged) {   // this sequence's token; its raw rows end at it (b < kMaxRagged)
+    t = pb;
+    raw_pos0 = t - L + 1;
   }
-  if (blockIdx.x == 0 && gridDim.x == 2 && (t + 1) % a.m != 0) return;   // no entry completes
-  if (blockIdx.x == gridDim.x - 1) {
+  if (win_block) {
     if (threadIdx.x >= 64) return;
-    const int lane = threadIdx.x;
-    float y[VPL];
-    load_bf16_row<VPL>(a.raw + ((int64_t)b * a.L + (t - raw_pos0)) * D + lane * VPL, y);
-    rmsnorm_wave<VPL>(y, a.gamma, lane, a.eps);
-    rotate_and_pack<VPL>(a.win + ((int64_t)b * a.win_rows + a.win_row) * (D + a.R), y, lane, a.R, t,
-                         a.rope);
+    pack_row_wave<VPL>(raw + ((int64_t)b * L + (t - raw_pos0)) * D, gamma,
+                       win + ((int64_t)b * win_rows + win_row) * (D + R), t, a.rope, R, eps,
+                       threadIdx.x);
     return;
   }
-  const int64_t j = (t + 1) / a.m - 1;
-  pool_entry<VPL>(a.raw, a.tok_score, a.pos_bias, a.gamma, a.L, a.R, raw_pos0, a.m, j, b, a.eps,
-                  a.rope, a.ent + ((int64_t)b * a.ent_rows + j) * (D + a.R), a.raw_idx, a.dI,
-                  a.kidx ? a.kidx + ((int64_t)b * a.ent_rows + j) * a.dI : nullptr);
+  // t + 1 = (j + 1) m + r (positions below 2^31 take the 32-bit division)
+  int64_t j1;
+  int r;
+  if ((uint64_t)(t + 1) < (1ull << 31)) {
+    j1 = (uint32_t)(t + 1) / (uint32_t)m;
+    r = (int)((uint32_t)(t + 1) - (uint32_t)j1 * (uint32_t)m);
+  } else {
+    j1 = (t + 1) / m;
+    r = (int)((t + 1) - j1 * m);
+  }
+  if (r != 0) return;   // no entry completes
+  const int64_t j = j1 - 1;
+  pool_entry<VPL>(raw, tok_score, pos_bias, gamma, L, R, raw_pos0, m, j, b, eps, a.rope,
+                  ent + ((int64_t)b * ent_rows + j) * (D + R), raw_idx, dI,
+                  kidx ? kidx + ((int64_t)b * ent_rows + j) * dI : nullptr);
 }
 
 hipError_t launch_compress_steps(const CompressStepArgs* a, int n, hipStream_t st) {
   if (n < 1 || n > kMaxSteps) return hipErrorInvalidValue;
-  CompressStepBatch bt{};
-  bool pool = false;
+  int order[kMaxSteps];
   int maxB = 0;
+  bool pool = false;
   for (int z = 0; z < n; ++z) {
     if (a[z].D != a[0].D) return hipErrorInvalidValue;   // one kernel instance
-    bt.s[z] = a[z];
+    order[z] = z;
     maxB = a[z].B > maxB ? a[z].B : maxB;
     if (a[z].ragged) {
       for (int b = 0; b < a[z].B; ++b) pool = pool || (a[z].pos.p[b] + 1) % a[z].m == 0;
@@ -388,7 +442,16 @@ hipError_t launch_compress_steps(const CompressStepArgs* a, int n, hipStream_t s
     }
   }
   if (maxB == 0) return hipSuccess;
-  dim3 grid(pool ? 2 : 1, maxB, n);
+  // longest pooling windows first: they take the longest
+  for (int i = 1; i < n; ++i)
+    for (int k = i; k > 0 && a[order[k]].m > a[order[k - 1]].m; --k) {
+      const int tmp = order[k];
+      order[k] = order[k - 1];
+      order[k - 1] = tmp;
+    }
+  CompressStepBatch bt{};
+  for (int k = 0; k < n; ++k) bt.s[k] = a[order[k]];
+  const dim3 grid((unsigned)maxB, (unsigned)n, pool ? 2u : 1u);
 #define V4_STEP(VPL) compress_step_kernel<VPL><<<grid, kPoolThreads, 0, st>>>(bt)
   switch (a[0].D) {
     case 128: V4_STEP(2); break;

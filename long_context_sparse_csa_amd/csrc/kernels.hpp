@@ -64,7 +64,7 @@ hipError_t launch_compress_step(const CompressStepArgs& a, hipStream_t st);
 // Several layers' decode steps (same D) in one launch.
 constexpr int kMaxSteps = 2;   // the arguments of every layer travel in the kernel arguments
 struct CompressStepBatch {
-  CompressStepArgs s[kMaxSteps];
+  CompressStepArgs s[kMaxSteps];   // in launch order
 };
 hipError_t launch_compress_steps(const CompressStepArgs* a, int n, hipStream_t st);
 
