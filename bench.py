@@ -57,11 +57,11 @@ COPY_BYTES = 1 << 30           # calibration copy for the HBM byte counters
 # HBM bytes of one index_score launch at the decode shape, from two
 # rocprofv3 --pmc passes over `bench.py --counters` (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
-# for torch's elementwise kernel over 1 GiB in and 1 GiB out (FETCH 524,319
+# for torch's elementwise kernel over 1 GiB in and 1 GiB out (FETCH 524,321
 # KiB -> x2.0; WRITE 1,048,576 KiB -> x1.0).  Valid only for the kernel
 # sources they were taken with (hash below); otherwise reported as null.
-TRAFFIC = {"sources_sha256_16": "bfeba9f6fe104e16",
-           "fetch_kib": 262708.2, "fetch_scale": 2.0,
+TRAFFIC = {"sources_sha256_16": "1c36a3067db23e74",
+           "fetch_kib": 262707.6, "fetch_scale": 2.0,
            "write_kib": 8192.0, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("long_context_sparse_csa_amd/csrc/indexer.hip",
                    "long_context_sparse_csa_amd/csrc/common.hpp")
@@ -812,6 +812,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the two-stream and HIP-graph timings of the step (a profile of the "
+                         "one-stream launches alone)")
     ap.add_argument("--no-extra-decode", action="store_true",
                     help="skip the 128K CSA layer and the alternating layer stack")
     ap.add_argument("--cpu-seconds", type=float, default=30.0)
@@ -944,16 +947,17 @@ def main():
     # compress steps in one launch, the HCA attention on a second stream
     # beside the CSA indexer, top-k and attention (not open to a dependent
     # stack, where each layer waits for the previous one)
-    ms2, _ = run_timed_concurrent(st, args.rotate, args.steps, args.warmup)
-    msg, _ = run_timed_graphs(st, args.rotate, args.steps, args.warmup)
-    res["two_stream_overlap"] = {
-        "what": "independent CSA and HCA batches overlapped on two streams (both compress steps "
-                "in one launch, HCA attention beside the CSA chain)",
-        "step_us": round(ms2 * 1e3, 2),
-        "query_token_layers_per_s": round((c.B + h.B) / (ms2 * 1e-3), 1),
-        "hip_graph_replay_step_us": round(msg * 1e3, 2),
-    }
-    log("two-stream overlap: " + json.dumps(res["two_stream_overlap"]))
+    if not args.no_overlap:
+        ms2, _ = run_timed_concurrent(st, args.rotate, args.steps, args.warmup)
+        msg, _ = run_timed_graphs(st, args.rotate, args.steps, args.warmup)
+        res["two_stream_overlap"] = {
+            "what": "independent CSA and HCA batches overlapped on two streams (both compress "
+                    "steps in one launch, HCA attention beside the CSA chain)",
+            "step_us": round(ms2 * 1e3, 2),
+            "query_token_layers_per_s": round((c.B + h.B) / (ms2 * 1e-3), 1),
+            "hip_graph_replay_step_us": round(msg * 1e3, 2),
+        }
+        log("two-stream overlap: " + json.dumps(res["two_stream_overlap"]))
     if not args.no_extra_decode:
         log("csa decode 128k")
         res["csa_decode_128k"] = csa_128k_section(dev, args.steps)

@@ -86,7 +86,7 @@ size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 TopkWs topk_ws(int B, int Tq, int64_t n_entries, int64_t q_pos0, int m, int k) {
   TopkWs w;
   const int64_t vmax = vmax_of(Tq, n_entries, q_pos0, m);
-  w.plan = v4::topk_plan(vmax, k);
+  w.plan = v4::topk_plan(0, vmax, k);   // any row length up to vmax
   const int64_t rows = (int64_t)B * Tq;
   const int64_t np = w.plan.nparts;
   w.part_bytes = align256((size_t)(rows * np) * sizeof(int));
@@ -430,8 +430,14 @@ hipError_t run_topk(const float* scores, int64_t stride, int B, int Tq, int64_t 
   ta.q_pos0 = q_pos0;
   ta.m = m;
   ta.k = k;
-  ta.direct_max = w.plan.direct_max;
-  ta.nparts = w.plan.nparts;
+  // the launch's own rows: visible counts from the first query of the
+  // earliest sequence to vmax (part slots at most the workspace's)
+  int64_t vmin = min64(n_entries, (q_pos0 + 1) / m);
+  if (sp)
+    for (int b = 0; b < B; ++b) vmin = std::min(vmin, min64(n_entries, (sp->p[b] + 1) / m));
+  const v4::TopkPlan plan = v4::topk_plan(vmin, vmax_of(Tq, n_entries, q_pos0, m), k);
+  ta.direct_max = plan.direct_max;
+  ta.nparts = plan.nparts;
   ta.part_tau = ta.part_over = nullptr;
   ta.part_cnt = nullptr;
   ta.cand_key = ta.run_key = nullptr;
@@ -447,7 +453,7 @@ hipError_t run_topk(const float* scores, int64_t stride, int B, int Tq, int64_t 
   }
   ta.topk = topk;
   ta.topk_score = topk_score;
-  return v4::launch_topk(ta, w.plan, st);
+  return v4::launch_topk(ta, plan, st);
 }
 
 int check_score_fp8_args(const uint8_t* q8, const float* q_scale, const float* w_idx,

@@ -150,7 +150,9 @@ struct TopkPlan {
   bool parts;          // longer rows exist: run the part kernel
   int nparts;          // part slots per row (the most any row of the launch has)
 };
-TopkPlan topk_plan(int64_t vmax, int k);
+// The plan for rows of vmin .. vmax visible entries (part slots for the most
+// parts any length in that range takes).
+TopkPlan topk_plan(int64_t vmin, int64_t vmax, int k);
 
 struct TopkArgs {
   const float* scores;     // [B*Tq, score_stride]

@@ -53,12 +53,12 @@ static_assert(kTopkPartLen == 16 * 64, "a part is at most 16 keys per lane of on
 // scores; for a small k a row of more than 2048 keys is spread over part
 // waves first (each part's leaders hold every one of its keys in the row's
 // top 16, so the per-row step sees ~32 keys a part instead of 1024).
-TopkPlan topk_plan(int64_t vmax, int k) {
+TopkPlan topk_plan(int64_t vmin, int64_t vmax, int k) {
   TopkPlan p;
   p.direct_max = k <= 32 ? 2048 : kTopkSel;
   p.parts = vmax > p.direct_max;
   // a row's part count is largest at its own length or just below a length
-  // where the part length halves (rows of a launch may be shorter than vmax)
+  // where the part length halves
   int64_t np = 0;
   auto consider = [&](int64_t V) {
     if (V <= 0) return;
@@ -66,8 +66,10 @@ TopkPlan topk_plan(int64_t vmax, int k) {
     np = std::max(np, (V + P - 1) / P);
   };
   consider(vmax);
-  for (int P = kTopkPartLen; P > kTopkPartMin; P >>= 1)   // P halves below V = k P / 4
-    consider(std::min(vmax, (int64_t)k * P / 4 - 1));
+  for (int P = kTopkPartLen; P > kTopkPartMin; P >>= 1) {   // P halves below V = k P / 4
+    const int64_t v = (int64_t)k * P / 4 - 1;
+    if (v >= vmin && v <= vmax) consider(v);
+  }
   p.nparts = p.parts ? (int)np : 0;
   return p;
 }
