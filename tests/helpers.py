@@ -55,8 +55,9 @@ def assert_attn_close(got, want, what=""):
     queries (an element whose exact value lies within the kernel's ~1e-3
     relative logit-path error of a rounding midpoint lands on the far
     neighbour), against a float64 model of the kernel's roundings (two-term
-    E4M3 q~, bf16 rotary q~, two-term E4M3 probabilities, fp32 partials,
-    bf16 output) that gives 1.3-1.5e-2 per query."""
+    E4M3 q~, bf16 rotary q~, two-term E4M3 probabilities, bf16 output; the
+    16-bit split partials add about 2^-15 of a head's largest partial) that
+    gives 1.3-1.5e-2 per query."""
     max_abs, rel_l2 = err_stats(got, want)
     bar_abs = MAX_ABS + bf16_half_spacing(want)
     assert max_abs <= bar_abs and rel_l2 <= REL_L2, \
