@@ -837,6 +837,23 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   __shared__ float s_w[HPW][64];
   __shared__ float s_cs[R / 2][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The partials do not depend on the weights: the first kSp of them are
+  // requested before the (max, sum, scale) records, so the two round trips
+  // overlap (slots past S read as zero and touch no memory).
+  constexpr int kSp = 16;
+  const int hh = tid / QPH, d = 4 * (tid % QPH);
+  const int h = h0 + hh;
+  const bool mine = hh < HPW && h < a.H;
+  const int64_t sstride = (int64_t)a.H * D;   // elements between a query's split slots
+  const __amdgpu_buffer_rsrc_t rs =
+      buf_rsrc(a.part_o + slot0 * sstride, (uint32_t)(S * sstride * 2));
+  const uint32_t voff = mine ? (uint32_t)((h * D + d) * 2) : 0x7FFFFF00u;
+  u32x2 v0[kSp];
+#pragma unroll
+  for (int u = 0; u < kSp; ++u) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + (uint32_t)(u * sstride * 2), 0, 0);
+    v0[u] = u32x2{w[0], w[1]};
+  }
   if (tid < R / 2) {
     float cs, sn;
     rope_cos_sin(t, a.rope.t[tid], &cs, &sn);
@@ -844,13 +861,13 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
     s_cs[tid][1] = sn;
   }
   for (int hw = wave; hw < HPW; hw += 4) {
-    const int h = h0 + hw;
-    if (h >= a.H) break;
-    const float* pm = a.part_ml + (slot0 * a.H + h) * 4;
+    const int hx = h0 + hw;
+    if (hx >= a.H) break;
+    const float* pm = a.part_ml + (slot0 * a.H + hx) * 4;
     const bool own = lane < S;
     const f32x4 ml = own ? *reinterpret_cast<const f32x4*>(pm + (int64_t)lane * a.H * 4)
                          : f32x4{-INFINITY, 0.f, 0.f, 0.f};
-    const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+    const float z2 = a.sink ? a.sink[hx] * kLog2e : -INFINITY;
     const float M = fmaxf(wave_max(ml.x), z2);
     const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
     float den = wave_sum(ml.y * w);
@@ -859,26 +876,25 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
     // also undoes the partial's scale: O = q 2^e / 32767
     s_w[hw][lane] = ldexpf(w * inv, (int)ml.z) * (1.0f / 32767.0f);
     if (a.lse && lane == 0)
-      a.lse[(int64_t)qr * a.H + h] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
+      a.lse[(int64_t)qr * a.H + hx] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
   }
   __syncthreads();
-  const int hh = tid / QPH, d = 4 * (tid % QPH);
-  const int h = h0 + hh;
-  if (hh >= HPW || h >= a.H) return;
-  const uint16_t* po = a.part_o + (slot0 * a.H + h) * D + d;
-  const int64_t sstride = (int64_t)a.H * D;
+  if (!mine) return;
+  auto add = [](f32x4& x, float w, u32x2 v) {
+    x += w * f32x4{(float)(int)(short)(v.x & 0xFFFFu), (float)((int)v.x >> 16),
+                   (float)(int)(short)(v.y & 0xFFFFu), (float)((int)v.y >> 16)};
+  };
   f32x4 x = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 8) {   // eight split partials in flight
+#pragma unroll
+  for (int u = 0; u < kSp; ++u) add(x, u < S ? s_w[hh][u] : 0.f, v0[u]);
+  const uint16_t* po = a.part_o + (slot0 * a.H + h) * D + d;
+  for (int s0 = kSp; s0 < S; s0 += 8) {   // more splits: eight partials in flight
     u32x2 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       v[u] = *reinterpret_cast<const u32x2*>(po + (int64_t)min(s0 + u, S - 1) * sstride);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float w = s0 + u < S ? s_w[hh][s0 + u] : 0.f;
-      x += w * f32x4{(float)(int)(short)(v[u].x & 0xFFFFu), (float)((int)v[u].x >> 16),
-                     (float)(int)(short)(v[u].y & 0xFFFFu), (float)((int)v[u].y >> 16)};
-    }
+    for (int u = 0; u < 8; ++u) add(x, s0 + u < S ? s_w[hh][s0 + u] : 0.f, v[u]);
   }
   float y[4] = {x[0], x[1], x[2], x[3]};
   if (d >= D - R) {

@@ -96,6 +96,12 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, double turns_per_pos, 
   sincosf(r, s, c);
 }
 
+// A raw buffer resource over the n bytes at p (a load at an offset past n
+// returns 0 and touches no memory).  p must be the same in every lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll
