@@ -1002,7 +1002,8 @@ int run_backward(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
   if (!out || !lse || !dout || !dq) return fail(V4ATTN_EINVAL, "null out, lse, dout or dq");
   if (Ncap > 0 && !d_entries) return fail(V4ATTN_EINVAL, "null d_entries with Ncap > 0");
   if (W > 0 && !d_win) return fail(V4ATTN_EINVAL, "null d_win with W > 0");
-  if (!aligned16(dout) || !aligned16(dq)) return fail(V4ATTN_EINVAL, "dout and dq must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(dq))
+    return fail(V4ATTN_EINVAL, "q, out, dout and dq must be 16-byte aligned");
   const size_t need = bwd_ws(B, Tq, D, rows_max);
   if (!ws || ws_bytes < need)
     return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);

@@ -181,68 +181,118 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a, int q0) {
   if (lane == 0) a.rowmap[(int64_t)qc * a.np + x] = map;
 }
 
+// The eight bf16 of a 16-byte word as floats.
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& w, float (&x)[8]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(ws[i] << 16);
+    x[2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 f32_to_bf16x8(const float (&x)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(x[2 * i]) | ((uint32_t)f2bf(x[2 * i + 1]) << 16);
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
+// (cos, sin) of the rotary pairs among dims d .. d + 7 at position t ((1, 0)
+// below the rotary dims); the turn table is read with clamped indices, so
+// every lane loads and no branch waits on a load.
+__device__ __forceinline__ void lane_rot8(const BwdArgs& a, int d, int64_t t, float (&cs)[4],
+                                          float (&sn)[4]) {
+  double tv[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i = (d + 2 * p - (a.D - a.R)) >> 1;
+    tv[p] = a.rope.t[i < 0 ? 0 : (i > 31 ? 31 : i)];
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    cs[p] = 1.f;
+    sn[p] = 0.f;
+    if (d + 2 * p >= a.D - a.R) rope_cos_sin(t, tv[p], &cs[p], &sn[p]);
+  }
+}
+
 // Y[qc] = [q~ (64 head slots); do = RoPE_t(dout) (64 slots)] as bf16, Dh =
-// dout . out, dsink += -p_sink Dh.  One wave per head; lane holds the dim
-// pairs (2 lane + 128 e, +1).
+// dout . out, the query's d_sink share -p_sink Dh.  One wave per head; lane l
+// holds dims 8 l .. 8 l + 7 (16-byte loads and stores).
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int q0) {
   const int qc = blockIdx.y, qr = q0 + qc;
   const int r = qr % a.Tq;
   const int64_t t = a.q_pos0 + r;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  uint16_t* yq = a.Y + ((int64_t)qc * 128 + h) * a.D;
-  uint16_t* yd = a.Y + ((int64_t)qc * 128 + 64 + h) * a.D;
+  const int d = 8 * lane;
+  const bool act = d < a.D;
+  uint16_t* yq = a.Y + ((int64_t)qc * 128 + h) * a.D + d;
+  uint16_t* yd = a.Y + ((int64_t)qc * 128 + 64 + h) * a.D + d;
   if (h >= a.H) {
-    for (int d = lane; d < a.D; d += 64) yq[d] = yd[d] = 0;
+    if (act) *reinterpret_cast<uint4*>(yq) = *reinterpret_cast<uint4*>(yd) = uint4{0u, 0u, 0u, 0u};
     return;
   }
-  const uint16_t* qp = a.q + ((int64_t)qr * a.H + h) * a.D;
-  const uint16_t* gp = a.dout + ((int64_t)qr * a.H + h) * a.D;
-  const uint16_t* op = a.out + ((int64_t)qr * a.H + h) * a.D;
-  const int NP = a.D / 128;   // pairs per lane
+  const int64_t off = ((int64_t)qr * a.H + h) * a.D + d;
+  uint4 qw{0u, 0u, 0u, 0u}, gw{0u, 0u, 0u, 0u}, ow{0u, 0u, 0u, 0u};
+  float gm[8];
+  if (act) {
+    qw = *reinterpret_cast<const uint4*>(a.q + off);
+    gw = *reinterpret_cast<const uint4*>(a.dout + off);
+    ow = *reinterpret_cast<const uint4*>(a.out + off);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gm[e] = act ? a.gamma_q[d + e] : 0.f;
+  float cs[4], sn[4];
+  lane_rot8(a, d, t, cs, sn);
+  float x[8], g[8], o[8];
+  bf16x8_to_f32(qw, x);
+  bf16x8_to_f32(gw, g);
+  bf16x8_to_f32(ow, o);
   float ss = 0.f, dd = 0.f;
-  for (int e = 0; e < NP; ++e) {
-    const int d = 2 * lane + 128 * e;
-    const float q0v = bf16f(qp[d]), q1v = bf16f(qp[d + 1]);
-    ss += q0v * q0v + q1v * q1v;
-    dd += bf16f(gp[d]) * bf16f(op[d]) + bf16f(gp[d + 1]) * bf16f(op[d + 1]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ss += x[e] * x[e];
+    dd += g[e] * o[e];
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    ss += __shfl_xor(ss, o);
-    dd += __shfl_xor(dd, o);
-  }
+  ss = wave_sum(ss);
+  dd = wave_sum(dd);
   const float rsn = 1.0f / sqrtf(ss / (float)a.D + a.eps);
-  for (int e = 0; e < NP; ++e) {
-    const int d = 2 * lane + 128 * e;
-    float x0 = a.gamma_q[d] * (bf16f(qp[d]) * rsn), x1 = a.gamma_q[d + 1] * (bf16f(qp[d + 1]) * rsn);
-    float g0 = bf16f(gp[d]), g1 = bf16f(gp[d + 1]);
-    if (d >= a.D - a.R) {
-      float cs, sn;
-      rope_cos_sin(t, a.rope.t[(d - (a.D - a.R)) >> 1], &cs, &sn);
-      const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
-      x0 = y0;
-      x1 = y1;
-      const float u0 = g0 * cs - g1 * sn, u1 = g0 * sn + g1 * cs;   // do = RoPE_t(dout)
-      g0 = u0;
-      g1 = u1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = gm[e] * (x[e] * rsn);
+  if (d >= a.D - a.R) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float x0 = x[2 * p], x1 = x[2 * p + 1], g0 = g[2 * p], g1 = g[2 * p + 1];
+      x[2 * p] = x0 * cs[p] - x1 * sn[p];
+      x[2 * p + 1] = x0 * sn[p] + x1 * cs[p];
+      g[2 * p] = g0 * cs[p] - g1 * sn[p];       // do = RoPE_t(dout)
+      g[2 * p + 1] = g0 * sn[p] + g1 * cs[p];
     }
-    yq[d] = f2bf(x0);
-    yq[d + 1] = f2bf(x1);
-    yd[d] = f2bf(g0);
-    yd[d + 1] = f2bf(g1);
+  }
+  if (act) {
+    *reinterpret_cast<uint4*>(yq) = f32_to_bf16x8(x);
+    *reinterpret_cast<uint4*>(yd) = f32_to_bf16x8(g);
   }
   if (lane == 0) {
     a.Dh[(int64_t)qc * 64 + h] = dd;
-    if (a.sink && a.d_sink) {
+    float ds = 0.f;
+    if (a.sink) {
       const float lse = a.lse[(int64_t)qr * a.H + h];
       const float pz = lse == -INFINITY ? 0.f : expf(a.sink[h] - lse);
-      atomicAdd(a.d_sink + h, -pz * dd);
+      ds = -pz * dd;
     }
+    // row qc sums the shares of the queries qc, qc + chunk, .. (the chunks
+    // run in order on one stream); bwd_reduce_kernel adds the rows at the end
+    float* dsp = a.DS + (int64_t)qc * 64 + h;
+    *dsp = (q0 == 0 ? 0.f : *dsp) + ds;
   }
 }
 
 // T[qc] = [scale dL; P] (bf16, 64 head slots each) from [S; dP]: P =
 // exp(scale S - lse), dL = P (dP - Dh); absent rows and head slots >= H: 0.
-// One thread per row slot, all heads; p_sel (entry slots) is the head sum.
+// One thread per row slot, all heads, eight heads' loads in flight at a
+// time; p_sel (entry slots) is the head sum.
 __global__ __launch_bounds__(256) void bwd_softmax_kernel(BwdArgs a, int q0) {
   __shared__ float s_l2[64], s_dh[64];
   const int qc = blockIdx.y, qr = q0 + qc;
@@ -260,80 +310,122 @@ __global__ __launch_bounds__(256) void bwd_softmax_kernel(BwdArgs a, int q0) {
   const bool present = a.rowmap[(int64_t)qc * a.np + x] != -1;
   const float sl2 = a.scale * kL2e;
   float psum = 0.f;
-  for (int h = 0; h < 64; ++h) {
-    float p = 0.f, dl = 0.f;
-    if (present && s_l2[h] != -INFINITY) {
-      p = exp2f(sp[(int64_t)h * a.np] * sl2 - s_l2[h]);
-      dl = p * (sp[(int64_t)(64 + h) * a.np] - s_dh[h]);
+#pragma unroll 1
+  for (int h0 = 0; h0 < 64; h0 += 8) {
+    float sv[8], dv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sv[u] = sp[(int64_t)(h0 + u) * a.np];
+      dv[u] = sp[(int64_t)(64 + h0 + u) * a.np];
     }
-    psum += p;
-    tp[(int64_t)h * a.np] = f2bf(a.scale * dl);
-    tp[(int64_t)(64 + h) * a.np] = f2bf(p);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int h = h0 + u;
+      float p = 0.f, dl = 0.f;
+      if (present && s_l2[h] != -INFINITY) {
+        p = exp2f(sv[u] * sl2 - s_l2[h]);
+        dl = p * (dv[u] - s_dh[h]);
+      }
+      psum += p;
+      tp[(int64_t)h * a.np] = f2bf(a.scale * dl);
+      tp[(int64_t)(64 + h) * a.np] = f2bf(p);
+    }
   }
   if (a.p_sel && x < a.k_sel) a.p_sel[(int64_t)qr * a.k_sel + x] = psum;
 }
 
-// dq = RMSNorm backward of RoPE_t^T(dq~); d_gamma_q += sum over heads.  A
-// workgroup takes four heads of one query (one a wave); lane holds dim pairs.
-__global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a, int q0) {
-  __shared__ float s_dg[4][512];
-  const int qc = blockIdx.y, qr = q0 + qc;
+// dq = RMSNorm backward of RoPE_t^T(dq~); the query's d_gamma_q share
+// (summed over its heads) is added to row qc of G.  One workgroup of 16 waves per
+// query; wave w takes heads w, w + 16, ..; lane l holds dims 8 l .. 8 l + 7.
+// (Adding every workgroup's share into d_gamma_q directly put ~1,000 atomic
+// adds per chunk on each of its addresses.)
+__global__ __launch_bounds__(1024) void bwd_q_kernel(BwdArgs a, int q0) {
+  __shared__ float s_dg[16][512];
+  const int qc = blockIdx.x, qr = q0 + qc;
   const int r = qr % a.Tq;
   const int64_t t = a.q_pos0 + r;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int NP = a.D / 128;
+  const int d = 8 * lane;
+  const bool act = d < a.D;
   float dg[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dg[i] = 0.f;
-  if (blockIdx.x * 4 >= a.H) return;
-  for (int h = blockIdx.x * 4 + wave; h < a.H && h < blockIdx.x * 4 + 4; h += 4) {
-    const uint16_t* qp = a.q + ((int64_t)qr * a.H + h) * a.D;
-    const float* gq = a.DQT + ((int64_t)qc * 64 + h) * a.D;
+  for (int e = 0; e < 8; ++e) dg[e] = 0.f;
+  float gm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gm[e] = act ? a.gamma_q[d + e] : 0.f;
+  float cs[4], sn[4];
+  lane_rot8(a, d, t, cs, sn);
+  for (int h = wave; h < a.H; h += 16) {
+    uint4 qw{0u, 0u, 0u, 0u};
+    f32x4 u0{0.f, 0.f, 0.f, 0.f}, u1{0.f, 0.f, 0.f, 0.f};
+    if (act) {
+      qw = *reinterpret_cast<const uint4*>(a.q + ((int64_t)qr * a.H + h) * a.D + d);
+      const float* gq = a.DQT + ((int64_t)qc * 64 + h) * a.D + d;
+      u0 = *reinterpret_cast<const f32x4*>(gq);
+      u1 = *reinterpret_cast<const f32x4*>(gq + 4);
+    }
+    float xq[8], u[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+    bf16x8_to_f32(qw, xq);
     float ss = 0.f;
-    for (int e = 0; e < NP; ++e) {
-      const int d = 2 * lane + 128 * e;
-      ss += bf16f(qp[d]) * bf16f(qp[d]) + bf16f(qp[d + 1]) * bf16f(qp[d + 1]);
-    }
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += xq[e] * xq[e];
+    ss = wave_sum(ss);
     const float rsn = 1.0f / sqrtf(ss / (float)a.D + a.eps);
-    float gx[8], xq[8];
-    float dot = 0.f;
-    for (int e = 0; e < NP; ++e) {
-      const int d = 2 * lane + 128 * e;
-      float u0 = gq[d], u1 = gq[d + 1];
-      if (d >= a.D - a.R) {   // RoPE_t transposed = rotation by -t
-        float cs, sn;
-        rope_cos_sin(t, a.rope.t[(d - (a.D - a.R)) >> 1], &cs, &sn);
-        const float v0 = u0 * cs + u1 * sn, v1 = -u0 * sn + u1 * cs;
-        u0 = v0;
-        u1 = v1;
+    if (d >= a.D - a.R) {   // RoPE_t transposed = rotation by -t
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float v0 = u[2 * p], v1 = u[2 * p + 1];
+        u[2 * p] = v0 * cs[p] + v1 * sn[p];
+        u[2 * p + 1] = -v0 * sn[p] + v1 * cs[p];
       }
-      xq[2 * e] = bf16f(qp[d]);
-      xq[2 * e + 1] = bf16f(qp[d + 1]);
-      dg[2 * e] += u0 * xq[2 * e] * rsn;
-      dg[2 * e + 1] += u1 * xq[2 * e + 1] * rsn;
-      gx[2 * e] = u0 * a.gamma_q[d];
-      gx[2 * e + 1] = u1 * a.gamma_q[d + 1];
-      dot += gx[2 * e] * xq[2 * e] + gx[2 * e + 1] * xq[2 * e + 1];
     }
-    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+    float gx[8], dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dg[e] += u[e] * xq[e] * rsn;
+      gx[e] = u[e] * gm[e];
+      dot += gx[e] * xq[e];
+    }
+    dot = wave_sum(dot);
     const float c3 = dot * rsn * rsn * rsn / (float)a.D;
-    float* dqp = a.dq + ((int64_t)qr * a.H + h) * a.D;
-    for (int e = 0; e < NP; ++e) {
-      const int d = 2 * lane + 128 * e;
-      dqp[d] = gx[2 * e] * rsn - xq[2 * e] * c3;
-      dqp[d + 1] = gx[2 * e + 1] * rsn - xq[2 * e + 1] * c3;
+    if (act) {
+      float* dqp = a.dq + ((int64_t)qr * a.H + h) * a.D + d;
+      *reinterpret_cast<f32x4*>(dqp) = f32x4{gx[0] * rsn - xq[0] * c3, gx[1] * rsn - xq[1] * c3,
+                                             gx[2] * rsn - xq[2] * c3, gx[3] * rsn - xq[3] * c3};
+      *reinterpret_cast<f32x4*>(dqp + 4) = f32x4{gx[4] * rsn - xq[4] * c3, gx[5] * rsn - xq[5] * c3,
+                                                 gx[6] * rsn - xq[6] * c3, gx[7] * rsn - xq[7] * c3};
     }
   }
-  if (!a.d_gamma_q) return;
-  for (int e = 0; e < NP; ++e) {
-    const int d = 2 * lane + 128 * e;
-    s_dg[wave][d] = dg[2 * e];
-    s_dg[wave][d + 1] = dg[2 * e + 1];
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_dg[wave][d + e] = dg[e];
   }
   __syncthreads();
-  for (int d = threadIdx.x; d < a.D; d += 256)
-    atomicAdd(a.d_gamma_q + d, s_dg[0][d] + s_dg[1][d] + s_dg[2][d] + s_dg[3][d]);
+  for (int x = threadIdx.x; x < a.D; x += 1024) {
+    float z = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) z += s_dg[w][x];
+    float* gp = a.G + (int64_t)qc * a.D + x;   // accumulated over the chunks, as DS
+    *gp = (q0 == 0 ? 0.f : *gp) + z;
+  }
+}
+
+// After the last chunk: d_gamma_q += the G rows summed, d_sink += the DS rows
+// summed (one atomic add per address).  Thread x of the grid takes column x.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int qc_n) {
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (a.d_gamma_q && x < a.D) {
+    float z = 0.f;
+#pragma unroll 8
+    for (int q = 0; q < qc_n; ++q) z += a.G[(int64_t)q * a.D + x];
+    atomicAdd(a.d_gamma_q + x, z);
+  }
+  if (a.sink && a.d_sink && blockIdx.x == 0 && x < a.H) {
+    float z = 0.f;
+#pragma unroll 8
+    for (int q = 0; q < qc_n; ++q) z += a.DS[(int64_t)q * 64 + x];
+    atomicAdd(a.d_sink + x, z);
+  }
 }
 
 // ---- compressor backward: one workgroup per (sequence, entry).  Recomputes
@@ -593,7 +685,9 @@ size_t bwd_query_bytes(int D, int64_t np) {
          + al((size_t)64 * 4)            // Dh
          + al((size_t)128 * np * 4)      // [S; dP]
          + al((size_t)128 * np * 2)      // T
-         + al((size_t)64 * D * 4);       // dq~
+         + al((size_t)64 * D * 4)        // dq~
+         + al((size_t)D * 4)             // G
+         + al((size_t)64 * 4);           // DS
 }
 
 hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t st) {
@@ -607,7 +701,9 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t s
   a.Dh = reinterpret_cast<float*>(w);          w += al((size_t)qchunk * 64 * 4);
   a.SP = reinterpret_cast<float*>(w);          w += al((size_t)qchunk * 128 * np * 4);
   a.T = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * 128 * np * 2);
-  a.DQT = reinterpret_cast<float*>(w);
+  a.DQT = reinterpret_cast<float*>(w);       w += al((size_t)qchunk * 64 * a.D * 4);
+  a.G = reinterpret_cast<float*>(w);         w += al((size_t)qchunk * a.D * 4);
+  a.DS = reinterpret_cast<float*>(w);
   for (int q0 = 0; q0 < nq; q0 += qchunk) {
     const int qc = nq - q0 < qchunk ? nq - q0 : qchunk;
     bwd_gather_kernel<<<dim3((unsigned)((np + 3) / 4), qc), 256, 0, st>>>(a, q0);
@@ -636,8 +732,10 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t s
     g3.rowmap = a.rowmap; g3.rowmap_batch = np;
     e = gemm<true, false>(g3, (int)np, a.D, qc, st);
     if (e != hipSuccess) return e;
-    bwd_q_kernel<<<dim3((unsigned)((a.H + 3) / 4), qc), 256, 0, st>>>(a, q0);
+    bwd_q_kernel<<<qc, 1024, 0, st>>>(a, q0);
   }
+  if (a.d_gamma_q || (a.sink && a.d_sink))
+    bwd_reduce_kernel<<<(unsigned)((a.D + 255) / 256), 256, 0, st>>>(a, nq < qchunk ? nq : qchunk);
   return hipGetLastError();
 }
 

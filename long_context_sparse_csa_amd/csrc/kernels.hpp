@@ -306,6 +306,8 @@ struct BwdArgs {
   float* SP;
   uint16_t* T;
   float* DQT;
+  float* G;                  // [chunk, D] a query's d_gamma_q share (its heads summed)
+  float* DS;                 // [chunk, 64] a query's d_sink share per head
 };
 int64_t bwd_rows_padded(int64_t rows_max);
 size_t bwd_query_bytes(int D, int64_t np);
