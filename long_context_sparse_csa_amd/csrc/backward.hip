@@ -101,24 +101,39 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
     __syncthreads();
   }
   // lane (c, gq) holds rows 4 gq + v, column c of each 16 x 16 block
+  if (!g.rowmap) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = m0 + wm * 32 + 16 * i + 4 * gq + v;
+          const int n = n0 + wn * 32 + 16 * j + c;
+          if (n < g.n_valid) g.c[(int64_t)z * g.c_batch + (int64_t)m * g.ldc + n] = g.alpha * acc[i][j][v];
+        }
+    return;
+  }
+  // scattered adds: the tile goes through LDS so that one wave's atomic
+  // instruction covers 64 consecutive floats of one row (two whole cache
+  // lines) rather than 16 floats of four rows
+  __shared__ float sC[64][65];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * 32 + 16 * i + 4 * gq + v;
-        const int n = n0 + wn * 32 + 16 * j + c;
-        const float x = g.alpha * acc[i][j][v];
-        if (n >= g.n_valid) continue;
-        if (!g.rowmap) {
-          g.c[(int64_t)z * g.c_batch + (int64_t)m * g.ldc + n] = x;
-        } else {
-          const int64_t r = g.rowmap[(int64_t)z * g.rowmap_batch + m];
-          if (r >= 0) atomicAdd(g.c + r * g.ldc + n, x);
-          else if (r <= -2) atomicAdd(g.c2 + (-2 - r) * g.ldc + n, x);
-        }
-      }
+      for (int v = 0; v < 4; ++v) sC[wm * 32 + 16 * i + 4 * gq + v][wn * 32 + 16 * j + c] = acc[i][j][v];
+  __syncthreads();
+  const int n = n0 + lane;
+  if (n >= g.n_valid) return;
+#pragma unroll 4
+  for (int mm = wave; mm < 64; mm += 4) {
+    const int64_t r = g.rowmap[(int64_t)z * g.rowmap_batch + m0 + mm];
+    const float x = g.alpha * sC[mm][lane];
+    if (r >= 0) atomicAdd(g.c + r * g.ldc + n, x);
+    else if (r <= -2) atomicAdd(g.c2 + (-2 - r) * g.ldc + n, x);
+  }
 }
 
 // X[qc, x, :] = the query's row x as bf16 (zeros if absent), rowmap = where
