@@ -170,7 +170,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   const int b = qr / a.Tq, r = qr % a.Tq;
   const int64_t qpos = a.ragged ? a.pos.p[b] : a.q_pos0;   // this sequence's first query
   const int64_t t = qpos + r;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave as a scalar: the LDS destinations of the tile copies (m0) are then
+  // formed with scalar arithmetic instead of a vector add and a readfirstlane
+  // per copy
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;   // lane column (head / row / dim), k group
   const int head = wave * 16 + c;
 
