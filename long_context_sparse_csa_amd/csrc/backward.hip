@@ -136,6 +136,134 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
+// C[z] = alpha A[z] B[z] on TM x 128 tiles, k in steps of 32 (M, N and K
+// multiples of TM, 128 and 32).  Four waves as 2 x 2, each (TM / 2) x 64 on
+// the 32x32x16 bf16 MFMAs; the next k-step's tiles come from global memory
+// while the current one's MFMAs run and go to the other of two LDS buffers
+// (one barrier a step).  A is M x K (AT: stored K x M), B is K x N (BT:
+// stored N x K); a source stored k-major is transposed on its way into LDS.
+// With rowmap, each result row is added into its row of c (or c2) through
+// LDS, so that one atomic instruction covers 64 consecutive floats of a row.
+template <int TM, bool AT, bool BT>
+__global__ __launch_bounds__(256) void gemm32_kernel(GemmArgs g) {
+  constexpr int TN = 128, BK = 32, KP = 40;   // KP: padded k stride (elements) of the LDS tiles
+  constexpr int WM = TM / 2, MB = WM / 32;    // rows per wave, 32-row blocks per wave
+  constexpr int LA = TM * BK / 8 / 256;       // 16-byte loads per thread per step (A)
+  constexpr int LB = TN * BK / 8 / 256;       // (B)
+  constexpr int AB_BYTES = 2 * (TM + TN) * KP * 2;
+  constexpr int C_BYTES = TM * (TN + 1) * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[AB_BYTES > C_BYTES ? AB_BYTES : C_BYTES];
+  auto sA = reinterpret_cast<uint16_t (*)[TM][KP]>(smem);
+  auto sB = reinterpret_cast<uint16_t (*)[TN][KP]>(smem + 2 * TM * KP * 2);
+  const int z = blockIdx.z;
+  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
+  const uint16_t* A = g.a + (int64_t)z * g.a_batch;
+  const uint16_t* B = g.b + (int64_t)z * g.b_batch;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // load i of this thread: rows x k source: row x / 4, k chunk x % 4; k x rows
+  // source: k x / (ROWS / 8), row chunk x % (ROWS / 8)  (x = tid + 256 i)
+  auto fetch = [&](const uint16_t* p, int64_t ld, int r0, int k0, bool tr, int rows, int i) -> uint4 {
+    const int x = tid + 256 * i;
+    if (!tr) return *reinterpret_cast<const uint4*>(p + (int64_t)(r0 + (x >> 2)) * ld + k0 + 8 * (x & 3));
+    const int cpr = rows / 8;
+    return *reinterpret_cast<const uint4*>(p + (int64_t)(k0 + x / cpr) * ld + r0 + 8 * (x % cpr));
+  };
+  auto put = [&](uint16_t (*s)[KP], uint4 v, bool tr, int rows, int i) {
+    const int x = tid + 256 * i;
+    if (!tr) {
+      *reinterpret_cast<uint4*>(&s[x >> 2][8 * (x & 3)]) = v;
+      return;
+    }
+    const int cpr = rows / 8, kk = x / cpr, ch = x % cpr;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[8 * ch + 2 * e][kk] = (uint16_t)(w[e] & 0xFFFFu);
+      s[8 * ch + 2 * e + 1][kk] = (uint16_t)(w[e] >> 16);
+    }
+  };
+  uint4 ra[LA], rb[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) ra[i] = fetch(A, g.lda, m0, 0, AT, TM, i);
+#pragma unroll
+  for (int i = 0; i < LB; ++i) rb[i] = fetch(B, g.ldb, n0, 0, !BT, TN, i);
+  f32x16 acc[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
+  int buf = 0;
+  for (int k0 = 0; k0 < g.K; k0 += BK) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) put(sA[buf], ra[i], AT, TM, i);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) put(sB[buf], rb[i], !BT, TN, i);
+    __syncthreads();   // buffer buf complete; every wave is done with buf ^ 1's last reads
+    if (k0 + BK < g.K) {
+#pragma unroll
+      for (int i = 0; i < LA; ++i) ra[i] = fetch(A, g.lda, m0, k0 + BK, AT, TM, i);
+#pragma unroll
+      for (int i = 0; i < LB; ++i) rb[i] = fetch(B, g.ldb, n0, k0 + BK, !BT, TN, i);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 av[MB], bv[2];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        av[mb] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * WM + 32 * mb + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        bv[nb] = *reinterpret_cast<const bf16x8*>(&sB[buf][wn * 64 + 32 * nb + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+    }
+    buf ^= 1;
+  }
+  // lane holds column lane % 32 of each 32 x 32 block, rows (e/4) 8 + (lane/32) 4 + e % 4
+  if (!g.rowmap) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int n = n0 + wn * 64 + 32 * nb + (lane & 31);
+        if (n >= g.n_valid) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm * WM + 32 * mb + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+          g.c[(int64_t)z * g.c_batch + (int64_t)m * g.ldc + n] = g.alpha * acc[mb][nb][e];
+        }
+      }
+    return;
+  }
+  __syncthreads();   // every wave is done with the operand tiles: the space holds C now
+  auto sC = reinterpret_cast<float (*)[TN + 1]>(smem);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sC[wm * WM + 32 * mb + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)][wn * 64 + 32 * nb + (lane & 31)] =
+            acc[mb][nb][e];
+  __syncthreads();
+  for (int mm = wave; mm < TM; mm += 4) {
+    const int64_t r = g.rowmap[(int64_t)z * g.rowmap_batch + m0 + mm];
+    if (r == -1) continue;
+    float* dst = r >= 0 ? g.c + r * g.ldc : g.c2 + (-2 - r) * g.ldc;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int n = n0 + 64 * h + lane;
+      if (n < g.n_valid) atomicAdd(dst + n, g.alpha * sC[mm][64 * h + lane]);
+    }
+  }
+}
+
 // X[qc, x, :] = the query's row x as bf16 (zeros if absent), rowmap = where
 // its gradient goes: entry b Ncap + j (>= 0), window row -2 - (b (Tq+W-1) + r),
 // or -1.  One wave per row slot.
@@ -688,9 +816,20 @@ hipError_t gemm(const GemmArgs& g, int M, int N, int Z, hipStream_t st) {
   return hipGetLastError();
 }
 
+// [S; dP] = Y X^T of the attention backward (M = 128, N a multiple of 128,
+// neither operand transposed).  The products whose operands are stored
+// k-major (dq~ = T X, dX = T^T Y) stay on gemm_bf16_kernel: transposing them
+// element by element into the larger tiles cost more than the faster MFMAs
+// saved (measured 49.5 and 193.8 us against 29.9 and 139.6 us per chunk).
+template <bool AT, bool BT>
+hipError_t gemm32(const GemmArgs& g, int M, int N, int Z, hipStream_t st) {
+  gemm32_kernel<128, AT, BT><<<dim3(N / 128, M / 128, Z), 256, 0, st>>>(g);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-int64_t bwd_rows_padded(int64_t rows_max) { return (rows_max + 63) / 64 * 64; }
+int64_t bwd_rows_padded(int64_t rows_max) { return (rows_max + 127) / 128 * 128; }
 
 size_t bwd_query_bytes(int D, int64_t np) {
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
@@ -728,7 +867,7 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t s
     g1.a = a.Y; g1.lda = a.D; g1.a_batch = 128 * (int64_t)a.D;
     g1.b = a.X; g1.ldb = a.D; g1.b_batch = np * a.D;
     g1.c = a.SP; g1.ldc = np; g1.c_batch = 128 * np; g1.K = a.D; g1.alpha = 1.f; g1.n_valid = (int)np;
-    hipError_t e = gemm<false, true>(g1, 128, (int)np, qc, st);
+    hipError_t e = gemm32<false, true>(g1, 128, (int)np, qc, st);
     if (e != hipSuccess) return e;
     bwd_softmax_kernel<<<dim3((unsigned)((np + 255) / 256), qc), 256, 0, st>>>(a, q0);
     // dq~ = (scale dL) X: M = 64, N = D, K = np
