@@ -136,23 +136,28 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-// C[z] = alpha A[z] B[z] on TM x 128 tiles, k in steps of 32 (M, N and K
+// Tiles of C[z] = A[z] B[z], TM x 128, k in steps of 32 (M, N and K
 // multiples of TM, 128 and 32).  Four waves as 2 x 2, each (TM / 2) x 64 on
 // the 32x32x16 bf16 MFMAs; the next k-step's tiles come from global memory
 // while the current one's MFMAs run and go to the other of two LDS buffers
 // (one barrier a step).  A is M x K (AT: stored K x M), B is K x N (BT:
 // stored N x K); a source stored k-major is transposed on its way into LDS.
-// With rowmap, each result row is added into its row of c (or c2) through
-// LDS, so that one atomic instruction covers 64 consecutive floats of a row.
+// (The two products with k-major operands, dq~ = T X and dX = T^T Y, stay on
+// gemm_bf16_kernel: transposing them element by element into these larger
+// tiles cost more than the faster MFMAs saved.)
+template <int TM>
+constexpr int gemm32_smem_bytes() {
+  return 2 * (TM + 128) * 40 * 2 > TM * 129 * 4 ? 2 * (TM + 128) * 40 * 2 : TM * 129 * 4;
+}
+
+// The main loop of gemm32: this workgroup's TM x 128 tile of A[z] B[z] in acc
+// (lane: column lane % 32 of each 32 x 32 block, rows (e/4) 8 + (lane/32) 4 + e % 4).
 template <int TM, bool AT, bool BT>
-__global__ __launch_bounds__(256) void gemm32_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm32_main(const GemmArgs& g, uint8_t* smem, f32x16 (&acc)[TM / 64][2]) {
   constexpr int TN = 128, BK = 32, KP = 40;   // KP: padded k stride (elements) of the LDS tiles
   constexpr int WM = TM / 2, MB = WM / 32;    // rows per wave, 32-row blocks per wave
   constexpr int LA = TM * BK / 8 / 256;       // 16-byte loads per thread per step (A)
   constexpr int LB = TN * BK / 8 / 256;       // (B)
-  constexpr int AB_BYTES = 2 * (TM + TN) * KP * 2;
-  constexpr int C_BYTES = TM * (TN + 1) * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[AB_BYTES > C_BYTES ? AB_BYTES : C_BYTES];
   auto sA = reinterpret_cast<uint16_t (*)[TM][KP]>(smem);
   auto sB = reinterpret_cast<uint16_t (*)[TN][KP]>(smem + 2 * TM * KP * 2);
   const int z = blockIdx.z;
@@ -188,7 +193,6 @@ __global__ __launch_bounds__(256) void gemm32_kernel(GemmArgs g) {
   for (int i = 0; i < LA; ++i) ra[i] = fetch(A, g.lda, m0, 0, AT, TM, i);
 #pragma unroll
   for (int i = 0; i < LB; ++i) rb[i] = fetch(B, g.ldb, n0, 0, !BT, TN, i);
-  f32x16 acc[MB][2];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -225,43 +229,59 @@ __global__ __launch_bounds__(256) void gemm32_kernel(GemmArgs g) {
     }
     buf ^= 1;
   }
-  // lane holds column lane % 32 of each 32 x 32 block, rows (e/4) 8 + (lane/32) 4 + e % 4
-  if (!g.rowmap) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int n = n0 + wn * 64 + 32 * nb + (lane & 31);
-        if (n >= g.n_valid) continue;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm * WM + 32 * mb + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-          g.c[(int64_t)z * g.c_batch + (int64_t)m * g.ldc + n] = g.alpha * acc[mb][nb][e];
-        }
-      }
-    return;
+}
+
+// [S; dP] = Y X^T for one query (z) and 128 row slots, with the softmax
+// gradient as its epilogue: T = [scale dL; P] (bf16) with P = exp(scale S -
+// lse), dL = P (dP - D_h), 0 for absent rows and head slots >= H, and p_sel
+// (the head sum of P) for entry slots.  The fp32 [S; dP] never leaves LDS.
+__global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int q0) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[gemm32_smem_bytes<128>()];
+  __shared__ float s_l2[64], s_dh[64], s_ps[128];
+  const int z = blockIdx.z, qr = q0 + z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < 64) {
+    const float lse = tid < a.H ? a.lse[(int64_t)qr * a.H + tid] : -INFINITY;
+    s_l2[tid] = lse * kL2e;
+    s_dh[tid] = a.Dh[(int64_t)z * 64 + tid];
   }
-  __syncthreads();   // every wave is done with the operand tiles: the space holds C now
-  auto sC = reinterpret_cast<float (*)[TN + 1]>(smem);
+  f32x16 acc[2][2];
+  gemm32_main<128, false, true>(g, smem, acc);
+  const int n0 = blockIdx.x * 128;
+  const int wm = wave >> 1, wn = wave & 1;
+  __syncthreads();   // the operand tiles are done with: the space holds [S; dP]
+  auto sC = reinterpret_cast<float (*)[129]>(smem);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        sC[wm * WM + 32 * mb + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)][wn * 64 + 32 * nb + (lane & 31)] =
+        sC[wm * 64 + 32 * mb + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)][wn * 64 + 32 * nb + (lane & 31)] =
             acc[mb][nb][e];
   __syncthreads();
-  for (int mm = wave; mm < TM; mm += 4) {
-    const int64_t r = g.rowmap[(int64_t)z * g.rowmap_batch + m0 + mm];
-    if (r == -1) continue;
-    float* dst = r >= 0 ? g.c + r * g.ldc : g.c2 + (-2 - r) * g.ldc;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int n = n0 + 64 * h + lane;
-      if (n < g.n_valid) atomicAdd(dst + n, g.alpha * sC[mm][64 * h + lane]);
+  // thread: row slot c = tid % 128 of the tile, heads 32 (tid / 128) .. + 31
+  const int c = tid & 127, hh = tid >> 7;
+  const int64_t x = n0 + c;
+  const bool present = a.rowmap[(int64_t)z * a.np + x] != -1;
+  const float sl2 = a.scale * kL2e;
+  uint16_t* tp = a.T + (int64_t)z * 128 * a.np + x;
+  float psum = 0.f;
+#pragma unroll 8
+  for (int i = 0; i < 32; ++i) {
+    const int h = 32 * hh + i;
+    float p = 0.f, dl = 0.f;
+    if (present && s_l2[h] != -INFINITY) {
+      p = exp2f(sC[h][c] * sl2 - s_l2[h]);
+      dl = p * (sC[64 + h][c] - s_dh[h]);
     }
+    psum += p;
+    tp[(int64_t)h * a.np] = f2bf(a.scale * dl);
+    tp[(int64_t)(64 + h) * a.np] = f2bf(p);
   }
+  if (hh == 1) s_ps[c] = psum;
+  __syncthreads();
+  if (hh == 0 && a.p_sel && x < a.k_sel) a.p_sel[(int64_t)qr * a.k_sel + x] = psum + s_ps[c];
 }
 
 // X[qc, x, :] = the query's row x as bf16 (zeros if absent), rowmap = where
@@ -430,51 +450,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int q0) {
     float* dsp = a.DS + (int64_t)qc * 64 + h;
     *dsp = (q0 == 0 ? 0.f : *dsp) + ds;
   }
-}
-
-// T[qc] = [scale dL; P] (bf16, 64 head slots each) from [S; dP]: P =
-// exp(scale S - lse), dL = P (dP - Dh); absent rows and head slots >= H: 0.
-// One thread per row slot, all heads, eight heads' loads in flight at a
-// time; p_sel (entry slots) is the head sum.
-__global__ __launch_bounds__(256) void bwd_softmax_kernel(BwdArgs a, int q0) {
-  __shared__ float s_l2[64], s_dh[64];
-  const int qc = blockIdx.y, qr = q0 + qc;
-  if (threadIdx.x < 64) {
-    const int h = threadIdx.x;
-    const float lse = h < a.H ? a.lse[(int64_t)qr * a.H + h] : -INFINITY;
-    s_l2[h] = lse * kL2e;
-    s_dh[h] = a.Dh[(int64_t)qc * 64 + h];
-  }
-  __syncthreads();
-  const int x = blockIdx.x * 256 + threadIdx.x;
-  if (x >= a.np) return;
-  const float* sp = a.SP + (int64_t)qc * 128 * a.np + x;
-  uint16_t* tp = a.T + (int64_t)qc * 128 * a.np + x;
-  const bool present = a.rowmap[(int64_t)qc * a.np + x] != -1;
-  const float sl2 = a.scale * kL2e;
-  float psum = 0.f;
-#pragma unroll 1
-  for (int h0 = 0; h0 < 64; h0 += 8) {
-    float sv[8], dv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      sv[u] = sp[(int64_t)(h0 + u) * a.np];
-      dv[u] = sp[(int64_t)(64 + h0 + u) * a.np];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int h = h0 + u;
-      float p = 0.f, dl = 0.f;
-      if (present && s_l2[h] != -INFINITY) {
-        p = exp2f(sv[u] * sl2 - s_l2[h]);
-        dl = p * (dv[u] - s_dh[h]);
-      }
-      psum += p;
-      tp[(int64_t)h * a.np] = f2bf(a.scale * dl);
-      tp[(int64_t)(64 + h) * a.np] = f2bf(p);
-    }
-  }
-  if (a.p_sel && x < a.k_sel) a.p_sel[(int64_t)qr * a.k_sel + x] = psum;
 }
 
 // dq = RMSNorm backward of RoPE_t^T(dq~); the query's d_gamma_q share
@@ -816,16 +791,6 @@ hipError_t gemm(const GemmArgs& g, int M, int N, int Z, hipStream_t st) {
   return hipGetLastError();
 }
 
-// [S; dP] = Y X^T of the attention backward (M = 128, N a multiple of 128,
-// neither operand transposed).  The products whose operands are stored
-// k-major (dq~ = T X, dX = T^T Y) stay on gemm_bf16_kernel: transposing them
-// element by element into the larger tiles cost more than the faster MFMAs
-// saved (measured 49.5 and 193.8 us against 29.9 and 139.6 us per chunk).
-template <bool AT, bool BT>
-hipError_t gemm32(const GemmArgs& g, int M, int N, int Z, hipStream_t st) {
-  gemm32_kernel<128, AT, BT><<<dim3(N / 128, M / 128, Z), 256, 0, st>>>(g);
-  return hipGetLastError();
-}
 
 }  // namespace
 
@@ -837,7 +802,6 @@ size_t bwd_query_bytes(int D, int64_t np) {
          + al((size_t)np * 8)            // rowmap
          + al((size_t)128 * D * 2)       // Y
          + al((size_t)64 * 4)            // Dh
-         + al((size_t)128 * np * 4)      // [S; dP]
          + al((size_t)128 * np * 2)      // T
          + al((size_t)64 * D * 4)        // dq~
          + al((size_t)D * 4)             // G
@@ -853,7 +817,6 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t s
   a.rowmap = reinterpret_cast<int64_t*>(w);    w += al((size_t)qchunk * np * 8);
   a.Y = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * 128 * a.D * 2);
   a.Dh = reinterpret_cast<float*>(w);          w += al((size_t)qchunk * 64 * 4);
-  a.SP = reinterpret_cast<float*>(w);          w += al((size_t)qchunk * 128 * np * 4);
   a.T = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * 128 * np * 2);
   a.DQT = reinterpret_cast<float*>(w);       w += al((size_t)qchunk * 64 * a.D * 4);
   a.G = reinterpret_cast<float*>(w);         w += al((size_t)qchunk * a.D * 4);
@@ -862,14 +825,14 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t s
     const int qc = nq - q0 < qchunk ? nq - q0 : qchunk;
     bwd_gather_kernel<<<dim3((unsigned)((np + 3) / 4), qc), 256, 0, st>>>(a, q0);
     bwd_prep_kernel<<<dim3(16, qc), 256, 0, st>>>(a, q0);
-    // [S; dP] = Y X^T: M = 128, N = np, K = D
+    // [S; dP] = Y X^T (M = 128, N = np, K = D) and, from it, T = [scale dL; P]
     GemmArgs g1{};
     g1.a = a.Y; g1.lda = a.D; g1.a_batch = 128 * (int64_t)a.D;
     g1.b = a.X; g1.ldb = a.D; g1.b_batch = np * a.D;
-    g1.c = a.SP; g1.ldc = np; g1.c_batch = 128 * np; g1.K = a.D; g1.alpha = 1.f; g1.n_valid = (int)np;
-    hipError_t e = gemm32<false, true>(g1, 128, (int)np, qc, st);
+    g1.K = a.D; g1.alpha = 1.f; g1.n_valid = (int)np;
+    bwd_sdp_kernel<<<dim3((unsigned)(np / 128), 1, qc), 256, 0, st>>>(g1, a, q0);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    bwd_softmax_kernel<<<dim3((unsigned)((np + 255) / 256), qc), 256, 0, st>>>(a, q0);
     // dq~ = (scale dL) X: M = 64, N = D, K = np
     GemmArgs g2{};
     g2.a = a.T; g2.lda = np; g2.a_batch = 128 * np;

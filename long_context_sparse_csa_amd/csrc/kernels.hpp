@@ -303,7 +303,6 @@ struct BwdArgs {
   int64_t* rowmap;
   uint16_t* Y;
   float* Dh;
-  float* SP;
   uint16_t* T;
   float* DQT;
   float* G;                  // [chunk, D] a query's d_gamma_q share (its heads summed)
