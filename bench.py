@@ -57,11 +57,11 @@ COPY_BYTES = 1 << 30           # calibration copy for the HBM byte counters
 # HBM bytes of one index_score launch at the decode shape, from two
 # rocprofv3 --pmc passes over `bench.py --counters` (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
-# for torch's elementwise kernel over 1 GiB in and 1 GiB out (FETCH 524,321
+# for torch's elementwise kernel over 1 GiB in and 1 GiB out (FETCH 524,319
 # KiB -> x2.0; WRITE 1,048,576 KiB -> x1.0).  Valid only for the kernel
 # sources they were taken with (hash below); otherwise reported as null.
-TRAFFIC = {"sources_sha256_16": "1c36a3067db23e74",
-           "fetch_kib": 262707.6, "fetch_scale": 2.0,
+TRAFFIC = {"sources_sha256_16": "4eb24fe14ebb2406",
+           "fetch_kib": 262707.5, "fetch_scale": 2.0,
            "write_kib": 8192.0, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("long_context_sparse_csa_amd/csrc/indexer.hip",
                    "long_context_sparse_csa_amd/csrc/common.hpp")
@@ -215,6 +215,22 @@ def run_breakdown(launches, steps):
         for i, n in enumerate(names):
             tot[n] += evs[s][i].elapsed_time(evs[s][i + 1])
     return {n: tot[n] / steps * 1e3 for n in names}   # microseconds
+
+
+def run_back_to_back(fn, n, warmup=3):
+    """Average duration of one launch of fn: n launches back to back between
+    two HIP events on the launching (current) stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3   # microseconds
 
 
 def prefill_section(dev, reps):
@@ -896,11 +912,17 @@ def main():
             ent["TFLOPs"] = round(aflops[k] / (us * 1e-6) / 1e12, 2)
         kernels[k] = ent
     dom = "index_score"
-    ach = abytes[dom] / (br[dom] * 1e-6) / 1e9
+    # the dominant kernel's average launch duration: 20 launches back to back
+    # (the per-call pairs above also hold the dispatch gap after the call before)
+    t_dom = run_back_to_back(dict(launches)[dom], 20)
+    ach = abytes[dom] / (t_dom * 1e-6) / 1e9
     roofline = {"kernel": "index_score_kernel<128,4>", "bound": "hbm",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                "algorithmic_bytes_per_launch": abytes[dom]}
+                "algorithmic_bytes_per_launch": abytes[dom],
+                "launch_us": round(t_dom, 2),
+                "timing": "20 launches back to back between two HIP events on the launching "
+                          "stream"}
 
     def layer(nq, us, names):
         by = sum(abytes.get(n, 0) for n in names)
