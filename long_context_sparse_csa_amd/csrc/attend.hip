@@ -103,17 +103,19 @@ struct RowSpace {
   int64_t n_rows;   // entries + window rows
 };
 
-__device__ __forceinline__ RowSpace row_space(const AttendArgs& a, bool csa, int64_t t) {
+__device__ __forceinline__ RowSpace row_space(bool csa, int64_t t, int k, int m, int64_t n_entries,
+                                               int W) {
   RowSpace rs;
   if (csa) {
-    rs.n_ent = a.k;
-  } else {
-    int64_t v = (t + 1) / a.m;
-    rs.n_ent = v < a.n_entries ? v : a.n_entries;
+    rs.n_ent = k;
+  } else {   // positions below 2^31 take the 32-bit division
+    const int64_t v = (uint64_t)(t + 1) < (1ull << 31) ? (int64_t)((uint32_t)(t + 1) / (uint32_t)m)
+                                                       : (t + 1) / m;
+    rs.n_ent = v < n_entries ? v : n_entries;
   }
-  int64_t lo = t - a.W + 1;
+  int64_t lo = t - W + 1;
   rs.win_lo = lo > 0 ? lo : 0;
-  const int64_t n_win = a.W > 0 ? (t - rs.win_lo + 1) : 0;
+  const int64_t n_win = W > 0 ? (t - rs.win_lo + 1) : 0;
   rs.n_rows = rs.n_ent + n_win;
   return rs;
 }
@@ -122,6 +124,11 @@ __device__ __forceinline__ RowSpace row_space(const AttendArgs& a, bool csa, int
 __host__ __device__ inline int64_t split_chunk(int64_t n_rows, int splits) {
   const int64_t c = (n_rows + splits - 1) / splits;
   return (c + kAttRows - 1) / kAttRows * kAttRows;
+}
+// The same for n_rows below 2^31, with a 32-bit division.
+__device__ __forceinline__ int64_t split_chunk32(int n_rows, int splits) {
+  const unsigned c = ((unsigned)n_rows + (unsigned)splits - 1u) / (unsigned)splits;
+  return (int64_t)((c + kAttRows - 1) / kAttRows * kAttRows);
 }
 
 // out = g1 * y + g0 * o0 + g2 * o2 for four dims (the gated sum of the
@@ -149,31 +156,67 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   constexpr int R = G::R, NJ = G::NJ, NB8 = G::NB8, NB = G::NB, ROW = G::ROW;
   constexpr int BFC = G::FP8_CPR;   // first bf16 chunk
   const AttendArgs& a = ab.p[blockIdx.z];   // the problem of this grid layer
-  int qr, split, nsplit;
-  int64_t slot;   // this split's partial slot
-  if (a.flat) {   // ragged decode: workgroup x is slot x of sequence b
-    const int x = blockIdx.x;
-    if (x >= a.slot0[a.B]) return;
-    int bb = 0;
-    while (bb + 1 < a.B && x >= a.slot0[bb + 1]) ++bb;
-    qr = bb;
-    split = x - a.slot0[bb];
-    nsplit = a.slot0[bb + 1] - a.slot0[bb];
-    slot = x;
-  } else {
-    qr = blockIdx.y;
-    split = blockIdx.x;
-    if (split >= a.splits) return;   // a layer with fewer splits than the grid
-    nsplit = a.splits;
-    slot = (int64_t)qr * a.splits + split;
-  }
-  const int b = qr / a.Tq, r = qr % a.Tq;
-  const int64_t qpos = a.ragged ? a.pos.p[b] : a.q_pos0;   // this sequence's first query
-  const int64_t t = qpos + r;
   // wave as a scalar: the LDS destinations of the tile copies (m0) are then
   // formed with scalar arithmetic instead of a vector add and a readfirstlane
   // per copy
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Every argument the prologue needs is read in one round, before any
+  // branch: each dependent round trip to the argument segment costs a memory
+  // latency, and the compiler would otherwise sink the reads into the
+  // branches that use them, one after another (the empty asm statements pin
+  // them here).
+  const bool flat = a.flat, ragged = a.ragged;
+  const int B = a.B, Tq = a.Tq, H = a.H, W = a.W, splits = a.splits, kk = a.k, m = a.m;
+  const int sel_m = a.sel_m, slot_first = a.slot0[0];
+  const int64_t q_pos0 = a.q_pos0, Ncap = a.Ncap, n_entries = a.n_entries;
+  const uint16_t* const qg = a.q;
+  const uint8_t* const entries = a.entries;
+  const uint8_t* const wing = a.win;
+  const float* const gamma_q = a.gamma_q;
+  const int32_t* const topk = a.topk;
+  asm volatile("" ::"s"(qg), "s"(entries), "s"(wing), "s"(gamma_q), "s"(topk), "s"(q_pos0),
+               "s"(Ncap), "s"(n_entries));
+  asm volatile("" ::"s"((int)flat), "s"((int)ragged), "s"(B), "s"(Tq), "s"(H), "s"(W), "s"(splits),
+               "s"(kk), "s"(m), "s"(sel_m), "s"(slot_first));
+  const double rturn = a.rope.t[lane & 31];
+  // The per-sequence tables are read only where they are used, through the
+  // argument segment's address with a run-time offset (the compiler hoists
+  // reads of `a` out of branches, and a value in flight that is never used
+  // holds its register until the compiler waits for it to reuse that;
+  // taking the address of a member of `a` would copy the whole argument
+  // block to scratch memory).
+  static_assert(kMaxRagged == 64, "one lane per sequence of a flat grid");
+  const char* const my_args =
+      (const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+      offsetof(AttendBatch, p) + (size_t)blockIdx.z * sizeof(AttendArgs);
+  int qr, split, nsplit;
+  int64_t slot;   // this split's partial slot
+  if (flat) {   // ragged decode: workgroup x is slot x of sequence b
+    // lane l: the slot after sequence l's last
+    const int slot_nx =
+        *reinterpret_cast<const int*>(my_args + offsetof(AttendArgs, slot0) + sizeof(int) * (lane + 1));
+    const int x = blockIdx.x;
+    if (x >= __builtin_amdgcn_readlane(slot_nx, B - 1)) return;
+    // slot0 ascends: b = the number of sequences (but the last) whose slots end at or before x
+    const int bb = (int)__popcll(__ballot(lane + 1 < B && x >= slot_nx));
+    const int s0 = bb > 0 ? __builtin_amdgcn_readlane(slot_nx, bb - 1) : slot_first;
+    qr = bb;
+    split = x - s0;
+    nsplit = __builtin_amdgcn_readlane(slot_nx, bb) - s0;
+    slot = x;
+  } else {
+    qr = blockIdx.y;
+    split = blockIdx.x;
+    if (split >= splits) return;   // a layer with fewer splits than the grid
+    nsplit = splits;
+    slot = (int64_t)qr * splits + split;
+  }
+  const int b = qr / Tq, r = qr % Tq;
+  int64_t qpos = q_pos0;   // this sequence's first query
+  if (ragged)
+    qpos = *reinterpret_cast<const int64_t*>(my_args + offsetof(AttendArgs, pos) +
+                                             sizeof(int64_t) * (b & (kMaxRagged - 1)));
+  const int64_t t = qpos + r;
   const int c = lane & 15, g = lane >> 4;   // lane column (head / row / dim), k group
   const int head = wave * 16 + c;
 
@@ -184,8 +227,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   __shared__ __attribute__((aligned(16))) uint8_t s_zero[32];   // K bytes past the E4M3 dims
   __shared__ __attribute__((aligned(16))) float s_gamma[D];      // gamma_q, read per q~ slot
 
-  const RowSpace rs = row_space(a, CSA, t);
-  const int64_t chunk = split_chunk(rs.n_rows, nsplit);
+  const RowSpace rs = row_space(CSA, t, kk, m, n_entries, W);
+  const int64_t chunk = rs.n_rows < (1ll << 31) ? split_chunk32((int)rs.n_rows, nsplit)
+                                                 : split_chunk(rs.n_rows, nsplit);
   const int64_t row_beg = (int64_t)split * chunk;
   int64_t row_end = row_beg + chunk;
   if (row_end > rs.n_rows) row_end = rs.n_rows;
@@ -193,53 +237,48 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   // split-local row numbers fit in 32 bits
   const int nloc = (int)(row_end - row_beg);
   const int ent_loc = (int)max((int64_t)0, min(rs.n_ent, row_end) - row_beg);  // entry rows here
-  const uint8_t* ent_b = a.entries + (int64_t)b * a.Ncap * ROW;
-  const uint8_t* win_b = a.win + ((int64_t)b * (a.Tq + a.W - 1) +
-                                  (rs.win_lo - (qpos - (a.W - 1)))) * ROW;
+  const uint8_t* ent_b = entries + (int64_t)b * Ncap * ROW;
+  const uint8_t* win_b = wing + ((int64_t)b * (Tq + W - 1) + (rs.win_lo - (qpos - (W - 1)))) * ROW;
   const int win_first = (int)(rs.n_ent - row_beg);   // split-local row of the first window row
 
   // The loads the first barrier waits for go out first (a wave's vector loads
-  // complete in order): this split's slice of the top-k list (CSA), the
-  // rotary frequency and gamma_q.  Then q, before the first tile's copies,
-  // so that its loads are not queued behind them; they stay in flight across
-  // the barrier.
+  // complete in order): this split's slice of the top-k list and the top-k
+  // slots of the first tile's rows (CSA), and gamma_q.  Then q, before the
+  // first tile's copies, so that its loads are not queued behind them; they
+  // stay in flight across the barrier.  No load sits in a branch (the
+  // compiler waits for a load inside a branch at once): the top-k slots are
+  // read through a buffer resource over the query's list, an index past it
+  // reading 0, and the other addresses are in bounds for every lane.
   constexpr int SELR = CSA ? kSelCap / kAttThreads : 1;
-  int selv[SELR];
+  int selv[SELR];   // the slot's value as read; turned into a row when stored to LDS
+  int sel0 = 0;     // top-k slot of this lane's row of tile 0 (32 wave + lane % 32)
   if constexpr (CSA) {
-    if (a.sel_m > 1) {   // slots hold blocks of sel_m consecutive rows
-      const int32_t* sel = a.topk + (int64_t)qr * (a.k / a.sel_m);
+    const int nsl = sel_m > 1 ? kk / sel_m : kk;   // list entries per query
+    const __amdgpu_buffer_rsrc_t rsel = buf_rsrc(topk + (int64_t)qr * nsl, (uint32_t)nsl * 4u);
+    const uint32_t past = (uint32_t)nsl * 4u;
 #pragma unroll
-      for (int i = 0; i < SELR; ++i) {
-        const int x = tid + i * kAttThreads;
-        const int p = (int)row_beg + x;
-        const int blk = x < ent_loc ? sel[p / a.sel_m] : -1;
-        selv[i] = blk >= 0 ? blk * a.sel_m + p % a.sel_m : -1;
-      }
-    } else {
-      const int32_t* sel = a.topk + (int64_t)qr * a.k + row_beg;
-#pragma unroll
-      for (int i = 0; i < SELR; ++i) {
-        const int x = tid + i * kAttThreads;
-        selv[i] = x < ent_loc ? sel[x] : 0;
-      }
+    for (int i = 0; i < SELR; ++i) {
+      const int x = tid + i * kAttThreads;
+      const int p = (int)row_beg + x;
+      const uint32_t off = x < ent_loc ? (uint32_t)(sel_m > 1 ? p / sel_m : p) * 4u : past;
+      selv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rsel, off, 0, 0);
     }
+    const int x0 = 32 * wave + (lane & 31);
+    sel0 = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        rsel, x0 < ent_loc && sel_m <= 1 ? (uint32_t)((int)row_beg + x0) * 4u : past, 0, 0);
   }
-  const double rturn = tid < R / 2 ? a.rope.t[tid] : 0.0;
-  f32x4 gv = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (tid < D / 4) gv = reinterpret_cast<const f32x4*>(a.gamma_q)[tid];
+  const f32x4 gv = reinterpret_cast<const f32x4*>(gamma_q)[tid & (D / 4 - 1)];
   constexpr int NSL = 4 * NJ + 2;
   auto slot_dim = [&](int sl) {
     return sl < 4 * NJ ? 128 * (sl >> 2) + 32 * g + 8 * (sl & 3) : (D - R) + 32 * (sl - 4 * NJ) + 8 * g;
   };
   // slots of the last E4M3 k-step beyond the E4M3 dims stay zero
   auto slot_ok = [&](int sl) { return sl >= 4 * NJ || slot_dim(sl) < D - R; };
-  const uint16_t* qp = a.q + ((int64_t)qr * a.H + min(head, a.H - 1)) * D;
+  // (slots past the E4M3 dims read rotary dims, in the row; they count as zero)
+  const uint16_t* qp = qg + ((int64_t)qr * H + min(head, H - 1)) * D;
   u32x4 qv[NSL];
 #pragma unroll
-  for (int sl = 0; sl < NSL; ++sl) {
-    qv[sl] = u32x4{0u, 0u, 0u, 0u};
-    if (slot_ok(sl)) qv[sl] = *reinterpret_cast<const u32x4*>(qp + slot_dim(sl));
-  }
+  for (int sl = 0; sl < NSL; ++sl) qv[sl] = *reinterpret_cast<const u32x4*>(qp + slot_dim(sl));
 
   // ---- staging: wave w copies tile rows 32w..32w+31 as WPW windows of 64
   // 16-byte slots; slot s holds physical chunk s % CPR of row s / CPR, loaded
@@ -301,13 +340,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   // list (the LDS copy of the split's slice serves the later tiles).
   bool early0 = false;
   if constexpr (CSA) {
-    if (!base0 && ntiles > 0 && a.sel_m <= 1) {
+    if (!base0 && ntiles > 0 && sel_m <= 1) {
       const int x = 32 * wave + (lane & 31);
       const uint8_t* rp = nullptr;
       if (x < nloc) {
         if (x < ent_loc) {
-          const int64_t j = a.topk[(int64_t)qr * a.k + row_beg + x];
-          if (j >= 0 && j < a.Ncap) rp = ent_b + j * ROW;
+          const int64_t j = sel0;
+          if (j >= 0 && j < Ncap) rp = ent_b + j * ROW;
         } else {
           rp = win_b + (int64_t)(x - win_first) * ROW;
         }
@@ -327,7 +366,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
 #pragma unroll
     for (int i = 0; i < SELR; ++i) {
       const int x = tid + i * kAttThreads;
-      if (x < ent_loc) s_sel[x] = selv[i];
+      const int p = (int)row_beg + x;
+      // sel_m > 1: the slot holds a block of sel_m rows (-1: empty)
+      const int row = sel_m > 1 ? (selv[i] >= 0 ? selv[i] * sel_m + p % sel_m : -1) : selv[i];
+      if (x < ent_loc) s_sel[x] = row;
     }
   }
   if (tid < 8) reinterpret_cast<unsigned*>(s_zero)[tid] = 0u;
@@ -375,7 +417,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
   bf16x8 qt[2];
   float qscale_inv;   // 2^-qe
   {
-    if (head >= a.H) {
+    if (head >= H) {
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl) qv[sl] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -391,7 +433,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
       const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_bits_to_f32(qv[sl][e] & 0xFFFFu), hi = bf16_bits_to_f32(qv[sl][e] >> 16);
+        const bool ok = slot_ok(sl);
+        const float lo = ok ? bf16_bits_to_f32(qv[sl][e] & 0xFFFFu) : 0.f;
+        const float hi = ok ? bf16_bits_to_f32(qv[sl][e] >> 16) : 0.f;
         ss += lo * lo + hi * hi;
         const float glo = gm[2 * e] * lo, ghi = gm[2 * e + 1] * hi;
         if (sl >= 4 * NJ) mr2 = fmaxf(mr2, glo * glo + ghi * ghi);
@@ -828,15 +872,41 @@ template <int D>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   const AttendArgs& a = ab.p[blockIdx.z];
   const int qr = blockIdx.y;
-  if (qr >= a.B * a.Tq) return;
-  const int S = a.flat ? a.slot0[qr + 1] - a.slot0[qr] : a.splits;
+  // every argument read in one round before any branch, as in attend_kernel
+  const bool flat = a.flat, ragged = a.ragged;
+  const int B = a.B, Tq = a.Tq, H = a.H, splits = a.splits;
+  const int64_t q_pos0 = a.q_pos0;
+  const uint16_t* const part_o = a.part_o;
+  const float* const part_ml = a.part_ml;
+  const float* const sink = a.sink;
+  float* const lse = a.lse;
+  uint16_t* const out = a.out;
+  const float* const mix_gates = a.mix_gates;
+  asm volatile("" ::"s"(part_o), "s"(part_ml), "s"(sink), "s"(lse), "s"(out), "s"(mix_gates),
+               "s"(q_pos0));
+  asm volatile("" ::"s"((int)flat), "s"((int)ragged), "s"(B), "s"(Tq), "s"(H), "s"(splits));
+  const double rturn = a.rope.t[threadIdx.x & 31];
+  if (qr >= B * Tq) return;
+  // the per-sequence tables through the argument segment's address (see attend_kernel)
+  const char* const my_args = (const char*)__builtin_amdgcn_kernarg_segment_ptr() +
+                              offsetof(AttendBatch, p) + (size_t)blockIdx.z * sizeof(AttendArgs);
+  int S = splits;
+  int64_t slot0 = (int64_t)qr * S;   // this query's first partial slot
+  if (flat) {
+    const int* sl = reinterpret_cast<const int*>(my_args + offsetof(AttendArgs, slot0)) + qr;
+    slot0 = sl[0];
+    S = sl[1] - sl[0];
+  }
   if (S <= 1) return;   // the attention kernel stored this query's output itself
-  const int64_t slot0 = a.flat ? a.slot0[qr] : (int64_t)qr * S;   // its first partial slot
+  int64_t qpos = q_pos0;
+  if (ragged)
+    qpos = *reinterpret_cast<const int64_t*>(my_args + offsetof(AttendArgs, pos) +
+                                             sizeof(int64_t) * ((qr / Tq) & (kMaxRagged - 1)));
   constexpr int R = 64;
   constexpr int QPH = D / 4;          // threads per head (four dims each)
   constexpr int HPW = 256 / QPH;      // heads per workgroup
   const int h0 = blockIdx.x * HPW;
-  const int64_t t = (a.ragged ? a.pos.p[qr / a.Tq] : a.q_pos0) + (qr % a.Tq);
+  const int64_t t = qpos + (qr % Tq);
   __shared__ float s_w[HPW][64];
   __shared__ float s_cs[R / 2][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -846,10 +916,10 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   constexpr int kSp = 16;
   const int hh = tid / QPH, d = 4 * (tid % QPH);
   const int h = h0 + hh;
-  const bool mine = hh < HPW && h < a.H;
-  const int64_t sstride = (int64_t)a.H * D;   // elements between a query's split slots
+  const bool mine = hh < HPW && h < H;
+  const int64_t sstride = (int64_t)H * D;   // elements between a query's split slots
   const __amdgpu_buffer_rsrc_t rs =
-      buf_rsrc(a.part_o + slot0 * sstride, (uint32_t)(S * sstride * 2));
+      buf_rsrc(part_o + slot0 * sstride, (uint32_t)(S * sstride * 2));
   const uint32_t voff = mine ? (uint32_t)((h * D + d) * 2) : 0x7FFFFF00u;
   u32x2 v0[kSp];
 #pragma unroll
@@ -859,18 +929,28 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   }
   if (tid < R / 2) {
     float cs, sn;
-    rope_cos_sin(t, a.rope.t[tid], &cs, &sn);
+    rope_cos_sin(t, rturn, &cs, &sn);
     s_cs[tid][0] = cs;
     s_cs[tid][1] = sn;
   }
   for (int hw = wave; hw < HPW; hw += 4) {
     const int hx = h0 + hw;
-    if (hx >= a.H) break;
-    const float* pm = a.part_ml + (slot0 * a.H + hx) * 4;
+    if (hx >= H) break;
+    // both records of the head through buffer resources (no load in a
+    // branch: the compiler would wait for each at once): split `lane`'s
+    // (max, sum, e), reading 0 past the S splits, and the sink
     const bool own = lane < S;
-    const f32x4 ml = own ? *reinterpret_cast<const f32x4*>(pm + (int64_t)lane * a.H * 4)
+    const __amdgpu_buffer_rsrc_t rml =
+        buf_rsrc(part_ml + (slot0 * H + hx) * 4, (uint32_t)(S * H * 16));
+    const __amdgpu_buffer_rsrc_t rsk = buf_rsrc(sink, (uint32_t)(H * 4));
+    const auto mlv = __builtin_amdgcn_raw_buffer_load_b128(
+        rml, own ? (uint32_t)(lane * H * 16) : 0x7FFFFF00u, 0, 0);
+    const unsigned skv = __builtin_amdgcn_raw_buffer_load_b32(
+        rsk, sink ? (uint32_t)(hx * 4) : 0x7FFFFF00u, 0, 0);
+    const f32x4 ml = own ? f32x4{__uint_as_float(mlv[0]), __uint_as_float(mlv[1]),
+                                 __uint_as_float(mlv[2]), __uint_as_float(mlv[3])}
                          : f32x4{-INFINITY, 0.f, 0.f, 0.f};
-    const float z2 = a.sink ? a.sink[hx] * kLog2e : -INFINITY;
+    const float z2 = sink ? __uint_as_float(skv) * kLog2e : -INFINITY;
     const float M = fmaxf(wave_max(ml.x), z2);
     const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
     float den = wave_sum(ml.y * w);
@@ -878,8 +958,8 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
     const float inv = den > 0.f ? 1.0f / den : 0.f;
     // also undoes the partial's scale: O = q 2^e / 32767
     s_w[hw][lane] = ldexpf(w * inv, (int)ml.z) * (1.0f / 32767.0f);
-    if (a.lse && lane == 0)
-      a.lse[(int64_t)qr * a.H + hx] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
+    if (lse && lane == 0)
+      lse[(int64_t)qr * H + hx] = den > 0.f ? (M + log2f(den)) * 0.69314718055994531f : -INFINITY;
   }
   __syncthreads();
   if (!mine) return;
@@ -890,7 +970,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
   f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < kSp; ++u) add(x, u < S ? s_w[hh][u] : 0.f, v0[u]);
-  const uint16_t* po = a.part_o + (slot0 * a.H + h) * D + d;
+  const uint16_t* po = part_o + (slot0 * H + h) * D + d;
   for (int s0 = kSp; s0 < S; s0 += 8) {   // more splits: eight partials in flight
     u32x2 v[8];
 #pragma unroll
@@ -910,8 +990,8 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendBatch ab) {
       y[e + 1] = -x0 * sn + x1 * cs;
     }
   }
-  const int64_t qh = (int64_t)qr * a.H + h;
-  *reinterpret_cast<u32x2*>(a.out + qh * D + d) = final_bf16x4<true>(a, qh * D + d, qh, y);
+  const int64_t qh = (int64_t)qr * H + h;
+  *reinterpret_cast<u32x2*>(out + qh * D + d) = final_bf16x4<true>(a, qh * D + d, qh, y);
 }
 
 int attend_splits(int B, int Tq, int64_t rows_max, bool csa, int wg_budget) {
