@@ -55,6 +55,12 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
   constexpr int P = RB / 16;         // 16-byte pieces per key row
   constexpr int KPI = 64 / P;        // keys per load instruction
   constexpr int NL = 32 / KPI;       // load instructions per 32-key chunk
+  // every argument read in one round before any branch (each dependent round
+  // trip to the argument segment costs a memory latency; the empty asm
+  // statements keep the compiler from issuing the reads where first used)
+  asm volatile("" ::"s"(a.q_idx), "s"(a.w_idx), "s"(a.k_idx), "s"(a.Ncap), "s"(a.n_entries),
+               "s"(a.q_pos0), "s"(a.scores), "s"(a.score_stride));
+  asm volatile("" ::"s"(a.B), "s"(a.Tq), "s"(a.HI), "s"(a.m), "s"((int)a.ragged));
   int b = blockIdx.z, blk = blockIdx.x, nblk = gridDim.x;
   const int r = blockIdx.y;
   if (a.ragged && a.Tq == 1) {   // flat grid: find this workgroup's sequence
@@ -65,7 +71,9 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = (a.ragged ? a.pos.p[b] : a.q_pos0) + r;
-  int64_t V = (t + 1) / a.m;
+  // positions below 2^31 take the 32-bit division
+  int64_t V = (uint64_t)(t + 1) < (1ull << 31) ? (int64_t)((uint32_t)(t + 1) / (uint32_t)a.m)
+                                               : (t + 1) / a.m;
   if (V > a.n_entries) V = a.n_entries;
   // 32-key chunks are dealt round-robin over the row's waves, so at any time
   // the waves of a row read one compact front of the key array

@@ -75,9 +75,28 @@ TopkPlan topk_plan(int64_t vmin, int64_t vmax, int k) {
 }
 
 __device__ __forceinline__ int64_t visible_of(const TopkArgs& a, int64_t qr) {
-  const int64_t t = (a.ragged ? a.pos.p[qr / a.Tq] : a.q_pos0) + (qr % a.Tq);
-  const int64_t v = (t + 1) / a.m;
+  const int Tq = a.Tq;   // rows below 2^31 take 32-bit divisions
+  const int64_t b = qr < (1ll << 31) ? (int64_t)((uint32_t)qr / (uint32_t)Tq) : qr / Tq;
+  const int64_t t = (a.ragged ? a.pos.p[b] : a.q_pos0) + (qr - b * Tq);
+  const int64_t v = (uint64_t)(t + 1) < (1ull << 31) ? (int64_t)((uint32_t)(t + 1) / (uint32_t)a.m)
+                                                     : (t + 1) / a.m;
   return v < a.n_entries ? v : a.n_entries;
+}
+
+// Every argument read in one round at the top of a kernel, before any
+// branch: each dependent round trip to the argument segment costs a memory
+// latency, and the compiler would otherwise issue the reads where they are
+// first used, one round after another (the empty asm statements pin them).
+__device__ __forceinline__ void read_args(const TopkArgs& a) {
+  asm volatile("" ::"s"(a.scores), "s"(a.score_stride), "s"(a.q_pos0), "s"(a.n_entries),
+               "s"(a.direct_max), "s"(a.part_tau), "s"(a.part_cnt), "s"(a.part_over));
+  asm volatile("" ::"s"(a.cand_key), "s"(a.cand_idx), "s"(a.topk), "s"(a.topk_score),
+               "s"(a.run_key), "s"(a.Tq), "s"(a.m), "s"(a.k), "s"(a.nparts), "s"((int)a.ragged));
+}
+
+// Parts of a row of V entries with parts of P (a power of two) entries.
+__device__ __forceinline__ int64_t parts_of(int64_t V, int P) {
+  return (V + P - 1) >> __builtin_ctz((unsigned)P);
 }
 
 // Exclusive scan of one value per thread across the block; returns the
@@ -126,14 +145,15 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 __device__ __forceinline__ void load_part(const TopkArgs& a, int64_t qr, int64_t V, int64_t base,
                                           int P, int lane, unsigned (&key)[16]) {
   const float* src = a.scores + qr * a.score_stride;
-  const int kpl = P >> 6;
   int64_t end = base + P;
   if (end > V) end = V;
+  // every load is issued (a load in a branch is waited for at once); one
+  // past the part or the row re-reads the part's first score (base < V)
   float f[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t i = base + 64 * r + lane;
-    f[r] = r < kpl ? src[i < V ? i : (V > 0 ? V - 1 : 0)] : 0.f;
+    f[r] = src[i < end ? i : base];
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) key[r] = base + 64 * r + lane < end ? score_key(f[r]) : 0u;
@@ -143,13 +163,14 @@ __device__ __forceinline__ void load_part(const TopkArgs& a, int64_t qr, int64_t
 // lanes hold a valid key), then the part's keys >= max(x_p, 1) in position
 // order, the first kTopkPartCap stored, the largest of the rest recorded.
 __global__ __launch_bounds__(256) void topk_part_kernel(TopkArgs a) {
+  read_args(a);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t qr = blockIdx.y;
   const int p = blockIdx.x * 4 + wave;
   const int64_t V = visible_of(a, qr);
   if (V <= a.direct_max) return;   // such a row is selected directly
   const int P = topk_part_len(V, a.k);
-  if (p >= (V + P - 1) / P) return;   // past this row's parts
+  if (p >= parts_of(V, P)) return;   // past this row's parts
   const int64_t base = (int64_t)p * P;
   unsigned x = 0u, over = 0u;
   int cnt = 0;
@@ -584,28 +605,33 @@ __device__ __forceinline__ bool topk_select_fast(const TopkArgs& a, unsigned* sm
   const int* ci = a.cand_idx + qr * (int64_t)ns * kTopkPartCap;
   const int q = tid / TPP, s0 = (tid % TPP) * KPT;   // part, first slot
   const bool own = q < np;
-  const int cpart = own ? min(a.part_cnt[qr * ns + q], kTopkPartCap) : 0;
-  const int cq = max(0, min(cpart - s0, KPT));          // this thread's stored leaders
   const bool lead = own && s0 == 0;                     // the part's record holder
-  const unsigned tau = lead ? a.part_tau[qr * ns + q] : 0u;
-  const unsigned over = lead ? a.part_over[qr * ns + q] : 0u;
+  // Every record and leader load is issued before any is used (a load in a
+  // branch is waited for at once): a thread past the row's parts reads part
+  // np - 1's (np >= 1 here) and drops it.
+  const int qc = own ? q : np - 1;
+  const int cnt_raw = a.part_cnt[qr * ns + qc];
+  const unsigned tau_raw = a.part_tau[qr * ns + qc];
+  const unsigned over_raw = a.part_over[qr * ns + qc];
+  u32x4 kk[KPT / 4], ii[KPT / 4];
+#pragma unroll
+  for (int u = 0; u < KPT / 4; ++u) {
+    kk[u] = *reinterpret_cast<const u32x4*>(ck + qc * kTopkPartCap + s0 + 4 * u);
+    ii[u] = *reinterpret_cast<const u32x4*>(ci + qc * kTopkPartCap + s0 + 4 * u);
+  }
+  const int cpart = own ? min(cnt_raw, kTopkPartCap) : 0;
+  const int cq = max(0, min(cpart - s0, KPT));          // this thread's stored leaders
+  const unsigned tau = lead ? tau_raw : 0u;
+  const unsigned over = lead ? over_raw : 0u;
   unsigned key[KPT];
   int idx[KPT];
-  if (own) {
 #pragma unroll
-    for (int u = 0; u < KPT / 4; ++u) {
-      const u32x4 kk = *reinterpret_cast<const u32x4*>(ck + q * kTopkPartCap + s0 + 4 * u);
-      const u32x4 ii = *reinterpret_cast<const u32x4*>(ci + q * kTopkPartCap + s0 + 4 * u);
+  for (int u = 0; u < KPT / 4; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        key[4 * u + e] = 4 * u + e < cq ? kk[e] : 0u;
-        idx[4 * u + e] = (int)ii[e];
-      }
+    for (int e = 0; e < 4; ++e) {
+      key[4 * u + e] = 4 * u + e < cq ? kk[u][e] : 0u;
+      idx[4 * u + e] = (int)ii[u][e];
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = 0u;
-  }
   // range of the present leaders and their number
   unsigned kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
@@ -734,9 +760,10 @@ __device__ __forceinline__ bool topk_select_fast(const TopkArgs& a, unsigned* sm
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   extern __shared__ unsigned smem[];
+  read_args(a);
   const int64_t qr = blockIdx.x;
   const int64_t V = visible_of(a, qr);
-  const int np = V > a.direct_max ? (int)((V + topk_part_len(V, a.k) - 1) / topk_part_len(V, a.k)) : 0;
+  const int np = V > a.direct_max ? (int)parts_of(V, topk_part_len(V, a.k)) : 0;
   if (V > a.direct_max && np <= kSelThreads / 2) {
     if (topk_select_fast<kTopkPartCap / 2>(a, smem, qr, np)) return;
   } else if (V > a.direct_max && np <= kSelThreads) {
