@@ -762,9 +762,15 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
         issue_tile(tile + 1, cur ^ 1);
       }
       T = s_tile[cur];
-      qk(T, cur, sacc, mp, mo, [&](int st) {
-        if (st < G::WPW && nbase) issue_copy(nbase, cur ^ 1, st);
-      });
+      // two instances of the step sequence, so that no branch splits it (a
+      // branch around each copy let the compiler move the MFMAs of several
+      // steps past the loads and copies of the next ones)
+      if (nbase)
+        qk(T, cur, sacc, mp, mo, [&](int st) {
+          if (st < G::WPW) issue_copy(nbase, cur ^ 1, st);
+        });
+      else
+        qk(T, cur, sacc, mp, mo, [](int) {});
       if (!CSA && a.logits2 && head < a.H) {   // the tile's logits (log2 units; absent rows -inf)
         float* lp = a.logits2 + ((int64_t)qr * a.logits_stride + row_beg +
                                  (int64_t)tile * kAttRows + 4 * g) * 64 + head;
