@@ -102,11 +102,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// Wave-wide inclusive scan on the DPP lane paths: shifts by 1, 2, 4 and 8
+// lanes within each row of 16 lanes, then the broadcasts of lanes 15 and 31
+// into the rows after them.  Six dependent VALU steps; a shuffle by index
+// takes a round trip through the LDS unit (ds_bpermute) per step.  Lanes a
+// step does not write take `ident`, the identity of op.
+template <typename Op>
+__device__ __forceinline__ int wave_incl_scan_i(int x, int ident, Op op) {
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
+}
+
+// Reductions over the wave (every lane gets the result): the scan's last lane.
+__device__ __forceinline__ unsigned wave_min_u(unsigned v) {
+  const int x = wave_incl_scan_i((int)v, -1, [](int a, int b) { return (int)min((unsigned)a, (unsigned)b); });
+  return (unsigned)__builtin_amdgcn_readlane(x, 63);
+}
+__device__ __forceinline__ unsigned wave_max_u(unsigned v) {
+  const int x = wave_incl_scan_i((int)v, 0, [](int a, int b) { return (int)max((unsigned)a, (unsigned)b); });
+  return (unsigned)__builtin_amdgcn_readlane(x, 63);
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan_i(v, 0, [](int a, int b) { return a + b; }), 63);
+}
+// fmaxf is order-independent, so this equals the butterfly it replaces
+__device__ __forceinline__ float wave_max(float v) {
+  const int x = wave_incl_scan_i(__float_as_int(v), __float_as_int(-INFINITY), [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  });
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -103,12 +103,7 @@ __device__ __forceinline__ int64_t parts_of(int64_t V, int P) {
 // prefix and writes the block total to *total.
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan_i(v, 0, [](int a, int b) { return a + b; });
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   int before = 0, all = 0;
@@ -123,21 +118,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
   return before + x - v;
 }
 
-__device__ __forceinline__ unsigned wave_min_u(unsigned v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o));
-  return v;
-}
-__device__ __forceinline__ unsigned wave_max_u(unsigned v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o));
-  return v;
-}
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // The keys of lane `lane` in the part starting at `base` of row qr:
 // positions base + 64r + lane for r < P / 64 (absent past the part
