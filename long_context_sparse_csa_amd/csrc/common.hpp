@@ -138,16 +138,17 @@ __device__ __forceinline__ float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 
+// The sum in scan order (lane 0 first), not a butterfly: the same value in
+// every lane, rounded as that order rounds it.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  const int x = wave_incl_scan_i(__float_as_int(v), 0, [](int a, int b) {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b));
+  });
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 
 __device__ __forceinline__ unsigned wave_sum_u(unsigned v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return (unsigned)wave_sum_i((int)v);
 }
 
 // Order-preserving map of a float score to an unsigned key: larger float ->
