@@ -442,11 +442,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
         else mb = fmaxf(mb, fmaxf(fabsf(glo), fabsf(ghi)));
       }
     }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
+    ss = lane_pair<16>(ss, [](float a, float b) { return a + b; });
+    ss = lane_pair<32>(ss, [](float a, float b) { return a + b; });
     mb = fmaxf(mb, sqrtf(mr2));
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    mb = lane_pair<16>(mb, [](float a, float b) { return fmaxf(a, b); });
+    mb = lane_pair<32>(mb, [](float a, float b) { return fmaxf(a, b); });
     const float rsn = 1.0f / sqrtf(ss / (float)D + a.eps);
     // 2^qe puts the bound (so every |q~|) at most 256, the largest near it
     const float mx = mb * rsn;
@@ -625,8 +625,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[rb][i]);
       m *= sl2;
-      mp[h] = fmaxf(m, __shfl_xor(m, 16));
-      mo[h] = __shfl_xor(mp[h], 32);
+      mp[h] = lane_pair<16>(m, [](float a, float b) { return fmaxf(a, b); });
+      mo[h] = lane_xor32(mp[h]);
     }
   };
   //  pv: online softmax of the tile against the running max m_run, then
@@ -803,8 +803,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
 
   if (head >= a.H) return;
   // full denominator of this lane's head: all four lane groups
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = lane_pair<16>(l_run, [](float a, float b) { return a + b; });
+  l_run = lane_pair<32>(l_run, [](float a, float b) { return a + b; });
   // accumulator i of block db holds dim 16 db + 4g + i
   if (nsplit > 1) {
     // unnormalised partial O in block floating point: 16-bit signed
@@ -818,8 +818,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendBatch ab) {
     for (int db = 0; db < NB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[db][i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = lane_pair<16>(amax, [](float a, float b) { return fmaxf(a, b); });
+    amax = lane_pair<32>(amax, [](float a, float b) { return fmaxf(a, b); });
     const int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;   // amax < 2^ex
     const float to_unit = ldexpf(1.0f, -ex);   // |O| 2^-ex < 1: snorm16 = round(32767 |O| 2^-ex)
     uint16_t* po = a.part_o + (slot * a.H + head) * D;

@@ -118,6 +118,34 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int ident, Op op) {
   return x;
 }
 
+// Exchanges between lanes l and l ^ 16 or l ^ 32 through the gfx950 lane
+// swaps (v_permlane16_swap / v_permlane32_swap, no trip through the LDS
+// unit).  Swapping a value with itself leaves, in every lane, the two values
+// of its pair of rows (16 swap) or halves (32 swap) in the two results,
+// in row order: the first result holds the even row's (lower half's) value
+// in both rows of the pair, the second the odd row's (upper half's).
+__device__ __forceinline__ float lane_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+// x combined with its lane ^ 16 (ROWS = 16) or lane ^ 32 partner; commutative
+// ops only (the two lanes of a pair compute op(even, odd) alike)
+template <int ROWS, typename Op>
+__device__ __forceinline__ float lane_pair(float x, Op op) {
+  const unsigned u = __float_as_uint(x);
+  if constexpr (ROWS == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+
 // Reductions over the wave (every lane gets the result): the scan's last lane.
 __device__ __forceinline__ unsigned wave_min_u(unsigned v) {
   const int x = wave_incl_scan_i((int)v, -1, [](int a, int b) { return (int)min((unsigned)a, (unsigned)b); });
