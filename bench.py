@@ -60,8 +60,8 @@ COPY_BYTES = 1 << 30           # calibration copy for the HBM byte counters
 # for torch's elementwise kernel over 1 GiB in and 1 GiB out (FETCH 524,318
 # KiB -> x2.0; WRITE 1,048,576 KiB -> x1.0).  Valid only for the kernel
 # sources they were taken with (hash below); otherwise reported as null.
-TRAFFIC = {"sources_sha256_16": "67642e004e42418f",
-           "fetch_kib": 262707.9, "fetch_scale": 2.0,
+TRAFFIC = {"sources_sha256_16": "cc2d1ee3cd142591",
+           "fetch_kib": 262708.0, "fetch_scale": 2.0,
            "write_kib": 8192.0, "write_scale": 1.0}
 TRAFFIC_SOURCES = ("long_context_sparse_csa_amd/csrc/indexer.hip",
                    "long_context_sparse_csa_amd/csrc/common.hpp")
