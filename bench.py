@@ -489,7 +489,7 @@ def backward_section(dev, reps):
              "d_win": torch.zeros((1, Tq + W - 1, D), dtype=torch.float32, device=dev),
              "d_sink": torch.zeros(H, dtype=torch.float32, device=dev),
              "d_gamma_q": torch.zeros(D, dtype=torch.float32, device=dev)}
-    ws = torch.empty(ops.lib().v4attn_csa_attend_backward_workspace(1, Tq, H, D, k, W),
+    ws = torch.empty(ops.lib().v4attn_csa_attend_backward_workspace(1, Tq, H, D, k, W, Nc),
                      dtype=torch.uint8, device=dev)
     att = lambda: ops.csa_attend_backward(q, ent, topk, win, gq, sink, out, lse, dout, q_pos0=P,
                                           W=W, grads=grads, p_sel=p_sel, workspace=ws)

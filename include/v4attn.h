@@ -488,14 +488,22 @@ int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries,
  *   d_sink f32 [H], d_gamma_q f32 [D]: added to; nullable
  *   p_sel f32 [B, Tq, k] (CSA only, nullable): written with sum_h p_hx of
  *            every top-k slot (0 for -1 slots): the indexer loss's target
- *   ws / ws_bytes >= the matching *_backward_workspace(...) bytes
+ *   ws / ws_bytes: device workspace, 16-byte aligned.  With the bytes the
+ *            matching *_backward_workspace(...) query returns, the row
+ *            gradients are grouped: every (query, row slot) gradient is
+ *            stored densely (at most 12 GiB per group of queries), the slots
+ *            are sorted by destination row and each row is added to once.
+ *            A smaller workspace, down to the per-chunk buffers alone (the
+ *            minimum V4ATTN_EWORKSPACE reports), adds the row gradients
+ *            with fp32 atomics instead; the results agree to rounding.
  * Arithmetic: every attended row is gathered as bf16 (exact); q~, do and the
  * probabilities and dl enter bf16 matrix-core products with fp32
- * accumulation.  Row gradients use fp32 atomics, so their summation order
- * (and last bits) vary from run to run when rows are shared.
+ * accumulation.  A row shared by several queries gets their gradients in an
+ * order that varies from run to run (the sort by destination, or the
+ * atomics), so the last bits of those rows vary too.
  */
 size_t v4attn_csa_attend_backward_workspace(int B, int Tq, int H, int D,
-                                            int k, int W);
+                                            int k, int W, int64_t Ncap);
 int v4attn_csa_attend_backward(const uint16_t* q, const uint8_t* entries,
                                const int32_t* topk, const uint8_t* win,
                                const float* gamma_q, const float* sink,
@@ -509,7 +517,8 @@ int v4attn_csa_attend_backward(const uint16_t* q, const uint8_t* entries,
                                size_t ws_bytes, void* stream);
 size_t v4attn_hca_attend_backward_workspace(int B, int Tq, int H, int D,
                                             int64_t n_entries, int m,
-                                            int64_t q_pos0, int W);
+                                            int64_t q_pos0, int W,
+                                            int64_t Ncap);
 int v4attn_hca_attend_backward(const uint16_t* q, const uint8_t* entries,
                                const uint8_t* win, const float* gamma_q,
                                const float* sink, int B, int Tq, int H, int D,

@@ -992,6 +992,40 @@ size_t bwd_ws(int B, int Tq, int D, int64_t rows_max) {
   return (size_t)bwd_chunk(nq, D, np) * v4::bwd_query_bytes(D, np);
 }
 
+// Grouped row gradients: destinations (entry rows, then window rows), and
+// the queries per group: a whole multiple of the query chunk (or all
+// queries) whose dense gradients fit both 12 GiB and what the workspace holds
+// beyond the per-chunk buffers; 0 (atomic row gradients) when not even one
+// chunk fits or the ids overflow 32 bits.
+int64_t bwd_ndest(int B, int Tq, int W, int64_t Ncap) {
+  return (int64_t)B * Ncap + (W > 0 ? (int64_t)B * (Tq + W - 1) : 0);
+}
+int64_t bwd_group_queries(int B, int Tq, int D, int64_t rows_max, int64_t ndest,
+                          size_t ws_bytes) {
+  const int64_t nq = (int64_t)B * Tq;
+  const int64_t np = v4::bwd_rows_padded(rows_max > 0 ? rows_max : 1);
+  if (nq == 0 || ndest + 1 >= ((int64_t)1 << 31) || nq * np >= ((int64_t)1 << 31)) return 0;
+  const int64_t qc = bwd_chunk(nq, D, np);
+  const size_t base = bwd_ws(B, Tq, D, rows_max);
+  const auto fits = [&](int64_t g) {
+    const size_t need = base + v4::bwd_group_bytes(D, np, g, ndest);
+    return need <= ws_bytes && (size_t)g * np * D * 4 <= ((size_t)12 << 30);
+  };
+  if (fits(nq)) return nq;
+  int64_t lo = 0, hi = (nq - 1) / qc;  // chunks per group: fits(lo * qc) holds or lo = 0
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (fits(mid * qc)) lo = mid; else hi = mid - 1;
+  }
+  return lo * qc;
+}
+size_t bwd_ws_grouped(int B, int Tq, int D, int64_t rows_max, int W, int64_t Ncap) {
+  const int64_t np = v4::bwd_rows_padded(rows_max > 0 ? rows_max : 1);
+  const int64_t nd = bwd_ndest(B, Tq, W, Ncap);
+  const int64_t gq = bwd_group_queries(B, Tq, D, rows_max, nd, ~(size_t)0);
+  return bwd_ws(B, Tq, D, rows_max) + v4::bwd_group_bytes(D, np, gq, nd);
+}
+
 int run_backward(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
                  const uint8_t* win, const float* gamma_q, const float* sink, int B, int Tq, int H,
                  int D, int R, int64_t Ncap, int k, int64_t n_entries, int m, int W,
@@ -1007,6 +1041,9 @@ int run_backward(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
   const size_t need = bwd_ws(B, Tq, D, rows_max);
   if (!ws || ws_bytes < need)
     return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  // the grouped row gradients when the workspace holds them, else atomics
+  const int64_t ndest = bwd_ndest(B, Tq, W, Ncap);
+  const int64_t gq = bwd_group_queries(B, Tq, D, rows_max, ndest, ws_bytes);
   if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
   const int64_t nq = (int64_t)B * Tq;
   if (nq == 0) return hip_status(hipSuccess, "");
@@ -1019,15 +1056,17 @@ int run_backward(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
   a.np = v4::bwd_rows_padded(rows_max > 0 ? rows_max : 1);
   a.dq = dq; a.d_entries = d_entries; a.d_win = d_win; a.d_sink = d_sink; a.d_gamma_q = d_gamma_q;
   a.p_sel = p_sel; a.k_sel = topk ? k : 0;
-  return hip_status(v4::launch_attend_backward(a, bwd_chunk(nq, D, a.np), ws, (hipStream_t)stream),
+  a.nent = (int64_t)B * Ncap; a.ndest = ndest;
+  return hip_status(v4::launch_attend_backward(a, bwd_chunk(nq, D, a.np), gq, ws, (hipStream_t)stream),
                     "attention backward launch");
 }
 
 }  // namespace
 
-size_t v4attn_csa_attend_backward_workspace(int B, int Tq, int H, int D, int k, int W) {
-  if (B < 0 || Tq < 0 || H < 1 || D < 1 || k < 1 || W < 0) return 0;
-  return bwd_ws(B, Tq, D, (int64_t)k + W);
+size_t v4attn_csa_attend_backward_workspace(int B, int Tq, int H, int D, int k, int W,
+                                            int64_t Ncap) {
+  if (B < 0 || Tq < 0 || H < 1 || D < 1 || k < 1 || W < 0 || Ncap < 0) return 0;
+  return bwd_ws_grouped(B, Tq, D, (int64_t)k + W, W, Ncap);
 }
 
 int v4attn_csa_attend_backward(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
@@ -1049,9 +1088,11 @@ int v4attn_csa_attend_backward(const uint16_t* q, const uint8_t* entries, const 
 }
 
 size_t v4attn_hca_attend_backward_workspace(int B, int Tq, int H, int D, int64_t n_entries, int m,
-                                            int64_t q_pos0, int W) {
-  if (B < 0 || Tq < 0 || H < 1 || D < 1 || n_entries < 0 || m < 1 || q_pos0 < 0 || W < 0) return 0;
-  return bwd_ws(B, Tq, D, vmax_of(Tq, n_entries, q_pos0, m) + W);
+                                            int64_t q_pos0, int W, int64_t Ncap) {
+  if (B < 0 || Tq < 0 || H < 1 || D < 1 || n_entries < 0 || m < 1 || q_pos0 < 0 || W < 0 ||
+      Ncap < 0)
+    return 0;
+  return bwd_ws_grouped(B, Tq, D, vmax_of(Tq, n_entries, q_pos0, m) + W, W, Ncap);
 }
 
 int v4attn_hca_attend_backward(const uint16_t* q, const uint8_t* entries, const uint8_t* win,

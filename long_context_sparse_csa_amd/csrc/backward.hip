@@ -15,9 +15,11 @@
 //     dq~       = (scale dL) X
 //     dX        = [scale dL; P]^T Y        (key and value paths at once)
 // with P = exp(scale S - lse) and dL = P (dP - D), D_h = dout_h . out_h, in
-// between (an elementwise kernel).  dX rows are added into the caller's
-// row gradients with atomics (a row may be attended by many queries); dq~
-// goes back through RoPE_t and the RMSNorm.
+// between (an elementwise kernel).  A row may be attended by many queries:
+// with room in the workspace, every slot's dX row is stored densely, the
+// slots are sorted by destination row (a counting sort) and each row's
+// gradient is added once; otherwise the dX rows are added with atomics.
+// dq~ goes back through RoPE_t and the RMSNorm.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -36,6 +38,21 @@ __device__ __forceinline__ uint16_t f2bf(float f) {   // round to nearest even (
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// The tile (x, y) and batch z of this workgroup in a batched launch.
+// Workgroups go to the eight XCDs in turn (linear id mod 8), each XCD with
+// its own L2; when the batch count is a multiple of 8 the linear id is
+// remapped so that XCD c runs every tile of batches c, c + 8, ..., one batch
+// after another, and each batch's operands are read into one L2 only.
+struct BatchTile { int x, y, z; };
+__device__ __forceinline__ BatchTile xcd_batch_tile() {
+  const int gx = gridDim.x, gy = gridDim.y;
+  if (gridDim.z & 7) return BatchTile{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+  const int P = gx * gy;
+  const int L = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int j = L >> 3, p = j % P;
+  return BatchTile{p % gx, p / gx, (j / P) * 8 + (L & 7)};
+}
+
 // C[z] = alpha A[z] B[z] on 64 x 64 tiles, K in steps of 32 (all multiples:
 // the caller pads).  A is M x K (AT: stored K x M), B is K x N (BT: stored
 // N x K); bf16 in, fp32 accumulate.  Four waves, 32 x 32 each.
@@ -43,8 +60,9 @@ template <bool AT, bool BT>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[64][kLdsK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[64][kLdsK];
-  const int z = blockIdx.z;
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64;
+  const BatchTile bt = xcd_batch_tile();
+  const int z = bt.z;
+  const int n0 = bt.x * 64, m0 = bt.y * 64;
   const uint16_t* A = g.a + (int64_t)z * g.a_batch;
   const uint16_t* B = g.b + (int64_t)z * g.b_batch;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -100,23 +118,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     __syncthreads();
   }
-  // lane (c, gq) holds rows 4 gq + v, column c of each 16 x 16 block
-  if (!g.rowmap) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = m0 + wm * 32 + 16 * i + 4 * gq + v;
-          const int n = n0 + wn * 32 + 16 * j + c;
-          if (n < g.n_valid) g.c[(int64_t)z * g.c_batch + (int64_t)m * g.ldc + n] = g.alpha * acc[i][j][v];
-        }
-    return;
-  }
-  // scattered adds: the tile goes through LDS so that one wave's atomic
-  // instruction covers 64 consecutive floats of one row (two whole cache
-  // lines) rather than 16 floats of four rows
+  // lane (c, gq) holds rows 4 gq + v, column c of each 16 x 16 block.  The
+  // tile goes through LDS so that one wave's store (or atomic) instruction
+  // covers 64 consecutive floats of one row (two whole cache lines) rather
+  // than 16 floats of four rows.
   __shared__ float sC[64][65];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -127,6 +132,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   __syncthreads();
   const int n = n0 + lane;
   if (n >= g.n_valid) return;
+  if (!g.rowmap) {
+    float* cz = g.c + (int64_t)z * g.c_batch + n;
+    if (g.stream_c) {   // written once, read back much later: past the caches
+#pragma unroll 4
+      for (int mm = wave; mm < 64; mm += 4)
+        __builtin_nontemporal_store(g.alpha * sC[mm][lane], cz + (int64_t)(m0 + mm) * g.ldc);
+    } else {
+#pragma unroll 4
+      for (int mm = wave; mm < 64; mm += 4) cz[(int64_t)(m0 + mm) * g.ldc] = g.alpha * sC[mm][lane];
+    }
+    return;
+  }
+  // scattered adds
 #pragma unroll 4
   for (int mm = wave; mm < 64; mm += 4) {
     const int64_t r = g.rowmap[(int64_t)z * g.rowmap_batch + m0 + mm];
@@ -153,15 +171,14 @@ constexpr int gemm32_smem_bytes() {
 // The main loop of gemm32: this workgroup's TM x 128 tile of A[z] B[z] in acc
 // (lane: column lane % 32 of each 32 x 32 block, rows (e/4) 8 + (lane/32) 4 + e % 4).
 template <int TM, bool AT, bool BT>
-__device__ __forceinline__ void gemm32_main(const GemmArgs& g, uint8_t* smem, f32x16 (&acc)[TM / 64][2]) {
+__device__ __forceinline__ void gemm32_main(const GemmArgs& g, uint8_t* smem, f32x16 (&acc)[TM / 64][2],
+                                            int n0, int m0, int z) {
   constexpr int TN = 128, BK = 32, KP = 40;   // KP: padded k stride (elements) of the LDS tiles
   constexpr int WM = TM / 2, MB = WM / 32;    // rows per wave, 32-row blocks per wave
   constexpr int LA = TM * BK / 8 / 256;       // 16-byte loads per thread per step (A)
   constexpr int LB = TN * BK / 8 / 256;       // (B)
   auto sA = reinterpret_cast<uint16_t (*)[TM][KP]>(smem);
   auto sB = reinterpret_cast<uint16_t (*)[TN][KP]>(smem + 2 * TM * KP * 2);
-  const int z = blockIdx.z;
-  const int n0 = blockIdx.x * TN, m0 = blockIdx.y * TM;
   const uint16_t* A = g.a + (int64_t)z * g.a_batch;
   const uint16_t* B = g.b + (int64_t)z * g.b_batch;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -238,7 +255,9 @@ __device__ __forceinline__ void gemm32_main(const GemmArgs& g, uint8_t* smem, f3
 __global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int q0) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[gemm32_smem_bytes<128>()];
   __shared__ float s_l2[64], s_dh[64], s_ps[128];
-  const int z = blockIdx.z, qr = q0 + z;
+  const BatchTile bt = xcd_batch_tile();
+  const int z = bt.z, qr = q0 + z;
+  const int n0 = bt.x * 128;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < 64) {
     const float lse = tid < a.H ? a.lse[(int64_t)qr * a.H + tid] : -INFINITY;
@@ -246,8 +265,7 @@ __global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int
     s_dh[tid] = a.Dh[(int64_t)z * 64 + tid];
   }
   f32x16 acc[2][2];
-  gemm32_main<128, false, true>(g, smem, acc);
-  const int n0 = blockIdx.x * 128;
+  gemm32_main<128, false, true>(g, smem, acc, n0, 0, z);
   const int wm = wave >> 1, wn = wave & 1;
   __syncthreads();   // the operand tiles are done with: the space holds [S; dP]
   auto sC = reinterpret_cast<float (*)[129]>(smem);
@@ -288,60 +306,84 @@ __global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int
 // its gradient goes: entry b Ncap + j (>= 0), window row -2 - (b (Tq+W-1) + r),
 // or -1.  One wave per row slot.
 __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a, int q0) {
+  // the arguments are read in one round before any branch (the empty asm
+  // statements keep the compiler from sinking each read into the branch
+  // that uses it, one dependent round trip after another)
+  const int Tq = a.Tq, k = a.k, m = a.m, W = a.W, D = a.D, R = a.R, group_q0 = a.group_q0;
+  const int64_t np = a.np, q_pos0 = a.q_pos0, Ncap = a.Ncap, n_entries = a.n_entries, nent = a.nent;
+  const int32_t* const topk = a.topk;
+  const uint8_t* const entries = a.entries;
+  const uint8_t* const win = a.win;
+  uint16_t* const X = a.X;
+  int64_t* const rowmap = a.rowmap;
+  int32_t* const dest = a.dest;
+  uint32_t* const cnt = a.cnt;
+  const bool grouped = a.dXd != nullptr;
+  asm volatile("" ::"s"(topk), "s"(entries), "s"(win), "s"(X), "s"(rowmap), "s"(dest), "s"(cnt),
+               "s"(np), "s"(q_pos0), "s"(Ncap), "s"(n_entries), "s"(nent));
+  asm volatile("" ::"s"(Tq), "s"(k), "s"(m), "s"(W), "s"(D), "s"(R), "s"(group_q0),
+               "s"((int)grouped));
   const int qc = blockIdx.y, qr = q0 + qc;
-  const int b = qr / a.Tq, r = qr % a.Tq;
-  const int64_t t = a.q_pos0 + r;
+  const int b = qr / Tq, r = qr % Tq;
+  const int64_t t = q_pos0 + r;
   const int x = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (x >= a.np) return;
+  if (x >= np) return;
   int64_t n_ent;
-  if (a.topk) {
-    n_ent = a.k;
+  if (topk) {
+    n_ent = k;
   } else {
-    const int64_t v = (t + 1) / a.m;
-    n_ent = v < a.n_entries ? v : a.n_entries;
+    const int64_t v = (t + 1) / m;
+    n_ent = v < n_entries ? v : n_entries;
   }
-  const int64_t lo = t - a.W + 1 > 0 ? t - a.W + 1 : 0;
-  const int64_t n_win = a.W > 0 ? t - lo + 1 : 0;
-  const int ROW = a.D + a.R;
+  const int64_t lo = t - W + 1 > 0 ? t - W + 1 : 0;
+  const int64_t n_win = W > 0 ? t - lo + 1 : 0;
+  const int ROW = D + R;
   const uint8_t* src = nullptr;
   int64_t map = -1;
   if (x < n_ent) {
-    const int64_t j = a.topk ? (int64_t)a.topk[(int64_t)qr * a.k + x] : (int64_t)x;
-    if (j >= 0 && j < a.Ncap) {
-      src = a.entries + ((int64_t)b * a.Ncap + j) * ROW;
-      map = (int64_t)b * a.Ncap + j;
+    const int64_t j = topk ? (int64_t)topk[(int64_t)qr * k + x] : (int64_t)x;
+    if (j >= 0 && j < Ncap) {
+      src = entries + ((int64_t)b * Ncap + j) * ROW;
+      map = (int64_t)b * Ncap + j;
     }
   } else if (x < n_ent + n_win) {
-    const int64_t wrow = lo + (x - n_ent) - (a.q_pos0 - (a.W - 1));
-    const int64_t grow = (int64_t)b * (a.Tq + a.W - 1) + wrow;
-    src = a.win + grow * ROW;
+    const int64_t wrow = lo + (x - n_ent) - (q_pos0 - (W - 1));
+    const int64_t grow = (int64_t)b * (Tq + W - 1) + wrow;
+    src = win + grow * ROW;
     map = -2 - grow;
   }
-  uint16_t* dst = a.X + ((int64_t)qc * a.np + x) * a.D;
-  const int E = a.D - a.R;
+  if (lane == 0) {
+    rowmap[(int64_t)qc * np + x] = map;
+    if (grouped) {   // grouped row gradients: the destination and its count
+      const int64_t d = map >= 0 ? map : (map <= -2 ? nent + (-2 - map) : -1);
+      dest[(int64_t)(qr - group_q0) * np + x] = (int32_t)d;
+      if (d >= 0) atomicAdd(cnt + d, 1u);
+    }
+  }
+  uint16_t* dst = X + ((int64_t)qc * np + x) * D;
+  const int E = D - R;
   const int d = 8 * lane;   // this lane's 8 dims (E and D are multiples of 8)
-  if (d < a.D) {
+  if (d < D) {
     uint4 o = {0u, 0u, 0u, 0u};
     if (src) {
       if (d < E) {   // 8 E4M3 bytes -> 8 bf16 (exact)
         const uint2 b8 = *reinterpret_cast<const uint2*>(src + d);
         const uint32_t w2[2] = {b8.x, b8.y};
-        uint32_t r[4];
+        uint32_t rr[4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w2[h], false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w2[h], true);
-          r[2 * h] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
-          r[2 * h + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+          const f32x2 lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w2[h], false);
+          const f32x2 hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w2[h], true);
+          rr[2 * h] = (__float_as_uint(lo2[0]) >> 16) | (__float_as_uint(lo2[1]) & 0xFFFF0000u);
+          rr[2 * h + 1] = (__float_as_uint(hi2[0]) >> 16) | (__float_as_uint(hi2[1]) & 0xFFFF0000u);
         }
-        o = uint4{r[0], r[1], r[2], r[3]};
+        o = uint4{rr[0], rr[1], rr[2], rr[3]};
       } else {       // bf16 dims as stored
         o = *reinterpret_cast<const uint4*>(src + E + 2 * (d - E));
       }
     }
     *reinterpret_cast<uint4*>(dst + d) = o;
   }
-  if (lane == 0) a.rowmap[(int64_t)qc * a.np + x] = map;
 }
 
 // The eight bf16 of a 16-byte word as floats.
@@ -792,6 +834,149 @@ hipError_t gemm(const GemmArgs& g, int M, int N, int Z, hipStream_t st) {
 }
 
 
+// ---- grouped row gradients: a counting sort of the group's (query, row
+// slot) gradients by destination row, then one sum per destination.
+
+__global__ __launch_bounds__(256) void bwd_fill_u32_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
+// off[0..n] = exclusive prefix sum of cnt[0..n), in tiles of 4096
+// destinations (a workgroup of 256 threads, 16 consecutive counts a thread):
+// the tiles' sums, their exclusive scan (one workgroup), then each tile's
+// offsets; the last pass clears cnt (it becomes the destinations' cursors).
+constexpr int kGroupTile = 4096;
+
+__device__ inline void load16_u32(const uint32_t* p, int64_t i0, int64_t n, uint32_t (&c)[16]) {
+  if (i0 + 16 <= n) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint4 u = *reinterpret_cast<const uint4*>(p + i0 + 4 * v);
+      c[4 * v] = u.x; c[4 * v + 1] = u.y; c[4 * v + 2] = u.z; c[4 * v + 3] = u.w;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) c[v] = i0 + v < n ? p[i0 + v] : 0u;
+  }
+}
+
+// Exclusive scan over a 256-thread workgroup; *total receives the sum.
+__device__ inline uint32_t block_excl_scan_256(uint32_t x, uint32_t* s_w, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = (uint32_t)wave_incl_scan_i((int)x, 0, [](int u, int v) { return u + v; });
+  if (lane == 63) s_w[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0u;
+  for (int w = 0; w < wave; ++w) base += s_w[w];
+  *total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+  return base + inc - x;
+}
+
+__global__ __launch_bounds__(256) void bwd_group_tile_sum_kernel(const uint32_t* cnt, uint32_t* tsum,
+                                                                 int64_t n) {
+  __shared__ uint32_t s_w[4];
+  uint32_t c[16];
+  load16_u32(cnt, (int64_t)blockIdx.x * kGroupTile + 16 * threadIdx.x, n, c);
+  uint32_t x = 0u;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x += c[v];
+  uint32_t total;
+  block_excl_scan_256(x, s_w, &total);
+  if (threadIdx.x == 0) tsum[blockIdx.x] = total;
+}
+
+// tsum[0..nt) -> its exclusive scan, in place; off[n] = the grand total.
+__global__ __launch_bounds__(256) void bwd_group_tile_scan_kernel(uint32_t* tsum, int64_t nt,
+                                                                  uint32_t* off, int64_t n) {
+  __shared__ uint32_t s_w[4];
+  uint32_t carry = 0u;
+  for (int64_t i0 = 0; i0 < nt; i0 += 256) {
+    const int64_t i = i0 + threadIdx.x;
+    const uint32_t x = i < nt ? tsum[i] : 0u;
+    uint32_t total;
+    const uint32_t e = block_excl_scan_256(x, s_w, &total);
+    if (i < nt) tsum[i] = carry + e;
+    carry += total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) off[n] = carry;
+}
+
+__global__ __launch_bounds__(256) void bwd_group_tile_offsets_kernel(uint32_t* cnt, uint32_t* off,
+                                                                     const uint32_t* tsum, int64_t n) {
+  __shared__ uint32_t s_w[4];
+  uint32_t c[16];
+  const int64_t i0 = (int64_t)blockIdx.x * kGroupTile + 16 * threadIdx.x;
+  load16_u32(cnt, i0, n, c);
+  uint32_t x = 0u;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x += c[v];
+  uint32_t total;
+  uint32_t run = tsum[blockIdx.x] + block_excl_scan_256(x, s_w, &total);
+  if (i0 + 16 <= n) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      uint4 o;
+      o.x = run; run += c[4 * v];
+      o.y = run; run += c[4 * v + 1];
+      o.z = run; run += c[4 * v + 2];
+      o.w = run; run += c[4 * v + 3];
+      *reinterpret_cast<uint4*>(off + i0 + 4 * v) = o;
+      *reinterpret_cast<uint4*>(cnt + i0 + 4 * v) = uint4{0u, 0u, 0u, 0u};
+    }
+  } else {
+    for (int v = 0; v < 16 && i0 + v < n; ++v) {
+      off[i0 + v] = run;
+      run += c[v];
+      cnt[i0 + v] = 0u;
+    }
+  }
+}
+
+// list[off[d] ..] = the slots whose destination is d (in no fixed order).
+__global__ __launch_bounds__(256) void bwd_group_scatter_kernel(const int32_t* dest, uint32_t* cnt,
+                                                                const uint32_t* off, int32_t* list,
+                                                                int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int32_t d = dest[i];
+    if (d >= 0) list[off[d] + atomicAdd(cnt + d, 1u)] = (int32_t)i;
+  }
+}
+
+// One wave per destination row: the sum of its slots' gradients, added to
+// the row of d_entries or d_win (lane l: dims 8 l .. 8 l + 7, D <= 512).
+// Four slots' rows are in flight at a time; a group past the list re-reads
+// the last slot and drops it.
+__global__ __launch_bounds__(256) void bwd_group_reduce_kernel(BwdArgs a) {
+  const int64_t d = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (d >= a.ndest) return;
+  const int lane = threadIdx.x & 63, dd = 8 * lane;
+  const uint32_t o0 = a.off[d], o1 = a.off[d + 1];
+  if (o0 == o1 || dd >= a.D) return;
+  f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+  for (uint32_t o = o0; o < o1; o += 4) {
+    f32x4 v0[4], v1[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t id = a.list[min(o + (uint32_t)u, o1 - 1u)];
+      const float* r = a.dXd + id * a.D + dd;
+      v0[u] = *reinterpret_cast<const f32x4*>(r);
+      v1[u] = *reinterpret_cast<const f32x4*>(r + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (o + (uint32_t)u < o1) {
+        s0 += v0[u];
+        s1 += v1[u];
+      }
+  }
+  float* t = d < a.nent ? a.d_entries + d * a.D + dd : a.d_win + (d - a.nent) * a.D + dd;
+  f32x4* t4 = reinterpret_cast<f32x4*>(t);
+  t4[0] = t4[0] + s0;
+  t4[1] = t4[1] + s1;
+}
+
 }  // namespace
 
 int64_t bwd_rows_padded(int64_t rows_max) { return (rows_max + 127) / 128 * 128; }
@@ -808,7 +993,16 @@ size_t bwd_query_bytes(int D, int64_t np) {
          + al((size_t)64 * 4);           // DS
 }
 
-hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t st) {
+size_t bwd_group_bytes(int D, int64_t np, int64_t gq, int64_t ndest) {
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  if (gq <= 0) return 0;
+  return al((size_t)gq * np * D * 4)        // dense dX
+         + 2 * al((size_t)gq * np * 4)      // dest, list
+         + 2 * al((size_t)(ndest + 1) * 4)  // cnt, off
+         + al((size_t)((ndest + kGroupTile - 1) / kGroupTile) * 4);   // tile sums
+}
+
+hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, hipStream_t st) {
   const int nq = a.B * a.Tq;
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
   const int64_t np = a.np;
@@ -820,36 +1014,74 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t s
   a.T = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * 128 * np * 2);
   a.DQT = reinterpret_cast<float*>(w);       w += al((size_t)qchunk * 64 * a.D * 4);
   a.G = reinterpret_cast<float*>(w);         w += al((size_t)qchunk * a.D * 4);
-  a.DS = reinterpret_cast<float*>(w);
-  for (int q0 = 0; q0 < nq; q0 += qchunk) {
-    const int qc = nq - q0 < qchunk ? nq - q0 : qchunk;
-    bwd_gather_kernel<<<dim3((unsigned)((np + 3) / 4), qc), 256, 0, st>>>(a, q0);
-    bwd_prep_kernel<<<dim3(16, qc), 256, 0, st>>>(a, q0);
-    // [S; dP] = Y X^T (M = 128, N = np, K = D) and, from it, T = [scale dL; P]
-    GemmArgs g1{};
-    g1.a = a.Y; g1.lda = a.D; g1.a_batch = 128 * (int64_t)a.D;
-    g1.b = a.X; g1.ldb = a.D; g1.b_batch = np * a.D;
-    g1.K = a.D; g1.alpha = 1.f; g1.n_valid = (int)np;
-    bwd_sdp_kernel<<<dim3((unsigned)(np / 128), 1, qc), 256, 0, st>>>(g1, a, q0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // dq~ = (scale dL) X: M = 64, N = D, K = np
-    GemmArgs g2{};
-    g2.a = a.T; g2.lda = np; g2.a_batch = 128 * np;
-    g2.b = a.X; g2.ldb = a.D; g2.b_batch = np * a.D;
-    g2.c = a.DQT; g2.ldc = a.D; g2.c_batch = 64 * (int64_t)a.D; g2.K = (int)np; g2.alpha = 1.f;
-    g2.n_valid = a.D;
-    e = gemm<false, false>(g2, 64, a.D, qc, st);
-    if (e != hipSuccess) return e;
-    // dX = T^T Y, added into the row gradients: M = np, N = D, K = 128
-    GemmArgs g3{};
-    g3.a = a.T; g3.lda = np; g3.a_batch = 128 * np;
-    g3.b = a.Y; g3.ldb = a.D; g3.b_batch = 128 * (int64_t)a.D;
-    g3.c = a.d_entries; g3.c2 = a.d_win; g3.ldc = a.D; g3.K = 128; g3.alpha = 1.f; g3.n_valid = a.D;
-    g3.rowmap = a.rowmap; g3.rowmap_batch = np;
-    e = gemm<true, false>(g3, (int)np, a.D, qc, st);
-    if (e != hipSuccess) return e;
-    bwd_q_kernel<<<qc, 1024, 0, st>>>(a, q0);
+  a.DS = reinterpret_cast<float*>(w);        w += al((size_t)qchunk * 64 * 4);
+  a.dXd = nullptr;
+  uint32_t* tsum = nullptr;
+  const int64_t ntile = (a.ndest + kGroupTile - 1) / kGroupTile;
+  if (gq > 0) {
+    a.dXd = reinterpret_cast<float*>(w);     w += al((size_t)gq * np * a.D * 4);
+    a.dest = reinterpret_cast<int32_t*>(w);  w += al((size_t)gq * np * 4);
+    a.list = reinterpret_cast<int32_t*>(w);  w += al((size_t)gq * np * 4);
+    a.cnt = reinterpret_cast<uint32_t*>(w);  w += al((size_t)(a.ndest + 1) * 4);
+    a.off = reinterpret_cast<uint32_t*>(w);  w += al((size_t)(a.ndest + 1) * 4);
+    tsum = reinterpret_cast<uint32_t*>(w);
+  }
+  const int64_t gstep = gq > 0 ? gq : nq;
+  for (int64_t g0 = 0; g0 < nq; g0 += gstep) {
+    const int64_t g1 = g0 + gstep < nq ? g0 + gstep : nq;
+    if (gq > 0) {
+      a.group_q0 = (int)g0;
+      bwd_fill_u32_kernel<<<256, 256, 0, st>>>(a.cnt, a.ndest + 1);
+    }
+    for (int q0 = (int)g0; q0 < g1; q0 += qchunk) {
+      const int qc = g1 - q0 < qchunk ? (int)(g1 - q0) : qchunk;
+      bwd_gather_kernel<<<dim3((unsigned)((np + 3) / 4), qc), 256, 0, st>>>(a, q0);
+      bwd_prep_kernel<<<dim3(16, qc), 256, 0, st>>>(a, q0);
+      // [S; dP] = Y X^T (M = 128, N = np, K = D) and, from it, T = [scale dL; P]
+      GemmArgs g1{};
+      g1.a = a.Y; g1.lda = a.D; g1.a_batch = 128 * (int64_t)a.D;
+      g1.b = a.X; g1.ldb = a.D; g1.b_batch = np * a.D;
+      g1.K = a.D; g1.alpha = 1.f; g1.n_valid = (int)np;
+      bwd_sdp_kernel<<<dim3((unsigned)(np / 128), 1, qc), 256, 0, st>>>(g1, a, q0);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      // dq~ = (scale dL) X: M = 64, N = D, K = np
+      GemmArgs g2{};
+      g2.a = a.T; g2.lda = np; g2.a_batch = 128 * np;
+      g2.b = a.X; g2.ldb = a.D; g2.b_batch = np * a.D;
+      g2.c = a.DQT; g2.ldc = a.D; g2.c_batch = 64 * (int64_t)a.D; g2.K = (int)np; g2.alpha = 1.f;
+      g2.n_valid = a.D;
+      e = gemm<false, false>(g2, 64, a.D, qc, st);
+      if (e != hipSuccess) return e;
+      // dX = T^T Y: M = np, N = D, K = 128; added into the row gradients
+      // (atomics), or stored densely for the group's sum by destination
+      GemmArgs g3{};
+      g3.a = a.T; g3.lda = np; g3.a_batch = 128 * np;
+      g3.b = a.Y; g3.ldb = a.D; g3.b_batch = 128 * (int64_t)a.D;
+      g3.ldc = a.D; g3.K = 128; g3.alpha = 1.f; g3.n_valid = a.D;
+      if (a.dXd) {
+        g3.c = a.dXd + (int64_t)(q0 - g0) * np * a.D; g3.c_batch = np * a.D; g3.stream_c = 1;
+      } else {
+        g3.c = a.d_entries; g3.c2 = a.d_win; g3.rowmap = a.rowmap; g3.rowmap_batch = np;
+      }
+      e = gemm<true, false>(g3, (int)np, a.D, qc, st);
+      if (e != hipSuccess) return e;
+      bwd_q_kernel<<<qc, 1024, 0, st>>>(a, q0);
+    }
+    if (gq > 0) {
+      const int64_t nslots = (g1 - g0) * np;
+      if (ntile > 0) {
+        bwd_group_tile_sum_kernel<<<(unsigned)ntile, 256, 0, st>>>(a.cnt, tsum, a.ndest);
+        bwd_group_tile_scan_kernel<<<1, 256, 0, st>>>(tsum, ntile, a.off, a.ndest);
+        bwd_group_tile_offsets_kernel<<<(unsigned)ntile, 256, 0, st>>>(a.cnt, a.off, tsum, a.ndest);
+      }
+      const int64_t sb = (nslots + 255) / 256;
+      bwd_group_scatter_kernel<<<(unsigned)(sb < 4096 ? sb : 4096), 256, 0, st>>>(a.dest, a.cnt, a.off,
+                                                                                   a.list, nslots);
+      if (a.ndest > 0) bwd_group_reduce_kernel<<<(unsigned)((a.ndest + 3) / 4), 256, 0, st>>>(a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (a.d_gamma_q || (a.sink && a.d_sink))
     bwd_reduce_kernel<<<(unsigned)((a.D + 255) / 256), 256, 0, st>>>(a, nq < qchunk ? nq : qchunk);

@@ -268,6 +268,7 @@ struct GemmArgs {
   int K;
   float alpha;
   int n_valid;               // columns >= n_valid are not stored
+  int stream_c;              // dense C stored non-temporally
 };
 
 // Attention backward (both kinds: CSA when topk != nullptr).
@@ -307,10 +308,28 @@ struct BwdArgs {
   float* DQT;
   float* G;                  // [chunk, D] a query's d_gamma_q share (its heads summed)
   float* DS;                 // [chunk, 64] a query's d_sink share per head
+  // grouped row gradients (dXd != nullptr): the dX product stores every
+  // (query, row slot)'s gradient densely; after each group of queries the
+  // slots are grouped by destination row (a counting sort) and each row's
+  // slots summed once into d_entries / d_win
+  float* dXd;                // [group, np, D]
+  int32_t* dest;             // [group, np] destination row: b Ncap + j, or
+                             // B Ncap + window row, or -1
+  int32_t* list;             // [group, np] slot ids grouped by destination
+  uint32_t* cnt;             // [ndest + 1] slots per destination (then cursors)
+  uint32_t* off;             // [ndest + 1] first list position per destination
+  int64_t nent;              // B Ncap: destinations below are entries
+  int64_t ndest;             // B Ncap + B (Tq + W - 1)
+  int group_q0;              // first query of the current group
 };
 int64_t bwd_rows_padded(int64_t rows_max);
 size_t bwd_query_bytes(int D, int64_t np);
-hipError_t launch_attend_backward(BwdArgs a, int qchunk, void* ws, hipStream_t st);
+// Workspace bytes of the grouped row gradients for groups of `gq` queries
+// (0: none) and ndest destination rows.
+size_t bwd_group_bytes(int D, int64_t np, int64_t gq, int64_t ndest);
+// gq = 0: row gradients by atomic adds; gq > 0: grouped, gq queries (a
+// multiple of qchunk) per group, ndest destinations.
+hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, hipStream_t st);
 
 // Compressor (POOL) backward for entries entry0 .. entry0+n_out-1.
 struct CompressBwdArgs {

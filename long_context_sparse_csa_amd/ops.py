@@ -62,7 +62,7 @@ _SIGS = {
                                _F, _F, _F, _P, _P, _P, _Z, _P]),
     "v4attn_hca_attend_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I, _L,
                                        _P, _F, _F, _F, _P, _P, _P]),
-    "v4attn_csa_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "v4attn_csa_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _I, _I, _L]),
     "v4attn_csa_attend_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _I, _I,
                                         _L, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                         _Z, _P]),
@@ -71,7 +71,7 @@ _SIGS = {
     "v4attn_index_kl_backward_workspace": (_Z, [_I, _I, _I, _I]),
     "v4attn_index_kl_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _P, _P, _P, _P,
                                       _P, _Z, _P]),
-    "v4attn_hca_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I]),
+    "v4attn_hca_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I, _L]),
     "v4attn_hca_attend_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _I, _I,
                                         _L, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                                         _P]),
@@ -669,10 +669,13 @@ def _bwd_outputs(q, entries, win, H, D, grads):
 
 def csa_attend_backward(q, entries, topk, win, gamma_q, sink, out, lse, dout, *, q_pos0, W,
                         scale=None, eps=1e-6, rope_base=10000.0, R=64, grads=None,
-                        p_sel=None, workspace=None):
+                        p_sel=None, workspace=None, workspace_bytes=None):
     """Gradients of csa_attend.  Returns (dq, d_entries, d_win, d_sink,
     d_gamma_q); the last four are added into `grads` entries if given.
-    p_sel (f32 [B, Tq, k], optional) receives sum_h p of every top-k slot."""
+    p_sel (f32 [B, Tq, k], optional) receives sum_h p of every top-k slot.
+    workspace_bytes below the queried size (down to the per-chunk buffers)
+    makes the library add the row gradients with atomics instead of
+    grouping them."""
     _need(dout, "dout", torch.bfloat16, 4)
     _need(out, "out", torch.bfloat16, 4)
     _need(lse, "lse", torch.float32, 3)
@@ -680,7 +683,8 @@ def csa_attend_backward(q, entries, topk, win, gamma_q, sink, out, lse, dout, *,
     k = topk.shape[2]
     scale = D ** -0.5 if scale is None else scale
     dq, d_ent, d_win, d_sink, d_gamma = _bwd_outputs(q, entries, win, H, D, grads)
-    nbytes = lib().v4attn_csa_attend_backward_workspace(B, Tq, H, D, k, W)
+    nbytes = lib().v4attn_csa_attend_backward_workspace(B, Tq, H, D, k, W, entries.shape[1])
+    nbytes = nbytes if workspace_bytes is None else int(workspace_bytes)
     workspace = _workspace(nbytes, q.device, workspace)
     check(lib().v4attn_csa_attend_backward(
         _ptr(q), _ptr(entries), _ptr(topk), _ptr(win), _ptr(gamma_q), _ptr(sink), B, Tq, H, D, R,
@@ -692,7 +696,7 @@ def csa_attend_backward(q, entries, topk, win, gamma_q, sink, out, lse, dout, *,
 
 def hca_attend_backward(q, entries, win, gamma_q, sink, out, lse, dout, *, n_entries, m, q_pos0,
                         W, scale=None, eps=1e-6, rope_base=10000.0, R=64, grads=None,
-                        workspace=None):
+                        workspace=None, workspace_bytes=None):
     """Gradients of hca_attend (see csa_attend_backward)."""
     _need(dout, "dout", torch.bfloat16, 4)
     _need(out, "out", torch.bfloat16, 4)
@@ -700,7 +704,9 @@ def hca_attend_backward(q, entries, win, gamma_q, sink, out, lse, dout, *, n_ent
     B, Tq, H, D = q.shape
     scale = D ** -0.5 if scale is None else scale
     dq, d_ent, d_win, d_sink, d_gamma = _bwd_outputs(q, entries, win, H, D, grads)
-    nbytes = lib().v4attn_hca_attend_backward_workspace(B, Tq, H, D, n_entries, m, q_pos0, W)
+    nbytes = lib().v4attn_hca_attend_backward_workspace(B, Tq, H, D, n_entries, m, q_pos0, W,
+                                                        entries.shape[1])
+    nbytes = nbytes if workspace_bytes is None else int(workspace_bytes)
     workspace = _workspace(nbytes, q.device, workspace)
     check(lib().v4attn_hca_attend_backward(
         _ptr(q), _ptr(entries), _ptr(win), _ptr(gamma_q), _ptr(sink), B, Tq, H, D, R,

@@ -187,6 +187,38 @@ def test_hca_attend_backward_matches_oracle(case):
     _check(got, want, f"hca {case}")
 
 
+def test_csa_backward_row_gradient_paths_match_oracle():
+    """The row gradients grouped in one group (the queried workspace), in
+    several groups (a byte less: 64 + 16 queries), and added with atomics
+    (room for the per-chunk buffers only), on 80 queries whose window rows
+    and top-k entries are shared.  At this shape the per-chunk buffers take
+    64 x ~131 KiB ~ 8.4 MB and a 64-query group's dense gradients 4.2 MB, so
+    the queried size less 4.5 MB holds no group."""
+    B, Tq, H, D, Ncap, k, W, q_pos0 = 2, 40, 8, 128, 300, 48, 16, 700
+    q, ent, win, gq, sink, dout = _inputs(B, Tq, H, D, Ncap, W, 17)
+    g = torch.Generator().manual_seed(9)
+    topk = torch.stack([torch.stack([torch.randperm(120, generator=g)[:k].sort().values
+                                     for _ in range(Tq)]) for _ in range(B)]).to(torch.int32)
+    topk = topk.to(DEV)
+    scale = D ** -0.5
+    out, lse = ops().csa_attend(q, ent, topk, win, gq, sink, q_pos0=q_pos0, W=W, scale=scale,
+                                want_lse=True)
+    full = ops().lib().v4attn_csa_attend_backward_workspace(B, Tq, H, D, k, W, Ncap)
+    tk = topk.cpu().numpy()
+
+    def rows_of(b, r, t):
+        return tk[b, r], _win_rows(t, q_pos0, W)
+
+    want = _reference(q, ent, win, gq, sink, dout, rows_of, q_pos0, W, scale, D)
+    for nbytes, what in ((full, "one group"), (full - 1, "two groups"),
+                         (full - (9 << 19), "atomics")):
+        log(f"csa backward row gradients: {what}, workspace {nbytes} of {full} bytes")
+        got = ops().csa_attend_backward(q, ent, topk, win, gq, sink, out, lse, dout,
+                                        q_pos0=q_pos0, W=W, scale=scale, workspace_bytes=nbytes)
+        torch.cuda.synchronize()
+        _check(got, want, f"csa rows {what}")
+
+
 def test_backward_adds_into_given_gradients():
     """Row, sink and gamma gradients are added to what the buffers hold."""
     B, Tq, H, D, Ncap, k, W, q_pos0 = 1, 2, 16, 128, 64, 16, 4, 100
