@@ -134,14 +134,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   if (n >= g.n_valid) return;
   if (!g.rowmap) {
     float* cz = g.c + (int64_t)z * g.c_batch + n;
-    if (g.stream_c) {   // written once, read back much later: past the caches
 #pragma unroll 4
-      for (int mm = wave; mm < 64; mm += 4)
-        __builtin_nontemporal_store(g.alpha * sC[mm][lane], cz + (int64_t)(m0 + mm) * g.ldc);
-    } else {
-#pragma unroll 4
-      for (int mm = wave; mm < 64; mm += 4) cz[(int64_t)(m0 + mm) * g.ldc] = g.alpha * sC[mm][lane];
-    }
+    for (int mm = wave; mm < 64; mm += 4) cz[(int64_t)(m0 + mm) * g.ldc] = g.alpha * sC[mm][lane];
     return;
   }
   // scattered adds
@@ -160,9 +154,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 // while the current one's MFMAs run and go to the other of two LDS buffers
 // (one barrier a step).  A is M x K (AT: stored K x M), B is K x N (BT:
 // stored N x K); a source stored k-major is transposed on its way into LDS.
-// (The two products with k-major operands, dq~ = T X and dX = T^T Y, stay on
-// gemm_bf16_kernel: transposing them element by element into these larger
-// tiles cost more than the faster MFMAs saved.)
+// (dq~ = T X, whose X operand is k-major, stays on gemm_bf16_kernel:
+// transposing X element by element into these larger tiles cost more than
+// the faster MFMAs saved.  dX = T^T Y runs here on operands that the
+// softmax-gradient and prep kernels also write transposed.)
 template <int TM>
 constexpr int gemm32_smem_bytes() {
   return 2 * (TM + 128) * 40 * 2 > TM * 129 * 4 ? 2 * (TM + 128) * 40 * 2 : TM * 129 * 4;
@@ -283,9 +278,11 @@ __global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int
   const int64_t x = n0 + c;
   const bool present = a.rowmap[(int64_t)z * a.np + x] != -1;
   const float sl2 = a.scale * kL2e;
-  uint16_t* tp = a.T + (int64_t)z * 128 * a.np + x;
+  uint16_t* tp = a.T + (int64_t)z * 64 * a.np + x;        // scale dL, head rows (dq~)
+  uint16_t* ttp = a.TT + ((int64_t)z * a.np + x) * 128;    // [scale dL; P] of slot x (dX)
   float psum = 0.f;
-#pragma unroll 8
+  uint32_t tdl[16], tpp[16];
+#pragma unroll
   for (int i = 0; i < 32; ++i) {
     const int h = 32 * hh + i;
     float p = 0.f, dl = 0.f;
@@ -294,12 +291,64 @@ __global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int
       dl = p * (sC[64 + h][c] - s_dh[h]);
     }
     psum += p;
-    tp[(int64_t)h * a.np] = f2bf(a.scale * dl);
-    tp[(int64_t)(64 + h) * a.np] = f2bf(p);
+    const uint32_t bdl = f2bf(a.scale * dl), bp = f2bf(p);
+    tp[(int64_t)h * a.np] = (uint16_t)bdl;
+    tdl[i >> 1] = (i & 1) ? tdl[i >> 1] | (bdl << 16) : bdl;
+    tpp[i >> 1] = (i & 1) ? tpp[i >> 1] | (bp << 16) : bp;
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    reinterpret_cast<uint4*>(ttp + 32 * hh)[v] = uint4{tdl[4 * v], tdl[4 * v + 1], tdl[4 * v + 2], tdl[4 * v + 3]};
+    reinterpret_cast<uint4*>(ttp + 64 + 32 * hh)[v] =
+        uint4{tpp[4 * v], tpp[4 * v + 1], tpp[4 * v + 2], tpp[4 * v + 3]};
   }
   if (hh == 1) s_ps[c] = psum;
   __syncthreads();
   if (hh == 0 && a.p_sel && x < a.k_sel) a.p_sel[(int64_t)qr * a.k_sel + x] = psum + s_ps[c];
+}
+
+// dX = [scale dL; P]^T [q~; do] for one query (z), a tile of 128 row slots x
+// 128 dims, K = 128 head slots: both operands read k-contiguous (TT and YT).
+// The tile is stored densely past the caches (it is read back once, by the
+// grouped sum) or, with rowmap, added into the row gradients with atomics.
+__global__ __launch_bounds__(256) void bwd_dx_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[gemm32_smem_bytes<128>()];
+  const BatchTile bt = xcd_batch_tile();
+  const int z = bt.z, n0 = bt.x * 128, m0 = bt.y * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  f32x16 acc[2][2];
+  gemm32_main<128, false, true>(g, smem, acc, n0, m0, z);
+  const int wm = wave >> 1, wn = wave & 1;
+  __syncthreads();   // the operand tiles are done with: the space holds the C tile
+  auto sC = reinterpret_cast<float (*)[129]>(smem);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sC[wm * 64 + 32 * mb + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)][wn * 64 + 32 * nb + (lane & 31)] =
+            acc[mb][nb][e];
+  __syncthreads();
+  if (!g.rowmap) {
+    float* cz = g.c + (int64_t)z * g.c_batch + n0 + lane;
+#pragma unroll 4
+    for (int mm = wave; mm < 128; mm += 4) {
+      float* row = cz + (int64_t)(m0 + mm) * g.ldc;
+      __builtin_nontemporal_store(sC[mm][lane], row);
+      __builtin_nontemporal_store(sC[mm][64 + lane], row + 64);
+    }
+    return;
+  }
+#pragma unroll 4
+  for (int mm = wave; mm < 128; mm += 4) {
+    const int64_t r = g.rowmap[(int64_t)z * g.rowmap_batch + m0 + mm];
+    float* row = r >= 0 ? g.c + r * g.ldc : (r <= -2 ? g.c2 + (-2 - r) * g.ldc : nullptr);
+    if (row) {
+      atomicAdd(row + n0 + lane, sC[mm][lane]);
+      atomicAdd(row + n0 + 64 + lane, sC[mm][64 + lane]);
+    }
+  }
 }
 
 // X[qc, x, :] = the query's row x as bf16 (zeros if absent), rowmap = where
@@ -422,10 +471,12 @@ __device__ __forceinline__ void lane_rot8(const BwdArgs& a, int d, int64_t t, fl
   }
 }
 
-// Y[qc] = [q~ (64 head slots); do = RoPE_t(dout) (64 slots)] as bf16, Dh =
-// dout . out, the query's d_sink share -p_sink Dh.  One wave per head; lane l
-// holds dims 8 l .. 8 l + 7 (16-byte loads and stores).
+// Y[qc] = [q~ (64 head slots); do = RoPE_t(dout) (64 slots)] as bf16, and
+// the same transposed (YT[qc], dims x head slots, through LDS), Dh = dout .
+// out, the query's d_sink share -p_sink Dh.  One wave per head; lane l holds
+// dims 8 l .. 8 l + 7 (16-byte loads and stores).
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int q0) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_y[2][4][512];
   const int qc = blockIdx.y, qr = q0 + qc;
   const int r = qr % a.Tq;
   const int64_t t = a.q_pos0 + r;
@@ -434,14 +485,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int q0) {
   const bool act = d < a.D;
   uint16_t* yq = a.Y + ((int64_t)qc * 128 + h) * a.D + d;
   uint16_t* yd = a.Y + ((int64_t)qc * 128 + 64 + h) * a.D + d;
-  if (h >= a.H) {
-    if (act) *reinterpret_cast<uint4*>(yq) = *reinterpret_cast<uint4*>(yd) = uint4{0u, 0u, 0u, 0u};
-    return;
-  }
-  const int64_t off = ((int64_t)qr * a.H + h) * a.D + d;
+  const bool live = h < a.H;   // head slots >= H are zeros
+  const int64_t off = ((int64_t)qr * a.H + (live ? h : 0)) * a.D + d;
   uint4 qw{0u, 0u, 0u, 0u}, gw{0u, 0u, 0u, 0u}, ow{0u, 0u, 0u, 0u};
   float gm[8];
-  if (act) {
+  if (act && live) {
     qw = *reinterpret_cast<const uint4*>(a.q + off);
     gw = *reinterpret_cast<const uint4*>(a.dout + off);
     ow = *reinterpret_cast<const uint4*>(a.out + off);
@@ -475,11 +523,27 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int q0) {
       g[2 * p + 1] = g0 * sn[p] + g1 * cs[p];
     }
   }
+  const int w = threadIdx.x >> 6;
   if (act) {
-    *reinterpret_cast<uint4*>(yq) = f32_to_bf16x8(x);
-    *reinterpret_cast<uint4*>(yd) = f32_to_bf16x8(g);
+    const uint4 vq = live ? f32_to_bf16x8(x) : uint4{0u, 0u, 0u, 0u};
+    const uint4 vd = live ? f32_to_bf16x8(g) : uint4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<uint4*>(yq) = vq;
+    *reinterpret_cast<uint4*>(yd) = vd;
+    *reinterpret_cast<uint4*>(&s_y[0][w][d]) = vq;
+    *reinterpret_cast<uint4*>(&s_y[1][w][d]) = vd;
   }
-  if (lane == 0) {
+  __syncthreads();
+  // YT[qc][e][64 p + 4 blockIdx.x ..]: this workgroup's four head slots of
+  // dim e, 8 bytes a store
+  uint16_t* yt = a.YT + (int64_t)qc * a.D * 128 + 4 * blockIdx.x;
+  for (int e = threadIdx.x; e < a.D; e += 256)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint2 v{(uint32_t)s_y[p][0][e] | ((uint32_t)s_y[p][1][e] << 16),
+                    (uint32_t)s_y[p][2][e] | ((uint32_t)s_y[p][3][e] << 16)};
+      *reinterpret_cast<uint2*>(yt + (int64_t)e * 128 + 64 * p) = v;
+    }
+  if (lane == 0 && live) {
     a.Dh[(int64_t)qc * 64 + h] = dd;
     float ds = 0.f;
     if (a.sink) {
@@ -986,8 +1050,10 @@ size_t bwd_query_bytes(int D, int64_t np) {
   return al((size_t)np * D * 2)          // X
          + al((size_t)np * 8)            // rowmap
          + al((size_t)128 * D * 2)       // Y
+         + al((size_t)D * 128 * 2)       // YT
          + al((size_t)64 * 4)            // Dh
-         + al((size_t)128 * np * 2)      // T
+         + al((size_t)64 * np * 2)       // T
+         + al((size_t)np * 128 * 2)      // TT
          + al((size_t)64 * D * 4)        // dq~
          + al((size_t)D * 4)             // G
          + al((size_t)64 * 4);           // DS
@@ -1010,8 +1076,10 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, h
   a.X = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * np * a.D * 2);
   a.rowmap = reinterpret_cast<int64_t*>(w);    w += al((size_t)qchunk * np * 8);
   a.Y = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * 128 * a.D * 2);
+  a.YT = reinterpret_cast<uint16_t*>(w);       w += al((size_t)qchunk * a.D * 128 * 2);
   a.Dh = reinterpret_cast<float*>(w);          w += al((size_t)qchunk * 64 * 4);
-  a.T = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * 128 * np * 2);
+  a.T = reinterpret_cast<uint16_t*>(w);        w += al((size_t)qchunk * 64 * np * 2);
+  a.TT = reinterpret_cast<uint16_t*>(w);       w += al((size_t)qchunk * np * 128 * 2);
   a.DQT = reinterpret_cast<float*>(w);       w += al((size_t)qchunk * 64 * a.D * 4);
   a.G = reinterpret_cast<float*>(w);         w += al((size_t)qchunk * a.D * 4);
   a.DS = reinterpret_cast<float*>(w);        w += al((size_t)qchunk * 64 * 4);
@@ -1047,7 +1115,7 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, h
       if (e != hipSuccess) return e;
       // dq~ = (scale dL) X: M = 64, N = D, K = np
       GemmArgs g2{};
-      g2.a = a.T; g2.lda = np; g2.a_batch = 128 * np;
+      g2.a = a.T; g2.lda = np; g2.a_batch = 64 * np;
       g2.b = a.X; g2.ldb = a.D; g2.b_batch = np * a.D;
       g2.c = a.DQT; g2.ldc = a.D; g2.c_batch = 64 * (int64_t)a.D; g2.K = (int)np; g2.alpha = 1.f;
       g2.n_valid = a.D;
@@ -1056,16 +1124,15 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, h
       // dX = T^T Y: M = np, N = D, K = 128; added into the row gradients
       // (atomics), or stored densely for the group's sum by destination
       GemmArgs g3{};
-      g3.a = a.T; g3.lda = np; g3.a_batch = 128 * np;
-      g3.b = a.Y; g3.ldb = a.D; g3.b_batch = 128 * (int64_t)a.D;
+      g3.a = a.TT; g3.lda = 128; g3.a_batch = np * 128;
+      g3.b = a.YT; g3.ldb = 128; g3.b_batch = (int64_t)a.D * 128;
       g3.ldc = a.D; g3.K = 128; g3.alpha = 1.f; g3.n_valid = a.D;
       if (a.dXd) {
-        g3.c = a.dXd + (int64_t)(q0 - g0) * np * a.D; g3.c_batch = np * a.D; g3.stream_c = 1;
+        g3.c = a.dXd + (int64_t)(q0 - g0) * np * a.D; g3.c_batch = np * a.D;
       } else {
         g3.c = a.d_entries; g3.c2 = a.d_win; g3.rowmap = a.rowmap; g3.rowmap_batch = np;
       }
-      e = gemm<true, false>(g3, (int)np, a.D, qc, st);
-      if (e != hipSuccess) return e;
+      bwd_dx_kernel<<<dim3((unsigned)(a.D / 128), (unsigned)(np / 128), qc), 256, 0, st>>>(g3);
       bwd_q_kernel<<<qc, 1024, 0, st>>>(a, q0);
     }
     if (gq > 0) {

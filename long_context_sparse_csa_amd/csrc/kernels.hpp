@@ -268,7 +268,6 @@ struct GemmArgs {
   int K;
   float alpha;
   int n_valid;               // columns >= n_valid are not stored
-  int stream_c;              // dense C stored non-temporally
 };
 
 // Attention backward (both kinds: CSA when topk != nullptr).
@@ -302,9 +301,11 @@ struct BwdArgs {
   // workspace views (set by the launcher)
   uint16_t* X;
   int64_t* rowmap;
-  uint16_t* Y;
+  uint16_t* Y;                // [chunk, 128, D] [q~; do] (head slot rows)
+  uint16_t* YT;               // [chunk, D, 128] the same, transposed
   float* Dh;
-  uint16_t* T;
+  uint16_t* T;                // [chunk, 64, np] scale dL (head slot rows)
+  uint16_t* TT;               // [chunk, np, 128] [scale dL; P] per row slot
   float* DQT;
   float* G;                  // [chunk, D] a query's d_gamma_q share (its heads summed)
   float* DS;                 // [chunk, 64] a query's d_sink share per head
