@@ -279,7 +279,6 @@ __global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int
   const bool present = a.rowmap[(int64_t)z * a.np + x] != -1;
   const float sl2 = a.scale * kL2e;
   uint16_t* tp = a.T + (int64_t)z * 64 * a.np + x;        // scale dL, head rows (dq~)
-  uint16_t* ttp = a.TT + ((int64_t)z * a.np + x) * 128;    // [scale dL; P] of slot x (dX)
   float psum = 0.f;
   uint32_t tdl[16], tpp[16];
 #pragma unroll
@@ -293,14 +292,25 @@ __global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int
     psum += p;
     const uint32_t bdl = f2bf(a.scale * dl), bp = f2bf(p);
     tp[(int64_t)h * a.np] = (uint16_t)bdl;
+    // [scale dL; P] of slot x, head-contiguous, for dX
     tdl[i >> 1] = (i & 1) ? tdl[i >> 1] | (bdl << 16) : bdl;
     tpp[i >> 1] = (i & 1) ? tpp[i >> 1] | (bp << 16) : bp;
   }
+  // the tile's TT rows (128 slots x 256 bytes, one contiguous block) go out
+  // through LDS as whole 1 KB wave stores
+  __syncthreads();   // every thread is done reading [S; dP]
+  auto sT = reinterpret_cast<uint4 (*)[17]>(smem);   // [slot][16 units + 1 pad] of 8 bf16
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    reinterpret_cast<uint4*>(ttp + 32 * hh)[v] = uint4{tdl[4 * v], tdl[4 * v + 1], tdl[4 * v + 2], tdl[4 * v + 3]};
-    reinterpret_cast<uint4*>(ttp + 64 + 32 * hh)[v] =
-        uint4{tpp[4 * v], tpp[4 * v + 1], tpp[4 * v + 2], tpp[4 * v + 3]};
+    sT[c][4 * hh + v] = uint4{tdl[4 * v], tdl[4 * v + 1], tdl[4 * v + 2], tdl[4 * v + 3]};
+    sT[c][8 + 4 * hh + v] = uint4{tpp[4 * v], tpp[4 * v + 1], tpp[4 * v + 2], tpp[4 * v + 3]};
+  }
+  __syncthreads();
+  uint4* tt = reinterpret_cast<uint4*>(a.TT + ((int64_t)z * a.np + n0) * 128);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int u = tid + 256 * i;   // 16-byte unit u % 16 of slot u / 16
+    tt[u] = sT[u >> 4][u & 15];
   }
   if (hh == 1) s_ps[c] = psum;
   __syncthreads();
@@ -473,14 +483,14 @@ __device__ __forceinline__ void lane_rot8(const BwdArgs& a, int d, int64_t t, fl
 
 // Y[qc] = [q~ (64 head slots); do = RoPE_t(dout) (64 slots)] as bf16, and
 // the same transposed (YT[qc], dims x head slots, through LDS), Dh = dout .
-// out, the query's d_sink share -p_sink Dh.  One wave per head; lane l holds
-// dims 8 l .. 8 l + 7 (16-byte loads and stores).
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int q0) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_y[2][4][512];
+// out, the query's d_sink share -p_sink Dh.  One wave per head, 16 heads a
+// workgroup; lane l holds dims 8 l .. 8 l + 7 (16-byte loads and stores).
+__global__ __launch_bounds__(1024) void bwd_prep_kernel(BwdArgs a, int q0) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_y[2][16][512];
   const int qc = blockIdx.y, qr = q0 + qc;
   const int r = qr % a.Tq;
   const int64_t t = a.q_pos0 + r;
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int h = blockIdx.x * 16 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int d = 8 * lane;
   const bool act = d < a.D;
   uint16_t* yq = a.Y + ((int64_t)qc * 128 + h) * a.D + d;
@@ -533,16 +543,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a, int q0) {
     *reinterpret_cast<uint4*>(&s_y[1][w][d]) = vd;
   }
   __syncthreads();
-  // YT[qc][e][64 p + 4 blockIdx.x ..]: this workgroup's four head slots of
-  // dim e, 8 bytes a store
-  uint16_t* yt = a.YT + (int64_t)qc * a.D * 128 + 4 * blockIdx.x;
-  for (int e = threadIdx.x; e < a.D; e += 256)
+  // YT[qc][e][64 p + 16 blockIdx.x ..]: this workgroup's 16 head slots of
+  // dim e (32 bytes), a (dim, half) pair per thread
+  uint16_t* yt = a.YT + (int64_t)qc * a.D * 128 + 16 * blockIdx.x;
+  for (int i = threadIdx.x; i < 2 * a.D; i += 1024) {
+    const int e = i >> 1, p = i & 1;
+    uint32_t v[8];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint2 v{(uint32_t)s_y[p][0][e] | ((uint32_t)s_y[p][1][e] << 16),
-                    (uint32_t)s_y[p][2][e] | ((uint32_t)s_y[p][3][e] << 16)};
-      *reinterpret_cast<uint2*>(yt + (int64_t)e * 128 + 64 * p) = v;
-    }
+    for (int j = 0; j < 8; ++j)
+      v[j] = (uint32_t)s_y[p][2 * j][e] | ((uint32_t)s_y[p][2 * j + 1][e] << 16);
+    uint4* dst = reinterpret_cast<uint4*>(yt + (int64_t)e * 128 + 64 * p);
+    dst[0] = uint4{v[0], v[1], v[2], v[3]};
+    dst[1] = uint4{v[4], v[5], v[6], v[7]};
+  }
   if (lane == 0 && live) {
     a.Dh[(int64_t)qc * 64 + h] = dd;
     float ds = 0.f;
@@ -1104,7 +1117,7 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, h
     for (int q0 = (int)g0; q0 < g1; q0 += qchunk) {
       const int qc = g1 - q0 < qchunk ? (int)(g1 - q0) : qchunk;
       bwd_gather_kernel<<<dim3((unsigned)((np + 3) / 4), qc), 256, 0, st>>>(a, q0);
-      bwd_prep_kernel<<<dim3(16, qc), 256, 0, st>>>(a, q0);
+      bwd_prep_kernel<<<dim3(4, qc), 1024, 0, st>>>(a, q0);
       // [S; dP] = Y X^T (M = 128, N = np, K = D) and, from it, T = [scale dL; P]
       GemmArgs g1{};
       g1.a = a.Y; g1.lda = a.D; g1.a_batch = 128 * (int64_t)a.D;
