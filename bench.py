@@ -497,7 +497,7 @@ def backward_section(dev, reps):
     wi = synth.normal((1, Tq, HI), seed, "w", dev)
     ki = synth.normal((1, Nc, dI), seed, "kI", dev, dtype=torch.bfloat16)
     dk = torch.zeros((1, Nc, dI), dtype=torch.float32, device=dev)
-    kws = torch.empty(ops.lib().v4attn_index_kl_backward_workspace(1, Tq, dI, k),
+    kws = torch.empty(ops.lib().v4attn_index_kl_backward_workspace(1, Tq, dI, k, Nc),
                       dtype=torch.uint8, device=dev)
     kl = lambda: ops.index_kl_backward(qi, wi, ki, topk, p_sel, dk=dk, workspace=kws)
     raw = synth.normal((1, Tq + m, D), seed, "raw", dev, dtype=torch.bfloat16)

@@ -574,12 +574,20 @@ int v4attn_compress_backward(const uint16_t* raw, const float* tok_score,
  *   sel i32 [B, Tq, ns], target f32 [B, Tq, ns]
  *   loss f32 [B, Tq] (written, nullable); dq_idx f32 [B, Tq, HI, dI] and
  *   dw_idx f32 [B, Tq, HI] (written); dk_idx f32 [B, Ncap, dI] (added to)
- *   ws / ws_bytes >= v4attn_index_kl_backward_workspace(B, Tq, dI, ns)
+ *   ws / ws_bytes: device workspace, 16-byte aligned.  With the bytes of
+ *            v4attn_index_kl_backward_workspace(B, Tq, dI, ns, Ncap) and a
+ *            16-byte aligned dk_idx, the key gradients are grouped: every
+ *            (query, slot) dk row is stored densely (at most 12 GiB per
+ *            group of queries), the slots are sorted by entry and each
+ *            entry's row is added to once.  A smaller workspace, down to the
+ *            per-chunk buffers (the minimum V4ATTN_EWORKSPACE reports), adds
+ *            the dk rows with fp32 atomics instead.
  * 1 <= ns <= 4096, dI in {32, 64, 128}, HI <= 64.  q^I.k^I in fp32 from the
  * bf16 inputs (exact products); ds w [q.k > 0] enters the dq and dk
- * products as bf16; dk rows use fp32 atomics.
+ * products as bf16; an entry chosen by several queries gets their dk rows
+ * in an order that varies from run to run (the last bits vary).
  */
-size_t v4attn_index_kl_backward_workspace(int B, int Tq, int dI, int ns);
+size_t v4attn_index_kl_backward_workspace(int B, int Tq, int dI, int ns, int64_t Ncap);
 int v4attn_index_kl_backward(const uint16_t* q_idx, const float* w_idx,
                              const uint16_t* k_idx, const int32_t* sel,
                              const float* target, int B, int Tq, int HI,

@@ -1041,9 +1041,11 @@ int run_backward(const uint16_t* q, const uint8_t* entries, const int32_t* topk,
   const size_t need = bwd_ws(B, Tq, D, rows_max);
   if (!ws || ws_bytes < need)
     return fail(V4ATTN_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
-  // the grouped row gradients when the workspace holds them, else atomics
+  // the grouped row gradients (16-byte row adds) when the workspace holds
+  // them and the row gradients are 16-byte aligned, else atomics
   const int64_t ndest = bwd_ndest(B, Tq, W, Ncap);
-  const int64_t gq = bwd_group_queries(B, Tq, D, rows_max, ndest, ws_bytes);
+  const bool rows_aligned = (!d_entries || aligned16(d_entries)) && (!d_win || aligned16(d_win));
+  const int64_t gq = rows_aligned ? bwd_group_queries(B, Tq, D, rows_max, ndest, ws_bytes) : 0;
   if (!aligned16(ws)) return fail(V4ATTN_EINVAL, "workspace must be 16-byte aligned");
   const int64_t nq = (int64_t)B * Tq;
   if (nq == 0) return hip_status(hipSuccess, "");
@@ -1159,13 +1161,45 @@ size_t kl_ws(int B, int Tq, int dI, int ns) {
   return (size_t)kl_chunk((int64_t)B * Tq, nsp, dIp) * v4::kl_query_bytes(nsp, dIp);
 }
 
+// Grouped key gradients (as the attention backward's row gradients): the
+// queries per group, a whole multiple of the chunk (or all queries) whose
+// dense dK fits both 12 GiB and what the workspace holds beyond the
+// per-chunk buffers; 0 (atomic adds) when not even one chunk fits or the
+// ids overflow 32 bits.
+int64_t kl_group_queries(int B, int Tq, int dI, int ns, int64_t ndest, size_t ws_bytes) {
+  const int64_t nq = (int64_t)B * Tq;
+  const int64_t nsp = (ns + 63) / 64 * 64;
+  const int dIp = (dI + 63) / 64 * 64;
+  if (nq == 0 || ndest + 1 >= ((int64_t)1 << 31) || nq * nsp >= ((int64_t)1 << 31)) return 0;
+  const int64_t qc = kl_chunk(nq, nsp, dIp);
+  const size_t base = kl_ws(B, Tq, dI, ns);
+  const auto fits = [&](int64_t g) {
+    return base + v4::kl_group_bytes(dI, nsp, g, ndest) <= ws_bytes &&
+           (size_t)g * nsp * dI * 4 <= ((size_t)12 << 30);
+  };
+  if (fits(nq)) return nq;
+  int64_t lo = 0, hi = (nq - 1) / qc;   // chunks per group: fits(lo * qc) holds or lo = 0
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (fits(mid * qc)) lo = mid; else hi = mid - 1;
+  }
+  return lo * qc;
+}
+
+size_t kl_ws_grouped(int B, int Tq, int dI, int ns, int64_t Ncap) {
+  const int64_t nsp = (ns + 63) / 64 * 64;
+  const int64_t nd = (int64_t)B * Ncap;
+  const int64_t gq = kl_group_queries(B, Tq, dI, ns, nd, ~(size_t)0);
+  return kl_ws(B, Tq, dI, ns) + v4::kl_group_bytes(dI, nsp, gq, nd);
+}
+
 }  // namespace
 
 extern "C" {
 
-size_t v4attn_index_kl_backward_workspace(int B, int Tq, int dI, int ns) {
-  if (B < 0 || Tq < 0 || dI < 1 || ns < 1) return 0;
-  return kl_ws(B, Tq, dI, ns);
+size_t v4attn_index_kl_backward_workspace(int B, int Tq, int dI, int ns, int64_t Ncap) {
+  if (B < 0 || Tq < 0 || dI < 1 || ns < 1 || Ncap < 0) return 0;
+  return kl_ws_grouped(B, Tq, dI, ns, Ncap);
 }
 
 int v4attn_index_kl_backward(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx,
@@ -1193,7 +1227,11 @@ int v4attn_index_kl_backward(const uint16_t* q_idx, const float* w_idx, const ui
   a.B = B; a.Tq = Tq; a.HI = HI; a.dI = dI; a.dIp = (dI + 63) / 64 * 64; a.Ncap = Ncap;
   a.ns = ns; a.nsp = (ns + 63) / 64 * 64;
   a.loss = loss; a.dq = dq_idx; a.dw = dw_idx; a.dk = dk_idx;
-  return hip_status(v4::launch_index_kl_backward(a, kl_chunk(nq, a.nsp, a.dIp), ws,
+  // the grouped key gradients (16-byte row adds) when the workspace holds
+  // them and dk is 16-byte aligned, else atomics
+  const int64_t ndest = (int64_t)B * Ncap;
+  const int64_t gq = aligned16(dk_idx) ? kl_group_queries(B, Tq, dI, ns, ndest, ws_bytes) : 0;
+  return hip_status(v4::launch_index_kl_backward(a, kl_chunk(nq, a.nsp, a.dIp), gq, ndest, ws,
                                                  (hipStream_t)stream),
                     "indexer KL backward launch");
 }

@@ -874,24 +874,33 @@ __global__ __launch_bounds__(256) void kl_grad_kernel(KlArgs a, int q0) {
 __global__ __launch_bounds__(256) void kl_gather_kernel(KlArgs a, int q0) {
   const int qc = blockIdx.y, qr = q0 + qc;
   const int b = qr / a.Tq;
-  const int x = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // key rows: dIp / 8 threads a row, 16 bytes each (16 or 32 rows a workgroup)
+  const int cpr = a.dIp >> 3;
+  const int x = blockIdx.x * (256 / cpr) + threadIdx.x / cpr, e = 8 * (threadIdx.x % cpr);
   if (x < a.nsp) {
     const int32_t j = x < a.ns ? a.sel[(int64_t)qr * a.ns + x] : -1;
     const bool ok = j >= 0 && j < a.Ncap;
     uint16_t* dst = a.K + ((int64_t)qc * a.nsp + x) * a.dIp;
     const uint16_t* src = a.k_idx + ((int64_t)b * a.Ncap + (ok ? j : 0)) * a.dI;
-    for (int e = 8 * lane; e < a.dIp; e += 512)   // 16-byte pieces
-      *reinterpret_cast<uint4*>(dst + e) =
-          ok && e < a.dI ? *reinterpret_cast<const uint4*>(src + e) : uint4{0u, 0u, 0u, 0u};
-    if (lane == 0) a.rowmap[(int64_t)qc * a.nsp + x] = ok ? (int64_t)b * a.Ncap + j : -1;
+    *reinterpret_cast<uint4*>(dst + e) =
+        ok && e < a.dI ? *reinterpret_cast<const uint4*>(src + e) : uint4{0u, 0u, 0u, 0u};
+    if (e == 0) {
+      const int64_t d = ok ? (int64_t)b * a.Ncap + j : -1;
+      a.rowmap[(int64_t)qc * a.nsp + x] = d;
+      if (a.dKd) {   // grouped key gradients: the destination and its count
+        a.dest[(int64_t)(qr - a.group_q0) * a.nsp + x] = (int32_t)d;
+        if (d >= 0) atomicAdd(a.cnt + d, 1u);
+      }
+    }
   }
   if (blockIdx.x < 16) {   // 64 head slots of q^I, four a workgroup
+    const int lane = threadIdx.x & 63;
     const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
     uint16_t* dst = a.Qi + ((int64_t)qc * 64 + h) * a.dIp;
     const uint16_t* src = a.q_idx + ((int64_t)qr * a.HI + (h < a.HI ? h : 0)) * a.dI;
-    for (int e = 8 * lane; e < a.dIp; e += 512)
-      *reinterpret_cast<uint4*>(dst + e) =
-          h < a.HI && e < a.dI ? *reinterpret_cast<const uint4*>(src + e) : uint4{0u, 0u, 0u, 0u};
+    for (int e2 = 8 * lane; e2 < a.dIp; e2 += 512)
+      *reinterpret_cast<uint4*>(dst + e2) =
+          h < a.HI && e2 < a.dI ? *reinterpret_cast<const uint4*>(src + e2) : uint4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -1021,23 +1030,27 @@ __global__ __launch_bounds__(256) void bwd_group_scatter_kernel(const int32_t* d
   }
 }
 
-// One wave per destination row: the sum of its slots' gradients, added to
-// the row of d_entries or d_win (lane l: dims 8 l .. 8 l + 7, D <= 512).
-// Four slots' rows are in flight at a time; a group past the list re-reads
-// the last slot and drops it.
-__global__ __launch_bounds__(256) void bwd_group_reduce_kernel(BwdArgs a) {
-  const int64_t d = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (d >= a.ndest) return;
-  const int lane = threadIdx.x & 63, dd = 8 * lane;
-  const uint32_t o0 = a.off[d], o1 = a.off[d + 1];
-  if (o0 == o1 || dd >= a.D) return;
+// The sum of each destination row's slots (dense rows of D floats, D / 8
+// lanes a row, 64 / (D / 8) rows a wave), added to row d of out1 (d < n1)
+// or row d - n1 of out2.  Four slots' rows are in flight at a time; a group
+// past the list re-reads the last slot and drops it.
+template <int LPR>
+__global__ __launch_bounds__(256) void group_reduce_kernel(const float* dense, const int32_t* list,
+                                                           const uint32_t* off, int64_t ndest, int D,
+                                                           float* out1, int64_t n1, float* out2) {
+  const int lane = threadIdx.x & 63;
+  const int64_t d = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;
+  if (d >= ndest) return;
+  const int dd = 8 * (lane % LPR);
+  const uint32_t o0 = off[d], o1 = off[d + 1];
+  if (o0 == o1) return;
   f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
   for (uint32_t o = o0; o < o1; o += 4) {
     f32x4 v0[4], v1[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t id = a.list[min(o + (uint32_t)u, o1 - 1u)];
-      const float* r = a.dXd + id * a.D + dd;
+      const int64_t id = list[min(o + (uint32_t)u, o1 - 1u)];
+      const float* r = dense + id * D + dd;
       v0[u] = *reinterpret_cast<const f32x4*>(r);
       v1[u] = *reinterpret_cast<const f32x4*>(r + 4);
     }
@@ -1048,10 +1061,72 @@ __global__ __launch_bounds__(256) void bwd_group_reduce_kernel(BwdArgs a) {
         s1 += v1[u];
       }
   }
-  float* t = d < a.nent ? a.d_entries + d * a.D + dd : a.d_win + (d - a.nent) * a.D + dd;
+  float* t = d < n1 ? out1 + d * D + dd : out2 + (d - n1) * D + dd;
   f32x4* t4 = reinterpret_cast<f32x4*>(t);
   t4[0] = t4[0] + s0;
   t4[1] = t4[1] + s1;
+}
+
+// Buffers of a grouped sum: per-destination counts (zeroed before the
+// group; the gather counts into them), offsets, tile sums and slot lists.
+struct GroupBufs {
+  int32_t* dest;
+  int32_t* list;
+  uint32_t* cnt;
+  uint32_t* off;
+  uint32_t* tsum;
+  int64_t ndest;
+};
+
+uint8_t* group_layout(GroupBufs& gb, uint8_t* w, int64_t slots, int64_t ndest) {
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  gb.ndest = ndest;
+  gb.dest = reinterpret_cast<int32_t*>(w);  w += al((size_t)slots * 4);
+  gb.list = reinterpret_cast<int32_t*>(w);  w += al((size_t)slots * 4);
+  gb.cnt = reinterpret_cast<uint32_t*>(w);  w += al((size_t)(ndest + 1) * 4);
+  gb.off = reinterpret_cast<uint32_t*>(w);  w += al((size_t)(ndest + 1) * 4);
+  gb.tsum = reinterpret_cast<uint32_t*>(w); w += al((size_t)((ndest + kGroupTile - 1) / kGroupTile) * 4);
+  return w;
+}
+
+size_t group_bytes(int64_t slots, int64_t ndest) {
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  return 2 * al((size_t)slots * 4) + 2 * al((size_t)(ndest + 1) * 4) +
+         al((size_t)((ndest + kGroupTile - 1) / kGroupTile) * 4);
+}
+
+hipError_t group_begin(const GroupBufs& gb, hipStream_t st) {
+  bwd_fill_u32_kernel<<<256, 256, 0, st>>>(gb.cnt, gb.ndest + 1);
+  return hipGetLastError();
+}
+
+// After a group of nslots slots: counts to offsets, the slots listed by
+// destination, and each destination's sum added into its row.
+hipError_t group_sum(const GroupBufs& gb, int64_t nslots, const float* dense, int D, float* out1,
+                     int64_t n1, float* out2, hipStream_t st) {
+  const int64_t ntile = (gb.ndest + kGroupTile - 1) / kGroupTile;
+  if (ntile == 0) return hipSuccess;
+  bwd_group_tile_sum_kernel<<<(unsigned)ntile, 256, 0, st>>>(gb.cnt, gb.tsum, gb.ndest);
+  bwd_group_tile_scan_kernel<<<1, 256, 0, st>>>(gb.tsum, ntile, gb.off, gb.ndest);
+  bwd_group_tile_offsets_kernel<<<(unsigned)ntile, 256, 0, st>>>(gb.cnt, gb.off, gb.tsum, gb.ndest);
+  const int64_t sb = (nslots + 255) / 256;
+  bwd_group_scatter_kernel<<<(unsigned)(sb < 4096 ? sb : 4096), 256, 0, st>>>(gb.dest, gb.cnt, gb.off,
+                                                                               gb.list, nslots);
+  const int lpr = D / 8;
+  const int64_t per_wg = 4 * (64 / lpr);
+  const unsigned grid = (unsigned)((gb.ndest + per_wg - 1) / per_wg);
+#define V4_GROUP_REDUCE(L) \
+  group_reduce_kernel<L><<<grid, 256, 0, st>>>(dense, gb.list, gb.off, gb.ndest, D, out1, n1, out2)
+  switch (lpr) {
+    case 4: V4_GROUP_REDUCE(4); break;
+    case 8: V4_GROUP_REDUCE(8); break;
+    case 16: V4_GROUP_REDUCE(16); break;
+    case 32: V4_GROUP_REDUCE(32); break;
+    case 64: V4_GROUP_REDUCE(64); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef V4_GROUP_REDUCE
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -1075,10 +1150,7 @@ size_t bwd_query_bytes(int D, int64_t np) {
 size_t bwd_group_bytes(int D, int64_t np, int64_t gq, int64_t ndest) {
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
   if (gq <= 0) return 0;
-  return al((size_t)gq * np * D * 4)        // dense dX
-         + 2 * al((size_t)gq * np * 4)      // dest, list
-         + 2 * al((size_t)(ndest + 1) * 4)  // cnt, off
-         + al((size_t)((ndest + kGroupTile - 1) / kGroupTile) * 4);   // tile sums
+  return al((size_t)gq * np * D * 4) + group_bytes(gq * np, ndest);   // dense dX, then the sort
 }
 
 hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, hipStream_t st) {
@@ -1097,22 +1169,20 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, h
   a.G = reinterpret_cast<float*>(w);         w += al((size_t)qchunk * a.D * 4);
   a.DS = reinterpret_cast<float*>(w);        w += al((size_t)qchunk * 64 * 4);
   a.dXd = nullptr;
-  uint32_t* tsum = nullptr;
-  const int64_t ntile = (a.ndest + kGroupTile - 1) / kGroupTile;
+  GroupBufs gb{};
   if (gq > 0) {
     a.dXd = reinterpret_cast<float*>(w);     w += al((size_t)gq * np * a.D * 4);
-    a.dest = reinterpret_cast<int32_t*>(w);  w += al((size_t)gq * np * 4);
-    a.list = reinterpret_cast<int32_t*>(w);  w += al((size_t)gq * np * 4);
-    a.cnt = reinterpret_cast<uint32_t*>(w);  w += al((size_t)(a.ndest + 1) * 4);
-    a.off = reinterpret_cast<uint32_t*>(w);  w += al((size_t)(a.ndest + 1) * 4);
-    tsum = reinterpret_cast<uint32_t*>(w);
+    group_layout(gb, w, gq * np, a.ndest);
+    a.dest = gb.dest;
+    a.cnt = gb.cnt;
   }
   const int64_t gstep = gq > 0 ? gq : nq;
   for (int64_t g0 = 0; g0 < nq; g0 += gstep) {
     const int64_t g1 = g0 + gstep < nq ? g0 + gstep : nq;
     if (gq > 0) {
       a.group_q0 = (int)g0;
-      bwd_fill_u32_kernel<<<256, 256, 0, st>>>(a.cnt, a.ndest + 1);
+      const hipError_t e = group_begin(gb, st);
+      if (e != hipSuccess) return e;
     }
     for (int q0 = (int)g0; q0 < g1; q0 += qchunk) {
       const int qc = g1 - q0 < qchunk ? (int)(g1 - q0) : qchunk;
@@ -1149,17 +1219,7 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, h
       bwd_q_kernel<<<qc, 1024, 0, st>>>(a, q0);
     }
     if (gq > 0) {
-      const int64_t nslots = (g1 - g0) * np;
-      if (ntile > 0) {
-        bwd_group_tile_sum_kernel<<<(unsigned)ntile, 256, 0, st>>>(a.cnt, tsum, a.ndest);
-        bwd_group_tile_scan_kernel<<<1, 256, 0, st>>>(tsum, ntile, a.off, a.ndest);
-        bwd_group_tile_offsets_kernel<<<(unsigned)ntile, 256, 0, st>>>(a.cnt, a.off, tsum, a.ndest);
-      }
-      const int64_t sb = (nslots + 255) / 256;
-      bwd_group_scatter_kernel<<<(unsigned)(sb < 4096 ? sb : 4096), 256, 0, st>>>(a.dest, a.cnt, a.off,
-                                                                                   a.list, nslots);
-      if (a.ndest > 0) bwd_group_reduce_kernel<<<(unsigned)((a.ndest + 3) / 4), 256, 0, st>>>(a);
-      hipError_t e = hipGetLastError();
+      const hipError_t e = group_sum(gb, (g1 - g0) * np, a.dXd, a.D, a.d_entries, a.nent, a.d_win, st);
       if (e != hipSuccess) return e;
     }
   }
@@ -1181,7 +1241,14 @@ size_t kl_query_bytes(int64_t nsp, int dIp) {
          al((size_t)nsp * 4);
 }
 
-hipError_t launch_index_kl_backward(KlArgs a, int qchunk, void* ws, hipStream_t st) {
+size_t kl_group_bytes(int dI, int64_t nsp, int64_t gq, int64_t ndest) {
+  auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+  if (gq <= 0) return 0;
+  return al((size_t)gq * nsp * dI * 4) + group_bytes(gq * nsp, ndest);   // dense dK, then the sort
+}
+
+hipError_t launch_index_kl_backward(KlArgs a, int qchunk, int64_t gq, int64_t ndest, void* ws,
+                                    hipStream_t st) {
   const int nq = a.B * a.Tq;
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -1192,39 +1259,66 @@ hipError_t launch_index_kl_backward(KlArgs a, int qchunk, void* ws, hipStream_t 
   a.Am = reinterpret_cast<float*>(w);        w += al((size_t)qchunk * 64 * nsp * 4);
   a.Gm = reinterpret_cast<uint16_t*>(w);     w += al((size_t)qchunk * 64 * nsp * 2);
   a.DQ = reinterpret_cast<float*>(w);        w += al((size_t)qchunk * 64 * a.dIp * 4);
-  a.Sb = reinterpret_cast<float*>(w);
-  for (int q0 = 0; q0 < nq; q0 += qchunk) {
-    const int qc = nq - q0 < qchunk ? nq - q0 : qchunk;
-    const unsigned gx = (unsigned)((nsp + 3) / 4 > 16 ? (nsp + 3) / 4 : 16);
-    kl_gather_kernel<<<dim3(gx, qc), 256, 0, st>>>(a, q0);
-    // A = Qi K^T: M = 64, N = nsp, K = dIp
-    GemmArgs g1{};
-    g1.a = a.Qi; g1.lda = a.dIp; g1.a_batch = 64 * (int64_t)a.dIp;
-    g1.b = a.K; g1.ldb = a.dIp; g1.b_batch = nsp * a.dIp;
-    g1.c = a.Am; g1.ldc = nsp; g1.c_batch = 64 * nsp; g1.K = a.dIp; g1.alpha = 1.f;
-    g1.n_valid = (int)nsp;
-    hipError_t e = gemm<false, true>(g1, 64, (int)nsp, qc, st);
-    if (e != hipSuccess) return e;
-    kl_score_kernel<<<dim3((unsigned)((nsp + 255) / 256), qc), 256, 0, st>>>(a, q0);
-    kl_reduce_kernel<<<qc, 256, 0, st>>>(a, q0);
-    kl_grad_kernel<<<dim3((unsigned)((nsp + 255) / 256), qc), 256, 0, st>>>(a, q0);
-    // dq = G K: M = 64, N = dIp, K = nsp
-    GemmArgs g2{};
-    g2.a = a.Gm; g2.lda = nsp; g2.a_batch = 64 * nsp;
-    g2.b = a.K; g2.ldb = a.dIp; g2.b_batch = nsp * a.dIp;
-    g2.c = a.DQ; g2.ldc = a.dIp; g2.c_batch = 64 * (int64_t)a.dIp; g2.K = (int)nsp; g2.alpha = 1.f;
-    g2.n_valid = a.dIp;
-    e = gemm<false, false>(g2, 64, a.dIp, qc, st);
-    if (e != hipSuccess) return e;
-    kl_dq_kernel<<<qc, 256, 0, st>>>(a, q0);
-    // dK = G^T Qi, added into dk rows: M = nsp, N = dIp (first dI kept), K = 64
-    GemmArgs g3{};
-    g3.a = a.Gm; g3.lda = nsp; g3.a_batch = 64 * nsp;
-    g3.b = a.Qi; g3.ldb = a.dIp; g3.b_batch = 64 * (int64_t)a.dIp;
-    g3.c = a.dk; g3.ldc = a.dI; g3.K = 64; g3.alpha = 1.f; g3.n_valid = a.dI;
-    g3.rowmap = a.rowmap; g3.rowmap_batch = nsp;
-    e = gemm<true, false>(g3, (int)nsp, a.dIp, qc, st);
-    if (e != hipSuccess) return e;
+  a.Sb = reinterpret_cast<float*>(w);      w += al((size_t)qchunk * nsp * 4);
+  a.dKd = nullptr;
+  GroupBufs gb{};
+  if (gq > 0) {
+    a.dKd = reinterpret_cast<float*>(w);     w += al((size_t)gq * nsp * a.dI * 4);
+    group_layout(gb, w, gq * nsp, ndest);
+    a.dest = gb.dest;
+    a.cnt = gb.cnt;
+  }
+  const int64_t gstep = gq > 0 ? gq : nq;
+  for (int64_t g0 = 0; g0 < nq; g0 += gstep) {
+    const int64_t g1 = g0 + gstep < nq ? g0 + gstep : nq;
+    if (gq > 0) {
+      a.group_q0 = (int)g0;
+      const hipError_t e = group_begin(gb, st);
+      if (e != hipSuccess) return e;
+    }
+    for (int q0 = (int)g0; q0 < g1; q0 += qchunk) {
+      const int qc = g1 - q0 < qchunk ? (int)(g1 - q0) : qchunk;
+      const int64_t rpw = 2048 / a.dIp;   // key rows a gather workgroup
+      const unsigned gx = (unsigned)((nsp + rpw - 1) / rpw > 16 ? (nsp + rpw - 1) / rpw : 16);
+      kl_gather_kernel<<<dim3(gx, qc), 256, 0, st>>>(a, q0);
+      // A = Qi K^T: M = 64, N = nsp, K = dIp
+      GemmArgs g1{};
+      g1.a = a.Qi; g1.lda = a.dIp; g1.a_batch = 64 * (int64_t)a.dIp;
+      g1.b = a.K; g1.ldb = a.dIp; g1.b_batch = nsp * a.dIp;
+      g1.c = a.Am; g1.ldc = nsp; g1.c_batch = 64 * nsp; g1.K = a.dIp; g1.alpha = 1.f;
+      g1.n_valid = (int)nsp;
+      hipError_t e = gemm<false, true>(g1, 64, (int)nsp, qc, st);
+      if (e != hipSuccess) return e;
+      kl_score_kernel<<<dim3((unsigned)((nsp + 255) / 256), qc), 256, 0, st>>>(a, q0);
+      kl_reduce_kernel<<<qc, 256, 0, st>>>(a, q0);
+      kl_grad_kernel<<<dim3((unsigned)((nsp + 255) / 256), qc), 256, 0, st>>>(a, q0);
+      // dq = G K: M = 64, N = dIp, K = nsp
+      GemmArgs g2{};
+      g2.a = a.Gm; g2.lda = nsp; g2.a_batch = 64 * nsp;
+      g2.b = a.K; g2.ldb = a.dIp; g2.b_batch = nsp * a.dIp;
+      g2.c = a.DQ; g2.ldc = a.dIp; g2.c_batch = 64 * (int64_t)a.dIp; g2.K = (int)nsp; g2.alpha = 1.f;
+      g2.n_valid = a.dIp;
+      e = gemm<false, false>(g2, 64, a.dIp, qc, st);
+      if (e != hipSuccess) return e;
+      kl_dq_kernel<<<qc, 256, 0, st>>>(a, q0);
+      // dK = G^T Qi: M = nsp, N = dIp (first dI kept), K = 64; stored densely
+      // for the group's sum by destination, or added into dk rows (atomics)
+      GemmArgs g3{};
+      g3.a = a.Gm; g3.lda = nsp; g3.a_batch = 64 * nsp;
+      g3.b = a.Qi; g3.ldb = a.dIp; g3.b_batch = 64 * (int64_t)a.dIp;
+      g3.ldc = a.dI; g3.K = 64; g3.alpha = 1.f; g3.n_valid = a.dI;
+      if (a.dKd) {
+        g3.c = a.dKd + (int64_t)(q0 - g0) * nsp * a.dI; g3.c_batch = nsp * a.dI;
+      } else {
+        g3.c = a.dk; g3.rowmap = a.rowmap; g3.rowmap_batch = nsp;
+      }
+      e = gemm<true, false>(g3, (int)nsp, a.dIp, qc, st);
+      if (e != hipSuccess) return e;
+    }
+    if (gq > 0) {
+      const hipError_t e = group_sum(gb, (g1 - g0) * nsp, a.dKd, a.dI, a.dk, ndest, nullptr, st);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipGetLastError();
 }

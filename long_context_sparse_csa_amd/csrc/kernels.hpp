@@ -316,9 +316,7 @@ struct BwdArgs {
   float* dXd;                // [group, np, D]
   int32_t* dest;             // [group, np] destination row: b Ncap + j, or
                              // B Ncap + window row, or -1
-  int32_t* list;             // [group, np] slot ids grouped by destination
-  uint32_t* cnt;             // [ndest + 1] slots per destination (then cursors)
-  uint32_t* off;             // [ndest + 1] first list position per destination
+  uint32_t* cnt;             // [ndest + 1] slots per destination
   int64_t nent;              // B Ncap: destinations below are entries
   int64_t ndest;             // B Ncap + B (Tq + W - 1)
   int group_q0;              // first query of the current group
@@ -375,8 +373,19 @@ struct KlArgs {
   uint16_t* Gm;
   float* DQ;
   float* Sb;                 // [chunk, nsp] scores, then d loss / d score
+  // grouped key gradients (dKd != nullptr), as the attention backward's
+  // row gradients: dense dK per (query, slot), summed per destination row
+  float* dKd;                // [group, nsp, dI]
+  int32_t* dest;             // [group, nsp] b Ncap + j, or -1
+  uint32_t* cnt;             // [B Ncap + 1] slots per destination
+  int group_q0;
 };
 size_t kl_query_bytes(int64_t nsp, int dIp);
-hipError_t launch_index_kl_backward(KlArgs a, int qchunk, void* ws, hipStream_t st);
+// Workspace bytes of the grouped key gradients for groups of gq queries.
+size_t kl_group_bytes(int dI, int64_t nsp, int64_t gq, int64_t ndest);
+// gq = 0: key gradients by atomic adds; gq > 0: grouped (a multiple of
+// qchunk, or all queries), ndest = B Ncap destinations.
+hipError_t launch_index_kl_backward(KlArgs a, int qchunk, int64_t gq, int64_t ndest, void* ws,
+                                    hipStream_t st);
 
 }  // namespace v4

@@ -68,7 +68,7 @@ _SIGS = {
                                         _Z, _P]),
     "v4attn_compress_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _L, _I, _F, _F, _P,
                                       _P, _P, _P, _P, _P]),
-    "v4attn_index_kl_backward_workspace": (_Z, [_I, _I, _I, _I]),
+    "v4attn_index_kl_backward_workspace": (_Z, [_I, _I, _I, _I, _L]),
     "v4attn_index_kl_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _I, _P, _P, _P, _P,
                                       _P, _Z, _P]),
     "v4attn_hca_attend_backward_workspace": (_Z, [_I, _I, _I, _I, _L, _I, _L, _I, _L]),
@@ -745,10 +745,13 @@ def compress_backward(raw, tok_score, pos_bias, gamma, d_entries, *, raw_pos0, m
     return d_raw, d_score, d_bias, d_gamma
 
 
-def index_kl_backward(q_idx, w_idx, k_idx, sel, target, *, dk=None, workspace=None):
+def index_kl_backward(q_idx, w_idx, k_idx, sel, target, *, dk=None, workspace=None,
+                      workspace_bytes=None):
     """Indexer KL loss over the entry set `sel` (int32 [B, Tq, ns]) with target
     weights (f32 [B, Tq, ns]).  Returns (loss [B, Tq], dq_idx, dw_idx, dk_idx);
-    dk_idx is added into `dk` if given."""
+    dk_idx is added into `dk` if given.  workspace_bytes below the queried
+    size (down to the per-chunk buffers) makes the library add the dk rows
+    with atomics instead of grouping them."""
     _need(q_idx, "q_idx", torch.bfloat16, 4)
     _need(k_idx, "k_idx", torch.bfloat16, 3)
     _need(sel, "sel", torch.int32, 3)
@@ -761,7 +764,8 @@ def index_kl_backward(q_idx, w_idx, k_idx, sel, target, *, dk=None, workspace=No
     dw = torch.empty((B, Tq, HI), dtype=torch.float32, device=dev)
     if dk is None:
         dk = torch.zeros((B, k_idx.shape[1], dI), dtype=torch.float32, device=dev)
-    nbytes = lib().v4attn_index_kl_backward_workspace(B, Tq, dI, ns)
+    nbytes = lib().v4attn_index_kl_backward_workspace(B, Tq, dI, ns, k_idx.shape[1])
+    nbytes = nbytes if workspace_bytes is None else int(workspace_bytes)
     workspace = _workspace(nbytes, dev, workspace)
     check(lib().v4attn_index_kl_backward(
         _ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(sel), _ptr(target), B, Tq, HI, dI,

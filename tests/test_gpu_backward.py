@@ -295,11 +295,7 @@ KL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", KL_CASES)
-def test_index_kl_backward_matches_oracle(case):
-    B, Tq, HI, dI, Ncap, ns, nv = case
-    log(f"indexer KL backward {case}")
-    seed = sum(case[:6]) % 953
+def _kl_inputs(B, Tq, HI, dI, Ncap, ns, nv, seed):
     qi = synth.normal((B, Tq, HI, dI), seed, "qI", DEV, dtype=torch.bfloat16)
     wi = synth.normal((B, Tq, HI), seed, "w", DEV)
     ki = synth.normal((B, Ncap, dI), seed, "kI", DEV, dtype=torch.bfloat16)
@@ -311,13 +307,15 @@ def test_index_kl_backward_matches_oracle(case):
             sel[b, r, :n] = torch.randperm(Ncap, generator=g)[:n].sort().values.to(torch.int32)
     tgt = torch.rand((B, Tq, ns), generator=g)
     tgt[tgt < 0.1] = 0.0
-    sel, tgt = sel.to(DEV), tgt.to(DEV)
-    loss, dq, dw, dk = ops().index_kl_backward(qi, wi, ki, sel, tgt)
-    torch.cuda.synchronize()
+    return qi, wi, ki, sel.to(DEV), tgt.to(DEV)
+
+
+def _kl_reference(qi, wi, ki, sel, tgt):
+    B, Tq, HI, dI = qi.shape
     qn, kn = bf16_to_f64(qi), bf16_to_f64(ki)
     wn, seln, tn = wi.cpu().double().numpy(), sel.cpu().numpy(), tgt.cpu().double().numpy()
     r_loss, r_dq, r_dw = np.zeros((B, Tq)), np.zeros((B, Tq, HI, dI)), np.zeros((B, Tq, HI))
-    r_dk = np.zeros((B, Ncap, dI))
+    r_dk = np.zeros((B, ki.shape[1], dI))
     for b in range(B):
         for r in range(Tq):
             v = seln[b, r] >= 0
@@ -326,6 +324,12 @@ def test_index_kl_backward_matches_oracle(case):
             l_, dq_, dw_, dk_ = ob.indexer_kl(qn[b, r], wn[b, r], kn[b][idx], P)
             r_loss[b, r], r_dq[b, r], r_dw[b, r] = l_, dq_, dw_
             np.add.at(r_dk[b], idx, dk_)
+    return r_loss, r_dq, r_dw, r_dk
+
+
+def _kl_check(got, want):
+    loss, dq, dw, dk = got
+    r_loss, r_dq, r_dw, r_dk = want
     np.testing.assert_allclose(loss.cpu().double().numpy(), r_loss, rtol=1e-4, atol=1e-6)
     for n, g_, w_, tol in (("dw", dw, r_dw, 1e-4), ("dq", dq, r_dq, REL_L2), ("dk", dk, r_dk, REL_L2)):
         g_ = g_.cpu().double().numpy()
@@ -333,6 +337,32 @@ def test_index_kl_backward_matches_oracle(case):
         mx = np.abs(g_ - w_).max() / np.abs(w_).max()
         log(f"  {n}: rel-L2 {rel:.2e}, max-abs/max {mx:.2e}")
         assert rel <= tol and mx <= max(tol, MAX_REL if n != "dw" else 1e-4), n
+
+
+@pytest.mark.parametrize("case", KL_CASES)
+def test_index_kl_backward_matches_oracle(case):
+    B, Tq, HI, dI, Ncap, ns, nv = case
+    log(f"indexer KL backward {case}")
+    inp = _kl_inputs(B, Tq, HI, dI, Ncap, ns, nv, sum(case[:6]) % 953)
+    got = ops().index_kl_backward(*inp)
+    torch.cuda.synchronize()
+    _kl_check(got, _kl_reference(*inp))
+
+
+def test_index_kl_backward_key_gradient_paths_match_oracle():
+    """dk grouped in one group (the queried workspace), in several (a byte
+    less: 256 + 44 queries), and added with atomics (2 MiB less: at this
+    shape the per-chunk buffers take 256 x ~57 KiB ~ 14.6 MB and a 256-query
+    group's dense dk 2.1 MB), on 300 queries whose sets share keys."""
+    B, Tq, HI, dI, Ncap, ns = 1, 300, 4, 32, 200, 64
+    inp = _kl_inputs(B, Tq, HI, dI, Ncap, ns, 60, 23)
+    want = _kl_reference(*inp)
+    full = ops().lib().v4attn_index_kl_backward_workspace(B, Tq, dI, ns, Ncap)
+    for nbytes, what in ((full, "one group"), (full - 1, "two groups"), (full - (1 << 21), "atomics")):
+        log(f"indexer KL backward dk: {what}, workspace {nbytes} of {full} bytes")
+        got = ops().index_kl_backward(*inp, workspace_bytes=nbytes)
+        torch.cuda.synchronize()
+        _kl_check(got, want)
 
 
 def test_attention_backward_p_sel_is_the_kl_target():
