@@ -165,7 +165,8 @@ constexpr int gemm32_smem_bytes() {
 
 // The main loop of gemm32: this workgroup's TM x 128 tile of A[z] B[z] in acc
 // (lane: column lane % 32 of each 32 x 32 block, rows (e/4) 8 + (lane/32) 4 + e % 4).
-template <int TM, bool AT, bool BT>
+// PF k-tiles are in flight from global memory (K a multiple of PF x 32).
+template <int TM, bool AT, bool BT, int PF>
 __device__ __forceinline__ void gemm32_main(const GemmArgs& g, uint8_t* smem, f32x16 (&acc)[TM / 64][2],
                                             int n0, int m0, int z) {
   constexpr int TN = 128, BK = 32, KP = 40;   // KP: padded k stride (elements) of the LDS tiles
@@ -200,11 +201,16 @@ __device__ __forceinline__ void gemm32_main(const GemmArgs& g, uint8_t* smem, f3
       s[8 * ch + 2 * e + 1][kk] = (uint16_t)(w[e] >> 16);
     }
   };
-  uint4 ra[LA], rb[LB];
+  uint4 ra[PF][LA], rb[PF][LB];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) ra[i] = fetch(A, g.lda, m0, 0, AT, TM, i);
+  for (int p = 0; p < PF; ++p) {
+    if (p * BK < g.K) {
 #pragma unroll
-  for (int i = 0; i < LB; ++i) rb[i] = fetch(B, g.ldb, n0, 0, !BT, TN, i);
+      for (int i = 0; i < LA; ++i) ra[p][i] = fetch(A, g.lda, m0, p * BK, AT, TM, i);
+#pragma unroll
+      for (int i = 0; i < LB; ++i) rb[p][i] = fetch(B, g.ldb, n0, p * BK, !BT, TN, i);
+    }
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -212,34 +218,38 @@ __device__ __forceinline__ void gemm32_main(const GemmArgs& g, uint8_t* smem, f3
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
   int buf = 0;
-  for (int k0 = 0; k0 < g.K; k0 += BK) {
+  for (int k00 = 0; k00 < g.K; k00 += PF * BK) {
 #pragma unroll
-    for (int i = 0; i < LA; ++i) put(sA[buf], ra[i], AT, TM, i);
+    for (int p = 0; p < PF; ++p) {
+      const int k0 = k00 + p * BK;
 #pragma unroll
-    for (int i = 0; i < LB; ++i) put(sB[buf], rb[i], !BT, TN, i);
-    __syncthreads();   // buffer buf complete; every wave is done with buf ^ 1's last reads
-    if (k0 + BK < g.K) {
+      for (int i = 0; i < LA; ++i) put(sA[buf], ra[p][i], AT, TM, i);
 #pragma unroll
-      for (int i = 0; i < LA; ++i) ra[i] = fetch(A, g.lda, m0, k0 + BK, AT, TM, i);
+      for (int i = 0; i < LB; ++i) put(sB[buf], rb[p][i], !BT, TN, i);
+      __syncthreads();   // buffer buf complete; every wave is done with buf ^ 1's last reads
+      if (k0 + PF * BK < g.K) {
 #pragma unroll
-      for (int i = 0; i < LB; ++i) rb[i] = fetch(B, g.ldb, n0, k0 + BK, !BT, TN, i);
-    }
+        for (int i = 0; i < LA; ++i) ra[p][i] = fetch(A, g.lda, m0, k0 + PF * BK, AT, TM, i);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 av[MB], bv[2];
+        for (int i = 0; i < LB; ++i) rb[p][i] = fetch(B, g.ldb, n0, k0 + PF * BK, !BT, TN, i);
+      }
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        av[mb] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * WM + 32 * mb + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        bf16x8 av[MB], bv[2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        bv[nb] = *reinterpret_cast<const bf16x8*>(&sB[buf][wn * 64 + 32 * nb + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
+          av[mb] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * WM + 32 * mb + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+          bv[nb] = *reinterpret_cast<const bf16x8*>(&sB[buf][wn * 64 + 32 * nb + (lane & 31)][16 * ks + 8 * (lane >> 5)]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+      }
+      buf ^= 1;
     }
-    buf ^= 1;
   }
 }
 
@@ -260,7 +270,7 @@ __global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int
     s_dh[tid] = a.Dh[(int64_t)z * 64 + tid];
   }
   f32x16 acc[2][2];
-  gemm32_main<128, false, true>(g, smem, acc, n0, 0, z);
+  gemm32_main<128, false, true, 2>(g, smem, acc, n0, 0, z);
   const int wm = wave >> 1, wn = wave & 1;
   __syncthreads();   // the operand tiles are done with: the space holds [S; dP]
   auto sC = reinterpret_cast<float (*)[129]>(smem);
@@ -327,7 +337,7 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(GemmArgs g) {
   const int z = bt.z, n0 = bt.x * 128, m0 = bt.y * 128;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   f32x16 acc[2][2];
-  gemm32_main<128, false, true>(g, smem, acc, n0, m0, z);
+  gemm32_main<128, false, true, 1>(g, smem, acc, n0, m0, z);
   const int wm = wave >> 1, wn = wave & 1;
   __syncthreads();   // the operand tiles are done with: the space holds the C tile
   auto sC = reinterpret_cast<float (*)[129]>(smem);
