@@ -373,7 +373,11 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(GemmArgs g) {
 
 // X[qc, x, :] = the query's row x as bf16 (zeros if absent), rowmap = where
 // its gradient goes: entry b Ncap + j (>= 0), window row -2 - (b (Tq+W-1) + r),
-// or -1.  One wave per row slot.
+// or -1.  One wave per kGatherRows row slots (their loads in flight together).
+#ifndef V4_GATHER_ROWS
+#define V4_GATHER_ROWS 2
+#endif
+constexpr int kGatherRows = V4_GATHER_ROWS;
 __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a, int q0) {
   // the arguments are read in one round before any branch (the empty asm
   // statements keep the compiler from sinking each read into the branch
@@ -395,8 +399,9 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a, int q0) {
   const int qc = blockIdx.y, qr = q0 + qc;
   const int b = qr / Tq, r = qr % Tq;
   const int64_t t = q_pos0 + r;
-  const int x = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (x >= np) return;
+  constexpr int RPW = kGatherRows;
+  const int x0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW, lane = threadIdx.x & 63;
+  if (x0 >= np) return;   // np is a multiple of 128: all RPW slots exist
   int64_t n_ent;
   if (topk) {
     n_ent = k;
@@ -407,51 +412,70 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(BwdArgs a, int q0) {
   const int64_t lo = t - W + 1 > 0 ? t - W + 1 : 0;
   const int64_t n_win = W > 0 ? t - lo + 1 : 0;
   const int ROW = D + R;
-  const uint8_t* src = nullptr;
-  int64_t map = -1;
-  if (x < n_ent) {
-    const int64_t j = topk ? (int64_t)topk[(int64_t)qr * k + x] : (int64_t)x;
-    if (j >= 0 && j < Ncap) {
-      src = entries + ((int64_t)b * Ncap + j) * ROW;
-      map = (int64_t)b * Ncap + j;
+  const uint8_t* src[RPW];
+  int64_t map[RPW];
+#pragma unroll
+  for (int u = 0; u < RPW; ++u) {
+    const int x = x0 + u;
+    src[u] = nullptr;
+    map[u] = -1;
+    if (x < n_ent) {
+      const int64_t j = topk ? (int64_t)topk[(int64_t)qr * k + x] : (int64_t)x;
+      if (j >= 0 && j < Ncap) {
+        src[u] = entries + ((int64_t)b * Ncap + j) * ROW;
+        map[u] = (int64_t)b * Ncap + j;
+      }
+    } else if (x < n_ent + n_win) {
+      const int64_t wrow = lo + (x - n_ent) - (q_pos0 - (W - 1));
+      const int64_t grow = (int64_t)b * (Tq + W - 1) + wrow;
+      src[u] = win + grow * ROW;
+      map[u] = -2 - grow;
     }
-  } else if (x < n_ent + n_win) {
-    const int64_t wrow = lo + (x - n_ent) - (q_pos0 - (W - 1));
-    const int64_t grow = (int64_t)b * (Tq + W - 1) + wrow;
-    src = win + grow * ROW;
-    map = -2 - grow;
   }
-  if (lane == 0) {
-    rowmap[(int64_t)qc * np + x] = map;
+  if (lane < RPW) {   // lane u: slot x0 + u's bookkeeping
+    int64_t mp = map[0];
+#pragma unroll
+    for (int u = 1; u < RPW; ++u) mp = lane == u ? map[u] : mp;
+    rowmap[(int64_t)qc * np + x0 + lane] = mp;
     if (grouped) {   // grouped row gradients: the destination and its count
-      const int64_t d = map >= 0 ? map : (map <= -2 ? nent + (-2 - map) : -1);
-      dest[(int64_t)(qr - group_q0) * np + x] = (int32_t)d;
+      const int64_t d = mp >= 0 ? mp : (mp <= -2 ? nent + (-2 - mp) : -1);
+      dest[(int64_t)(qr - group_q0) * np + x0 + lane] = (int32_t)d;
       if (d >= 0) atomicAdd(cnt + d, 1u);
     }
   }
-  uint16_t* dst = X + ((int64_t)qc * np + x) * D;
   const int E = D - R;
   const int d = 8 * lane;   // this lane's 8 dims (E and D are multiples of 8)
-  if (d < D) {
-    uint4 o = {0u, 0u, 0u, 0u};
-    if (src) {
-      if (d < E) {   // 8 E4M3 bytes -> 8 bf16 (exact)
-        const uint2 b8 = *reinterpret_cast<const uint2*>(src + d);
-        const uint32_t w2[2] = {b8.x, b8.y};
-        uint32_t rr[4];
+  if (d >= D) return;
+  // every slot's load is issued before the first conversion and store
+  uint4 o[RPW];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f32x2 lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w2[h], false);
-          const f32x2 hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w2[h], true);
-          rr[2 * h] = (__float_as_uint(lo2[0]) >> 16) | (__float_as_uint(lo2[1]) & 0xFFFF0000u);
-          rr[2 * h + 1] = (__float_as_uint(hi2[0]) >> 16) | (__float_as_uint(hi2[1]) & 0xFFFF0000u);
-        }
-        o = uint4{rr[0], rr[1], rr[2], rr[3]};
-      } else {       // bf16 dims as stored
-        o = *reinterpret_cast<const uint4*>(src + E + 2 * (d - E));
+  for (int u = 0; u < RPW; ++u) {
+    o[u] = uint4{0u, 0u, 0u, 0u};
+    if (src[u]) {
+      if (d < E) {
+        const uint2 b8 = *reinterpret_cast<const uint2*>(src[u] + d);
+        o[u] = uint4{b8.x, b8.y, 0u, 0u};
+      } else {
+        o[u] = *reinterpret_cast<const uint4*>(src[u] + E + 2 * (d - E));
       }
     }
-    *reinterpret_cast<uint4*>(dst + d) = o;
+  }
+#pragma unroll
+  for (int u = 0; u < RPW; ++u) {
+    uint4 w = o[u];
+    if (src[u] && d < E) {   // 8 E4M3 bytes -> 8 bf16 (exact)
+      const uint32_t w2[2] = {o[u].x, o[u].y};
+      uint32_t rr[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x2 lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w2[h], false);
+        const f32x2 hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w2[h], true);
+        rr[2 * h] = (__float_as_uint(lo2[0]) >> 16) | (__float_as_uint(lo2[1]) & 0xFFFF0000u);
+        rr[2 * h + 1] = (__float_as_uint(hi2[0]) >> 16) | (__float_as_uint(hi2[1]) & 0xFFFF0000u);
+      }
+      w = uint4{rr[0], rr[1], rr[2], rr[3]};
+    }
+    *reinterpret_cast<uint4*>(X + ((int64_t)qc * np + x0 + u) * D + d) = w;
   }
 }
 
@@ -1196,7 +1220,8 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, h
     }
     for (int q0 = (int)g0; q0 < g1; q0 += qchunk) {
       const int qc = g1 - q0 < qchunk ? (int)(g1 - q0) : qchunk;
-      bwd_gather_kernel<<<dim3((unsigned)((np + 3) / 4), qc), 256, 0, st>>>(a, q0);
+      bwd_gather_kernel<<<dim3((unsigned)((np + 4 * kGatherRows - 1) / (4 * kGatherRows)), qc), 256, 0,
+                          st>>>(a, q0);
       bwd_prep_kernel<<<dim3(4, qc), 1024, 0, st>>>(a, q0);
       // [S; dP] = Y X^T (M = 128, N = np, K = D) and, from it, T = [scale dL; P]
       GemmArgs g1{};
