@@ -206,6 +206,30 @@ def test_workspace_sizes_are_host_arithmetic():
     assert L().v4attn_hca_attend_workspace(32, 1, 64, 512, 8192, 128, (1 << 20) - 1, 128) > 0
 
 
+def test_backward_workspaces_hold_the_grouped_gradients():
+    """The backward workspace queries include the dense per-slot gradients
+    and the sort buffers of one group (all queries, under 12 GiB), so they
+    grow with the number of queries and destination rows; past 32-bit slot
+    or destination ids the grouped path is off and the query returns the
+    per-chunk part alone."""
+    csa = L().v4attn_csa_attend_backward_workspace
+    # 4096 queries x (1024 + 128) rows x 512 dims fp32 = 9.66 GB of dense dX
+    n = csa(1, 4096, 64, 512, 1024, 128, 262144)
+    assert 4096 * 1152 * 512 * 4 < n < (12 << 30) + (2 << 30)
+    assert csa(1, 64, 64, 512, 1024, 128, 262144) < n          # one chunk
+    assert csa(1, 4096, 64, 512, 1024, 128, 1 << 20) > n       # more destinations
+    base = csa(1, 4096, 64, 512, 1024, 128, 1 << 31)          # ids past 2^31: atomics
+    assert base < 4096 * 1152 * 512 * 4 < n
+    assert csa(1, 4096, 64, 512, 1024, 128, -1) == 0
+    hca = L().v4attn_hca_attend_backward_workspace
+    assert hca(2, 8, 64, 512, 300, 128, 300 * 128 + 5, 16, 300) > 0
+    kl = L().v4attn_index_kl_backward_workspace
+    n = kl(1, 4096, 128, 1024, 262144)                         # 2.15 GB of dense dk
+    assert 4096 * 1024 * 128 * 4 < n
+    assert kl(1, 4096, 128, 1024, 1 << 31) < 4096 * 1024 * 128 * 4
+    assert kl(1, 4096, 128, 1024, -1) == 0
+
+
 def _csa(**kw):
     a = dict(q=FAKE, e=FAKE, t=FAKE, w=FAKE, g=FAKE, s=FAKE, B=1, Tq=1, H=64, D=512, R=64,
              Ncap=100, k=64, W=128, q_pos0=500, scale=0.04, eps=1e-6, base=1e4, out=FAKE,

@@ -219,6 +219,44 @@ def test_csa_backward_row_gradient_paths_match_oracle():
         _check(got, want, f"csa rows {what}")
 
 
+def _misaligned_zeros(shape):
+    """Zeros whose first element sits 4 bytes past a 16-byte boundary."""
+    n = int(np.prod(shape))
+    return torch.zeros(n + 1, dtype=torch.float32, device=DEV)[1:].view(shape)
+
+
+def test_backward_misaligned_row_gradients_take_the_atomic_path():
+    """Row and key gradients not 16-byte aligned cannot take the grouped
+    sum's vector adds: the calls fall back to atomics and still match the
+    oracle."""
+    B, Tq, H, D, Ncap, k, W, q_pos0 = 1, 6, 16, 128, 100, 24, 8, 300
+    q, ent, win, gq, sink, dout = _inputs(B, Tq, H, D, Ncap, W, 31)
+    g = torch.Generator().manual_seed(3)
+    topk = torch.stack([torch.randperm(40, generator=g)[:k].sort().values
+                        for _ in range(Tq)])[None].to(torch.int32).to(DEV)
+    scale = D ** -0.5
+    out, lse = ops().csa_attend(q, ent, topk, win, gq, sink, q_pos0=q_pos0, W=W, scale=scale,
+                                want_lse=True)
+    grads = {"d_entries": _misaligned_zeros((B, Ncap, D)),
+             "d_win": _misaligned_zeros((B, Tq + W - 1, D))}
+    assert grads["d_entries"].data_ptr() % 16 == 4
+    got = ops().csa_attend_backward(q, ent, topk, win, gq, sink, out, lse, dout, q_pos0=q_pos0,
+                                    W=W, scale=scale, grads=grads)
+    torch.cuda.synchronize()
+    tk = topk.cpu().numpy()
+
+    def rows_of(b, r, t):
+        return tk[b, r], _win_rows(t, q_pos0, W)
+
+    _check(got, _reference(q, ent, win, gq, sink, dout, rows_of, q_pos0, W, scale, D),
+           "csa misaligned rows")
+    inp = _kl_inputs(1, 5, 8, 64, 90, 64, 40, 41)
+    dk = _misaligned_zeros((1, 90, 64))
+    got = ops().index_kl_backward(*inp, dk=dk)
+    torch.cuda.synchronize()
+    _kl_check(got, _kl_reference(*inp))
+
+
 def test_backward_adds_into_given_gradients():
     """Row, sink and gamma gradients are added to what the buffers hold."""
     B, Tq, H, D, Ncap, k, W, q_pos0 = 1, 2, 16, 128, 64, 16, 4, 100
