@@ -493,9 +493,12 @@ int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries,
  *            gradients are grouped: every (query, row slot) gradient is
  *            stored densely (at most 12 GiB per group of queries), the slots
  *            are sorted by destination row and each row is added to once.
- *            A smaller workspace, down to the per-chunk buffers alone (the
- *            minimum V4ATTN_EWORKSPACE reports), adds the row gradients
- *            with fp32 atomics instead; the results agree to rounding.
+ *            A smaller workspace (fewer queries per group) or, down to the
+ *            per-chunk buffers alone (the minimum V4ATTN_EWORKSPACE
+ *            reports), d_entries / d_win not 16-byte aligned or ids past
+ *            32 bits add the row gradients with fp32 atomics instead; the
+ *            results agree to rounding.  The queries' Ncap is the entry
+ *            capacity of d_entries (the destinations the sort counts).
  * Arithmetic: every attended row is gathered as bf16 (exact); q~, do and the
  * probabilities and dl enter bf16 matrix-core products with fp32
  * accumulation.  A row shared by several queries gets their gradients in an
