@@ -63,16 +63,6 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexScoreArgs a) {
   asm volatile("" ::"s"(a.B), "s"(a.Tq), "s"(a.HI), "s"(a.m), "s"((int)a.ragged));
   int b = blockIdx.z, blk = blockIdx.x, nblk = gridDim.x;
   const int r = blockIdx.y;
-  if (!(a.ragged && a.Tq == 1) && gridDim.y == 1 && (gridDim.z & 7) == 0) {
-    // Workgroups go to the eight XCDs in turn (linear id mod 8), each with
-    // its own L2: with the rows a multiple of 8, the linear id is remapped so
-    // that every workgroup of row b runs on XCD b mod 8, where the top-k
-    // part and select passes of that row run too and find its scores in L2.
-    const int L = blockIdx.x + (int)gridDim.x * blockIdx.z;
-    const int j = L >> 3;
-    b = (j / (int)gridDim.x) * 8 + (L & 7);
-    blk = j % (int)gridDim.x;
-  }
   if (a.ragged && a.Tq == 1) {   // flat grid: find this workgroup's sequence
     b = 0;
     while (b + 1 < a.B && (int)blockIdx.x >= a.wg_start[b + 1]) ++b;

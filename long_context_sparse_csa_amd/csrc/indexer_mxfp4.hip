@@ -86,25 +86,15 @@ __global__ __launch_bounds__(256) void index_score_mxfp4_kernel(IndexScoreMxfp4A
   constexpr int NL = CK / KPI;       // load instructions per chunk
   constexpr int NB = CK / 32;        // 32-key MFMA blocks per chunk
   constexpr int KSTR = RB + 16;      // padded LDS row: the operand reads hit distinct banks
-  // with the rows a multiple of 8, every workgroup of row b runs on XCD
-  // b mod 8 (workgroups go to the XCDs in turn), as the top-k passes of the
-  // row do: they find its scores in that XCD's L2
-  int b = blockIdx.z, bx = blockIdx.x;
-  if (gridDim.y == 1 && (gridDim.z & 7) == 0) {
-    const int L = blockIdx.x + (int)gridDim.x * blockIdx.z;
-    const int j = L >> 3;
-    b = (j / (int)gridDim.x) * 8 + (L & 7);
-    bx = j % (int)gridDim.x;
-  }
-  const int r = blockIdx.y;
+  const int b = blockIdx.z, r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = a.q_pos0 + r;
   int64_t V = (t + 1) / a.m;
   if (V > a.n_entries) V = a.n_entries;
   const int64_t nch = (V + CK - 1) / CK;
   const int64_t NW = (int64_t)gridDim.x * 4;
-  const int64_t gw = (int64_t)bx * 4 + wave;
-  if ((int64_t)bx * 4 >= nch) return;   // the whole block is past the visible keys
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+  if ((int64_t)blockIdx.x * 4 >= nch) return;   // the whole block is past the visible keys
 
   __shared__ __attribute__((aligned(16))) uint8_t s_k[4][CK * KSTR];
   __shared__ __attribute__((aligned(16))) float s_w[64];

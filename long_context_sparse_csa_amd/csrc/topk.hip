@@ -145,18 +145,8 @@ __device__ __forceinline__ void load_part(const TopkArgs& a, int64_t qr, int64_t
 __global__ __launch_bounds__(256) void topk_part_kernel(TopkArgs a) {
   read_args(a);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int64_t qr = blockIdx.y;
-  int bx = blockIdx.x;
-  if ((gridDim.y & 7) == 0) {
-    // every part of row qr on XCD qr mod 8 (workgroups go to the XCDs in
-    // turn): the decode indexer wrote the row's scores there, and the
-    // select workgroup of the row (workgroup qr) runs there too
-    const int L = blockIdx.x + (int)gridDim.x * blockIdx.y;
-    const int j = L >> 3;
-    qr = (j / (int)gridDim.x) * 8 + (L & 7);
-    bx = j % (int)gridDim.x;
-  }
-  const int p = bx * 4 + wave;
+  const int64_t qr = blockIdx.y;
+  const int p = blockIdx.x * 4 + wave;
   const int64_t V = visible_of(a, qr);
   if (V <= a.direct_max) return;   // such a row is selected directly
   const int P = topk_part_len(V, a.k);
