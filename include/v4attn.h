@@ -491,8 +491,10 @@ int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries,
  *   ws / ws_bytes: device workspace, 16-byte aligned.  With the bytes the
  *            matching *_backward_workspace(...) query returns, the row
  *            gradients are grouped: every (query, row slot) gradient is
- *            stored densely (at most 12 GiB per group of queries), the slots
- *            are sorted by destination row and each row is added to once.
+ *            stored densely as a 24-bit float (fp32 rounded to 16 mantissa
+ *            bits, nearest even; at most 12 GiB per group of queries), the
+ *            slots are sorted by destination row and each row is added to
+ *            once in fp32.
  *            A smaller workspace (fewer queries per group) or, down to the
  *            per-chunk buffers alone (the minimum V4ATTN_EWORKSPACE
  *            reports), d_entries / d_win not 16-byte aligned or ids past

@@ -1009,7 +1009,7 @@ int64_t bwd_group_queries(int B, int Tq, int D, int64_t rows_max, int64_t ndest,
   const size_t base = bwd_ws(B, Tq, D, rows_max);
   const auto fits = [&](int64_t g) {
     const size_t need = base + v4::bwd_group_bytes(D, np, g, ndest);
-    return need <= ws_bytes && (size_t)g * np * D * 4 <= ((size_t)12 << 30);
+    return need <= ws_bytes && (size_t)g * np * D * 3 <= ((size_t)12 << 30);   // 24-bit values
   };
   if (fits(nq)) return nq;
   int64_t lo = 0, hi = (nq - 1) / qc;  // chunks per group: fits(lo * qc) holds or lo = 0

@@ -327,6 +327,27 @@ __global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int
   if (hh == 0 && a.p_sel && x < a.k_sel) a.p_sel[(int64_t)qr * a.k_sel + x] = psum + s_ps[c];
 }
 
+typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
+
+// Dense per-slot gradients are kept as 24-bit floats (fp32 with the low 8
+// mantissa bits rounded off, to nearest even): four values in three words.
+// The relative rounding, 2^-16, is far below the bf16 roundings the products
+// already carry (2^-9), and the dense round trip moves 3/4 of the bytes.
+__device__ __forceinline__ uint32_t f24_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+__device__ __forceinline__ u32x3 f24_pack4(float a, float b, float c, float d) {
+  const uint32_t u0 = f24_bits(a), u1 = f24_bits(b), u2 = f24_bits(c), u3 = f24_bits(d);
+  return u32x3{u0 | (u1 << 24), (u1 >> 8) | (u2 << 16), (u2 >> 16) | (u3 << 8)};
+}
+__device__ __forceinline__ void f24_unpack4(uint32_t w0, uint32_t w1, uint32_t w2, float* o) {
+  o[0] = __uint_as_float(w0 << 8);
+  o[1] = __uint_as_float(((w0 >> 24) | (w1 << 8)) << 8);
+  o[2] = __uint_as_float(((w1 >> 16) | (w2 << 16)) << 8);
+  o[3] = __uint_as_float((w2 >> 8) << 8);
+}
+
 // dX = [scale dL; P]^T [q~; do] for one query (z), a tile of 128 row slots x
 // 128 dims, K = 128 head slots: both operands read k-contiguous (TT and YT).
 // The tile is stored densely past the caches (it is read back once, by the
@@ -350,13 +371,14 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(GemmArgs g) {
         sC[wm * 64 + 32 * mb + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)][wn * 64 + 32 * nb + (lane & 31)] =
             acc[mb][nb][e];
   __syncthreads();
-  if (!g.rowmap) {
-    float* cz = g.c + (int64_t)z * g.c_batch + n0 + lane;
+  if (!g.rowmap) {   // rows of ldc 24-bit values (3 ldc / 4 words); two rows a wave store
+    uint32_t* cz = reinterpret_cast<uint32_t*>(g.c) + ((int64_t)z * g.c_batch + n0) / 4 * 3;
+    const int half = lane >> 5, l = lane & 31;
 #pragma unroll 4
-    for (int mm = wave; mm < 128; mm += 4) {
-      float* row = cz + (int64_t)(m0 + mm) * g.ldc;
-      __builtin_nontemporal_store(sC[mm][lane], row);
-      __builtin_nontemporal_store(sC[mm][64 + lane], row + 64);
+    for (int mm = 2 * wave + half; mm < 128; mm += 8) {
+      u32x3* dst = reinterpret_cast<u32x3*>(cz + (int64_t)(m0 + mm) * (g.ldc / 4 * 3) + 3 * l);
+      __builtin_nontemporal_store(
+          f24_pack4(sC[mm][4 * l], sC[mm][4 * l + 1], sC[mm][4 * l + 2], sC[mm][4 * l + 3]), dst);
     }
     return;
   }
@@ -1068,7 +1090,7 @@ __global__ __launch_bounds__(256) void bwd_group_scatter_kernel(const int32_t* d
 // lanes a row, 64 / (D / 8) rows a wave), added to row d of out1 (d < n1)
 // or row d - n1 of out2.  Four slots' rows are in flight at a time; a group
 // past the list re-reads the last slot and drops it.
-template <int LPR>
+template <int LPR, bool F24>
 __global__ __launch_bounds__(256) void group_reduce_kernel(const float* dense, const int32_t* list,
                                                            const uint32_t* off, int64_t ndest, int D,
                                                            float* out1, int64_t n1, float* out2) {
@@ -1084,9 +1106,20 @@ __global__ __launch_bounds__(256) void group_reduce_kernel(const float* dense, c
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t id = list[min(o + (uint32_t)u, o1 - 1u)];
-      const float* r = dense + id * D + dd;
-      v0[u] = *reinterpret_cast<const f32x4*>(r);
-      v1[u] = *reinterpret_cast<const f32x4*>(r + 4);
+      if constexpr (F24) {   // 8 values in six words (three 8-byte loads)
+        const uint2* r = reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(dense) +
+                                                        id * (D / 4 * 3) + dd / 4 * 3);
+        const uint2 a = r[0], b = r[1], c = r[2];
+        float f[8];
+        f24_unpack4(a.x, a.y, b.x, f);
+        f24_unpack4(b.y, c.x, c.y, f + 4);
+        v0[u] = f32x4{f[0], f[1], f[2], f[3]};
+        v1[u] = f32x4{f[4], f[5], f[6], f[7]};
+      } else {
+        const float* r = dense + id * D + dd;
+        v0[u] = *reinterpret_cast<const f32x4*>(r);
+        v1[u] = *reinterpret_cast<const f32x4*>(r + 4);
+      }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -1136,8 +1169,8 @@ hipError_t group_begin(const GroupBufs& gb, hipStream_t st) {
 
 // After a group of nslots slots: counts to offsets, the slots listed by
 // destination, and each destination's sum added into its row.
-hipError_t group_sum(const GroupBufs& gb, int64_t nslots, const float* dense, int D, float* out1,
-                     int64_t n1, float* out2, hipStream_t st) {
+hipError_t group_sum(const GroupBufs& gb, int64_t nslots, const float* dense, int D, bool f24,
+                     float* out1, int64_t n1, float* out2, hipStream_t st) {
   const int64_t ntile = (gb.ndest + kGroupTile - 1) / kGroupTile;
   if (ntile == 0) return hipSuccess;
   bwd_group_tile_sum_kernel<<<(unsigned)ntile, 256, 0, st>>>(gb.cnt, gb.tsum, gb.ndest);
@@ -1149,8 +1182,11 @@ hipError_t group_sum(const GroupBufs& gb, int64_t nslots, const float* dense, in
   const int lpr = D / 8;
   const int64_t per_wg = 4 * (64 / lpr);
   const unsigned grid = (unsigned)((gb.ndest + per_wg - 1) / per_wg);
-#define V4_GROUP_REDUCE(L) \
-  group_reduce_kernel<L><<<grid, 256, 0, st>>>(dense, gb.list, gb.off, gb.ndest, D, out1, n1, out2)
+#define V4_GROUP_REDUCE(L)                                                                       \
+  (f24 ? group_reduce_kernel<L, true><<<grid, 256, 0, st>>>(dense, gb.list, gb.off, gb.ndest, D, \
+                                                             out1, n1, out2)                      \
+       : group_reduce_kernel<L, false><<<grid, 256, 0, st>>>(dense, gb.list, gb.off, gb.ndest, D, \
+                                                              out1, n1, out2))
   switch (lpr) {
     case 4: V4_GROUP_REDUCE(4); break;
     case 8: V4_GROUP_REDUCE(8); break;
@@ -1184,7 +1220,7 @@ size_t bwd_query_bytes(int D, int64_t np) {
 size_t bwd_group_bytes(int D, int64_t np, int64_t gq, int64_t ndest) {
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
   if (gq <= 0) return 0;
-  return al((size_t)gq * np * D * 4) + group_bytes(gq * np, ndest);   // dense dX, then the sort
+  return al((size_t)gq * np * D * 3) + group_bytes(gq * np, ndest);   // dense dX (24-bit), then the sort
 }
 
 hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, hipStream_t st) {
@@ -1205,7 +1241,7 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, h
   a.dXd = nullptr;
   GroupBufs gb{};
   if (gq > 0) {
-    a.dXd = reinterpret_cast<float*>(w);     w += al((size_t)gq * np * a.D * 4);
+    a.dXd = reinterpret_cast<float*>(w);     w += al((size_t)gq * np * a.D * 3);   // 24-bit values
     group_layout(gb, w, gq * np, a.ndest);
     a.dest = gb.dest;
     a.cnt = gb.cnt;
@@ -1246,7 +1282,10 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, h
       g3.b = a.YT; g3.ldb = 128; g3.b_batch = (int64_t)a.D * 128;
       g3.ldc = a.D; g3.K = 128; g3.alpha = 1.f; g3.n_valid = a.D;
       if (a.dXd) {
-        g3.c = a.dXd + (int64_t)(q0 - g0) * np * a.D; g3.c_batch = np * a.D;
+        // 24-bit values: the chunk's first slot is 3 np D (q0 - g0) bytes in
+        g3.c = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.dXd) +
+                                        (size_t)(q0 - g0) * np * a.D * 3);
+        g3.c_batch = np * a.D;
       } else {
         g3.c = a.d_entries; g3.c2 = a.d_win; g3.rowmap = a.rowmap; g3.rowmap_batch = np;
       }
@@ -1254,7 +1293,8 @@ hipError_t launch_attend_backward(BwdArgs a, int qchunk, int64_t gq, void* ws, h
       bwd_q_kernel<<<qc, 1024, 0, st>>>(a, q0);
     }
     if (gq > 0) {
-      const hipError_t e = group_sum(gb, (g1 - g0) * np, a.dXd, a.D, a.d_entries, a.nent, a.d_win, st);
+      const hipError_t e =
+          group_sum(gb, (g1 - g0) * np, a.dXd, a.D, true, a.d_entries, a.nent, a.d_win, st);
       if (e != hipSuccess) return e;
     }
   }
@@ -1351,7 +1391,7 @@ hipError_t launch_index_kl_backward(KlArgs a, int qchunk, int64_t gq, int64_t nd
       if (e != hipSuccess) return e;
     }
     if (gq > 0) {
-      const hipError_t e = group_sum(gb, (g1 - g0) * nsp, a.dKd, a.dI, a.dk, ndest, nullptr, st);
+      const hipError_t e = group_sum(gb, (g1 - g0) * nsp, a.dKd, a.dI, false, a.dk, ndest, nullptr, st);
       if (e != hipSuccess) return e;
     }
   }

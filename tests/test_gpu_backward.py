@@ -18,6 +18,8 @@ sum, so the bf16 rounding of out bounds its error by 2^-9 sum_d |dout out|,
 not by 2^-9 |D_h|.  Its bar is element-wise:
 |d d_sink_h| <= 2^-8 (sum_q p_sink sum_d |dout_qhd out_qhd| + |d_sink_h|)."""
 
+import re
+
 import numpy as np
 import pytest
 import torch
@@ -187,13 +189,21 @@ def test_hca_attend_backward_matches_oracle(case):
     _check(got, want, f"hca {case}")
 
 
+def _min_workspace(call):
+    """The smallest workspace a call accepts (the per-chunk buffers alone),
+    as the V4ATTN_EWORKSPACE error of a call with 16 bytes reports it."""
+    with pytest.raises(ops().V4AttnError) as err:
+        call(16)
+    m = re.search(r"need (\d+)", str(err.value))
+    assert err.value.status == -3 and m, str(err.value)
+    return int(m.group(1))
+
+
 def test_csa_backward_row_gradient_paths_match_oracle():
     """The row gradients grouped in one group (the queried workspace), in
     several groups (a byte less: 64 + 16 queries), and added with atomics
-    (room for the per-chunk buffers only), on 80 queries whose window rows
-    and top-k entries are shared.  At this shape the per-chunk buffers take
-    64 x ~131 KiB ~ 8.4 MB and a 64-query group's dense gradients 4.2 MB, so
-    the queried size less 4.5 MB holds no group."""
+    (the per-chunk buffers alone: the smallest workspace accepted), on 80
+    queries whose window rows and top-k entries are shared."""
     B, Tq, H, D, Ncap, k, W, q_pos0 = 2, 40, 8, 128, 300, 48, 16, 700
     q, ent, win, gq, sink, dout = _inputs(B, Tq, H, D, Ncap, W, 17)
     g = torch.Generator().manual_seed(9)
@@ -210,11 +220,16 @@ def test_csa_backward_row_gradient_paths_match_oracle():
         return tk[b, r], _win_rows(t, q_pos0, W)
 
     want = _reference(q, ent, win, gq, sink, dout, rows_of, q_pos0, W, scale, D)
-    for nbytes, what in ((full, "one group"), (full - 1, "two groups"),
-                         (full - (9 << 19), "atomics")):
+
+    def call(nbytes):
+        return ops().csa_attend_backward(q, ent, topk, win, gq, sink, out, lse, dout,
+                                         q_pos0=q_pos0, W=W, scale=scale, workspace_bytes=nbytes)
+
+    least = _min_workspace(call)
+    assert least < full - 1
+    for nbytes, what in ((full, "one group"), (full - 1, "two groups"), (least, "atomics")):
         log(f"csa backward row gradients: {what}, workspace {nbytes} of {full} bytes")
-        got = ops().csa_attend_backward(q, ent, topk, win, gq, sink, out, lse, dout,
-                                        q_pos0=q_pos0, W=W, scale=scale, workspace_bytes=nbytes)
+        got = call(nbytes)
         torch.cuda.synchronize()
         _check(got, want, f"csa rows {what}")
 
@@ -389,14 +404,15 @@ def test_index_kl_backward_matches_oracle(case):
 
 def test_index_kl_backward_key_gradient_paths_match_oracle():
     """dk grouped in one group (the queried workspace), in several (a byte
-    less: 256 + 44 queries), and added with atomics (2 MiB less: at this
-    shape the per-chunk buffers take 256 x ~57 KiB ~ 14.6 MB and a 256-query
-    group's dense dk 2.1 MB), on 300 queries whose sets share keys."""
+    less: 256 + 44 queries), and added with atomics (the per-chunk buffers
+    alone), on 300 queries whose sets share keys."""
     B, Tq, HI, dI, Ncap, ns = 1, 300, 4, 32, 200, 64
     inp = _kl_inputs(B, Tq, HI, dI, Ncap, ns, 60, 23)
     want = _kl_reference(*inp)
     full = ops().lib().v4attn_index_kl_backward_workspace(B, Tq, dI, ns, Ncap)
-    for nbytes, what in ((full, "one group"), (full - 1, "two groups"), (full - (1 << 21), "atomics")):
+    least = _min_workspace(lambda n: ops().index_kl_backward(*inp, workspace_bytes=n))
+    assert least < full - 1
+    for nbytes, what in ((full, "one group"), (full - 1, "two groups"), (least, "atomics")):
         log(f"indexer KL backward dk: {what}, workspace {nbytes} of {full} bytes")
         got = ops().index_kl_backward(*inp, workspace_bytes=nbytes)
         torch.cuda.synchronize()
