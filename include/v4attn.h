@@ -582,9 +582,10 @@ int v4attn_compress_backward(const uint16_t* raw, const float* tok_score,
  *   ws / ws_bytes: device workspace, 16-byte aligned.  With the bytes of
  *            v4attn_index_kl_backward_workspace(B, Tq, dI, ns, Ncap) and a
  *            16-byte aligned dk_idx, the key gradients are grouped: every
- *            (query, slot) dk row is stored densely (at most 12 GiB per
+ *            (query, slot) dk row is stored densely as 24-bit floats (fp32
+ *            rounded to 16 mantissa bits, nearest even; at most 12 GiB per
  *            group of queries), the slots are sorted by entry and each
- *            entry's row is added to once.  A smaller workspace, down to the
+ *            entry's row is added to once in fp32.  A smaller workspace, down to the
  *            per-chunk buffers (the minimum V4ATTN_EWORKSPACE reports), adds
  *            the dk rows with fp32 atomics instead.
  * 1 <= ns <= 4096, dI in {32, 64, 128}, HI <= 64.  q^I.k^I in fp32 from the

@@ -1175,7 +1175,7 @@ int64_t kl_group_queries(int B, int Tq, int dI, int ns, int64_t ndest, size_t ws
   const size_t base = kl_ws(B, Tq, dI, ns);
   const auto fits = [&](int64_t g) {
     return base + v4::kl_group_bytes(dI, nsp, g, ndest) <= ws_bytes &&
-           (size_t)g * nsp * dI * 4 <= ((size_t)12 << 30);
+           (size_t)g * nsp * dI * 3 <= ((size_t)12 << 30);   // 24-bit values
   };
   if (fits(nq)) return nq;
   int64_t lo = 0, hi = (nq - 1) / qc;   // chunks per group: fits(lo * qc) holds or lo = 0

@@ -38,6 +38,27 @@ __device__ __forceinline__ uint16_t f2bf(float f) {   // round to nearest even (
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
+
+// Dense per-slot gradients are kept as 24-bit floats (fp32 with the low 8
+// mantissa bits rounded off, to nearest even): four values in three words.
+// The relative rounding, 2^-16, is far below the bf16 roundings the products
+// already carry (2^-9), and the dense round trip moves 3/4 of the bytes.
+__device__ __forceinline__ uint32_t f24_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+__device__ __forceinline__ u32x3 f24_pack4(float a, float b, float c, float d) {
+  const uint32_t u0 = f24_bits(a), u1 = f24_bits(b), u2 = f24_bits(c), u3 = f24_bits(d);
+  return u32x3{u0 | (u1 << 24), (u1 >> 8) | (u2 << 16), (u2 >> 16) | (u3 << 8)};
+}
+__device__ __forceinline__ void f24_unpack4(uint32_t w0, uint32_t w1, uint32_t w2, float* o) {
+  o[0] = __uint_as_float(w0 << 8);
+  o[1] = __uint_as_float(((w0 >> 24) | (w1 << 8)) << 8);
+  o[2] = __uint_as_float(((w1 >> 16) | (w2 << 16)) << 8);
+  o[3] = __uint_as_float((w2 >> 8) << 8);
+}
+
 // The tile (x, y) and batch z of this workgroup in a batched launch.
 // Workgroups go to the eight XCDs in turn (linear id mod 8), each XCD with
 // its own L2; when the batch count is a multiple of 8 the linear id is
@@ -130,6 +151,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) sC[wm * 32 + 16 * i + 4 * gq + v][wn * 32 + 16 * j + c] = acc[i][j][v];
   __syncthreads();
+  if (!g.rowmap && g.f24) {   // rows of ldc 24-bit values; 16 lanes a row, 4 values a lane
+    const int cg = lane & 15;
+    if (n0 + 4 * cg >= g.n_valid) return;   // n_valid is a multiple of 4
+    uint32_t* cz = reinterpret_cast<uint32_t*>(g.c) + ((int64_t)z * g.c_batch + n0) / 4 * 3 + 3 * cg;
+#pragma unroll 4
+    for (int mm = 4 * wave + (lane >> 4); mm < 64; mm += 16)
+      __builtin_nontemporal_store(f24_pack4(g.alpha * sC[mm][4 * cg], g.alpha * sC[mm][4 * cg + 1],
+                                            g.alpha * sC[mm][4 * cg + 2], g.alpha * sC[mm][4 * cg + 3]),
+                                  reinterpret_cast<u32x3*>(cz + (int64_t)(m0 + mm) * (g.ldc / 4 * 3)));
+    return;
+  }
   const int n = n0 + lane;
   if (n >= g.n_valid) return;
   if (!g.rowmap) {
@@ -325,27 +357,6 @@ __global__ __launch_bounds__(256) void bwd_sdp_kernel(GemmArgs g, BwdArgs a, int
   if (hh == 1) s_ps[c] = psum;
   __syncthreads();
   if (hh == 0 && a.p_sel && x < a.k_sel) a.p_sel[(int64_t)qr * a.k_sel + x] = psum + s_ps[c];
-}
-
-typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
-
-// Dense per-slot gradients are kept as 24-bit floats (fp32 with the low 8
-// mantissa bits rounded off, to nearest even): four values in three words.
-// The relative rounding, 2^-16, is far below the bf16 roundings the products
-// already carry (2^-9), and the dense round trip moves 3/4 of the bytes.
-__device__ __forceinline__ uint32_t f24_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
-}
-__device__ __forceinline__ u32x3 f24_pack4(float a, float b, float c, float d) {
-  const uint32_t u0 = f24_bits(a), u1 = f24_bits(b), u2 = f24_bits(c), u3 = f24_bits(d);
-  return u32x3{u0 | (u1 << 24), (u1 >> 8) | (u2 << 16), (u2 >> 16) | (u3 << 8)};
-}
-__device__ __forceinline__ void f24_unpack4(uint32_t w0, uint32_t w1, uint32_t w2, float* o) {
-  o[0] = __uint_as_float(w0 << 8);
-  o[1] = __uint_as_float(((w0 >> 24) | (w1 << 8)) << 8);
-  o[2] = __uint_as_float(((w1 >> 16) | (w2 << 16)) << 8);
-  o[3] = __uint_as_float((w2 >> 8) << 8);
 }
 
 // dX = [scale dL; P]^T [q~; do] for one query (z), a tile of 128 row slots x
@@ -1319,7 +1330,7 @@ size_t kl_query_bytes(int64_t nsp, int dIp) {
 size_t kl_group_bytes(int dI, int64_t nsp, int64_t gq, int64_t ndest) {
   auto al = [](size_t n) { return (n + 255) / 256 * 256; };
   if (gq <= 0) return 0;
-  return al((size_t)gq * nsp * dI * 4) + group_bytes(gq * nsp, ndest);   // dense dK, then the sort
+  return al((size_t)gq * nsp * dI * 3) + group_bytes(gq * nsp, ndest);   // dense dK (24-bit), then the sort
 }
 
 hipError_t launch_index_kl_backward(KlArgs a, int qchunk, int64_t gq, int64_t ndest, void* ws,
@@ -1338,7 +1349,7 @@ hipError_t launch_index_kl_backward(KlArgs a, int qchunk, int64_t gq, int64_t nd
   a.dKd = nullptr;
   GroupBufs gb{};
   if (gq > 0) {
-    a.dKd = reinterpret_cast<float*>(w);     w += al((size_t)gq * nsp * a.dI * 4);
+    a.dKd = reinterpret_cast<float*>(w);     w += al((size_t)gq * nsp * a.dI * 3);   // 24-bit values
     group_layout(gb, w, gq * nsp, ndest);
     a.dest = gb.dest;
     a.cnt = gb.cnt;
@@ -1382,8 +1393,10 @@ hipError_t launch_index_kl_backward(KlArgs a, int qchunk, int64_t gq, int64_t nd
       g3.a = a.Gm; g3.lda = nsp; g3.a_batch = 64 * nsp;
       g3.b = a.Qi; g3.ldb = a.dIp; g3.b_batch = 64 * (int64_t)a.dIp;
       g3.ldc = a.dI; g3.K = 64; g3.alpha = 1.f; g3.n_valid = a.dI;
-      if (a.dKd) {
-        g3.c = a.dKd + (int64_t)(q0 - g0) * nsp * a.dI; g3.c_batch = nsp * a.dI;
+      if (a.dKd) {   // 24-bit values: the chunk's first slot is 3 nsp dI (q0 - g0) bytes in
+        g3.c = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.dKd) +
+                                        (size_t)(q0 - g0) * nsp * a.dI * 3);
+        g3.c_batch = nsp * a.dI; g3.f24 = 1;
       } else {
         g3.c = a.dk; g3.rowmap = a.rowmap; g3.rowmap_batch = nsp;
       }
@@ -1391,7 +1404,7 @@ hipError_t launch_index_kl_backward(KlArgs a, int qchunk, int64_t gq, int64_t nd
       if (e != hipSuccess) return e;
     }
     if (gq > 0) {
-      const hipError_t e = group_sum(gb, (g1 - g0) * nsp, a.dKd, a.dI, false, a.dk, ndest, nullptr, st);
+      const hipError_t e = group_sum(gb, (g1 - g0) * nsp, a.dKd, a.dI, true, a.dk, ndest, nullptr, st);
       if (e != hipSuccess) return e;
     }
   }

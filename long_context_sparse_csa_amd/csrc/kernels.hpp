@@ -268,6 +268,7 @@ struct GemmArgs {
   int K;
   float alpha;
   int n_valid;               // columns >= n_valid are not stored
+  int f24;                   // dense C stored as 24-bit values (4 in 3 words)
 };
 
 // Attention backward (both kinds: CSA when topk != nullptr).
