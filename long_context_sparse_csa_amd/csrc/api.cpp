@@ -976,13 +976,15 @@ int v4attn_nsa_attend(const uint16_t* q, const uint8_t* entries, const uint8_t* 
 
 namespace {
 
-// Attention backward: queries are processed in chunks whose per-query
-// buffers (gathered rows, [S; dP], [scale dL; P], ...) fit about 1 GiB.
+// Attention backward: queries are processed in chunks of at most 128 whose
+// per-query buffers (gathered rows, [S; dP], [scale dL; P], ...) fit about
+// 1 GiB (128 rather than 64 queries a chunk: 11.8 -> 11.2 ms at 4096 x 1152
+// rows; 256 gained nothing more).
 int bwd_chunk(int64_t nq, int D, int64_t np) {
   const size_t per = v4::bwd_query_bytes(D, np);
   int64_t c = (int64_t)(((size_t)1 << 30) / per);
   if (c < 1) c = 1;
-  if (c > 64) c = 64;
+  if (c > 128) c = 128;
   return (int)(c < nq ? c : (nq > 0 ? nq : 1));
 }
 

@@ -201,10 +201,10 @@ def _min_workspace(call):
 
 def test_csa_backward_row_gradient_paths_match_oracle():
     """The row gradients grouped in one group (the queried workspace), in
-    several groups (a byte less: 64 + 16 queries), and added with atomics
-    (the per-chunk buffers alone: the smallest workspace accepted), on 80
+    several groups (a byte less: 128 + 32 queries), and added with atomics
+    (the per-chunk buffers alone: the smallest workspace accepted), on 160
     queries whose window rows and top-k entries are shared."""
-    B, Tq, H, D, Ncap, k, W, q_pos0 = 2, 40, 8, 128, 300, 48, 16, 700
+    B, Tq, H, D, Ncap, k, W, q_pos0 = 2, 80, 8, 128, 300, 48, 16, 700
     q, ent, win, gq, sink, dout = _inputs(B, Tq, H, D, Ncap, W, 17)
     g = torch.Generator().manual_seed(9)
     topk = torch.stack([torch.stack([torch.randperm(120, generator=g)[:k].sort().values
