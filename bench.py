@@ -197,6 +197,38 @@ def run_timed_graphs(st, rotate, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def run_timed_replays(graphs, steps, warmup):
+    """Replays of HIP graphs used in turn, between two HIP events on the
+    current stream: milliseconds per replay."""
+    import torch
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def one_stream_graphs(st, rotate):
+    """One HIP graph per HCA cache copy of the headline step's one-stream
+    calls (the CSA layer's, then the HCA layer's)."""
+    import torch
+    from long_context_sparse_csa_amd import decode
+    graphs = []
+    for r in range(rotate):
+        f = st.calls(r)
+        lr = [(n, f[n]) for n in CSA_LAYER + HCA_LAYER]
+        for _, fn in lr:
+            fn()
+        torch.cuda.synchronize()
+        graphs.append(decode.capture_launches(lr))
+    return graphs
+
+
 def run_breakdown(launches, steps):
     """Per-call HIP-event durations on the launching (current) stream."""
     import torch
@@ -653,17 +685,19 @@ def stack_section(dev, steps, pairs=2):
     import torch
     from long_context_sparse_csa_amd import decode
     from long_context_sparse_csa_amd.configs import CSA_1M, HCA_1M
-    launches = []
+    sts = []
     for i in range(pairs):
         c = CSA_1M.with_(seed=CSA_1M.seed + 1000 * (i + 1))
         h = HCA_1M.with_(B=CSA_1M.B, seed=HCA_1M.seed + 1000 * (i + 1))
         st = decode.DecodeStep(decode.build_inputs(c, h, dev), c, h, dev)
-        f = st.calls(0)
-        launches += [(f"L{2 * i}_{n}", f[n]) for n in CSA_LAYER]
-        launches += [(f"L{2 * i + 1}_{n}", f[n]) for n in HCA_LAYER]
+        sts.append(st)
+    launches = decode.stack_launches(sts)
     torch.cuda.synchronize()
     ms, _ = run_timed(launches, steps, 5)
     br = run_breakdown(launches, 20)
+    # the whole stack as one HIP graph (the launches have run eagerly above)
+    g = decode.capture_launches(launches)
+    ms_g = run_timed_replays([g], steps, 5)
     B, L = CSA_1M.B, 2 * pairs
     t_csa = sum(v for k, v in br.items() if k.split("_", 1)[1] in CSA_LAYER) / pairs
     t_hca = sum(v for k, v in br.items() if k.split("_", 1)[1] in HCA_LAYER) / pairs
@@ -672,6 +706,8 @@ def stack_section(dev, steps, pairs=2):
                     f"(CSA m=4 k=1024, HCA m'=128; W=128, H=64, D=512), each with its own caches",
         "stack_us": round(ms * 1e3, 2),
         "query_token_layers_per_s": round(B * L / (ms * 1e-3), 1),
+        "hip_graph_replay_stack_us": round(ms_g * 1e3, 2),
+        "hip_graph_query_token_layers_per_s": round(B * L / (ms_g * 1e-3), 1),
         "csa_layer_us": round(t_csa, 2),
         "hca_layer_us": round(t_hca, 2),
     }
@@ -964,7 +1000,16 @@ def main():
         "roofline": roofline,
         "wall_s": round(wall, 3),
     }
+    # the same one-stream step replayed from HIP graphs (one per HCA cache copy)
+    ms_g = run_timed_replays(one_stream_graphs(st, args.rotate), args.steps, args.warmup)
+    res["hip_graph_one_stream"] = {
+        "what": "the headline step's calls (CSA layer, then HCA layer, one stream) replayed "
+                "from HIP graphs, one per HCA cache copy",
+        "step_us": round(ms_g * 1e3, 2),
+        "query_token_layers_per_s": round((c.B + h.B) / (ms_g * 1e-3), 1),
+    }
     log("per layer: " + json.dumps(res["per_layer"]))
+    log("one-stream graph replay: " + json.dumps(res["hip_graph_one_stream"]))
     # the same calls with the two layers' independent batches overlapped: both
     # compress steps in one launch, the HCA attention on a second stream
     # beside the CSA indexer, top-k and attention (not open to a dependent

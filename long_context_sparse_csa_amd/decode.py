@@ -12,6 +12,9 @@ the CSA layer's indexer, top-k and attention on the launching stream and the
 HCA layer's attention on a second stream beside them (every kernel that
 reads an entry, an indexer key or a window row runs after the compress step
 that writes it).  `capture` records that schedule in a HIP graph.
+`stack_launches` lists the calls of a dependent stack of alternating CSA and
+HCA layers (each layer's calls after the previous layer's, one stream) and
+`capture_launches` records such a list in one HIP graph.
 
 Inputs are seeded synthetic tensors shaped like the workloads in configs.py
 (the random-number recipe is in synth.py).  The HCA caches can rotate over
@@ -186,3 +189,32 @@ class DecodeStep:
         with torch.cuda.graph(g):
             self.run_concurrent(rot)
         return g
+
+
+# the calls of one layer, in order (the per-layer compress steps)
+CSA_LAYER = ("csa_compress", "index_score", "topk_select", "csa_attend")
+HCA_LAYER = ("hca_compress", "hca_attend")
+
+
+def stack_launches(steps, rot=0):
+    """(name, fn) launches of a stack of alternating layers: for each
+    DecodeStep in `steps`, its CSA layer's calls and then its HCA layer's
+    (layers 2i and 2i + 1), all on the current stream, so every layer runs
+    after the one before it as in a model."""
+    out = []
+    for i, st in enumerate(steps):
+        f = st.calls(rot)
+        out += [(f"L{2 * i}_{n}", f[n]) for n in CSA_LAYER]
+        out += [(f"L{2 * i + 1}_{n}", f[n]) for n in HCA_LAYER]
+    return out
+
+
+def capture_launches(launches):
+    """A HIP graph of the launches in order on one stream.  Run them eagerly
+    once before capturing, so that nothing is allocated during the capture;
+    the library itself allocates nothing and records no memset."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, fn in launches:
+            fn()
+    return g

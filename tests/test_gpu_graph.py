@@ -160,3 +160,40 @@ def test_decode_step_schedules_and_graph_replays_match_eager():
         st.run_eager(1 - r)
         assert _same(_snap(st), ref[1 - r]), f"eager run after replay {i}"
         torch.zeros(1 << 20, device=DEV).sum().item()
+
+
+def test_layer_stack_graph_replays_match_eager():
+    """Four alternating layers (CSA, HCA, CSA, HCA, each pair with its own
+    caches) on one stream, captured as one HIP graph: every replay equals the
+    eager launches bit for bit, with the written rows poisoned before each run
+    and eager work and synchronisation between replays."""
+    c, h = _small()
+    sts = []
+    for i in range(2):
+        ci = c.with_(seed=c.seed + 1000 * (i + 1))
+        hi = h.with_(seed=h.seed + 1000 * (i + 1))
+        sts.append(decode.DecodeStep(decode.build_inputs(ci, hi, DEV, rotate=1), ci, hi, DEV))
+    launches = decode.stack_launches(sts)
+    names = [n for n, _ in launches]
+    assert names[:6] == ["L0_csa_compress", "L0_index_score", "L0_topk_select",
+                         "L0_csa_attend", "L1_hca_compress", "L1_hca_attend"]
+    assert len(names) == 12
+
+    def run_eager():
+        for st in sts:
+            _poison(st, 0)
+        for _, fn in launches:
+            fn()
+        return [x for st in sts for x in _snap(st)]
+
+    ref = run_eager()
+    assert not torch.equal(ref[1], ref[6]), "the two CSA layers should differ"
+    g = decode.capture_launches(launches)
+    for i in range(4):
+        for st in sts:
+            _poison(st, 0)
+        g.replay()
+        got = [x for st in sts for x in _snap(st)]
+        assert _same(got, ref), f"stack replay {i}"
+        assert _same(run_eager(), ref), f"eager stack after replay {i}"
+        torch.zeros(1 << 20, device=DEV).sum().item()
