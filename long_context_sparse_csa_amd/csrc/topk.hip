@@ -121,22 +121,41 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
 
 // The keys of lane `lane` in the part starting at `base` of row qr:
 // positions base + 64r + lane for r < P / 64 (absent past the part
-// and past the row's visible entries).
-__device__ __forceinline__ void load_part(const TopkArgs& a, int64_t qr, int64_t V, int64_t base,
-                                          int P, int lane, unsigned (&key)[16]) {
-  const float* src = a.scores + qr * a.score_stride;
+// and past the row's visible entries).  part_loads issues the loads and
+// returns how many of the part's keys exist; part_keys turns the loaded
+// scores into keys once they are needed.  The loads go through one buffer
+// resource over the part's scores: they share the lane's offset (each with
+// its own immediate offset), and a read past the part returns 0 without a
+// memory access, so no per-load address arithmetic or clamping is needed.
+__device__ __forceinline__ int part_loads(const TopkArgs& a, int64_t qr, int64_t V, int64_t base,
+                                          int P, int lane, float (&f)[16]) {
+  // every caller's part is the same across the wave: say so, so that the
+  // buffer resource is a scalar one
+  base = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)base) |
+         ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32);
   int64_t end = base + P;
   if (end > V) end = V;
-  // every load is issued (a load in a branch is waited for at once); one
-  // past the part or the row re-reads the part's first score (base < V)
+  const int n = end > base ? (int)(end - base) : 0;   // the part's keys (none past the row)
+  const __amdgpu_buffer_rsrc_t rs =
+      buf_rsrc(a.scores + qr * a.score_stride + base, (uint32_t)n * 4u);
+  const uint32_t lo = (uint32_t)lane * 4u;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    f[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, lo + 256u * r, 0, 0));
+  return n;
+}
+
+__device__ __forceinline__ void part_keys(const float (&f)[16], int n, int lane,
+                                          unsigned (&key)[16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) key[r] = lane < n - 64 * r ? score_key(f[r]) : 0u;
+}
+
+__device__ __forceinline__ void load_part(const TopkArgs& a, int64_t qr, int64_t V, int64_t base,
+                                          int P, int lane, unsigned (&key)[16]) {
   float f[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t i = base + 64 * r + lane;
-    f[r] = src[i < end ? i : base];
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) key[r] = base + 64 * r + lane < end ? score_key(f[r]) : 0u;
+  const int n = part_loads(a, qr, V, base, P, lane, f);
+  part_keys(f, n, lane, key);
 }
 
 // ---- part leaders: x_p = the 16th largest lane maximum (0 if fewer than 16
@@ -144,19 +163,31 @@ __device__ __forceinline__ void load_part(const TopkArgs& a, int64_t qr, int64_t
 // order, the first kTopkPartCap stored, the largest of the rest recorded.
 __global__ __launch_bounds__(256) void topk_part_kernel(TopkArgs a) {
   read_args(a);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index as a scalar: the part's buffer resources are then
+  // uniform (no per-lane waterfall around each buffer access)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t qr = blockIdx.y;
-  const int p = blockIdx.x * 4 + wave;
   const int64_t V = visible_of(a, qr);
   if (V <= a.direct_max) return;   // such a row is selected directly
   const int P = topk_part_len(V, a.k);
-  if (p >= parts_of(V, P)) return;   // past this row's parts
-  const int64_t base = (int64_t)p * P;
-  unsigned x = 0u, over = 0u;
-  int cnt = 0;
-  if (base < V) {
+  const int np = (int)parts_of(V, P);
+  // A wave takes parts p, p + stride, ... of its row (one part a wave when
+  // the grid spans the row's parts; several when rows are many), the next
+  // part's loads in flight while it works on the current one.  A part past
+  // the row loads nothing (its buffer range is empty).
+  const int stride = (int)gridDim.x * 4;
+  int p = blockIdx.x * 4 + wave;
+  if (p >= np) return;   // past this row's parts
+  float f[16];
+  int n = part_loads(a, qr, V, (int64_t)p * P, P, lane, f);
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (; p < np; p += stride) {
     unsigned key[16];
-    load_part(a, qr, V, base, P, lane, key);
+    part_keys(f, n, lane, key);
+    n = part_loads(a, qr, V, (int64_t)(p + stride) * P, P, lane, f);   // the next part
+    const int64_t base = (int64_t)p * P;
+    unsigned x = 0u, over = 0u;
+    int cnt = 0;
     unsigned lmax = 0u;
 #pragma unroll
     for (int r = 0; r < 16; ++r) lmax = max(lmax, key[r]);
@@ -166,28 +197,31 @@ __global__ __launch_bounds__(256) void topk_part_kernel(TopkArgs a) {
       if (__popcll(__ballot(lmax >= cand)) >= 16) x = cand;
     }
     const unsigned thr = x > 0u ? x : 1u;
-    const unsigned long long lt = (1ull << lane) - 1ull;
-    unsigned* ck = a.cand_key + ((int64_t)qr * a.nparts + p) * kTopkPartCap;
-    int* ci = a.cand_idx + ((int64_t)qr * a.nparts + p) * kTopkPartCap;
+    // the part's candidate slots through buffer resources (32-bit offsets,
+    // no 64-bit address arithmetic per store)
+    const int64_t cbase = ((int64_t)qr * a.nparts + p) * kTopkPartCap;
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.cand_key + cbase, kTopkPartCap * 4u);
+    const __amdgpu_buffer_rsrc_t ri = buf_rsrc(a.cand_idx + cbase, kTopkPartCap * 4u);
+    const int ib = (int)base + lane;   // parts start below 2^31
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const bool pass = key[r] >= thr;
       const unsigned long long bl = __ballot(pass);
       const int pos = cnt + __popcll(bl & lt);
       if (pass && pos < kTopkPartCap) {
-        ck[pos] = key[r];
-        ci[pos] = (int)(base + 64 * r + lane);
+        __builtin_amdgcn_raw_buffer_store_b32(key[r], rk, (uint32_t)pos * 4u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32((unsigned)(ib + 64 * r), ri, (uint32_t)pos * 4u, 0, 0);
       } else if (pass) {
         over = max(over, key[r]);
       }
       cnt += __popcll(bl);
     }
     over = wave_max_u(over);
-  }
-  if (lane == 0) {
-    a.part_tau[qr * a.nparts + p] = x;
-    a.part_cnt[qr * a.nparts + p] = cnt;
-    a.part_over[qr * a.nparts + p] = over;
+    if (lane == 0) {
+      a.part_tau[qr * a.nparts + p] = x;
+      a.part_cnt[qr * a.nparts + p] = cnt;
+      a.part_over[qr * a.nparts + p] = over;
+    }
   }
 }
 
@@ -767,7 +801,11 @@ hipError_t launch_topk(const TopkArgs& a, const TopkPlan& plan, hipStream_t st) 
     g_topk_attr_set = true;
   }
   if (plan.parts) {
-    const dim3 grid((unsigned)((plan.nparts + 3) / 4), (unsigned)rows);
+    // one part a wave over the chip when the rows are few (decode); with
+    // more than ~64K parts in all, four parts a wave, each wave's next part
+    // loading while it works on the current one
+    const int ppw = (int64_t)plan.nparts * rows > 65536 ? 4 : 1;
+    const dim3 grid((unsigned)((plan.nparts + 4 * ppw - 1) / (4 * ppw)), (unsigned)rows);
     topk_part_kernel<<<grid, 256, 0, st>>>(a);
   }
   topk_select_kernel<<<(unsigned)rows, kSelThreads, lds, st>>>(a);
