@@ -35,6 +35,7 @@
 // lowest-positioned keys inside it, so the output comes out in ascending
 // index order.
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -787,18 +788,25 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
 }
 
 
-static bool g_topk_attr_set = false;
+// devices (bit d: device d < 64) on which the select kernel's dynamic LDS
+// limit has been raised; the attribute is set once per device, the first
+// time a launch there needs it (setting it twice is harmless)
+static std::atomic<uint64_t> g_topk_attr_devices{0};
 
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& plan, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.Tq;
   if (rows == 0) return hipSuccess;
   const size_t lds =
       (size_t)(2 * kTopkSel + kHistBins + kTopkMaxParts + 1 + kTopkMaxParts / 32) * sizeof(unsigned);
-  if (!g_topk_attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
+  if (!bit || !(g_topk_attr_devices.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute((const void*)topk_select_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    g_topk_attr_set = true;
+    g_topk_attr_devices.fetch_or(bit, std::memory_order_release);
   }
   if (plan.parts) {
     // one part a wave over the chip when the rows are few (decode); with
